@@ -1,0 +1,392 @@
+// escha_api.cpp -- the C ABI of libescha.so (declared in include/escha.h):
+// host-side validation, workspace layout and launch sequencing. No entry
+// point allocates memory; every launch goes on the caller's stream.
+#include <hip/hip_runtime_api.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "escha.h"
+#include "escha_launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(ESCHA_E_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int32_t kMaxTopK = 64;
+constexpr int32_t kMaxHidden = 16384;  // k_combine keeps one fp32 row in LDS
+constexpr int32_t kMaxExpertsRoute = 1024;
+
+int check_proj(const escha_proj_t* w, const char* what) {
+  if (!w) return fail(ESCHA_E_NULL, "%s: descriptor is NULL", what);
+  if (!w->code || !w->rin || !w->rout) return fail(ESCHA_E_NULL, "%s: code/rin/rout is NULL", what);
+  if (w->k_bits != 2 && w->k_bits != 3)
+    return fail(ESCHA_E_KBITS, "%s: k_bits=%d, must be 2 or 3", what, (int)w->k_bits);
+  if (w->n_experts < 1) return fail(ESCHA_E_SHAPE, "%s: n_experts=%d", what, (int)w->n_experts);
+  if (w->in_features < 128 || w->in_features % 128)
+    return fail(ESCHA_E_SHAPE, "%s: in_features=%d is not a positive multiple of 128", what,
+                (int)w->in_features);
+  if (w->out_features < 256 || w->out_features % 256)
+    return fail(ESCHA_E_SHAPE, "%s: out_features=%d is not a positive multiple of 256", what,
+                (int)w->out_features);
+  if (!aligned(w->code, 16)) return fail(ESCHA_E_ARG, "%s: code is not 16-byte aligned", what);
+  if (!aligned(w->rin, 2) || !aligned(w->rout, 2))
+    return fail(ESCHA_E_ARG, "%s: rin/rout are not 2-byte aligned", what);
+  return ESCHA_OK;
+}
+
+int check_layer(const escha_moe_layer_t* L) {
+  if (!L) return fail(ESCHA_E_NULL, "layer descriptor is NULL");
+  int rc = check_proj(&L->gate_up, "gate_up");
+  if (rc) return rc;
+  rc = check_proj(&L->down, "down");
+  if (rc) return rc;
+  if (L->gate_up.in_features != L->hidden || L->gate_up.out_features != 2 * L->inter ||
+      L->down.in_features != L->inter || L->down.out_features != L->hidden)
+    return fail(ESCHA_E_SHAPE,
+                "layer shapes disagree: hidden=%d inter=%d gate_up %dx%d down %dx%d", L->hidden,
+                L->inter, L->gate_up.in_features, L->gate_up.out_features, L->down.in_features,
+                L->down.out_features);
+  if (L->gate_up.n_experts != L->down.n_experts)
+    return fail(ESCHA_E_SHAPE, "gate_up has %d experts, down has %d", L->gate_up.n_experts,
+                L->down.n_experts);
+  if (L->hidden > kMaxHidden) return fail(ESCHA_E_UNSUPPORTED, "hidden=%d > %d", L->hidden, kMaxHidden);
+  if (L->top_k < 1 || L->top_k > kMaxTopK || L->top_k > L->gate_up.n_experts)
+    return fail(ESCHA_E_ARG, "top_k=%d out of range", L->top_k);
+  return ESCHA_OK;
+}
+
+// ---------------------------------------------------------------- decode ws
+struct DecodeWs {
+  float* gu_part;  // [P][hidden/128][2*inter]
+  float* dn_part;  // [P][inter/128][hidden]
+};
+
+size_t decode_ws_bytes(const escha_moe_layer_t* L, int64_t T) {
+  const int64_t P = T * L->top_k;
+  const size_t gu = (size_t)P * (L->hidden / 128) * (2 * L->inter) * sizeof(float);
+  const size_t dn = (size_t)P * (L->inter / 128) * L->hidden * sizeof(float);
+  return round_up(gu) + round_up(dn);
+}
+
+DecodeWs decode_ws_carve(const escha_moe_layer_t* L, int64_t T, void* ws) {
+  const int64_t P = T * L->top_k;
+  const size_t gu = (size_t)P * (L->hidden / 128) * (2 * L->inter) * sizeof(float);
+  char* b = (char*)ws;
+  DecodeWs d;
+  d.gu_part = (float*)b;
+  d.dn_part = (float*)(b + round_up(gu));
+  return d;
+}
+
+// One layer over T tokens through the streaming kernels.
+int run_layer_decode(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
+                     const float* w, float* y, float* inter_out, uint16_t* x_next, float eps,
+                     const DecodeWs& ws, hipStream_t s) {
+  const int P = T * L->top_k;
+  escha::InPartialArgs a{};
+  a.code = (const uint16_t*)L->gate_up.code;
+  a.rin = (const uint16_t*)L->gate_up.rin;
+  a.n_experts = L->gate_up.n_experts;
+  a.in_f = L->hidden;
+  a.out_f = 2 * L->inter;
+  a.n_pairs = P;
+  a.top_k = L->top_k;
+  a.ids = ids;
+  a.fixed_expert = 0;
+  a.x_bf16 = x;
+  a.partial = ws.gu_part;
+  hipError_t e = escha::launch_in_partial(a, L->gate_up.k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "gate_up partial launch");
+
+  escha::DownPartialArgs d{};
+  d.code = (const uint16_t*)L->down.code;
+  d.rin = (const uint16_t*)L->down.rin;
+  d.n_experts = L->down.n_experts;
+  d.in_f = L->inter;
+  d.out_f = L->hidden;
+  d.n_pairs = P;
+  d.ids = ids;
+  d.gu_partial = ws.gu_part;
+  d.gu_chunks = L->hidden / 128;
+  d.gu_rout = (const uint16_t*)L->gate_up.rout;
+  d.inter_out = inter_out;
+  d.partial = ws.dn_part;
+  e = escha::launch_down_partial(d, L->down.k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "down partial launch");
+
+  escha::CombineArgs c{};
+  c.partial = ws.dn_part;
+  c.n_chunks = L->inter / 128;
+  c.rout = (const uint16_t*)L->down.rout;
+  c.ids = ids;
+  c.w = w;
+  c.n_experts = L->down.n_experts;
+  c.hidden = L->hidden;
+  c.top_k = L->top_k;
+  c.n_tokens = T;
+  c.y = y;
+  c.x_next = x_next;
+  c.eps = eps;
+  e = escha::launch_combine(c, s);
+  if (e != hipSuccess) return hip_fail(e, "combine launch");
+  return ESCHA_OK;
+}
+
+// Token batch of the streaming path used by the prefill entry point.
+constexpr int32_t kPrefillBatch = 64;
+
+int check_layer_call(const escha_moe_layer_t* L, const uint16_t* x, int32_t T, const int32_t* ids,
+                     const float* w, const float* y) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (T < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", T);
+  if (T > 0 && (!x || !ids || !w || !y)) return fail(ESCHA_E_NULL, "x/topk_ids/topk_w/y is NULL");
+  return ESCHA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* escha_last_error(void) { return g_err; }
+
+int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t* w_f16, void* stream) {
+  int rc = check_proj(w, "decode_tiles");
+  if (rc) return rc;
+  if (expert < 0 || expert >= w->n_experts)
+    return fail(ESCHA_E_ARG, "expert=%d out of [0, %d)", expert, w->n_experts);
+  if (!w_f16) return fail(ESCHA_E_NULL, "w_f16 is NULL");
+  if (!aligned(w_f16, 8)) return fail(ESCHA_E_ARG, "w_f16 is not 8-byte aligned");
+  const size_t per_expert = (size_t)(w->in_features / 16) * (w->out_features / 16) * 16 * w->k_bits;
+  const uint16_t* code_e = (const uint16_t*)w->code + (size_t)expert * per_expert;
+  hipError_t e = escha::launch_decode_tiles(code_e, w->in_features, w->out_features, w->k_bits,
+                                            w_f16, (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "decode_tiles launch");
+}
+
+int escha_hadamard128(const float* x, int64_t rows, int32_t n, float* y, void* stream) {
+  if (rows < 0 || n < 128 || n % 128) return fail(ESCHA_E_SHAPE, "rows=%lld n=%d", (long long)rows, n);
+  if (rows == 0) return ESCHA_OK;
+  if (!x || !y) return fail(ESCHA_E_NULL, "x/y is NULL");
+  hipError_t e = escha::launch_hadamard128(x, rows, n, y, (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "hadamard128 launch");
+}
+
+int escha_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                     int32_t* topk_ids, float* topk_w, void* stream) {
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n_experts < 1 || n_experts > kMaxExpertsRoute)
+    return fail(ESCHA_E_ARG, "n_experts=%d out of [1, %d]", n_experts, kMaxExpertsRoute);
+  if (top_k < 1 || top_k > 32 || top_k > n_experts) return fail(ESCHA_E_ARG, "top_k=%d", top_k);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!logits || !topk_ids || !topk_w) return fail(ESCHA_E_NULL, "logits/topk_ids/topk_w is NULL");
+  hipError_t e = escha::launch_route_topk(logits, n_tokens, n_experts, top_k, topk_ids, topk_w,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "route_topk launch");
+}
+
+size_t escha_moe_group_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts) {
+  if (n_tokens < 0 || top_k < 1 || n_experts < 1) return 0;
+  const size_t P = (size_t)n_tokens * top_k;
+  const size_t chunks = (P + 63) / 64;
+  return 2 * round_up(chunks * n_experts * sizeof(int32_t)) + round_up(P * sizeof(int32_t)) + 256;
+}
+
+int escha_moe_group(const int32_t* topk_ids, int32_t n_tokens, int32_t top_k, int32_t n_experts,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0 || top_k < 1 || n_experts < 1 || n_experts > kMaxExpertsRoute)
+    return fail(ESCHA_E_ARG, "n_tokens=%d top_k=%d n_experts=%d", n_tokens, top_k, n_experts);
+  if ((int64_t)n_tokens * top_k > (int64_t)1 << 30) return fail(ESCHA_E_ARG, "too many pairs");
+  if (!counts || !offsets) return fail(ESCHA_E_NULL, "counts/offsets is NULL");
+  const int P = n_tokens * top_k;
+  if (P > 0 && (!topk_ids || !perm)) return fail(ESCHA_E_NULL, "topk_ids/perm is NULL");
+  const size_t need = escha_moe_group_workspace_bytes(n_tokens, top_k, n_experts);
+  if (workspace_bytes < need || (!workspace && need))
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const size_t chunks = ((size_t)P + 63) / 64;
+  char* b = (char*)workspace;
+  int32_t* hist = (int32_t*)b;
+  int32_t* base = (int32_t*)(b + round_up(chunks * n_experts * sizeof(int32_t)));
+  int32_t* rank = (int32_t*)(b + 2 * round_up(chunks * n_experts * sizeof(int32_t)));
+  hipError_t e = escha::launch_group(topk_ids, P, n_experts, counts, offsets, perm, hist, base,
+                                     rank, (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "group launch");
+}
+
+size_t escha_expert_gemv_workspace_bytes(const escha_proj_t* w, int32_t n_tokens) {
+  if (!w || n_tokens < 0 || w->in_features < 128 || w->out_features < 256) return 0;
+  return round_up((size_t)n_tokens * (w->in_features / 128) * w->out_features * sizeof(float));
+}
+
+int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_bf16,
+                      int32_t n_tokens, float* y, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  int rc = check_proj(w, "expert_gemv");
+  if (rc) return rc;
+  if (expert < 0 || expert >= w->n_experts)
+    return fail(ESCHA_E_ARG, "expert=%d out of [0, %d)", expert, w->n_experts);
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!x_bf16 || !y) return fail(ESCHA_E_NULL, "x/y is NULL");
+  const size_t need = escha_expert_gemv_workspace_bytes(w, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  escha::InPartialArgs a{};
+  a.code = (const uint16_t*)w->code;
+  a.rin = (const uint16_t*)w->rin;
+  a.n_experts = w->n_experts;
+  a.in_f = w->in_features;
+  a.out_f = w->out_features;
+  a.n_pairs = n_tokens;
+  a.top_k = 1;
+  a.ids = nullptr;
+  a.fixed_expert = expert;
+  a.x_bf16 = x_bf16;
+  a.partial = (float*)workspace;
+  hipError_t e = escha::launch_in_partial(a, w->k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "expert_gemv partial launch");
+  escha::FinishArgs f{};
+  f.partial = (const float*)workspace;
+  f.n_chunks = w->in_features / 128;
+  f.rout = (const uint16_t*)w->rout;
+  f.n_experts = w->n_experts;
+  f.out_f = w->out_features;
+  f.n_pairs = n_tokens;
+  f.ids = nullptr;
+  f.fixed_expert = expert;
+  f.y = y;
+  e = escha::launch_proj_finish(f, s);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "expert_gemv finish launch");
+}
+
+size_t escha_moe_workspace_bytes(const escha_moe_layer_t* L, int32_t n_tokens, int32_t prefill) {
+  if (!L || n_tokens < 0 || L->top_k < 1 || L->hidden < 128 || L->inter < 128) return 0;
+  const int64_t T = prefill ? (n_tokens < kPrefillBatch ? n_tokens : kPrefillBatch) : n_tokens;
+  return decode_ws_bytes(L, T);
+}
+
+int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
+                           const int32_t* topk_ids, const float* topk_w, float* y,
+                           float* inter_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  int rc = check_layer_call(L, x_bf16, n_tokens, topk_ids, topk_w, y);
+  if (rc) return rc;
+  if (n_tokens == 0) return ESCHA_OK;
+  const size_t need = escha_moe_workspace_bytes(L, n_tokens, 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const DecodeWs ws = decode_ws_carve(L, n_tokens, workspace);
+  return run_layer_decode(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, nullptr, 0.f, ws,
+                          (hipStream_t)stream);
+}
+
+int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
+                            const int32_t* topk_ids, const float* topk_w, float* y,
+                            float* inter_out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  int rc = check_layer_call(L, x_bf16, n_tokens, topk_ids, topk_w, y);
+  if (rc) return rc;
+  if (n_tokens == 0) return ESCHA_OK;
+  const size_t need = escha_moe_workspace_bytes(L, n_tokens, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const int k = L->top_k;
+  for (int32_t t0 = 0; t0 < n_tokens; t0 += kPrefillBatch) {
+    const int32_t nt = n_tokens - t0 < kPrefillBatch ? n_tokens - t0 : kPrefillBatch;
+    const DecodeWs ws = decode_ws_carve(L, nt, workspace);
+    rc = run_layer_decode(L, x_bf16 + (size_t)t0 * L->hidden, nt, topk_ids + (size_t)t0 * k,
+                          topk_w + (size_t)t0 * k, y + (size_t)t0 * L->hidden,
+                          inter_out ? inter_out + (size_t)t0 * k * L->inter : nullptr, nullptr,
+                          0.f, ws, (hipStream_t)stream);
+    if (rc) return rc;
+  }
+  return ESCHA_OK;
+}
+
+int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, float eps, uint16_t* x_bf16,
+                       void* stream) {
+  if (n_tokens < 0 || n < 1) return fail(ESCHA_E_ARG, "n_tokens=%d n=%d", n_tokens, n);
+  if (!(eps >= 0.f)) return fail(ESCHA_E_ARG, "eps must be >= 0");
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!y || !x_bf16) return fail(ESCHA_E_NULL, "y/x is NULL");
+  hipError_t e = escha::launch_rmsnorm_bf16(y, n_tokens, n, eps, x_bf16, (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "rmsnorm launch");
+}
+
+size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t n_layers,
+                                       int32_t n_tokens) {
+  if (!layers || n_layers < 1 || n_tokens < 0) return 0;
+  const escha_moe_layer_t* L = &layers[0];
+  const size_t xbuf = round_up((size_t)n_tokens * L->hidden * sizeof(uint16_t));
+  const size_t ybuf = round_up((size_t)n_tokens * L->hidden * sizeof(float));
+  return decode_ws_bytes(L, n_tokens) + 2 * xbuf + ybuf;
+}
+
+int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
+                           const uint16_t* x0_bf16, int32_t n_tokens, const int32_t* topk_ids,
+                           const float* topk_w, float eps, float* y_last, uint16_t* x_chain,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!layers) return fail(ESCHA_E_NULL, "layers is NULL");
+  if (n_layers < 1) return fail(ESCHA_E_ARG, "n_layers=%d", n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    int rc = check_layer_call(&layers[l], x0_bf16, n_tokens, topk_ids, topk_w, y_last);
+    if (rc) return rc;
+    if (layers[l].hidden != layers[0].hidden || layers[l].inter != layers[0].inter ||
+        layers[l].top_k != layers[0].top_k)
+      return fail(ESCHA_E_SHAPE, "layer %d differs from layer 0 in hidden/inter/top_k", l);
+  }
+  if (!(eps >= 0.f)) return fail(ESCHA_E_ARG, "eps must be >= 0");
+  if (n_tokens == 0) return ESCHA_OK;
+  const size_t need = escha_moe_stack_workspace_bytes(layers, n_layers, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const escha_moe_layer_t* L0 = &layers[0];
+  const int H = L0->hidden, k = L0->top_k;
+  char* b = (char*)workspace;
+  const DecodeWs ws = decode_ws_carve(L0, n_tokens, b);
+  b += decode_ws_bytes(L0, n_tokens);
+  const size_t xbuf = round_up((size_t)n_tokens * H * sizeof(uint16_t));
+  uint16_t* xa = (uint16_t*)b;
+  uint16_t* xb = (uint16_t*)(b + xbuf);
+  float* ytmp = (float*)(b + 2 * xbuf);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t xs = (size_t)n_tokens * H;
+  if (x_chain) {
+    hipError_t e = hipMemcpyAsync(x_chain, x0_bf16, xs * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "x_chain copy");
+  }
+  const uint16_t* x = x0_bf16;
+  for (int l = 0; l < n_layers; ++l) {
+    const bool last = l == n_layers - 1;
+    uint16_t* x_next = nullptr;
+    if (!last) x_next = x_chain ? x_chain + (size_t)(l + 1) * xs : ((l & 1) ? xb : xa);
+    float* y = last ? y_last : ytmp;
+    int rc = run_layer_decode(&layers[l], x, n_tokens, topk_ids + (size_t)l * n_tokens * k,
+                              topk_w + (size_t)l * n_tokens * k, y, nullptr, x_next, eps, ws, s);
+    if (rc) return rc;
+    x = x_next;
+  }
+  return ESCHA_OK;
+}
+
+}  // extern "C"

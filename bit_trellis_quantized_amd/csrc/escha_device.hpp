@@ -1,0 +1,176 @@
+// escha_device.hpp -- device routines shared by the gfx950 kernels of
+// libescha: the trellis tile decoder, the in-wave 128-point Hadamard and
+// number-format helpers.
+//
+// Format (sources: model card "Qwen3.6-35B-A3B-Escha-W2-trellis-mlx",
+// exactness table; hipfire PR "Escha-W2 port: 2-bit trellis decoded in the
+// GEMV", closing summary "What it is"):
+//  - a 16x16 tile is 16*K little-endian uint16 words = a 256*K-bit stream,
+//    bit b being bit b%16 of word b/16;
+//  - weight i (input row i/16, output column i%16 of the tile) is the
+//    16-bit window of the stream starting at bit K*i, first bit least
+//    significant, wrapping at the end of the tile;
+//  - a state s decodes as r = (s*0xCBAC1FED mod 2^32 & 0x8FFF8FFF) ^
+//    0x3B603B60, weight = fp16(lo16 r) + fp16(hi16 r) rounded to nearest
+//    even.
+//
+// Work split inside a wave: four lanes share one tile. Lane q of the four
+// holds a quarter of the stream (16 B at K=2, 24 B at K=3) plus the first
+// dword of the next quarter, and decodes the 64 weights whose windows start
+// in its quarter: input rows 4q..4q+3 of the tile, all 16 output columns.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace escha {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kInvSqrt128 = 0.08838834764831845f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Decode the two 16-bit states packed in V (low and high half) into two fp16
+// weights packed the same way.
+//
+// With C = C1*2^16 + C0 (C1 = 0xCBAC, C0 = 0x1FED), s*C mod 2^32 has low half
+// lo16(s*C0) and high half hi16(s*C0) + lo16(s*C1) (mod 2^16). The two
+// 16x16->32 products s*C0 are the only full-width multiplies; the rest runs
+// on packed 16-bit lanes, and one packed fp16 add (round-to-nearest-even,
+// the hardware default) forms both weights.
+__device__ __forceinline__ h16x2 cba_decode_pair(uint32_t V) {
+  const uint32_t a = V & 0xFFFFu;
+  const uint32_t b = V >> 16;
+  const uint32_t ma = a * 0x1FEDu;
+  const uint32_t mb = b * 0x1FEDu;
+  uint32_t lo = __builtin_amdgcn_perm(mb, ma, 0x05040100u);        // lo16(ma) | lo16(mb) << 16
+  const uint32_t zh = __builtin_amdgcn_perm(mb, ma, 0x07060302u);  // hi16(ma) | hi16(mb) << 16
+  const u16x2 c1 = {(unsigned short)0xCBAC, (unsigned short)0xCBAC};
+  const u16x2 hv = __builtin_bit_cast(u16x2, V) * c1 + __builtin_bit_cast(u16x2, zh);
+  uint32_t hi = __builtin_bit_cast(uint32_t, hv);
+  lo = (lo & 0x8FFF8FFFu) ^ 0x3B603B60u;
+  hi = (hi & 0x8FFF8FFFu) ^ 0x3B603B60u;
+  return __builtin_bit_cast(h16x2, lo) + __builtin_bit_cast(h16x2, hi);
+}
+
+// 32 stream bits starting at bit `o` of the lane's dwords d[] (o known at
+// compile time after unrolling).
+template <int O>
+__device__ __forceinline__ uint32_t window32(const uint32_t* d) {
+  if constexpr (O % 32 == 0) {
+    return d[O / 32];
+  } else {
+    return __builtin_amdgcn_alignbit(d[O / 32 + 1], d[O / 32], O % 32);
+  }
+}
+
+// Packed states of weights (kk, n) and (kk, n+8) of the lane's quarter:
+// relative stream offsets K*(16*kk + n) and that + 8*K.
+template <int K, int KK, int N>
+__device__ __forceinline__ uint32_t quarter_state_pair(const uint32_t* d) {
+  constexpr int o = K * (16 * KK + N);
+  if constexpr (K == 2) {
+    // the partner window starts 16 bits later: one 32-bit window holds both
+    return window32<o>(d);
+  } else {
+    // the partner starts 24 bits later: take its 16 bits from the window
+    // that begins 8 bits after ours (its bits 16..31)
+    const uint32_t w0 = window32<o>(d);
+    const uint32_t w1 = window32<o + 8>(d);
+    return __builtin_amdgcn_perm(w1, w0, 0x07060100u);
+  }
+}
+
+// Number of dwords a lane holds: its quarter (2K) plus the next quarter's
+// first dword (the wrap reaches at most 15 bits into it).
+template <int K>
+struct Quarter {
+  static constexpr int kOwn = 2 * K;
+  static constexpr int kAll = 2 * K + 1;
+};
+
+// Decode the lane's 64 weights and hand each packed pair to f(kk, n, w):
+// w.x = weight (row 4q+kk, column n), w.y = weight (row 4q+kk, column n+8).
+template <int K, int KK = 0, int N = 0, class F>
+__device__ __forceinline__ void decode_quarter(const uint32_t* d, F&& f) {
+  if constexpr (KK < 4) {
+    if constexpr (N < 8) {
+      const h16x2 w = cba_decode_pair(quarter_state_pair<K, KK, N>(d));
+      f(KK, N, w);
+      decode_quarter<K, KK, N + 1>(d, f);
+    } else {
+      decode_quarter<K, KK + 1, 0>(d, f);
+    }
+  }
+}
+
+// Load the lane's quarter of a tile. `tq` points at the quarter's first
+// word (16-byte aligned at K=2, 8-byte aligned at K=3).
+template <int K>
+__device__ __forceinline__ void load_quarter(const uint16_t* tq, uint32_t* d) {
+  if constexpr (K == 2) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tq));
+    d[0] = v.x;
+    d[1] = v.y;
+    d[2] = v.z;
+    d[3] = v.w;
+  } else {
+    const u32x2* p = reinterpret_cast<const u32x2*>(tq);
+    const u32x2 a = __builtin_nontemporal_load(p + 0);
+    const u32x2 b = __builtin_nontemporal_load(p + 1);
+    const u32x2 c = __builtin_nontemporal_load(p + 2);
+    d[0] = a.x;
+    d[1] = a.y;
+    d[2] = b.x;
+    d[3] = b.y;
+    d[4] = c.x;
+    d[5] = c.y;
+  }
+}
+
+// First dword of the next quarter of the same tile (lanes 4t..4t+3 share a
+// tile; lane 4t+3 wraps to lane 4t). quad_perm [1,2,3,0].
+__device__ __forceinline__ uint32_t next_quarter_dword(uint32_t d0) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0x39, 0xF, 0xF, false);
+}
+
+// 128-point Sylvester Walsh-Hadamard transform (unscaled) across one wave:
+// element i of the block is v0 of lane i for i < 64 and v1 of lane i-64
+// otherwise. Butterflies: bit 6 inside the lane, bits 5..0 across lanes.
+__device__ __forceinline__ void fwht128(float& v0, float& v1) {
+  const float a = v0 + v1;
+  const float b = v0 - v1;
+  v0 = a;
+  v1 = b;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) {
+    const float p0 = __shfl_xor(v0, h, 64);
+    const float p1 = __shfl_xor(v1, h, 64);
+    const bool upper = (lane & h) != 0;
+    v0 = upper ? (p0 - v0) : (v0 + p0);
+    v1 = upper ? (p1 - v1) : (v1 + p1);
+  }
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+}  // namespace escha

@@ -1,0 +1,560 @@
+// escha_kernels.hip -- gfx950 kernels of the trellis-coded expert path and
+// their host-side launchers (called by escha_api.cpp after validation).
+//
+// Streaming-decode kernels (small batches): one wave per (pair, group of 16
+// output tiles = 256 outputs, chunk of 128 inputs = one Hadamard block).
+// Each wave rotates its 128-input block of the activation in registers,
+// streams 8 tile-rows of codes (one 16-byte load per lane per tile-row at
+// K=2), decodes in registers and accumulates in fp32. Splits over the input
+// dimension land in a partial buffer that the next kernel reduces in a
+// fixed order, so results are bit-reproducible with no atomics.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "escha_device.hpp"
+#include "escha_launch.hpp"
+
+namespace escha {
+
+// ------------------------------------------------------------------------
+// Shared inner loop: 8 tile-rows (one 128-input chunk) of 16 output tiles.
+// xs: the chunk's rotated activations (LDS, 128 floats). Returns the 16
+// per-column sums of this lane's quarter; the caller reduces the quarters.
+// ------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ void chunk_mac(const uint16_t* __restrict__ code_e, int n_nt, int kt0,
+                                          int nt, int q, const float* xs, float (&acc)[16]) {
+  constexpr int kOwn = Quarter<K>::kOwn;
+  uint32_t raw[8][kOwn];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint16_t* tq = code_e + ((size_t)(kt0 + j) * n_nt + nt) * (16 * K) + q * (4 * K);
+    load_quarter<K>(tq, raw[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t d[kOwn + 1];
+#pragma unroll
+    for (int i = 0; i < kOwn; ++i) d[i] = raw[j][i];
+    d[kOwn] = next_quarter_dword(raw[j][0]);
+    const float4 xv = *reinterpret_cast<const float4*>(xs + 16 * j + 4 * q);
+    const float xk[4] = {xv.x, xv.y, xv.z, xv.w};
+    decode_quarter<K>(d, [&](int kk, int n, h16x2 w) {
+      acc[n] = __builtin_fmaf((float)w.x, xk[kk], acc[n]);
+      acc[n + 8] = __builtin_fmaf((float)w.y, xk[kk], acc[n + 8]);
+    });
+  }
+}
+
+// Sum the four quarter-lanes' column sums; every lane of the quad gets the
+// total. Lane q then owns output columns 4q..4q+3 of its tile.
+__device__ __forceinline__ float4 quad_reduce_pick(float (&acc)[16], int q) {
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    acc[n] += __shfl_xor(acc[n], 1, 64);
+    acc[n] += __shfl_xor(acc[n], 2, 64);
+  }
+  float4 r;
+  r.x = q == 0 ? acc[0] : q == 1 ? acc[4] : q == 2 ? acc[8] : acc[12];
+  r.y = q == 0 ? acc[1] : q == 1 ? acc[5] : q == 2 ? acc[9] : acc[13];
+  r.z = q == 0 ? acc[2] : q == 1 ? acc[6] : q == 2 ? acc[10] : acc[14];
+  r.w = q == 0 ? acc[3] : q == 1 ? acc[7] : q == 2 ? acc[11] : acc[15];
+  return r;
+}
+
+// ------------------------------------------------------------------------
+// gate_up (or any single projection) partial sums.
+// grid.x = n_pairs * n_chunks * n_groups, block = 64.
+// ------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(64) void k_in_partial(InPartialArgs a) {
+  const int n_groups = a.out_f / 256;
+  const int n_chunks = a.in_f / 128;
+  int bid = blockIdx.x;
+  const int g = bid % n_groups;
+  bid /= n_groups;
+  const int c = bid % n_chunks;
+  const int p = bid / n_chunks;
+  const int lane = threadIdx.x;
+  float* out = a.partial + ((size_t)p * n_chunks + c) * a.out_f + g * 256;
+  const int e = a.ids ? a.ids[p] : a.fixed_expert;
+  if (e < 0 || e >= a.n_experts) {
+    reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int t = p / a.top_k;
+
+  __shared__ __attribute__((aligned(16))) float xs[128];
+  {
+    const uint16_t* xr = a.x_bf16 + (size_t)t * a.in_f + c * 128;
+    const uint16_t* rr = a.rin + (size_t)e * a.in_f + c * 128;
+    float v0 = bf16_to_f32(xr[lane]) * f16_to_f32(rr[lane]);
+    float v1 = bf16_to_f32(xr[lane + 64]) * f16_to_f32(rr[lane + 64]);
+    fwht128(v0, v1);
+    xs[lane] = v0 * kInvSqrt128;
+    xs[lane + 64] = v1 * kInvSqrt128;
+  }
+  __syncthreads();
+
+  const int q = lane & 3;
+  const int nt = g * 16 + (lane >> 2);
+  const int n_nt = a.out_f / 16;
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.in_f / 16) * n_nt * (16 * K);
+  float acc[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+  chunk_mac<K>(code_e, n_nt, 8 * c, nt, q, xs, acc);
+  reinterpret_cast<float4*>(out)[lane] = quad_reduce_pick(acc, q);
+}
+
+// ------------------------------------------------------------------------
+// down partial sums. The prologue finishes gate_up for the 128 inter
+// channels of this wave's chunk: reduce the gate_up partials, H128, rout,
+// SiLU(gate)*up; then rin and H128 of down. A chunk whose 128 h values are
+// all exactly zero contributes exactly zero and is skipped.
+// ------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(64) void k_down_partial(DownPartialArgs a) {
+  const int n_groups = a.out_f / 256;
+  const int n_chunks = a.in_f / 128;  // in_f = inter
+  int bid = blockIdx.x;
+  const int g = bid % n_groups;
+  bid /= n_groups;
+  const int c = bid % n_chunks;
+  const int p = bid / n_chunks;
+  const int lane = threadIdx.x;
+  float* out = a.partial + ((size_t)p * n_chunks + c) * a.out_f + g * 256;
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.n_experts) {
+    reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  const int inter = a.in_f;
+  const int g2 = 2 * inter;
+
+  float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+  {
+    const float* gp = a.gu_partial + (size_t)p * a.gu_chunks * g2 + 128 * c;
+    for (int cc = 0; cc < a.gu_chunks; ++cc) {
+      const float* b = gp + (size_t)cc * g2;
+      g0 += b[lane];
+      g1 += b[lane + 64];
+      u0 += b[inter + lane];
+      u1 += b[inter + lane + 64];
+    }
+  }
+  fwht128(g0, g1);
+  fwht128(u0, u1);
+  const uint16_t* ro = a.gu_rout + (size_t)e * g2 + 128 * c;
+  g0 = g0 * kInvSqrt128 * f16_to_f32(ro[lane]);
+  g1 = g1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
+  u0 = u0 * kInvSqrt128 * f16_to_f32(ro[inter + lane]);
+  u1 = u1 * kInvSqrt128 * f16_to_f32(ro[inter + lane + 64]);
+  const float h0 = silu(g0) * u0;
+  const float h1 = silu(g1) * u1;
+  if (a.inter_out && g == 0) {
+    float* io = a.inter_out + (size_t)p * inter + 128 * c;
+    io[lane] = h0;
+    io[lane + 64] = h1;
+  }
+  if (__ballot((h0 != 0.f) || (h1 != 0.f)) == 0) {
+    reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+
+  __shared__ __attribute__((aligned(16))) float xs[128];
+  {
+    const uint16_t* rr = a.rin + (size_t)e * inter + 128 * c;
+    float v0 = h0 * f16_to_f32(rr[lane]);
+    float v1 = h1 * f16_to_f32(rr[lane + 64]);
+    fwht128(v0, v1);
+    xs[lane] = v0 * kInvSqrt128;
+    xs[lane + 64] = v1 * kInvSqrt128;
+  }
+  __syncthreads();
+
+  const int q = lane & 3;
+  const int nt = g * 16 + (lane >> 2);
+  const int n_nt = a.out_f / 16;
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)(inter / 16) * n_nt * (16 * K);
+  float acc[16];
+#pragma unroll
+  for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+  chunk_mac<K>(code_e, n_nt, 8 * c, nt, q, xs, acc);
+  reinterpret_cast<float4*>(out)[lane] = quad_reduce_pick(acc, q);
+}
+
+// ------------------------------------------------------------------------
+// Finish one projection per pair: reduce partials, H128, rout.
+// grid.x = n_pairs * (out_f / 128), block = 64.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
+  const int nb = a.out_f / 128;
+  const int b = blockIdx.x % nb;
+  const int p = blockIdx.x / nb;
+  const int lane = threadIdx.x;
+  const int e = a.ids ? a.ids[p] : a.fixed_expert;
+  float* y = a.y + (size_t)p * a.out_f + 128 * b;
+  if (e < 0 || e >= a.n_experts) {
+    y[lane] = 0.f;
+    y[lane + 64] = 0.f;
+    return;
+  }
+  float z0 = 0.f, z1 = 0.f;
+  const float* pp = a.partial + (size_t)p * a.n_chunks * a.out_f + 128 * b;
+  for (int cc = 0; cc < a.n_chunks; ++cc) {
+    z0 += pp[(size_t)cc * a.out_f + lane];
+    z1 += pp[(size_t)cc * a.out_f + lane + 64];
+  }
+  fwht128(z0, z1);
+  const uint16_t* ro = a.rout + (size_t)e * a.out_f + 128 * b;
+  y[lane] = z0 * kInvSqrt128 * f16_to_f32(ro[lane]);
+  y[lane + 64] = z1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
+}
+
+// ------------------------------------------------------------------------
+// Combine: per token, finish down for each slot (reduce partials, H128,
+// rout) and sum the slots in order, weighted by the router probabilities.
+// Optionally RMS-normalise the row and round it to bf16 for the next layer.
+// grid.x = n_tokens, block = 1024 (16 waves; wave w owns blocks w, w+16, ..).
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float row[];  // hidden floats
+  __shared__ float wave_ss[16];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nb = a.hidden / 128;
+  float ss = 0.f;
+  for (int b = wave; b < nb; b += 16) {
+    float acc0 = 0.f, acc1 = 0.f;
+    for (int j = 0; j < a.top_k; ++j) {
+      const int p = t * a.top_k + j;
+      const int e = a.ids[p];
+      if (e < 0 || e >= a.n_experts) continue;
+      const float wt = a.w[p];
+      float z0 = 0.f, z1 = 0.f;
+      const float* pp = a.partial + (size_t)p * a.n_chunks * a.hidden + 128 * b;
+      for (int cc = 0; cc < a.n_chunks; ++cc) {
+        z0 += pp[(size_t)cc * a.hidden + lane];
+        z1 += pp[(size_t)cc * a.hidden + lane + 64];
+      }
+      fwht128(z0, z1);
+      const uint16_t* ro = a.rout + (size_t)e * a.hidden + 128 * b;
+      const float y0 = z0 * kInvSqrt128 * f16_to_f32(ro[lane]);
+      const float y1 = z1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
+      acc0 = __builtin_fmaf(wt, y0, acc0);
+      acc1 = __builtin_fmaf(wt, y1, acc1);
+    }
+    float* y = a.y + (size_t)t * a.hidden + 128 * b;
+    y[lane] = acc0;
+    y[lane + 64] = acc1;
+    row[128 * b + lane] = acc0;
+    row[128 * b + lane + 64] = acc1;
+    ss = __builtin_fmaf(acc0, acc0, ss);
+    ss = __builtin_fmaf(acc1, acc1, ss);
+  }
+  if (!a.x_next) return;  // uniform across the block
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
+  if (lane == 0) wave_ss[wave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int w = 0; w < 16; ++w) tot += wave_ss[w];
+  const float inv = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
+  uint16_t* xo = a.x_next + (size_t)t * a.hidden;
+  for (int i = threadIdx.x; i < a.hidden; i += 1024) xo[i] = f32_to_bf16_rne(row[i] * inv);
+}
+
+// ------------------------------------------------------------------------
+// Standalone RMSNorm -> bf16. grid.x = n_tokens, block = 256.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* __restrict__ y, int n, float eps,
+                                                      uint16_t* __restrict__ x) {
+  __shared__ float wave_ss[4];
+  const float* yr = y + (size_t)blockIdx.x * n;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < n; i += 256) ss = __builtin_fmaf(yr[i], yr[i], ss);
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
+  if ((threadIdx.x & 63) == 0) wave_ss[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = wave_ss[0] + wave_ss[1] + wave_ss[2] + wave_ss[3];
+  const float inv = 1.0f / sqrtf(tot / (float)n + eps);
+  uint16_t* xr = x + (size_t)blockIdx.x * n;
+  for (int i = threadIdx.x; i < n; i += 256) xr[i] = f32_to_bf16_rne(yr[i] * inv);
+}
+
+// ------------------------------------------------------------------------
+// Decode one expert's weights to fp16 [out][in] (bit-exact export).
+// grid.x = (in/16) * (out/256), block = 64.
+// ------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(64) void k_decode_tiles(const uint16_t* __restrict__ code_e, int in_f,
+                                                     int out_f, uint16_t* __restrict__ w) {
+  const int n_groups = out_f / 256;
+  const int g = blockIdx.x % n_groups;
+  const int kt = blockIdx.x / n_groups;
+  const int lane = threadIdx.x;
+  const int q = lane & 3;
+  const int nt = g * 16 + (lane >> 2);
+  const int n_nt = out_f / 16;
+  constexpr int kOwn = Quarter<K>::kOwn;
+  uint32_t d[kOwn + 1];
+  load_quarter<K>(code_e + ((size_t)kt * n_nt + nt) * (16 * K) + q * (4 * K), d);
+  d[kOwn] = next_quarter_dword(d[0]);
+  uint32_t cols[16][2];  // per output column n: rows 4q..4q+3 as two packed pairs
+  decode_quarter<K>(d, [&](int kk, int n, h16x2 wv) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, wv);
+    const uint32_t lo = bits & 0xFFFFu, hi = bits >> 16;
+    uint32_t& c0 = cols[n][kk >> 1];
+    uint32_t& c8 = cols[n + 8][kk >> 1];
+    if (kk & 1) {
+      c0 |= lo << 16;
+      c8 |= hi << 16;
+    } else {
+      c0 = lo;
+      c8 = hi;
+    }
+  });
+#pragma unroll
+  for (int n = 0; n < 16; ++n) {
+    uint16_t* dst = w + (size_t)(16 * nt + n) * in_f + 16 * kt + 4 * q;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(cols[n][0], cols[n][1]);
+  }
+}
+
+// ------------------------------------------------------------------------
+// y = H_n x per 128-block. grid.x = rows * (n/128), block = 64.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_hadamard128(const float* x, int n, float* y) {
+  const int nb = n / 128;
+  const size_t r = blockIdx.x / nb;
+  const int b = blockIdx.x % nb;
+  const int lane = threadIdx.x;
+  const float* xr = x + r * n + 128 * b;
+  float v0 = xr[lane], v1 = xr[lane + 64];
+  fwht128(v0, v1);
+  float* yr = y + r * n + 128 * b;
+  yr[lane] = v0 * kInvSqrt128;
+  yr[lane + 64] = v1 * kInvSqrt128;
+}
+
+// ------------------------------------------------------------------------
+// Router: softmax + top-k per token. grid.x = n_tokens, block = 64.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_route_topk(const float* __restrict__ logits, int E, int k,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ w) {
+  constexpr int kMaxPer = 16;  // E <= 1024
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* l = logits + (size_t)t * E;
+  float v[kMaxPer];
+  uint32_t taken = 0;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? l[e] : -INFINITY;
+    m = fmaxf(m, v[j]);
+    if (e >= E) taken |= 1u << j;
+  }
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j)
+    if (lane + 64 * j < E) s += expf(v[j] - m);
+#pragma unroll
+  for (int h = 32; h >= 1; h >>= 1) s += __shfl_xor(s, h, 64);
+  for (int r = 0; r < k; ++r) {
+    // lane-local best untaken: larger value, then lower index
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int e = lane + 64 * j;
+      if (!(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+      const float ov = __shfl_xor(bv, h, 64);
+      const int oi = __shfl_xor(bi, h, 64);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == 0) {
+      ids[(size_t)t * k + r] = bi;
+      w[(size_t)t * k + r] = expf(bv - m) / s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Grouping pairs by expert (counting sort, stable in the pair index).
+// Pass 1: per chunk of 64 pairs, per-expert counts and in-chunk ranks.
+// Pass 2: one block scans the chunk counts per expert and the totals.
+// Pass 3: scatter.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_group_count(const int32_t* __restrict__ ids, int P, int E,
+                                                    int32_t* __restrict__ hist,
+                                                    int32_t* __restrict__ rank) {
+  const int chunk = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int i = chunk * 64 + lane;
+  const int e = i < P ? ids[i] : -1;
+  const bool valid = e >= 0 && e < E;
+  int r = 0;
+  for (int s = 0; s < 64; ++s) {
+    const int es = __shfl(e, s, 64);
+    if (s < lane && es == e) ++r;
+  }
+  int32_t* hrow = hist + (size_t)chunk * E;
+  for (int x = lane; x < E; x += 64) hrow[x] = 0;
+  __syncthreads();
+  // the last lane of each run of equal experts (highest rank) writes the count
+  bool last = valid;
+  for (int s = 0; s < 64; ++s) {
+    const int es = __shfl(e, s, 64);
+    if (s > lane && es == e) last = false;
+  }
+  if (valid && last) hrow[e] = r + 1;
+  if (i < P) rank[i] = valid ? r : -1;
+}
+
+__global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ hist, int n_chunks,
+                                                    int E, int32_t* __restrict__ base,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[1024];
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int32_t run = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      base[(size_t)c * E + e] = run;
+      run += hist[(size_t)c * E + e];
+    }
+    tot[e] = run;
+    counts[e] = run;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = acc;
+      acc += tot[e];
+    }
+    offsets[E] = acc;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict__ ids, int P, int E,
+                                                      const int32_t* __restrict__ base,
+                                                      const int32_t* __restrict__ rank,
+                                                      const int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm) {
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= P) return;
+  const int e = ids[i];
+  if (e < 0 || e >= E) return;
+  perm[offsets[e] + base[(size_t)blockIdx.x * E + e] + rank[i]] = i;
+}
+
+// ------------------------------------------------------------------------
+// Host launchers.
+// ------------------------------------------------------------------------
+static hipError_t last_launch() { return hipGetLastError(); }
+
+hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)a.n_pairs * (a.in_f / 128) * (a.out_f / 256));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_in_partial<2>, dim3(grid), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_in_partial<3>, dim3(grid), dim3(64), 0, s, a);
+  return last_launch();
+}
+
+hipError_t launch_down_partial(const DownPartialArgs& a, int k_bits, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)a.n_pairs * (a.in_f / 128) * (a.out_f / 256));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_down_partial<2>, dim3(grid), dim3(64), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_down_partial<3>, dim3(grid), dim3(64), 0, s, a);
+  return last_launch();
+}
+
+hipError_t launch_proj_finish(const FinishArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)a.n_pairs * (a.out_f / 128));
+  hipLaunchKernelGGL(k_proj_finish, dim3(grid), dim3(64), 0, s, a);
+  return last_launch();
+}
+
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine, dim3(a.n_tokens), dim3(1024), (size_t)a.hidden * sizeof(float), s,
+                     a);
+  return last_launch();
+}
+
+hipError_t launch_rmsnorm_bf16(const float* y, int n_tokens, int n, float eps, uint16_t* x,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(n_tokens), dim3(256), 0, s, y, n, eps, x);
+  return last_launch();
+}
+
+hipError_t launch_decode_tiles(const uint16_t* code_e, int in_f, int out_f, int k_bits,
+                               uint16_t* w, hipStream_t s) {
+  const unsigned grid = (unsigned)((in_f / 16) * (out_f / 256));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_decode_tiles<2>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+  else
+    hipLaunchKernelGGL(k_decode_tiles<3>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+  return last_launch();
+}
+
+hipError_t launch_hadamard128(const float* x, int64_t rows, int n, float* y, hipStream_t s) {
+  const size_t blocks = (size_t)rows * (n / 128);
+  const size_t max_grid = 0x7FFFFFFFu;
+  // split very tall inputs into several launches of whole rows
+  const int64_t rows_per = (int64_t)(max_grid / (n / 128));
+  for (int64_t r0 = 0; r0 < rows; r0 += rows_per) {
+    const int64_t nr = rows - r0 < rows_per ? rows - r0 : rows_per;
+    hipLaunchKernelGGL(k_hadamard128, dim3((unsigned)(nr * (n / 128))), dim3(64), 0, s,
+                       x + r0 * n, n, y + r0 * n);
+    const hipError_t err = last_launch();
+    if (err != hipSuccess) return err;
+  }
+  (void)blocks;
+  return hipSuccess;
+}
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_route_topk, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
+  return last_launch();
+}
+
+hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, int32_t* hist, int32_t* base, int32_t* rank,
+                        hipStream_t s) {
+  const int n_chunks = (P + 63) / 64;
+  if (n_chunks > 0) {
+    hipLaunchKernelGGL(k_group_count, dim3(n_chunks), dim3(64), 0, s, ids, P, E, hist, rank);
+    hipError_t err = last_launch();
+    if (err != hipSuccess) return err;
+  }
+  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(256), 0, s, hist, n_chunks, E, base, counts,
+                     offsets);
+  hipError_t err = last_launch();
+  if (err != hipSuccess || n_chunks == 0) return err;
+  hipLaunchKernelGGL(k_group_scatter, dim3(n_chunks), dim3(64), 0, s, ids, P, E, base, rank,
+                     offsets, perm);
+  return last_launch();
+}
+
+}  // namespace escha

@@ -1,0 +1,322 @@
+"""Python binding of libescha.so (the C ABI in include/escha.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their pointers and the current HIP stream are handed to the C
+entry point of the same name, and a non-zero status becomes ``EschaError``.
+Every step of the path runs in the library's HIP kernels; if the library is
+missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libescha.so"
+
+if not _LIB_PATH.exists():
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -m bit_trellis_quantized_amd.build` "
+        "(the trellis path has no fallback)")
+
+_lib = ctypes.CDLL(str(_LIB_PATH))
+
+ESCHA_OK = 0
+STATUS = {
+    -1: "ESCHA_E_NULL", -2: "ESCHA_E_SHAPE", -3: "ESCHA_E_KBITS", -4: "ESCHA_E_WORKSPACE",
+    -5: "ESCHA_E_HIP", -6: "ESCHA_E_UNSUPPORTED", -7: "ESCHA_E_ARG",
+}
+
+
+class EschaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class escha_proj_t(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_void_p), ("rin", ctypes.c_void_p), ("rout", ctypes.c_void_p),
+                ("n_experts", ctypes.c_int32), ("in_features", ctypes.c_int32),
+                ("out_features", ctypes.c_int32), ("k_bits", ctypes.c_int32)]
+
+
+class escha_moe_layer_t(ctypes.Structure):
+    _fields_ = [("gate_up", escha_proj_t), ("down", escha_proj_t), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
+_vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_P = ctypes.POINTER
+
+_SIGS = {
+    "escha_decode_tiles": ([_P(escha_proj_t), _i32, _vp, _vp], ctypes.c_int),
+    "escha_hadamard128": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
+    "escha_route_topk": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "escha_moe_group_workspace_bytes": ([_i32, _i32, _i32], _sz),
+    "escha_moe_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "escha_expert_gemv_workspace_bytes": ([_P(escha_proj_t), _i32], _sz),
+    "escha_expert_gemv": ([_P(escha_proj_t), _i32, _vp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "escha_moe_workspace_bytes": ([_P(escha_moe_layer_t), _i32, _i32], _sz),
+    "escha_moe_layer_decode": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                               ctypes.c_int),
+    "escha_moe_layer_prefill": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                                ctypes.c_int),
+    "escha_rmsnorm_bf16": ([_vp, _i32, _i32, _f32, _vp, _vp], ctypes.c_int),
+    "escha_moe_stack_workspace_bytes": ([_P(escha_moe_layer_t), _i32, _i32], _sz),
+    "escha_moe_stack_decode": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp,
+                                _vp, _sz, _vp], ctypes.c_int),
+    "escha_last_error": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+def _check(rc: int):
+    if rc != ESCHA_OK:
+        raise EschaError(rc, _lib.escha_last_error().decode())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_U16 = (torch.int16, torch.uint16, torch.float16, torch.bfloat16)
+
+
+# ------------------------------------------------------------------ descriptors
+
+ESCHA_LEAVES = ("escha_code", "escha_rin", "escha_rout")
+# optional leaves a checkpoint may carry; they change nothing in the path
+# (s_in/s_out ship as ones, config/layer_meta are informational)
+ESCHA_OPTIONAL = ("escha_s_in", "escha_s_out", "escha_config")
+
+
+@dataclass
+class Proj:
+    """One coded projection for all experts of a layer (device tensors)."""
+    code: torch.Tensor  # int16 [E][in/16][out/16][16K]
+    rin: torch.Tensor   # fp16 bits [E][in]
+    rout: torch.Tensor  # fp16 bits [E][out]
+
+    def __post_init__(self):
+        if self.code.dim() == 3:
+            self.code = self.code.unsqueeze(0)
+        if self.rin.dim() == 1:
+            self.rin = self.rin.unsqueeze(0)
+        if self.rout.dim() == 1:
+            self.rout = self.rout.unsqueeze(0)
+        if self.code.dim() != 4 or self.code.shape[-1] % 16:
+            raise ValueError(f"code shape {tuple(self.code.shape)} is not [E][in/16][out/16][16K]")
+
+    @property
+    def k_bits(self) -> int:
+        # K comes from the code tensor's own last dimension
+        return self.code.shape[-1] // 16
+
+    @property
+    def in_features(self) -> int:
+        return self.code.shape[1] * 16
+
+    @property
+    def out_features(self) -> int:
+        return self.code.shape[2] * 16
+
+    @property
+    def n_experts(self) -> int:
+        return self.code.shape[0]
+
+    def c(self) -> escha_proj_t:
+        E = self.n_experts
+        if tuple(self.rin.shape) != (E, self.in_features) or tuple(self.rout.shape) != (E, self.out_features):
+            raise ValueError("rin/rout shapes do not match the code tensor")
+        return escha_proj_t(_ptr(self.code, _U16, "code").value, _ptr(self.rin, _U16, "rin").value,
+                            _ptr(self.rout, _U16, "rout").value, E, self.in_features,
+                            self.out_features, self.k_bits)
+
+    @classmethod
+    def from_leaves(cls, leaves: dict, prefix: str = ""):
+        """Build from checkpoint-style leaves ``{prefix}escha_code`` etc.
+
+        The three required leaves must all be present; an unknown ``escha_*``
+        leaf (a rotation variant this path does not implement) is an error.
+        """
+        names = {k[len(prefix):]: v for k, v in leaves.items() if k.startswith(prefix)}
+        missing = [n for n in ESCHA_LEAVES if n not in names]
+        if missing:
+            raise ValueError(f"missing required leaves: {missing}")
+        unknown = [n for n in names if n.startswith("escha_") and n not in ESCHA_LEAVES + ESCHA_OPTIONAL]
+        if unknown:
+            raise ValueError(f"unknown escha leaves (unsupported variant): {unknown}")
+        return cls(names["escha_code"], names["escha_rin"], names["escha_rout"])
+
+
+@dataclass
+class MoeLayer:
+    gate_up: Proj
+    down: Proj
+    top_k: int = 8
+
+    @property
+    def hidden(self) -> int:
+        return self.gate_up.in_features
+
+    @property
+    def inter(self) -> int:
+        return self.down.in_features
+
+    def c(self) -> escha_moe_layer_t:
+        return escha_moe_layer_t(self.gate_up.c(), self.down.c(), self.hidden, self.inter, self.top_k)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ entry points
+
+def escha_decode_tiles(w: Proj, expert: int, out: torch.Tensor | None = None, stream=None):
+    if out is None:
+        out = torch.empty(w.out_features, w.in_features, dtype=torch.int16, device=w.code.device)
+    wc = w.c()
+    _check(_lib.escha_decode_tiles(ctypes.byref(wc), expert, _ptr(out, _U16, "out"), _stream(stream)))
+    return out
+
+
+def escha_hadamard128(x: torch.Tensor, out: torch.Tensor | None = None, stream=None):
+    n = x.shape[-1]
+    rows = x.numel() // n if n else 0
+    if out is None:
+        out = torch.empty_like(x)
+    _check(_lib.escha_hadamard128(_ptr(x, torch.float32, "x"), rows, n, _ptr(out, torch.float32, "y"),
+                                  _stream(stream)))
+    return out
+
+
+def escha_route_topk(logits: torch.Tensor, top_k: int, stream=None):
+    T, E = logits.shape
+    ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    _check(_lib.escha_route_topk(_ptr(logits, torch.float32, "logits"), T, E, top_k,
+                                 _ptr(ids), _ptr(w), _stream(stream)))
+    return ids, w
+
+
+def escha_moe_group(topk_ids: torch.Tensor, n_experts: int, stream=None):
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(n_experts, dtype=torch.int32, device=dev)
+    offsets = torch.empty(n_experts + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    nbytes = _lib.escha_moe_group_workspace_bytes(T, k, n_experts)
+    ws = _ws(nbytes, dev)
+    _check(_lib.escha_moe_group(_ptr(topk_ids, torch.int32, "topk_ids"), T, k, n_experts,
+                                _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws), nbytes,
+                                _stream(stream)))
+    return counts, offsets, perm[:T * k]
+
+
+def escha_expert_gemv(w: Proj, expert: int, x_bf16: torch.Tensor, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    x2 = x_bf16.reshape(-1, w.in_features)
+    T = x2.shape[0]
+    if out is None:
+        out = torch.empty(T, w.out_features, dtype=torch.float32, device=x_bf16.device)
+    wc = w.c()
+    nbytes = _lib.escha_expert_gemv_workspace_bytes(ctypes.byref(wc), T)
+    if workspace is None:
+        workspace = _ws(nbytes, x_bf16.device)
+    _check(_lib.escha_expert_gemv(ctypes.byref(wc), expert, _ptr(x2, _U16, "x"), T,
+                                  _ptr(out, torch.float32, "y"), _ptr(workspace),
+                                  workspace.numel(), _stream(stream)))
+    return out
+
+
+def escha_moe_workspace_bytes(layer: MoeLayer, n_tokens: int, prefill: bool = False) -> int:
+    lc = layer.c()
+    return int(_lib.escha_moe_workspace_bytes(ctypes.byref(lc), n_tokens, int(prefill)))
+
+
+def _moe_call(fn, layer, x_bf16, topk_ids, topk_w, out, inter_out, workspace, stream, prefill):
+    T = x_bf16.shape[0]
+    lc = layer.c()
+    if out is None:
+        out = torch.empty(T, layer.hidden, dtype=torch.float32, device=x_bf16.device)
+    nbytes = _lib.escha_moe_workspace_bytes(ctypes.byref(lc), T, int(prefill))
+    if workspace is None:
+        workspace = _ws(nbytes, x_bf16.device)
+    _check(fn(ctypes.byref(lc), _ptr(x_bf16, _U16, "x"), T, _ptr(topk_ids, torch.int32, "topk_ids"),
+              _ptr(topk_w, torch.float32, "topk_w"), _ptr(out, torch.float32, "y"),
+              _ptr(inter_out, torch.float32, "inter_out"), _ptr(workspace), workspace.numel(),
+              _stream(stream)))
+    return out
+
+
+def escha_moe_layer_decode(layer: MoeLayer, x_bf16, topk_ids, topk_w, out=None, inter_out=None,
+                           workspace=None, stream=None):
+    return _moe_call(_lib.escha_moe_layer_decode, layer, x_bf16, topk_ids, topk_w, out, inter_out,
+                     workspace, stream, False)
+
+
+def escha_moe_layer_prefill(layer: MoeLayer, x_bf16, topk_ids, topk_w, out=None, inter_out=None,
+                            workspace=None, stream=None):
+    return _moe_call(_lib.escha_moe_layer_prefill, layer, x_bf16, topk_ids, topk_w, out, inter_out,
+                     workspace, stream, True)
+
+
+def escha_rmsnorm_bf16(y: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | None = None, stream=None):
+    T, n = y.shape
+    if out is None:
+        out = torch.empty(T, n, dtype=torch.int16, device=y.device)
+    _check(_lib.escha_rmsnorm_bf16(_ptr(y, torch.float32, "y"), T, n, eps, _ptr(out, _U16, "x"),
+                                   _stream(stream)))
+    return out
+
+
+class Stack:
+    """A host array of layer descriptors for escha_moe_stack_decode."""
+
+    def __init__(self, layers):
+        self.layers = list(layers)
+        self.arr = (escha_moe_layer_t * len(self.layers))(*[l.c() for l in self.layers])
+
+    def workspace_bytes(self, n_tokens: int) -> int:
+        return int(_lib.escha_moe_stack_workspace_bytes(self.arr, len(self.layers), n_tokens))
+
+
+def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6, out=None,
+                           x_chain=None, workspace=None, stream=None):
+    T = x0_bf16.shape[0]
+    hidden = stack.layers[0].hidden
+    if out is None:
+        out = torch.empty(T, hidden, dtype=torch.float32, device=x0_bf16.device)
+    nbytes = stack.workspace_bytes(T)
+    if workspace is None:
+        workspace = _ws(nbytes, x0_bf16.device)
+    _check(_lib.escha_moe_stack_decode(stack.arr, len(stack.layers), _ptr(x0_bf16, _U16, "x0"), T,
+                                       _ptr(topk_ids, torch.int32, "topk_ids"),
+                                       _ptr(topk_w, torch.float32, "topk_w"), eps,
+                                       _ptr(out, torch.float32, "y"), _ptr(x_chain, _U16, "x_chain"),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out

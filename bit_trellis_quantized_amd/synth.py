@@ -46,7 +46,7 @@ def code_words(seed: int, layer: int, expert: int, proj: int, in_f: int, out_f: 
     """uint16 [in/16][out/16][16K], uniform random words."""
     n_words = (in_f // 16) * (out_f // 16) * 16 * K
     raw = rng(seed, layer, expert, proj + _T_CODE).bytes(2 * n_words)
-    return np.frombuffer(raw, dtype=np.uint16).reshape(in_f // 16, out_f // 16, 16 * K).copy()
+    return np.frombuffer(raw, dtype=np.uint16).reshape(in_f // 16, out_f // 16, 16 * K)
 
 
 def sign_vector(seed: int, layer: int, expert: int, proj: int, n: int) -> np.ndarray:
@@ -144,13 +144,18 @@ def layer_tensors(seed: int, layer: int, n_experts: int = N_EXPERTS, experts=Non
     """Stacked leaves of a layer, [E][...] each. ``experts`` limits which
     experts carry generated data (the others are left zero), which the
     oracle uses to rebuild only what a routing touches."""
-    first = expert_tensors(seed, layer, 0, **kw)
-    out = {k: np.zeros((n_experts,) + v.shape, dtype=v.dtype) for k, v in first.items()}
-    todo = range(n_experts) if experts is None else sorted(set(int(e) for e in experts))
+    todo = list(range(n_experts)) if experts is None else sorted(set(int(e) for e in experts))
+    out = None
     for e in todo:
-        t = first if e == 0 else expert_tensors(seed, layer, e, **kw)
+        t = expert_tensors(seed, layer, e, **kw)
+        if out is None:
+            alloc = np.empty if experts is None else np.zeros
+            out = {k: alloc((n_experts,) + v.shape, dtype=v.dtype) for k, v in t.items()}
         for k, v in t.items():
             out[k][e] = v
+    if out is None:  # no expert requested: shapes from expert 0, all zero
+        t = expert_tensors(seed, layer, 0, **kw)
+        out = {k: np.zeros((n_experts,) + v.shape, dtype=v.dtype) for k, v in t.items()}
     return out
 
 

@@ -1,0 +1,205 @@
+/*
+ * escha.h -- C ABI of libescha.so: the trellis-coded ("eschamoe",
+ * EXL3-style) routed-expert path of a Qwen3.6-35B-A3B-class MoE layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The experts stay in their packed form and are decoded inside the kernels;
+ * no entry point except escha_decode_tiles ever writes decoded weights to
+ * memory.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller, contiguous,
+ *    row-major, and at least 16-byte aligned. bf16 and fp16 values are passed
+ *    as their uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void*. All work is enqueued on it,
+ *    asynchronously; nothing runs on the null stream unless the caller passes
+ *    it. The caller keeps every buffer alive until the stream has finished.
+ *  - The library allocates nothing and keeps no reference after a call
+ *    returns. Scratch memory is the caller's `workspace`; its required size
+ *    comes from the matching *_workspace_bytes function, and a larger
+ *    workspace is accepted.
+ *  - Every argument is validated on the host before anything is launched.
+ *    The return value is ESCHA_OK (0) or a negative ESCHA_E_* code;
+ *    escha_last_error() then holds a readable message for the calling
+ *    thread. A validation failure launches nothing.
+ *  - Expert ids read from device memory (topk_ids) are not visible to the
+ *    host: the kernels skip an out-of-range id (its pair contributes zero)
+ *    instead of reading outside the expert arrays.
+ *
+ * Sources (page title, section):
+ *  [trellis-mlx] model card "Qwen3.6-35B-A3B-Escha-W2-trellis-mlx",
+ *                exactness table and Hadamard note;
+ *  [escha-card]  model card "Qwen3.6-35B-A3B-Escha-W2", Format notes;
+ *  [hipfire]     PR "Escha-W2 port: 2-bit trellis decoded in the GEMV",
+ *                commit notes and the closing summary "What it is".
+ */
+#ifndef ESCHA_H_
+#define ESCHA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define ESCHA_API __attribute__((visibility("default")))
+#else
+#define ESCHA_API
+#endif
+
+enum escha_status {
+  ESCHA_OK = 0,
+  ESCHA_E_NULL = -1,        /* a required pointer is NULL */
+  ESCHA_E_SHAPE = -2,       /* sizes inconsistent or not tile/block aligned */
+  ESCHA_E_KBITS = -3,       /* k_bits is not 2 or 3 */
+  ESCHA_E_WORKSPACE = -4,   /* workspace smaller than required */
+  ESCHA_E_HIP = -5,         /* a HIP launch or runtime call failed */
+  ESCHA_E_UNSUPPORTED = -6, /* valid request this build does not serve */
+  ESCHA_E_ARG = -7,         /* scalar argument out of range */
+};
+
+/*
+ * One coded projection, for every expert of a layer ([hipfire] "What it is";
+ * [escha-card] Format notes):
+ *   code  int16 [n_experts][in_features/16][out_features/16][16*k_bits]
+ *         verbatim trellis words, input-tile index outermost. Each 16x16
+ *         tile is a stream of 256*k_bits bits; weight i of the tile is the
+ *         fp16 value of the 16-bit window starting at bit k_bits*i (windows
+ *         wrap at the tile end), decoded by the hash of [trellis-mlx].
+ *   rin   fp16  [n_experts][in_features]   input sign/scale vector
+ *   rout  fp16  [n_experts][out_features]  output scale vector; a zero
+ *         entry is a pruned channel and its output is exactly zero.
+ *   k_bits must equal the code tensor's last dimension / 16 (2 or 3).
+ * Alignment: in_features % 128 == 0 and out_features % 256 == 0.
+ */
+typedef struct escha_proj {
+  const void* code;
+  const void* rin;
+  const void* rout;
+  int32_t n_experts;
+  int32_t in_features;
+  int32_t out_features;
+  int32_t k_bits;
+} escha_proj_t;
+
+/*
+ * One MoE layer's routed experts: gate_up (hidden -> 2*inter; rows
+ * [0, inter) are the gate, [inter, 2*inter) the up projection) and down
+ * (inter -> hidden). [hipfire] commit notes: gate is the first half.
+ */
+typedef struct escha_moe_layer {
+  escha_proj_t gate_up;
+  escha_proj_t down;
+  int32_t hidden;
+  int32_t inter;
+  int32_t top_k;
+} escha_moe_layer_t;
+
+/*
+ * Decode every weight of one expert to fp16, bit-exact: the one entry point
+ * that writes decoded weights, for checking the codec.
+ * [trellis-mlx] exactness table (hash, two fp16 halves summed with
+ * round-to-nearest-even); [hipfire] "What it is" (tiles and windows).
+ *   w_f16  out: fp16 bits [out_features][in_features] of expert `expert`.
+ */
+ESCHA_API int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t* w_f16, void* stream);
+
+/*
+ * y = H_n x on each consecutive block of 128 values of every row, with H the
+ * Sylvester-ordered 128-point Hadamard matrix and H_n = H / sqrt(128)
+ * ([trellis-mlx] Hadamard note). x, y fp32 [rows][n]; n % 128 == 0; x and y
+ * may alias.
+ */
+ESCHA_API int escha_hadamard128(const float* x, int64_t rows, int32_t n, float* y, void* stream);
+
+/*
+ * Router step: softmax over each row of fp32 logits [n_tokens][n_experts],
+ * then the top_k experts by logit (ties to the lower expert index).
+ * topk_ids int32 [n_tokens][top_k] in decreasing-logit order; topk_w fp32
+ * [n_tokens][top_k] the selected softmax probabilities, not renormalised.
+ * 1 <= top_k <= 32, top_k <= n_experts <= 1024.
+ */
+ESCHA_API int escha_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, int32_t top_k,
+                     int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * Group the n_tokens*top_k (token, slot) pairs by expert ([hipfire] grouped
+ * GEMM notes: expert_offsets and a permutation). counts int32 [n_experts];
+ * offsets int32 [n_experts+1] exclusive prefix sums; perm int32
+ * [n_tokens*top_k] pair indices t*top_k+j sorted by expert, stable in the
+ * pair index. Ids out of range are not counted and are left out of perm;
+ * perm's tail past offsets[n_experts] is then unspecified.
+ * workspace >= escha_moe_group_workspace_bytes(n_tokens, top_k, n_experts).
+ */
+ESCHA_API size_t escha_moe_group_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts);
+ESCHA_API int escha_moe_group(const int32_t* topk_ids, int32_t n_tokens, int32_t top_k, int32_t n_experts,
+                    int32_t* counts, int32_t* offsets, int32_t* perm, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
+ * One coded projection of one expert on n_tokens activations:
+ *   y[t] = rout (.) H_n( W~ H_n( rin (.) x[t] ) )
+ * with W~ the decoded [out][in] weights ([hipfire] "What it is": Hadamard on
+ * both sides; rin applied before the input rotation, rout as the final
+ * multiply). x bf16 [n_tokens][in_features]; y fp32 [n_tokens][out_features].
+ */
+ESCHA_API size_t escha_expert_gemv_workspace_bytes(const escha_proj_t* w, int32_t n_tokens);
+ESCHA_API int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_bf16,
+                      int32_t n_tokens, float* y, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * One MoE layer: for every token t and slot j with e = topk_ids[t][j],
+ *   g,u = split(gate_up_e(x[t]));  h = SiLU(g) * u;
+ *   y[t] = sum_j topk_w[t][j] * down_e(h)       (summed in slot order).
+ * x bf16 [n_tokens][hidden]; topk_ids int32 / topk_w fp32 [n_tokens][top_k];
+ * y fp32 [n_tokens][hidden]; inter_out (nullable) fp32
+ * [n_tokens*top_k][inter] receives h per pair, in pair order t*top_k+j.
+ * _decode streams every pair's expert weights (small batches);
+ * _prefill groups the pairs by expert and decodes each weight tile once per
+ * expert for all its tokens (long prompts). Both compute the same function.
+ */
+ESCHA_API size_t escha_moe_workspace_bytes(const escha_moe_layer_t* L, int32_t n_tokens, int32_t prefill);
+ESCHA_API int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
+                           const int32_t* topk_ids, const float* topk_w, float* y,
+                           float* inter_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+ESCHA_API int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
+                            const int32_t* topk_ids, const float* topk_w, float* y,
+                            float* inter_out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
+ * Between stacked layers: x = bf16( y / sqrt(mean(y^2) + eps) ) per row,
+ * unit weight, no residual. y fp32 [n_tokens][n]; x_bf16 [n_tokens][n].
+ */
+ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, float eps, uint16_t* x_bf16,
+                       void* stream);
+
+/*
+ * A stack of n_layers MoE layers applied in turn to n_tokens tokens:
+ *   x_0 = x0_bf16; y_l = layer_l(x_l); x_{l+1} = rmsnorm_bf16(y_l).
+ * `layers` is a HOST array of n_layers descriptors (their tensors are on
+ * the device). topk_ids int32 / topk_w fp32 [n_layers][n_tokens][top_k];
+ * y_last fp32 [n_tokens][hidden] = y_{n_layers-1}; x_chain (nullable) bf16
+ * [n_layers][n_tokens][hidden] receives each layer's input x_l.
+ * All layers must share hidden, inter and top_k.
+ */
+ESCHA_API size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t n_layers,
+                                       int32_t n_tokens);
+ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
+                           const uint16_t* x0_bf16, int32_t n_tokens, const int32_t* topk_ids,
+                           const float* topk_w, float eps, float* y_last, uint16_t* x_chain,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+ESCHA_API const char* escha_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ESCHA_H_ */

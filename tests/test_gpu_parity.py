@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator; routings fed to the layer tests are
+the oracle's (the GPU router is tested on its own). Decoded weights and every
+integer result must match exactly; fp32 outputs must meet the relative-L2 and
+max-abs bounds in ``_gpu_util``.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_trellis_quantized_amd import synth
+from tests._gpu_util import announce, assert_close, errors, layer_to_dev, to_dev, u16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def escha():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from bit_trellis_quantized_amd import escha as mod
+    return mod
+
+
+@pytest.fixture(scope="module")
+def layer2():
+    """Config 2's layer: 256 experts, gate_up K=2, down K=3, prune masks."""
+    return synth.layer_tensors(2, 0)
+
+
+@pytest.fixture(scope="module")
+def layer2_dev(escha, layer2):
+    return layer_to_dev(layer2)
+
+
+# ------------------------------------------------------------------ decode
+
+def test_decode_tiles_config1_bit_exact(escha):
+    announce("decode_tiles config1 256x256 K=2")
+    code, rin, rout = synth.single_proj(1, 256, 256, 2)
+    w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
+    got = u16(escha.escha_decode_tiles(w, 0))
+    ref = oracle.reconstruct(code, 256, 256, 2)
+    assert np.count_nonzero(got != ref) == 0
+
+
+@pytest.mark.parametrize("expert", [0, 1, 137, 255])
+def test_decode_tiles_layer_experts_bit_exact(escha, layer2, layer2_dev, expert):
+    announce(f"decode_tiles layer2 expert {expert}")
+    got_gu = u16(escha.escha_decode_tiles(layer2_dev.gate_up, expert))
+    got_dn = u16(escha.escha_decode_tiles(layer2_dev.down, expert))
+    ref_gu = oracle.reconstruct(layer2["gu_code"][expert], 2048, 1024, 2)
+    ref_dn = oracle.reconstruct(layer2["dn_code"][expert], 512, 2048, 3)
+    assert np.count_nonzero(got_gu != ref_gu) == 0
+    assert np.count_nonzero(got_dn != ref_dn) == 0
+
+
+@pytest.mark.parametrize("K", [2, 3])
+def test_decode_tiles_special_words(escha, K):
+    """All-zero, all-one and alternating words (wrap windows included)."""
+    announce(f"decode_tiles special words K={K}")
+    in_f, out_f = 128, 256
+    shape = (in_f // 16, out_f // 16, 16 * K)
+    for fill in (0x0000, 0xFFFF, 0xAAAA, 0x8001):
+        code = np.full(shape, fill, dtype=np.uint16)
+        _, rin, rout = synth.single_proj(3, in_f, out_f, K)
+        w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
+        got = u16(escha.escha_decode_tiles(w, 0))
+        assert np.array_equal(got, oracle.reconstruct(code, in_f, out_f, K)), hex(fill)
+
+
+# ------------------------------------------------------------------ Hadamard
+
+def test_hadamard128(escha):
+    announce("hadamard128")
+    eye = torch.eye(256, dtype=torch.float32, device="cuda")
+    Hn = escha.escha_hadamard128(eye).cpu().numpy().astype(np.float64)
+    assert np.allclose(Hn @ Hn.T, np.eye(256), atol=1e-6)
+    x = np.random.default_rng(0).standard_normal((37, 384)).astype(np.float32)
+    got = escha.escha_hadamard128(to_dev(x)).cpu().numpy()
+    ref = oracle.hadamard128(x.astype(np.float64))
+    assert np.max(np.abs(got - ref)) <= 1e-5 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ routing
+
+@pytest.mark.parametrize("cfg,T", [(2, 1), (3, 64), (5, 4096), (3, 7)])
+def test_route_topk_vs_oracle(escha, cfg, T):
+    announce(f"route_topk cfg{cfg} T={T}")
+    logits = synth.zipf_logits(cfg, T) if cfg == 3 else synth.normal_logits(cfg, T)
+    ids, w = escha.escha_route_topk(to_dev(logits), 8)
+    ref_ids, ref_w = oracle.route_topk(logits, 8)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=0)
+
+
+def test_route_topk_ties(escha):
+    announce("route_topk ties")
+    logits = np.zeros((2, 256), dtype=np.float32)
+    logits[0, [200, 17, 90, 3, 250, 11, 40, 8, 9]] = 1.0
+    logits[1, :] = 0.5  # all tied
+    ids, _ = escha.escha_route_topk(to_dev(logits), 8)
+    ref_ids, _ = oracle.route_topk(logits, 8)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
+@pytest.mark.parametrize("cfg,T", [(2, 1), (3, 64), (5, 4096), (3, 3)])
+def test_group_vs_oracle(escha, cfg, T):
+    announce(f"moe_group cfg{cfg} T={T}")
+    logits = synth.zipf_logits(cfg, T) if cfg == 3 else synth.normal_logits(cfg, T)
+    ids, _ = oracle.route_topk(logits, 8)
+    counts, offsets, perm = escha.escha_moe_group(to_dev(ids), 256)
+    rc, ro, rp = oracle.group(ids, 256)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(perm.cpu().numpy(), rp)
+
+
+# ------------------------------------------------------------------ projections
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_expert_gemv_config1(escha, T):
+    announce(f"expert_gemv config1 T={T}")
+    code, rin, rout = synth.single_proj(1, 256, 256, 2)
+    x = synth.activations(1, T, 256)
+    w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
+    y = escha.escha_expert_gemv(w, 0, to_dev(x)).cpu().numpy()
+    ref = oracle.expert_gemv(code, rin, rout, 256, 256, 2, x)
+    assert_close(y, ref, f"expert_gemv T={T}")
+
+
+def test_expert_gemv_layer_shapes(escha, layer2, layer2_dev):
+    """gate_up (K=2) and down (K=3) of one expert through the single-projection call."""
+    e = 77
+    x_gu = synth.activations(11, 2, 2048)
+    y = escha.escha_expert_gemv(layer2_dev.gate_up, e, to_dev(x_gu)).cpu().numpy()
+    ref = oracle.expert_gemv(layer2["gu_code"][e], layer2["gu_rin"][e], layer2["gu_rout"][e],
+                             2048, 1024, 2, x_gu)
+    assert_close(y, ref, "expert_gemv gate_up")
+    assert np.all(y[:, np.concatenate([layer2["mask"][e]] * 2)] == 0.0)
+    x_dn = synth.activations(12, 2, 512)
+    y = escha.escha_expert_gemv(layer2_dev.down, e, to_dev(x_dn)).cpu().numpy()
+    ref = oracle.expert_gemv(layer2["dn_code"][e], layer2["dn_rin"][e], layer2["dn_rout"][e],
+                             512, 2048, 3, x_dn)
+    assert_close(y, ref, "expert_gemv down")
+
+
+# ------------------------------------------------------------------ MoE layer
+
+def _check_layer(escha, L, Ldev, x, ids, w, entry, what):
+    inter = torch.empty(ids.size, 512, dtype=torch.float32, device="cuda")
+    y = entry(Ldev, to_dev(x), to_dev(ids), to_dev(w.astype(np.float32)), inter_out=inter)
+    y = y.cpu().numpy()
+    inter = inter.cpu().numpy()
+    ref_y, ref_inter = oracle.moe_layer(L, x, ids, w.astype(np.float32), want_inter=True)
+    assert_close(y, ref_y, f"{what} y")
+    assert_close(inter, ref_inter, f"{what} h")
+    for p, e in enumerate(ids.ravel()):
+        assert np.all(inter[p][L["mask"][e]] == 0.0), f"pair {p}: pruned channel not zero"
+    return y
+
+
+def test_layer_decode_config2(escha, layer2, layer2_dev):
+    announce("moe_layer_decode config2 T=1")
+    x = synth.activations(2, 1, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(2, 1), 8)
+    y1 = _check_layer(escha, layer2, layer2_dev, x, ids, w, escha.escha_moe_layer_decode, "cfg2")
+    y2 = escha.escha_moe_layer_decode(layer2_dev, to_dev(x), to_dev(ids),
+                                      to_dev(w.astype(np.float32))).cpu().numpy()
+    assert np.array_equal(y1, y2), "decode is not bit-reproducible"
+
+
+def test_layer_decode_config3_zipf(escha):
+    announce("moe_layer_decode config3 T=64 zipf")
+    L = synth.layer_tensors(3, 0)
+    Ldev = layer_to_dev(L)
+    x = synth.activations(3, 64, 2048)
+    ids, w = oracle.route_topk(synth.zipf_logits(3, 64), 8)
+    _check_layer(escha, L, Ldev, x, ids, w, escha.escha_moe_layer_decode, "cfg3")
+
+
+def test_layer_ragged_and_bad_ids(escha, layer2, layer2_dev):
+    """T=5 (ragged), and out-of-range ids contribute exactly nothing."""
+    announce("moe_layer_decode ragged T=5 with bad ids")
+    x = synth.activations(21, 5, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(21, 5), 8)
+    bad = ids.copy()
+    bad[1, 3] = -1
+    bad[4, 0] = 256
+    y = escha.escha_moe_layer_decode(layer2_dev, to_dev(x), to_dev(bad),
+                                     to_dev(w.astype(np.float32))).cpu().numpy()
+    w0 = w.astype(np.float32).copy()
+    w0[1, 3] = 0.0
+    w0[4, 0] = 0.0
+    ref = oracle.moe_layer(layer2, x, ids, w0)
+    assert_close(y, ref, "bad ids")
+
+
+def test_layer_prefill_matches_oracle_on_subset(escha):
+    """Config 5: 4096 tokens; oracle on tokens 0..255; pruned h == 0 for all pairs."""
+    announce("moe_layer_prefill config5 T=4096")
+    L = synth.layer_tensors(5, 0)
+    Ldev = layer_to_dev(L)
+    T, n_check = 4096, 256
+    x = synth.activations(5, T, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(5, T), 8)
+    inter = torch.empty(T * 8, 512, dtype=torch.float32, device="cuda")
+    y = escha.escha_moe_layer_prefill(Ldev, to_dev(x), to_dev(ids), to_dev(w.astype(np.float32)),
+                                      inter_out=inter).cpu().numpy()
+    inter = inter.cpu().numpy()
+    ref_y, ref_inter = oracle.moe_layer(L, x[:n_check], ids[:n_check], w[:n_check].astype(np.float32),
+                                        want_inter=True)
+    assert_close(y[:n_check], ref_y, "prefill y[0:256]")
+    assert_close(inter[:n_check * 8], ref_inter, "prefill h[0:256]")
+    masks = L["mask"][ids.ravel()]
+    assert np.all(inter[masks] == 0.0)
+    assert np.all(np.isfinite(y))
+
+
+def test_prefill_equals_decode_path(escha, layer2, layer2_dev):
+    """Both entry points compute the same function (T=100, ragged)."""
+    announce("prefill vs decode T=100")
+    x = synth.activations(31, 100, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(31, 100), 8)
+    a = escha.escha_moe_layer_decode(layer2_dev, to_dev(x), to_dev(ids), to_dev(w.astype(np.float32)))
+    b = escha.escha_moe_layer_prefill(layer2_dev, to_dev(x), to_dev(ids), to_dev(w.astype(np.float32)))
+    rel, mx = errors(b.cpu().numpy(), a.cpu().numpy())
+    assert rel <= 1e-3 and mx <= 2e-3
+
+
+def test_zero_tokens_is_a_no_op(escha, layer2_dev):
+    x = torch.empty(0, 2048, dtype=torch.int16, device="cuda")
+    ids = torch.empty(0, 8, dtype=torch.int32, device="cuda")
+    w = torch.empty(0, 8, dtype=torch.float32, device="cuda")
+    y = escha.escha_moe_layer_decode(layer2_dev, x, ids, w)
+    assert y.shape == (0, 2048)
+
+
+def test_rmsnorm_bf16(escha):
+    announce("rmsnorm_bf16")
+    y = np.random.default_rng(4).standard_normal((8, 2048)) * 3
+    got = u16(escha.escha_rmsnorm_bf16(to_dev(y.astype(np.float32))))
+    ref = oracle.rmsnorm_bf16(y.astype(np.float32).astype(np.float64))
+    # the same decision in different precision may differ by one bf16 step
+    diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
+    assert diff.max() <= 1 and np.mean(diff) < 1e-2
