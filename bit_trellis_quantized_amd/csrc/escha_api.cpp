@@ -31,7 +31,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int32_t kMaxTopK = 64;
-constexpr int32_t kMaxHidden = 16384;  // k_combine keeps one fp32 row in LDS
+constexpr int32_t kMaxHidden = 16384;  // k_rmsnorm_bf16 keeps one sum per 128-block in LDS
 constexpr int32_t kMaxExpertsRoute = 1024;
 
 int check_proj(const escha_proj_t* w, const char* what) {
@@ -77,29 +77,44 @@ int check_layer(const escha_moe_layer_t* L) {
 struct DecodeWs {
   float* gu_part;  // [P][hidden/128][2*inter]
   float* dn_part;  // [P][inter/128][hidden]
+  float* ss;       // [T][hidden/128] per-block sums of squares of y
 };
 
 size_t decode_ws_bytes(const escha_moe_layer_t* L, int64_t T) {
   const int64_t P = T * L->top_k;
   const size_t gu = (size_t)P * (L->hidden / 128) * (2 * L->inter) * sizeof(float);
   const size_t dn = (size_t)P * (L->inter / 128) * L->hidden * sizeof(float);
-  return round_up(gu) + round_up(dn);
+  const size_t ss = (size_t)T * (L->hidden / 128) * sizeof(float);
+  return round_up(gu) + round_up(dn) + round_up(ss);
 }
 
 DecodeWs decode_ws_carve(const escha_moe_layer_t* L, int64_t T, void* ws) {
   const int64_t P = T * L->top_k;
   const size_t gu = (size_t)P * (L->hidden / 128) * (2 * L->inter) * sizeof(float);
+  const size_t dn = (size_t)P * (L->inter / 128) * L->hidden * sizeof(float);
   char* b = (char*)ws;
   DecodeWs d;
   d.gu_part = (float*)b;
   d.dn_part = (float*)(b + round_up(gu));
+  d.ss = (float*)(b + round_up(gu) + round_up(dn));
   return d;
 }
 
+// Where a layer's input row comes from: bf16 rows, or the previous layer's
+// fp32 output with its block sums of squares (RMSNorm applied on the fly).
+struct LayerInput {
+  const uint16_t* x_bf16;
+  const float* y_prev;
+  const float* ss_prev;
+  float eps;
+  uint16_t* x_out;  // nullable: the bf16 rows the layer consumed
+};
+
 // One layer over T tokens through the streaming kernels.
-int run_layer_decode(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
-                     const float* w, float* y, float* inter_out, uint16_t* x_next, float eps,
-                     const DecodeWs& ws, hipStream_t s) {
+int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, const int32_t* ids,
+                     const float* w, float* y, float* inter_out, const DecodeWs& ws,
+                     hipStream_t s, hipEvent_t probe_before = nullptr,
+                     hipEvent_t probe_after = nullptr) {
   const int P = T * L->top_k;
   escha::InPartialArgs a{};
   a.code = (const uint16_t*)L->gate_up.code;
@@ -111,10 +126,19 @@ int run_layer_decode(const escha_moe_layer_t* L, const uint16_t* x, int T, const
   a.top_k = L->top_k;
   a.ids = ids;
   a.fixed_expert = 0;
-  a.x_bf16 = x;
+  a.x_bf16 = in.x_bf16;
+  a.y_prev = in.y_prev;
+  a.ss_prev = in.ss_prev;
+  a.eps = in.eps;
+  a.x_out = in.x_out;
   a.partial = ws.gu_part;
-  hipError_t e = escha::launch_in_partial(a, L->gate_up.k_bits, s);
+  hipError_t e;
+  if (probe_before && (e = hipEventRecord(probe_before, s)) != hipSuccess)
+    return hip_fail(e, "probe event record");
+  e = escha::launch_in_partial(a, L->gate_up.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "gate_up partial launch");
+  if (probe_after && (e = hipEventRecord(probe_after, s)) != hipSuccess)
+    return hip_fail(e, "probe event record");
 
   escha::DownPartialArgs d{};
   d.code = (const uint16_t*)L->down.code;
@@ -143,8 +167,7 @@ int run_layer_decode(const escha_moe_layer_t* L, const uint16_t* x, int T, const
   c.top_k = L->top_k;
   c.n_tokens = T;
   c.y = y;
-  c.x_next = x_next;
-  c.eps = eps;
+  c.ss = ws.ss;
   e = escha::launch_combine(c, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   return ESCHA_OK;
@@ -296,7 +319,8 @@ int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, i
   if (!workspace || workspace_bytes < need)
     return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   const DecodeWs ws = decode_ws_carve(L, n_tokens, workspace);
-  return run_layer_decode(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, nullptr, 0.f, ws,
+  const LayerInput in{x_bf16, nullptr, nullptr, 0.f, nullptr};
+  return run_layer_decode(L, in, n_tokens, topk_ids, topk_w, y, inter_out, ws,
                           (hipStream_t)stream);
 }
 
@@ -314,10 +338,11 @@ int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, 
   for (int32_t t0 = 0; t0 < n_tokens; t0 += kPrefillBatch) {
     const int32_t nt = n_tokens - t0 < kPrefillBatch ? n_tokens - t0 : kPrefillBatch;
     const DecodeWs ws = decode_ws_carve(L, nt, workspace);
-    rc = run_layer_decode(L, x_bf16 + (size_t)t0 * L->hidden, nt, topk_ids + (size_t)t0 * k,
-                          topk_w + (size_t)t0 * k, y + (size_t)t0 * L->hidden,
-                          inter_out ? inter_out + (size_t)t0 * k * L->inter : nullptr, nullptr,
-                          0.f, ws, (hipStream_t)stream);
+    const LayerInput in{x_bf16 + (size_t)t0 * L->hidden, nullptr, nullptr, 0.f, nullptr};
+    rc = run_layer_decode(L, in, nt, topk_ids + (size_t)t0 * k, topk_w + (size_t)t0 * k,
+                          y + (size_t)t0 * L->hidden,
+                          inter_out ? inter_out + (size_t)t0 * k * L->inter : nullptr, ws,
+                          (hipStream_t)stream);
     if (rc) return rc;
   }
   return ESCHA_OK;
@@ -325,7 +350,9 @@ int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, 
 
 int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, float eps, uint16_t* x_bf16,
                        void* stream) {
-  if (n_tokens < 0 || n < 1) return fail(ESCHA_E_ARG, "n_tokens=%d n=%d", n_tokens, n);
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n < 128 || n % 128 || n > kMaxHidden)
+    return fail(ESCHA_E_SHAPE, "n=%d is not a multiple of 128 in [128, %d]", n, kMaxHidden);
   if (!(eps >= 0.f)) return fail(ESCHA_E_ARG, "eps must be >= 0");
   if (n_tokens == 0) return ESCHA_OK;
   if (!y || !x_bf16) return fail(ESCHA_E_NULL, "y/x is NULL");
@@ -337,15 +364,15 @@ size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t 
                                        int32_t n_tokens) {
   if (!layers || n_layers < 1 || n_tokens < 0) return 0;
   const escha_moe_layer_t* L = &layers[0];
-  const size_t xbuf = round_up((size_t)n_tokens * L->hidden * sizeof(uint16_t));
   const size_t ybuf = round_up((size_t)n_tokens * L->hidden * sizeof(float));
-  return decode_ws_bytes(L, n_tokens) + 2 * xbuf + ybuf;
+  return decode_ws_bytes(L, n_tokens) + ybuf;
 }
 
 int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
                            const uint16_t* x0_bf16, int32_t n_tokens, const int32_t* topk_ids,
                            const float* topk_w, float eps, float* y_last, uint16_t* x_chain,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, void* const* probe_events,
+                           void* stream) {
   if (!layers) return fail(ESCHA_E_NULL, "layers is NULL");
   if (n_layers < 1) return fail(ESCHA_E_ARG, "n_layers=%d", n_layers);
   for (int l = 0; l < n_layers; ++l) {
@@ -364,27 +391,32 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
   const int H = L0->hidden, k = L0->top_k;
   char* b = (char*)workspace;
   const DecodeWs ws = decode_ws_carve(L0, n_tokens, b);
-  b += decode_ws_bytes(L0, n_tokens);
-  const size_t xbuf = round_up((size_t)n_tokens * H * sizeof(uint16_t));
-  uint16_t* xa = (uint16_t*)b;
-  uint16_t* xb = (uint16_t*)(b + xbuf);
-  float* ytmp = (float*)(b + 2 * xbuf);
+  float* ytmp = (float*)(b + decode_ws_bytes(L0, n_tokens));
   hipStream_t s = (hipStream_t)stream;
   const size_t xs = (size_t)n_tokens * H;
   if (x_chain) {
-    hipError_t e = hipMemcpyAsync(x_chain, x0_bf16, xs * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
+    hipError_t e =
+        hipMemcpyAsync(x_chain, x0_bf16, xs * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "x_chain copy");
   }
-  const uint16_t* x = x0_bf16;
   for (int l = 0; l < n_layers; ++l) {
-    const bool last = l == n_layers - 1;
-    uint16_t* x_next = nullptr;
-    if (!last) x_next = x_chain ? x_chain + (size_t)(l + 1) * xs : ((l & 1) ? xb : xa);
-    float* y = last ? y_last : ytmp;
-    int rc = run_layer_decode(&layers[l], x, n_tokens, topk_ids + (size_t)l * n_tokens * k,
-                              topk_w + (size_t)l * n_tokens * k, y, nullptr, x_next, eps, ws, s);
+    // layer 0 reads x0; layer l > 0 reads RMSNorm(y_{l-1}) from ytmp, which
+    // its own combine then overwrites with y_l (stream order)
+    LayerInput in{};
+    if (l == 0) {
+      in.x_bf16 = x0_bf16;
+    } else {
+      in.y_prev = ytmp;
+      in.ss_prev = ws.ss;
+      in.eps = eps;
+      in.x_out = x_chain ? x_chain + (size_t)l * xs : nullptr;
+    }
+    float* y = l == n_layers - 1 ? y_last : ytmp;
+    hipEvent_t before = probe_events ? (hipEvent_t)probe_events[2 * l] : nullptr;
+    hipEvent_t after = probe_events ? (hipEvent_t)probe_events[2 * l + 1] : nullptr;
+    int rc = run_layer_decode(&layers[l], in, n_tokens, topk_ids + (size_t)l * n_tokens * k,
+                              topk_w + (size_t)l * n_tokens * k, y, nullptr, ws, s, before, after);
     if (rc) return rc;
-    x = x_next;
   }
   return ESCHA_OK;
 }

@@ -1,13 +1,15 @@
 // escha_kernels.hip -- gfx950 kernels of the trellis-coded expert path and
 // their host-side launchers (called by escha_api.cpp after validation).
 //
-// Streaming-decode kernels (small batches): one wave per (pair, group of 16
-// output tiles = 256 outputs, chunk of 128 inputs = one Hadamard block).
-// Each wave rotates its 128-input block of the activation in registers,
-// streams 8 tile-rows of codes (one 16-byte load per lane per tile-row at
-// K=2), decodes in registers and accumulates in fp32. Splits over the input
-// dimension land in a partial buffer that the next kernel reduces in a
-// fixed order, so results are bit-reproducible with no atomics.
+// Streaming-decode kernels (small batches): one work-group per (pair, group
+// of 16 output tiles = 256 outputs, chunk of 128 inputs = one Hadamard
+// block). Each wave first issues the loads of its tile-rows of codes (one
+// 16-byte load per lane per tile-row at K=2; the codes do not depend on the
+// activations), then wave 0 rotates the chunk's 128 inputs in registers
+// while the bytes are in flight; every wave then decodes in registers and
+// accumulates in fp32. The waves' sums meet in LDS and splits over the
+// input dimension land in a partial buffer that the next kernel reduces in
+// a fixed order, so results are bit-reproducible with no atomics.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -17,27 +19,35 @@
 namespace escha {
 
 // ------------------------------------------------------------------------
-// Shared inner loop: 8 tile-rows (one 128-input chunk) of 16 output tiles.
-// xs: the chunk's rotated activations (LDS, 128 floats). Returns the 16
-// per-column sums of this lane's quarter; the caller reduces the quarters.
+// Shared pieces of the streaming kernels.
 // ------------------------------------------------------------------------
-template <int K>
-__device__ __forceinline__ void chunk_mac(const uint16_t* __restrict__ code_e, int n_nt, int kt0,
-                                          int nt, int q, const float* xs, float (&acc)[16]) {
-  constexpr int kOwn = Quarter<K>::kOwn;
-  uint32_t raw[8][kOwn];
+
+// Issue the loads of NKT consecutive tile-rows (kt0, kt0+1, ..) of output
+// tile nt, this lane's quarter. Nothing here waits for the data.
+template <int K, int NKT>
+__device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ code_e, int n_nt, int kt0,
+                                           int nt, int q, uint32_t (&raw)[NKT][Quarter<K>::kOwn]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NKT; ++j) {
     const uint16_t* tq = code_e + ((size_t)(kt0 + j) * n_nt + nt) * (16 * K) + q * (4 * K);
     load_quarter<K>(tq, raw[j]);
   }
+}
+
+// Decode the loaded rows and accumulate: acc[n] += W[.., n] * x~[k] over this
+// lane's 4 input rows of each tile-row. xs: the 128 rotated inputs of the
+// chunk (LDS); j0: index of the first row inside the chunk.
+template <int K, int NKT>
+__device__ __forceinline__ void mac_rows(const uint32_t (&raw)[NKT][Quarter<K>::kOwn], int j0, int q,
+                                         const float* xs, float (&acc)[16]) {
+  constexpr int kOwn = Quarter<K>::kOwn;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NKT; ++j) {
     uint32_t d[kOwn + 1];
 #pragma unroll
     for (int i = 0; i < kOwn; ++i) d[i] = raw[j][i];
     d[kOwn] = next_quarter_dword(raw[j][0]);
-    const float4 xv = *reinterpret_cast<const float4*>(xs + 16 * j + 4 * q);
+    const float4 xv = *reinterpret_cast<const float4*>(xs + 16 * (j0 + j) + 4 * q);
     const float xk[4] = {xv.x, xv.y, xv.z, xv.w};
     decode_quarter<K>(d, [&](int kk, int n, h16x2 w) {
       acc[n] = __builtin_fmaf((float)w.x, xk[kk], acc[n]);
@@ -62,12 +72,18 @@ __device__ __forceinline__ float4 quad_reduce_pick(float (&acc)[16], int q) {
   return r;
 }
 
+__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
 // ------------------------------------------------------------------------
-// gate_up (or any single projection) partial sums.
-// grid.x = n_pairs * n_chunks * n_groups, block = 64.
+// gate_up (or any single projection) partial sums over one 128-input chunk.
+// grid.x = n_pairs * n_chunks * n_groups; block = 4 waves, wave w streams
+// tile-rows 8c+2w and 8c+2w+1 of the 16 output tiles of group g.
 // ------------------------------------------------------------------------
-template <int K>
-__global__ __launch_bounds__(64) void k_in_partial(InPartialArgs a) {
+template <int K, bool FROM_Y>
+__global__ __launch_bounds__(256) void k_in_partial(InPartialArgs a) {
+  constexpr int kOwn = Quarter<K>::kOwn;
   const int n_groups = a.out_f / 256;
   const int n_chunks = a.in_f / 128;
   int bid = blockIdx.x;
@@ -75,46 +91,93 @@ __global__ __launch_bounds__(64) void k_in_partial(InPartialArgs a) {
   bid /= n_groups;
   const int c = bid % n_chunks;
   const int p = bid / n_chunks;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   float* out = a.partial + ((size_t)p * n_chunks + c) * a.out_f + g * 256;
   const int e = a.ids ? a.ids[p] : a.fixed_expert;
-  if (e < 0 || e >= a.n_experts) {
-    reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
+  const bool valid = e >= 0 && e < a.n_experts;  // uniform over the block
   const int t = p / a.top_k;
+  const int q = lane & 3;
+  const int nt = g * 16 + (lane >> 2);
+  const int n_nt = a.out_f / 16;
 
+  // 1. the codes do not depend on the activations: start streaming them now
+  uint32_t raw[2][kOwn];
+  if (valid) {
+    const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.in_f / 16) * n_nt * (16 * K);
+    issue_rows<K, 2>(code_e, n_nt, 8 * c + 2 * wave, nt, q, raw);
+  }
+
+  // 2. rotated inputs of this chunk: x~ = H_n(rin (.) x)
   __shared__ __attribute__((aligned(16))) float xs[128];
-  {
-    const uint16_t* xr = a.x_bf16 + (size_t)t * a.in_f + c * 128;
+  __shared__ float4 red[4][64];
+  if (wave == 0) {
+    float x0, x1;
+    if constexpr (FROM_Y) {
+      // RMSNorm of the previous layer's output row, rounded to bf16
+      const int nb = a.in_f / 128;
+      const float* ss = a.ss_prev + (size_t)t * nb;
+      float tot = 0.f;
+      for (int b = 0; b < nb; ++b) tot += ss[b];
+      const float inv = 1.0f / sqrtf(tot / (float)a.in_f + a.eps);
+      const float* yr = a.y_prev + (size_t)t * a.in_f + c * 128;
+      const uint16_t b0 = f32_to_bf16_rne(yr[lane] * inv);
+      const uint16_t b1 = f32_to_bf16_rne(yr[lane + 64] * inv);
+      if (a.x_out && g == 0 && p % a.top_k == 0) {
+        uint16_t* xo = a.x_out + (size_t)t * a.in_f + c * 128;
+        xo[lane] = b0;
+        xo[lane + 64] = b1;
+      }
+      x0 = bf16_to_f32(b0);
+      x1 = bf16_to_f32(b1);
+    } else {
+      const uint16_t* xr = a.x_bf16 + (size_t)t * a.in_f + c * 128;
+      x0 = bf16_to_f32(xr[lane]);
+      x1 = bf16_to_f32(xr[lane + 64]);
+    }
+    if (!valid) {  // an out-of-range expert id contributes nothing
+      reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+      return;
+    }
     const uint16_t* rr = a.rin + (size_t)e * a.in_f + c * 128;
-    float v0 = bf16_to_f32(xr[lane]) * f16_to_f32(rr[lane]);
-    float v1 = bf16_to_f32(xr[lane + 64]) * f16_to_f32(rr[lane + 64]);
+    float v0 = x0 * f16_to_f32(rr[lane]);
+    float v1 = x1 * f16_to_f32(rr[lane + 64]);
     fwht128(v0, v1);
     xs[lane] = v0 * kInvSqrt128;
     xs[lane + 64] = v1 * kInvSqrt128;
   }
+  if (!valid) return;
   __syncthreads();
 
-  const int q = lane & 3;
-  const int nt = g * 16 + (lane >> 2);
-  const int n_nt = a.out_f / 16;
-  const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.in_f / 16) * n_nt * (16 * K);
+  // 3. decode and accumulate this wave's two tile-rows
   float acc[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-  chunk_mac<K>(code_e, n_nt, 8 * c, nt, q, xs, acc);
-  reinterpret_cast<float4*>(out)[lane] = quad_reduce_pick(acc, q);
+  mac_rows<K, 2>(raw, 2 * wave, q, xs, acc);
+  red[wave][lane] = quad_reduce_pick(acc, q);
+  __syncthreads();
+
+  // 4. fixed-order sum over the four waves
+  if (wave == 0) {
+    float4 r = red[0][lane];
+    r = f4add(r, red[1][lane]);
+    r = f4add(r, red[2][lane]);
+    r = f4add(r, red[3][lane]);
+    reinterpret_cast<float4*>(out)[lane] = r;
+  }
 }
 
 // ------------------------------------------------------------------------
-// down partial sums. The prologue finishes gate_up for the 128 inter
-// channels of this wave's chunk: reduce the gate_up partials, H128, rout,
-// SiLU(gate)*up; then rin and H128 of down. A chunk whose 128 h values are
-// all exactly zero contributes exactly zero and is skipped.
+// down partial sums over one 128-channel chunk of the inter dimension.
+// grid.x = n_pairs * n_chunks * n_groups; block = 8 waves, wave w streams
+// tile-row 8c+w. Wave 0 finishes gate_up for the chunk's channels: reduce
+// the gate_up partials, H128, rout, SiLU(gate)*up; then rin and H128 of
+// down. A chunk whose 128 h values are all exactly zero (every channel
+// pruned) contributes exactly zero: its decode is skipped.
 // ------------------------------------------------------------------------
 template <int K>
-__global__ __launch_bounds__(64) void k_down_partial(DownPartialArgs a) {
+__global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
+  constexpr int kOwn = Quarter<K>::kOwn;
   const int n_groups = a.out_f / 256;
   const int n_chunks = a.in_f / 128;  // in_f = inter
   int bid = blockIdx.x;
@@ -122,19 +185,31 @@ __global__ __launch_bounds__(64) void k_down_partial(DownPartialArgs a) {
   bid /= n_groups;
   const int c = bid % n_chunks;
   const int p = bid / n_chunks;
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   float* out = a.partial + ((size_t)p * n_chunks + c) * a.out_f + g * 256;
   const int e = a.ids[p];
   if (e < 0 || e >= a.n_experts) {
-    reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (wave == 0) reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
     return;
   }
   const int inter = a.in_f;
   const int g2 = 2 * inter;
+  const int q = lane & 3;
+  const int nt = g * 16 + (lane >> 2);
+  const int n_nt = a.out_f / 16;
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)(inter / 16) * n_nt * (16 * K);
 
-  float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
-  {
+  uint32_t raw[1][kOwn];
+  issue_rows<K, 1>(code_e, n_nt, 8 * c + wave, nt, q, raw);
+
+  __shared__ __attribute__((aligned(16))) float xs[128];
+  __shared__ float4 red[8][64];
+  __shared__ int skip;
+  if (wave == 0) {
+    float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
     const float* gp = a.gu_partial + (size_t)p * a.gu_chunks * g2 + 128 * c;
+#pragma unroll 16
     for (int cc = 0; cc < a.gu_chunks; ++cc) {
       const float* b = gp + (size_t)cc * g2;
       g0 += b[lane];
@@ -142,46 +217,46 @@ __global__ __launch_bounds__(64) void k_down_partial(DownPartialArgs a) {
       u0 += b[inter + lane];
       u1 += b[inter + lane + 64];
     }
-  }
-  fwht128(g0, g1);
-  fwht128(u0, u1);
-  const uint16_t* ro = a.gu_rout + (size_t)e * g2 + 128 * c;
-  g0 = g0 * kInvSqrt128 * f16_to_f32(ro[lane]);
-  g1 = g1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
-  u0 = u0 * kInvSqrt128 * f16_to_f32(ro[inter + lane]);
-  u1 = u1 * kInvSqrt128 * f16_to_f32(ro[inter + lane + 64]);
-  const float h0 = silu(g0) * u0;
-  const float h1 = silu(g1) * u1;
-  if (a.inter_out && g == 0) {
-    float* io = a.inter_out + (size_t)p * inter + 128 * c;
-    io[lane] = h0;
-    io[lane + 64] = h1;
-  }
-  if (__ballot((h0 != 0.f) || (h1 != 0.f)) == 0) {
-    reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
-    return;
-  }
-
-  __shared__ __attribute__((aligned(16))) float xs[128];
-  {
+    fwht128(g0, g1);
+    fwht128(u0, u1);
+    const uint16_t* ro = a.gu_rout + (size_t)e * g2 + 128 * c;
+    g0 = g0 * kInvSqrt128 * f16_to_f32(ro[lane]);
+    g1 = g1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
+    u0 = u0 * kInvSqrt128 * f16_to_f32(ro[inter + lane]);
+    u1 = u1 * kInvSqrt128 * f16_to_f32(ro[inter + lane + 64]);
+    const float h0 = silu(g0) * u0;
+    const float h1 = silu(g1) * u1;
+    if (a.inter_out && g == 0) {
+      float* io = a.inter_out + (size_t)p * inter + 128 * c;
+      io[lane] = h0;
+      io[lane + 64] = h1;
+    }
+    const bool all_zero = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
     const uint16_t* rr = a.rin + (size_t)e * inter + 128 * c;
     float v0 = h0 * f16_to_f32(rr[lane]);
     float v1 = h1 * f16_to_f32(rr[lane + 64]);
     fwht128(v0, v1);
     xs[lane] = v0 * kInvSqrt128;
     xs[lane + 64] = v1 * kInvSqrt128;
+    if (lane == 0) skip = all_zero ? 1 : 0;
   }
   __syncthreads();
-
-  const int q = lane & 3;
-  const int nt = g * 16 + (lane >> 2);
-  const int n_nt = a.out_f / 16;
-  const uint16_t* code_e = a.code + (size_t)e * (size_t)(inter / 16) * n_nt * (16 * K);
+  if (skip) {  // uniform over the block
+    if (wave == 0) reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    return;
+  }
   float acc[16];
 #pragma unroll
   for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-  chunk_mac<K>(code_e, n_nt, 8 * c, nt, q, xs, acc);
-  reinterpret_cast<float4*>(out)[lane] = quad_reduce_pick(acc, q);
+  mac_rows<K, 1>(raw, wave, q, xs, acc);
+  red[wave][lane] = quad_reduce_pick(acc, q);
+  __syncthreads();
+  if (wave == 0) {
+    float4 r = red[0][lane];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) r = f4add(r, red[w][lane]);
+    reinterpret_cast<float4*>(out)[lane] = r;
+  }
 }
 
 // ------------------------------------------------------------------------
@@ -202,6 +277,7 @@ __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
   }
   float z0 = 0.f, z1 = 0.f;
   const float* pp = a.partial + (size_t)p * a.n_chunks * a.out_f + 128 * b;
+#pragma unroll 8
   for (int cc = 0; cc < a.n_chunks; ++cc) {
     z0 += pp[(size_t)cc * a.out_f + lane];
     z1 += pp[(size_t)cc * a.out_f + lane + 64];
@@ -213,76 +289,84 @@ __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
 }
 
 // ------------------------------------------------------------------------
-// Combine: per token, finish down for each slot (reduce partials, H128,
-// rout) and sum the slots in order, weighted by the router probabilities.
-// Optionally RMS-normalise the row and round it to bf16 for the next layer.
-// grid.x = n_tokens, block = 1024 (16 waves; wave w owns blocks w, w+16, ..).
+// Combine: one wave per (token, 128-block of hidden). For each slot: reduce
+// down's partials, H128, rout; then sum the slots in order, weighted by the
+// router probabilities. Also writes the block's sum of squares.
+// grid.x = n_tokens * (hidden / 128), block = 64.
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_combine(CombineArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float row[];  // hidden floats
-  __shared__ float wave_ss[16];
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
+  constexpr int kBatch = 8;
   const int nb = a.hidden / 128;
-  float ss = 0.f;
-  for (int b = wave; b < nb; b += 16) {
-    float acc0 = 0.f, acc1 = 0.f;
-    for (int j = 0; j < a.top_k; ++j) {
+  const int b = blockIdx.x % nb;
+  const int t = blockIdx.x / nb;
+  const int lane = threadIdx.x;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int j0 = 0; j0 < a.top_k; j0 += kBatch) {
+    float z0[kBatch], z1[kBatch];
+    // all loads of the batch first, then the transforms
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      z0[jj] = 0.f;
+      z1[jj] = 0.f;
+      const int j = j0 + jj;
+      if (j < a.top_k) {
+        const float* pp = a.partial + (size_t)(t * a.top_k + j) * a.n_chunks * a.hidden + 128 * b;
+        for (int cc = 0; cc < a.n_chunks; ++cc) {
+          z0[jj] += pp[(size_t)cc * a.hidden + lane];
+          z1[jj] += pp[(size_t)cc * a.hidden + lane + 64];
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < kBatch; ++jj) {
+      const int j = j0 + jj;
+      if (j >= a.top_k) break;
       const int p = t * a.top_k + j;
       const int e = a.ids[p];
-      if (e < 0 || e >= a.n_experts) continue;
-      const float wt = a.w[p];
-      float z0 = 0.f, z1 = 0.f;
-      const float* pp = a.partial + (size_t)p * a.n_chunks * a.hidden + 128 * b;
-      for (int cc = 0; cc < a.n_chunks; ++cc) {
-        z0 += pp[(size_t)cc * a.hidden + lane];
-        z1 += pp[(size_t)cc * a.hidden + lane + 64];
-      }
-      fwht128(z0, z1);
+      if (e < 0 || e >= a.n_experts) continue;  // uniform over the wave
+      float v0 = z0[jj], v1 = z1[jj];
+      fwht128(v0, v1);
       const uint16_t* ro = a.rout + (size_t)e * a.hidden + 128 * b;
-      const float y0 = z0 * kInvSqrt128 * f16_to_f32(ro[lane]);
-      const float y1 = z1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
-      acc0 = __builtin_fmaf(wt, y0, acc0);
-      acc1 = __builtin_fmaf(wt, y1, acc1);
+      const float wt = a.w[p];
+      acc0 = __builtin_fmaf(wt, v0 * kInvSqrt128 * f16_to_f32(ro[lane]), acc0);
+      acc1 = __builtin_fmaf(wt, v1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]), acc1);
     }
-    float* y = a.y + (size_t)t * a.hidden + 128 * b;
-    y[lane] = acc0;
-    y[lane + 64] = acc1;
-    row[128 * b + lane] = acc0;
-    row[128 * b + lane + 64] = acc1;
-    ss = __builtin_fmaf(acc0, acc0, ss);
-    ss = __builtin_fmaf(acc1, acc1, ss);
   }
-  if (!a.x_next) return;  // uniform across the block
+  float* y = a.y + (size_t)t * a.hidden + 128 * b;
+  y[lane] = acc0;
+  y[lane + 64] = acc1;
+  float ss = __builtin_fmaf(acc0, acc0, acc1 * acc1);
 #pragma unroll
   for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
-  if (lane == 0) wave_ss[wave] = ss;
-  __syncthreads();
-  float tot = 0.f;
-  for (int w = 0; w < 16; ++w) tot += wave_ss[w];
-  const float inv = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
-  uint16_t* xo = a.x_next + (size_t)t * a.hidden;
-  for (int i = threadIdx.x; i < a.hidden; i += 1024) xo[i] = f32_to_bf16_rne(row[i] * inv);
+  if (lane == 0) a.ss[(size_t)t * nb + b] = ss;
 }
 
 // ------------------------------------------------------------------------
-// Standalone RMSNorm -> bf16. grid.x = n_tokens, block = 256.
+// Standalone RMSNorm -> bf16, with the same arithmetic as the fused path of
+// the layer stack (block sums of squares as in k_combine, summed over the
+// blocks in order, then the scale as in k_in_partial). grid.x = n_tokens,
+// block = 1024 (wave w handles 128-blocks w, w+16, ..).
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float* __restrict__ y, int n, float eps,
-                                                      uint16_t* __restrict__ x) {
-  __shared__ float wave_ss[4];
+__global__ __launch_bounds__(1024) void k_rmsnorm_bf16(const float* __restrict__ y, int n, float eps,
+                                                       uint16_t* __restrict__ x) {
+  __shared__ float block_ss[128];  // n <= 16384
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nb = n / 128;
   const float* yr = y + (size_t)blockIdx.x * n;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < n; i += 256) ss = __builtin_fmaf(yr[i], yr[i], ss);
+  for (int b = wave; b < nb; b += 16) {
+    const float a0 = yr[128 * b + lane], a1 = yr[128 * b + lane + 64];
+    float ss = __builtin_fmaf(a0, a0, a1 * a1);
 #pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
-  if ((threadIdx.x & 63) == 0) wave_ss[threadIdx.x >> 6] = ss;
+    for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
+    if (lane == 0) block_ss[b] = ss;
+  }
   __syncthreads();
-  const float tot = wave_ss[0] + wave_ss[1] + wave_ss[2] + wave_ss[3];
+  float tot = 0.f;
+  for (int b = 0; b < nb; ++b) tot += block_ss[b];
   const float inv = 1.0f / sqrtf(tot / (float)n + eps);
   uint16_t* xr = x + (size_t)blockIdx.x * n;
-  for (int i = threadIdx.x; i < n; i += 256) xr[i] = f32_to_bf16_rne(yr[i] * inv);
+  for (int i = threadIdx.x; i < n; i += 1024) xr[i] = f32_to_bf16_rne(yr[i] * inv);
 }
 
 // ------------------------------------------------------------------------
@@ -473,19 +557,27 @@ static hipError_t last_launch() { return hipGetLastError(); }
 
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s) {
   const unsigned grid = (unsigned)((size_t)a.n_pairs * (a.in_f / 128) * (a.out_f / 256));
-  if (k_bits == 2)
-    hipLaunchKernelGGL(k_in_partial<2>, dim3(grid), dim3(64), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_in_partial<3>, dim3(grid), dim3(64), 0, s, a);
+  const bool from_y = a.x_bf16 == nullptr;
+  if (k_bits == 2) {
+    if (from_y)
+      hipLaunchKernelGGL((k_in_partial<2, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_in_partial<2, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (from_y)
+      hipLaunchKernelGGL((k_in_partial<3, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_in_partial<3, false>), dim3(grid), dim3(256), 0, s, a);
+  }
   return last_launch();
 }
 
 hipError_t launch_down_partial(const DownPartialArgs& a, int k_bits, hipStream_t s) {
   const unsigned grid = (unsigned)((size_t)a.n_pairs * (a.in_f / 128) * (a.out_f / 256));
   if (k_bits == 2)
-    hipLaunchKernelGGL(k_down_partial<2>, dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_down_partial<2>, dim3(grid), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL(k_down_partial<3>, dim3(grid), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(k_down_partial<3>, dim3(grid), dim3(512), 0, s, a);
   return last_launch();
 }
 
@@ -496,14 +588,14 @@ hipError_t launch_proj_finish(const FinishArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(a.n_tokens), dim3(1024), (size_t)a.hidden * sizeof(float), s,
-                     a);
+  const unsigned grid = (unsigned)((size_t)a.n_tokens * (a.hidden / 128));
+  hipLaunchKernelGGL(k_combine, dim3(grid), dim3(64), 0, s, a);
   return last_launch();
 }
 
 hipError_t launch_rmsnorm_bf16(const float* y, int n_tokens, int n, float eps, uint16_t* x,
                                hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(n_tokens), dim3(256), 0, s, y, n, eps, x);
+  hipLaunchKernelGGL(k_rmsnorm_bf16, dim3(n_tokens), dim3(1024), 0, s, y, n, eps, x);
   return last_launch();
 }
 

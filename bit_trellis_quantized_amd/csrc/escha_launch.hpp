@@ -9,9 +9,12 @@
 
 namespace escha {
 
-// Partial sums of a projection whose input is a bf16 activation row.
-// Pair p uses token p / top_k and expert ids[p] (or fixed_expert when ids is
-// null). partial: fp32 [n_pairs][in_f/128][out_f].
+// Partial sums of a projection. Pair p uses token p / top_k and expert ids[p]
+// (or fixed_expert when ids is null). The input row is either bf16 (x_bf16)
+// or, when x_bf16 is null, the previous layer's fp32 output y_prev with its
+// per-128-block sums of squares ss_prev: the kernel applies the RMSNorm
+// (unit weight, eps) and rounds to bf16 itself, and writes those bf16 rows
+// to x_out when x_out is not null. partial: fp32 [n_pairs][in_f/128][out_f].
 struct InPartialArgs {
   const uint16_t* code;
   const uint16_t* rin;
@@ -19,6 +22,10 @@ struct InPartialArgs {
   const int32_t* ids;
   int32_t fixed_expert;
   const uint16_t* x_bf16;
+  const float* y_prev;
+  const float* ss_prev;
+  float eps;
+  uint16_t* x_out;
   float* partial;
 };
 
@@ -47,7 +54,9 @@ struct FinishArgs {
   float* y;
 };
 
-// Per-token weighted slot sum of down outputs (+ optional RMSNorm -> bf16).
+// Per-token weighted slot sum of down outputs. y fp32 [n_tokens][hidden];
+// ss fp32 [n_tokens][hidden/128] receives each 128-block's sum of squares
+// (the next layer's RMSNorm).
 struct CombineArgs {
   const float* partial;
   int32_t n_chunks;
@@ -56,8 +65,7 @@ struct CombineArgs {
   const float* w;
   int32_t n_experts, hidden, top_k, n_tokens;
   float* y;
-  uint16_t* x_next;
-  float eps;
+  float* ss;
 };
 
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s);

@@ -66,7 +66,7 @@ _SIGS = {
     "escha_rmsnorm_bf16": ([_vp, _i32, _i32, _f32, _vp, _vp], ctypes.c_int),
     "escha_moe_stack_workspace_bytes": ([_P(escha_moe_layer_t), _i32, _i32], _sz),
     "escha_moe_stack_decode": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp,
-                                _vp, _sz, _vp], ctypes.c_int),
+                                _vp, _sz, _vp, _vp], ctypes.c_int),
     "escha_last_error": ([], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -306,7 +306,8 @@ class Stack:
 
 
 def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6, out=None,
-                           x_chain=None, workspace=None, stream=None):
+                           x_chain=None, workspace=None, probe_events=None, stream=None):
+    """probe_events: optional sequence of 2*n_layers raw hipEvent_t handles (ints)."""
     T = x0_bf16.shape[0]
     hidden = stack.layers[0].hidden
     if out is None:
@@ -318,5 +319,14 @@ def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float =
                                        _ptr(topk_ids, torch.int32, "topk_ids"),
                                        _ptr(topk_w, torch.float32, "topk_w"), eps,
                                        _ptr(out, torch.float32, "y"), _ptr(x_chain, _U16, "x_chain"),
-                                       _ptr(workspace), workspace.numel(), _stream(stream)))
+                                       _ptr(workspace), workspace.numel(),
+                                       _events(probe_events, 2 * len(stack.layers)), _stream(stream)))
     return out
+
+
+def _events(handles, n):
+    if handles is None:
+        return None
+    if len(handles) != n:
+        raise ValueError(f"need {n} probe events, got {len(handles)}")
+    return ctypes.cast((ctypes.c_void_p * n)(*[int(h) for h in handles]), ctypes.c_void_p)

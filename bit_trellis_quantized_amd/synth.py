@@ -161,6 +161,17 @@ def layer_tensors(seed: int, layer: int, n_experts: int = N_EXPERTS, experts=Non
 
 # ---------------------------------------------------------------- workloads
 
+def stack_token_inputs(seed: int, n_layers: int, T: int, entry: int, E: int = N_EXPERTS,
+                       hidden: int = HIDDEN):
+    """Inputs of one decode step of the layer stack: x0 bf16 bits [T][hidden]
+    and router logits fp32 [n_layers][T][E], N(0, 1). ``entry`` selects one
+    of several independent steps (a pool the benchmark cycles through)."""
+    x0 = activations(seed, T, hidden, layer=100000 + entry)
+    logits = np.stack([normal_logits(seed, T, E, layer=1000 * (entry + 1) + l)
+                       for l in range(n_layers)])
+    return x0, logits
+
+
 CONFIGS = {
     1: dict(name="gemv-256x256-k2", in_f=256, out_f=256, K=2, T=1),
     2: dict(name="layer-decode-b1", T=1, logits="normal"),

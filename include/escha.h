@@ -174,7 +174,9 @@ ESCHA_API int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t
 
 /*
  * Between stacked layers: x = bf16( y / sqrt(mean(y^2) + eps) ) per row,
- * unit weight, no residual. y fp32 [n_tokens][n]; x_bf16 [n_tokens][n].
+ * unit weight, no residual. y fp32 [n_tokens][n]; x_bf16 [n_tokens][n];
+ * n a multiple of 128, at most 16384. Bit-identical to the normalisation
+ * escha_moe_stack_decode applies between its layers.
  */
 ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, float eps, uint16_t* x_bf16,
                        void* stream);
@@ -187,13 +189,18 @@ ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, fl
  * y_last fp32 [n_tokens][hidden] = y_{n_layers-1}; x_chain (nullable) bf16
  * [n_layers][n_tokens][hidden] receives each layer's input x_l.
  * All layers must share hidden, inter and top_k.
+ * probe_events (nullable): a HOST array of 2*n_layers hipEvent_t handles;
+ * events[2l] and events[2l+1] are recorded on `stream` right before and
+ * right after layer l's gate_up kernel, so a caller can time that kernel
+ * inside a longer run. The library does not create or destroy them.
  */
 ESCHA_API size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t n_layers,
                                        int32_t n_tokens);
 ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
                            const uint16_t* x0_bf16, int32_t n_tokens, const int32_t* topk_ids,
                            const float* topk_w, float eps, float* y_last, uint16_t* x_chain,
-                           void* workspace, size_t workspace_bytes, void* stream);
+                           void* workspace, size_t workspace_bytes, void* const* probe_events,
+                           void* stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 ESCHA_API const char* escha_last_error(void);

@@ -19,6 +19,7 @@ def _declared():
 
 @pytest.fixture(scope="module")
 def lib():
+    import torch  # noqa: F401  (load torch's HIP runtime first, as the binding does)
     if not LIB.exists():
         from bit_trellis_quantized_amd import build
         build.build()
@@ -139,14 +140,14 @@ def test_stack_validation(lib):
     f = lib.escha_moe_stack_decode
     f.argtypes = [ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     arr = (Layer * 2)(_layer(), _layer(inter=256))
     arr[1].gate_up.out_features = 512
     arr[1].down.in_features = 256
-    assert f(arr, 2, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, 1 << 40, None) == -2
-    assert f(arr, 0, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, 1 << 40, None) == -7
+    assert f(arr, 2, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, 1 << 40, None, None) == -2
+    assert f(arr, 0, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, 1 << 40, None, None) == -7
     arr2 = (Layer * 1)(_layer())
-    assert f(arr2, 1, FAKE, 1, FAKE, FAKE, -1.0, FAKE, None, FAKE, 1 << 40, None) == -7
+    assert f(arr2, 1, FAKE, 1, FAKE, FAKE, -1.0, FAKE, None, FAKE, 1 << 40, None, None) == -7
 
 
 def test_leaf_contract():
