@@ -208,13 +208,13 @@ def main():
     ms_total = hip.elapsed_ms(start, stop)
     ms_per_step = ms_total / args.steps
 
-    # gate_up kernel durations from the probes of each pool entry's last step
-    gu_ms = []
+    # per-layer durations from the probes of each pool entry's last step
+    layer_ms = []
     if not args.no_probe:
         for p in pool:
             for l in range(NL):
-                gu_ms.append(hip.elapsed_ms(p["probes"][2 * l], p["probes"][2 * l + 1]))
-    gu_avg_ms = float(np.mean(gu_ms)) if gu_ms else None
+                layer_ms.append(hip.elapsed_ms(p["probes"][2 * l], p["probes"][2 * l + 1]))
+    layer_avg_ms = float(np.mean(layer_ms)) if layer_ms else None
 
     # algorithmic bytes: the packed codes of the distinct experts each layer
     # routes to (at batch 1 every one of the 8 is distinct), averaged over the pool
@@ -226,15 +226,17 @@ def main():
     tok_s = T / (ms_per_step / 1e3)
     gbs = code_bytes_step / (ms_per_step / 1e3) / 1e9
 
-    gu_bytes_launch = T * k * GU_BYTES_PER_PAIR
+    layer_bytes = code_bytes_step / NL
     roofline = None
-    if gu_avg_ms:
-        achieved = gu_bytes_launch / (gu_avg_ms / 1e3) / 1e9
-        roofline = {"kernel": "k_in_partial<2> (gate_up, K=2)", "bound": "hbm",
+    if layer_avg_ms:
+        achieved = layer_bytes / (layer_avg_ms / 1e3) / 1e9
+        roofline = {"kernel": "one layer's decode launches (k_in_partial + k_down_partial + "
+                              "k_combine)",
+                    "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "bytes_per_launch": gu_bytes_launch, "avg_launch_us": round(gu_avg_ms * 1e3, 3),
-                    "samples": len(gu_ms)}
+                    "bytes_per_launch": int(layer_bytes), "avg_launch_us": round(layer_avg_ms * 1e3, 3),
+                    "samples": len(layer_ms)}
 
     checks = {}
     cpu = None

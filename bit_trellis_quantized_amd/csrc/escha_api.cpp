@@ -137,8 +137,6 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
     return hip_fail(e, "probe event record");
   e = escha::launch_in_partial(a, L->gate_up.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "gate_up partial launch");
-  if (probe_after && (e = hipEventRecord(probe_after, s)) != hipSuccess)
-    return hip_fail(e, "probe event record");
 
   escha::DownPartialArgs d{};
   d.code = (const uint16_t*)L->down.code;
@@ -170,6 +168,8 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   c.ss = ws.ss;
   e = escha::launch_combine(c, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
+  if (probe_after && (e = hipEventRecord(probe_after, s)) != hipSuccess)
+    return hip_fail(e, "probe event record");
   return ESCHA_OK;
 }
 

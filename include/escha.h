@@ -190,9 +190,9 @@ ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, fl
  * [n_layers][n_tokens][hidden] receives each layer's input x_l.
  * All layers must share hidden, inter and top_k.
  * probe_events (nullable): a HOST array of 2*n_layers hipEvent_t handles;
- * events[2l] and events[2l+1] are recorded on `stream` right before and
- * right after layer l's gate_up kernel, so a caller can time that kernel
- * inside a longer run. The library does not create or destroy them.
+ * events[2l] and events[2l+1] are recorded on `stream` right before layer
+ * l's first kernel and right after its last one, so a caller can time each
+ * layer inside a longer run. The library does not create or destroy them.
  */
 ESCHA_API size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t n_layers,
                                        int32_t n_tokens);
