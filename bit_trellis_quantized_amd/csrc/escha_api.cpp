@@ -119,6 +119,7 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   escha::InPartialArgs a{};
   a.code = (const uint16_t*)L->gate_up.code;
   a.rin = (const uint16_t*)L->gate_up.rin;
+  a.rout = (const uint16_t*)L->gate_up.rout;
   a.n_experts = L->gate_up.n_experts;
   a.in_f = L->hidden;
   a.out_f = 2 * L->inter;
@@ -141,14 +142,15 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   escha::DownPartialArgs d{};
   d.code = (const uint16_t*)L->down.code;
   d.rin = (const uint16_t*)L->down.rin;
+  d.rout = (const uint16_t*)L->down.rout;
   d.n_experts = L->down.n_experts;
   d.in_f = L->inter;
   d.out_f = L->hidden;
   d.n_pairs = P;
   d.ids = ids;
+  d.w = w;
   d.gu_partial = ws.gu_part;
   d.gu_chunks = L->hidden / 128;
-  d.gu_rout = (const uint16_t*)L->gate_up.rout;
   d.inter_out = inter_out;
   d.partial = ws.dn_part;
   e = escha::launch_down_partial(d, L->down.k_bits, s);
@@ -157,10 +159,6 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   escha::CombineArgs c{};
   c.partial = ws.dn_part;
   c.n_chunks = L->inter / 128;
-  c.rout = (const uint16_t*)L->down.rout;
-  c.ids = ids;
-  c.w = w;
-  c.n_experts = L->down.n_experts;
   c.hidden = L->hidden;
   c.top_k = L->top_k;
   c.n_tokens = T;
@@ -277,6 +275,7 @@ int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_b
   escha::InPartialArgs a{};
   a.code = (const uint16_t*)w->code;
   a.rin = (const uint16_t*)w->rin;
+  a.rout = (const uint16_t*)w->rout;
   a.n_experts = w->n_experts;
   a.in_f = w->in_features;
   a.out_f = w->out_features;
@@ -291,12 +290,8 @@ int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_b
   escha::FinishArgs f{};
   f.partial = (const float*)workspace;
   f.n_chunks = w->in_features / 128;
-  f.rout = (const uint16_t*)w->rout;
-  f.n_experts = w->n_experts;
   f.out_f = w->out_features;
   f.n_pairs = n_tokens;
-  f.ids = nullptr;
-  f.fixed_expert = expert;
   f.y = y;
   e = escha::launch_proj_finish(f, s);
   return e == hipSuccess ? ESCHA_OK : hip_fail(e, "expert_gemv finish launch");

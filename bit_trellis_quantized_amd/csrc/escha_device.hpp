@@ -152,23 +152,89 @@ __device__ __forceinline__ uint32_t next_quarter_dword(uint32_t d0) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)d0, 0x39, 0xF, 0xF, false);
 }
 
+// ---- cross-lane data movement inside one wave (no LDS traffic) ----------
+
+// DPP move: lane i receives src from the lane selected by CTRL.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+constexpr int kQuadXor1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kQuadXor3 = 0x1B;     // quad_perm [3,2,1,0]
+constexpr int kHalfMirror = 0x141;  // lane i <- lane 7-i inside each group of 8
+constexpr int kRowRor8 = 0x128;     // rotate by 8 inside each row of 16 = xor 8
+
+// Value of lane i^H for H = 1, 2, 4, 8.
+template <int H>
+__device__ __forceinline__ float xor_lane(float v) {
+  if constexpr (H == 1) return dpp<kQuadXor1>(v);
+  if constexpr (H == 2) return dpp<kQuadXor2>(v);
+  if constexpr (H == 4) return dpp<kHalfMirror>(dpp<kQuadXor3>(v));  // (i^3)^7 = i^4
+  if constexpr (H == 8) return dpp<kRowRor8>(v);
+}
+
+// One butterfly across lanes i and i^H: low lane gets low+high, high lane
+// gets low-high. s = +1 on low lanes, -1 on high lanes; fma(+-1, a, b) is the
+// exactly rounded b +- a, identical to an add or a subtract.
+template <int H>
+__device__ __forceinline__ float butterfly(float v, float s) {
+  if constexpr (H <= 8) {
+    return __builtin_fmaf(s, v, xor_lane<H>(v));
+  } else {
+    // rows 16 apart (H = 16) or halves 32 apart (H = 32): swap the odd
+    // rows / upper half of a copy with the even rows / lower half of
+    // another copy; r[0] then holds the low element and r[1] the high one
+    // on both sides of the pair.
+    const unsigned u = __float_as_uint(v);
+    unsigned a, b;
+    if constexpr (H == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      a = r[0];
+      b = r[1];
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      a = r[0];
+      b = r[1];
+    }
+    return __builtin_fmaf(s, __uint_as_float(b), __uint_as_float(a));
+  }
+}
+
+__device__ __forceinline__ float lane_sign(int lane, int h) { return (lane & h) ? -1.0f : 1.0f; }
+
 // 128-point Sylvester Walsh-Hadamard transform (unscaled) across one wave:
 // element i of the block is v0 of lane i for i < 64 and v1 of lane i-64
-// otherwise. Butterflies: bit 6 inside the lane, bits 5..0 across lanes.
+// otherwise. Butterflies: bit 6 inside the lane, bits 0..5 across lanes.
+// The butterflies of different bits commute, so the order is free.
 __device__ __forceinline__ void fwht128(float& v0, float& v1) {
   const float a = v0 + v1;
   const float b = v0 - v1;
-  v0 = a;
-  v1 = b;
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) {
-    const float p0 = __shfl_xor(v0, h, 64);
-    const float p1 = __shfl_xor(v1, h, 64);
-    const bool upper = (lane & h) != 0;
-    v0 = upper ? (p0 - v0) : (v0 + p0);
-    v1 = upper ? (p1 - v1) : (v1 + p1);
+  const float s1 = lane_sign(lane, 1), s2 = lane_sign(lane, 2), s4 = lane_sign(lane, 4);
+  const float s8 = lane_sign(lane, 8), s16 = lane_sign(lane, 16), s32 = lane_sign(lane, 32);
+  v0 = butterfly<32>(butterfly<16>(butterfly<8>(butterfly<4>(butterfly<2>(butterfly<1>(a, s1), s2), s4), s8), s16), s32);
+  v1 = butterfly<32>(butterfly<16>(butterfly<8>(butterfly<4>(butterfly<2>(butterfly<1>(b, s1), s2), s4), s8), s16), s32);
+}
+
+// Sum over the 64 lanes; every lane gets the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += xor_lane<1>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<4>(v);
+  v += xor_lane<8>(v);
+  {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
+  {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return v;
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }

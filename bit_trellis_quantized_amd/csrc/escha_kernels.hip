@@ -56,13 +56,14 @@ __device__ __forceinline__ void mac_rows(const uint32_t (&raw)[NKT][Quarter<K>::
   }
 }
 
-// Sum the four quarter-lanes' column sums; every lane of the quad gets the
-// total. Lane q then owns output columns 4q..4q+3 of its tile.
+// Sum the four quarter-lanes' column sums (DPP inside each quad; all four
+// lanes get the same bits). Lane q then owns output columns 4q..4q+3 of its
+// tile, i.e. outputs 4*lane .. 4*lane+3 of the wave's 256.
 __device__ __forceinline__ float4 quad_reduce_pick(float (&acc)[16], int q) {
 #pragma unroll
   for (int n = 0; n < 16; ++n) {
-    acc[n] += __shfl_xor(acc[n], 1, 64);
-    acc[n] += __shfl_xor(acc[n], 2, 64);
+    acc[n] += xor_lane<1>(acc[n]);
+    acc[n] += xor_lane<2>(acc[n]);
   }
   float4 r;
   r.x = q == 0 ? acc[0] : q == 1 ? acc[4] : q == 2 ? acc[8] : acc[12];
@@ -76,10 +77,27 @@ __device__ __forceinline__ float4 f4add(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
+// Output transform of one 256-output group held in LDS (zs, in output
+// order): waves 0 and 1 each take one 128-block, apply H_n, multiply by
+// rout (and the weight wt) and store. out points at the group's first output.
+__device__ __forceinline__ void transform_store(const float* zs, const uint16_t* __restrict__ rout_g,
+                                                float wt, float* __restrict__ out, int wave,
+                                                int lane) {
+  if (wave < 2) {
+    float z0 = zs[128 * wave + lane];
+    float z1 = zs[128 * wave + lane + 64];
+    fwht128(z0, z1);
+    const uint16_t* ro = rout_g + 128 * wave;
+    out[128 * wave + lane] = z0 * kInvSqrt128 * f16_to_f32(ro[lane]) * wt;
+    out[128 * wave + lane + 64] = z1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]) * wt;
+  }
+}
+
 // ------------------------------------------------------------------------
-// gate_up (or any single projection) partial sums over one 128-input chunk.
-// grid.x = n_pairs * n_chunks * n_groups; block = 4 waves, wave w streams
-// tile-rows 8c+2w and 8c+2w+1 of the 16 output tiles of group g.
+// gate_up (or any single projection): transformed partial sums over one
+// 128-input chunk. grid.x = n_pairs * n_chunks * n_groups; block = 4 waves,
+// wave w streams tile-rows 8c+2w and 8c+2w+1 of the 16 output tiles of
+// group g.
 // ------------------------------------------------------------------------
 template <int K, bool FROM_Y>
 __global__ __launch_bounds__(256) void k_in_partial(InPartialArgs a) {
@@ -110,6 +128,7 @@ __global__ __launch_bounds__(256) void k_in_partial(InPartialArgs a) {
 
   // 2. rotated inputs of this chunk: x~ = H_n(rin (.) x)
   __shared__ __attribute__((aligned(16))) float xs[128];
+  __shared__ __attribute__((aligned(16))) float zs[256];
   __shared__ float4 red[4][64];
   if (wave == 0) {
     float x0, x1;
@@ -157,23 +176,25 @@ __global__ __launch_bounds__(256) void k_in_partial(InPartialArgs a) {
   red[wave][lane] = quad_reduce_pick(acc, q);
   __syncthreads();
 
-  // 4. fixed-order sum over the four waves
+  // 4. fixed-order sum over the four waves, then the output transform
   if (wave == 0) {
     float4 r = red[0][lane];
     r = f4add(r, red[1][lane]);
     r = f4add(r, red[2][lane]);
     r = f4add(r, red[3][lane]);
-    reinterpret_cast<float4*>(out)[lane] = r;
+    reinterpret_cast<float4*>(zs)[lane] = r;
   }
+  __syncthreads();
+  transform_store(zs, a.rout + (size_t)e * a.out_f + g * 256, 1.0f, out, wave, lane);
 }
 
 // ------------------------------------------------------------------------
-// down partial sums over one 128-channel chunk of the inter dimension.
-// grid.x = n_pairs * n_chunks * n_groups; block = 8 waves, wave w streams
-// tile-row 8c+w. Wave 0 finishes gate_up for the chunk's channels: reduce
-// the gate_up partials, H128, rout, SiLU(gate)*up; then rin and H128 of
-// down. A chunk whose 128 h values are all exactly zero (every channel
-// pruned) contributes exactly zero: its decode is skipped.
+// down: transformed, router-weighted partial sums over one 128-channel
+// chunk of the inter dimension. grid.x = n_pairs * n_chunks * n_groups;
+// block = 8 waves, wave w streams tile-row 8c+w. Wave 0 forms the chunk's
+// h = SiLU(gate) * up from gate_up's transformed partials, then rin and
+// H128 of down. A chunk whose 128 h values are all exactly zero (every
+// channel pruned) contributes exactly zero: its decode is skipped.
 // ------------------------------------------------------------------------
 template <int K>
 __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
@@ -204,6 +225,7 @@ __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
   issue_rows<K, 1>(code_e, n_nt, 8 * c + wave, nt, q, raw);
 
   __shared__ __attribute__((aligned(16))) float xs[128];
+  __shared__ __attribute__((aligned(16))) float zs[256];
   __shared__ float4 red[8][64];
   __shared__ int skip;
   if (wave == 0) {
@@ -217,13 +239,6 @@ __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
       u0 += b[inter + lane];
       u1 += b[inter + lane + 64];
     }
-    fwht128(g0, g1);
-    fwht128(u0, u1);
-    const uint16_t* ro = a.gu_rout + (size_t)e * g2 + 128 * c;
-    g0 = g0 * kInvSqrt128 * f16_to_f32(ro[lane]);
-    g1 = g1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
-    u0 = u0 * kInvSqrt128 * f16_to_f32(ro[inter + lane]);
-    u1 = u1 * kInvSqrt128 * f16_to_f32(ro[inter + lane + 64]);
     const float h0 = silu(g0) * u0;
     const float h1 = silu(g1) * u1;
     if (a.inter_out && g == 0) {
@@ -255,12 +270,15 @@ __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
     float4 r = red[0][lane];
 #pragma unroll
     for (int w = 1; w < 8; ++w) r = f4add(r, red[w][lane]);
-    reinterpret_cast<float4*>(out)[lane] = r;
+    reinterpret_cast<float4*>(zs)[lane] = r;
   }
+  __syncthreads();
+  const float wt = a.w ? a.w[p] : 1.0f;
+  transform_store(zs, a.rout + (size_t)e * a.out_f + g * 256, wt, out, wave, lane);
 }
 
 // ------------------------------------------------------------------------
-// Finish one projection per pair: reduce partials, H128, rout.
+// Finish one projection per pair: the fixed-order sum of its chunks.
 // grid.x = n_pairs * (out_f / 128), block = 64.
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
@@ -268,13 +286,6 @@ __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
   const int b = blockIdx.x % nb;
   const int p = blockIdx.x / nb;
   const int lane = threadIdx.x;
-  const int e = a.ids ? a.ids[p] : a.fixed_expert;
-  float* y = a.y + (size_t)p * a.out_f + 128 * b;
-  if (e < 0 || e >= a.n_experts) {
-    y[lane] = 0.f;
-    y[lane + 64] = 0.f;
-    return;
-  }
   float z0 = 0.f, z1 = 0.f;
   const float* pp = a.partial + (size_t)p * a.n_chunks * a.out_f + 128 * b;
 #pragma unroll 8
@@ -282,62 +293,33 @@ __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
     z0 += pp[(size_t)cc * a.out_f + lane];
     z1 += pp[(size_t)cc * a.out_f + lane + 64];
   }
-  fwht128(z0, z1);
-  const uint16_t* ro = a.rout + (size_t)e * a.out_f + 128 * b;
-  y[lane] = z0 * kInvSqrt128 * f16_to_f32(ro[lane]);
-  y[lane + 64] = z1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]);
+  float* y = a.y + (size_t)p * a.out_f + 128 * b;
+  y[lane] = z0;
+  y[lane + 64] = z1;
 }
 
 // ------------------------------------------------------------------------
-// Combine: one wave per (token, 128-block of hidden). For each slot: reduce
-// down's partials, H128, rout; then sum the slots in order, weighted by the
-// router probabilities. Also writes the block's sum of squares.
-// grid.x = n_tokens * (hidden / 128), block = 64.
+// Combine: one wave per (token, 128-block of hidden): the sum over slots (in
+// order) and chunks (in order) of down's weighted, transformed partials,
+// plus the block's sum of squares. grid.x = n_tokens * (hidden / 128).
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
-  constexpr int kBatch = 8;
   const int nb = a.hidden / 128;
   const int b = blockIdx.x % nb;
   const int t = blockIdx.x / nb;
   const int lane = threadIdx.x;
+  const int n = a.top_k * a.n_chunks;  // partial rows of this token, in order
+  const float* pp = a.partial + (size_t)t * n * a.hidden + 128 * b;
   float acc0 = 0.f, acc1 = 0.f;
-  for (int j0 = 0; j0 < a.top_k; j0 += kBatch) {
-    float z0[kBatch], z1[kBatch];
-    // all loads of the batch first, then the transforms
-#pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      z0[jj] = 0.f;
-      z1[jj] = 0.f;
-      const int j = j0 + jj;
-      if (j < a.top_k) {
-        const float* pp = a.partial + (size_t)(t * a.top_k + j) * a.n_chunks * a.hidden + 128 * b;
-        for (int cc = 0; cc < a.n_chunks; ++cc) {
-          z0[jj] += pp[(size_t)cc * a.hidden + lane];
-          z1[jj] += pp[(size_t)cc * a.hidden + lane + 64];
-        }
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < kBatch; ++jj) {
-      const int j = j0 + jj;
-      if (j >= a.top_k) break;
-      const int p = t * a.top_k + j;
-      const int e = a.ids[p];
-      if (e < 0 || e >= a.n_experts) continue;  // uniform over the wave
-      float v0 = z0[jj], v1 = z1[jj];
-      fwht128(v0, v1);
-      const uint16_t* ro = a.rout + (size_t)e * a.hidden + 128 * b;
-      const float wt = a.w[p];
-      acc0 = __builtin_fmaf(wt, v0 * kInvSqrt128 * f16_to_f32(ro[lane]), acc0);
-      acc1 = __builtin_fmaf(wt, v1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]), acc1);
-    }
+#pragma unroll 8
+  for (int r = 0; r < n; ++r) {
+    acc0 += pp[(size_t)r * a.hidden + lane];
+    acc1 += pp[(size_t)r * a.hidden + lane + 64];
   }
   float* y = a.y + (size_t)t * a.hidden + 128 * b;
   y[lane] = acc0;
   y[lane + 64] = acc1;
-  float ss = __builtin_fmaf(acc0, acc0, acc1 * acc1);
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
+  const float ss = wave_sum(__builtin_fmaf(acc0, acc0, acc1 * acc1));
   if (lane == 0) a.ss[(size_t)t * nb + b] = ss;
 }
 
@@ -356,9 +338,7 @@ __global__ __launch_bounds__(1024) void k_rmsnorm_bf16(const float* __restrict__
   const float* yr = y + (size_t)blockIdx.x * n;
   for (int b = wave; b < nb; b += 16) {
     const float a0 = yr[128 * b + lane], a1 = yr[128 * b + lane + 64];
-    float ss = __builtin_fmaf(a0, a0, a1 * a1);
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) ss += __shfl_xor(ss, h, 64);
+    const float ss = wave_sum(__builtin_fmaf(a0, a0, a1 * a1));
     if (lane == 0) block_ss[b] = ss;
   }
   __syncthreads();

@@ -9,15 +9,19 @@
 
 namespace escha {
 
-// Partial sums of a projection. Pair p uses token p / top_k and expert ids[p]
-// (or fixed_expert when ids is null). The input row is either bf16 (x_bf16)
-// or, when x_bf16 is null, the previous layer's fp32 output y_prev with its
-// per-128-block sums of squares ss_prev: the kernel applies the RMSNorm
-// (unit weight, eps) and rounds to bf16 itself, and writes those bf16 rows
-// to x_out when x_out is not null. partial: fp32 [n_pairs][in_f/128][out_f].
+// Output-transformed partial sums of a projection: for each 128-input chunk c,
+// partial[p][c] = rout (.) H_n(W~[:, chunk c] x~[chunk c]); the projection's
+// output is the fixed-order sum over c. Pair p uses token p / top_k and
+// expert ids[p] (or fixed_expert when ids is null). The input row is either
+// bf16 (x_bf16) or, when x_bf16 is null, the previous layer's fp32 output
+// y_prev with its per-128-block sums of squares ss_prev: the kernel applies
+// the RMSNorm (unit weight, eps) and rounds to bf16 itself, and writes those
+// bf16 rows to x_out when x_out is not null. partial: fp32
+// [n_pairs][in_f/128][out_f].
 struct InPartialArgs {
   const uint16_t* code;
   const uint16_t* rin;
+  const uint16_t* rout;
   int32_t n_experts, in_f, out_f, n_pairs, top_k;
   const int32_t* ids;
   int32_t fixed_expert;
@@ -29,41 +33,36 @@ struct InPartialArgs {
   float* partial;
 };
 
-// Partial sums of down_proj; the input h is produced from gate_up's partials
-// (gu_partial fp32 [n_pairs][gu_chunks][2*in_f]). inter_out nullable.
+// Output-transformed partial sums of down_proj, already weighted by the
+// router probability w[p] (w may be null: weight 1). The input h comes from
+// gate_up's transformed partials (gu_partial fp32 [n_pairs][gu_chunks][2*in_f]):
+// h = SiLU(sum gate) * (sum up). inter_out (nullable) receives h.
 struct DownPartialArgs {
   const uint16_t* code;
   const uint16_t* rin;
+  const uint16_t* rout;
   int32_t n_experts, in_f, out_f, n_pairs;
   const int32_t* ids;
+  const float* w;
   const float* gu_partial;
   int32_t gu_chunks;
-  const uint16_t* gu_rout;
   float* inter_out;
   float* partial;
 };
 
-// y[p] = rout (.) H_n(sum of partials) for one projection per pair.
+// y[p] = sum over the chunks of a pair's transformed partials.
 struct FinishArgs {
   const float* partial;
-  int32_t n_chunks;
-  const uint16_t* rout;
-  int32_t n_experts, out_f, n_pairs;
-  const int32_t* ids;
-  int32_t fixed_expert;
+  int32_t n_chunks, out_f, n_pairs;
   float* y;
 };
 
-// Per-token weighted slot sum of down outputs. y fp32 [n_tokens][hidden];
-// ss fp32 [n_tokens][hidden/128] receives each 128-block's sum of squares
-// (the next layer's RMSNorm).
+// Per-token sum over slots (in order) and chunks of down's weighted partials.
+// y fp32 [n_tokens][hidden]; ss fp32 [n_tokens][hidden/128] receives each
+// 128-block's sum of squares (the next layer's RMSNorm).
 struct CombineArgs {
   const float* partial;
-  int32_t n_chunks;
-  const uint16_t* rout;
-  const int32_t* ids;
-  const float* w;
-  int32_t n_experts, hidden, top_k, n_tokens;
+  int32_t n_chunks, hidden, top_k, n_tokens;
   float* y;
   float* ss;
 };
