@@ -48,6 +48,14 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
+    ap.add_argument("--workload", choices=["stack", "layer"], default="stack",
+                    help="stack: the 40-layer decode (default); layer: one MoE layer call")
+    ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5],
+                    help="layer workload: 2 = batch-1 decode, 3 = 64 tokens Zipf, 5 = 4096-token prefill")
+    ap.add_argument("--entry", choices=["decode", "prefill"], default=None,
+                    help="layer workload: entry point (default: prefill for config 5, else decode)")
+    ap.add_argument("--distinct-layers", type=int, default=8,
+                    help="layer workload: distinct layers cycled (defeats the 256 MB Infinity Cache)")
     return ap.parse_args()
 
 
@@ -128,6 +136,80 @@ def cpu_baseline(synth, n_layers, x0, logits, threads, log):
     return t_oracle, used, first
 
 
+def layer_workload(args, log):
+    """One MoE layer per step (configs 2, 3 or 5), cycling over distinct layers."""
+    import torch
+    from bit_trellis_quantized_amd import escha, synth
+
+    cfg = args.config
+    T = {2: 1, 3: 64, 5: 4096}[cfg]
+    entry = args.entry or ("prefill" if cfg == 5 else "decode")
+    fn = escha.escha_moe_layer_prefill if entry == "prefill" else escha.escha_moe_layer_decode
+    NLw, k = args.distinct_layers, synth.TOP_K
+    hip = Hip()
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    layers = []
+    for l in range(NLw):
+        L = synth.layer_tensors(cfg, l)
+        layers.append(escha.MoeLayer(escha.Proj(dev(L["gu_code"]), dev(L["gu_rin"]), dev(L["gu_rout"])),
+                                     escha.Proj(dev(L["dn_code"]), dev(L["dn_rin"]), dev(L["dn_rout"])), k))
+    log(f"{NLw} layers resident")
+    ws = torch.empty(escha.escha_moe_workspace_bytes(layers[0], T, entry == "prefill"),
+                     dtype=torch.uint8, device="cuda")
+    pool = []
+    for l in range(NLw):
+        x = synth.activations(cfg, T, synth.HIDDEN, layer=l)
+        logits = (synth.zipf_logits(cfg, T, layer=l) if cfg == 3 else synth.normal_logits(cfg, T, layer=l))
+        pool.append(dict(x=dev(x), logits=torch.from_numpy(logits).cuda(),
+                         y=torch.empty(T, synth.HIDDEN, dtype=torch.float32, device="cuda"),
+                         ev=(hip.event(), hip.event())))
+
+    def step(i):
+        p = pool[i % NLw]
+        ids, w = escha.escha_route_topk(p["logits"], k)
+        p["ids"], p["w"] = ids, w
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        hip.lib.hipEventRecord(ctypes.c_void_p(p["ev"][0]), stream)
+        fn(layers[i % NLw], p["x"], ids, w, out=p["y"], workspace=ws)
+        hip.lib.hipEventRecord(ctypes.c_void_p(p["ev"][1]), stream)
+
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, stop = hip.event(), hip.event()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    t_wall = time.perf_counter()
+    hip.lib.hipEventRecord(ctypes.c_void_p(start), stream)
+    for i in range(args.steps):
+        step(i)
+    hip.lib.hipEventRecord(ctypes.c_void_p(stop), stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = hip.elapsed_ms(start, stop) / args.steps
+    layer_ms = float(np.mean([hip.elapsed_ms(*p["ev"]) for p in pool]))
+    distinct = np.mean([len(set(p["ids"].cpu().numpy().ravel().tolist())) for p in pool])
+    code_bytes = distinct * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR)
+    flops = 2.0 * T * k * (2048 * 1024 + 512 * 2048)
+    out = {
+        "metric": "MoE-layer decode tokens/s at batch 1/8/64 + achieved HBM GB/s vs peak",
+        "value": round(T / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp16-decode/fp32-acc",
+        "data": "synthetic", "config": {"workload": f"one MoE layer, config {cfg}, T={T}, entry={entry}, "
+                                                    f"{NLw} distinct layers cycled"},
+        "layer_us": round(layer_ms * 1e3, 2),
+        "code_gbs": round(code_bytes / (layer_ms / 1e3) / 1e9, 1),
+        "distinct_experts": float(distinct),
+        "tflops": round(flops / (layer_ms / 1e3) / 1e12, 2),
+        "wall_ms_per_step": round(t_wall / args.steps * 1e3, 4),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -142,6 +224,9 @@ def main():
     from bit_trellis_quantized_amd import escha, synth
 
     torch.cuda.set_device(0)
+    if args.workload == "layer":
+        layer_workload(args, log)
+        return
     T, NL, R = args.batch, args.layers, args.pool
     hidden, E, k = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K
 

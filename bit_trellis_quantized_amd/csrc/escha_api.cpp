@@ -70,6 +70,8 @@ int check_layer(const escha_moe_layer_t* L) {
   if (L->hidden > kMaxHidden) return fail(ESCHA_E_UNSUPPORTED, "hidden=%d > %d", L->hidden, kMaxHidden);
   if (L->top_k < 1 || L->top_k > kMaxTopK || L->top_k > L->gate_up.n_experts)
     return fail(ESCHA_E_ARG, "top_k=%d out of range", L->top_k);
+  if (L->gate_up.n_experts > kMaxExpertsRoute)
+    return fail(ESCHA_E_UNSUPPORTED, "n_experts=%d > %d", L->gate_up.n_experts, kMaxExpertsRoute);
   return ESCHA_OK;
 }
 
@@ -171,8 +173,105 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   return ESCHA_OK;
 }
 
-// Token batch of the streaming path used by the prefill entry point.
-constexpr int32_t kPrefillBatch = 64;
+// ---------------------------------------------------------------- grouped ws
+constexpr int32_t kTileTokens = 128;  // tokens per grouped tile (escha_grouped.hip)
+
+int32_t grouped_max_tiles(const escha_moe_layer_t* L, int64_t T) {
+  const int64_t P = T * L->top_k;
+  return (int32_t)((P + kTileTokens - 1) / kTileTokens + L->gate_up.n_experts);
+}
+
+struct GroupedWs {
+  int32_t *hist, *base, *rank;          // grouping scratch
+  int32_t *counts, *offsets, *perm, *inv;
+  int32_t *t_expert, *t_row0, *t_rows, *n_tiles;
+  uint16_t* xg;  // fp16 [P][hidden]
+  uint16_t* xd;  // fp16 [P][inter]
+  float* yd;     // fp32 [P][hidden]
+};
+
+// Carves the grouped workspace; with ws == nullptr only sizes it.
+size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* out) {
+  const int64_t P = T * L->top_k;
+  const int E = L->gate_up.n_experts;
+  const int32_t mt = grouped_max_tiles(L, T);
+  const size_t chunks = ((size_t)P + 63) / 64;
+  size_t off = 0;
+  char* b = (char*)ws;
+  auto take = [&](size_t bytes) {
+    char* p = b ? b + off : nullptr;
+    off += round_up(bytes);
+    return p;
+  };
+  GroupedWs g{};
+  g.hist = (int32_t*)take(chunks * E * sizeof(int32_t));
+  g.base = (int32_t*)take(chunks * E * sizeof(int32_t));
+  g.rank = (int32_t*)take((size_t)P * sizeof(int32_t));
+  g.counts = (int32_t*)take((size_t)E * sizeof(int32_t));
+  g.offsets = (int32_t*)take((size_t)(E + 1) * sizeof(int32_t));
+  g.perm = (int32_t*)take((size_t)P * sizeof(int32_t));
+  g.inv = (int32_t*)take((size_t)P * sizeof(int32_t));
+  g.t_expert = (int32_t*)take((size_t)mt * sizeof(int32_t));
+  g.t_row0 = (int32_t*)take((size_t)mt * sizeof(int32_t));
+  g.t_rows = (int32_t*)take((size_t)mt * sizeof(int32_t));
+  g.n_tiles = (int32_t*)take(sizeof(int32_t));
+  g.xg = (uint16_t*)take((size_t)P * L->hidden * sizeof(uint16_t));
+  g.xd = (uint16_t*)take((size_t)P * L->inter * sizeof(uint16_t));
+  g.yd = (float*)take((size_t)P * L->hidden * sizeof(float));
+  if (out) *out = g;
+  return off;
+}
+
+// One layer over T tokens through the grouped kernels: group the pairs by
+// expert, decode every weight tile once per tile of <= 64 tokens of its
+// expert, contract on the matrix cores, combine in slot order.
+int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
+                      const float* w, float* y, float* inter_out, const GroupedWs& g,
+                      hipStream_t s) {
+  const int P = T * L->top_k;
+  const int E = L->gate_up.n_experts;
+  const int32_t max_tiles = grouped_max_tiles(L, T);
+  hipError_t e = escha::launch_group(ids, P, E, g.counts, g.offsets, g.perm, g.inv, g.hist, g.base,
+                                     g.rank, s);
+  if (e != hipSuccess) return hip_fail(e, "group launch");
+  e = escha::launch_make_tiles(g.offsets, E, max_tiles, g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s);
+  if (e != hipSuccess) return hip_fail(e, "tile list launch");
+  escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
+                       L->top_k, g.xg};
+  e = escha::launch_xin_gather(ga, P, s);
+  if (e != hipSuccess) return hip_fail(e, "input gather launch");
+  escha::GroupedArgs gu{};
+  gu.code = (const uint16_t*)L->gate_up.code;
+  gu.rout = (const uint16_t*)L->gate_up.rout;
+  gu.rin2 = (const uint16_t*)L->down.rin;
+  gu.hidden = L->hidden;
+  gu.inter = L->inter;
+  gu.x_in = g.xg;
+  gu.x_out = g.xd;
+  gu.inter_out = inter_out;
+  gu.perm = g.perm;
+  gu.w = w;
+  gu.t_expert = g.t_expert;
+  gu.t_row0 = g.t_row0;
+  gu.t_rows = g.t_rows;
+  gu.n_tiles = g.n_tiles;
+  e = escha::launch_grouped_gate_up(gu, max_tiles, L->gate_up.k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "grouped gate_up launch");
+  escha::GroupedArgs dn = gu;
+  dn.code = (const uint16_t*)L->down.code;
+  dn.rout = (const uint16_t*)L->down.rout;
+  dn.rin2 = nullptr;
+  dn.x_in = g.xd;
+  dn.x_out = nullptr;
+  dn.y_out = g.yd;
+  dn.inter_out = nullptr;
+  e = escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "grouped down launch");
+  escha::SortedCombineArgs c{g.yd, g.inv, L->hidden, L->top_k, T, y, nullptr};
+  e = escha::launch_combine_sorted(c, s);
+  if (e != hipSuccess) return hip_fail(e, "sorted combine launch");
+  return ESCHA_OK;
+}
 
 int check_layer_call(const escha_moe_layer_t* L, const uint16_t* x, int32_t T, const int32_t* ids,
                      const float* w, const float* y) {
@@ -248,8 +347,8 @@ int escha_moe_group(const int32_t* topk_ids, int32_t n_tokens, int32_t top_k, in
   int32_t* hist = (int32_t*)b;
   int32_t* base = (int32_t*)(b + round_up(chunks * n_experts * sizeof(int32_t)));
   int32_t* rank = (int32_t*)(b + 2 * round_up(chunks * n_experts * sizeof(int32_t)));
-  hipError_t e = escha::launch_group(topk_ids, P, n_experts, counts, offsets, perm, hist, base,
-                                     rank, (hipStream_t)stream);
+  hipError_t e = escha::launch_group(topk_ids, P, n_experts, counts, offsets, perm, nullptr, hist,
+                                     base, rank, (hipStream_t)stream);
   return e == hipSuccess ? ESCHA_OK : hip_fail(e, "group launch");
 }
 
@@ -299,8 +398,8 @@ int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_b
 
 size_t escha_moe_workspace_bytes(const escha_moe_layer_t* L, int32_t n_tokens, int32_t prefill) {
   if (!L || n_tokens < 0 || L->top_k < 1 || L->hidden < 128 || L->inter < 128) return 0;
-  const int64_t T = prefill ? (n_tokens < kPrefillBatch ? n_tokens : kPrefillBatch) : n_tokens;
-  return decode_ws_bytes(L, T);
+  if (prefill) return grouped_ws(L, n_tokens, nullptr, nullptr);
+  return decode_ws_bytes(L, n_tokens);
 }
 
 int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
@@ -329,18 +428,10 @@ int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, 
   const size_t need = escha_moe_workspace_bytes(L, n_tokens, 1);
   if (!workspace || workspace_bytes < need)
     return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-  const int k = L->top_k;
-  for (int32_t t0 = 0; t0 < n_tokens; t0 += kPrefillBatch) {
-    const int32_t nt = n_tokens - t0 < kPrefillBatch ? n_tokens - t0 : kPrefillBatch;
-    const DecodeWs ws = decode_ws_carve(L, nt, workspace);
-    const LayerInput in{x_bf16 + (size_t)t0 * L->hidden, nullptr, nullptr, 0.f, nullptr};
-    rc = run_layer_decode(L, in, nt, topk_ids + (size_t)t0 * k, topk_w + (size_t)t0 * k,
-                          y + (size_t)t0 * L->hidden,
-                          inter_out ? inter_out + (size_t)t0 * k * L->inter : nullptr, ws,
-                          (hipStream_t)stream);
-    if (rc) return rc;
-  }
-  return ESCHA_OK;
+  GroupedWs g;
+  grouped_ws(L, n_tokens, workspace, &g);
+  return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g,
+                           (hipStream_t)stream);
 }
 
 int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, float eps, uint16_t* x_bf16,

@@ -1,0 +1,493 @@
+// escha_grouped.hip -- the grouped path: pairs sorted by expert, each weight
+// tile decoded once per tile of up to 64 tokens of the same expert (into
+// LDS, as fp16) and contracted on the matrix cores (v_mfma_f32_32x32x16_f16,
+// fp32 accumulate). Used by the prefill entry point and by decode calls
+// with enough tokens.
+//
+// Sources: hipfire PR "Escha-W2 port: 2-bit trellis decoded in the GEMV",
+// grouped-GEMM notes (expert_offsets + permutation; each weight tile
+// decoded once and reused by several activation tiles). Activations enter
+// the contraction as fp16 (the decoded weights are exactly fp16).
+//
+// Layout in one work-group (8 waves):
+//  - waves 0-3 decode: lane = 4*tile + q, tile = 16*kt_local + nt_local: 64
+//    tiles (4 tile-rows x 16 output tiles) = one 64-input step for 256
+//    outputs, written to LDS one step ahead of the matrix waves;
+//  - LDS W fp16 in 16-byte k-chunks: element (row, k) of a step sits at
+//    halves ((k/8)*256 + pi(row))*8 + k%8, pi(row) = row ^ ((row>>4) & 15).
+//    A decode store (16 output tiles, rows 16 apart) then hits 16 distinct
+//    16-byte slots, and an MFMA operand read (32 consecutive rows) uses each
+//    slot exactly twice. Two buffers, one barrier per step;
+//  - the decoder waves also stage the step's activation tile (fp16,
+//    [k/8][token][8]) in LDS; codes and activations are issued two steps
+//    ahead of their use;
+//  - waves 4-7 run the matrix cores on the current step from LDS, so decode
+//    (VALU) and contraction (MFMA) overlap on every SIMD;
+//  - wave (wo, wt) owns outputs 128wo..128wo+127 (four 32-row MFMA tiles)
+//    for tokens 64wt..64wt+63 (two 32-token MFMA tiles): 8 accumulators of
+//    16 fp32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "escha_device.hpp"
+#include "escha_launch.hpp"
+
+namespace escha {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTM = 128;         // tokens per tile
+constexpr int kStep = 64;        // inputs per step (4 tile-rows)
+constexpr int kWBuf = 256 * kStep;  // halves per W buffer (32 KiB)
+constexpr int kXBuf = kTM * kStep;  // halves per activation buffer (16 KiB)
+constexpr int kSmemBytes = 2 * (kWBuf + kXBuf) * 2;  // 96 KiB; the epilogue reuses it
+constexpr int kEPitch = 257;     // LDS row pitch of the epilogue (floats)
+
+// ------------------------------------------------------------------------
+// Tile list: for every expert, ceil(count / 64) tiles of consecutive sorted
+// pairs. One block of 1024 threads; n_experts <= 1024.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__ offsets, int E,
+                                                     int max_tiles, int32_t* __restrict__ t_expert,
+                                                     int32_t* __restrict__ t_row0,
+                                                     int32_t* __restrict__ t_rows,
+                                                     int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t scan[1024];
+  const int e = threadIdx.x;
+  int32_t cnt = 0, nt = 0;
+  if (e < E) {
+    cnt = offsets[e + 1] - offsets[e];
+    nt = (cnt + kTM - 1) / kTM;
+  }
+  scan[e] = nt;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan
+    const int32_t v = e >= d ? scan[e - d] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  const int32_t base = scan[e] - nt;
+  for (int i = 0; i < nt; ++i) {
+    const int32_t ti = base + i;
+    if (ti < max_tiles) {
+      t_expert[ti] = e;
+      t_row0[ti] = offsets[e] + i * kTM;
+      t_rows[ti] = cnt - i * kTM < kTM ? cnt - i * kTM : kTM;
+    }
+  }
+  if (e == 1023) *n_tiles = scan[1023] < max_tiles ? scan[1023] : max_tiles;
+}
+
+// ------------------------------------------------------------------------
+// Rotated gate_up inputs per sorted pair: Xg[i] = fp16(H_n(rin_e (.) x_t)).
+// grid.x = n_pairs, block = 256 (wave w handles blocks w, w+4, ..).
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
+  const int i = blockIdx.x;
+  if (i >= a.offsets[a.n_experts]) return;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int p = a.perm[i];
+  const int e = a.ids[p];
+  const int t = p / a.top_k;
+  for (int b = wave; b < a.hidden / 128; b += 4) {
+    const uint16_t* xr = a.x_bf16 + (size_t)t * a.hidden + 128 * b;
+    const uint16_t* rr = a.rin + (size_t)e * a.hidden + 128 * b;
+    float v0 = bf16_to_f32(xr[lane]) * f16_to_f32(rr[lane]);
+    float v1 = bf16_to_f32(xr[lane + 64]) * f16_to_f32(rr[lane + 64]);
+    fwht128(v0, v1);
+    _Float16* xo = reinterpret_cast<_Float16*>(a.xg) + (size_t)i * a.hidden + 128 * b;
+    xo[lane] = (_Float16)(v0 * kInvSqrt128);
+    xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+  }
+}
+
+// ------------------------------------------------------------------------
+// Shared main loop: acc[mt][tt] += W[256 outputs][K] * X[128 tokens][K]^T.
+// Wave (wo, wt) = (wave >> 1, wave & 1) owns outputs 128*wo + 32*mt (mt 0..3)
+// and tokens 64*wt + 32*tt (tt 0..1). Step s's matrix-core work is issued
+// in the same loop body as the decode of step s+1 (into the other LDS
+// buffer), so the VALU decode and the MFMAs overlap; codes run two steps
+// and activations one step ahead.
+// out_tile(j) maps the local output tile j (0..15) to its global tile index.
+// ------------------------------------------------------------------------
+template <int K>
+__device__ __forceinline__ void decode_to_lds(const uint32_t (&raw)[Quarter<K>::kOwn], int dkt,
+                                              int dnt, int q, _Float16* wb) {
+  constexpr int kOwn = Quarter<K>::kOwn;
+  uint32_t d[kOwn + 1];
+#pragma unroll
+  for (int i = 0; i < kOwn; ++i) d[i] = raw[i];
+  d[kOwn] = next_quarter_dword(raw[0]);
+  uint32_t lo[8][2], hi[8][2];  // rows n and n+8: k pairs (0,1) and (2,3)
+  decode_quarter<K>(d, [&](int kk, int n, h16x2 w) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, w);
+    if (kk & 1) {
+      lo[n][kk >> 1] = __builtin_amdgcn_perm(bits, lo[n][kk >> 1], 0x05040100u);
+      hi[n][kk >> 1] = __builtin_amdgcn_perm(bits, hi[n][kk >> 1], 0x07060100u);
+    } else {
+      lo[n][kk >> 1] = bits;
+      hi[n][kk >> 1] = bits >> 16;
+    }
+  });
+  // rows 16*dnt + n and 16*dnt + n + 8, inputs 16*dkt + 4q .. +3 (one 8-byte half-chunk)
+  _Float16* chunk = wb + (2 * dkt + (q >> 1)) * (256 * 8) + 4 * (q & 1);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    *reinterpret_cast<uint2*>(chunk + (16 * dnt + (n ^ dnt)) * 8) = make_uint2(lo[n][0], lo[n][1]);
+    *reinterpret_cast<uint2*>(chunk + (16 * dnt + ((n + 8) ^ dnt)) * 8) =
+        make_uint2(hi[n][0], hi[n][1]);
+  }
+}
+
+// One step's operands as held by a decoder lane between issue and use: its
+// quarter of one code tile and four 16-byte chunks of the activation tile.
+template <int K>
+struct StepLoads {
+  uint32_t raw[Quarter<K>::kOwn];
+  h8 x[4];
+};
+
+// The matrix waves' part of every step: NT live 32-token sub-tiles (1 or 2)
+// against four 32-row output tiles; operands of sub-step ks+1 are read from
+// LDS while sub-step ks's MFMAs issue. One barrier per step, matching the
+// decoder waves'.
+template <int NT>
+__device__ __forceinline__ void mma_steps(const _Float16* wl, const _Float16* xl, int n_steps, int wo,
+                                          int wt, int lane, f32x16 (&acc)[4][2]) {
+  constexpr int kKs = kStep / 16;
+  const int l32 = lane & 31;
+  const int khi = lane >> 5;
+  int prow[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int row = 128 * wo + 32 * mt + l32;
+    prow[mt] = row ^ ((row >> 4) & 15);
+  }
+  for (int s = 0; s < n_steps; ++s) {
+    const _Float16* wb = wl + (s & 1) * kWBuf;
+    const _Float16* xb = xl + (s & 1) * kXBuf;
+    auto load_ops = [&](int ks, h8 (&a)[4], h8 (&b)[2]) {
+      const int kc = 2 * ks + khi;
+#pragma unroll
+      for (int tt = 0; tt < NT; ++tt)
+        b[tt] = *reinterpret_cast<const h8*>(xb + (kc * kTM + 64 * wt + 32 * tt + l32) * 8);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const h8*>(wb + (kc * 256 + prow[mt]) * 8);
+    };
+    h8 a0[4], b0[2], a1[4], b1[2];
+    load_ops(0, a0, b0);
+#pragma unroll
+    for (int ks = 0; ks < kKs; ks += 2) {
+      load_ops(ks + 1, a1, b1);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          acc[mt][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mt], b0[tt], acc[mt][tt], 0, 0, 0);
+      if (ks + 2 < kKs) load_ops(ks + 2, a0, b0);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          acc[mt][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mt], b1[tt], acc[mt][tt], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+}
+
+template <int K, class OutTile>
+__device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ code_e, int n_nt,
+                                                 int in_f, const _Float16* __restrict__ X,
+                                                 int x_pitch, int row0, int rows, OutTile out_tile,
+                                                 _Float16* wl, _Float16* xl,
+                                                 f32x16 (&acc)[4][2]) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform per wave
+  const int lane = tid & 63;
+  const bool decoder = wave < 4;
+  const int n_steps = in_f / kStep;
+
+  if (decoder) {
+    // waves 0-3: codes and activations of step s+2 are issued at step s
+    // (two steps of latency cover); at step s the lane decodes step s+1's
+    // quarter tile into W and copies its activation chunks into the X tile.
+    const int q = tid & 3;
+    const int dtile = tid >> 2;
+    const int dkt = dtile >> 4;  // tile-row inside the step
+    const int dnt = dtile & 15;  // output tile inside the group
+    const int gnt = out_tile(dnt);
+    const int xtok = tid & 127;        // activation row of this lane
+    const int xkc0 = 4 * (tid >> 7);   // first of its four 16-byte k-chunks
+    const _Float16* xrow = X + (size_t)(row0 + (xtok < rows ? xtok : rows - 1)) * x_pitch + 8 * xkc0;
+    auto issue = [&](int s, StepLoads<K>& L) {
+      load_quarter<K>(code_e + ((size_t)(4 * s + dkt) * n_nt + gnt) * (16 * K) + q * (4 * K), L.raw);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) L.x[j] = *reinterpret_cast<const h8*>(xrow + s * kStep + 8 * j);
+    };
+    auto consume = [&](int s, const StepLoads<K>& L) {
+      decode_to_lds<K>(L.raw, dkt, dnt, q, wl + (s & 1) * kWBuf);
+      _Float16* xb = xl + (s & 1) * kXBuf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<h8*>(xb + ((xkc0 + j) * kTM + xtok) * 8) = L.x[j];
+    };
+    StepLoads<K> ring[2];
+    issue(0, ring[0]);
+    if (n_steps > 1) issue(1, ring[1]);
+    consume(0, ring[0]);
+    if (n_steps > 2) issue(2, ring[0]);
+    __syncthreads();
+    // step s consumes ring[(s+1)&1] (issued two steps earlier) and reuses it
+    for (int s = 0; s < n_steps; s += 2) {
+      if (s + 1 < n_steps) {
+        consume(s + 1, ring[1]);
+        if (s + 3 < n_steps) issue(s + 3, ring[1]);
+      }
+      __syncthreads();
+      if (s + 1 < n_steps) {
+        if (s + 2 < n_steps) {
+          consume(s + 2, ring[0]);
+          if (s + 4 < n_steps) issue(s + 4, ring[0]);
+        }
+        __syncthreads();
+      }
+    }
+  } else {
+    // waves 4-7: matrix cores on step s from LDS. (wo, wt): outputs
+    // 128*wo + 32*mt, tokens 64*wt + 32*tt. Token sub-tiles without a real
+    // token are skipped (uniform per wave); padded columns of a live
+    // sub-tile hold a clamped row and are never stored.
+    const int mw = wave - 4;
+    const int wo = mw >> 1, wt = mw & 1;
+    const int live = 64 * wt + 32 < rows ? 2 : (64 * wt < rows ? 1 : 0);
+    __syncthreads();
+    if (live == 2)
+      mma_steps<2>(wl, xl, n_steps, wo, wt, lane, acc);
+    else if (live == 1)
+      mma_steps<1>(wl, xl, n_steps, wo, wt, lane, acc);
+    else
+      for (int s = 0; s < n_steps; ++s) __syncthreads();
+  }
+}
+
+// Accumulators of the matrix waves with token half wt == h -> LDS E[64
+// tokens][256 outputs] (fp32).
+__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el, int h) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (wave < 4) return;
+  const int wo = (wave - 4) >> 1, wt = (wave - 4) & 1;
+  if (wt != h) return;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row in the 32x32 tile
+        const int j = lane & 31;                                  // column (token)
+        el[(32 * tt + j) * kEPitch + 128 * wo + 32 * mt + i] = acc[mt][tt][r];
+      }
+}
+
+// ------------------------------------------------------------------------
+// gate_up, grouped. grid.x = max_tiles * (inter / 128), block = 256.
+// A work-group takes the gate rows and the up rows of one 128-channel block
+// c (256 outputs) for one tile; its epilogue finishes h = SiLU(gate) * up
+// for those channels and writes down's rotated fp16 input block c.
+// ------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(512) void k_grouped_gate_up(GroupedArgs a) {
+  const int nb = a.inter / 128;
+  const int c = blockIdx.x % nb;
+  const int tile = blockIdx.x / nb;
+  if (tile >= *a.n_tiles) return;  // uniform
+  const int e = a.t_expert[tile];
+  const int row0 = a.t_row0[tile];
+  const int rows = a.t_rows[tile];
+  const int n_nt = 2 * a.inter / 16;
+  const int gate_nt0 = 8 * c, up_nt0 = a.inter / 16 + 8 * c;
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.hidden / 16) * n_nt * (16 * K);
+
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  _Float16* wl = reinterpret_cast<_Float16*>(smem);
+  _Float16* xl = wl + 2 * kWBuf;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][tt][r] = 0.f;
+  grouped_mainloop<K>(code_e, n_nt, a.hidden, reinterpret_cast<const _Float16*>(a.x_in), a.hidden,
+                      row0, rows,
+                      [&](int j) { return j < 8 ? gate_nt0 + j : up_nt0 + j - 8; }, wl, xl, acc);
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* rg = a.rout + (size_t)e * (2 * a.inter) + 128 * c;
+  const uint16_t* ru = rg + a.inter;
+  const uint16_t* rd = a.rin2 + (size_t)e * a.inter + 128 * c;
+  const float rg0 = f16_to_f32(rg[lane]), rg1 = f16_to_f32(rg[lane + 64]);
+  const float ru0 = f16_to_f32(ru[lane]), ru1 = f16_to_f32(ru[lane + 64]);
+  const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
+  float* el = reinterpret_cast<float*>(smem);
+  for (int h = 0; h < 2; ++h) {  // token halves of the tile
+    acc_to_lds(acc, el, h);
+    __syncthreads();
+    for (int tl = 8 * wave; tl < 8 * wave + 8; ++tl) {
+      const int tok = 64 * h + tl;
+      if (tok >= rows) break;  // uniform over the wave
+      const float* er = el + tl * kEPitch;
+      float g0 = er[lane], g1 = er[lane + 64], u0 = er[128 + lane], u1 = er[192 + lane];
+      fwht128(g0, g1);
+      fwht128(u0, u1);
+      g0 *= kInvSqrt128 * rg0;
+      g1 *= kInvSqrt128 * rg1;
+      u0 *= kInvSqrt128 * ru0;
+      u1 *= kInvSqrt128 * ru1;
+      const float h0 = silu(g0) * u0;
+      const float h1 = silu(g1) * u1;
+      const int i = row0 + tok;
+      if (a.inter_out) {
+        float* io = a.inter_out + (size_t)a.perm[i] * a.inter + 128 * c;
+        io[lane] = h0;
+        io[lane + 64] = h1;
+      }
+      float v0 = h0 * rd0, v1 = h1 * rd1;
+      fwht128(v0, v1);
+      _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
+      xo[lane] = (_Float16)(v0 * kInvSqrt128);
+      xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------
+// down, grouped. grid.x = max_tiles * (hidden / 256), block = 256. The
+// epilogue applies H_n, rout and the pair's router weight and stores the
+// pair's 256 outputs (fp32) at its sorted index.
+// ------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(512) void k_grouped_down(GroupedArgs a) {
+  const int ng = a.hidden / 256;
+  const int r = blockIdx.x % ng;
+  const int tile = blockIdx.x / ng;
+  if (tile >= *a.n_tiles) return;
+  const int e = a.t_expert[tile];
+  const int row0 = a.t_row0[tile];
+  const int rows = a.t_rows[tile];
+  const int n_nt = a.hidden / 16;
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.inter / 16) * n_nt * (16 * K);
+
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  _Float16* wl = reinterpret_cast<_Float16*>(smem);
+  _Float16* xl = wl + 2 * kWBuf;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mt][tt][q] = 0.f;
+  grouped_mainloop<K>(code_e, n_nt, a.inter, reinterpret_cast<const _Float16*>(a.x_in), a.inter,
+                      row0, rows, [&](int j) { return 16 * r + j; }, wl, xl, acc);
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* ro = a.rout + (size_t)e * a.hidden + 256 * r;
+  const float r00 = f16_to_f32(ro[lane]), r01 = f16_to_f32(ro[lane + 64]);
+  const float r10 = f16_to_f32(ro[128 + lane]), r11 = f16_to_f32(ro[192 + lane]);
+  float* el = reinterpret_cast<float*>(smem);
+  for (int h = 0; h < 2; ++h) {
+    acc_to_lds(acc, el, h);
+    __syncthreads();
+    for (int tl = 8 * wave; tl < 8 * wave + 8; ++tl) {
+      const int tok = 64 * h + tl;
+      if (tok >= rows) break;
+      const int i = row0 + tok;
+      const float wt = a.w[a.perm[i]];
+      const float* er = el + tl * kEPitch;
+      float z0 = er[lane], z1 = er[lane + 64], z2 = er[128 + lane], z3 = er[192 + lane];
+      fwht128(z0, z1);
+      fwht128(z2, z3);
+      float* yo = a.y_out + (size_t)i * a.hidden + 256 * r;
+      yo[lane] = z0 * kInvSqrt128 * r00 * wt;
+      yo[lane + 64] = z1 * kInvSqrt128 * r01 * wt;
+      yo[128 + lane] = z2 * kInvSqrt128 * r10 * wt;
+      yo[192 + lane] = z3 * kInvSqrt128 * r11 * wt;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------------
+// Combine from sorted rows: y[t] = sum over slots j (in order) of the row of
+// pair t*k+j (skipped if the pair has no row). grid.x = n_tokens *
+// (hidden / 128), block = 64.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
+  const int nb = a.hidden / 128;
+  const int b = blockIdx.x % nb;
+  const int t = blockIdx.x / nb;
+  const int lane = threadIdx.x;
+  float acc0 = 0.f, acc1 = 0.f;
+  for (int j = 0; j < a.top_k; ++j) {
+    const int i = a.inv[t * a.top_k + j];
+    if (i < 0) continue;
+    const float* yr = a.rows + (size_t)i * a.hidden + 128 * b;
+    acc0 += yr[lane];
+    acc1 += yr[lane + 64];
+  }
+  float* y = a.y + (size_t)t * a.hidden + 128 * b;
+  y[lane] = acc0;
+  y[lane + 64] = acc1;
+  if (a.ss) {
+    const float ss = wave_sum(__builtin_fmaf(acc0, acc0, acc1 * acc1));
+    if (lane == 0) a.ss[(size_t)t * nb + b] = ss;
+  }
+}
+
+// ------------------------------------------------------------------------
+// Launchers.
+// ------------------------------------------------------------------------
+hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,
+                             int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s) {
+  hipLaunchKernelGGL(k_make_tiles, dim3(1), dim3(1024), 0, s, offsets, E, max_tiles, t_expert,
+                     t_row0, t_rows, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s) {
+  hipLaunchKernelGGL(k_xin_gather, dim3(n_pairs), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)max_tiles * (a.inter / 128));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_grouped_gate_up<2>, dim3(grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_grouped_gate_up<3>, dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)max_tiles * (a.hidden / 256));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_grouped_down<2>, dim3(grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_grouped_down<3>, dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)a.n_tokens * (a.hidden / 128));
+  hipLaunchKernelGGL(k_combine_sorted, dim3(grid), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace escha

@@ -493,41 +493,68 @@ __global__ __launch_bounds__(64) void k_group_count(const int32_t* __restrict__ 
   if (i < P) rank[i] = valid ? r : -1;
 }
 
+// Pass 2a: one block per expert: exclusive scan of its chunk counts.
 __global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ hist, int n_chunks,
                                                     int E, int32_t* __restrict__ base,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets) {
-  __shared__ int32_t tot[1024];
-  for (int e = threadIdx.x; e < E; e += 256) {
-    int32_t run = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      base[(size_t)c * E + e] = run;
-      run += hist[(size_t)c * E + e];
-    }
-    tot[e] = run;
-    counts[e] = run;
-  }
+                                                    int32_t* __restrict__ counts) {
+  __shared__ int32_t part[256];
+  const int e = blockIdx.x;
+  const int tid = threadIdx.x;
+  // each thread owns a contiguous run of chunks
+  const int per = (n_chunks + 255) / 256;
+  const int c0 = tid * per;
+  int32_t run = 0;
+  for (int c = c0; c < c0 + per && c < n_chunks; ++c) run += hist[(size_t)c * E + e];
+  part[tid] = run;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t acc = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = acc;
-      acc += tot[e];
-    }
-    offsets[E] = acc;
+  for (int d = 1; d < 256; d <<= 1) {
+    const int32_t v = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
   }
+  int32_t acc = part[tid] - run;  // exclusive prefix of this thread's run
+  for (int c = c0; c < c0 + per && c < n_chunks; ++c) {
+    base[(size_t)c * E + e] = acc;
+    acc += hist[(size_t)c * E + e];
+  }
+  if (tid == 255) counts[e] = part[255];
+}
+
+// Pass 2b: offsets = exclusive prefix sums of the counts (E <= 1024).
+__global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restrict__ counts, int E,
+                                                        int32_t* __restrict__ offsets) {
+  __shared__ int32_t scan[1024];
+  const int e = threadIdx.x;
+  const int32_t v0 = e < E ? counts[e] : 0;
+  scan[e] = v0;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int32_t v = e >= d ? scan[e - d] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  if (e < E) offsets[e] = scan[e] - v0;
+  if (e == 0) offsets[E] = scan[1023];
 }
 
 __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict__ ids, int P, int E,
                                                       const int32_t* __restrict__ base,
                                                       const int32_t* __restrict__ rank,
                                                       const int32_t* __restrict__ offsets,
-                                                      int32_t* __restrict__ perm) {
+                                                      int32_t* __restrict__ perm,
+                                                      int32_t* __restrict__ inv) {
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= P) return;
   const int e = ids[i];
-  if (e < 0 || e >= E) return;
-  perm[offsets[e] + base[(size_t)blockIdx.x * E + e] + rank[i]] = i;
+  if (e < 0 || e >= E) {
+    if (inv) inv[i] = -1;
+    return;
+  }
+  const int pos = offsets[e] + base[(size_t)blockIdx.x * E + e] + rank[i];
+  perm[pos] = i;
+  if (inv) inv[i] = pos;
 }
 
 // ------------------------------------------------------------------------
@@ -612,7 +639,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 }
 
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* hist, int32_t* base, int32_t* rank,
+                        int32_t* perm, int32_t* inv, int32_t* hist, int32_t* base, int32_t* rank,
                         hipStream_t s) {
   const int n_chunks = (P + 63) / 64;
   if (n_chunks > 0) {
@@ -620,12 +647,14 @@ hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32
     hipError_t err = last_launch();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(k_group_scan, dim3(1), dim3(256), 0, s, hist, n_chunks, E, base, counts,
-                     offsets);
+  hipLaunchKernelGGL(k_group_scan, dim3(E), dim3(256), 0, s, hist, n_chunks, E, base, counts);
   hipError_t err = last_launch();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_group_offsets, dim3(1), dim3(1024), 0, s, counts, E, offsets);
+  err = last_launch();
   if (err != hipSuccess || n_chunks == 0) return err;
   hipLaunchKernelGGL(k_group_scatter, dim3(n_chunks), dim3(64), 0, s, ids, P, E, base, rank,
-                     offsets, perm);
+                     offsets, perm, inv);
   return last_launch();
 }
 

@@ -67,6 +67,49 @@ struct CombineArgs {
   float* ss;
 };
 
+// Grouped path (pairs sorted by expert; see escha_grouped.hip).
+struct GatherArgs {
+  const uint16_t* x_bf16;  // [T][hidden]
+  const uint16_t* rin;     // gate_up rin [E][hidden]
+  const int32_t* ids;      // [T*top_k]
+  const int32_t* perm;     // sorted index -> pair
+  const int32_t* offsets;  // [E+1]; offsets[E] = number of sorted pairs
+  int32_t n_experts, hidden, top_k;
+  uint16_t* xg;            // fp16 [P][hidden] at the sorted index
+};
+
+struct GroupedArgs {
+  const uint16_t* code;     // this projection's codes
+  const uint16_t* rout;     // this projection's rout
+  const uint16_t* rin2;     // gate_up kernel: down's rin (for its epilogue)
+  int32_t hidden, inter;
+  const uint16_t* x_in;     // fp16 rows at the sorted index
+  uint16_t* x_out;          // gate_up: fp16 rotated down input [P][inter]
+  float* y_out;             // down: fp32 weighted outputs [P][hidden]
+  float* inter_out;         // nullable: h per pair, pair order
+  const int32_t* perm;
+  const float* w;           // router weights per pair
+  const int32_t* t_expert;
+  const int32_t* t_row0;
+  const int32_t* t_rows;
+  const int32_t* n_tiles;
+};
+
+struct SortedCombineArgs {
+  const float* rows;   // [P][hidden] at the sorted index
+  const int32_t* inv;  // pair -> sorted index, -1 if the pair has none
+  int32_t hidden, top_k, n_tokens;
+  float* y;
+  float* ss;  // nullable
+};
+
+hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,
+                             int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s);
+hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s);
+hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
+hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
+hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s);
+
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s);
 hipError_t launch_down_partial(const DownPartialArgs& a, int k_bits, hipStream_t s);
 hipError_t launch_proj_finish(const FinishArgs& a, hipStream_t s);
@@ -78,8 +121,9 @@ hipError_t launch_decode_tiles(const uint16_t* code_e, int in_f, int out_f, int 
 hipError_t launch_hadamard128(const float* x, int64_t rows, int n, float* y, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
+// inv (nullable): pair -> sorted index, -1 for a pair with an out-of-range id
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
-                        int32_t* perm, int32_t* hist, int32_t* base, int32_t* rank,
+                        int32_t* perm, int32_t* inv, int32_t* hist, int32_t* base, int32_t* rank,
                         hipStream_t s);
 
 }  // namespace escha

@@ -245,3 +245,41 @@ def test_rmsnorm_bf16(escha):
     # the same decision in different precision may differ by one bf16 step
     diff = np.abs(got.astype(np.int32) - ref.astype(np.int32))
     assert diff.max() <= 1 and np.mean(diff) < 1e-2
+
+
+# ------------------------------------------------------------------ grouped path
+
+def test_grouped_config3_zipf(escha):
+    """Config 3 (64 tokens, Zipf routing) through the grouped kernels: each
+    expert's tiles decoded once per 64-token tile, MFMA contraction."""
+    announce("grouped (prefill entry) config3 T=64 zipf")
+    L = synth.layer_tensors(3, 0)
+    Ldev = layer_to_dev(L)
+    x = synth.activations(3, 64, 2048)
+    ids, w = oracle.route_topk(synth.zipf_logits(3, 64), 8)
+    _check_layer(escha, L, Ldev, x, ids, w, escha.escha_moe_layer_prefill, "grouped cfg3")
+
+
+@pytest.mark.parametrize("T", [1, 2, 65])
+def test_grouped_small_batches_and_bad_ids(escha, layer2, layer2_dev, T):
+    announce(f"grouped T={T} with a bad id")
+    x = synth.activations(40 + T, T, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(40 + T, T), 8)
+    bad = ids.copy()
+    bad[0, 5] = 1000
+    y = escha.escha_moe_layer_prefill(layer2_dev, to_dev(x), to_dev(bad),
+                                      to_dev(w.astype(np.float32))).cpu().numpy()
+    w0 = w.astype(np.float32).copy()
+    w0[0, 5] = 0.0
+    ref = oracle.moe_layer(layer2, x, ids, w0)
+    assert_close(y, ref, f"grouped T={T}")
+
+
+def test_grouped_one_hot_expert(escha, layer2, layer2_dev):
+    """Every token routed to the same 8 experts: 130 tokens per expert = 3 tiles."""
+    announce("grouped, all tokens on the same experts")
+    T = 130
+    x = synth.activations(50, T, 2048)
+    ids = np.tile(np.array([[3, 9, 27, 81, 100, 200, 250, 7]], dtype=np.int32), (T, 1))
+    w = np.full((T, 8), 0.125, dtype=np.float32)
+    _check_layer(escha, layer2, layer2_dev, x, ids, w, escha.escha_moe_layer_prefill, "hot experts")
