@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--pool", type=int, default=8, help="independent steps cycled")
+    ap.add_argument("--path", choices=["persistent", "layered"], default="layered",
+                    help="stack: three launches per layer (default) or one persistent launch")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -234,6 +236,11 @@ def main():
     stack = escha.Stack(layers)
     hip = Hip()
 
+    persistent = args.path == "persistent"
+    stack_fn = (escha.escha_moe_stack_decode_persistent if persistent
+                else escha.escha_moe_stack_decode)
+    n_probe = 2 if persistent else 2 * NL
+
     # a pool of independent steps, each with its own buffers (so each can be
     # captured in its own graph)
     pool = []
@@ -245,14 +252,14 @@ def main():
             logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
             y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
             ws=torch.empty(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
-            probes=None if args.no_probe else [hip.event() for _ in range(2 * NL)],
+            probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
         ))
 
     def step(p):
         ids, w = escha.escha_route_topk(p["logits"], k)
         p["ids"], p["w"] = ids, w  # keep the graph's buffers alive
-        escha.escha_moe_stack_decode(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
-                                     out=p["y"], workspace=p["ws"], probe_events=p["probes"])
+        stack_fn(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
+                 out=p["y"], workspace=p["ws"], probe_events=p["probes"])
 
     use_graph = not args.no_graph
     graphs = []
@@ -293,13 +300,14 @@ def main():
     ms_total = hip.elapsed_ms(start, stop)
     ms_per_step = ms_total / args.steps
 
-    # per-layer durations from the probes of each pool entry's last step
-    layer_ms = []
+    # probe durations of each pool entry's last step: the persistent kernel
+    # (one per step) or each layer's three launches
+    probe_ms = []
     if not args.no_probe:
         for p in pool:
-            for l in range(NL):
-                layer_ms.append(hip.elapsed_ms(p["probes"][2 * l], p["probes"][2 * l + 1]))
-    layer_avg_ms = float(np.mean(layer_ms)) if layer_ms else None
+            for j in range(n_probe // 2):
+                probe_ms.append(hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]))
+    probe_avg_ms = float(np.mean(probe_ms)) if probe_ms else None
 
     # algorithmic bytes: the packed codes of the distinct experts each layer
     # routes to (at batch 1 every one of the 8 is distinct), averaged over the pool
@@ -311,17 +319,18 @@ def main():
     tok_s = T / (ms_per_step / 1e3)
     gbs = code_bytes_step / (ms_per_step / 1e3) / 1e9
 
-    layer_bytes = code_bytes_step / NL
     roofline = None
-    if layer_avg_ms:
-        achieved = layer_bytes / (layer_avg_ms / 1e3) / 1e9
-        roofline = {"kernel": "one layer's decode launches (k_in_partial + k_down_partial + "
-                              "k_combine)",
-                    "bound": "hbm",
+    if probe_avg_ms:
+        launch_bytes = code_bytes_step if persistent else code_bytes_step / NL
+        achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
+        kernel = ("k_stack_decode (one persistent launch: all layers)" if persistent else
+                  "one layer's decode launches (k_in_partial + k_down_partial + k_combine)")
+        roofline = {"kernel": kernel, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                    "bytes_per_launch": int(layer_bytes), "avg_launch_us": round(layer_avg_ms * 1e3, 3),
-                    "samples": len(layer_ms)}
+                    "bytes_per_launch": int(launch_bytes),
+                    "avg_launch_us": round(probe_avg_ms * 1e3, 3),
+                    "samples": len(probe_ms)}
 
     checks = {}
     cpu = None
@@ -358,7 +367,7 @@ def main():
         "config": {"workload": f"expert stack streaming: {NL} layers x {E} experts, "
                                f"decode batch {T}, top-{k}, hidden {hidden}, inter 512, "
                                f"gate_up K=2 / down K=3, codes {NL * E * 917504 / 1e9:.2f} GB in HBM",
-                   "batch": T, "layers": NL, "graph": use_graph},
+                   "batch": T, "layers": NL, "graph": use_graph, "path": args.path},
         "code_gbs_step": round(gbs, 1),
         "code_bytes_per_step": code_bytes_step,
         "wall_ms_per_step": round(t_wall / args.steps * 1e3, 4),

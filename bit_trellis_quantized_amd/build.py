@@ -18,7 +18,7 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libescha.so"
 ARCH = "gfx950"
 
-SOURCES = ["escha_kernels.hip", "escha_grouped.hip", "escha_api.cpp"]
+SOURCES = ["escha_kernels.hip", "escha_grouped.hip", "escha_stack.hip", "escha_api.cpp"]
 
 
 def hipcc() -> str:

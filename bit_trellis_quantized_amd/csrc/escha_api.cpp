@@ -33,6 +33,7 @@ size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 constexpr int32_t kMaxTopK = 64;
 constexpr int32_t kMaxHidden = 16384;  // k_rmsnorm_bf16 keeps one sum per 128-block in LDS
 constexpr int32_t kMaxExpertsRoute = 1024;
+constexpr int32_t kMaxStackTokens = 64;  // persistent stack path
 
 int check_proj(const escha_proj_t* w, const char* what) {
   if (!w) return fail(ESCHA_E_NULL, "%s: descriptor is NULL", what);
@@ -282,6 +283,59 @@ int check_layer_call(const escha_moe_layer_t* L, const uint16_t* x, int32_t T, c
   return ESCHA_OK;
 }
 
+
+// ---------------------------------------------------------------- stack
+// Control block at the start of a stack workspace: a 64-int header (ticket,
+// status word) and the persistent kernel's dependency counters, one per
+// kCtrStride ints: gate_up tasks done per (layer, pair), down tasks done per
+// (layer, token, output group), groups combined per (layer, token).
+constexpr int64_t kCtlHeaderInts = 64;
+
+int64_t stack_ctl_ints(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
+  const int64_t P = T * L->top_k;
+  const int64_t ngd = L->hidden / 256;
+  return kCtlHeaderInts + n_layers * (P * escha::kPollStride + T * ngd * escha::kCtrStride +
+                                      T * escha::kYRep * escha::kPollStride);
+}
+
+size_t stack_ctl_bytes(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
+  return round_up((size_t)stack_ctl_ints(L, n_layers, T) * sizeof(int32_t));
+}
+
+// Per-layer outputs of the persistent path (every layer but the last, each
+// at an address of its own): y [n_layers-1][T][hidden], then the sums of
+// squares [n_layers-1][T][ss_tok], one 256-byte-aligned row per token so
+// that no cache line holds two tokens' sums.
+int64_t stack_ss_tok(const escha_moe_layer_t* L) { return (L->hidden / 128 + 63) / 64 * 64; }
+
+int64_t stack_ss_stride(const escha_moe_layer_t* L, int64_t T) { return T * stack_ss_tok(L); }
+
+size_t stack_layer_bufs_bytes(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
+  const int64_t n = n_layers - 1;
+  return round_up((size_t)n * T * L->hidden * sizeof(float)) +
+         round_up((size_t)n * stack_ss_stride(L, T) * sizeof(float));
+}
+
+int check_stack_call(const escha_moe_layer_t* layers, int32_t n_layers, const uint16_t* x0_bf16,
+                     int32_t n_tokens, const int32_t* topk_ids, const float* topk_w, float eps,
+                     const float* y_last, const void* workspace, size_t workspace_bytes) {
+  if (!layers) return fail(ESCHA_E_NULL, "layers is NULL");
+  if (n_layers < 1) return fail(ESCHA_E_ARG, "n_layers=%d", n_layers);
+  for (int l = 0; l < n_layers; ++l) {
+    int rc = check_layer_call(&layers[l], x0_bf16, n_tokens, topk_ids, topk_w, y_last);
+    if (rc) return rc;
+    if (layers[l].hidden != layers[0].hidden || layers[l].inter != layers[0].inter ||
+        layers[l].top_k != layers[0].top_k)
+      return fail(ESCHA_E_SHAPE, "layer %d differs from layer 0 in hidden/inter/top_k", l);
+  }
+  if (!(eps >= 0.f)) return fail(ESCHA_E_ARG, "eps must be >= 0");
+  if (n_tokens == 0) return ESCHA_OK;
+  const size_t need = escha_moe_stack_workspace_bytes(layers, n_layers, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return ESCHA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -451,7 +505,8 @@ size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t 
   if (!layers || n_layers < 1 || n_tokens < 0) return 0;
   const escha_moe_layer_t* L = &layers[0];
   const size_t ybuf = round_up((size_t)n_tokens * L->hidden * sizeof(float));
-  return decode_ws_bytes(L, n_tokens) + ybuf;
+  return stack_ctl_bytes(L, n_layers, n_tokens) + decode_ws_bytes(L, n_tokens) + ybuf +
+         stack_layer_bufs_bytes(L, n_layers, n_tokens);
 }
 
 int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
@@ -459,23 +514,12 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
                            const float* topk_w, float eps, float* y_last, uint16_t* x_chain,
                            void* workspace, size_t workspace_bytes, void* const* probe_events,
                            void* stream) {
-  if (!layers) return fail(ESCHA_E_NULL, "layers is NULL");
-  if (n_layers < 1) return fail(ESCHA_E_ARG, "n_layers=%d", n_layers);
-  for (int l = 0; l < n_layers; ++l) {
-    int rc = check_layer_call(&layers[l], x0_bf16, n_tokens, topk_ids, topk_w, y_last);
-    if (rc) return rc;
-    if (layers[l].hidden != layers[0].hidden || layers[l].inter != layers[0].inter ||
-        layers[l].top_k != layers[0].top_k)
-      return fail(ESCHA_E_SHAPE, "layer %d differs from layer 0 in hidden/inter/top_k", l);
-  }
-  if (!(eps >= 0.f)) return fail(ESCHA_E_ARG, "eps must be >= 0");
-  if (n_tokens == 0) return ESCHA_OK;
-  const size_t need = escha_moe_stack_workspace_bytes(layers, n_layers, n_tokens);
-  if (!workspace || workspace_bytes < need)
-    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  int rc = check_stack_call(layers, n_layers, x0_bf16, n_tokens, topk_ids, topk_w, eps, y_last,
+                            workspace, workspace_bytes);
+  if (rc || n_tokens == 0) return rc;
   const escha_moe_layer_t* L0 = &layers[0];
   const int H = L0->hidden, k = L0->top_k;
-  char* b = (char*)workspace;
+  char* b = (char*)workspace + stack_ctl_bytes(L0, n_layers, n_tokens);
   const DecodeWs ws = decode_ws_carve(L0, n_tokens, b);
   float* ytmp = (float*)(b + decode_ws_bytes(L0, n_tokens));
   hipStream_t s = (hipStream_t)stream;
@@ -504,6 +548,105 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
                               topk_w + (size_t)l * n_tokens * k, y, nullptr, ws, s, before, after);
     if (rc) return rc;
   }
+  return ESCHA_OK;
+}
+
+int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n_layers,
+                                      const uint16_t* x0_bf16, int32_t n_tokens,
+                                      const int32_t* topk_ids, const float* topk_w, float eps,
+                                      float* y_last, uint16_t* x_chain, void* workspace,
+                                      size_t workspace_bytes, void* const* probe_events,
+                                      void* stream) {
+  int rc = check_stack_call(layers, n_layers, x0_bf16, n_tokens, topk_ids, topk_w, eps, y_last,
+                            workspace, workspace_bytes);
+  if (rc) return rc;
+  if (n_layers > escha::kMaxStackLayers)
+    return fail(ESCHA_E_UNSUPPORTED, "n_layers=%d > %d", n_layers, escha::kMaxStackLayers);
+  if (n_tokens > kMaxStackTokens)
+    return fail(ESCHA_E_UNSUPPORTED, "n_tokens=%d > %d", n_tokens, kMaxStackTokens);
+  const escha_moe_layer_t* L0 = &layers[0];
+  for (int l = 1; l < n_layers; ++l) {
+    const escha_moe_layer_t* L = &layers[l];
+    if (L->gate_up.n_experts != L0->gate_up.n_experts || L->gate_up.k_bits != L0->gate_up.k_bits ||
+        L->down.k_bits != L0->down.k_bits)
+      return fail(ESCHA_E_UNSUPPORTED,
+                  "layer %d differs from layer 0 in n_experts or k_bits (persistent path)", l);
+  }
+  if (n_tokens == 0) return ESCHA_OK;
+  const int64_t T = n_tokens, P = T * L0->top_k, H = L0->hidden, I = L0->inter;
+  const int64_t per_layer = P * (H / 128) * (2 * I / 256) + P * (I / 128) * (H / 256);
+  const int64_t n_tasks = per_layer * n_layers;
+  if (n_tasks > ((int64_t)1 << 30))
+    return fail(ESCHA_E_UNSUPPORTED, "%lld tasks exceed the task counter", (long long)n_tasks);
+
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* ctl = (int32_t*)workspace;
+  char* b = (char*)workspace + stack_ctl_bytes(L0, n_layers, T);
+  const DecodeWs ws = decode_ws_carve(L0, T, b);
+  b += decode_ws_bytes(L0, T) + round_up((size_t)T * H * sizeof(float));
+  float* y_layers = (float*)b;
+  float* ss_layers = (float*)(b + round_up((size_t)(n_layers - 1) * T * H * sizeof(float)));
+
+  escha::StackArgs a{};
+  for (int l = 0; l < n_layers; ++l) {
+    a.layer[l].gu_code = (const uint16_t*)layers[l].gate_up.code;
+    a.layer[l].gu_rin = (const uint16_t*)layers[l].gate_up.rin;
+    a.layer[l].gu_rout = (const uint16_t*)layers[l].gate_up.rout;
+    a.layer[l].dn_code = (const uint16_t*)layers[l].down.code;
+    a.layer[l].dn_rin = (const uint16_t*)layers[l].down.rin;
+    a.layer[l].dn_rout = (const uint16_t*)layers[l].down.rout;
+  }
+  a.n_layers = n_layers;
+  a.n_tokens = n_tokens;
+  a.top_k = L0->top_k;
+  a.hidden = L0->hidden;
+  a.inter = L0->inter;
+  a.n_experts = L0->gate_up.n_experts;
+  a.n_tasks = (int32_t)n_tasks;
+  a.eps = eps;
+  a.ids = topk_ids;
+  a.w = topk_w;
+  a.x0 = x0_bf16;
+  a.y_layers = y_layers;
+  a.ss_layers = ss_layers;
+  a.ss_stride = stack_ss_stride(L0, T);
+  a.ss_tok = (int32_t)stack_ss_tok(L0);
+  a.y_last = y_last;
+  a.x_chain = x_chain;
+  a.gu_part = ws.gu_part;
+  a.dn_part = ws.dn_part;
+  a.ticket = ctl;
+  a.error = ctl + 1;
+  a.gu_done = ctl + kCtlHeaderInts;
+  a.c_done = a.gu_done + (size_t)n_layers * P * escha::kPollStride;
+  a.y_done = a.c_done + (size_t)n_layers * T * (H / 256) * escha::kCtrStride;
+
+  int groups = 0;
+  hipError_t e = escha::stack_resident_groups(L0->gate_up.k_bits, L0->down.k_bits, &groups);
+  if (e != hipSuccess) return hip_fail(e, "occupancy query");
+  if (groups < 1) return fail(ESCHA_E_HIP, "persistent kernel does not fit on the device");
+  if ((int64_t)groups > n_tasks) groups = (int)n_tasks;
+
+  e = escha::launch_fill_zero(ctl, (size_t)stack_ctl_ints(L0, n_layers, T), s);
+  if (e != hipSuccess) return hip_fail(e, "counter clear launch");
+  if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[0], s)) != hipSuccess)
+    return hip_fail(e, "probe event record");
+  e = escha::launch_stack_decode(a, L0->gate_up.k_bits, L0->down.k_bits, groups, s);
+  if (e != hipSuccess) return hip_fail(e, "persistent stack launch");
+  if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[1], s)) != hipSuccess)
+    return hip_fail(e, "probe event record");
+  return ESCHA_OK;
+}
+
+int escha_moe_stack_status(const void* workspace, int32_t* status, void* stream) {
+  if (!workspace || !status) return fail(ESCHA_E_NULL, "workspace/status is NULL");
+  int32_t v = 0;
+  hipError_t e = hipMemcpyAsync(&v, (const int32_t*)workspace + 1, sizeof(v), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "status copy");
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "status copy");
+  *status = v;
   return ESCHA_OK;
 }
 

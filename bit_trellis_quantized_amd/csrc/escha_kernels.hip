@@ -15,83 +15,9 @@
 
 #include "escha_device.hpp"
 #include "escha_launch.hpp"
+#include "escha_stream.hpp"
 
 namespace escha {
-
-// ------------------------------------------------------------------------
-// Shared pieces of the streaming kernels.
-// ------------------------------------------------------------------------
-
-// Issue the loads of NKT consecutive tile-rows (kt0, kt0+1, ..) of output
-// tile nt, this lane's quarter. Nothing here waits for the data.
-template <int K, int NKT>
-__device__ __forceinline__ void issue_rows(const uint16_t* __restrict__ code_e, int n_nt, int kt0,
-                                           int nt, int q, uint32_t (&raw)[NKT][Quarter<K>::kOwn]) {
-#pragma unroll
-  for (int j = 0; j < NKT; ++j) {
-    const uint16_t* tq = code_e + ((size_t)(kt0 + j) * n_nt + nt) * (16 * K) + q * (4 * K);
-    load_quarter<K>(tq, raw[j]);
-  }
-}
-
-// Decode the loaded rows and accumulate: acc[n] += W[.., n] * x~[k] over this
-// lane's 4 input rows of each tile-row. xs: the 128 rotated inputs of the
-// chunk (LDS); j0: index of the first row inside the chunk.
-template <int K, int NKT>
-__device__ __forceinline__ void mac_rows(const uint32_t (&raw)[NKT][Quarter<K>::kOwn], int j0, int q,
-                                         const float* xs, float (&acc)[16]) {
-  constexpr int kOwn = Quarter<K>::kOwn;
-#pragma unroll
-  for (int j = 0; j < NKT; ++j) {
-    uint32_t d[kOwn + 1];
-#pragma unroll
-    for (int i = 0; i < kOwn; ++i) d[i] = raw[j][i];
-    d[kOwn] = next_quarter_dword(raw[j][0]);
-    const float4 xv = *reinterpret_cast<const float4*>(xs + 16 * (j0 + j) + 4 * q);
-    const float xk[4] = {xv.x, xv.y, xv.z, xv.w};
-    decode_quarter<K>(d, [&](int kk, int n, h16x2 w) {
-      acc[n] = __builtin_fmaf((float)w.x, xk[kk], acc[n]);
-      acc[n + 8] = __builtin_fmaf((float)w.y, xk[kk], acc[n + 8]);
-    });
-  }
-}
-
-// Sum the four quarter-lanes' column sums (DPP inside each quad; all four
-// lanes get the same bits). Lane q then owns output columns 4q..4q+3 of its
-// tile, i.e. outputs 4*lane .. 4*lane+3 of the wave's 256.
-__device__ __forceinline__ float4 quad_reduce_pick(float (&acc)[16], int q) {
-#pragma unroll
-  for (int n = 0; n < 16; ++n) {
-    acc[n] += xor_lane<1>(acc[n]);
-    acc[n] += xor_lane<2>(acc[n]);
-  }
-  float4 r;
-  r.x = q == 0 ? acc[0] : q == 1 ? acc[4] : q == 2 ? acc[8] : acc[12];
-  r.y = q == 0 ? acc[1] : q == 1 ? acc[5] : q == 2 ? acc[9] : acc[13];
-  r.z = q == 0 ? acc[2] : q == 1 ? acc[6] : q == 2 ? acc[10] : acc[14];
-  r.w = q == 0 ? acc[3] : q == 1 ? acc[7] : q == 2 ? acc[11] : acc[15];
-  return r;
-}
-
-__device__ __forceinline__ float4 f4add(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-}
-
-// Output transform of one 256-output group held in LDS (zs, in output
-// order): waves 0 and 1 each take one 128-block, apply H_n, multiply by
-// rout (and the weight wt) and store. out points at the group's first output.
-__device__ __forceinline__ void transform_store(const float* zs, const uint16_t* __restrict__ rout_g,
-                                                float wt, float* __restrict__ out, int wave,
-                                                int lane) {
-  if (wave < 2) {
-    float z0 = zs[128 * wave + lane];
-    float z1 = zs[128 * wave + lane + 64];
-    fwht128(z0, z1);
-    const uint16_t* ro = rout_g + 128 * wave;
-    out[128 * wave + lane] = z0 * kInvSqrt128 * f16_to_f32(ro[lane]) * wt;
-    out[128 * wave + lane + 64] = z1 * kInvSqrt128 * f16_to_f32(ro[lane + 64]) * wt;
-  }
-}
 
 // ------------------------------------------------------------------------
 // gate_up (or any single projection): transformed partial sums over one

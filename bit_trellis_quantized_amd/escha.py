@@ -67,6 +67,9 @@ _SIGS = {
     "escha_moe_stack_workspace_bytes": ([_P(escha_moe_layer_t), _i32, _i32], _sz),
     "escha_moe_stack_decode": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp,
                                 _vp, _sz, _vp, _vp], ctypes.c_int),
+    "escha_moe_stack_decode_persistent": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32,
+                                           _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
+    "escha_moe_stack_status": ([_vp, _P(_i32), _vp], ctypes.c_int),
     "escha_last_error": ([], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -305,9 +308,8 @@ class Stack:
         return int(_lib.escha_moe_stack_workspace_bytes(self.arr, len(self.layers), n_tokens))
 
 
-def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6, out=None,
-                           x_chain=None, workspace=None, probe_events=None, stream=None):
-    """probe_events: optional sequence of 2*n_layers raw hipEvent_t handles (ints)."""
+def _stack_call(fn, n_events, stack, x0_bf16, topk_ids, topk_w, eps, out, x_chain, workspace,
+                probe_events, stream):
     T = x0_bf16.shape[0]
     hidden = stack.layers[0].hidden
     if out is None:
@@ -315,13 +317,33 @@ def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float =
     nbytes = stack.workspace_bytes(T)
     if workspace is None:
         workspace = _ws(nbytes, x0_bf16.device)
-    _check(_lib.escha_moe_stack_decode(stack.arr, len(stack.layers), _ptr(x0_bf16, _U16, "x0"), T,
-                                       _ptr(topk_ids, torch.int32, "topk_ids"),
-                                       _ptr(topk_w, torch.float32, "topk_w"), eps,
-                                       _ptr(out, torch.float32, "y"), _ptr(x_chain, _U16, "x_chain"),
-                                       _ptr(workspace), workspace.numel(),
-                                       _events(probe_events, 2 * len(stack.layers)), _stream(stream)))
+    _check(fn(stack.arr, len(stack.layers), _ptr(x0_bf16, _U16, "x0"), T,
+              _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"), eps,
+              _ptr(out, torch.float32, "y"), _ptr(x_chain, _U16, "x_chain"), _ptr(workspace),
+              workspace.numel(), _events(probe_events, n_events), _stream(stream)))
     return out
+
+
+def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6, out=None,
+                           x_chain=None, workspace=None, probe_events=None, stream=None):
+    """probe_events: optional sequence of 2*n_layers raw hipEvent_t handles (ints)."""
+    return _stack_call(_lib.escha_moe_stack_decode, 2 * len(stack.layers), stack, x0_bf16, topk_ids,
+                       topk_w, eps, out, x_chain, workspace, probe_events, stream)
+
+
+def escha_moe_stack_decode_persistent(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6,
+                                      out=None, x_chain=None, workspace=None, probe_events=None,
+                                      stream=None):
+    """One persistent launch for the whole stack; probe_events: 2 raw hipEvent_t handles."""
+    return _stack_call(_lib.escha_moe_stack_decode_persistent, 2, stack, x0_bf16, topk_ids, topk_w,
+                       eps, out, x_chain, workspace, probe_events, stream)
+
+
+def escha_moe_stack_status(workspace: torch.Tensor, stream=None) -> int:
+    """Status word of the last persistent stack call on this workspace (waits for the stream)."""
+    v = ctypes.c_int32(-1)
+    _check(_lib.escha_moe_stack_status(_ptr(workspace), ctypes.byref(v), _stream(stream)))
+    return int(v.value)
 
 
 def _events(handles, n):

@@ -202,6 +202,37 @@ ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_
                            void* workspace, size_t workspace_bytes, void* const* probe_events,
                            void* stream);
 
+/*
+ * The same stack in ONE persistent kernel launch (plus a small kernel that
+ * clears the launch's dependency counters first). Same arguments, same
+ * workspace size, and results bit-identical to escha_moe_stack_decode: the
+ * per-task arithmetic is shared. Work is handed out as numbered tasks
+ * through an atomic counter; a work-group loads and decodes a task's codes
+ * before waiting for the outputs the task reads, so code streaming and
+ * decode of later layers overlap the dependency chain of earlier ones.
+ * Additional requirements: n_layers <= 64; every layer has the same
+ * n_experts and the same gate_up and down k_bits; n_tokens <= 64.
+ * probe_events (nullable): a HOST array of 2 hipEvent_t handles, recorded
+ * right before and right after the persistent kernel.
+ * A dependency wait that exceeds its bound (it cannot happen while the
+ * device makes progress) makes every work-group stop at its next wait; the
+ * outputs are then incomplete and escha_moe_stack_status reports 1.
+ * Calls sharing one workspace must be ordered (same stream or synchronised).
+ */
+ESCHA_API int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n_layers,
+                                      const uint16_t* x0_bf16, int32_t n_tokens,
+                                      const int32_t* topk_ids, const float* topk_w, float eps,
+                                      float* y_last, uint16_t* x_chain, void* workspace,
+                                      size_t workspace_bytes, void* const* probe_events,
+                                      void* stream);
+
+/*
+ * Status word of the last escha_moe_stack_decode_persistent call on this
+ * workspace: waits for `stream`, then stores 0 (complete) or 1 (a wait gave
+ * up) in *status (a HOST pointer).
+ */
+ESCHA_API int escha_moe_stack_status(const void* workspace, int32_t* status, void* stream);
+
 /* Message for the calling thread's last failed call ("" if none). */
 ESCHA_API const char* escha_last_error(void);
 

@@ -150,6 +150,49 @@ def test_stack_validation(lib):
     assert f(arr2, 1, FAKE, 1, FAKE, FAKE, -1.0, FAKE, None, FAKE, 1 << 40, None, None) == -7
 
 
+def test_persistent_stack_validation(lib):
+    f = lib.escha_moe_stack_decode_persistent
+    f.argtypes = [ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    big = 1 << 44
+    # shared checks with the layer-by-layer stack
+    assert f(None, 1, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, big, None, None) == -1
+    arr1 = (Layer * 1)(_layer())
+    assert f(arr1, 1, FAKE, 1, FAKE, FAKE, -1.0, FAKE, None, FAKE, big, None, None) == -7
+    assert f(arr1, 1, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, 16, None, None) == -4
+    # limits of the persistent path
+    arr65 = (Layer * 65)(*[_layer() for _ in range(65)])
+    assert f(arr65, 65, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, big, None, None) == -6
+    assert "n_layers" in _err(lib)
+    assert f(arr1, 1, FAKE, 65, FAKE, FAKE, 1e-6, FAKE, None, FAKE, big, None, None) == -6
+    mixed = (Layer * 2)(_layer(), _layer())
+    mixed[1].down.k_bits = 2
+    assert f(mixed, 2, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, big, None, None) == -6
+    assert "k_bits" in _err(lib)
+    mixed = (Layer * 2)(_layer(), _layer())
+    mixed[1].gate_up.n_experts = mixed[1].down.n_experts = 128
+    assert f(mixed, 2, FAKE, 1, FAKE, FAKE, 1e-6, FAKE, None, FAKE, big, None, None) == -6
+    # zero tokens: a no-op that launches nothing
+    assert f(arr1, 1, None, 0, None, None, 1e-6, None, None, None, 0, None, None) == 0
+    s = lib.escha_moe_stack_status
+    s.argtypes = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]
+    assert s(None, None, None) == -1
+
+
+def test_stack_workspace_holds_the_counters(lib):
+    """The stack workspace grows with the layers' dependency counters."""
+    ws = lib.escha_moe_stack_workspace_bytes
+    ws.argtypes = [ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_int32]
+    ws.restype = ctypes.c_size_t
+    arr = (Layer * 40)(*[_layer() for _ in range(40)])
+    one, two = ws(arr, 1, 1), ws(arr, 2, 1)
+    # one more layer: 8 pair counters + 8 group counters + 1 token counter, 64 B each
+    assert two - one >= (8 + 8 + 1) * 64 - 255
+    lay1 = ws(arr, 40, 1)
+    assert lay1 >= 40 * (8 + 8 + 1) * 64
+
+
 def test_leaf_contract():
     """Required leaves must be present; unknown escha_* leaves are rejected by name."""
     import importlib.util

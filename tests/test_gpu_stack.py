@@ -102,3 +102,82 @@ def test_stack_sampled_tokens_vs_oracle_batch8(escha, stack):
             assert_close(y[pick], ref, f"T=8 layer {l}")
         nxt = oracle.rmsnorm_bf16(ref)
         xs = {t: nxt[i:i + 1] for i, t in enumerate(pick)}
+
+
+# ---------------------------------------------------------------- persistent
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_persistent_equals_layered_stack(escha, stack, T):
+    """One persistent launch gives the layer-by-layer stack's results bit for
+    bit (every layer input and the last output), also when it is called
+    again on the same workspace."""
+    announce(f"persistent stack vs layered stack, T={T}")
+    x0, logits = synth.stack_token_inputs(SEED, NL, T, 3)
+    ids, w = _route(escha, logits)
+    x0d = to_dev(x0)
+    ws = torch.empty(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    c1 = torch.empty(NL, T, synth.HIDDEN, dtype=torch.int16, device="cuda")
+    c2 = torch.full_like(c1, 0x7FC1)
+    y1 = escha.escha_moe_stack_decode(stack, x0d, ids, w, x_chain=c1, workspace=ws)
+    y2 = escha.escha_moe_stack_decode_persistent(stack, x0d, ids, w, x_chain=c2, workspace=ws)
+    assert escha.escha_moe_stack_status(ws) == 0
+    for l in range(NL):
+        assert torch.equal(c1[l], c2[l]), f"layer {l} input differs"
+    assert torch.equal(y1, y2)
+    y3 = escha.escha_moe_stack_decode_persistent(stack, x0d, ids, w, workspace=ws)
+    assert escha.escha_moe_stack_status(ws) == 0
+    assert torch.equal(y1, y3)
+
+
+def test_persistent_first_layer_vs_oracle(escha, stack):
+    """Direct check against the oracle: the persistent stack's input of layer
+    1 is RMSNorm(layer 0(x0)); it must match the oracle's to one bf16 step."""
+    announce("persistent stack layer 0 vs oracle, T=2")
+    T = 2
+    x0, logits = synth.stack_token_inputs(SEED, NL, T, 5)
+    ids, w = _route(escha, logits)
+    chain = torch.empty(NL, T, synth.HIDDEN, dtype=torch.int16, device="cuda")
+    escha.escha_moe_stack_decode_persistent(stack, to_dev(x0), ids, w, x_chain=chain)
+    ids0 = ids[0].cpu().numpy()
+    w0 = w[0].cpu().numpy()
+    L = synth.layer_tensors(SEED, 0, experts=ids0.ravel())
+    ref = oracle.moe_layer(L, x0, ids0, w0)
+    x1 = oracle.rmsnorm_bf16(ref)
+    got = u16(chain[1])
+    diff = np.abs(got.astype(np.int32) - x1.astype(np.int32))
+    announce(f"bf16 steps off: max {diff.max()}, count {(diff > 0).sum()} of {diff.size}")
+    assert diff.max() <= 1
+    assert (diff > 0).mean() < 0.01
+
+
+def test_persistent_small_stack_edge_cases(escha):
+    """3 layers x 16 experts, 3 tokens: out-of-range expert ids (the pair
+    contributes zero), an expert whose up-projection output is pruned on a
+    whole 128-channel chunk (that down chunk is skipped), and n_tokens that
+    is not a multiple of anything."""
+    announce("persistent small stack, bad ids and pruned chunk, T=3")
+    E, NLs, T = 16, 3, 3
+    host = [synth.layer_tensors(11, l, n_experts=E) for l in range(NLs)]
+    # expert 5 of layer 1: up rows 0..127 of the intermediate have rout = 0
+    host[1]["gu_rout"][5, synth.INTER:synth.INTER + 128] = 0
+    layers = [layer_to_dev(L) for L in host]
+    st = escha.Stack(layers)
+    rs = np.random.default_rng(0)
+    ids = np.stack([np.stack([rs.permutation(E)[:8] for _ in range(T)]) for _ in range(NLs)])
+    ids = ids.astype(np.int32)
+    ids[1, 0, 0] = 5
+    ids[1, 2, 3] = 5
+    ids[0, 1, 2] = -1
+    ids[2, 2, 7] = E  # out of range
+    w = rs.random((NLs, T, 8)).astype(np.float32)
+    x0 = synth.activations(11, T, synth.HIDDEN, layer=7)
+    idd, wd, x0d = to_dev(ids), to_dev(w), to_dev(x0)
+    ws = torch.empty(st.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    c1 = torch.empty(NLs, T, synth.HIDDEN, dtype=torch.int16, device="cuda")
+    c2 = torch.empty_like(c1)
+    y1 = escha.escha_moe_stack_decode(st, x0d, idd, wd, x_chain=c1, workspace=ws)
+    y2 = escha.escha_moe_stack_decode_persistent(st, x0d, idd, wd, x_chain=c2, workspace=ws)
+    assert escha.escha_moe_stack_status(ws) == 0
+    assert torch.equal(c1, c2)
+    assert torch.equal(y1, y2)
+    assert torch.isfinite(y2).all()
