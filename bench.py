@@ -50,8 +50,10 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
-    ap.add_argument("--workload", choices=["stack", "layer"], default="stack",
-                    help="stack: the 40-layer decode (default); layer: one MoE layer call")
+    ap.add_argument("--workload", choices=["stack", "layer", "copy"], default="stack",
+                    help="stack: the 40-layer decode (default); layer: one MoE layer call; "
+                         "copy: a plain device copy (HBM calibration and counter scale)")
+    ap.add_argument("--copy-mib", type=int, default=2048, help="copy workload: bytes per copy")
     ap.add_argument("--config", type=int, default=5, choices=[2, 3, 5],
                     help="layer workload: 2 = batch-1 decode, 3 = 64 tokens Zipf, 5 = 4096-token prefill")
     ap.add_argument("--entry", choices=["decode", "prefill"], default=None,
@@ -212,6 +214,35 @@ def layer_workload(args, log):
     print(json.dumps(out), flush=True)
 
 
+def copy_workload(args, log):
+    """A plain device-to-device copy of a known size: the achievable HBM rate
+    on this machine, and the reference that scales the FETCH_SIZE / WRITE_SIZE
+    counters (a copy of B bytes reads B and writes B)."""
+    import torch
+    hip = Hip()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    n = args.copy_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.random_(0, 256)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    start, stop = hip.event(), hip.event()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.lib.hipEventRecord(ctypes.c_void_p(start), stream)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    hip.lib.hipEventRecord(ctypes.c_void_p(stop), stream)
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(start, stop) / args.steps
+    moved = 2 * n
+    print(json.dumps({"workload": "copy", "bytes_per_copy": n, "bytes_moved_per_copy": moved,
+                      "ms_per_copy": round(ms, 4), "hbm_gbs": round(moved / (ms / 1e3) / 1e9, 1),
+                      "frac_of_8tbs": round(moved / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "steps": args.steps, "warmup": args.warmup}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -226,6 +257,9 @@ def main():
     from bit_trellis_quantized_amd import escha, synth
 
     torch.cuda.set_device(0)
+    if args.workload == "copy":
+        copy_workload(args, log)
+        return
     if args.workload == "layer":
         layer_workload(args, log)
         return

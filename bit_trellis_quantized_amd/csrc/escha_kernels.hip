@@ -127,11 +127,22 @@ __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
   constexpr int kOwn = Quarter<K>::kOwn;
   const int n_groups = a.out_f / 256;
   const int n_chunks = a.in_f / 128;  // in_f = inter
-  int bid = blockIdx.x;
-  const int g = bid % n_groups;
-  bid /= n_groups;
-  const int c = bid % n_chunks;
-  const int p = bid / n_chunks;
+  // Work-groups are dealt to the 8 XCDs round-robin by index. All groups of
+  // one (pair, chunk) read the same gate_up partials, so they are placed on
+  // one XCD, whose L2 then fetches those partials once instead of 8 times.
+  const int bid = blockIdx.x;
+  const int n_pc = a.n_pairs * n_chunks;
+  int g, pc;
+  if (n_pc % 8 == 0) {
+    const int i = bid >> 3;
+    g = i % n_groups;
+    pc = (i / n_groups) * 8 + (bid & 7);
+  } else {
+    g = bid % n_groups;
+    pc = bid / n_groups;
+  }
+  const int c = pc % n_chunks;
+  const int p = pc / n_chunks;
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   float* out = a.partial + ((size_t)p * n_chunks + c) * a.out_f + g * 256;

@@ -52,6 +52,7 @@ namespace escha {
 namespace {
 
 constexpr int kSpinLimit = 1 << 21;  // polls before a wait gives up
+constexpr int kGroupsPerCu = 2;      // persistent work-groups per compute unit
 
 __device__ __forceinline__ int ld_relaxed(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -78,7 +79,13 @@ __device__ bool wait_count(const int32_t* ctr, int target, int32_t* err) {
         return false;
       }
     }
-    __builtin_amdgcn_s_sleep(1);
+    // back off: a task claimed far ahead of the chain polls less often
+    if (it < 8)
+      __builtin_amdgcn_s_sleep(1);
+    else if (it < 32)
+      __builtin_amdgcn_s_sleep(4);
+    else
+      __builtin_amdgcn_s_sleep(12);
   }
 }
 
@@ -131,6 +138,21 @@ __device__ __forceinline__ void zero4_agent(float* out, int lane) {
 __device__ __forceinline__ void claim_next(int32_t* ticket, int& next) {
   if (threadIdx.x == 0) next = add_relaxed(ticket, 1);
   __builtin_amdgcn_s_setprio(3);
+}
+
+// Keep decoded weights where they are: an empty asm that claims to modify
+// each register, so the compiler cannot sink the decode past the wait (it
+// would otherwise recompute it there to shorten register live ranges).
+template <int NKT>
+__device__ __forceinline__ void pin_decoded(h16x2 (&wv)[NKT][32]) {
+#pragma unroll
+  for (int j = 0; j < NKT; ++j)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      uint32_t u = __builtin_bit_cast(uint32_t, wv[j][i]);
+      asm volatile("" : "+v"(u));
+      wv[j][i] = __builtin_bit_cast(h16x2, u);
+    }
 }
 
 // group_signal on each of the kYRep copies of a counter (waiters poll one
@@ -203,6 +225,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const float ro0 = f16_to_f32(ro[lane]);
       const float ro1 = f16_to_f32(ro[lane + 64]);
       decode_rows<KG, 2>(raw, wv);
+      pin_decoded(wv);
       if (l > 0 &&
           !group_wait(a.y_done + (((size_t)(l - 1) * T + t) * kYRep + blockIdx.x % kYRep) * kPollStride,
                       ngd, a.error, &sh.ok))
@@ -300,6 +323,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
       const float ro1 = f16_to_f32(ro[lane + 64]);
       const float wt = a.w[(size_t)l * P + p];
       decode_rows<KD, 2>(raw, wv);
+      pin_decoded(wv);
       if (!group_wait(a.gu_done + ((size_t)l * P + p) * kPollStride, ncg * ngg, a.error, &sh.ok))
         return;
       claim_next(a.ticket, next);
@@ -394,6 +418,9 @@ hipError_t resident(int* groups) {
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stack_decode<KG, KD>, 256, 0);
   if (e != hipSuccess) return e;
+  // two groups per compute unit measured fastest at batch 1 (more groups
+  // decode further ahead but poll more and lengthen every memory round trip)
+  if (per_cu > kGroupsPerCu) per_cu = kGroupsPerCu;
   *groups = cus * per_cu;
   return hipSuccess;
 }
