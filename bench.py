@@ -44,8 +44,8 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--pool", type=int, default=8, help="independent steps cycled")
-    ap.add_argument("--path", choices=["persistent", "layered"], default="layered",
-                    help="stack: three launches per layer (default) or one persistent launch")
+    ap.add_argument("--path", choices=["flow", "layered"], default="flow",
+                    help="stack: one launch for all layers (default) or three launches per layer")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -194,8 +194,9 @@ def layer_workload(args, log):
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     ms = hip.elapsed_ms(start, stop) / args.steps
-    layer_ms = float(np.mean([hip.elapsed_ms(*p["ev"]) for p in pool]))
-    distinct = np.mean([len(set(p["ids"].cpu().numpy().ravel().tolist())) for p in pool])
+    ran = [p for p in pool if "ids" in p]  # entries some step reached
+    layer_ms = float(np.mean([hip.elapsed_ms(*p["ev"]) for p in ran]))
+    distinct = np.mean([len(set(p["ids"].cpu().numpy().ravel().tolist())) for p in ran])
     code_bytes = distinct * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR)
     flops = 2.0 * T * k * (2048 * 1024 + 512 * 2048)
     out = {
@@ -270,10 +271,10 @@ def main():
     stack = escha.Stack(layers)
     hip = Hip()
 
-    persistent = args.path == "persistent"
-    stack_fn = (escha.escha_moe_stack_decode_persistent if persistent
+    one_launch = args.path == "flow"
+    stack_fn = (escha.escha_moe_stack_decode_persistent if one_launch
                 else escha.escha_moe_stack_decode)
-    n_probe = 2 if persistent else 2 * NL
+    n_probe = 2 if one_launch else 2 * NL
 
     # a pool of independent steps, each with its own buffers (so each can be
     # captured in its own graph)
@@ -334,11 +335,13 @@ def main():
     ms_total = hip.elapsed_ms(start, stop)
     ms_per_step = ms_total / args.steps
 
-    # probe durations of each pool entry's last step: the persistent kernel
+    # probe durations of each pool entry's last step: the one-launch kernel
     # (one per step) or each layer's three launches
     probe_ms = []
     if not args.no_probe:
         for p in pool:
+            if "ids" not in p:
+                continue
             for j in range(n_probe // 2):
                 probe_ms.append(hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]))
     probe_avg_ms = float(np.mean(probe_ms)) if probe_ms else None
@@ -347,6 +350,8 @@ def main():
     # routes to (at batch 1 every one of the 8 is distinct), averaged over the pool
     distinct = []
     for p in pool:
+        if "ids" not in p:  # a pool entry no step reached (fewer steps than entries)
+            continue
         ids = p["ids"].view(NL, T * k).cpu().numpy()
         distinct.append(sum(len(set(row.tolist())) for row in ids))
     code_bytes_step = int(np.mean(distinct) * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR))
@@ -355,9 +360,9 @@ def main():
 
     roofline = None
     if probe_avg_ms:
-        launch_bytes = code_bytes_step if persistent else code_bytes_step / NL
+        launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
         achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
-        kernel = ("k_stack_decode (one persistent launch: all layers)" if persistent else
+        kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
                   "one layer's decode launches (k_in_partial + k_down_partial + k_combine)")
         roofline = {"kernel": kernel, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -367,6 +372,8 @@ def main():
                     "samples": len(probe_ms)}
 
     checks = {}
+    if one_launch:  # every timed call completed (no wait gave up)
+        checks["status"] = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pool))
     cpu = None
     if not args.no_cpu_baseline:
         p0 = pool[0]

@@ -285,35 +285,50 @@ int check_layer_call(const escha_moe_layer_t* L, const uint16_t* x, int32_t T, c
 
 
 // ---------------------------------------------------------------- stack
-// Control block at the start of a stack workspace: a 64-int header (ticket,
-// status word) and the persistent kernel's dependency counters, one per
-// kCtrStride ints: gate_up tasks done per (layer, pair), down tasks done per
-// (layer, token, output group), groups combined per (layer, token).
-constexpr int64_t kCtlHeaderInts = 64;
+// Control block at the start of a stack workspace: a 512-int header (word 1:
+// status of the one-launch path; words 256 + 32x: XCD x's task ticket) and
+// that path's flag words (zeroed before
+// every launch): per (layer, pair) one word per gate_up task and one per
+// down task, per (layer, token, XCD) one word per combine task. Each group
+// of words that one XCD writes starts on a 128-byte line of its own.
+constexpr int64_t kCtlHeaderInts = 512;  // word 1: status; words 256 + 32x: XCD x's ticket
 
-int64_t stack_ctl_ints(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
-  const int64_t P = T * L->top_k;
-  const int64_t ngd = L->hidden / 256;
-  return kCtlHeaderInts + n_layers * (P * escha::kPollStride + T * ngd * escha::kCtrStride +
-                                      T * escha::kYRep * escha::kPollStride);
+int64_t round32(int64_t n) { return (n + 31) / 32 * 32; }
+
+struct FlowLayout {
+  int64_t p8, gf_pair, df_pair, cf_x, ss_x;
+  int64_t gflag, dflag, cflag, ctl_ints;  // offsets / total, in ints
+  size_t gu_part, dn_part, dn_copy, ycb, sscb, data_bytes;  // offsets in bytes from the data start
+};
+
+FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
+  FlowLayout f{};
+  const int64_t H = L->hidden, I = L->inter;
+  f.p8 = (T * L->top_k + 7) / 8 * 8;
+  f.gf_pair = round32((H / 128) * (2 * I / 256));
+  f.df_pair = round32((I / 128) * (H / 256));
+  f.cf_x = round32(H / 256);
+  f.ss_x = round32(H / 128);
+  f.gflag = kCtlHeaderInts;
+  f.dflag = f.gflag + n_layers * f.p8 * f.gf_pair;
+  f.cflag = f.dflag + n_layers * f.p8 * f.df_pair;
+  f.ctl_ints = f.cflag + n_layers * T * 8 * f.cf_x;
+  f.dn_copy = (size_t)f.p8 * (I / 128) * H;
+  size_t off = 0;
+  f.gu_part = off;
+  off += round_up((size_t)f.p8 * (H / 128) * (2 * I) * sizeof(float));
+  f.dn_part = off;
+  off += round_up(2 * f.dn_copy * sizeof(float));
+  f.ycb = off;
+  off += round_up((size_t)T * 8 * H * sizeof(float));
+  f.sscb = off;
+  off += round_up((size_t)T * 8 * f.ss_x * sizeof(float));
+  f.data_bytes = off;
+  return f;
 }
 
 size_t stack_ctl_bytes(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
-  return round_up((size_t)stack_ctl_ints(L, n_layers, T) * sizeof(int32_t));
-}
-
-// Per-layer outputs of the persistent path (every layer but the last, each
-// at an address of its own): y [n_layers-1][T][hidden], then the sums of
-// squares [n_layers-1][T][ss_tok], one 256-byte-aligned row per token so
-// that no cache line holds two tokens' sums.
-int64_t stack_ss_tok(const escha_moe_layer_t* L) { return (L->hidden / 128 + 63) / 64 * 64; }
-
-int64_t stack_ss_stride(const escha_moe_layer_t* L, int64_t T) { return T * stack_ss_tok(L); }
-
-size_t stack_layer_bufs_bytes(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
-  const int64_t n = n_layers - 1;
-  return round_up((size_t)n * T * L->hidden * sizeof(float)) +
-         round_up((size_t)n * stack_ss_stride(L, T) * sizeof(float));
+  return round_up((size_t)flow_layout(L, n_layers, T).ctl_ints * sizeof(int32_t));
 }
 
 int check_stack_call(const escha_moe_layer_t* layers, int32_t n_layers, const uint16_t* x0_bf16,
@@ -504,9 +519,11 @@ size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t 
                                        int32_t n_tokens) {
   if (!layers || n_layers < 1 || n_tokens < 0) return 0;
   const escha_moe_layer_t* L = &layers[0];
+  // the control block, then the layer-by-layer path's buffers, then the
+  // one-launch path's
   const size_t ybuf = round_up((size_t)n_tokens * L->hidden * sizeof(float));
   return stack_ctl_bytes(L, n_layers, n_tokens) + decode_ws_bytes(L, n_tokens) + ybuf +
-         stack_layer_bufs_bytes(L, n_layers, n_tokens);
+         flow_layout(L, n_layers, n_tokens).data_bytes;
 }
 
 int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
@@ -570,24 +587,25 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
     if (L->gate_up.n_experts != L0->gate_up.n_experts || L->gate_up.k_bits != L0->gate_up.k_bits ||
         L->down.k_bits != L0->down.k_bits)
       return fail(ESCHA_E_UNSUPPORTED,
-                  "layer %d differs from layer 0 in n_experts or k_bits (persistent path)", l);
+                  "layer %d differs from layer 0 in n_experts or k_bits (one-launch path)", l);
   }
+  const int64_t T = n_tokens, H = L0->hidden, I = L0->inter, k = L0->top_k;
+  // one wave polls all the flags a task waits for
+  if (2 * (H / 128) > 64 || k * (I / 128) > 64 || H / 256 > 64)
+    return fail(ESCHA_E_UNSUPPORTED, "hidden=%lld / top_k*inter/128=%lld exceed the one-launch path",
+                (long long)H, (long long)(k * (I / 128)));
   if (n_tokens == 0) return ESCHA_OK;
-  const int64_t T = n_tokens, P = T * L0->top_k, H = L0->hidden, I = L0->inter;
-  const int64_t per_layer = P * (H / 128) * (2 * I / 256) + P * (I / 128) * (H / 256);
-  const int64_t n_tasks = per_layer * n_layers;
-  if (n_tasks > ((int64_t)1 << 30))
-    return fail(ESCHA_E_UNSUPPORTED, "%lld tasks exceed the task counter", (long long)n_tasks);
+  const int64_t blocks = escha::flow_blocks_per_layer((int)H, (int)I, (int)k, (int)T) * n_layers;
+  if (blocks + escha::kFlowSpare > 0x7FFFFFFF)
+    return fail(ESCHA_E_UNSUPPORTED, "%lld work-groups exceed one grid", (long long)blocks);
 
   hipStream_t s = (hipStream_t)stream;
+  const FlowLayout f = flow_layout(L0, n_layers, T);
   int32_t* ctl = (int32_t*)workspace;
-  char* b = (char*)workspace + stack_ctl_bytes(L0, n_layers, T);
-  const DecodeWs ws = decode_ws_carve(L0, T, b);
-  b += decode_ws_bytes(L0, T) + round_up((size_t)T * H * sizeof(float));
-  float* y_layers = (float*)b;
-  float* ss_layers = (float*)(b + round_up((size_t)(n_layers - 1) * T * H * sizeof(float)));
+  char* data = (char*)workspace + stack_ctl_bytes(L0, n_layers, T) + decode_ws_bytes(L0, T) +
+               round_up((size_t)T * H * sizeof(float));
 
-  escha::StackArgs a{};
+  escha::FlowArgs a{};
   for (int l = 0; l < n_layers; ++l) {
     a.layer[l].gu_code = (const uint16_t*)layers[l].gate_up.code;
     a.layer[l].gu_rin = (const uint16_t*)layers[l].gate_up.rin;
@@ -598,41 +616,39 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   }
   a.n_layers = n_layers;
   a.n_tokens = n_tokens;
-  a.top_k = L0->top_k;
-  a.hidden = L0->hidden;
-  a.inter = L0->inter;
+  a.top_k = (int32_t)k;
+  a.hidden = (int32_t)H;
+  a.inter = (int32_t)I;
   a.n_experts = L0->gate_up.n_experts;
-  a.n_tasks = (int32_t)n_tasks;
+  a.p8 = (int32_t)f.p8;
   a.eps = eps;
   a.ids = topk_ids;
   a.w = topk_w;
   a.x0 = x0_bf16;
-  a.y_layers = y_layers;
-  a.ss_layers = ss_layers;
-  a.ss_stride = stack_ss_stride(L0, T);
-  a.ss_tok = (int32_t)stack_ss_tok(L0);
   a.y_last = y_last;
   a.x_chain = x_chain;
-  a.gu_part = ws.gu_part;
-  a.dn_part = ws.dn_part;
-  a.ticket = ctl;
+  a.gu_part = (float*)(data + f.gu_part);
+  a.dn_part = (float*)(data + f.dn_part);
+  a.dn_copy = (int64_t)f.dn_copy;
+  a.ycb = (float*)(data + f.ycb);
+  a.sscb = (float*)(data + f.sscb);
+  a.ss_x = (int32_t)f.ss_x;
+  a.gflag = ctl + f.gflag;
+  a.gf_pair = (int32_t)f.gf_pair;
+  a.dflag = ctl + f.dflag;
+  a.df_pair = (int32_t)f.df_pair;
+  a.cflag = ctl + f.cflag;
+  a.cf_x = (int32_t)f.cf_x;
+  a.cf_tok = (int32_t)(8 * f.cf_x);
+  a.ticket = ctl + 256;
   a.error = ctl + 1;
-  a.gu_done = ctl + kCtlHeaderInts;
-  a.c_done = a.gu_done + (size_t)n_layers * P * escha::kPollStride;
-  a.y_done = a.c_done + (size_t)n_layers * T * (H / 256) * escha::kCtrStride;
 
-  int groups = 0;
-  hipError_t e = escha::stack_resident_groups(L0->gate_up.k_bits, L0->down.k_bits, &groups);
-  if (e != hipSuccess) return hip_fail(e, "occupancy query");
-  if (groups < 1) return fail(ESCHA_E_HIP, "persistent kernel does not fit on the device");
-  if ((int64_t)groups > n_tasks) groups = (int)n_tasks;
-
-  e = escha::launch_fill_zero(ctl, (size_t)stack_ctl_ints(L0, n_layers, T), s);
-  if (e != hipSuccess) return hip_fail(e, "counter clear launch");
+  hipError_t e = escha::launch_fill_zero(ctl, (size_t)f.ctl_ints, s);
+  if (e != hipSuccess) return hip_fail(e, "flag clear launch");
   if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[0], s)) != hipSuccess)
     return hip_fail(e, "probe event record");
-  e = escha::launch_stack_decode(a, L0->gate_up.k_bits, L0->down.k_bits, groups, s);
-  if (e != hipSuccess) return hip_fail(e, "persistent stack launch");
+  e = escha::launch_stack_flow(a, L0->gate_up.k_bits, L0->down.k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "one-launch stack launch");
   if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[1], s)) != hipSuccess)
     return hip_fail(e, "probe event record");
   return ESCHA_OK;

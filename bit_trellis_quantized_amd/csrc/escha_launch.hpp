@@ -103,12 +103,9 @@ struct SortedCombineArgs {
   float* ss;  // nullable
 };
 
-// Persistent decode of a whole stack of layers (escha_stack.hip). Every
+// Decode of a whole stack of layers in one launch (escha_stack.hip). Every
 // layer has the same hidden/inter/top_k/n_experts and the same k_bits pair.
 constexpr int kMaxStackLayers = 64;
-constexpr int kCtrStride = 16;    // ints between two counters nobody polls (64 B)
-constexpr int kPollStride = 256;  // ints between two polled counters (1 KB)
-constexpr int kYRep = 8;          // copies of each per-token layer-done counter
 
 struct StackLayer {
   const uint16_t* gu_code;
@@ -119,34 +116,38 @@ struct StackLayer {
   const uint16_t* dn_rout;
 };
 
-struct StackArgs {
+// Flag words are zero at launch and set to 1 once; every region written by
+// one XCD starts on a 128-byte line of its own.
+struct FlowArgs {
   StackLayer layer[kMaxStackLayers];
-  int32_t n_layers, n_tokens, top_k, hidden, inter, n_experts, n_tasks;
+  int32_t n_layers, n_tokens, top_k, hidden, inter, n_experts;
+  int32_t p8;          // n_tokens * top_k rounded up to a multiple of 8
   float eps;
   const int32_t* ids;  // [n_layers][n_tokens * top_k]
   const float* w;      // same layout
   const uint16_t* x0;  // bf16 [n_tokens][hidden]
-  float* y_layers;     // fp32 [n_layers - 1][n_tokens][hidden]: outputs of every layer but the last
-  float* ss_layers;    // fp32 [n_layers - 1][n_tokens][ss_tok]: their per-128-block sums of squares
-  int64_t ss_stride;   // n_tokens * ss_tok
-  int32_t ss_tok;      // hidden/128 rounded up to a multiple of 64 (256 B)
   float* y_last;       // fp32 [n_tokens][hidden]
   uint16_t* x_chain;   // nullable: bf16 [n_layers][n_tokens][hidden]
-  float* gu_part;      // [P][hidden/128][2*inter]
-  float* dn_part;      // [P][inter/128][hidden]
-  int32_t* ticket;     // next task number
-  int32_t* error;      // set to 1 when a wait gives up
-  int32_t* gu_done;    // [n_layers][P] gate_up tasks finished per pair (kPollStride apart)
-  int32_t* c_done;     // [n_layers][n_tokens][hidden/256] down tasks finished per output group
-                       // (kCtrStride apart)
-  int32_t* y_done;     // [n_layers][n_tokens][kYRep] output groups combined per token, every
-                       // copy counting the same (kPollStride apart)
+  float* gu_part;      // [p8][hidden/128][2*inter], written and read on the pair's XCD
+  float* dn_part;      // 2 copies of [p8][inter/128][hidden], read on every XCD
+  int64_t dn_copy;     // floats per copy
+  float* ycb;          // [n_tokens][8][hidden]: each XCD's copy of the layer output
+  float* sscb;         // [n_tokens][8][ss_x]: its per-128-block sums of squares
+  int32_t ss_x;
+  int32_t* gflag;      // [n_layers][p8][gf_pair]: gate_up task (g, c) at g * (hidden/128) + c
+  int32_t gf_pair;
+  int32_t* dflag;      // [n_layers][p8][df_pair]: down task (c, g) at c * (hidden/256) + g
+  int32_t df_pair;
+  int32_t* cflag;      // [n_layers][n_tokens][8][cf_x]: combine task (x, g) at x * cf_x + g
+  int32_t cf_tok, cf_x;
+  int32_t* ticket;     // [8][32]: next task of each XCD (word 32x)
+  int32_t* error;      // 1: a wait gave up
 };
+constexpr int kFlowSpare = 64;  // work-groups launched beyond the task count (8 per XCD)
 
-// Work-groups of the persistent kernel that fit on the device at once.
-hipError_t stack_resident_groups(int k_gu, int k_dn, int* groups);
+int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens);
 hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s);
-hipError_t launch_stack_decode(const StackArgs& a, int k_gu, int k_dn, int groups, hipStream_t s);
+hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s);
 
 hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,
                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s);

@@ -203,20 +203,23 @@ ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_
                            void* stream);
 
 /*
- * The same stack in ONE persistent kernel launch (plus a small kernel that
- * clears the launch's dependency counters first). Same arguments, same
- * workspace size, and results bit-identical to escha_moe_stack_decode: the
- * per-task arithmetic is shared. Work is handed out as numbered tasks
- * through an atomic counter; a work-group loads and decodes a task's codes
- * before waiting for the outputs the task reads, so code streaming and
- * decode of later layers overlap the dependency chain of earlier ones.
+ * The same stack in ONE kernel launch (plus a small kernel that clears the
+ * launch's flag words first). Same arguments, same workspace size, and
+ * results bit-identical to escha_moe_stack_decode: the per-task arithmetic
+ * is shared. Every task of every layer (gate_up and down pieces of one
+ * (token, expert) pair, and the per-token combine) is one work-group; a
+ * work-group loads and decodes its codes before it waits for the outputs
+ * it reads, so code streaming and decode of later layers overlap the
+ * dependency chain of earlier ones. The tasks of one pair run on one XCD of
+ * the device and exchange data through that XCD's L2.
  * Additional requirements: n_layers <= 64; every layer has the same
- * n_experts and the same gate_up and down k_bits; n_tokens <= 64.
+ * n_experts and the same gate_up and down k_bits; n_tokens <= 64;
+ * hidden <= 4096; top_k * inter / 128 <= 64.
  * probe_events (nullable): a HOST array of 2 hipEvent_t handles, recorded
- * right before and right after the persistent kernel.
- * A dependency wait that exceeds its bound (it cannot happen while the
- * device makes progress) makes every work-group stop at its next wait; the
- * outputs are then incomplete and escha_moe_stack_status reports 1.
+ * right before and right after the kernel.
+ * A dependency wait that exceeds its bound (half a second; it cannot happen
+ * while the device makes progress) makes every work-group stop at its next
+ * wait; the outputs are then incomplete and escha_moe_stack_status reports 1.
  * Calls sharing one workspace must be ordered (same stream or synchronised).
  */
 ESCHA_API int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n_layers,
