@@ -296,33 +296,30 @@ constexpr int64_t kCtlHeaderInts = 512;  // word 1: status; words 256 + 32x: XCD
 int64_t round32(int64_t n) { return (n + 31) / 32 * 32; }
 
 struct FlowLayout {
-  int64_t p8, gf_pair, df_pair, cf_x, ss_x;
+  int64_t p8, gf_pair, df_pair, cf_x;
   int64_t gflag, dflag, cflag, ctl_ints;  // offsets / total, in ints
-  size_t gu_part, dn_part, dn_copy, ycb, sscb, data_bytes;  // offsets in bytes from the data start
+  size_t gu_part, dn_part, dn_copy, xcb, data_bytes;  // offsets in bytes from the data start
 };
 
 FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
   FlowLayout f{};
   const int64_t H = L->hidden, I = L->inter;
   f.p8 = (T * L->top_k + 7) / 8 * 8;
-  f.gf_pair = round32((H / 128) * (2 * I / 256));
-  f.df_pair = round32((I / 128) * (H / 256));
-  f.cf_x = round32(H / 256);
-  f.ss_x = round32(H / 128);
+  f.gf_pair = round32((H / 512) * (2 * I / 256));
+  f.df_pair = round32(H / 256);
+  f.cf_x = 32;
   f.gflag = kCtlHeaderInts;
   f.dflag = f.gflag + n_layers * f.p8 * f.gf_pair;
   f.cflag = f.dflag + n_layers * f.p8 * f.df_pair;
   f.ctl_ints = f.cflag + n_layers * T * 8 * f.cf_x;
-  f.dn_copy = (size_t)f.p8 * (I / 128) * H;
+  f.dn_copy = (size_t)f.p8 * H;
   size_t off = 0;
   f.gu_part = off;
-  off += round_up((size_t)f.p8 * (H / 128) * (2 * I) * sizeof(float));
+  off += round_up((size_t)f.p8 * (H / 512) * (2 * I) * sizeof(float));
   f.dn_part = off;
   off += round_up(2 * f.dn_copy * sizeof(float));
-  f.ycb = off;
+  f.xcb = off;
   off += round_up((size_t)T * 8 * H * sizeof(float));
-  f.sscb = off;
-  off += round_up((size_t)T * 8 * f.ss_x * sizeof(float));
   f.data_bytes = off;
   return f;
 }
@@ -590,10 +587,14 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
                   "layer %d differs from layer 0 in n_experts or k_bits (one-launch path)", l);
   }
   const int64_t T = n_tokens, H = L0->hidden, I = L0->inter, k = L0->top_k;
-  // one wave polls all the flags a task waits for
-  if (2 * (H / 128) > 64 || k * (I / 128) > 64 || H / 256 > 64)
-    return fail(ESCHA_E_UNSUPPORTED, "hidden=%lld / top_k*inter/128=%lld exceed the one-launch path",
-                (long long)H, (long long)(k * (I / 128)));
+  // task shapes of the one-launch kernel: gate_up quarters of four 128-input
+  // chunks, one down task over all channels (at most four 128-blocks), one
+  // wave polling all the flags a task waits for
+  if (H % 512 != 0 || H > 4096 || I > 512 || k * (H / 256) > 64)
+    return fail(ESCHA_E_UNSUPPORTED,
+                "one-launch path needs hidden %% 512 == 0, hidden <= 4096, inter <= 512 and "
+                "top_k * hidden / 256 <= 64 (hidden=%lld inter=%lld top_k=%lld)",
+                (long long)H, (long long)I, (long long)k);
   if (n_tokens == 0) return ESCHA_OK;
   const int64_t blocks = escha::flow_blocks_per_layer((int)H, (int)I, (int)k, (int)T) * n_layers;
   if (blocks + escha::kFlowSpare > 0x7FFFFFFF)
@@ -630,9 +631,7 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   a.gu_part = (float*)(data + f.gu_part);
   a.dn_part = (float*)(data + f.dn_part);
   a.dn_copy = (int64_t)f.dn_copy;
-  a.ycb = (float*)(data + f.ycb);
-  a.sscb = (float*)(data + f.sscb);
-  a.ss_x = (int32_t)f.ss_x;
+  a.xcb = (float*)(data + f.xcb);
   a.gflag = ctl + f.gflag;
   a.gf_pair = (int32_t)f.gf_pair;
   a.dflag = ctl + f.dflag;
@@ -645,6 +644,10 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
 
   hipError_t e = escha::launch_fill_zero(ctl, (size_t)f.ctl_ints, s);
   if (e != hipSuccess) return hip_fail(e, "flag clear launch");
+  if (x_chain) {  // layer 0's input; the kernel writes the others
+    e = hipMemcpyAsync(x_chain, x0_bf16, (size_t)T * H * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "x_chain copy");
+  }
   if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[0], s)) != hipSuccess)
     return hip_fail(e, "probe event record");
   e = escha::launch_stack_flow(a, L0->gate_up.k_bits, L0->down.k_bits, s);

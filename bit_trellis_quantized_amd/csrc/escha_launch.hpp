@@ -128,17 +128,15 @@ struct FlowArgs {
   const uint16_t* x0;  // bf16 [n_tokens][hidden]
   float* y_last;       // fp32 [n_tokens][hidden]
   uint16_t* x_chain;   // nullable: bf16 [n_layers][n_tokens][hidden]
-  float* gu_part;      // [p8][hidden/128][2*inter], written and read on the pair's XCD
-  float* dn_part;      // 2 copies of [p8][inter/128][hidden], read on every XCD
+  float* gu_part;      // [p8][hidden/512][2*inter], written and read on the pair's XCD
+  float* dn_part;      // 2 copies of [p8][hidden]: each pair's weighted output, read on every XCD
   int64_t dn_copy;     // floats per copy
-  float* ycb;          // [n_tokens][8][hidden]: each XCD's copy of the layer output
-  float* sscb;         // [n_tokens][8][ss_x]: its per-128-block sums of squares
-  int32_t ss_x;
-  int32_t* gflag;      // [n_layers][p8][gf_pair]: gate_up task (g, c) at g * (hidden/128) + c
+  float* xcb;          // [n_tokens][8][hidden]: each XCD's copy of the next layer's input
+  int32_t* gflag;      // [n_layers][p8][gf_pair]: gate_up task (quarter cq, group g) at cq * ngg + g
   int32_t gf_pair;
-  int32_t* dflag;      // [n_layers][p8][df_pair]: down task (c, g) at c * (hidden/256) + g
+  int32_t* dflag;      // [n_layers][p8][df_pair]: down task of output group g at g
   int32_t df_pair;
-  int32_t* cflag;      // [n_layers][n_tokens][8][cf_x]: combine task (x, g) at x * cf_x + g
+  int32_t* cflag;      // [n_layers][n_tokens][8][cf_x]: combine task of (token, XCD) at word 0
   int32_t cf_tok, cf_x;
   int32_t* ticket;     // [8][32]: next task of each XCD (word 32x)
   int32_t* error;      // 1: a wait gave up

@@ -1,32 +1,38 @@
 // escha_stack.hip -- decode of a whole stack of MoE layers in one launch
 // (small batches: the token-by-token generation case).
 //
-// Every task of every layer is one work-group of a single grid, and the
-// work-groups are numbered in dependency order: layer by layer, first the
-// layer's gate_up tasks, then its down tasks, then its combine tasks.
-//   gate_up (pair p, 128-input chunk c, 256-output group g): the rotated
-//     inputs of the chunk (RMSNorm of the previous layer's output after the
-//     first layer), the decode of 8 tile-rows x 16 tiles and the output
-//     transform of the partial sums;
-//   down (p, 128-channel chunk c, output group g): h = SiLU(gate) * up from
-//     gate_up's partials, its rotation, the decode and the transform
-//     weighted by the router probability;
-//   combine (token t, XCD x, output group g): the fixed-order sum of the
-//     token's down partials over 256 outputs and the sums of squares of its
-//     two 128-blocks, for the next layer's RMSNorm.
-// The arithmetic of each task is that of the streaming kernels (the same
-// routines, the same order), so the results equal the layer-by-layer path
-// bit for bit.
+// Every task of every layer is one work-group of 16 waves, and the tasks
+// are numbered in dependency order: layer by layer, first the layer's
+// gate_up tasks, then its down tasks, then its combine tasks.
+//   gate_up (pair p, quarter cq of the inputs = four 128-input chunks,
+//     256-output group g): the rotated inputs of the four chunks, the decode
+//     of their 32 tile-rows x 16 tiles (two per wave), the sum over the
+//     chunks and the output transform of that sum;
+//   down (p, output group g): h = SiLU(gate) * up over all the intermediate
+//     channels from gate_up's quarter sums, its rotation (one 128-block per
+//     wave of the first four), the decode of every tile-row of the group
+//     (two per wave), the sum over the channels and the output transform,
+//     weighted by the router probability: the pair's finished output for
+//     the group;
+//   combine (token t, XCD x): the sum of the token's pair outputs in slot
+//     order, the RMSNorm (unit weight) and the rounding to bf16 of the next
+//     layer's input, which the next layer's gate_up tasks on XCD x read (in
+//     the last layer: the output y).
+// The arithmetic per projection is the method's (rin, H_n, the decoded
+// weights with fp32 accumulation, H_n, rout); the summation order differs
+// from the layer-by-layer kernels (here each task sums over more inputs
+// before the transform), so the two paths agree to rounding, not bit for
+// bit.
 //
 // A work-group first issues the loads of its codes and decodes them into
 // registers -- none of which depends on other tasks -- and only then waits
 // for the tasks whose outputs it reads. Work-groups start in index order
 // (per XCD), and every wait is on a task with a smaller number, so the
-// smallest unfinished task can always run; the device holds as many
-// later work-groups as fit, and their decode overlaps the dependency chain
-// of the earlier ones. Every wait is bounded all the same (by the constant
-// 100 MHz clock): when one gives up it sets the error word, and every
-// work-group leaves at its next wait.
+// smallest unfinished task can always run; the device holds as many later
+// work-groups as fit, and their decode overlaps the dependency chain of the
+// earlier ones. Every wait is bounded all the same (by the constant 100 MHz
+// clock): when one gives up it sets the error word, and every work-group
+// leaves at its next wait.
 //
 // Placement. Every XCD of the device has its own L2. Tasks are numbered so
 // that task i belongs to XCD i % 8 and all the tasks of pair p to XCD p % 8:
@@ -40,14 +46,14 @@
 // sc1 cache policy reads through the compute unit's cache to that L2 (or to
 // memory), so inside one XCD a plain store followed by an sc1 load is a
 // complete hand-off; a store with sc1 writes through to memory, which every
-// XCD's sc1 loads see. The down partials and their flags cross XCDs (sc1
-// stores); everything else is XCD-local (plain stores). Every load of data
-// written during the launch uses sc1.
+// XCD's sc1 loads see. The pair outputs of down and their flags cross XCDs
+// (sc1 stores); everything else is XCD-local (plain stores). Every load of
+// data written during the launch uses sc1.
 //
 // Buffers written during the launch and read by other work-groups are
 // reused from layer to layer where the dependency chain makes that safe (a
 // task that overwrites one waits, directly or transitively, for every task
-// that reads the previous contents); the down partials, which the combine
+// that reads the previous contents); the pair outputs, which the combine
 // tasks of all XCDs read, alternate between two copies by layer parity.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -139,25 +145,30 @@ __device__ __forceinline__ void pin_decoded(h16x2 (&wv)[NKT][32]) {
     }
 }
 
+constexpr int kWaves = 16;  // waves per work-group
+
 struct Lds {
-  float xs[128] __attribute__((aligned(16)));
-  float zs[256] __attribute__((aligned(16)));
-  float4 red[8][64];
-  int task, ok, go;
+  float xs[4][128] __attribute__((aligned(16)));  // rotated inputs of up to four 128-blocks
+  float gu[1024] __attribute__((aligned(16)));    // down: gate and up sums (2 * inter)
+  float zs[256] __attribute__((aligned(16)));     // summed partials of a 256-output group
+  float4 red[kWaves][64];
+  float ssb[32];
+  int skip[4];
+  int task, ok;
 };
 
-// Output transform of a 256-output group held in LDS (waves 0 and 1, one
-// 128-block each): H_n, then rout and the weight; REMOTE: sc1 stores.
-template <bool REMOTE>
-__device__ __forceinline__ void transform_out(const float* zs, float ro0, float ro1, float wt,
-                                              float* __restrict__ out, int wave, int lane) {
-  transform_store_rv<REMOTE>(zs, ro0, ro1, wt, out, wave, lane);
+// Sum of the 16 waves' partials (in wave order) into zs; wave 0.
+__device__ __forceinline__ void sum_waves(Lds& sh, int lane) {
+  float4 s = sh.red[0][lane];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) s = f4add(s, sh.red[w][lane]);
+  reinterpret_cast<float4*>(sh.zs)[lane] = s;
 }
 
 }  // namespace
 
 template <int KG, int KD>
-__global__ __launch_bounds__(256) void k_stack_flow(const FlowArgs a) {
+__global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   constexpr int kOwnG = Quarter<KG>::kOwn;
   constexpr int kOwnD = Quarter<KD>::kOwn;
   __shared__ Lds sh;
@@ -168,9 +179,10 @@ __global__ __launch_bounds__(256) void k_stack_flow(const FlowArgs a) {
   const int H = a.hidden, I = a.inter, k = a.top_k, T = a.n_tokens;
   const int P = T * k, P8 = a.p8;
   const int ncg = H / 128, ngg = (2 * I) / 256;  // gate_up chunks / groups
-  const int ncd = I / 128, ngd = H / 256;        // down chunks / groups
-  const int nb_gu = ncg * ngg * P8, nb_dn = ncd * ngd * P8;
-  const int per_layer = nb_gu + nb_dn + T * ngd * 8;
+  const int ncq = ncg / 4;                       // gate_up quarters (four chunks each)
+  const int ncd = I / 128, ngd = H / 256;        // down chunks (<= 4) / groups
+  const int nb_gu = ncq * ngg * P8, nb_dn = ngd * P8;
+  const int per_layer = nb_gu + nb_dn + T * 8;
 
   // claim this XCD's next task: the j-th work-group to start on XCD x runs
   // task 8j + x (the grid holds at least as many work-groups per XCD as the
@@ -188,6 +200,10 @@ __global__ __launch_bounds__(256) void k_stack_flow(const FlowArgs a) {
   const int l = bid / per_layer;
   int r = bid - l * per_layer;
   const StackLayer& Ly = a.layer[l];
+  // wave w works on 128-block cl = w / 4 of its task's inputs, tile-rows
+  // 2 (w % 4) and 2 (w % 4) + 1 of that block
+  const int cl = wave >> 2;
+  const int jr = 2 * (wave & 3);
 
   if (r < nb_gu) {
     // ------------------------------------------------------------ gate_up
@@ -195,14 +211,15 @@ __global__ __launch_bounds__(256) void k_stack_flow(const FlowArgs a) {
     if (p >= P) return;
     r /= P8;
     const int g = r % ngg;
-    const int c = r / ngg;
+    const int cq = r / ngg;
+    const int c = 4 * cq + cl;  // this wave's input chunk
     const int t = p / k;
     const int x = p & 7;
     const int e = a.ids[(size_t)l * P + p];
     const bool valid = e >= 0 && e < a.n_experts;
     const int n_nt = (2 * I) / 16;
     const int nt = g * 16 + (lane >> 2);
-    float* out = a.gu_part + ((size_t)p * ncg + c) * (2 * I) + g * 256;
+    float* out = a.gu_part + ((size_t)p * ncq + cq) * (2 * I) + g * 256;
 
     // an out-of-range id is decoded as expert 0 and its result discarded,
     // which keeps the register state the same on every path
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(256) void k_stack_flow(const FlowArgs a) {
     uint32_t raw[2][kOwnG];
     h16x2 wv[2][32];
     const uint16_t* code_e = Ly.gu_code + (size_t)es * (size_t)ncg * 8 * n_nt * (16 * KG);
-    issue_rows<KG, 2>(code_e, n_nt, 8 * c + 2 * wave, nt, q, raw);
+    issue_rows<KG, 2>(code_e, n_nt, 8 * c + jr, nt, q, raw);
     const uint16_t* rr = Ly.gu_rin + (size_t)es * H + c * 128;
     const float rin0 = f16_to_f32(rr[lane]);
     const float rin1 = f16_to_f32(rr[lane + 64]);
@@ -220,220 +237,202 @@ __global__ __launch_bounds__(256) void k_stack_flow(const FlowArgs a) {
     decode_rows<KG, 2>(raw, wv);
     pin_decoded(wv);
     if (l > 0) {
-      // the previous layer's combine tasks of this token on this XCD
+      // the previous layer's combine task of this token on this XCD
       const int32_t* cf = a.cflag + ((size_t)(l - 1) * T + t) * a.cf_tok + x * a.cf_x;
-      if (!group_wait(lane < ngd ? cf + lane : nullptr, a.error, &sh.ok)) return;
+      if (!group_wait(lane == 0 ? cf : nullptr, a.error, &sh.ok)) return;
     }
     __builtin_amdgcn_s_setprio(3);
 
-    if (wave == 0) {
+    if ((wave & 3) == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
       float x0, x1;
-      uint16_t* xo = nullptr;
-      if (a.x_chain && g == 0 && p % k == 0) xo = a.x_chain + ((size_t)l * T + t) * H + c * 128;
       if (l == 0) {
         const uint16_t* xr = a.x0 + (size_t)t * H + c * 128;
-        const uint16_t b0 = xr[lane], b1 = xr[lane + 64];
-        if (xo) {
-          xo[lane] = b0;
-          xo[lane + 64] = b1;
-        }
-        x0 = bf16_to_f32(b0);
-        x1 = bf16_to_f32(b1);
+        x0 = bf16_to_f32(xr[lane]);
+        x1 = bf16_to_f32(xr[lane + 64]);
       } else {
-        // RMSNorm of the previous layer's output row, rounded to bf16 (the
-        // arithmetic of the streaming gate_up kernel's prologue)
-        const float* yr = a.ycb + ((size_t)t * 8 + x) * H + c * 128;
-        const float* ss = a.sscb + ((size_t)t * 8 + x) * a.ss_x;
-        const float y0 = ld_fresh(yr + lane);
-        const float y1 = ld_fresh(yr + lane + 64);
-        // lane b loads block b's sum; the sum runs over the blocks in order
-        const float ssb = lane < ncg ? ld_fresh(ss + lane) : 0.f;
-        float tot = 0.f;
-#pragma unroll
-        for (int b = 0; b < 32; ++b)
-          if (b < ncg) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssb), b));
-        const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
-        const uint16_t b0 = f32_to_bf16_rne(y0 * inv);
-        const uint16_t b1 = f32_to_bf16_rne(y1 * inv);
-        if (xo) {
-          xo[lane] = b0;
-          xo[lane + 64] = b1;
-        }
-        x0 = bf16_to_f32(b0);
-        x1 = bf16_to_f32(b1);
+        const float* xr = a.xcb + ((size_t)t * 8 + x) * H + c * 128;
+        x0 = ld_fresh(xr + lane);
+        x1 = ld_fresh(xr + lane + 64);
       }
-      if (valid) {
-        float v0 = x0 * rin0;
-        float v1 = x1 * rin1;
-        fwht128(v0, v1);
-        sh.xs[lane] = v0 * kInvSqrt128;
-        sh.xs[lane + 64] = v1 * kInvSqrt128;
-      } else {  // an out-of-range expert id contributes nothing
-        reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      float v0 = x0 * rin0;
+      float v1 = x1 * rin1;
+      fwht128(v0, v1);
+      sh.xs[cl][lane] = v0 * kInvSqrt128;
+      sh.xs[cl][lane + 64] = v1 * kInvSqrt128;
     }
+    __syncthreads();
     if (valid) {  // uniform over the group
-      __syncthreads();
       float acc[16];
 #pragma unroll
       for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-      mac_decoded_row(wv[0], 2 * wave, q, sh.xs, acc);
-      mac_decoded_row(wv[1], 2 * wave + 1, q, sh.xs, acc);
+      mac_decoded_row(wv[0], jr, q, sh.xs[cl], acc);
+      mac_decoded_row(wv[1], jr + 1, q, sh.xs[cl], acc);
       sh.red[wave][lane] = quad_reduce_pick(acc, q);
       __syncthreads();
-      if (wave == 0) {
-        float4 s = sh.red[0][lane];
-        s = f4add(s, sh.red[1][lane]);
-        s = f4add(s, sh.red[2][lane]);
-        s = f4add(s, sh.red[3][lane]);
-        reinterpret_cast<float4*>(sh.zs)[lane] = s;
-      }
+      if (wave == 0) sum_waves(sh, lane);
       __syncthreads();
-      transform_out<false>(sh.zs, ro0, ro1, 1.0f, out, wave, lane);
+      transform_store_rv<false>(sh.zs, ro0, ro1, 1.0f, out, wave, lane);
+    } else if (wave == 0) {  // an out-of-range expert id contributes nothing
+      reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    group_signal<false>(a.gflag + ((size_t)l * P8 + p) * a.gf_pair + g * ncg + c);
+    group_signal<false>(a.gflag + ((size_t)l * P8 + p) * a.gf_pair + cq * ngg + g);
   } else if ((r -= nb_gu) < nb_dn) {
     // --------------------------------------------------------------- down
     const int p = r % P8;
     if (p >= P) return;
-    r /= P8;
-    const int g = r % ngd;
-    const int c = r / ngd;
+    const int g = r / P8;
     const int e = a.ids[(size_t)l * P + p];
     const bool valid = e >= 0 && e < a.n_experts;
+    const bool active = cl < ncd;  // this wave has tile-rows
     const int n_nt = H / 16;
     const int nt = g * 16 + (lane >> 2);
-    float* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + ((size_t)p * ncd + c) * H + g * 256;
+    float* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 256;
 
     const int es = valid ? e : 0;
     uint32_t raw[2][kOwnD];
     h16x2 wv[2][32];
     const uint16_t* code_e = Ly.dn_code + (size_t)es * (size_t)ncd * 8 * n_nt * (16 * KD);
-    issue_rows<KD, 2>(code_e, n_nt, 8 * c + 2 * wave, nt, q, raw);
-    const uint16_t* rr = Ly.dn_rin + (size_t)es * I + c * 128;
+    if (active) issue_rows<KD, 2>(code_e, n_nt, 8 * cl + jr, nt, q, raw);
+    const uint16_t* rr = Ly.dn_rin + (size_t)es * I + (active ? cl : 0) * 128;
     const float rin0 = f16_to_f32(rr[lane]);
     const float rin1 = f16_to_f32(rr[lane + 64]);
     const uint16_t* ro = Ly.dn_rout + (size_t)es * H + g * 256 + 128 * (wave & 1);
     const float ro0 = f16_to_f32(ro[lane]);
     const float ro1 = f16_to_f32(ro[lane + 64]);
     const float wt = a.w[(size_t)l * P + p];
-    decode_rows<KD, 2>(raw, wv);
+    if (active) decode_rows<KD, 2>(raw, wv);
     pin_decoded(wv);
     {
-      // gate_up tasks of this pair that produce the chunk's gate block (group
-      // 128c/256) and up block (group (I + 128c)/256), over every input chunk
+      // every gate_up task of this pair (all quarters, all groups)
       const int32_t* gf = a.gflag + ((size_t)l * P8 + p) * a.gf_pair;
-      const int gg = lane < ncg ? (128 * c) / 256 : (I + 128 * c) / 256;
-      const int32_t* mine = lane < 2 * ncg ? gf + gg * ncg + (lane % ncg) : nullptr;
-      if (!group_wait(mine, a.error, &sh.ok)) return;
+      if (!group_wait(lane < ncq * ngg ? gf + lane : nullptr, a.error, &sh.ok)) return;
     }
     __builtin_amdgcn_s_setprio(3);
 
-    // gate and up sums of this chunk's 128 channels: thread i sums value i
-    // (gate channel i, or up channel i-128) over gate_up's chunks, in order
+    // gate and up sums: thread i sums gate_up output i over the quarters
     if (valid) {
-      const int col = tid < 128 ? 128 * c + tid : I + 128 * c + (tid - 128);
-      const float* src = a.gu_part + (size_t)p * ncg * (2 * I) + col;
-      float s = 0.f;
-      for (int b0 = 0; b0 < ncg; b0 += 16) {
-        float v[16];
+      const float* src = a.gu_part + (size_t)p * ncq * (2 * I);
+      for (int i = tid; i < 2 * I; i += 1024) {
+        float v[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = b0 + i < ncg ? ld_fresh(src + (size_t)(b0 + i) * (2 * I)) : 0.f;
+        for (int j = 0; j < 8; ++j) v[j] = j < ncq ? ld_fresh(src + (size_t)j * (2 * I) + i) : 0.f;
+        float s = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (b0 + i < ncg) s += v[i];
+        for (int j = 0; j < 8; ++j)
+          if (j < ncq) s += v[j];
+        sh.gu[i] = s;
       }
-      sh.zs[tid] = s;
     }
     __syncthreads();
-    if (wave == 0) {
+    if ((wave & 3) == 0 && active) {  // one wave per 128-channel chunk
       int skip = 1;
       if (valid) {
-        const float h0 = silu(sh.zs[lane]) * sh.zs[128 + lane];
-        const float h1 = silu(sh.zs[lane + 64]) * sh.zs[192 + lane];
+        const float h0 = silu(sh.gu[128 * cl + lane]) * sh.gu[I + 128 * cl + lane];
+        const float h1 = silu(sh.gu[128 * cl + lane + 64]) * sh.gu[I + 128 * cl + lane + 64];
         skip = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
         float v0 = h0 * rin0;
         float v1 = h1 * rin1;
         fwht128(v0, v1);
-        sh.xs[lane] = v0 * kInvSqrt128;
-        sh.xs[lane + 64] = v1 * kInvSqrt128;
+        sh.xs[cl][lane] = v0 * kInvSqrt128;
+        sh.xs[cl][lane + 64] = v1 * kInvSqrt128;
       }
-      // an invalid expert, or a chunk whose h is all zero, contributes zero
-      if (skip) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st_agent(out + 4 * lane + i, 0.f);
-      }
-      if (lane == 0) sh.go = skip ? 0 : 1;
+      // a chunk whose h is all zero contributes exactly zero: its MAC is skipped
+      if (lane == 0) sh.skip[cl] = skip;
     }
     __syncthreads();
-    if (sh.go) {  // uniform over the group
-      float acc0[16], acc1[16];
+    if (valid) {  // uniform over the group
+      if (active && !sh.skip[cl]) {
+        float acc[16];
 #pragma unroll
-      for (int n = 0; n < 16; ++n) acc0[n] = acc1[n] = 0.f;
-      mac_decoded_row(wv[0], 2 * wave, q, sh.xs, acc0);
-      mac_decoded_row(wv[1], 2 * wave + 1, q, sh.xs, acc1);
-      sh.red[2 * wave][lane] = quad_reduce_pick(acc0, q);
-      sh.red[2 * wave + 1][lane] = quad_reduce_pick(acc1, q);
-      __syncthreads();
-      if (wave == 0) {
-        float4 s = sh.red[0][lane];
-#pragma unroll
-        for (int w = 1; w < 8; ++w) s = f4add(s, sh.red[w][lane]);
-        reinterpret_cast<float4*>(sh.zs)[lane] = s;
+        for (int n = 0; n < 16; ++n) acc[n] = 0.f;
+        mac_decoded_row(wv[0], jr, q, sh.xs[cl], acc);
+        mac_decoded_row(wv[1], jr + 1, q, sh.xs[cl], acc);
+        sh.red[wave][lane] = quad_reduce_pick(acc, q);
+      } else {
+        sh.red[wave][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
       }
       __syncthreads();
-      transform_out<true>(sh.zs, ro0, ro1, wt, out, wave, lane);
+      if (wave == 0) sum_waves(sh, lane);
+      __syncthreads();
+      transform_store_rv<true>(sh.zs, ro0, ro1, wt, out, wave, lane);
+    } else if (wave == 0) {  // an out-of-range expert id contributes nothing
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_agent(out + 4 * lane + i, 0.f);
     }
-    group_signal<true>(a.dflag + ((size_t)l * P8 + p) * a.df_pair + c * ngd + g);
+    group_signal<true>(a.dflag + ((size_t)l * P8 + p) * a.df_pair + g);
   } else {
     // ------------------------------------------------------------ combine
     r -= nb_dn;
     const int x = r & 7;
-    r >>= 3;
-    const int g = r % ngd;
-    const int t = r / ngd;
+    const int t = r >> 3;
     // combine tasks run only on XCDs that hold a pair of the token (the
     // next layer's gate_up tasks there read them); in the last layer only
-    // the XCD of the token's first pair runs them, to write y_last
+    // the XCD of the token's first pair runs one, to write y_last
     const int x_first = (t * k) & 7;
     const bool last = l == a.n_layers - 1;
     if (last ? x != x_first : (k < 8 && ((x - x_first) & 7) >= k)) return;
     {
+      // every down task of the token's pairs
       const int32_t* df = a.dflag + ((size_t)l * P8 + (size_t)t * k) * a.df_pair;
       const int32_t* mine =
-          lane < k * ncd ? df + (size_t)(lane / ncd) * a.df_pair + (lane % ncd) * ngd + g : nullptr;
+          lane < k * ngd ? df + (size_t)(lane / ngd) * a.df_pair + (lane % ngd) : nullptr;
       if (!group_wait(mine, a.error, &sh.ok)) return;
     }
     __builtin_amdgcn_s_setprio(3);
-    // wave w sums output (w & 1 ? lane + 64 : lane) of 128-block 2g + (w >> 1)
-    // over the token's rows (slot-major, chunk-minor), in order from 0
-    const int o = 256 * g + 128 * (wave >> 1) + 64 * (wave & 1) + lane;
-    const int n_rows = k * ncd;
-    const float* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)t * n_rows * H + o;
-    float acc = 0.f;
-    for (int b0 = 0; b0 < n_rows; b0 += 32) {
-      float v[32];
+    // wave w: 128-blocks w, w + 16, ..; lanes hold outputs lane and lane + 64
+    // of a block; the pair outputs are summed in slot order from 0
+    const int nb = H / 128;
+    const float* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)t * k * H;
+    float yv[2][2];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] = b0 + i < n_rows ? ld_fresh(pp + (size_t)(b0 + i) * H) : 0.f;
+    for (int s = 0; s < 2; ++s) {
+      const int b = wave + kWaves * s;
+      yv[s][0] = yv[s][1] = 0.f;
+      if (b < nb) {
+        float v[16][2];
 #pragma unroll
-      for (int i = 0; i < 32; ++i)
-        if (b0 + i < n_rows) acc += v[i];
+        for (int j = 0; j < 16; ++j) {
+          v[j][0] = j < k ? ld_fresh(pp + (size_t)j * H + 128 * b + lane) : 0.f;
+          v[j][1] = j < k ? ld_fresh(pp + (size_t)j * H + 128 * b + lane + 64) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (j < k) {
+            yv[s][0] += v[j][0];
+            yv[s][1] += v[j][1];
+          }
+        if (last) {
+          a.y_last[(size_t)t * H + 128 * b + lane] = yv[s][0];
+          a.y_last[(size_t)t * H + 128 * b + lane + 64] = yv[s][1];
+        } else {
+          const float sq = wave_sum(__builtin_fmaf(yv[s][0], yv[s][0], yv[s][1] * yv[s][1]));
+          if (lane == 0) sh.ssb[b] = sq;
+        }
+      }
     }
-    if (last) {
-      a.y_last[(size_t)t * H + o] = acc;
-      return;
-    }
-    sh.zs[o - 256 * g] = acc;
+    if (last) return;
     __syncthreads();
-    float* yx = a.ycb + ((size_t)t * 8 + x) * H + 256 * g;
-    yx[tid] = sh.zs[tid];
-    if (wave < 2) {  // block 2g + wave: its sum of squares
-      const float s0 = sh.zs[128 * wave + lane];
-      const float s1 = sh.zs[128 * wave + lane + 64];
-      const float sq = wave_sum(__builtin_fmaf(s0, s0, s1 * s1));
-      if (lane == 0) a.sscb[((size_t)t * 8 + x) * a.ss_x + 2 * g + wave] = sq;
+    // RMSNorm: the blocks' sums of squares in block order, then bf16
+    float tot = 0.f;
+    for (int b = 0; b < nb; ++b) tot += sh.ssb[b];
+    const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
+    float* xo = a.xcb + ((size_t)t * 8 + x) * H;
+    uint16_t* xc = (a.x_chain && x == x_first) ? a.x_chain + ((size_t)(l + 1) * T + t) * H : nullptr;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int b = wave + kWaves * s;
+      if (b < nb) {
+        const uint16_t b0 = f32_to_bf16_rne(yv[s][0] * inv);
+        const uint16_t b1 = f32_to_bf16_rne(yv[s][1] * inv);
+        xo[128 * b + lane] = bf16_to_f32(b0);
+        xo[128 * b + lane + 64] = bf16_to_f32(b1);
+        if (xc) {
+          xc[128 * b + lane] = b0;
+          xc[128 * b + lane + 64] = b1;
+        }
+      }
     }
-    group_signal<false>(a.cflag + ((size_t)l * T + t) * a.cf_tok + x * a.cf_x + g);
+    group_signal<false>(a.cflag + ((size_t)l * T + t) * a.cf_tok + x * a.cf_x);
   }
 }
 
@@ -453,14 +452,14 @@ hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s) {
 
 int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens) {
   const int64_t P8 = ((int64_t)n_tokens * top_k + 7) / 8 * 8;
-  return (int64_t)(hidden / 128) * (2 * inter / 256) * P8 + (int64_t)(inter / 128) * (hidden / 256) * P8 +
-         (int64_t)n_tokens * (hidden / 256) * 8;
+  return (int64_t)(hidden / 512) * (2 * inter / 256) * P8 + (int64_t)(hidden / 256) * P8 +
+         (int64_t)n_tokens * 8;
 }
 
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s) {
   const int64_t blocks =
       flow_blocks_per_layer(a.hidden, a.inter, a.top_k, a.n_tokens) * a.n_layers + kFlowSpare;
-  const dim3 grid((unsigned)blocks), block(256);
+  const dim3 grid((unsigned)blocks), block(1024);
   if (k_gu == 2 && k_dn == 3)
     hipLaunchKernelGGL((k_stack_flow<2, 3>), grid, block, 0, s, a);
   else if (k_gu == 2 && k_dn == 2)
