@@ -1,0 +1,212 @@
+// escha_mfma.hpp -- decode of trellis tiles straight into the operand layout
+// of the gfx950 matrix instruction v_mfma_f32_16x16x32_f16, and the
+// contraction of decoded tiles with activations on the matrix cores.
+//
+// Operand layouts of v_mfma_f32_16x16x32_f16 (D[16][16] += A[16][32] B[32][16]),
+// lane l of the wave: A[l % 16][8 (l / 16) + i] and B[8 (l / 16) + i][l % 16]
+// for i = 0..7 (8 halves, 4 registers); D[4 (l / 16) + j][l % 16] for
+// j = 0..3 (4 floats).
+//
+// Mapping: A is a pair of vertically adjacent 16x16 tiles (input tile-rows
+// kt and kt+1, output tile nt) with A's row m = output column n of the
+// tiles and A's k = 16 * (tile of the pair) + input row inside the tile; B
+// holds the 32 activations of those inputs, split into a high and a low
+// fp16 part in B's columns 0 and 1 (all other columns zero), so that
+// D[n][0] + D[n][1] is the fp32-accurate dot product of output n's weights
+// with the fp32 activations (the products of two fp16 values are exact in
+// fp32, and hi + lo carries 22 significant bits of each activation).
+//
+// A lane (n, g = l / 16) needs the 8 weights (input rows 8 (g & 1) + i of
+// tile g >> 1, column n): their states are the 16-bit windows at stream
+// bits K (16 (8 (g & 1) + i) + n). The codes of a wave's tiles are staged in
+// LDS first (one 16-byte load per lane and chunk, coalesced), each tile
+// followed by a copy of its first dword so that windows that run past the
+// end of the tile wrap without a special case.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "escha_device.hpp"
+
+namespace escha {
+
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// LDS staging of one wave's 8 tile-rows x 4 tiles.
+template <int K>
+struct Stage {
+  static constexpr int kTileDw = 8 * K;                 // dwords of a tile (16K words)
+  static constexpr int kStride = kTileDw + 1;           // + the wrap dword
+  static constexpr int kDw = 8 * 4 * kStride;           // dwords per wave
+  static constexpr int kChunks = 8 * 4 * kTileDw / 4;   // 16-byte chunks per wave
+  static constexpr int kPerLane = kChunks / 64;         // 2 (K=2) or 3 (K=3)
+};
+
+// Issue the global loads of tile-rows kt0..kt0+7, tiles nt0..nt0+3 (each
+// tile-row's four tiles are contiguous). Nothing waits for the data here.
+template <int K>
+__device__ __forceinline__ void stage_issue(const uint16_t* __restrict__ code_e, int n_nt, int kt0,
+                                            int nt0, int lane,
+                                            u32x4 (&v)[Stage<K>::kPerLane]) {
+  constexpr int kRowChunks = Stage<K>::kTileDw;  // 4 tiles x kTileDw dwords / 4 dwords per chunk
+#pragma unroll
+  for (int m = 0; m < Stage<K>::kPerLane; ++m) {
+    const int c = lane + 64 * m;
+    const int r = c / kRowChunks;
+    const int cc = c - r * kRowChunks;
+    const uint16_t* src = code_e + ((size_t)(kt0 + r) * n_nt + nt0) * (16 * K) + 8 * cc;
+    v[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  }
+}
+
+// Store the loaded chunks to the wave's LDS region (tile (r, j) at dword
+// (4 r + j) * kStride) with each tile's wrap dword; the wave can read them
+// back once this returns.
+template <int K>
+__device__ __forceinline__ void stage_store(uint32_t* lds, int lane,
+                                            const u32x4 (&v)[Stage<K>::kPerLane]) {
+  constexpr int kRowChunks = Stage<K>::kTileDw;
+  constexpr int kTileChunks = Stage<K>::kTileDw / 4;
+#pragma unroll
+  for (int m = 0; m < Stage<K>::kPerLane; ++m) {
+    const int c = lane + 64 * m;
+    const int r = c / kRowChunks;
+    const int cc = c - r * kRowChunks;
+    const int j = cc / kTileChunks;
+    const int d = 4 * (cc - j * kTileChunks);
+    uint32_t* t = lds + (4 * r + j) * Stage<K>::kStride;
+    t[d + 0] = v[m].x;
+    t[d + 1] = v[m].y;
+    t[d + 2] = v[m].z;
+    t[d + 3] = v[m].w;
+    if (d == 0) t[Stage<K>::kTileDw] = v[m].x;
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Decode, for every pair pp of adjacent tile-rows (2pp, 2pp+1) and tile j of
+// the staged region, this lane's 8 weights into A[pp][j] (A-operand layout).
+template <int K>
+__device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
+                                                  h16x8 (&A)[4][4]) {
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int h = g & 1;
+  // tile of the pair: rows 2pp + (g >> 1); lane-dependent part of the
+  // window positions
+  const uint32_t* base = lds + (g >> 1) * 4 * Stage<K>::kStride;
+  int a0, a1;
+  uint32_t s0, s1;
+  if constexpr (K == 2) {
+    // window i at bit 256h + 32i + 2n: dword 8h + i, shift 2n
+    a0 = a1 = 8 * h;
+    s0 = s1 = 2 * n;
+  } else {
+    // window i at bit 384h + 48i + 3n; for i = 2m: dword 12h + 3m + (3n >> 5),
+    // shift 3n & 31; for i = 2m + 1: dword 12h + 3m + ((48 + 3n) >> 5),
+    // shift (16 + 3n) & 31
+    a0 = 12 * h + ((3 * n) >> 5);
+    a1 = 12 * h + ((48 + 3 * n) >> 5);
+    s0 = (3 * n) & 31;
+    s1 = (16 + 3 * n) & 31;
+  }
+  const uint32_t* p0 = base + a0;
+  const uint32_t* p1 = base + a1;
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int toff = (2 * pp * 4 + j) * Stage<K>::kStride;
+      uint32_t win[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ci = K == 2 ? i : 3 * (i >> 1);
+        const uint32_t* p = (i & 1) ? p1 : p0;
+        win[i] = __builtin_amdgcn_alignbit(p[toff + ci + 1], p[toff + ci], (i & 1) ? s1 : s0);
+      }
+      h16x8 a;
+#pragma unroll
+      for (int i = 0; i < 8; i += 2) {
+        // states of rows 8h + i and 8h + i + 1 (low halves of two windows)
+        const h16x2 w = cba_decode_pair(__builtin_amdgcn_perm(win[i + 1], win[i], 0x05040100u));
+        a[i] = w.x;
+        a[i + 1] = w.y;
+      }
+      A[pp][j] = a;
+    }
+  }
+}
+
+static __device__ __noinline__ void scale_block(float m, float& scale, float& unscale);
+
+// Split a wave's 128 rotated activations (v0 at position lane, v1 at
+// lane + 64) into fp16 high and low parts for B, scaled by a power of two
+// that keeps the high part inside the fp16 range (1 unless the largest
+// magnitude exceeds 2^14). Returns the factor that undoes the scale.
+__device__ __forceinline__ float split_hilo(float v0, float v1, _Float16* xh, _Float16* xl,
+                                            int lane) {
+  float m = fmaxf(fabsf(v0), fabsf(v1));
+  float scale = 1.0f, unscale = 1.0f;
+  if (__ballot(!(m <= 16384.0f)) != 0) scale_block(m, scale, unscale);  // rare: large values
+  const float a0 = v0 * scale, a1 = v1 * scale;
+  const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
+  xh[lane] = h0;
+  xh[lane + 64] = h1;
+  xl[lane] = (_Float16)(a0 - (float)h0);
+  xl[lane + 64] = (_Float16)(a1 - (float)h1);
+  return unscale;
+}
+
+// The power-of-two scale of split_hilo for a block whose largest magnitude
+// exceeds 2^14 (m: this lane's largest magnitude; NaN and infinity leave the
+// scale at 1).
+static __device__ __noinline__ void scale_block(float m, float& scale, float& unscale) {
+  m = fmaxf(m, xor_lane<1>(m));
+  m = fmaxf(m, xor_lane<2>(m));
+  m = fmaxf(m, xor_lane<4>(m));
+  m = fmaxf(m, xor_lane<8>(m));
+  {
+    const unsigned u = __float_as_uint(m);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    const unsigned u = __float_as_uint(m);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  if (m > 16384.0f && m <= 3.0e38f) {
+    int ex;
+    frexpf(m * (1.0f / 16384.0f), &ex);
+    scale = ldexpf(1.0f, -ex);
+    unscale = ldexpf(1.0f, ex);
+  }
+}
+
+// B operand for the tile-row pair pp of a 128-input block: column 0 the
+// high parts, column 1 the low parts of inputs 32pp + 8 (l / 16) + i.
+__device__ __forceinline__ h16x8 make_b(const _Float16* xh, const _Float16* xl, int pp, int lane) {
+  const int col = lane & 15;
+  const int o = 32 * pp + 8 * (lane >> 4);
+  const h16x8 hi = *reinterpret_cast<const h16x8*>(xh + o);
+  const h16x8 lo = *reinterpret_cast<const h16x8*>(xl + o);
+  const h16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+  return col == 0 ? hi : (col == 1 ? lo : zero);
+}
+
+// z of the 4 tiles x 16 outputs of a wave from its accumulators: lane
+// 16g (g = 0..3) receives outputs 4g .. 4g+3 of tile j in zr[j] (high part
+// plus low part, times the unscale factor); other lanes' zr are unspecified.
+__device__ __forceinline__ void finish_mfma(const f32x4 (&D)[4], float unscale, float4 (&zr)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = (D[j][q] + dpp<0xF5>(D[j][q])) * unscale;  // + lane l+1 (column 1)
+    zr[j] = make_float4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+}  // namespace escha

@@ -60,6 +60,7 @@
 
 #include "escha_device.hpp"
 #include "escha_launch.hpp"
+#include "escha_mfma.hpp"
 #include "escha_stream.hpp"
 
 namespace escha {
@@ -147,35 +148,92 @@ __device__ __forceinline__ void pin_decoded(h16x2 (&wv)[NKT][32]) {
 
 constexpr int kWaves = 16;  // waves per work-group
 
+// Keep decoded operands where they are (see pin_decoded).
+__device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t u = __builtin_bit_cast(uint32_t, h16x2{A[pp][j][2 * i], A[pp][j][2 * i + 1]});
+        asm volatile("" : "+v"(u));
+        const h16x2 w = __builtin_bit_cast(h16x2, u);
+        A[pp][j][2 * i] = w.x;
+        A[pp][j][2 * i + 1] = w.y;
+      }
+}
+
 struct Lds {
-  float xs[4][128] __attribute__((aligned(16)));  // rotated inputs of up to four 128-blocks
-  float gu[1024] __attribute__((aligned(16)));    // down: gate and up sums (2 * inter)
-  float zs[256] __attribute__((aligned(16)));     // summed partials of a 256-output group
-  float4 red[kWaves][64];
+  uint32_t code[kWaves * Stage<3>::kDw];            // each wave's staged codes
+  _Float16 xh[4][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
+  _Float16 xl[4][128] __attribute__((aligned(16)));  // and their low parts
+  float xe[4];                                       // undo factor of each block's scale
+  float red[4][256] __attribute__((aligned(16)));    // per-block sums of a 256-output group
   float ssb[32];
   int skip[4];
   int task, ok;
 };
 
-// Sum of the 16 waves' partials (in wave order) into zs; wave 0.
-__device__ __forceinline__ void sum_waves(Lds& sh, int lane) {
-  float4 s = sh.red[0][lane];
+// Contract a wave's decoded tiles (8 tile-rows of 128-block cl x 4 output
+// tiles 4nq..4nq+3) with the block's activations on the matrix cores and
+// leave the 64 sums in sh.red[cl] (outputs 16 (4nq + j) + n of the group).
+__device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq,
+                                           int lane) {
+  f32x4 D[4];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) s = f4add(s, sh.red[w][lane]);
-  reinterpret_cast<float4*>(sh.zs)[lane] = s;
+  for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) {
+    const h16x8 B = make_b(sh.xh[cl], sh.xl[cl], pp, lane);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B, D[j], 0, 0, 0);
+  }
+  float4 zr[4];
+  finish_mfma(D, sh.xe[cl], zr);
+  if ((lane & 15) == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(&sh.red[cl][16 * (4 * nq + j) + 4 * (lane >> 4)]) = zr[j];
+  }
+}
+
+// Output transform of the group's 256 outputs: waves 0 and 1 sum their
+// 128-block over the first nb input blocks (in block order), apply H_n,
+// multiply by rout (ro0, ro1 at this lane's two outputs) and the weight, and
+// store (REMOTE: sc1 stores).
+template <bool REMOTE>
+__device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, float ro0, float ro1,
+                                                    float wt, float* __restrict__ out, int wave,
+                                                    int lane) {
+  if (wave < 2) {
+    const int o = 128 * wave + lane;
+    float z0 = sh.red[0][o], z1 = sh.red[0][o + 64];
+    for (int b = 1; b < nb; ++b) {
+      z0 += sh.red[b][o];
+      z1 += sh.red[b][o + 64];
+    }
+    fwht128(z0, z1);
+    const float o0 = z0 * kInvSqrt128 * ro0 * wt;
+    const float o1 = z1 * kInvSqrt128 * ro1 * wt;
+    if constexpr (REMOTE) {
+      st_agent(out + o, o0);
+      st_agent(out + o + 64, o1);
+    } else {
+      out[o] = o0;
+      out[o + 64] = o1;
+    }
+  }
 }
 
 }  // namespace
 
 template <int KG, int KD>
 __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
-  constexpr int kOwnG = Quarter<KG>::kOwn;
-  constexpr int kOwnD = Quarter<KD>::kOwn;
   __shared__ Lds sh;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
-  const int q = lane & 3;
   const int H = a.hidden, I = a.inter, k = a.top_k, T = a.n_tokens;
   const int P = T * k, P8 = a.p8;
   const int ncg = H / 128, ngg = (2 * I) / 256;  // gate_up chunks / groups
@@ -200,10 +258,10 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   const int l = bid / per_layer;
   int r = bid - l * per_layer;
   const StackLayer& Ly = a.layer[l];
-  // wave w works on 128-block cl = w / 4 of its task's inputs, tile-rows
-  // 2 (w % 4) and 2 (w % 4) + 1 of that block
+  // wave w works on 128-block cl = w / 4 of its task's inputs (its 8
+  // tile-rows) and output tiles 4 nq .. 4 nq + 3 (nq = w % 4) of the group
   const int cl = wave >> 2;
-  const int jr = 2 * (wave & 3);
+  const int nq = wave & 3;
 
   if (r < nb_gu) {
     // ------------------------------------------------------------ gate_up
@@ -218,24 +276,25 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const int e = a.ids[(size_t)l * P + p];
     const bool valid = e >= 0 && e < a.n_experts;
     const int n_nt = (2 * I) / 16;
-    const int nt = g * 16 + (lane >> 2);
     float* out = a.gu_part + ((size_t)p * ncq + cq) * (2 * I) + g * 256;
 
     // an out-of-range id is decoded as expert 0 and its result discarded,
     // which keeps the register state the same on every path
     const int es = valid ? e : 0;
-    uint32_t raw[2][kOwnG];
-    h16x2 wv[2][32];
     const uint16_t* code_e = Ly.gu_code + (size_t)es * (size_t)ncg * 8 * n_nt * (16 * KG);
-    issue_rows<KG, 2>(code_e, n_nt, 8 * c + jr, nt, q, raw);
+    u32x4 cv[Stage<KG>::kPerLane];
+    stage_issue<KG>(code_e, n_nt, 8 * c, 16 * g + 4 * nq, lane, cv);
     const uint16_t* rr = Ly.gu_rin + (size_t)es * H + c * 128;
     const float rin0 = f16_to_f32(rr[lane]);
     const float rin1 = f16_to_f32(rr[lane + 64]);
     const uint16_t* ro = Ly.gu_rout + (size_t)es * (2 * I) + g * 256 + 128 * (wave & 1);
     const float ro0 = f16_to_f32(ro[lane]);
     const float ro1 = f16_to_f32(ro[lane + 64]);
-    decode_rows<KG, 2>(raw, wv);
-    pin_decoded(wv);
+    uint32_t* stage = sh.code + wave * Stage<KG>::kDw;
+    stage_store<KG>(stage, lane, cv);
+    h16x8 A[4][4];
+    decode_stage_mfma<KG>(stage, lane, A);
+    pin_operands(A);
     if (l > 0) {
       // the previous layer's combine task of this token on this XCD
       const int32_t* cf = a.cflag + ((size_t)(l - 1) * T + t) * a.cf_tok + x * a.cf_x;
@@ -243,7 +302,7 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     }
     __builtin_amdgcn_s_setprio(3);
 
-    if ((wave & 3) == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
+    if (nq == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
       float x0, x1;
       if (l == 0) {
         const uint16_t* xr = a.x0 + (size_t)t * H + c * 128;
@@ -257,21 +316,14 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
       float v0 = x0 * rin0;
       float v1 = x1 * rin1;
       fwht128(v0, v1);
-      sh.xs[cl][lane] = v0 * kInvSqrt128;
-      sh.xs[cl][lane + 64] = v1 * kInvSqrt128;
+      const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cl], sh.xl[cl], lane);
+      if (lane == 0) sh.xe[cl] = xe;
     }
     __syncthreads();
     if (valid) {  // uniform over the group
-      float acc[16];
-#pragma unroll
-      for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-      mac_decoded_row(wv[0], jr, q, sh.xs[cl], acc);
-      mac_decoded_row(wv[1], jr + 1, q, sh.xs[cl], acc);
-      sh.red[wave][lane] = quad_reduce_pick(acc, q);
+      mfma_block(sh, A, cl, nq, lane);
       __syncthreads();
-      if (wave == 0) sum_waves(sh, lane);
-      __syncthreads();
-      transform_store_rv<false>(sh.zs, ro0, ro1, 1.0f, out, wave, lane);
+      sum_transform_store<false>(sh, 4, ro0, ro1, 1.0f, out, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
       reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
@@ -285,14 +337,12 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const bool valid = e >= 0 && e < a.n_experts;
     const bool active = cl < ncd;  // this wave has tile-rows
     const int n_nt = H / 16;
-    const int nt = g * 16 + (lane >> 2);
     float* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 256;
 
     const int es = valid ? e : 0;
-    uint32_t raw[2][kOwnD];
-    h16x2 wv[2][32];
     const uint16_t* code_e = Ly.dn_code + (size_t)es * (size_t)ncd * 8 * n_nt * (16 * KD);
-    if (active) issue_rows<KD, 2>(code_e, n_nt, 8 * cl + jr, nt, q, raw);
+    u32x4 cv[Stage<KD>::kPerLane];
+    if (active) stage_issue<KD>(code_e, n_nt, 8 * cl, 16 * g + 4 * nq, lane, cv);
     const uint16_t* rr = Ly.dn_rin + (size_t)es * I + (active ? cl : 0) * 128;
     const float rin0 = f16_to_f32(rr[lane]);
     const float rin1 = f16_to_f32(rr[lane + 64]);
@@ -300,8 +350,13 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const float ro0 = f16_to_f32(ro[lane]);
     const float ro1 = f16_to_f32(ro[lane + 64]);
     const float wt = a.w[(size_t)l * P + p];
-    if (active) decode_rows<KD, 2>(raw, wv);
-    pin_decoded(wv);
+    uint32_t* stage = sh.code + wave * Stage<KD>::kDw;
+    h16x8 A[4][4];
+    if (active) {
+      stage_store<KD>(stage, lane, cv);
+      decode_stage_mfma<KD>(stage, lane, A);
+    }
+    pin_operands(A);
     {
       // every gate_up task of this pair (all quarters, all groups)
       const int32_t* gf = a.gflag + ((size_t)l * P8 + p) * a.gf_pair;
@@ -309,32 +364,37 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     }
     __builtin_amdgcn_s_setprio(3);
 
-    // gate and up sums: thread i sums gate_up output i over the quarters
-    if (valid) {
-      const float* src = a.gu_part + (size_t)p * ncq * (2 * I);
-      for (int i = tid; i < 2 * I; i += 1024) {
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = j < ncq ? ld_fresh(src + (size_t)j * (2 * I) + i) : 0.f;
-        float s = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < ncq) s += v[j];
-        sh.gu[i] = s;
-      }
-    }
-    __syncthreads();
-    if ((wave & 3) == 0 && active) {  // one wave per 128-channel chunk
+    if (nq == 0 && active) {  // one wave per 128-channel chunk
       int skip = 1;
       if (valid) {
-        const float h0 = silu(sh.gu[128 * cl + lane]) * sh.gu[I + 128 * cl + lane];
-        const float h1 = silu(sh.gu[128 * cl + lane + 64]) * sh.gu[I + 128 * cl + lane + 64];
+        // gate and up sums of the chunk's channels over gate_up's quarters, in order
+        const float* src = a.gu_part + (size_t)p * ncq * (2 * I) + 128 * cl + lane;
+        float v[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float* sj = src + (size_t)j * (2 * I);
+          v[j][0] = j < ncq ? ld_fresh(sj) : 0.f;
+          v[j][1] = j < ncq ? ld_fresh(sj + 64) : 0.f;
+          v[j][2] = j < ncq ? ld_fresh(sj + I) : 0.f;
+          v[j][3] = j < ncq ? ld_fresh(sj + I + 64) : 0.f;
+        }
+        float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < ncq) {
+            g0 += v[j][0];
+            g1 += v[j][1];
+            u0 += v[j][2];
+            u1 += v[j][3];
+          }
+        const float h0 = silu(g0) * u0;
+        const float h1 = silu(g1) * u1;
         skip = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
         float v0 = h0 * rin0;
         float v1 = h1 * rin1;
         fwht128(v0, v1);
-        sh.xs[cl][lane] = v0 * kInvSqrt128;
-        sh.xs[cl][lane + 64] = v1 * kInvSqrt128;
+        const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cl], sh.xl[cl], lane);
+        if (lane == 0) sh.xe[cl] = xe;
       }
       // a chunk whose h is all zero contributes exactly zero: its MAC is skipped
       if (lane == 0) sh.skip[cl] = skip;
@@ -342,19 +402,15 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     __syncthreads();
     if (valid) {  // uniform over the group
       if (active && !sh.skip[cl]) {
-        float acc[16];
+        mfma_block(sh, A, cl, nq, lane);
+      } else if (active && (lane & 15) == 0) {
 #pragma unroll
-        for (int n = 0; n < 16; ++n) acc[n] = 0.f;
-        mac_decoded_row(wv[0], jr, q, sh.xs[cl], acc);
-        mac_decoded_row(wv[1], jr + 1, q, sh.xs[cl], acc);
-        sh.red[wave][lane] = quad_reduce_pick(acc, q);
-      } else {
-        sh.red[wave][lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<float4*>(&sh.red[cl][16 * (4 * nq + j) + 4 * (lane >> 4)]) =
+              make_float4(0.f, 0.f, 0.f, 0.f);
       }
       __syncthreads();
-      if (wave == 0) sum_waves(sh, lane);
-      __syncthreads();
-      transform_store_rv<true>(sh.zs, ro0, ro1, wt, out, wave, lane);
+      sum_transform_store<true>(sh, ncd, ro0, ro1, wt, out, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_agent(out + 4 * lane + i, 0.f);
