@@ -286,7 +286,7 @@ def main():
             x0=torch.from_numpy(x0.view(np.int16).copy()).cuda(),
             logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
             y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
-            ws=torch.empty(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
+            ws=torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
             probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
         ))
 

@@ -286,18 +286,18 @@ int check_layer_call(const escha_moe_layer_t* L, const uint16_t* x, int32_t T, c
 
 // ---------------------------------------------------------------- stack
 // Control block at the start of a stack workspace: a 512-int header (word 1:
-// status of the one-launch path; words 256 + 32x: XCD x's task ticket) and
-// that path's flag words (zeroed before
-// every launch): per (layer, pair) one word per gate_up task and one per
-// down task, per (layer, token, XCD) one word per combine task. Each group
-// of words that one XCD writes starts on a 128-byte line of its own.
-constexpr int64_t kCtlHeaderInts = 512;  // word 1: status; words 256 + 32x: XCD x's ticket
+// status of the one-launch path; word 2: its call number; words 256 + 32x:
+// XCD x's task ticket) and that path's flag words, one per (layer, pair,
+// down output group). The tickets and flags are zeroed before every launch;
+// each group of flag words that one XCD writes starts on a 128-byte line of
+// its own.
+constexpr int64_t kCtlHeaderInts = 512;
 
 int64_t round32(int64_t n) { return (n + 31) / 32 * 32; }
 
 struct FlowLayout {
-  int64_t p8, gf_pair, df_pair, cf_x;
-  int64_t gflag, dflag, cflag, ctl_ints;  // offsets / total, in ints
+  int64_t p8, df_pair;
+  int64_t dflag, ctl_ints;  // offset / total, in ints
   size_t gu_part, dn_part, dn_copy, xcb, data_bytes;  // offsets in bytes from the data start
 };
 
@@ -305,21 +305,17 @@ FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) 
   FlowLayout f{};
   const int64_t H = L->hidden, I = L->inter;
   f.p8 = (T * L->top_k + 7) / 8 * 8;
-  f.gf_pair = round32((H / 512) * (2 * I / 256));
   f.df_pair = round32(H / 256);
-  f.cf_x = 32;
-  f.gflag = kCtlHeaderInts;
-  f.dflag = f.gflag + n_layers * f.p8 * f.gf_pair;
-  f.cflag = f.dflag + n_layers * f.p8 * f.df_pair;
-  f.ctl_ints = f.cflag + n_layers * T * 8 * f.cf_x;
+  f.dflag = kCtlHeaderInts;
+  f.ctl_ints = f.dflag + n_layers * f.p8 * f.df_pair;
   f.dn_copy = (size_t)f.p8 * H;
   size_t off = 0;
   f.gu_part = off;
-  off += round_up((size_t)f.p8 * (H / 512) * (2 * I) * sizeof(float));
+  off += round_up((size_t)f.p8 * (H / 1024) * (2 * I) * sizeof(uint64_t));
   f.dn_part = off;
-  off += round_up(2 * f.dn_copy * sizeof(float));
+  off += round_up(2 * f.dn_copy * sizeof(uint64_t));
   f.xcb = off;
-  off += round_up((size_t)T * 8 * H * sizeof(float));
+  off += round_up((size_t)T * 8 * H * sizeof(uint64_t));
   f.data_bytes = off;
   return f;
 }
@@ -587,12 +583,12 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
                   "layer %d differs from layer 0 in n_experts or k_bits (one-launch path)", l);
   }
   const int64_t T = n_tokens, H = L0->hidden, I = L0->inter, k = L0->top_k;
-  // task shapes of the one-launch kernel: gate_up quarters of four 128-input
-  // chunks, one down task over all channels (at most four 128-blocks), one
-  // wave polling all the flags a task waits for
-  if (H % 512 != 0 || H > 4096 || I > 512 || k * (H / 256) > 64)
+  // task shapes of the one-launch kernel: gate_up tasks over 1024 inputs (two
+  // parts at most), one down task over all channels (at most four
+  // 128-blocks), one wave polling all the flags a task waits for
+  if (H % 1024 != 0 || H > 2048 || I > 512 || k * (H / 256) > 64)
     return fail(ESCHA_E_UNSUPPORTED,
-                "one-launch path needs hidden %% 512 == 0, hidden <= 4096, inter <= 512 and "
+                "one-launch path needs hidden 1024 or 2048, inter <= 512 and "
                 "top_k * hidden / 256 <= 64 (hidden=%lld inter=%lld top_k=%lld)",
                 (long long)H, (long long)I, (long long)k);
   if (n_tokens == 0) return ESCHA_OK;
@@ -628,21 +624,18 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   a.x0 = x0_bf16;
   a.y_last = y_last;
   a.x_chain = x_chain;
-  a.gu_part = (float*)(data + f.gu_part);
-  a.dn_part = (float*)(data + f.dn_part);
+  a.gu_part = (uint64_t*)(data + f.gu_part);
+  a.dn_part = (uint64_t*)(data + f.dn_part);
   a.dn_copy = (int64_t)f.dn_copy;
-  a.xcb = (float*)(data + f.xcb);
-  a.gflag = ctl + f.gflag;
-  a.gf_pair = (int32_t)f.gf_pair;
+  a.xcb = (uint64_t*)(data + f.xcb);
   a.dflag = ctl + f.dflag;
   a.df_pair = (int32_t)f.df_pair;
-  a.cflag = ctl + f.cflag;
-  a.cf_x = (int32_t)f.cf_x;
-  a.cf_tok = (int32_t)(8 * f.cf_x);
+  a.epoch = ctl + 2;
   a.ticket = ctl + 256;
   a.error = ctl + 1;
 
-  hipError_t e = escha::launch_fill_zero(ctl, (size_t)f.ctl_ints, s);
+  // status, tickets and flags to zero, the call number one further
+  hipError_t e = escha::launch_flow_prepare(ctl, (size_t)f.ctl_ints, s);
   if (e != hipSuccess) return hip_fail(e, "flag clear launch");
   if (x_chain) {  // layer 0's input; the kernel writes the others
     e = hipMemcpyAsync(x_chain, x0_bf16, (size_t)T * H * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);

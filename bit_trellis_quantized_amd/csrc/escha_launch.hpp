@@ -116,8 +116,9 @@ struct StackLayer {
   const uint16_t* dn_rout;
 };
 
-// Flag words are zero at launch and set to 1 once; every region written by
-// one XCD starts on a 128-byte line of its own.
+// Words handed between tasks are tagged 64-bit words {value, tag}; the tag
+// of layer l's words is (epoch << 8) + l + 1, epoch being the call number
+// that launch_flow_prepare advances before each launch.
 struct FlowArgs {
   StackLayer layer[kMaxStackLayers];
   int32_t n_layers, n_tokens, top_k, hidden, inter, n_experts;
@@ -128,23 +129,22 @@ struct FlowArgs {
   const uint16_t* x0;  // bf16 [n_tokens][hidden]
   float* y_last;       // fp32 [n_tokens][hidden]
   uint16_t* x_chain;   // nullable: bf16 [n_layers][n_tokens][hidden]
-  float* gu_part;      // [p8][hidden/512][2*inter], written and read on the pair's XCD
-  float* dn_part;      // 2 copies of [p8][hidden]: each pair's weighted output, read on every XCD
-  int64_t dn_copy;     // floats per copy
-  float* xcb;          // [n_tokens][8][hidden]: each XCD's copy of the next layer's input
-  int32_t* gflag;      // [n_layers][p8][gf_pair]: gate_up task (quarter cq, group g) at cq * ngg + g
-  int32_t gf_pair;
-  int32_t* dflag;      // [n_layers][p8][df_pair]: down task of output group g at g
+  uint64_t* gu_part;   // tagged [p8][hidden/1024][2*inter], written and read on the pair's XCD
+  uint64_t* dn_part;   // tagged, 2 copies of [p8][hidden]: each pair's weighted output
+  int64_t dn_copy;     // words per copy
+  uint64_t* xcb;       // tagged [n_tokens][8][hidden]: each XCD's copy of the next layer's input
+  int32_t* dflag;      // [n_layers][p8][df_pair]: down task of output group g at g (its tag)
   int32_t df_pair;
-  int32_t* cflag;      // [n_layers][n_tokens][8][cf_x]: combine task of (token, XCD) at word 0
-  int32_t cf_tok, cf_x;
+  const int32_t* epoch;  // the call number
   int32_t* ticket;     // [8][32]: next task of each XCD (word 32x)
   int32_t* error;      // 1: a wait gave up
 };
 constexpr int kFlowSpare = 64;  // work-groups launched beyond the task count (8 per XCD)
 
 int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens);
-hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s);
+// Zero the n words of a control block except word 2, the call number, which
+// it advances (modulo 2^24).
+hipError_t launch_flow_prepare(int32_t* ctl, size_t n, hipStream_t s);
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s);
 
 hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,

@@ -139,7 +139,7 @@ __device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
   }
 }
 
-static __device__ __noinline__ void scale_block(float m, float& scale, float& unscale);
+static __device__ __noinline__ float2 scale_block(float m);
 
 // Split a wave's 128 rotated activations (v0 at position lane, v1 at
 // lane + 64) into fp16 high and low parts for B, scaled by a power of two
@@ -149,7 +149,11 @@ __device__ __forceinline__ float split_hilo(float v0, float v1, _Float16* xh, _F
                                             int lane) {
   float m = fmaxf(fabsf(v0), fabsf(v1));
   float scale = 1.0f, unscale = 1.0f;
-  if (__ballot(!(m <= 16384.0f)) != 0) scale_block(m, scale, unscale);  // rare: large values
+  if (__ballot(!(m <= 16384.0f)) != 0) {  // rare: large values
+    const float2 su = scale_block(m);
+    scale = su.x;
+    unscale = su.y;
+  }
   const float a0 = v0 * scale, a1 = v1 * scale;
   const _Float16 h0 = (_Float16)a0, h1 = (_Float16)a1;
   xh[lane] = h0;
@@ -161,8 +165,8 @@ __device__ __forceinline__ float split_hilo(float v0, float v1, _Float16* xh, _F
 
 // The power-of-two scale of split_hilo for a block whose largest magnitude
 // exceeds 2^14 (m: this lane's largest magnitude; NaN and infinity leave the
-// scale at 1).
-static __device__ __noinline__ void scale_block(float m, float& scale, float& unscale) {
+// scale at 1): {scale, its inverse}.
+static __device__ __noinline__ float2 scale_block(float m) {
   m = fmaxf(m, xor_lane<1>(m));
   m = fmaxf(m, xor_lane<2>(m));
   m = fmaxf(m, xor_lane<4>(m));
@@ -177,12 +181,14 @@ static __device__ __noinline__ void scale_block(float m, float& scale, float& un
     const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
+  float scale = 1.0f, unscale = 1.0f;
   if (m > 16384.0f && m <= 3.0e38f) {
     int ex;
     frexpf(m * (1.0f / 16384.0f), &ex);
     scale = ldexpf(1.0f, -ex);
     unscale = ldexpf(1.0f, ex);
   }
+  return make_float2(scale, unscale);
 }
 
 // B operand for the tile-row pair pp of a 128-input block: column 0 the

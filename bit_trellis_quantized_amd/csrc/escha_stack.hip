@@ -77,57 +77,102 @@ __device__ __forceinline__ int xcc_id() {
 __device__ __forceinline__ int ld_fresh(const int32_t* p) {
   return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float ld_fresh(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 // sc1 store: written through to memory, for readers on other XCDs.
 __device__ __forceinline__ void st_remote(int32_t* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until this wave's stores have completed; also a compiler barrier.
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Tagged words: data that work-groups hand to each other is stored as a
+// 64-bit word {value bits, tag} with one store, so a reader sees a value
+// together with the tag written with it; the tag names the call and the
+// layer, so a reader recognises the word the current layer's producer
+// stored without any flag or store completion in between.
+__device__ __forceinline__ uint64_t tag_word(float v, uint32_t tag) {
+  return (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32);
+}
+__device__ __forceinline__ uint64_t ld_fresh64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_remote64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Wave-level wait: lane i (with a non-null `mine`) polls one flag word until
-// every polled word is non-zero. False when the error word is set or the
-// bound passes (then this wave sets it). Must be reached by a whole wave.
-__device__ bool wave_wait(const int32_t* mine, int32_t* err) {
+// Bound of every wait: true while the wait may go on; false once the error
+// word is set or the bound has passed (then this wave sets the error word).
+__device__ __forceinline__ bool keep_waiting(int it, long long t0, int32_t* err) {
+  if ((it & 15) == 15) {
+    if (ld_fresh(err)) return false;
+    if (wall_clock64() - t0 > kWaitTicks) {
+      st_remote(err, 1);
+      return false;
+    }
+  }
+  __builtin_amdgcn_s_sleep(2);
+  return true;
+}
+
+// Wave-level fetch of N tagged words per lane (word i at p(i); words i >=
+// n are not read) until every word the wave reads carries `tag`; out[i]
+// receives the values. False when a wait gives up. Whole wave.
+template <int N, class F>
+__device__ bool wave_fetch(F p, int n, uint32_t tag, float (&out)[N], int32_t* err) {
   const long long t0 = wall_clock64();
   for (int it = 0;; ++it) {
-    const int v = mine ? ld_fresh(mine) : 1;
-    if (__ballot(v == 0) == 0) return true;
-    if ((it & 15) == 15) {
-      if (ld_fresh(err)) return false;
-      if (wall_clock64() - t0 > kWaitTicks) {
-        st_remote(err, 1);
-        return false;
+    uint64_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = i < n ? ld_fresh64(p(i)) : tag_word(0.f, tag);
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ok = ok && (uint32_t)(v[i] >> 32) == tag;
+    if (__ballot(!ok) == 0) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) out[i] = __uint_as_float((uint32_t)v[i]);
+      return true;
+    }
+    if (!keep_waiting(it, t0, err)) return false;
+  }
+}
+
+// Wave-level fetch of up to two groups of four tagged words per lane (word
+// 4j + c at p(4j + c), groups j < n), added in group order to `start` once
+// every word the wave reads carries `tag`: sum.c = start.c + w(0, c) + ... +
+// w(n - 1, c). False when a wait gives up. Whole wave.
+template <class F>
+__device__ bool wave_fetch_sum4(F p, int n, uint32_t tag, float4 start, float4& sum, int32_t* err) {
+  constexpr int kGroups = 2;  // n <= kGroups
+  const long long t0 = wall_clock64();
+  for (int it = 0;; ++it) {
+    uint64_t v[4 * kGroups];
+#pragma unroll
+    for (int i = 0; i < 4 * kGroups; ++i) v[i] = (i >> 2) < n ? ld_fresh64(p(i)) : tag_word(0.f, tag);
+    bool ok = true;
+    float4 s = start;
+#pragma unroll
+    for (int j = 0; j < kGroups; ++j) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ok = ok && (uint32_t)(v[4 * j + c] >> 32) == tag;
+      if (j < n) {
+        s.x += __uint_as_float((uint32_t)v[4 * j + 0]);
+        s.y += __uint_as_float((uint32_t)v[4 * j + 1]);
+        s.z += __uint_as_float((uint32_t)v[4 * j + 2]);
+        s.w += __uint_as_float((uint32_t)v[4 * j + 3]);
       }
     }
-    __builtin_amdgcn_s_sleep(2);
+    if (__ballot(!ok) == 0) {
+      sum = s;
+      return true;
+    }
+    if (!keep_waiting(it, t0, err)) return false;
   }
 }
 
-// Work-group wait: wave 0 polls, everyone learns the outcome after the
-// barrier. Must be reached by all threads of the group.
-__device__ __forceinline__ bool group_wait(const int32_t* mine, int32_t* err, int* sh_ok) {
-  if ((threadIdx.x >> 6) == 0) {
-    const bool ok = wave_wait(mine, err);
-    if (threadIdx.x == 0) *sh_ok = ok ? 1 : 0;
-  }
-  __syncthreads();
-  return *sh_ok != 0;
-}
-
-// Every wave waits for its stores to complete, then thread 0 sets the flag
-// (a plain store for readers on this XCD, an sc1 store for all XCDs).
-template <bool REMOTE>
-__device__ __forceinline__ void group_signal(int32_t* flag) {
-  stores_done();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    if constexpr (REMOTE)
-      st_remote(flag, 1);
-    else
-      __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+// Wave-level wait: lane i (with a non-null `mine`) polls one flag word until
+// every polled word equals `want`. False when the wait gives up.
+__device__ bool wave_wait(const int32_t* mine, int want, int32_t* err) {
+  const long long t0 = wall_clock64();
+  for (int it = 0;; ++it) {
+    const int v = mine ? ld_fresh(mine) : want;
+    if (__ballot(v != want) == 0) return true;
+    if (!keep_waiting(it, t0, err)) return false;
   }
 }
 
@@ -166,20 +211,30 @@ __device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
 
 struct Lds {
   uint32_t code[kWaves * Stage<3>::kDw];            // each wave's staged codes
-  _Float16 xh[4][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
-  _Float16 xl[4][128] __attribute__((aligned(16)));  // and their low parts
-  float xe[4];                                       // undo factor of each block's scale
-  float red[4][256] __attribute__((aligned(16)));    // per-block sums of a 256-output group
+  _Float16 xh[8][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
+  _Float16 xl[8][128] __attribute__((aligned(16)));  // and their low parts
+  float xe[8];                                       // undo factor of each block's scale
+  float red[1024] __attribute__((aligned(16)));      // per-input-block sums of the task's outputs
   float ssb[32];
   int skip[4];
-  int task, ok;
+  int ok[kWaves];
+  int task;
 };
+
+// True when no wave of the group recorded a failed wait; after a barrier.
+__device__ __forceinline__ bool all_ok(const Lds& sh) {
+  int ok = 1;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ok &= sh.ok[w];
+  return ok != 0;
+}
 
 // Contract a wave's decoded tiles (8 tile-rows of 128-block cl x 4 output
 // tiles 4nq..4nq+3) with the block's activations on the matrix cores and
-// leave the 64 sums in sh.red[cl] (outputs 16 (4nq + j) + n of the group).
+// leave the 64 sums in sh.red[stride * cl + 16 (4nq + j) + n] (output
+// 16 (4nq + j) + n of the task).
 __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq,
-                                           int lane) {
+                                           int stride, int lane) {
   f32x4 D[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -194,34 +249,34 @@ __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int 
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(&sh.red[cl][16 * (4 * nq + j) + 4 * (lane >> 4)]) = zr[j];
+      *reinterpret_cast<float4*>(&sh.red[stride * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) = zr[j];
   }
 }
 
-// Output transform of the group's 256 outputs: waves 0 and 1 sum their
-// 128-block over the first nb input blocks (in block order), apply H_n,
-// multiply by rout (ro0, ro1 at this lane's two outputs) and the weight, and
-// store (REMOTE: sc1 stores).
+// Output transform of the task's outputs (stride of them, 128 per wave of
+// the first stride / 128): the sum over the first nb input blocks (in block
+// order), H_n, rout (ro0, ro1 at this lane's two outputs) and the weight,
+// stored as tagged words (REMOTE: sc1 stores).
 template <bool REMOTE>
-__device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, float ro0, float ro1,
-                                                    float wt, float* __restrict__ out, int wave,
-                                                    int lane) {
-  if (wave < 2) {
+__device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, int stride, float ro0,
+                                                    float ro1, float wt, uint64_t* __restrict__ out,
+                                                    uint32_t tag, int wave, int lane) {
+  if (wave < stride / 128) {
     const int o = 128 * wave + lane;
-    float z0 = sh.red[0][o], z1 = sh.red[0][o + 64];
+    float z0 = sh.red[o], z1 = sh.red[o + 64];
     for (int b = 1; b < nb; ++b) {
-      z0 += sh.red[b][o];
-      z1 += sh.red[b][o + 64];
+      z0 += sh.red[stride * b + o];
+      z1 += sh.red[stride * b + o + 64];
     }
     fwht128(z0, z1);
     const float o0 = z0 * kInvSqrt128 * ro0 * wt;
     const float o1 = z1 * kInvSqrt128 * ro1 * wt;
     if constexpr (REMOTE) {
-      st_agent(out + o, o0);
-      st_agent(out + o + 64, o1);
+      st_remote64(out + o, tag_word(o0, tag));
+      st_remote64(out + o + 64, tag_word(o1, tag));
     } else {
-      out[o] = o0;
-      out[o + 64] = o1;
+      out[o] = tag_word(o0, tag);
+      out[o + 64] = tag_word(o1, tag);
     }
   }
 }
@@ -236,10 +291,10 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   const int lane = tid & 63;
   const int H = a.hidden, I = a.inter, k = a.top_k, T = a.n_tokens;
   const int P = T * k, P8 = a.p8;
-  const int ncg = H / 128, ngg = (2 * I) / 256;  // gate_up chunks / groups
-  const int ncq = ncg / 4;                       // gate_up quarters (four chunks each)
-  const int ncd = I / 128, ngd = H / 256;        // down chunks (<= 4) / groups
-  const int nb_gu = ncq * ngg * P8, nb_dn = ngd * P8;
+  const int ncg = H / 128, ngb = (2 * I) / 128;  // gate_up input chunks / output blocks
+  const int nh = ncg / 8;                        // gate_up input eighths-of-1024 (8 chunks each)
+  const int ncd = I / 128, ngd = H / 256;        // down chunks (<= 4) / output groups
+  const int nb_gu = nh * ngb * P8, nb_dn = ngd * P8;
   const int per_layer = nb_gu + nb_dn + T * 8;
 
   // claim this XCD's next task: the j-th work-group to start on XCD x runs
@@ -257,37 +312,44 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   if (bid >= a.n_layers * per_layer) return;
   const int l = bid / per_layer;
   int r = bid - l * per_layer;
+  // tag of the words this layer's tasks write (the call's number, written
+  // by the kernel that precedes this launch, and the layer)
+  const uint32_t epoch = (uint32_t)a.epoch[0];
+  const uint32_t tag = (epoch << 8) + (uint32_t)l + 1u;
+  if (tid < kWaves) sh.ok[tid] = 1;
   const StackLayer& Ly = a.layer[l];
-  // wave w works on 128-block cl = w / 4 of its task's inputs (its 8
-  // tile-rows) and output tiles 4 nq .. 4 nq + 3 (nq = w % 4) of the group
-  const int cl = wave >> 2;
-  const int nq = wave & 3;
+
 
   if (r < nb_gu) {
     // ------------------------------------------------------------ gate_up
+    // task (pair p, inputs 1024 hh .. 1024 hh + 1023, outputs 128 g .. 128 g +
+    // 127); wave w: input chunk cl = w / 2 of the eight (its 8 tile-rows),
+    // output tiles 4 nq .. 4 nq + 3 (nq = w % 2) of the block
+    const int cl = wave >> 1;
+    const int nq = wave & 1;
     const int p = r % P8;
     if (p >= P) return;
     r /= P8;
-    const int g = r % ngg;
-    const int cq = r / ngg;
-    const int c = 4 * cq + cl;  // this wave's input chunk
+    const int g = r % ngb;
+    const int hh = r / ngb;
+    const int c = 8 * hh + cl;  // this wave's input chunk
     const int t = p / k;
     const int x = p & 7;
     const int e = a.ids[(size_t)l * P + p];
     const bool valid = e >= 0 && e < a.n_experts;
     const int n_nt = (2 * I) / 16;
-    float* out = a.gu_part + ((size_t)p * ncq + cq) * (2 * I) + g * 256;
+    uint64_t* out = a.gu_part + ((size_t)p * nh + hh) * (2 * I) + g * 128;
 
     // an out-of-range id is decoded as expert 0 and its result discarded,
     // which keeps the register state the same on every path
     const int es = valid ? e : 0;
     const uint16_t* code_e = Ly.gu_code + (size_t)es * (size_t)ncg * 8 * n_nt * (16 * KG);
     u32x4 cv[Stage<KG>::kPerLane];
-    stage_issue<KG>(code_e, n_nt, 8 * c, 16 * g + 4 * nq, lane, cv);
+    stage_issue<KG>(code_e, n_nt, 8 * c, 8 * g + 4 * nq, lane, cv);
     const uint16_t* rr = Ly.gu_rin + (size_t)es * H + c * 128;
     const float rin0 = f16_to_f32(rr[lane]);
     const float rin1 = f16_to_f32(rr[lane + 64]);
-    const uint16_t* ro = Ly.gu_rout + (size_t)es * (2 * I) + g * 256 + 128 * (wave & 1);
+    const uint16_t* ro = Ly.gu_rout + (size_t)es * (2 * I) + g * 128;
     const float ro0 = f16_to_f32(ro[lane]);
     const float ro1 = f16_to_f32(ro[lane + 64]);
     uint32_t* stage = sh.code + wave * Stage<KG>::kDw;
@@ -295,24 +357,22 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     h16x8 A[4][4];
     decode_stage_mfma<KG>(stage, lane, A);
     pin_operands(A);
-    if (l > 0) {
-      // the previous layer's combine task of this token on this XCD
-      const int32_t* cf = a.cflag + ((size_t)(l - 1) * T + t) * a.cf_tok + x * a.cf_x;
-      if (!group_wait(lane == 0 ? cf : nullptr, a.error, &sh.ok)) return;
-    }
-    __builtin_amdgcn_s_setprio(3);
-
+    __syncthreads();  // sh.ok initialised
     if (nq == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
-      float x0, x1;
+      float xv[2];
       if (l == 0) {
         const uint16_t* xr = a.x0 + (size_t)t * H + c * 128;
-        x0 = bf16_to_f32(xr[lane]);
-        x1 = bf16_to_f32(xr[lane + 64]);
+        xv[0] = bf16_to_f32(xr[lane]);
+        xv[1] = bf16_to_f32(xr[lane + 64]);
       } else {
-        const float* xr = a.xcb + ((size_t)t * 8 + x) * H + c * 128;
-        x0 = ld_fresh(xr + lane);
-        x1 = ld_fresh(xr + lane + 64);
+        // the previous layer's combine task of this token on this XCD wrote
+        // the chunk's inputs
+        const uint64_t* xr = a.xcb + ((size_t)t * 8 + x) * H + c * 128 + lane;
+        const bool ok = wave_fetch<2>([&](int i) { return xr + 64 * i; }, 2, tag - 1u, xv, a.error);
+        if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
+        __builtin_amdgcn_s_setprio(3);
       }
+      const float x0 = xv[0], x1 = xv[1];
       float v0 = x0 * rin0;
       float v1 = x1 * rin1;
       fwht128(v0, v1);
@@ -320,16 +380,22 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
       if (lane == 0) sh.xe[cl] = xe;
     }
     __syncthreads();
+    if (!all_ok(sh)) return;
+    __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
-      mfma_block(sh, A, cl, nq, lane);
+      mfma_block(sh, A, cl, nq, 128, lane);
       __syncthreads();
-      sum_transform_store<false>(sh, 4, ro0, ro1, 1.0f, out, wave, lane);
+      sum_transform_store<false>(sh, 8, 128, ro0, ro1, 1.0f, out, tag, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
-      reinterpret_cast<float4*>(out)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+      out[lane] = tag_word(0.f, tag);
+      out[lane + 64] = tag_word(0.f, tag);
     }
-    group_signal<false>(a.gflag + ((size_t)l * P8 + p) * a.gf_pair + cq * ngg + g);
   } else if ((r -= nb_gu) < nb_dn) {
     // --------------------------------------------------------------- down
+    // task (pair p, outputs 256 g .. 256 g + 255); wave w: channel chunk
+    // cl = w / 4 (its 8 tile-rows), output tiles 4 nq .. 4 nq + 3 (nq = w % 4)
+    const int cl = wave >> 2;
+    const int nq = wave & 3;
     const int p = r % P8;
     if (p >= P) return;
     const int g = r / P8;
@@ -337,7 +403,7 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const bool valid = e >= 0 && e < a.n_experts;
     const bool active = cl < ncd;  // this wave has tile-rows
     const int n_nt = H / 16;
-    float* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 256;
+    uint64_t* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 256;
 
     const int es = valid ? e : 0;
     const uint16_t* code_e = Ly.dn_code + (size_t)es * (size_t)ncd * 8 * n_nt * (16 * KD);
@@ -357,36 +423,30 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
       decode_stage_mfma<KD>(stage, lane, A);
     }
     pin_operands(A);
-    {
-      // every gate_up task of this pair (all quarters, all groups)
-      const int32_t* gf = a.gflag + ((size_t)l * P8 + p) * a.gf_pair;
-      if (!group_wait(lane < ncq * ngg ? gf + lane : nullptr, a.error, &sh.ok)) return;
-    }
-    __builtin_amdgcn_s_setprio(3);
-
+    __syncthreads();  // sh.ok initialised
     if (nq == 0 && active) {  // one wave per 128-channel chunk
       int skip = 1;
       if (valid) {
-        // gate and up sums of the chunk's channels over gate_up's quarters, in order
-        const float* src = a.gu_part + (size_t)p * ncq * (2 * I) + 128 * cl + lane;
-        float v[8][4];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float* sj = src + (size_t)j * (2 * I);
-          v[j][0] = j < ncq ? ld_fresh(sj) : 0.f;
-          v[j][1] = j < ncq ? ld_fresh(sj + 64) : 0.f;
-          v[j][2] = j < ncq ? ld_fresh(sj + I) : 0.f;
-          v[j][3] = j < ncq ? ld_fresh(sj + I + 64) : 0.f;
-        }
+        // gate and up sums of the chunk's channels over gate_up's input
+        // parts, in order, once every gate_up task of this pair has written them
+        const uint64_t* src = a.gu_part + (size_t)p * nh * (2 * I) + 128 * cl + lane;
+        auto word = [&](int i) {  // part i / 4; gate, gate + 64, up, up + 64
+          return src + (size_t)(i >> 2) * (2 * I) + ((i & 1) ? 64 : 0) + ((i & 2) ? I : 0);
+        };
         float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (j < ncq) {
-            g0 += v[j][0];
-            g1 += v[j][1];
-            u0 += v[j][2];
-            u1 += v[j][3];
-          }
+        bool ok = true;
+        for (int j0 = 0; j0 < nh && ok; j0 += 2) {  // two parts per fetch
+          float4 sum;
+          ok = wave_fetch_sum4([&](int i) { return word(4 * j0 + i); },
+                               nh - j0 < 2 ? nh - j0 : 2, tag, make_float4(g0, g1, u0, u1), sum,
+                               a.error);
+          g0 = sum.x;
+          g1 = sum.y;
+          u0 = sum.z;
+          u1 = sum.w;
+        }
+        if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
+        __builtin_amdgcn_s_setprio(3);
         const float h0 = silu(g0) * u0;
         const float h1 = silu(g1) * u1;
         skip = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
@@ -400,22 +460,26 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
       if (lane == 0) sh.skip[cl] = skip;
     }
     __syncthreads();
+    if (!all_ok(sh)) return;
+    __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
       if (active && !sh.skip[cl]) {
-        mfma_block(sh, A, cl, nq, lane);
+        mfma_block(sh, A, cl, nq, 256, lane);
       } else if (active && (lane & 15) == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(&sh.red[cl][16 * (4 * nq + j) + 4 * (lane >> 4)]) =
+          *reinterpret_cast<float4*>(&sh.red[256 * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
               make_float4(0.f, 0.f, 0.f, 0.f);
       }
       __syncthreads();
-      sum_transform_store<true>(sh, ncd, ro0, ro1, wt, out, wave, lane);
-    } else if (wave == 0) {  // an out-of-range expert id contributes nothing
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st_agent(out + 4 * lane + i, 0.f);
+      sum_transform_store<true>(sh, ncd, 256, ro0, ro1, wt, out, tag, wave, lane);
+    } else if (wave < 2) {  // an out-of-range expert id contributes nothing
+      st_remote64(out + 128 * wave + lane, tag_word(0.f, tag));
+      st_remote64(out + 128 * wave + lane + 64, tag_word(0.f, tag));
     }
-    group_signal<true>(a.dflag + ((size_t)l * P8 + p) * a.df_pair + g);
+    // flag for the combine tasks (a hint: the tags decide)
+    __syncthreads();
+    if (tid == 0) st_remote(a.dflag + ((size_t)l * P8 + p) * a.df_pair + g, (int)tag);
   } else {
     // ------------------------------------------------------------ combine
     r -= nb_dn;
@@ -427,36 +491,40 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const int x_first = (t * k) & 7;
     const bool last = l == a.n_layers - 1;
     if (last ? x != x_first : (k < 8 && ((x - x_first) & 7) >= k)) return;
-    {
-      // every down task of the token's pairs
+    if (wave == 0) {
+      // every down task of the token's pairs has flagged its output
       const int32_t* df = a.dflag + ((size_t)l * P8 + (size_t)t * k) * a.df_pair;
       const int32_t* mine =
           lane < k * ngd ? df + (size_t)(lane / ngd) * a.df_pair + (lane % ngd) : nullptr;
-      if (!group_wait(mine, a.error, &sh.ok)) return;
+      const bool ok = wave_wait(mine, (int)tag, a.error);
+      if (lane == 0) sh.ok[0] = ok ? 1 : 0;
     }
+    __syncthreads();
+    if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
     // wave w: 128-blocks w, w + 16, ..; lanes hold outputs lane and lane + 64
     // of a block; the pair outputs are summed in slot order from 0
     const int nb = H / 128;
-    const float* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)t * k * H;
+    const uint64_t* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)t * k * H;
     float yv[2][2];
+    bool ok = true;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int b = wave + kWaves * s;
       yv[s][0] = yv[s][1] = 0.f;
       if (b < nb) {
-        float v[16][2];
+        const uint64_t* pb = pp + 128 * b + lane;
+        for (int j0 = 0; j0 < k && ok; j0 += 8) {  // eight slots per fetch
+          float v[16];
+          ok = wave_fetch<16>([&](int i) { return pb + (size_t)(j0 + (i >> 1)) * H + ((i & 1) ? 64 : 0); },
+                              k - j0 < 8 ? 2 * (k - j0) : 16, tag, v, a.error);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          v[j][0] = j < k ? ld_fresh(pp + (size_t)j * H + 128 * b + lane) : 0.f;
-          v[j][1] = j < k ? ld_fresh(pp + (size_t)j * H + 128 * b + lane + 64) : 0.f;
+          for (int j = 0; j < 8; ++j)
+            if (j0 + j < k) {
+              yv[s][0] += v[2 * j];
+              yv[s][1] += v[2 * j + 1];
+            }
         }
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          if (j < k) {
-            yv[s][0] += v[j][0];
-            yv[s][1] += v[j][1];
-          }
         if (last) {
           a.y_last[(size_t)t * H + 128 * b + lane] = yv[s][0];
           a.y_last[(size_t)t * H + 128 * b + lane + 64] = yv[s][1];
@@ -466,13 +534,15 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
         }
       }
     }
+    if (lane == 0 && !ok) sh.ok[wave] = 0;
     if (last) return;
     __syncthreads();
+    if (!all_ok(sh)) return;
     // RMSNorm: the blocks' sums of squares in block order, then bf16
     float tot = 0.f;
     for (int b = 0; b < nb; ++b) tot += sh.ssb[b];
     const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
-    float* xo = a.xcb + ((size_t)t * 8 + x) * H;
+    uint64_t* xo = a.xcb + ((size_t)t * 8 + x) * H;
     uint16_t* xc = (a.x_chain && x == x_first) ? a.x_chain + ((size_t)(l + 1) * T + t) * H : nullptr;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -480,35 +550,37 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
       if (b < nb) {
         const uint16_t b0 = f32_to_bf16_rne(yv[s][0] * inv);
         const uint16_t b1 = f32_to_bf16_rne(yv[s][1] * inv);
-        xo[128 * b + lane] = bf16_to_f32(b0);
-        xo[128 * b + lane + 64] = bf16_to_f32(b1);
+        xo[128 * b + lane] = tag_word(bf16_to_f32(b0), tag);
+        xo[128 * b + lane + 64] = tag_word(bf16_to_f32(b1), tag);
         if (xc) {
           xc[128 * b + lane] = b0;
           xc[128 * b + lane + 64] = b1;
         }
       }
     }
-    group_signal<false>(a.cflag + ((size_t)l * T + t) * a.cf_tok + x * a.cf_x);
   }
 }
 
-__global__ __launch_bounds__(256) void k_fill_zero(int32_t* __restrict__ p, size_t n) {
+// Before a launch: zero the control block's n words except word 2, the call
+// number, which advances.
+__global__ __launch_bounds__(256) void k_flow_prepare(int32_t* __restrict__ ctl, size_t n) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0;
+    if (i != 2) ctl[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) ctl[2] = (int32_t)(((uint32_t)ctl[2] + 1u) & 0xFFFFFFu);
 }
 
-hipError_t launch_fill_zero(int32_t* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
+hipError_t launch_flow_prepare(int32_t* ctl, size_t n, hipStream_t s) {
   size_t blocks = (n + 255) / 256;
+  if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  hipLaunchKernelGGL(k_flow_prepare, dim3((unsigned)blocks), dim3(256), 0, s, ctl, n);
   return hipGetLastError();
 }
 
 int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens) {
   const int64_t P8 = ((int64_t)n_tokens * top_k + 7) / 8 * 8;
-  return (int64_t)(hidden / 512) * (2 * inter / 256) * P8 + (int64_t)(hidden / 256) * P8 +
+  return (int64_t)(hidden / 1024) * (2 * inter / 128) * P8 + (int64_t)(hidden / 256) * P8 +
          (int64_t)n_tokens * 8;
 }
 

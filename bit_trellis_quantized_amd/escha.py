@@ -194,7 +194,8 @@ class MoeLayer:
 
 
 def _ws(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    # zero-filled: the one-launch stack path requires it on first use
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ entry points

@@ -214,7 +214,10 @@ ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_
  * the device and exchange data through that XCD's L2.
  * Additional requirements: n_layers <= 64; every layer has the same
  * n_experts and the same gate_up and down k_bits; n_tokens <= 64;
- * hidden <= 4096; top_k * inter / 128 <= 64.
+ * hidden 1024 or 2048; inter <= 512; top_k * hidden / 256 <= 64.
+ * The workspace must be zero-filled before its first use by this call (the
+ * data handed between tasks carries a per-call tag kept in the workspace);
+ * afterwards the library keeps it consistent from call to call.
  * probe_events (nullable): a HOST array of 2 hipEvent_t handles, recorded
  * right before and right after the kernel.
  * A dependency wait that exceeds its bound (half a second; it cannot happen

@@ -159,7 +159,7 @@ def test_flow_every_layer_vs_oracle_batch1(escha, stack):
     announce("one-launch stack, every layer vs oracle, T=1")
     x0, logits = synth.stack_token_inputs(SEED, NL, 1, 3)
     ids, w = _route(escha, logits)
-    ws = torch.empty(stack.workspace_bytes(1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(stack.workspace_bytes(1), dtype=torch.uint8, device="cuda")
     y, chain = _flow(escha, stack, to_dev(x0), ids, w, ws)
     assert escha.escha_moe_stack_status(ws) == 0
     assert np.array_equal(u16(chain[0]), x0)
@@ -174,7 +174,7 @@ def test_flow_sampled_vs_oracle(escha, stack, T):
     announce(f"one-launch stack vs oracle, T={T}, sampled tokens and layers")
     x0, logits = synth.stack_token_inputs(SEED, NL, T, 4)
     ids, w = _route(escha, logits)
-    ws = torch.empty(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda")
     y, chain = _flow(escha, stack, to_dev(x0), ids, w, ws)
     assert escha.escha_moe_stack_status(ws) == 0
     assert torch.isfinite(y).all()
@@ -189,7 +189,7 @@ def test_flow_deterministic_and_graph_replay(escha, stack):
     x0, logits = synth.stack_token_inputs(SEED, NL, 1, 6)
     ids, w = _route(escha, logits)
     x0d = to_dev(x0)
-    ws = torch.empty(stack.workspace_bytes(1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(stack.workspace_bytes(1), dtype=torch.uint8, device="cuda")
     y1, c1 = _flow(escha, stack, x0d, ids, w, ws)
     y2, c2 = _flow(escha, stack, x0d, ids, w, ws)
     assert escha.escha_moe_stack_status(ws) == 0
@@ -234,7 +234,7 @@ def test_flow_small_stack_edge_cases(escha):
     w = rs.random((NLs, T, 8)).astype(np.float32)
     x0 = synth.activations(11, T, synth.HIDDEN, layer=7)
     idd, wd, x0d = to_dev(ids), to_dev(w), to_dev(x0)
-    ws = torch.empty(st.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(st.workspace_bytes(T), dtype=torch.uint8, device="cuda")
     chain = torch.empty(NLs, T, synth.HIDDEN, dtype=torch.int16, device="cuda")
     y = escha.escha_moe_stack_decode_persistent(st, x0d, idd, wd, x_chain=chain, workspace=ws)
     assert escha.escha_moe_stack_status(ws) == 0
