@@ -36,6 +36,33 @@ DN_BYTES_PER_PAIR = 512 // 16 * 2048 // 16 * 48 * 2    # 393,216
 HBM_PEAK_GBS = 8000.0
 
 
+# The one-launch kernel's measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# scaled by a plain copy's readings) and the hash of the sources it was taken
+# with; reported only while the sources still hash to that value.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "stack_decode_b1_flow_traffic.md")
+KERNEL_SOURCES = ["escha_stack.hip", "escha_mfma.hpp", "escha_device.hpp", "escha_stream.hpp",
+                  "escha_launch.hpp"]
+
+
+def measured_traffic():
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_trellis_quantized_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    try:
+        with open(TRAFFIC_PROFILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    want = re.search(r"kernel_sources_sha256_16: ([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch: ([0-9]+)", text)
+    if not want or not val or want.group(1) != h.hexdigest()[:16]:
+        return None
+    return int(val.group(1))
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -366,7 +393,8 @@ def main():
                   "one layer's decode launches (k_in_partial + k_down_partial + k_combine)")
         roofline = {"kernel": kernel, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic() if (one_launch and T == 1) else None,
                     "bytes_per_launch": int(launch_bytes),
                     "avg_launch_us": round(probe_avg_ms * 1e3, 3),
                     "samples": len(probe_ms)}
