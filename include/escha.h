@@ -158,9 +158,12 @@ ESCHA_API int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uin
  * x bf16 [n_tokens][hidden]; topk_ids int32 / topk_w fp32 [n_tokens][top_k];
  * y fp32 [n_tokens][hidden]; inter_out (nullable) fp32
  * [n_tokens*top_k][inter] receives h per pair, in pair order t*top_k+j.
- * _decode streams every pair's expert weights (small batches);
+ * _decode streams every pair's expert weights for fewer than 32 tokens,
+ * and from 32 tokens on runs the grouped kernels of _prefill;
  * _prefill groups the pairs by expert and decodes each weight tile once per
  * expert for all its tokens (long prompts). Both compute the same function.
+ * escha_moe_workspace_bytes(L, n_tokens, prefill) sizes the workspace of
+ * the call that will be made (prefill = 1 for _prefill, 0 for _decode).
  */
 ESCHA_API size_t escha_moe_workspace_bytes(const escha_moe_layer_t* L, int32_t n_tokens, int32_t prefill);
 ESCHA_API int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,

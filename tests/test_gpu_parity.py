@@ -219,10 +219,11 @@ def test_layer_prefill_matches_oracle_on_subset(escha):
 
 
 def test_prefill_equals_decode_path(escha, layer2, layer2_dev):
-    """Both entry points compute the same function (T=100, ragged)."""
-    announce("prefill vs decode T=100")
-    x = synth.activations(31, 100, 2048)
-    ids, w = oracle.route_topk(synth.normal_logits(31, 100), 8)
+    """Both entry points compute the same function (T=31: the decode entry
+    streams every pair, the prefill entry runs the grouped kernels)."""
+    announce("prefill vs decode T=31")
+    x = synth.activations(31, 31, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(31, 31), 8)
     a = escha.escha_moe_layer_decode(layer2_dev, to_dev(x), to_dev(ids), to_dev(w.astype(np.float32)))
     b = escha.escha_moe_layer_prefill(layer2_dev, to_dev(x), to_dev(ids), to_dev(w.astype(np.float32)))
     rel, mx = errors(b.cpu().numpy(), a.cpu().numpy())
