@@ -298,7 +298,7 @@ int64_t round32(int64_t n) { return (n + 31) / 32 * 32; }
 struct FlowLayout {
   int64_t p8, df_pair;
   int64_t dflag, ctl_ints;  // offset / total, in ints
-  size_t gu_part, dn_part, dn_copy, xcb, data_bytes;  // offsets in bytes from the data start
+  size_t gu_part, dn_part, dn_copy, ycb, sscb, data_bytes;  // offsets in bytes from the data start
 };
 
 FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
@@ -314,8 +314,10 @@ FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) 
   off += round_up((size_t)f.p8 * (H / 1024) * (2 * I) * sizeof(uint64_t));
   f.dn_part = off;
   off += round_up(2 * f.dn_copy * sizeof(uint64_t));
-  f.xcb = off;
+  f.ycb = off;
   off += round_up((size_t)T * 8 * H * sizeof(uint64_t));
+  f.sscb = off;
+  off += round_up((size_t)T * 8 * 32 * sizeof(uint64_t));
   f.data_bytes = off;
   return f;
 }
@@ -639,7 +641,8 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   a.gu_part = (uint64_t*)(data + f.gu_part);
   a.dn_part = (uint64_t*)(data + f.dn_part);
   a.dn_copy = (int64_t)f.dn_copy;
-  a.xcb = (uint64_t*)(data + f.xcb);
+  a.ycb = (uint64_t*)(data + f.ycb);
+  a.sscb = (uint64_t*)(data + f.sscb);
   a.dflag = ctl + f.dflag;
   a.df_pair = (int32_t)f.df_pair;
   a.epoch = ctl + 2;
@@ -649,10 +652,6 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   // status, tickets and flags to zero, the call number one further
   hipError_t e = escha::launch_flow_prepare(ctl, (size_t)f.ctl_ints, s);
   if (e != hipSuccess) return hip_fail(e, "flag clear launch");
-  if (x_chain) {  // layer 0's input; the kernel writes the others
-    e = hipMemcpyAsync(x_chain, x0_bf16, (size_t)T * H * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "x_chain copy");
-  }
   if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[0], s)) != hipSuccess)
     return hip_fail(e, "probe event record");
   e = escha::launch_stack_flow(a, L0->gate_up.k_bits, L0->down.k_bits, s);

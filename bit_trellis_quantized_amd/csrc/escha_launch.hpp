@@ -132,7 +132,8 @@ struct FlowArgs {
   uint64_t* gu_part;   // tagged [p8][hidden/1024][2*inter], written and read on the pair's XCD
   uint64_t* dn_part;   // tagged, 2 copies of [p8][hidden]: each pair's weighted output
   int64_t dn_copy;     // words per copy
-  uint64_t* xcb;       // tagged [n_tokens][8][hidden]: each XCD's copy of the next layer's input
+  uint64_t* ycb;       // tagged [n_tokens][8][hidden]: each XCD's copy of the layer output
+  uint64_t* sscb;      // tagged [n_tokens][8][32]: its per-128-block sums of squares
   int32_t* dflag;      // [n_layers][p8][df_pair]: down task of output group g at g (its tag)
   int32_t df_pair;
   const int32_t* epoch;  // the call number

@@ -14,10 +14,10 @@
 //     (two per wave), the sum over the channels and the output transform,
 //     weighted by the router probability: the pair's finished output for
 //     the group;
-//   combine (token t, XCD x): the sum of the token's pair outputs in slot
-//     order, the RMSNorm (unit weight) and the rounding to bf16 of the next
-//     layer's input, which the next layer's gate_up tasks on XCD x read (in
-//     the last layer: the output y).
+//   combine (token t, XCD x, 1024-output half): the sum of the token's
+//     pair outputs and the sums of squares of the half's 128-blocks, which
+//     the next layer's gate_up tasks on XCD x read and turn into their
+//     RMS-normalised bf16 inputs (in the last layer: the output y).
 // The arithmetic per projection is the method's (rin, H_n, the decoded
 // weights with fp32 accumulation, H_n, rout); the summation order differs
 // from the layer-by-layer kernels (here each task sums over more inputs
@@ -214,7 +214,7 @@ struct Lds {
   _Float16 xh[8][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
   _Float16 xl[8][128] __attribute__((aligned(16)));  // and their low parts
   float xe[8];                                       // undo factor of each block's scale
-  float red[1024] __attribute__((aligned(16)));      // per-input-block sums of the task's outputs
+  float red[2048] __attribute__((aligned(16)));      // per-input-block sums of the task's outputs
   float ssb[32];
   int skip[4];
   int ok[kWaves];
@@ -295,7 +295,8 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   const int nh = ncg / 8;                        // gate_up input eighths-of-1024 (8 chunks each)
   const int ncd = I / 128, ngd = H / 256;        // down chunks (<= 4) / output groups
   const int nb_gu = nh * ngb * P8, nb_dn = ngd * P8;
-  const int per_layer = nb_gu + nb_dn + T * 8;
+  const int nb = H / 128, nhf = (nb + 7) / 8;   // output blocks / combine tasks per (token, XCD)
+  const int per_layer = nb_gu + nb_dn + T * nhf * 8;
 
   // claim this XCD's next task: the j-th work-group to start on XCD x runs
   // task 8j + x (the grid holds at least as many work-groups per XCD as the
@@ -359,20 +360,37 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     pin_operands(A);
     __syncthreads();  // sh.ok initialised
     if (nq == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
-      float xv[2];
+      float x0, x1;
       if (l == 0) {
         const uint16_t* xr = a.x0 + (size_t)t * H + c * 128;
-        xv[0] = bf16_to_f32(xr[lane]);
-        xv[1] = bf16_to_f32(xr[lane + 64]);
+        x0 = bf16_to_f32(xr[lane]);
+        x1 = bf16_to_f32(xr[lane + 64]);
       } else {
-        // the previous layer's combine task of this token on this XCD wrote
-        // the chunk's inputs
-        const uint64_t* xr = a.xcb + ((size_t)t * 8 + x) * H + c * 128 + lane;
-        const bool ok = wave_fetch<2>([&](int i) { return xr + 64 * i; }, 2, tag - 1u, xv, a.error);
+        // the previous layer's combine tasks of this token on this XCD wrote
+        // the chunk's outputs y and every block's sum of squares: RMSNorm,
+        // rounded to bf16
+        const uint64_t* yr = a.ycb + ((size_t)t * 8 + x) * H + c * 128 + lane;
+        const uint64_t* sr = a.sscb + ((size_t)t * 8 + x) * 32 + (lane < ncg ? lane : 0);
+        float v[3];
+        const bool ok = wave_fetch<3>([&](int i) { return i < 2 ? yr + 64 * i : sr; }, 3, tag - 1u, v,
+                                      a.error);
         if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
         __builtin_amdgcn_s_setprio(3);
+        float tot = 0.f;  // the blocks' sums of squares in block order
+#pragma unroll
+        for (int b = 0; b < 32; ++b)
+          if (b < ncg) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[2]), b));
+        const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
+        const uint16_t b0 = f32_to_bf16_rne(v[0] * inv);
+        const uint16_t b1 = f32_to_bf16_rne(v[1] * inv);
+        x0 = bf16_to_f32(b0);
+        x1 = bf16_to_f32(b1);
       }
-      const float x0 = xv[0], x1 = xv[1];
+      if (a.x_chain && g == 0 && p % k == 0) {  // the layer input, recorded by one pair per token
+        uint16_t* xo = a.x_chain + ((size_t)l * T + t) * H + c * 128;
+        xo[lane] = f32_to_bf16_rne(x0);
+        xo[lane + 64] = f32_to_bf16_rne(x1);
+      }
       float v0 = x0 * rin0;
       float v1 = x1 * rin1;
       fwht128(v0, v1);
@@ -482,80 +500,72 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     if (tid == 0) st_remote(a.dflag + ((size_t)l * P8 + p) * a.df_pair + g, (int)tag);
   } else {
     // ------------------------------------------------------------ combine
+    // task (token t, XCD x, outputs 1024 hf .. 1024 hf + 1023): the sum of
+    // the token's pair outputs and the sums of squares of its 128-blocks,
+    // for the next layer's gate_up tasks on XCD x. Waves 2i and 2i + 1 take
+    // block 8 hf + i, lanes its outputs lane and lane + 64; the even wave
+    // sums the first half of the slots in order, the odd wave the second
+    // half, and the two halves are added (first + second).
     r -= nb_dn;
     const int x = r & 7;
-    const int t = r >> 3;
+    r >>= 3;
+    const int hf = r % nhf;
+    const int t = r / nhf;
     // combine tasks run only on XCDs that hold a pair of the token (the
     // next layer's gate_up tasks there read them); in the last layer only
-    // the XCD of the token's first pair runs one, to write y_last
+    // the XCD of the token's first pair runs them, to write y_last
     const int x_first = (t * k) & 7;
     const bool last = l == a.n_layers - 1;
     if (last ? x != x_first : (k < 8 && ((x - x_first) & 7) >= k)) return;
+    const int b = 8 * hf + (wave >> 1);  // this wave's 128-block
     if (wave == 0) {
-      // every down task of the token's pairs has flagged its output
-      const int32_t* df = a.dflag + ((size_t)l * P8 + (size_t)t * k) * a.df_pair;
+      // the down tasks of the token's pairs for these outputs have flagged
+      const int32_t* df = a.dflag + ((size_t)l * P8 + (size_t)t * k) * a.df_pair + 4 * hf;
       const int32_t* mine =
-          lane < k * ngd ? df + (size_t)(lane / ngd) * a.df_pair + (lane % ngd) : nullptr;
+          lane < 4 * k ? df + (size_t)(lane >> 2) * a.df_pair + (lane & 3) : nullptr;
       const bool ok = wave_wait(mine, (int)tag, a.error);
       if (lane == 0) sh.ok[0] = ok ? 1 : 0;
     }
     __syncthreads();
     if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
-    // wave w: 128-blocks w, w + 16, ..; lanes hold outputs lane and lane + 64
-    // of a block; the pair outputs are summed in slot order from 0
-    const int nb = H / 128;
-    const uint64_t* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)t * k * H;
-    float yv[2][2];
+    const int half = (k + 1) / 2;
+    const int j0 = (wave & 1) ? half : 0;  // this wave's slots j0 .. j1 - 1
+    const int j1 = (wave & 1) ? k : half;
+    const uint64_t* pp =
+        a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)(t * k + j0) * H + 128 * b + lane;
+    float y0 = 0.f, y1 = 0.f;
     bool ok = true;
+    if (b < nb) {
+      float v[16];
+      ok = wave_fetch<16>([&](int i) { return pp + (size_t)(i >> 1) * H + ((i & 1) ? 64 : 0); },
+                          2 * (j1 - j0), tag, v, a.error);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int b = wave + kWaves * s;
-      yv[s][0] = yv[s][1] = 0.f;
-      if (b < nb) {
-        const uint64_t* pb = pp + 128 * b + lane;
-        for (int j0 = 0; j0 < k && ok; j0 += 8) {  // eight slots per fetch
-          float v[16];
-          ok = wave_fetch<16>([&](int i) { return pb + (size_t)(j0 + (i >> 1)) * H + ((i & 1) ? 64 : 0); },
-                              k - j0 < 8 ? 2 * (k - j0) : 16, tag, v, a.error);
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j0 + j < k) {
-              yv[s][0] += v[2 * j];
-              yv[s][1] += v[2 * j + 1];
-            }
+      for (int j = 0; j < 8; ++j)
+        if (j < j1 - j0) {
+          y0 += v[2 * j];
+          y1 += v[2 * j + 1];
         }
-        if (last) {
-          a.y_last[(size_t)t * H + 128 * b + lane] = yv[s][0];
-          a.y_last[(size_t)t * H + 128 * b + lane + 64] = yv[s][1];
-        } else {
-          const float sq = wave_sum(__builtin_fmaf(yv[s][0], yv[s][0], yv[s][1] * yv[s][1]));
-          if (lane == 0) sh.ssb[b] = sq;
-        }
+      if (wave & 1) {  // second half of the slots to LDS
+        sh.red[128 * (wave >> 1) + lane] = y0;
+        sh.red[1024 + 128 * (wave >> 1) + lane] = y1;
       }
     }
     if (lane == 0 && !ok) sh.ok[wave] = 0;
-    if (last) return;
     __syncthreads();
     if (!all_ok(sh)) return;
-    // RMSNorm: the blocks' sums of squares in block order, then bf16
-    float tot = 0.f;
-    for (int b = 0; b < nb; ++b) tot += sh.ssb[b];
-    const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
-    uint64_t* xo = a.xcb + ((size_t)t * 8 + x) * H;
-    uint16_t* xc = (a.x_chain && x == x_first) ? a.x_chain + ((size_t)(l + 1) * T + t) * H : nullptr;
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int b = wave + kWaves * s;
-      if (b < nb) {
-        const uint16_t b0 = f32_to_bf16_rne(yv[s][0] * inv);
-        const uint16_t b1 = f32_to_bf16_rne(yv[s][1] * inv);
-        xo[128 * b + lane] = tag_word(bf16_to_f32(b0), tag);
-        xo[128 * b + lane + 64] = tag_word(bf16_to_f32(b1), tag);
-        if (xc) {
-          xc[128 * b + lane] = b0;
-          xc[128 * b + lane + 64] = b1;
-        }
+    if (!(wave & 1) && b < nb) {
+      y0 += sh.red[128 * (wave >> 1) + lane];
+      y1 += sh.red[1024 + 128 * (wave >> 1) + lane];
+      if (last) {
+        a.y_last[(size_t)t * H + 128 * b + lane] = y0;
+        a.y_last[(size_t)t * H + 128 * b + lane + 64] = y1;
+      } else {
+        uint64_t* yo = a.ycb + ((size_t)t * 8 + x) * H + 128 * b + lane;
+        yo[0] = tag_word(y0, tag);
+        yo[64] = tag_word(y1, tag);
+        const float sq = wave_sum(__builtin_fmaf(y0, y0, y1 * y1));
+        if (lane == 0) a.sscb[((size_t)t * 8 + x) * 32 + b] = tag_word(sq, tag);
       }
     }
   }
@@ -581,7 +591,7 @@ hipError_t launch_flow_prepare(int32_t* ctl, size_t n, hipStream_t s) {
 int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens) {
   const int64_t P8 = ((int64_t)n_tokens * top_k + 7) / 8 * 8;
   return (int64_t)(hidden / 1024) * (2 * inter / 128) * P8 + (int64_t)(hidden / 256) * P8 +
-         (int64_t)n_tokens * 8;
+         (int64_t)n_tokens * ((hidden / 128 + 7) / 8) * 8;
 }
 
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s) {
