@@ -191,17 +191,6 @@ static __device__ __noinline__ float2 scale_block(float m) {
   return make_float2(scale, unscale);
 }
 
-// B operand for the tile-row pair pp of a 128-input block: column 0 the
-// high parts, column 1 the low parts of inputs 32pp + 8 (l / 16) + i.
-__device__ __forceinline__ h16x8 make_b(const _Float16* xh, const _Float16* xl, int pp, int lane) {
-  const int col = lane & 15;
-  const int o = 32 * pp + 8 * (lane >> 4);
-  const h16x8 hi = *reinterpret_cast<const h16x8*>(xh + o);
-  const h16x8 lo = *reinterpret_cast<const h16x8*>(xl + o);
-  const h16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
-  return col == 0 ? hi : (col == 1 ? lo : zero);
-}
-
 // z of the 4 tiles x 16 outputs of a wave from its accumulators: lane
 // 16g (g = 0..3) receives outputs 4g .. 4g+3 of tile j in zr[j] (high part
 // plus low part, times the unscale factor); other lanes' zr are unspecified.

@@ -213,6 +213,7 @@ struct Lds {
   uint32_t code[kWaves * Stage<3>::kDw];            // each wave's staged codes
   _Float16 xh[8][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
   _Float16 xl[8][128] __attribute__((aligned(16)));  // and their low parts
+  _Float16 xz[128] __attribute__((aligned(16)));     // zeros (B's other columns)
   float xe[8];                                       // undo factor of each block's scale
   float red[2048] __attribute__((aligned(16)));      // per-input-block sums of the task's outputs
   float ssb[32];
@@ -235,15 +236,22 @@ __device__ __forceinline__ bool all_ok(const Lds& sh) {
 // 16 (4nq + j) + n of the task).
 __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq,
                                            int stride, int lane) {
+  // B operands of the four tile-row pairs: column 0 of B = high parts,
+  // column 1 = low parts, other columns zero (each lane reads its column)
+  const int col = lane & 15;
+  const _Float16* src = col == 0 ? sh.xh[cl] : (col == 1 ? sh.xl[cl] : sh.xz);
+  h16x8 B[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+    B[pp] = *reinterpret_cast<const h16x8*>(src + 32 * pp + 8 * (lane >> 4));
   f32x4 D[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    const h16x8 B = make_b(sh.xh[cl], sh.xl[cl], pp, lane);
+  for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B, D[j], 0, 0, 0);
-  }
+    for (int j = 0; j < 4; ++j)
+      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B[pp], D[j], 0, 0, 0);
   float4 zr[4];
   finish_mfma(D, sh.xe[cl], zr);
   if ((lane & 15) == 0) {
@@ -318,6 +326,7 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   const uint32_t epoch = (uint32_t)a.epoch[0];
   const uint32_t tag = (epoch << 8) + (uint32_t)l + 1u;
   if (tid < kWaves) sh.ok[tid] = 1;
+  if (tid < 64) reinterpret_cast<uint32_t*>(sh.xz)[tid] = 0u;
   const StackLayer& Ly = a.layer[l];
 
 
