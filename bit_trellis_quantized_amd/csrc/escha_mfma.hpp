@@ -61,9 +61,14 @@ __device__ __forceinline__ void stage_issue(const uint16_t* __restrict__ code_e,
   }
 }
 
+// LDS position (in tiles) of tile-row r, tile j of a wave's region: the odd
+// tile-rows after the even ones, so that the 16 tiles a lane decodes (rows
+// of one parity) are contiguous.
+__device__ __forceinline__ int stage_slot(int r, int j) { return (r & 1) * 16 + (r >> 1) * 4 + j; }
+
 // Store the loaded chunks to the wave's LDS region (tile (r, j) at dword
-// (4 r + j) * kStride) with each tile's wrap dword; the wave can read them
-// back once this returns.
+// stage_slot(r, j) * kStride) with each tile's wrap dword; the wave can read
+// them back once this returns.
 template <int K>
 __device__ __forceinline__ void stage_store(uint32_t* lds, int lane,
                                             const u32x4 (&v)[Stage<K>::kPerLane]) {
@@ -76,7 +81,7 @@ __device__ __forceinline__ void stage_store(uint32_t* lds, int lane,
     const int cc = c - r * kRowChunks;
     const int j = cc / kTileChunks;
     const int d = 4 * (cc - j * kTileChunks);
-    uint32_t* t = lds + (4 * r + j) * Stage<K>::kStride;
+    uint32_t* t = lds + stage_slot(r, j) * Stage<K>::kStride;
     t[d + 0] = v[m].x;
     t[d + 1] = v[m].y;
     t[d + 2] = v[m].z;
@@ -96,7 +101,7 @@ __device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
   const int h = g & 1;
   // tile of the pair: rows 2pp + (g >> 1); lane-dependent part of the
   // window positions
-  const uint32_t* base = lds + (g >> 1) * 4 * Stage<K>::kStride;
+  const uint32_t* base = lds + stage_slot(g >> 1, 0) * Stage<K>::kStride;
   int a0, a1;
   uint32_t s0, s1;
   if constexpr (K == 2) {
@@ -112,13 +117,18 @@ __device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
     s0 = (3 * n) & 31;
     s1 = (16 + 3 * n) & 31;
   }
-  const uint32_t* p0 = base + a0;
-  const uint32_t* p1 = base + a1;
+  // the tiles of pairs 2 and 3 through second base addresses (opaque to the
+  // compiler, so that it keeps them instead of adding a constant before
+  // every read: LDS read offsets reach 255 dwords)
+  int a0h = a0 + 8 * Stage<K>::kStride, a1h = a1 + 8 * Stage<K>::kStride;
+  asm volatile("" : "+v"(a0h), "+v"(a1h));
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp) {
+    const uint32_t* p0 = base + (pp < 2 ? a0 : a0h);
+    const uint32_t* p1 = base + (pp < 2 ? a1 : a1h);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int toff = (2 * pp * 4 + j) * Stage<K>::kStride;
+      const int toff = (stage_slot(2 * (pp & 1), j) - stage_slot(0, 0)) * Stage<K>::kStride;
       uint32_t win[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {

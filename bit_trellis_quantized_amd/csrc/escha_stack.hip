@@ -193,27 +193,26 @@ __device__ __forceinline__ void pin_decoded(h16x2 (&wv)[NKT][32]) {
 
 constexpr int kWaves = 16;  // waves per work-group
 
+// SiLU from the hardware exponential and reciprocal (each within about one
+// ulp): g / (1 + e^-g), within a few ulp of the correctly rounded value.
+// Large negative g gives e^-g = inf and a zero (signed) result.
+__device__ __forceinline__ float silu_fast(float g) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Keep decoded operands where they are (see pin_decoded).
 __device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t u = __builtin_bit_cast(uint32_t, h16x2{A[pp][j][2 * i], A[pp][j][2 * i + 1]});
-        asm volatile("" : "+v"(u));
-        const h16x2 w = __builtin_bit_cast(h16x2, u);
-        A[pp][j][2 * i] = w.x;
-        A[pp][j][2 * i + 1] = w.y;
-      }
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(A[pp][j]));
 }
 
 struct Lds {
   uint32_t code[kWaves * Stage<3>::kDw];            // each wave's staged codes
   _Float16 xh[8][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
   _Float16 xl[8][128] __attribute__((aligned(16)));  // and their low parts
-  _Float16 xz[128] __attribute__((aligned(16)));     // zeros (B's other columns)
   float xe[8];                                       // undo factor of each block's scale
   float red[2048] __attribute__((aligned(16)));      // per-input-block sums of the task's outputs
   float ssb[32];
@@ -237,13 +236,17 @@ __device__ __forceinline__ bool all_ok(const Lds& sh) {
 __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq,
                                            int stride, int lane) {
   // B operands of the four tile-row pairs: column 0 of B = high parts,
-  // column 1 = low parts, other columns zero (each lane reads its column)
+  // column 1 = low parts, other columns zero; only the lanes of columns 0
+  // and 1 read LDS
   const int col = lane & 15;
-  const _Float16* src = col == 0 ? sh.xh[cl] : (col == 1 ? sh.xl[cl] : sh.xz);
   h16x8 B[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-    B[pp] = *reinterpret_cast<const h16x8*>(src + 32 * pp + 8 * (lane >> 4));
+  for (int pp = 0; pp < 4; ++pp) B[pp] = h16x8{};
+  if (col < 2) {
+    const _Float16* src = (col == 0 ? sh.xh[cl] : sh.xl[cl]) + 8 * (lane >> 4);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) B[pp] = *reinterpret_cast<const h16x8*>(src + 32 * pp);
+  }
   f32x4 D[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -326,7 +329,6 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   const uint32_t epoch = (uint32_t)a.epoch[0];
   const uint32_t tag = (epoch << 8) + (uint32_t)l + 1u;
   if (tid < kWaves) sh.ok[tid] = 1;
-  if (tid < 64) reinterpret_cast<uint32_t*>(sh.xz)[tid] = 0u;
   const StackLayer& Ly = a.layer[l];
 
 
@@ -367,6 +369,11 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     h16x8 A[4][4];
     decode_stage_mfma<KG>(stage, lane, A);
     pin_operands(A);
+    // arguments the normalisation needs, read now rather than after the wait
+    float eps = a.eps;
+    float inv_h = __int_as_float((96 + __builtin_clz(H)) << 23);  // 1 / H (a power of two)
+    uint16_t* x_chain = a.x_chain;
+    asm volatile("" : "+s"(eps), "+s"(inv_h), "+s"(x_chain));
     __syncthreads();  // sh.ok initialised
     if (nq == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
       float x0, x1;
@@ -385,18 +392,17 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
                                       a.error);
         if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
         __builtin_amdgcn_s_setprio(3);
-        float tot = 0.f;  // the blocks' sums of squares in block order
-#pragma unroll
-        for (int b = 0; b < 32; ++b)
-          if (b < ncg) tot += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[2]), b));
-        const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
+        // the blocks' sums of squares (lane b: block b) summed across the
+        // wave, the same bits in every lane and every task of the token
+        const float tot = wave_sum(lane < ncg ? v[2] : 0.f);
+        const float inv = 1.0f / sqrtf(tot * inv_h + eps);
         const uint16_t b0 = f32_to_bf16_rne(v[0] * inv);
         const uint16_t b1 = f32_to_bf16_rne(v[1] * inv);
         x0 = bf16_to_f32(b0);
         x1 = bf16_to_f32(b1);
       }
-      if (a.x_chain && g == 0 && p % k == 0) {  // the layer input, recorded by one pair per token
-        uint16_t* xo = a.x_chain + ((size_t)l * T + t) * H + c * 128;
+      if (x_chain && g == 0 && p % k == 0) {  // the layer input, recorded by one pair per token
+        uint16_t* xo = x_chain + ((size_t)l * T + t) * H + c * 128;
         xo[lane] = f32_to_bf16_rne(x0);
         xo[lane + 64] = f32_to_bf16_rne(x1);
       }
@@ -474,8 +480,8 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
         }
         if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
         __builtin_amdgcn_s_setprio(3);
-        const float h0 = silu(g0) * u0;
-        const float h1 = silu(g1) * u1;
+        const float h0 = silu_fast(g0) * u0;
+        const float h1 = silu_fast(g1) * u1;
         skip = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
         float v0 = h0 * rin0;
         float v1 = h1 * rin1;
