@@ -288,7 +288,7 @@ int check_layer_call(const escha_moe_layer_t* L, const uint16_t* x, int32_t T, c
 // Control block at the start of a stack workspace: a 512-int header (word 1:
 // status of the one-launch path; word 2: its call number; words 256 + 32x:
 // XCD x's task ticket) and that path's flag words, one per (layer, pair,
-// down output group). The tickets and flags are zeroed before every launch;
+// down output block). The tickets and flags are zeroed before every launch;
 // each group of flag words that one XCD writes starts on a 128-byte line of
 // its own.
 constexpr int64_t kCtlHeaderInts = 512;
@@ -305,13 +305,13 @@ FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) 
   FlowLayout f{};
   const int64_t H = L->hidden, I = L->inter;
   f.p8 = (T * L->top_k + 7) / 8 * 8;
-  f.df_pair = round32(H / 256);
+  f.df_pair = round32(H / 128);
   f.dflag = kCtlHeaderInts;
   f.ctl_ints = f.dflag + n_layers * f.p8 * f.df_pair;
   f.dn_copy = (size_t)f.p8 * H;
   size_t off = 0;
   f.gu_part = off;
-  off += round_up((size_t)f.p8 * (H / 1024) * (2 * I) * sizeof(uint64_t));
+  off += round_up((size_t)f.p8 * (H / 512) * (2 * I) * sizeof(uint64_t));
   f.dn_part = off;
   off += round_up(2 * f.dn_copy * sizeof(uint64_t));
   f.ycb = off;
@@ -606,7 +606,18 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
                 "top_k * hidden / 256 <= 64 (hidden=%lld inter=%lld top_k=%lld)",
                 (long long)H, (long long)I, (long long)k);
   if (n_tokens == 0) return ESCHA_OK;
-  const int64_t blocks = escha::flow_blocks_per_layer((int)H, (int)I, (int)k, (int)T) * n_layers;
+  // Small batches fold the combine into the down tasks, whose waits on each
+  // other are deadlock-free only while one layer's down tasks of one XCD
+  // can all be resident at once.
+  int dev = 0, n_cu = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) e = escha::flow_groups_per_cu(L0->gate_up.k_bits, L0->down.k_bits, &per_cu);
+  if (e != hipSuccess) return hip_fail(e, "device query");
+  const int64_t p8 = (T * k + 7) / 8 * 8;
+  const bool fold = k <= 8 && (p8 / 8) * (H / 128) <= (int64_t)(n_cu / 8) * per_cu;
+  const int64_t blocks =
+      escha::flow_blocks_per_layer((int)H, (int)I, (int)k, (int)T, fold) * n_layers;
   if (blocks + escha::kFlowSpare > 0x7FFFFFFF)
     return fail(ESCHA_E_UNSUPPORTED, "%lld work-groups exceed one grid", (long long)blocks);
 
@@ -648,9 +659,10 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   a.epoch = ctl + 2;
   a.ticket = ctl + 256;
   a.error = ctl + 1;
+  a.fold = fold ? 1 : 0;
 
   // status, tickets and flags to zero, the call number one further
-  hipError_t e = escha::launch_flow_prepare(ctl, (size_t)f.ctl_ints, s);
+  e = escha::launch_flow_prepare(ctl, (size_t)f.ctl_ints, s);
   if (e != hipSuccess) return hip_fail(e, "flag clear launch");
   if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[0], s)) != hipSuccess)
     return hip_fail(e, "probe event record");

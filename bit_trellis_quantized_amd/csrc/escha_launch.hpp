@@ -129,24 +129,27 @@ struct FlowArgs {
   const uint16_t* x0;  // bf16 [n_tokens][hidden]
   float* y_last;       // fp32 [n_tokens][hidden]
   uint16_t* x_chain;   // nullable: bf16 [n_layers][n_tokens][hidden]
-  uint64_t* gu_part;   // tagged [p8][hidden/1024][2*inter], written and read on the pair's XCD
+  uint64_t* gu_part;   // tagged [p8][hidden/512][2*inter], written and read on the pair's XCD
   uint64_t* dn_part;   // tagged, 2 copies of [p8][hidden]: each pair's weighted output
   int64_t dn_copy;     // words per copy
   uint64_t* ycb;       // tagged [n_tokens][8][hidden]: each XCD's copy of the layer output
   uint64_t* sscb;      // tagged [n_tokens][8][32]: its per-128-block sums of squares
-  int32_t* dflag;      // [n_layers][p8][df_pair]: down task of output group g at g (its tag)
+  int32_t* dflag;      // [n_layers][p8][df_pair]: down task of output block g at g (its tag)
   int32_t df_pair;
   const int32_t* epoch;  // the call number
   int32_t* ticket;     // [8][32]: next task of each XCD (word 32x)
   int32_t* error;      // 1: a wait gave up
+  int32_t fold;        // 1: the down tasks combine the pair outputs (no combine tasks)
 };
 constexpr int kFlowSpare = 64;  // work-groups launched beyond the task count (8 per XCD)
 
-int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens);
+int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens, bool fold);
 // Zero the n words of a control block except word 2, the call number, which
 // it advances (modulo 2^24).
 hipError_t launch_flow_prepare(int32_t* ctl, size_t n, hipStream_t s);
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s);
+// Work-groups of the one-launch kernel that one compute unit holds at once.
+hipError_t flow_groups_per_cu(int k_gu, int k_dn, int* n);
 
 hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,
                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s);

@@ -191,7 +191,8 @@ __device__ __forceinline__ void pin_decoded(h16x2 (&wv)[NKT][32]) {
     }
 }
 
-constexpr int kWaves = 16;  // waves per work-group
+constexpr int kWaves = 8;    // waves per work-group (two work-groups per compute unit)
+constexpr int kChunks = 4;   // 128-input chunks of a gate_up task; channel chunks of a down task
 
 // SiLU from the hardware exponential and reciprocal (each within about one
 // ulp): g / (1 + e^-g), within a few ulp of the correctly rounded value.
@@ -210,13 +211,15 @@ __device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
 }
 
 struct Lds {
-  uint32_t code[kWaves * Stage<3>::kDw];            // each wave's staged codes
-  _Float16 xh[8][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per 128-block
-  _Float16 xl[8][128] __attribute__((aligned(16)));  // and their low parts
-  float xe[8];                                       // undo factor of each block's scale
-  float red[2048] __attribute__((aligned(16)));      // per-input-block sums of the task's outputs
-  float ssb[32];
-  int skip[4];
+  uint32_t code[kWaves * Stage<3>::kDw];                   // each wave's staged codes
+  _Float16 xh[kChunks][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per chunk
+  _Float16 xl[kChunks][128] __attribute__((aligned(16)));  // and their low parts
+  float xe[kChunks];                                       // undo factor of each chunk's scale
+  float red[kChunks * 128] __attribute__((aligned(16)));   // per-chunk sums of the task's outputs
+  float rin[kChunks][128];                                 // input scales of the task's chunks
+  float rout[128];                                         // output scales of its block
+  float4 part[kChunks][64];                                // down: second-half gate_up part sums
+  int skip[kChunks];
   int ok[kWaves];
   int task;
 };
@@ -264,24 +267,23 @@ __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int 
   }
 }
 
-// Output transform of the task's outputs (stride of them, 128 per wave of
-// the first stride / 128): the sum over the first nb input blocks (in block
-// order), H_n, rout (ro0, ro1 at this lane's two outputs) and the weight,
-// stored as tagged words (REMOTE: sc1 stores).
+// Output transform of the task's 128 outputs (wave 0): the sum over the
+// first nb input chunks (in chunk order), H_n, rout (sh.rout) and the
+// weight, stored as tagged words (REMOTE: sc1 stores).
 template <bool REMOTE>
-__device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, int stride, float ro0,
-                                                    float ro1, float wt, uint64_t* __restrict__ out,
-                                                    uint32_t tag, int wave, int lane) {
-  if (wave < stride / 128) {
-    const int o = 128 * wave + lane;
+__device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, float wt,
+                                                    uint64_t* __restrict__ out, uint32_t tag,
+                                                    int wave, int lane) {
+  if (wave == 0) {
+    const int o = lane;
     float z0 = sh.red[o], z1 = sh.red[o + 64];
     for (int b = 1; b < nb; ++b) {
-      z0 += sh.red[stride * b + o];
-      z1 += sh.red[stride * b + o + 64];
+      z0 += sh.red[128 * b + o];
+      z1 += sh.red[128 * b + o + 64];
     }
     fwht128(z0, z1);
-    const float o0 = z0 * kInvSqrt128 * ro0 * wt;
-    const float o1 = z1 * kInvSqrt128 * ro1 * wt;
+    const float o0 = z0 * kInvSqrt128 * sh.rout[o] * wt;
+    const float o1 = z1 * kInvSqrt128 * sh.rout[o + 64] * wt;
     if constexpr (REMOTE) {
       st_remote64(out + o, tag_word(o0, tag));
       st_remote64(out + o + 64, tag_word(o1, tag));
@@ -292,10 +294,28 @@ __device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, int s
   }
 }
 
+// A combined 128-block of a token's layer output (y0, y1: outputs lane and
+// lane + 64 of block b): in the last layer the output y; otherwise XCD x's
+// copy of it and the block's sum of squares, tagged. Whole wave.
+__device__ __forceinline__ void store_combined(const FlowArgs& a, bool last, int t, int x, int b,
+                                               int lane, float y0, float y1, uint32_t tag) {
+  const int H = a.hidden;
+  if (last) {
+    a.y_last[(size_t)t * H + 128 * b + lane] = y0;
+    a.y_last[(size_t)t * H + 128 * b + lane + 64] = y1;
+  } else {
+    uint64_t* yo = a.ycb + ((size_t)t * 8 + x) * H + 128 * b + lane;
+    yo[0] = tag_word(y0, tag);
+    yo[64] = tag_word(y1, tag);
+    const float sq = wave_sum(__builtin_fmaf(y0, y0, y1 * y1));
+    if (lane == 0) a.sscb[((size_t)t * 8 + x) * 32 + b] = tag_word(sq, tag);
+  }
+}
+
 }  // namespace
 
 template <int KG, int KD>
-__global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a) {
   __shared__ Lds sh;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -303,11 +323,11 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
   const int H = a.hidden, I = a.inter, k = a.top_k, T = a.n_tokens;
   const int P = T * k, P8 = a.p8;
   const int ncg = H / 128, ngb = (2 * I) / 128;  // gate_up input chunks / output blocks
-  const int nh = ncg / 8;                        // gate_up input eighths-of-1024 (8 chunks each)
-  const int ncd = I / 128, ngd = H / 256;        // down chunks (<= 4) / output groups
+  const int nh = ncg / kChunks;                  // gate_up input parts (kChunks chunks each)
+  const int ncd = I / 128, ngd = H / 128;        // down chunks (<= kChunks) / output blocks
   const int nb_gu = nh * ngb * P8, nb_dn = ngd * P8;
-  const int nb = H / 128, nhf = (nb + 7) / 8;   // output blocks / combine tasks per (token, XCD)
-  const int per_layer = nb_gu + nb_dn + T * nhf * 8;
+  const int nb = H / 128, nhf = (nb + 3) / 4;   // output blocks / combine tasks per (token, XCD)
+  const int per_layer = nb_gu + nb_dn + (a.fold ? 0 : T * nhf * 8);
 
   // claim this XCD's next task: the j-th work-group to start on XCD x runs
   // task 8j + x (the grid holds at least as many work-groups per XCD as the
@@ -334,8 +354,8 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
 
   if (r < nb_gu) {
     // ------------------------------------------------------------ gate_up
-    // task (pair p, inputs 1024 hh .. 1024 hh + 1023, outputs 128 g .. 128 g +
-    // 127); wave w: input chunk cl = w / 2 of the eight (its 8 tile-rows),
+    // task (pair p, inputs 512 hh .. 512 hh + 511, outputs 128 g .. 128 g +
+    // 127); wave w: input chunk cl = w / 2 of the four (its 8 tile-rows),
     // output tiles 4 nq .. 4 nq + 3 (nq = w % 2) of the block
     const int cl = wave >> 1;
     const int nq = wave & 1;
@@ -344,7 +364,7 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     r /= P8;
     const int g = r % ngb;
     const int hh = r / ngb;
-    const int c = 8 * hh + cl;  // this wave's input chunk
+    const int c = kChunks * hh + cl;  // this wave's input chunk
     const int t = p / k;
     const int x = p & 7;
     const int e = a.ids[(size_t)l * P + p];
@@ -358,14 +378,19 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const uint16_t* code_e = Ly.gu_code + (size_t)es * (size_t)ncg * 8 * n_nt * (16 * KG);
     u32x4 cv[Stage<KG>::kPerLane];
     stage_issue<KG>(code_e, n_nt, 8 * c, 8 * g + 4 * nq, lane, cv);
+    // the chunk's input scales and the block's output scales, kept in LDS
+    // until they are needed
     const uint16_t* rr = Ly.gu_rin + (size_t)es * H + c * 128;
-    const float rin0 = f16_to_f32(rr[lane]);
-    const float rin1 = f16_to_f32(rr[lane + 64]);
     const uint16_t* ro = Ly.gu_rout + (size_t)es * (2 * I) + g * 128;
-    const float ro0 = f16_to_f32(ro[lane]);
-    const float ro1 = f16_to_f32(ro[lane + 64]);
+    const uint16_t* rs = nq == 0 ? rr : ro;
+    const uint16_t s0 = rs[lane], s1 = rs[lane + 64];
     uint32_t* stage = sh.code + wave * Stage<KG>::kDw;
     stage_store<KG>(stage, lane, cv);
+    float* sd = nq == 0 ? sh.rin[cl] : sh.rout;
+    if (nq == 0 || wave == 1) {
+      sd[lane] = f16_to_f32(s0);
+      sd[lane + 64] = f16_to_f32(s1);
+    }
     h16x8 A[4][4];
     decode_stage_mfma<KG>(stage, lane, A);
     pin_operands(A);
@@ -406,8 +431,8 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
         xo[lane] = f32_to_bf16_rne(x0);
         xo[lane + 64] = f32_to_bf16_rne(x1);
       }
-      float v0 = x0 * rin0;
-      float v1 = x1 * rin1;
+      float v0 = x0 * sh.rin[cl][lane];
+      float v1 = x1 * sh.rin[cl][lane + 64];
       fwht128(v0, v1);
       const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cl], sh.xl[cl], lane);
       if (lane == 0) sh.xe[cl] = xe;
@@ -418,17 +443,17 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     if (valid) {  // uniform over the group
       mfma_block(sh, A, cl, nq, 128, lane);
       __syncthreads();
-      sum_transform_store<false>(sh, 8, 128, ro0, ro1, 1.0f, out, tag, wave, lane);
+      sum_transform_store<false>(sh, kChunks, 1.0f, out, tag, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
       out[lane] = tag_word(0.f, tag);
       out[lane + 64] = tag_word(0.f, tag);
     }
   } else if ((r -= nb_gu) < nb_dn) {
     // --------------------------------------------------------------- down
-    // task (pair p, outputs 256 g .. 256 g + 255); wave w: channel chunk
-    // cl = w / 4 (its 8 tile-rows), output tiles 4 nq .. 4 nq + 3 (nq = w % 4)
-    const int cl = wave >> 2;
-    const int nq = wave & 3;
+    // task (pair p, outputs 128 g .. 128 g + 127); wave w: channel chunk
+    // cl = w / 2 (its 8 tile-rows), output tiles 4 nq .. 4 nq + 3 (nq = w % 2)
+    const int cl = wave >> 1;
+    const int nq = wave & 1;
     const int p = r % P8;
     if (p >= P) return;
     const int g = r / P8;
@@ -436,55 +461,61 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const bool valid = e >= 0 && e < a.n_experts;
     const bool active = cl < ncd;  // this wave has tile-rows
     const int n_nt = H / 16;
-    uint64_t* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 256;
+    uint64_t* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 128;
 
     const int es = valid ? e : 0;
     const uint16_t* code_e = Ly.dn_code + (size_t)es * (size_t)ncd * 8 * n_nt * (16 * KD);
     u32x4 cv[Stage<KD>::kPerLane];
-    if (active) stage_issue<KD>(code_e, n_nt, 8 * cl, 16 * g + 4 * nq, lane, cv);
+    if (active) stage_issue<KD>(code_e, n_nt, 8 * cl, 8 * g + 4 * nq, lane, cv);
     const uint16_t* rr = Ly.dn_rin + (size_t)es * I + (active ? cl : 0) * 128;
-    const float rin0 = f16_to_f32(rr[lane]);
-    const float rin1 = f16_to_f32(rr[lane + 64]);
-    const uint16_t* ro = Ly.dn_rout + (size_t)es * H + g * 256 + 128 * (wave & 1);
-    const float ro0 = f16_to_f32(ro[lane]);
-    const float ro1 = f16_to_f32(ro[lane + 64]);
+    const uint16_t* ro = Ly.dn_rout + (size_t)es * H + g * 128;
+    const uint16_t* rs = nq == 0 ? rr : ro;
+    const uint16_t s0 = rs[lane], s1 = rs[lane + 64];
     const float wt = a.w[(size_t)l * P + p];
     uint32_t* stage = sh.code + wave * Stage<KD>::kDw;
     h16x8 A[4][4];
-    if (active) {
-      stage_store<KD>(stage, lane, cv);
-      decode_stage_mfma<KD>(stage, lane, A);
+    if (active) stage_store<KD>(stage, lane, cv);
+    float* sd = nq == 0 ? sh.rin[cl] : sh.rout;
+    if ((nq == 0 && active) || wave == 1) {
+      sd[lane] = f16_to_f32(s0);
+      sd[lane + 64] = f16_to_f32(s1);
     }
+    if (active) decode_stage_mfma<KD>(stage, lane, A);
     pin_operands(A);
     __syncthreads();  // sh.ok initialised
+    // gate and up sums of the chunk's channels over gate_up's input parts,
+    // once every gate_up task of this pair has written them: the chunk's
+    // wave nq fetches parts 2 nq and 2 nq + 1, and the sum is (part 0 +
+    // part 1) + (part 2 + part 3)
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (active && valid && 2 * nq < nh) {
+      const uint64_t* src = a.gu_part + ((size_t)p * nh + 2 * nq) * (2 * I) + 128 * cl + lane;
+      auto word = [&](int i) {  // part 2 nq + i / 4; gate, gate + 64, up, up + 64
+        return src + (size_t)(i >> 2) * (2 * I) + ((i & 1) ? 64 : 0) + ((i & 2) ? I : 0);
+      };
+      const bool ok = wave_fetch_sum4(word, nh - 2 * nq < 2 ? nh - 2 * nq : 2, tag,
+                                      make_float4(0.f, 0.f, 0.f, 0.f), sum, a.error);
+      if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
+      if (nq == 1) sh.part[cl][lane] = sum;
+    }
+    if (nh > 2) __syncthreads();  // second halves in LDS
     if (nq == 0 && active) {  // one wave per 128-channel chunk
       int skip = 1;
       if (valid) {
-        // gate and up sums of the chunk's channels over gate_up's input
-        // parts, in order, once every gate_up task of this pair has written them
-        const uint64_t* src = a.gu_part + (size_t)p * nh * (2 * I) + 128 * cl + lane;
-        auto word = [&](int i) {  // part i / 4; gate, gate + 64, up, up + 64
-          return src + (size_t)(i >> 2) * (2 * I) + ((i & 1) ? 64 : 0) + ((i & 2) ? I : 0);
-        };
-        float g0 = 0.f, g1 = 0.f, u0 = 0.f, u1 = 0.f;
-        bool ok = true;
-        for (int j0 = 0; j0 < nh && ok; j0 += 2) {  // two parts per fetch
-          float4 sum;
-          ok = wave_fetch_sum4([&](int i) { return word(4 * j0 + i); },
-                               nh - j0 < 2 ? nh - j0 : 2, tag, make_float4(g0, g1, u0, u1), sum,
-                               a.error);
-          g0 = sum.x;
-          g1 = sum.y;
-          u0 = sum.z;
-          u1 = sum.w;
-        }
-        if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
         __builtin_amdgcn_s_setprio(3);
+        if (nh > 2) {
+          const float4 q = sh.part[cl][lane];
+          sum.x += q.x;
+          sum.y += q.y;
+          sum.z += q.z;
+          sum.w += q.w;
+        }
+        const float g0 = sum.x, g1 = sum.y, u0 = sum.z, u1 = sum.w;
         const float h0 = silu_fast(g0) * u0;
         const float h1 = silu_fast(g1) * u1;
         skip = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
-        float v0 = h0 * rin0;
-        float v1 = h1 * rin1;
+        float v0 = h0 * sh.rin[cl][lane];
+        float v1 = h1 * sh.rin[cl][lane + 64];
         fwht128(v0, v1);
         const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cl], sh.xl[cl], lane);
         if (lane == 0) sh.xe[cl] = xe;
@@ -497,28 +528,54 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
       if (active && !sh.skip[cl]) {
-        mfma_block(sh, A, cl, nq, 256, lane);
+        mfma_block(sh, A, cl, nq, 128, lane);
       } else if (active && (lane & 15) == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(&sh.red[256 * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
+          *reinterpret_cast<float4*>(&sh.red[128 * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
               make_float4(0.f, 0.f, 0.f, 0.f);
       }
       __syncthreads();
-      sum_transform_store<true>(sh, ncd, 256, ro0, ro1, wt, out, tag, wave, lane);
-    } else if (wave < 2) {  // an out-of-range expert id contributes nothing
-      st_remote64(out + 128 * wave + lane, tag_word(0.f, tag));
-      st_remote64(out + 128 * wave + lane + 64, tag_word(0.f, tag));
+      sum_transform_store<true>(sh, ncd, wt, out, tag, wave, lane);
+    } else if (wave == 0) {  // an out-of-range expert id contributes nothing
+      st_remote64(out + lane, tag_word(0.f, tag));
+      st_remote64(out + lane + 64, tag_word(0.f, tag));
     }
-    // flag for the combine tasks (a hint: the tags decide)
-    __syncthreads();
-    if (tid == 0) st_remote(a.dflag + ((size_t)l * P8 + p) * a.df_pair + g, (int)tag);
+    if (a.fold) {
+      // the combine of this output block for the token's copy on this XCD:
+      // wave 0 (lanes outputs lane and lane + 64) adds the outputs of the
+      // token's pairs in slot order as soon as every one carries this
+      // layer's tag. The pair of slot j < 8 is the token's only pair on its
+      // XCD; in the last layer only slot 0 runs it, to write y.
+      const int t = p / k;
+      const int j = p - t * k;
+      if (wave == 0 && (l == a.n_layers - 1 ? j == 0 : j < 8)) {
+        const int b = g;
+        const uint64_t* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)t * k * H + 128 * b + lane;
+        float v[16];
+        if (wave_fetch<16>([&](int i) { return pp + (size_t)(i >> 1) * H + ((i & 1) ? 64 : 0); },
+                           2 * k, tag, v, a.error)) {
+          float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj)
+            if (jj < k) {
+              y0 += v[2 * jj];
+              y1 += v[2 * jj + 1];
+            }
+          store_combined(a, l == a.n_layers - 1, t, p & 7, b, lane, y0, y1, tag);
+        }
+      }
+    } else {
+      // flag for the combine tasks (a hint: the tags decide)
+      __syncthreads();
+      if (tid == 0) st_remote(a.dflag + ((size_t)l * P8 + p) * a.df_pair + g, (int)tag);
+    }
   } else {
     // ------------------------------------------------------------ combine
-    // task (token t, XCD x, outputs 1024 hf .. 1024 hf + 1023): the sum of
+    // task (token t, XCD x, outputs 512 hf .. 512 hf + 511): the sum of
     // the token's pair outputs and the sums of squares of its 128-blocks,
     // for the next layer's gate_up tasks on XCD x. Waves 2i and 2i + 1 take
-    // block 8 hf + i, lanes its outputs lane and lane + 64; the even wave
+    // block 4 hf + i, lanes its outputs lane and lane + 64; the even wave
     // sums the first half of the slots in order, the odd wave the second
     // half, and the two halves are added (first + second).
     r -= nb_dn;
@@ -532,7 +589,7 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     const int x_first = (t * k) & 7;
     const bool last = l == a.n_layers - 1;
     if (last ? x != x_first : (k < 8 && ((x - x_first) & 7) >= k)) return;
-    const int b = 8 * hf + (wave >> 1);  // this wave's 128-block
+    const int b = 4 * hf + (wave >> 1);  // this wave's 128-block
     if (wave == 0) {
       // the down tasks of the token's pairs for these outputs have flagged
       const int32_t* df = a.dflag + ((size_t)l * P8 + (size_t)t * k) * a.df_pair + 4 * hf;
@@ -563,7 +620,7 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
         }
       if (wave & 1) {  // second half of the slots to LDS
         sh.red[128 * (wave >> 1) + lane] = y0;
-        sh.red[1024 + 128 * (wave >> 1) + lane] = y1;
+        sh.red[128 * (wave >> 1) + 64 + lane] = y1;
       }
     }
     if (lane == 0 && !ok) sh.ok[wave] = 0;
@@ -571,17 +628,8 @@ __global__ __launch_bounds__(1024) void k_stack_flow(const FlowArgs a) {
     if (!all_ok(sh)) return;
     if (!(wave & 1) && b < nb) {
       y0 += sh.red[128 * (wave >> 1) + lane];
-      y1 += sh.red[1024 + 128 * (wave >> 1) + lane];
-      if (last) {
-        a.y_last[(size_t)t * H + 128 * b + lane] = y0;
-        a.y_last[(size_t)t * H + 128 * b + lane + 64] = y1;
-      } else {
-        uint64_t* yo = a.ycb + ((size_t)t * 8 + x) * H + 128 * b + lane;
-        yo[0] = tag_word(y0, tag);
-        yo[64] = tag_word(y1, tag);
-        const float sq = wave_sum(__builtin_fmaf(y0, y0, y1 * y1));
-        if (lane == 0) a.sscb[((size_t)t * 8 + x) * 32 + b] = tag_word(sq, tag);
-      }
+      y1 += sh.red[128 * (wave >> 1) + 64 + lane];
+      store_combined(a, last, t, x, b, lane, y0, y1, tag);
     }
   }
 }
@@ -603,16 +651,27 @@ hipError_t launch_flow_prepare(int32_t* ctl, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens) {
+int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens, bool fold) {
   const int64_t P8 = ((int64_t)n_tokens * top_k + 7) / 8 * 8;
-  return (int64_t)(hidden / 1024) * (2 * inter / 128) * P8 + (int64_t)(hidden / 256) * P8 +
-         (int64_t)n_tokens * ((hidden / 128 + 7) / 8) * 8;
+  return (int64_t)(hidden / 512) * (2 * inter / 128) * P8 + (int64_t)(hidden / 128) * P8 +
+         (fold ? 0 : (int64_t)n_tokens * ((hidden / 128 + 3) / 4) * 8);
+}
+
+hipError_t flow_groups_per_cu(int k_gu, int k_dn, int* n) {
+  const void* f = k_gu == 2 && k_dn == 3   ? (const void*)k_stack_flow<2, 3>
+                  : k_gu == 2 && k_dn == 2 ? (const void*)k_stack_flow<2, 2>
+                  : k_gu == 3 && k_dn == 3 ? (const void*)k_stack_flow<3, 3>
+                  : k_gu == 3 && k_dn == 2 ? (const void*)k_stack_flow<3, 2>
+                                           : nullptr;
+  if (!f) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, f, 64 * kWaves, 0);
 }
 
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s) {
   const int64_t blocks =
-      flow_blocks_per_layer(a.hidden, a.inter, a.top_k, a.n_tokens) * a.n_layers + kFlowSpare;
-  const dim3 grid((unsigned)blocks), block(1024);
+      flow_blocks_per_layer(a.hidden, a.inter, a.top_k, a.n_tokens, a.fold != 0) * a.n_layers +
+      kFlowSpare;
+  const dim3 grid((unsigned)blocks), block(64 * kWaves);
   if (k_gu == 2 && k_dn == 3)
     hipLaunchKernelGGL((k_stack_flow<2, 3>), grid, block, 0, s, a);
   else if (k_gu == 2 && k_dn == 2)
