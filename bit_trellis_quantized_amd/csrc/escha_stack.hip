@@ -1,23 +1,25 @@
 // escha_stack.hip -- decode of a whole stack of MoE layers in one launch
 // (small batches: the token-by-token generation case).
 //
-// Every task of every layer is one work-group of 16 waves, and the tasks
-// are numbered in dependency order: layer by layer, first the layer's
-// gate_up tasks, then its down tasks, then its combine tasks.
-//   gate_up (pair p, quarter cq of the inputs = four 128-input chunks,
-//     256-output group g): the rotated inputs of the four chunks, the decode
-//     of their 32 tile-rows x 16 tiles (two per wave), the sum over the
-//     chunks and the output transform of that sum;
-//   down (p, output group g): h = SiLU(gate) * up over all the intermediate
-//     channels from gate_up's quarter sums, its rotation (one 128-block per
-//     wave of the first four), the decode of every tile-row of the group
-//     (two per wave), the sum over the channels and the output transform,
-//     weighted by the router probability: the pair's finished output for
-//     the group;
-//   combine (token t, XCD x, 1024-output half): the sum of the token's
-//     pair outputs and the sums of squares of the half's 128-blocks, which
-//     the next layer's gate_up tasks on XCD x read and turn into their
-//     RMS-normalised bf16 inputs (in the last layer: the output y).
+// Every task of every layer is one work-group of 8 waves (two work-groups
+// share a compute unit), and the tasks are numbered in dependency order:
+// layer by layer, first the layer's gate_up tasks, then its down tasks, then
+// (larger batches only) its combine tasks.
+//   gate_up (pair p, part hh = four 128-input chunks, 128-output block g):
+//     the rotated inputs of the four chunks, the decode of their 32
+//     tile-rows x 8 tiles (32 tiles per wave), the sum over the chunks and
+//     the output transform of that sum;
+//   down (p, 128-output block g): h = SiLU(gate) * up over all the
+//     intermediate channels from gate_up's part sums, its rotation (one
+//     128-block per chunk), the decode of every tile-row of the block, the
+//     sum over the channels and the output transform, weighted by the
+//     router probability: the pair's finished output for the block. For
+//     small batches the down task then also combines: it adds the block's
+//     outputs of all the token's pairs (its own included) once they carry
+//     this layer's tag, and stores the sum and its sum of squares for the
+//     next layer's gate_up tasks on its XCD;
+//   combine (token t, XCD x, four 128-output blocks; larger batches): the
+//     same sum for XCD x as a task of its own, once the down tasks flag.
 // The arithmetic per projection is the method's (rin, H_n, the decoded
 // weights with fp32 accumulation, H_n, rout); the summation order differs
 // from the layer-by-layer kernels (here each task sums over more inputs
@@ -30,7 +32,10 @@
 // (per XCD), and every wait is on a task with a smaller number, so the
 // smallest unfinished task can always run; the device holds as many later
 // work-groups as fit, and their decode overlaps the dependency chain of the
-// earlier ones. Every wait is bounded all the same (by the constant 100 MHz
+// earlier ones. The down tasks that combine also wait on down tasks of the
+// same layer with larger numbers: the host enables that only when all of
+// one layer's down tasks of one XCD fit on the XCD at once, which keeps
+// the argument. Every wait is bounded all the same (by the constant 100 MHz
 // clock): when one gives up it sets the error word, and every work-group
 // leaves at its next wait.
 //
@@ -53,7 +58,7 @@
 // Buffers written during the launch and read by other work-groups are
 // reused from layer to layer where the dependency chain makes that safe (a
 // task that overwrites one waits, directly or transitively, for every task
-// that reads the previous contents); the pair outputs, which the combine
+// that reads the previous contents); the pair outputs, which the combining
 // tasks of all XCDs read, alternate between two copies by layer parity.
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -207,10 +207,12 @@ ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_
 
 /*
  * The same stack in ONE kernel launch (plus a small kernel that clears the
- * launch's flag words first). Same arguments, same workspace size, and
- * results bit-identical to escha_moe_stack_decode: the per-task arithmetic
- * is shared. Every task of every layer (gate_up and down pieces of one
- * (token, expert) pair, and the per-token combine) is one work-group; a
+ * launch's flag words first). Same arguments and workspace size; the
+ * results agree with escha_moe_stack_decode to rounding, not bit for bit
+ * (each task sums over more inputs before its output transform, so the
+ * fp32 summation order differs; both follow the same arithmetic). Every
+ * task of every layer (gate_up and down pieces of one (token, expert) pair,
+ * and for larger batches the per-token combine) is one work-group; a
  * work-group loads and decodes its codes before it waits for the outputs
  * it reads, so code streaming and decode of later layers overlap the
  * dependency chain of earlier ones. The tasks of one pair run on one XCD of
