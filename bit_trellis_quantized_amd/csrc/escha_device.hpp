@@ -99,6 +99,18 @@ __device__ __forceinline__ uint32_t quarter_state_pair(const uint32_t* d) {
   }
 }
 
+// Packed states of weights (row kk, column n) and (row kk, column n + 8) of
+// a lane's stream piece d (offsets K*(16*kk + n) and that + 8*K).
+template <int K>
+__device__ __forceinline__ uint32_t row_state_pair(const uint32_t* d, int kk, int n) {
+  const int o = K * (16 * kk + n);
+  const uint32_t w0 = __builtin_amdgcn_alignbit(d[(o >> 5) + 1], d[o >> 5], o & 31);
+  if constexpr (K == 2) return w0;
+  const int o1 = o + 8;
+  const uint32_t w1 = __builtin_amdgcn_alignbit(d[(o1 >> 5) + 1], d[o1 >> 5], o1 & 31);
+  return __builtin_amdgcn_perm(w1, w0, 0x07060100u);
+}
+
 // Number of dwords a lane holds: its quarter (2K) plus the next quarter's
 // first dword (the wrap reaches at most 15 bits into it).
 template <int K>

@@ -9,23 +9,26 @@
 // decoded once and reused by several activation tiles). Activations enter
 // the contraction as fp16 (the decoded weights are exactly fp16).
 //
-// Layout in one work-group (8 waves):
-//  - waves 0-3 decode: lane = 4*tile + q, tile = 16*kt_local + nt_local: 64
+// Layout in one work-group (12 waves, three per SIMD):
+//  - waves 0-7 decode: lane = 8*tile + o, tile = 16*kt_local + nt_local: 64
 //    tiles (4 tile-rows x 16 output tiles) = one 64-input step for 256
-//    outputs, written to LDS one step ahead of the matrix waves;
+//    outputs, written to LDS one step ahead of the matrix waves; lane o of a
+//    tile's eight decodes input rows 2o and 2o+1 (32 weights), so every SIMD
+//    has two decoder waves to hide the decode's latencies;
 //  - LDS W fp16 in 16-byte k-chunks: element (row, k) of a step sits at
 //    halves ((k/8)*256 + pi(row))*8 + k%8, pi(row) = row ^ ((row>>4) & 15).
-//    A decode store (16 output tiles, rows 16 apart) then hits 16 distinct
-//    16-byte slots, and an MFMA operand read (32 consecutive rows) uses each
-//    slot exactly twice. Two buffers, one barrier per step;
+//    A decode store (a 4-byte row pair of one output column per lane) then
+//    spreads over all 32 banks, and an MFMA operand read (32 consecutive
+//    rows) uses each 16-byte slot exactly twice. Two buffers, one barrier
+//    per step;
 //  - the decoder waves also stage the step's activation tile (fp16,
 //    [k/8][token][8]) in LDS; codes and activations are issued two steps
 //    ahead of their use;
-//  - waves 4-7 run the matrix cores on the current step from LDS, so decode
+//  - waves 8-11 run the matrix cores on the current step from LDS, so decode
 //    (VALU) and contraction (MFMA) overlap on every SIMD;
-//  - wave (wo, wt) owns outputs 128wo..128wo+127 (four 32-row MFMA tiles)
-//    for tokens 64wt..64wt+63 (two 32-token MFMA tiles): 8 accumulators of
-//    16 fp32.
+//  - matrix wave (wo, wt) owns outputs 128wo..128wo+127 (four 32-row MFMA
+//    tiles) for tokens 64wt..64wt+63 (two 32-token MFMA tiles): 8
+//    accumulators of 16 fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,6 +40,8 @@ namespace escha {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+constexpr int kDecWaves = 8;     // decoder waves per work-group
+constexpr int kThreads = 64 * (kDecWaves + 4);  // + four matrix waves
 constexpr int kTM = 128;         // tokens per tile
 constexpr int kStep = 64;        // inputs per step (4 tile-rows)
 constexpr int kWBuf = 256 * kStep;  // halves per W buffer (32 KiB)
@@ -113,41 +118,55 @@ __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
 // and activations one step ahead.
 // out_tile(j) maps the local output tile j (0..15) to its global tile index.
 // ------------------------------------------------------------------------
+// A lane's eighth of a tile: stream bits 32K*o .. 32K*o + 32K - 1 (input
+// rows 2o and 2o+1), K dwords, plus the first dword of the next eighth (the
+// windows reach at most 15 bits into it).
 template <int K>
-__device__ __forceinline__ void decode_to_lds(const uint32_t (&raw)[Quarter<K>::kOwn], int dkt,
-                                              int dnt, int q, _Float16* wb) {
-  constexpr int kOwn = Quarter<K>::kOwn;
-  uint32_t d[kOwn + 1];
+__device__ __forceinline__ void load_eighth(const uint16_t* te, uint32_t (&d)[K]) {
+  if constexpr (K == 2) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(te));
+    d[0] = v.x;
+    d[1] = v.y;
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(te);
 #pragma unroll
-  for (int i = 0; i < kOwn; ++i) d[i] = raw[i];
-  d[kOwn] = next_quarter_dword(raw[0]);
-  uint32_t lo[8][2], hi[8][2];  // rows n and n+8: k pairs (0,1) and (2,3)
-  decode_quarter<K>(d, [&](int kk, int n, h16x2 w) {
-    const uint32_t bits = __builtin_bit_cast(uint32_t, w);
-    if (kk & 1) {
-      lo[n][kk >> 1] = __builtin_amdgcn_perm(bits, lo[n][kk >> 1], 0x05040100u);
-      hi[n][kk >> 1] = __builtin_amdgcn_perm(bits, hi[n][kk >> 1], 0x07060100u);
-    } else {
-      lo[n][kk >> 1] = bits;
-      hi[n][kk >> 1] = bits >> 16;
-    }
-  });
-  // rows 16*dnt + n and 16*dnt + n + 8, inputs 16*dkt + 4q .. +3 (one 8-byte half-chunk)
-  _Float16* chunk = wb + (2 * dkt + (q >> 1)) * (256 * 8) + 4 * (q & 1);
+    for (int i = 0; i < K; ++i) d[i] = __builtin_nontemporal_load(p + i);
+  }
+}
+
+// Decode the lane's 32 weights (input rows 2o, 2o+1 of tile (dkt, dnt) of
+// the step, all 16 output columns) and store them to the W buffer.
+template <int K>
+__device__ __forceinline__ void decode_to_lds(const uint32_t (&raw)[K], int dkt, int dnt, int o,
+                                              int lane, _Float16* wb) {
+  uint32_t d[K + 1];
+#pragma unroll
+  for (int i = 0; i < K; ++i) d[i] = raw[i];
+  // first dword of the next eighth of the same tile: lane 8t + (o+1) % 8
+  d[K] = (uint32_t)__builtin_amdgcn_ds_bpermute(((lane & ~7) | ((lane + 1) & 7)) << 2, (int)raw[0]);
+  uint32_t lo[8], hi[8];  // columns n and n+8: rows (2o, 2o+1)
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
-    *reinterpret_cast<uint2*>(chunk + (16 * dnt + (n ^ dnt)) * 8) = make_uint2(lo[n][0], lo[n][1]);
-    *reinterpret_cast<uint2*>(chunk + (16 * dnt + ((n + 8) ^ dnt)) * 8) =
-        make_uint2(hi[n][0], hi[n][1]);
+    const uint32_t w0 = __builtin_bit_cast(uint32_t, cba_decode_pair(row_state_pair<K>(d, 0, n)));
+    const uint32_t w1 = __builtin_bit_cast(uint32_t, cba_decode_pair(row_state_pair<K>(d, 1, n)));
+    lo[n] = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+    hi[n] = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+  }
+  // rows 16*dnt + n and 16*dnt + n + 8, inputs 16*dkt + 2o, +1 (one 4-byte pair)
+  _Float16* chunk = wb + (2 * dkt + (o >> 2)) * (256 * 8) + 2 * (o & 3);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    *reinterpret_cast<uint32_t*>(chunk + (16 * dnt + (n ^ dnt)) * 8) = lo[n];
+    *reinterpret_cast<uint32_t*>(chunk + (16 * dnt + ((n + 8) ^ dnt)) * 8) = hi[n];
   }
 }
 
 // One step's operands as held by a decoder lane between issue and use: its
-// quarter of one code tile and four 16-byte chunks of the activation tile.
+// eighth of one code tile and two 16-byte chunks of the activation tile.
 template <int K>
 struct StepLoads {
-  uint32_t raw[Quarter<K>::kOwn];
-  h8 x[4];
+  uint32_t raw[K];
+  h8 x[2];
 };
 
 // The matrix waves' part of every step: NT live 32-token sub-tiles (1 or 2)
@@ -207,31 +226,32 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform per wave
   const int lane = tid & 63;
-  const bool decoder = wave < 4;
+  const bool decoder = wave < kDecWaves;
   const int n_steps = in_f / kStep;
 
   if (decoder) {
-    // waves 0-3: codes and activations of step s+2 are issued at step s
+    // waves 0-7: codes and activations of step s+2 are issued at step s
     // (two steps of latency cover); at step s the lane decodes step s+1's
-    // quarter tile into W and copies its activation chunks into the X tile.
-    const int q = tid & 3;
-    const int dtile = tid >> 2;
+    // eighth of a tile into W and copies its activation chunks into the X
+    // tile.
+    const int o = tid & 7;
+    const int dtile = tid >> 3;
     const int dkt = dtile >> 4;  // tile-row inside the step
     const int dnt = dtile & 15;  // output tile inside the group
     const int gnt = out_tile(dnt);
     const int xtok = tid & 127;        // activation row of this lane
-    const int xkc0 = 4 * (tid >> 7);   // first of its four 16-byte k-chunks
+    const int xkc0 = 2 * (tid >> 7);   // first of its two 16-byte k-chunks
     const _Float16* xrow = X + (size_t)(row0 + (xtok < rows ? xtok : rows - 1)) * x_pitch + 8 * xkc0;
     auto issue = [&](int s, StepLoads<K>& L) {
-      load_quarter<K>(code_e + ((size_t)(4 * s + dkt) * n_nt + gnt) * (16 * K) + q * (4 * K), L.raw);
+      load_eighth<K>(code_e + ((size_t)(4 * s + dkt) * n_nt + gnt) * (16 * K) + o * (2 * K), L.raw);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) L.x[j] = *reinterpret_cast<const h8*>(xrow + s * kStep + 8 * j);
+      for (int j = 0; j < 2; ++j) L.x[j] = *reinterpret_cast<const h8*>(xrow + s * kStep + 8 * j);
     };
     auto consume = [&](int s, const StepLoads<K>& L) {
-      decode_to_lds<K>(L.raw, dkt, dnt, q, wl + (s & 1) * kWBuf);
+      decode_to_lds<K>(L.raw, dkt, dnt, o, lane, wl + (s & 1) * kWBuf);
       _Float16* xb = xl + (s & 1) * kXBuf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<h8*>(xb + ((xkc0 + j) * kTM + xtok) * 8) = L.x[j];
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<h8*>(xb + ((xkc0 + j) * kTM + xtok) * 8) = L.x[j];
     };
     StepLoads<K> ring[2];
     issue(0, ring[0]);
@@ -255,11 +275,11 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
       }
     }
   } else {
-    // waves 4-7: matrix cores on step s from LDS. (wo, wt): outputs
+    // waves 8-11: matrix cores on step s from LDS. (wo, wt): outputs
     // 128*wo + 32*mt, tokens 64*wt + 32*tt. Token sub-tiles without a real
     // token are skipped (uniform per wave); padded columns of a live
     // sub-tile hold a clamped row and are never stored.
-    const int mw = wave - 4;
+    const int mw = wave - kDecWaves;
     const int wo = mw >> 1, wt = mw & 1;
     const int live = 64 * wt + 32 < rows ? 2 : (64 * wt < rows ? 1 : 0);
     __syncthreads();
@@ -277,8 +297,8 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
 __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el, int h) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wave < 4) return;
-  const int wo = (wave - 4) >> 1, wt = (wave - 4) & 1;
+  if (wave < kDecWaves) return;
+  const int wo = (wave - kDecWaves) >> 1, wt = (wave - kDecWaves) & 1;
   if (wt != h) return;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
@@ -299,7 +319,7 @@ __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el,
 // for those channels and writes down's rotated fp16 input block c.
 // ------------------------------------------------------------------------
 template <int K>
-__global__ __launch_bounds__(512) void k_grouped_gate_up(GroupedArgs a) {
+__global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
   const int nb = a.inter / 128;
   const int c = blockIdx.x % nb;
   const int tile = blockIdx.x / nb;
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(512) void k_grouped_gate_up(GroupedArgs a) {
   for (int h = 0; h < 2; ++h) {  // token halves of the tile
     acc_to_lds(acc, el, h);
     __syncthreads();
-    for (int tl = 8 * wave; tl < 8 * wave + 8; ++tl) {
+    for (int tl = 8 * wave; tl < 8 * wave + 8 && wave < 8; ++tl) {  // waves 0-7: 8 tokens each
       const int tok = 64 * h + tl;
       if (tok >= rows) break;  // uniform over the wave
       const float* er = el + tl * kEPitch;
@@ -372,7 +392,7 @@ __global__ __launch_bounds__(512) void k_grouped_gate_up(GroupedArgs a) {
 // pair's 256 outputs (fp32) at its sorted index.
 // ------------------------------------------------------------------------
 template <int K>
-__global__ __launch_bounds__(512) void k_grouped_down(GroupedArgs a) {
+__global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
   const int ng = a.hidden / 256;
   const int r = blockIdx.x % ng;
   const int tile = blockIdx.x / ng;
@@ -405,7 +425,7 @@ __global__ __launch_bounds__(512) void k_grouped_down(GroupedArgs a) {
   for (int h = 0; h < 2; ++h) {
     acc_to_lds(acc, el, h);
     __syncthreads();
-    for (int tl = 8 * wave; tl < 8 * wave + 8; ++tl) {
+    for (int tl = 8 * wave; tl < 8 * wave + 8 && wave < 8; ++tl) {  // waves 0-7: 8 tokens each
       const int tok = 64 * h + tl;
       if (tok >= rows) break;
       const int i = row0 + tok;
@@ -469,18 +489,18 @@ hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s) {
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
   const unsigned grid = (unsigned)((size_t)max_tiles * (a.inter / 128));
   if (k_bits == 2)
-    hipLaunchKernelGGL(k_grouped_gate_up<2>, dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(k_grouped_gate_up<2>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_grouped_gate_up<3>, dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(k_grouped_gate_up<3>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
   const unsigned grid = (unsigned)((size_t)max_tiles * (a.hidden / 256));
   if (k_bits == 2)
-    hipLaunchKernelGGL(k_grouped_down<2>, dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(k_grouped_down<2>, dim3(grid), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(k_grouped_down<3>, dim3(grid), dim3(512), 0, s, a);
+    hipLaunchKernelGGL(k_grouped_down<3>, dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
