@@ -251,3 +251,37 @@ def test_flow_small_stack_edge_cases(escha):
         else:
             mx, frac = _bf16_steps(ch[l + 1], oracle.rmsnorm_bf16(ref))
             assert mx <= 1 and frac < 0.02, f"small stack layer {l}: {mx} steps on {frac:.3%}"
+
+
+@pytest.mark.parametrize("hidden,inter,k,T", [(1024, 256, 4, 5), (1024, 512, 6, 2), (2048, 256, 8, 3),
+                                              (1024, 256, 10, 2)])
+def test_flow_other_shapes(escha, hidden, inter, k, T):
+    """The one-launch kernel away from the benchmark's shapes: hidden 1024
+    (two gate_up input parts), inter 256 (two channel chunks), top_k 4 and 6
+    (the combine folded into the down tasks, fewer experts than XCDs) and 10
+    (combine tasks, two pairs of a token on one XCD); every layer against the
+    oracle."""
+    announce(f"one-launch stack, hidden={hidden} inter={inter} top_k={k} T={T}")
+    E, NLs = 16, 3
+    host = [synth.layer_tensors(21, l, n_experts=E, hidden=hidden, inter=inter) for l in range(NLs)]
+    layers = [layer_to_dev(L, top_k=k) for L in host]
+    st = escha.Stack(layers)
+    rs = np.random.default_rng(hidden + inter + k + T)
+    ids = np.stack([np.stack([rs.permutation(E)[:k] for _ in range(T)]) for _ in range(NLs)])
+    ids = ids.astype(np.int32)
+    w = rs.random((NLs, T, k)).astype(np.float32)
+    x0 = synth.activations(21, T, hidden, layer=3)
+    ws = torch.zeros(st.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    chain = torch.empty(NLs, T, hidden, dtype=torch.int16, device="cuda")
+    y = escha.escha_moe_stack_decode_persistent(st, to_dev(x0), to_dev(ids), to_dev(w), x_chain=chain,
+                                                workspace=ws)
+    assert escha.escha_moe_stack_status(ws) == 0
+    ch = u16(chain)
+    assert np.array_equal(ch[0], x0)
+    for l in range(NLs):
+        ref = oracle.moe_layer(host[l], ch[l], ids[l], w[l])
+        if l == NLs - 1:
+            assert_close(y.cpu().numpy(), ref, f"shapes {hidden}/{inter}/{k} layer {l} output")
+        else:
+            mx, frac = _bf16_steps(ch[l + 1], oracle.rmsnorm_bf16(ref))
+            assert mx <= 1 and frac < 0.02, f"layer {l}: {mx} steps on {frac:.3%}"
