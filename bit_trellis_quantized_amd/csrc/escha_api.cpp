@@ -175,11 +175,28 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
 }
 
 // ---------------------------------------------------------------- grouped ws
-constexpr int32_t kTileTokens = 128;  // tokens per grouped tile (escha_grouped.hip)
+// Decode calls (single layers and the layer-by-layer stack) with at least
+// this many tokens take the grouped path: pairs sorted by expert, each
+// weight tile decoded once for all of an expert's tokens in a tile.
+constexpr int32_t kGroupedDecodeTokens = 32;
+constexpr int32_t kTileTokens = 128;      // tokens per grouped tile (escha_grouped.hip)
+constexpr int32_t kSmallTileTokens = 16;  // tokens per small tile
 
-int32_t grouped_max_tiles(const escha_moe_layer_t* L, int64_t T) {
+// Decode calls whose experts get at most 16 tokens on average take the small
+// tiles (weights decoded straight into matrix-core operands); prefill calls
+// and larger batches take the 128-token tiles, which decode each expert's
+// weights once for up to 128 of its tokens.
+bool grouped_small(const escha_moe_layer_t* L, int64_t T, bool prefill) {
   const int64_t P = T * L->top_k;
-  return (int32_t)((P + kTileTokens - 1) / kTileTokens + L->gate_up.n_experts);
+  return !prefill && L->inter % 256 == 0 && L->hidden % 256 == 0 &&
+         P <= (int64_t)kSmallTileTokens * L->gate_up.n_experts;
+}
+
+// Tile-list capacity: enough for either tile size.
+int32_t grouped_max_tiles(const escha_moe_layer_t* L, int64_t T, bool small) {
+  const int64_t P = T * L->top_k;
+  const int64_t tm = small ? kSmallTileTokens : kTileTokens;
+  return (int32_t)((P + tm - 1) / tm + L->gate_up.n_experts);
 }
 
 struct GroupedWs {
@@ -195,7 +212,7 @@ struct GroupedWs {
 size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* out) {
   const int64_t P = T * L->top_k;
   const int E = L->gate_up.n_experts;
-  const int32_t mt = grouped_max_tiles(L, T);
+  const int32_t mt = grouped_max_tiles(L, T, true);
   const size_t chunks = ((size_t)P + 63) / 64;
   size_t off = 0;
   char* b = (char*)ws;
@@ -228,14 +245,16 @@ size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* ou
 // expert, contract on the matrix cores, combine in slot order.
 int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
                       const float* w, float* y, float* inter_out, const GroupedWs& g,
-                      hipStream_t s) {
+                      bool prefill, hipStream_t s) {
   const int P = T * L->top_k;
   const int E = L->gate_up.n_experts;
-  const int32_t max_tiles = grouped_max_tiles(L, T);
+  const bool small = grouped_small(L, T, prefill);
+  const int32_t max_tiles = grouped_max_tiles(L, T, small);
   hipError_t e = escha::launch_group(ids, P, E, g.counts, g.offsets, g.perm, g.inv, g.hist, g.base,
                                      g.rank, s);
   if (e != hipSuccess) return hip_fail(e, "group launch");
-  e = escha::launch_make_tiles(g.offsets, E, max_tiles, g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s);
+  e = escha::launch_make_tiles(g.offsets, E, small ? kSmallTileTokens : kTileTokens, max_tiles,
+                               g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
   escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
                        L->top_k, g.xg};
@@ -256,7 +275,8 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   gu.t_row0 = g.t_row0;
   gu.t_rows = g.t_rows;
   gu.n_tiles = g.n_tiles;
-  e = escha::launch_grouped_gate_up(gu, max_tiles, L->gate_up.k_bits, s);
+  e = small ? escha::launch_small_gate_up(gu, max_tiles, L->gate_up.k_bits, s)
+            : escha::launch_grouped_gate_up(gu, max_tiles, L->gate_up.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "grouped gate_up launch");
   escha::GroupedArgs dn = gu;
   dn.code = (const uint16_t*)L->down.code;
@@ -266,7 +286,8 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   dn.x_out = nullptr;
   dn.y_out = g.yd;
   dn.inter_out = nullptr;
-  e = escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
+  e = small ? escha::launch_small_down(dn, max_tiles, L->down.k_bits, s)
+            : escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "grouped down launch");
   escha::SortedCombineArgs c{g.yd, g.inv, L->hidden, L->top_k, T, y, nullptr};
   e = escha::launch_combine_sorted(c, s);
@@ -324,6 +345,28 @@ FlowLayout flow_layout(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) 
 
 size_t stack_ctl_bytes(const escha_moe_layer_t* L, int64_t n_layers, int64_t T) {
   return round_up((size_t)flow_layout(L, n_layers, T).ctl_ints * sizeof(int32_t));
+}
+
+// The layer with the most experts (the grouped workspace is sized for it).
+const escha_moe_layer_t* widest_layer(const escha_moe_layer_t* layers, int32_t n_layers) {
+  const escha_moe_layer_t* w = &layers[0];
+  for (int l = 1; l < n_layers; ++l)
+    if (layers[l].gate_up.n_experts > w->gate_up.n_experts) w = &layers[l];
+  return w;
+}
+
+// Buffers of the layer-by-layer stack path after the control block: the
+// streaming kernels' workspace, or (at least kGroupedDecodeTokens tokens)
+// the grouped kernels' plus two bf16 layer inputs; the fp32 layer output
+// follows.
+size_t stack_layered_bytes(const escha_moe_layer_t* layers, int32_t n_layers, int64_t T) {
+  size_t a = decode_ws_bytes(&layers[0], T);
+  if (T >= kGroupedDecodeTokens) {
+    const size_t g = grouped_ws(widest_layer(layers, n_layers), T, nullptr, nullptr) +
+                     2 * round_up((size_t)T * layers[0].hidden * sizeof(uint16_t));
+    if (g > a) a = g;
+  }
+  return a;
 }
 
 int check_stack_call(const escha_moe_layer_t* layers, int32_t n_layers, const uint16_t* x0_bf16,
@@ -460,11 +503,6 @@ int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_b
   return e == hipSuccess ? ESCHA_OK : hip_fail(e, "expert_gemv finish launch");
 }
 
-// Decode calls with at least this many tokens take the grouped path: pairs
-// sorted by expert, each tile decoded once for all of an expert's tokens
-// (at 64 tokens with Zipf-skewed routing, 252 us per layer against 408 us
-// for one decode per pair).
-constexpr int32_t kGroupedDecodeTokens = 32;
 
 size_t escha_moe_workspace_bytes(const escha_moe_layer_t* L, int32_t n_tokens, int32_t prefill) {
   if (!L || n_tokens < 0 || L->top_k < 1 || L->hidden < 128 || L->inter < 128) return 0;
@@ -485,7 +523,7 @@ int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, i
   if (n_tokens >= kGroupedDecodeTokens) {
     GroupedWs g;
     grouped_ws(L, n_tokens, workspace, &g);
-    return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g,
+    return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g, false,
                              (hipStream_t)stream);
   }
   const DecodeWs ws = decode_ws_carve(L, n_tokens, workspace);
@@ -506,7 +544,7 @@ int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, 
     return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   GroupedWs g;
   grouped_ws(L, n_tokens, workspace, &g);
-  return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g,
+  return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g, true,
                            (hipStream_t)stream);
 }
 
@@ -529,8 +567,8 @@ size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t 
   // the control block, then the layer-by-layer path's buffers, then the
   // one-launch path's
   const size_t ybuf = round_up((size_t)n_tokens * L->hidden * sizeof(float));
-  return stack_ctl_bytes(L, n_layers, n_tokens) + decode_ws_bytes(L, n_tokens) + ybuf +
-         flow_layout(L, n_layers, n_tokens).data_bytes;
+  return stack_ctl_bytes(L, n_layers, n_tokens) + stack_layered_bytes(layers, n_layers, n_tokens) +
+         ybuf + flow_layout(L, n_layers, n_tokens).data_bytes;
 }
 
 int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
@@ -544,8 +582,7 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
   const escha_moe_layer_t* L0 = &layers[0];
   const int H = L0->hidden, k = L0->top_k;
   char* b = (char*)workspace + stack_ctl_bytes(L0, n_layers, n_tokens);
-  const DecodeWs ws = decode_ws_carve(L0, n_tokens, b);
-  float* ytmp = (float*)(b + decode_ws_bytes(L0, n_tokens));
+  float* ytmp = (float*)(b + stack_layered_bytes(layers, n_layers, n_tokens));
   hipStream_t s = (hipStream_t)stream;
   const size_t xs = (size_t)n_tokens * H;
   if (x_chain) {
@@ -553,6 +590,33 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
         hipMemcpyAsync(x_chain, x0_bf16, xs * sizeof(uint16_t), hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return hip_fail(e, "x_chain copy");
   }
+  if (n_tokens >= kGroupedDecodeTokens) {
+    // grouped kernels per layer, the next layer's input by the RMSNorm kernel
+    GroupedWs g;
+    const size_t gb = grouped_ws(widest_layer(layers, n_layers), n_tokens, b, &g);
+    uint16_t* xbuf[2] = {(uint16_t*)(b + gb),
+                         (uint16_t*)(b + gb + round_up(xs * sizeof(uint16_t)))};
+    const uint16_t* x = x0_bf16;
+    for (int l = 0; l < n_layers; ++l) {
+      float* y = l == n_layers - 1 ? y_last : ytmp;
+      hipError_t e;
+      if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[2 * l], s)) != hipSuccess)
+        return hip_fail(e, "probe event record");
+      int rc = run_layer_grouped(&layers[l], x, n_tokens, topk_ids + (size_t)l * n_tokens * k,
+                                 topk_w + (size_t)l * n_tokens * k, y, nullptr, g, false, s);
+      if (rc) return rc;
+      if (l + 1 < n_layers) {
+        uint16_t* next = x_chain ? x_chain + (size_t)(l + 1) * xs : xbuf[l & 1];
+        e = escha::launch_rmsnorm_bf16(y, n_tokens, H, eps, next, s);
+        if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
+        x = next;
+      }
+      if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[2 * l + 1], s)) != hipSuccess)
+        return hip_fail(e, "probe event record");
+    }
+    return ESCHA_OK;
+  }
+  const DecodeWs ws = decode_ws_carve(L0, n_tokens, b);
   for (int l = 0; l < n_layers; ++l) {
     // layer 0 reads x0; layer l > 0 reads RMSNorm(y_{l-1}) from ytmp, which
     // its own combine then overwrites with y_l (stream order)
@@ -624,8 +688,8 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   hipStream_t s = (hipStream_t)stream;
   const FlowLayout f = flow_layout(L0, n_layers, T);
   int32_t* ctl = (int32_t*)workspace;
-  char* data = (char*)workspace + stack_ctl_bytes(L0, n_layers, T) + decode_ws_bytes(L0, T) +
-               round_up((size_t)T * H * sizeof(float));
+  char* data = (char*)workspace + stack_ctl_bytes(L0, n_layers, T) +
+               stack_layered_bytes(layers, n_layers, T) + round_up((size_t)T * H * sizeof(float));
 
   escha::FlowArgs a{};
   for (int l = 0; l < n_layers; ++l) {

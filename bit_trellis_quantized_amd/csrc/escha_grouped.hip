@@ -34,6 +34,7 @@
 
 #include "escha_device.hpp"
 #include "escha_launch.hpp"
+#include "escha_mfma.hpp"
 
 namespace escha {
 
@@ -50,11 +51,13 @@ constexpr int kSmemBytes = 2 * (kWBuf + kXBuf) * 2;  // 96 KiB; the epilogue reu
 constexpr int kEPitch = 257;     // LDS row pitch of the epilogue (floats)
 
 // ------------------------------------------------------------------------
-// Tile list: for every expert, ceil(count / 64) tiles of consecutive sorted
-// pairs. One block of 1024 threads; n_experts <= 1024.
+// Tile list: for every expert, ceil(count / tm) tiles of consecutive sorted
+// pairs (tm tokens each, the last one shorter). One block of 1024 threads;
+// n_experts <= 1024.
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__ offsets, int E,
-                                                     int max_tiles, int32_t* __restrict__ t_expert,
+                                                     int tm, int max_tiles,
+                                                     int32_t* __restrict__ t_expert,
                                                      int32_t* __restrict__ t_row0,
                                                      int32_t* __restrict__ t_rows,
                                                      int32_t* __restrict__ n_tiles) {
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
   int32_t cnt = 0, nt = 0;
   if (e < E) {
     cnt = offsets[e + 1] - offsets[e];
-    nt = (cnt + kTM - 1) / kTM;
+    nt = (cnt + tm - 1) / tm;
   }
   scan[e] = nt;
   __syncthreads();
@@ -78,8 +81,8 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
     const int32_t ti = base + i;
     if (ti < max_tiles) {
       t_expert[ti] = e;
-      t_row0[ti] = offsets[e] + i * kTM;
-      t_rows[ti] = cnt - i * kTM < kTM ? cnt - i * kTM : kTM;
+      t_row0[ti] = offsets[e] + i * tm;
+      t_rows[ti] = cnt - i * tm < tm ? cnt - i * tm : tm;
     }
   }
   if (e == 1023) *n_tiles = scan[1023] < max_tiles ? scan[1023] : max_tiles;
@@ -445,6 +448,175 @@ __global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
 }
 
 // ------------------------------------------------------------------------
+// Small tiles (decode calls with few tokens per expert): a tile holds at
+// most 16 pairs of one expert, and every wave decodes its share of the
+// expert's weights straight into the A operands of v_mfma_f32_16x16x32_f16
+// (no LDS copy of the weights, no barrier per step); B holds the tile's
+// fp16 activations, one column per token. Wave w takes output quad w % 4
+// (four 16-output tiles) and input half w / 4; the halves are added in LDS
+// (half 0 + half 1) before the epilogue. Work-group: 8 waves.
+// ------------------------------------------------------------------------
+constexpr int kSmallTM = 16;
+
+struct SmallLds {
+  uint32_t stage[8 * Stage<3>::kDw];  // each wave's staged codes
+  float red[2][kSmallTM][256];        // per input half: [token][output]
+};
+
+// The wave's partial sums over chunks c0 .. c0 + nch - 1 of the 16 output
+// columns nt0 .. nt0 + 3 (x: the token rows, row n of the tile at xr(n),
+// tokens >= rows contribute zero); lane (n, g) ends with outputs
+// 16j + 4g + q of tile j for token n in D[j][q].
+template <int K, class XRow>
+__device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code_e, int n_nt, int c0,
+                                               int nch, int nt0, XRow xr, int rows, uint32_t* stage,
+                                               int lane, f32x4 (&D)[4]) {
+  const int n = lane & 15;
+  const int gq = lane >> 4;
+  const bool live = n < rows;
+  const _Float16* xrow = xr(live ? n : 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 cv[Stage<K>::kPerLane];
+  stage_issue<K>(code_e, n_nt, 8 * c0, nt0, lane, cv);
+  for (int ch = 0; ch < nch; ++ch) {
+    const int c = c0 + ch;
+    stage_store<K>(stage, lane, cv);
+    if (ch + 1 < nch) stage_issue<K>(code_e, n_nt, 8 * (c + 1), nt0, lane, cv);  // during the decode
+    h16x8 A[4][4];
+    decode_stage_mfma<K>(stage, lane, A);
+    pin_operands(A);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      h16x8 B = h16x8{};
+      if (live) B = *reinterpret_cast<const h16x8*>(xrow + 128 * c + 32 * pp + 8 * gq);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B, D[j], 0, 0, 0);
+    }
+  }
+}
+
+// D of a wave (output quad nq, input half kh) -> sh.red[kh][token][output].
+__device__ __forceinline__ void small_to_lds(const f32x4 (&D)[4], SmallLds& sh, int kh, int nq,
+                                             int lane) {
+  const int n = lane & 15;
+  const int gq = lane >> 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<float4*>(&sh.red[kh][n][16 * (4 * nq + j) + 4 * gq]) =
+        make_float4(D[j][0], D[j][1], D[j][2], D[j][3]);
+}
+
+// gate_up, small tiles. grid.x = max_tiles * (inter / 128), block = 512.
+// A work-group takes gate block c and up block c (256 outputs, quads 0-1
+// and 2-3) of one tile; its epilogue is the big tile kernel's: h =
+// SiLU(gate) * up for the block's channels, then down's rotated input.
+template <int K>
+__global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
+  const int nb = a.inter / 128;
+  const int c = blockIdx.x % nb;
+  const int tile = blockIdx.x / nb;
+  if (tile >= *a.n_tiles) return;  // uniform
+  const int e = a.t_expert[tile];
+  const int row0 = a.t_row0[tile];
+  const int rows = a.t_rows[tile];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nq = wave & 3, kh = wave >> 2;
+  const int n_nt = 2 * a.inter / 16;
+  const int ncg = a.hidden / 128;
+  const int nt0 = nq < 2 ? 8 * c + 4 * nq : a.inter / 16 + 8 * c + 4 * (nq - 2);
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)ncg * 8 * n_nt * (16 * K);
+  __shared__ SmallLds sh;
+  const _Float16* X = reinterpret_cast<const _Float16*>(a.x_in);
+  f32x4 D[4];
+  small_mainloop<K>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
+                    [&](int r) { return X + (size_t)(row0 + r) * a.hidden; }, rows,
+                    sh.stage + wave * Stage<K>::kDw, lane, D);
+  small_to_lds(D, sh, kh, nq, lane);
+  __syncthreads();
+  const uint16_t* rg = a.rout + (size_t)e * (2 * a.inter) + 128 * c;
+  const uint16_t* ru = rg + a.inter;
+  const uint16_t* rd = a.rin2 + (size_t)e * a.inter + 128 * c;
+  const float rg0 = f16_to_f32(rg[lane]), rg1 = f16_to_f32(rg[lane + 64]);
+  const float ru0 = f16_to_f32(ru[lane]), ru1 = f16_to_f32(ru[lane + 64]);
+  const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
+  for (int tok = 2 * wave; tok < 2 * wave + 2; ++tok) {
+    if (tok >= rows) break;  // uniform over the wave
+    const float* r0 = sh.red[0][tok];
+    const float* r1 = sh.red[1][tok];
+    float g0 = r0[lane] + r1[lane], g1 = r0[lane + 64] + r1[lane + 64];
+    float u0 = r0[128 + lane] + r1[128 + lane], u1 = r0[192 + lane] + r1[192 + lane];
+    fwht128(g0, g1);
+    fwht128(u0, u1);
+    g0 *= kInvSqrt128 * rg0;
+    g1 *= kInvSqrt128 * rg1;
+    u0 *= kInvSqrt128 * ru0;
+    u1 *= kInvSqrt128 * ru1;
+    const float h0 = silu(g0) * u0;
+    const float h1 = silu(g1) * u1;
+    const int i = row0 + tok;
+    if (a.inter_out) {
+      float* io = a.inter_out + (size_t)a.perm[i] * a.inter + 128 * c;
+      io[lane] = h0;
+      io[lane + 64] = h1;
+    }
+    float v0 = h0 * rd0, v1 = h1 * rd1;
+    fwht128(v0, v1);
+    _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
+    xo[lane] = (_Float16)(v0 * kInvSqrt128);
+    xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+  }
+}
+
+// down, small tiles. grid.x = max_tiles * (hidden / 256), block = 512. The
+// epilogue applies H_n, rout and the pair's router weight and stores the
+// pair's 256 outputs (fp32) at its sorted index.
+template <int K>
+__global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
+  const int ng = a.hidden / 256;
+  const int r = blockIdx.x % ng;
+  const int tile = blockIdx.x / ng;
+  if (tile >= *a.n_tiles) return;  // uniform
+  const int e = a.t_expert[tile];
+  const int row0 = a.t_row0[tile];
+  const int rows = a.t_rows[tile];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int nq = wave & 3, kh = wave >> 2;
+  const int n_nt = a.hidden / 16;
+  const int ncd = a.inter / 128;
+  const uint16_t* code_e = a.code + (size_t)e * (size_t)ncd * 8 * n_nt * (16 * K);
+  __shared__ SmallLds sh;
+  const _Float16* X = reinterpret_cast<const _Float16*>(a.x_in);
+  f32x4 D[4];
+  small_mainloop<K>(code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq,
+                    [&](int rr) { return X + (size_t)(row0 + rr) * a.inter; }, rows,
+                    sh.stage + wave * Stage<K>::kDw, lane, D);
+  small_to_lds(D, sh, kh, nq, lane);
+  __syncthreads();
+  const uint16_t* ro = a.rout + (size_t)e * a.hidden + 256 * r;
+  const float r00 = f16_to_f32(ro[lane]), r01 = f16_to_f32(ro[lane + 64]);
+  const float r10 = f16_to_f32(ro[128 + lane]), r11 = f16_to_f32(ro[192 + lane]);
+  for (int tok = 2 * wave; tok < 2 * wave + 2; ++tok) {
+    if (tok >= rows) break;
+    const int i = row0 + tok;
+    const float wt = a.w[a.perm[i]];
+    const float* q0 = sh.red[0][tok];
+    const float* q1 = sh.red[1][tok];
+    float z0 = q0[lane] + q1[lane], z1 = q0[lane + 64] + q1[lane + 64];
+    float z2 = q0[128 + lane] + q1[128 + lane], z3 = q0[192 + lane] + q1[192 + lane];
+    fwht128(z0, z1);
+    fwht128(z2, z3);
+    float* yo = a.y_out + (size_t)i * a.hidden + 256 * r;
+    yo[lane] = z0 * kInvSqrt128 * r00 * wt;
+    yo[lane + 64] = z1 * kInvSqrt128 * r01 * wt;
+    yo[128 + lane] = z2 * kInvSqrt128 * r10 * wt;
+    yo[192 + lane] = z3 * kInvSqrt128 * r11 * wt;
+  }
+}
+
+// ------------------------------------------------------------------------
 // Combine from sorted rows: y[t] = sum over slots j (in order) of the row of
 // pair t*k+j (skipped if the pair has no row). grid.x = n_tokens *
 // (hidden / 128), block = 64.
@@ -474,9 +646,9 @@ __global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
 // ------------------------------------------------------------------------
 // Launchers.
 // ------------------------------------------------------------------------
-hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,
+hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tiles, int32_t* t_expert,
                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(k_make_tiles, dim3(1), dim3(1024), 0, s, offsets, E, max_tiles, t_expert,
+  hipLaunchKernelGGL(k_make_tiles, dim3(1), dim3(1024), 0, s, offsets, E, tm, max_tiles, t_expert,
                      t_row0, t_rows, n_tiles);
   return hipGetLastError();
 }
@@ -501,6 +673,24 @@ hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, 
     hipLaunchKernelGGL(k_grouped_down<2>, dim3(grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL(k_grouped_down<3>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)max_tiles * (a.inter / 128));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_small_gate_up<2>, dim3(grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_small_gate_up<3>, dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
+  const unsigned grid = (unsigned)((size_t)max_tiles * (a.hidden / 256));
+  if (k_bits == 2)
+    hipLaunchKernelGGL(k_small_down<2>, dim3(grid), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_small_down<3>, dim3(grid), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

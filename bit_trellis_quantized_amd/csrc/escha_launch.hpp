@@ -151,11 +151,15 @@ hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t 
 // Work-groups of the one-launch kernel that one compute unit holds at once.
 hipError_t flow_groups_per_cu(int k_gu, int k_dn, int* n);
 
-hipError_t launch_make_tiles(const int32_t* offsets, int E, int max_tiles, int32_t* t_expert,
+hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tiles, int32_t* t_expert,
                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s);
 hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s);
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
+// Small tiles (at most 16 tokens of one expert; inter and hidden multiples
+// of 256): weights decoded straight into matrix-core operands.
+hipError_t launch_small_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
+hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
 hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s);
 
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s);

@@ -149,6 +149,16 @@ __device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
   }
 }
 
+// Keep decoded operands where they are: an empty asm that claims to modify
+// each register, so the compiler neither sinks the decode past a later
+// point (a wait, the contraction) nor recomputes it there.
+__device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(A[pp][j]));
+}
+
 static __device__ __noinline__ float2 scale_block(float m);
 
 // Split a wave's 128 rotated activations (v0 at position lane, v1 at

@@ -207,14 +207,6 @@ __device__ __forceinline__ float silu_fast(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Keep decoded operands where they are (see pin_decoded).
-__device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(A[pp][j]));
-}
-
 struct Lds {
   uint32_t code[kWaves * Stage<3>::kDw];                   // each wave's staged codes
   _Float16 xh[kChunks][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per chunk

@@ -159,9 +159,13 @@ ESCHA_API int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uin
  * y fp32 [n_tokens][hidden]; inter_out (nullable) fp32
  * [n_tokens*top_k][inter] receives h per pair, in pair order t*top_k+j.
  * _decode streams every pair's expert weights for fewer than 32 tokens,
- * and from 32 tokens on runs the grouped kernels of _prefill;
+ * and from 32 tokens on groups the pairs by expert like _prefill: with at
+ * most 16 tokens per expert on average (and hidden, inter multiples of
+ * 256) in tiles of up to 16 tokens whose weights are decoded straight into
+ * matrix-core operands, otherwise in the 128-token tiles of _prefill;
  * _prefill groups the pairs by expert and decodes each weight tile once per
- * expert for all its tokens (long prompts). Both compute the same function.
+ * 128-token tile of an expert (long prompts). All compute the same function
+ * (summation orders differ: results agree to rounding).
  * escha_moe_workspace_bytes(L, n_tokens, prefill) sizes the workspace of
  * the call that will be made (prefill = 1 for _prefill, 0 for _decode).
  */
@@ -187,6 +191,9 @@ ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, fl
 /*
  * A stack of n_layers MoE layers applied in turn to n_tokens tokens:
  *   x_0 = x0_bf16; y_l = layer_l(x_l); x_{l+1} = rmsnorm_bf16(y_l).
+ * Each layer runs the kernels escha_moe_layer_decode would run for
+ * n_tokens tokens, and the normalisation is escha_rmsnorm_bf16's, so the
+ * result equals those calls chained, bit for bit.
  * `layers` is a HOST array of n_layers descriptors (their tensors are on
  * the device). topk_ids int32 / topk_w fp32 [n_layers][n_tokens][top_k];
  * y_last fp32 [n_tokens][hidden] = y_{n_layers-1}; x_chain (nullable) bf16
