@@ -71,8 +71,10 @@ def parse():
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=40)
     ap.add_argument("--pool", type=int, default=8, help="independent steps cycled")
-    ap.add_argument("--path", choices=["flow", "layered"], default="flow",
-                    help="stack: one launch for all layers (default) or three launches per layer")
+    ap.add_argument("--path", choices=["auto", "flow", "layered"], default="auto",
+                    help="stack: one launch for all layers (flow), the layer-by-layer path "
+                         "(layered: per-pair streaming below 32 tokens, grouped kernels from 32 "
+                         "on), or auto: flow below 32 tokens, layered from 32 on")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -298,7 +300,8 @@ def main():
     stack = escha.Stack(layers)
     hip = Hip()
 
-    one_launch = args.path == "flow"
+    path = args.path if args.path != "auto" else ("flow" if T < 32 else "layered")
+    one_launch = path == "flow"
     stack_fn = (escha.escha_moe_stack_decode_persistent if one_launch
                 else escha.escha_moe_stack_decode)
     n_probe = 2 if one_launch else 2 * NL
@@ -390,7 +393,10 @@ def main():
         launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
         achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
         kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
-                  "one layer's decode launches (k_in_partial + k_down_partial + k_combine)")
+                  "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
+                  if T < 32 else
+                  "one layer's grouped launches (grouping + k_small_gate_up + k_small_down + "
+                  "k_combine_sorted + RMSNorm)")
         roofline = {"kernel": kernel, "bound": "hbm",
                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -436,7 +442,7 @@ def main():
         "config": {"workload": f"expert stack streaming: {NL} layers x {E} experts, "
                                f"decode batch {T}, top-{k}, hidden {hidden}, inter 512, "
                                f"gate_up K=2 / down K=3, codes {NL * E * 917504 / 1e9:.2f} GB in HBM",
-                   "batch": T, "layers": NL, "graph": use_graph, "path": args.path},
+                   "batch": T, "layers": NL, "graph": use_graph, "path": path},
         "code_gbs_step": round(gbs, 1),
         "code_bytes_per_step": code_bytes_step,
         "wall_ms_per_step": round(t_wall / args.steps * 1e3, 4),
