@@ -208,12 +208,17 @@ struct GroupedWs {
   float* yd;     // fp32 [P][hidden]
 };
 
-// Carves the grouped workspace; with ws == nullptr only sizes it.
-size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* out) {
+// Carves the grouped workspace; with ws == nullptr only sizes it. The
+// grouping and tile-list arrays are held for n_layers layers (layer l's at
+// the offsets that launch_group and launch_make_tiles use for layer l);
+// the activation buffers once.
+size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* out,
+                  int n_layers = 1) {
   const int64_t P = T * L->top_k;
   const int E = L->gate_up.n_experts;
   const int32_t mt = grouped_max_tiles(L, T, true);
   const size_t chunks = ((size_t)P + 63) / 64;
+  const size_t nl = (size_t)n_layers;
   size_t off = 0;
   char* b = (char*)ws;
   auto take = [&](size_t bytes) {
@@ -222,17 +227,17 @@ size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* ou
     return p;
   };
   GroupedWs g{};
-  g.hist = (int32_t*)take(chunks * E * sizeof(int32_t));
-  g.base = (int32_t*)take(chunks * E * sizeof(int32_t));
-  g.rank = (int32_t*)take((size_t)P * sizeof(int32_t));
-  g.counts = (int32_t*)take((size_t)E * sizeof(int32_t));
-  g.offsets = (int32_t*)take((size_t)(E + 1) * sizeof(int32_t));
-  g.perm = (int32_t*)take((size_t)P * sizeof(int32_t));
-  g.inv = (int32_t*)take((size_t)P * sizeof(int32_t));
-  g.t_expert = (int32_t*)take((size_t)mt * sizeof(int32_t));
-  g.t_row0 = (int32_t*)take((size_t)mt * sizeof(int32_t));
-  g.t_rows = (int32_t*)take((size_t)mt * sizeof(int32_t));
-  g.n_tiles = (int32_t*)take(sizeof(int32_t));
+  g.hist = (int32_t*)take(nl * chunks * E * sizeof(int32_t));
+  g.base = (int32_t*)take(nl * chunks * E * sizeof(int32_t));
+  g.rank = (int32_t*)take(nl * (size_t)P * sizeof(int32_t));
+  g.counts = (int32_t*)take(nl * (size_t)E * sizeof(int32_t));
+  g.offsets = (int32_t*)take(nl * (size_t)(E + 1) * sizeof(int32_t));
+  g.perm = (int32_t*)take(nl * (size_t)P * sizeof(int32_t));
+  g.inv = (int32_t*)take(nl * (size_t)P * sizeof(int32_t));
+  g.t_expert = (int32_t*)take(nl * (size_t)mt * sizeof(int32_t));
+  g.t_row0 = (int32_t*)take(nl * (size_t)mt * sizeof(int32_t));
+  g.t_rows = (int32_t*)take(nl * (size_t)mt * sizeof(int32_t));
+  g.n_tiles = (int32_t*)take(nl * sizeof(int32_t));
   g.xg = (uint16_t*)take((size_t)P * L->hidden * sizeof(uint16_t));
   g.xd = (uint16_t*)take((size_t)P * L->inter * sizeof(uint16_t));
   g.yd = (float*)take((size_t)P * L->hidden * sizeof(float));
@@ -240,22 +245,63 @@ size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* ou
   return off;
 }
 
-// One layer over T tokens through the grouped kernels: group the pairs by
-// expert, decode every weight tile once per tile of <= 64 tokens of its
-// expert, contract on the matrix cores, combine in slot order.
-int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
-                      const float* w, float* y, float* inter_out, const GroupedWs& g,
-                      bool prefill, hipStream_t s) {
+// Layer l's grouping and tile-list arrays of a workspace carved for
+// several layers.
+GroupedWs grouped_layer(const GroupedWs& g, const escha_moe_layer_t* L, int64_t T, int l) {
+  const int64_t P = T * L->top_k;
+  const int E = L->gate_up.n_experts;
+  const size_t chunks = ((size_t)P + 63) / 64;
+  const int32_t mt = grouped_max_tiles(L, T, true);
+  GroupedWs v = g;
+  v.hist += (size_t)l * chunks * E;
+  v.base += (size_t)l * chunks * E;
+  v.rank += (size_t)l * P;
+  v.counts += (size_t)l * E;
+  v.offsets += (size_t)l * (E + 1);
+  v.perm += (size_t)l * P;
+  v.inv += (size_t)l * P;
+  v.t_expert += (size_t)l * mt;
+  v.t_row0 += (size_t)l * mt;
+  v.t_rows += (size_t)l * mt;
+  v.n_tiles += l;
+  return v;
+}
+
+// The grouping and tile lists of n_layers layers (ids [n_layers][T][top_k])
+// into a workspace carved for n_layers layers.
+int group_layers(const escha_moe_layer_t* L, int T, const int32_t* ids, const GroupedWs& g,
+                 bool prefill, int n_layers, hipStream_t s) {
   const int P = T * L->top_k;
   const int E = L->gate_up.n_experts;
   const bool small = grouped_small(L, T, prefill);
-  const int32_t max_tiles = grouped_max_tiles(L, T, small);
   hipError_t e = escha::launch_group(ids, P, E, g.counts, g.offsets, g.perm, g.inv, g.hist, g.base,
-                                     g.rank, s);
+                                     g.rank, s, n_layers);
   if (e != hipSuccess) return hip_fail(e, "group launch");
-  e = escha::launch_make_tiles(g.offsets, E, small ? kSmallTileTokens : kTileTokens, max_tiles,
-                               g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s);
+  e = escha::launch_make_tiles(g.offsets, E, small ? kSmallTileTokens : kTileTokens,
+                               grouped_max_tiles(L, T, true), g.t_expert, g.t_row0, g.t_rows,
+                               g.n_tiles, s, n_layers);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
+  return ESCHA_OK;
+}
+
+// One layer over T tokens through the grouped kernels: group the pairs by
+// expert (unless `grouped`: g then already holds this layer's grouping),
+// decode every weight tile once per tile of its expert's tokens, contract
+// on the matrix cores, combine in slot order.
+int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
+                      const float* w, float* y, float* inter_out, const GroupedWs& g,
+                      bool prefill, hipStream_t s, bool grouped = false) {
+  const int P = T * L->top_k;
+  const int E = L->gate_up.n_experts;
+  const bool small = grouped_small(L, T, prefill);
+  // grid bound: the tile count for this tile size never exceeds it (the
+  // tile lists themselves are laid out for the small-tile bound)
+  const int32_t max_tiles = grouped_max_tiles(L, T, small);
+  hipError_t e;
+  if (!grouped) {
+    const int rc = group_layers(L, T, ids, g, prefill, 1, s);
+    if (rc) return rc;
+  }
   escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
                        L->top_k, g.xg};
   e = escha::launch_xin_gather(ga, P, s);
@@ -362,7 +408,7 @@ const escha_moe_layer_t* widest_layer(const escha_moe_layer_t* layers, int32_t n
 size_t stack_layered_bytes(const escha_moe_layer_t* layers, int32_t n_layers, int64_t T) {
   size_t a = decode_ws_bytes(&layers[0], T);
   if (T >= kGroupedDecodeTokens) {
-    const size_t g = grouped_ws(widest_layer(layers, n_layers), T, nullptr, nullptr) +
+    const size_t g = grouped_ws(widest_layer(layers, n_layers), T, nullptr, nullptr, n_layers) +
                      2 * round_up((size_t)T * layers[0].hidden * sizeof(uint16_t));
     if (g > a) a = g;
   }
@@ -591,19 +637,29 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
     if (e != hipSuccess) return hip_fail(e, "x_chain copy");
   }
   if (n_tokens >= kGroupedDecodeTokens) {
-    // grouped kernels per layer, the next layer's input by the RMSNorm kernel
+    // grouped kernels per layer, the next layer's input by the RMSNorm
+    // kernel; when every layer has the same number of experts, the pairs
+    // of all layers are grouped up front (the routing is known for all)
     GroupedWs g;
-    const size_t gb = grouped_ws(widest_layer(layers, n_layers), n_tokens, b, &g);
+    const escha_moe_layer_t* Lw = widest_layer(layers, n_layers);
+    const size_t gb = grouped_ws(Lw, n_tokens, b, &g, n_layers);
     uint16_t* xbuf[2] = {(uint16_t*)(b + gb),
                          (uint16_t*)(b + gb + round_up(xs * sizeof(uint16_t)))};
+    bool same_e = true;
+    for (int l = 1; l < n_layers; ++l) same_e &= layers[l].gate_up.n_experts == L0->gate_up.n_experts;
+    if (same_e) {
+      const int rc = group_layers(L0, n_tokens, topk_ids, g, false, n_layers, s);
+      if (rc) return rc;
+    }
     const uint16_t* x = x0_bf16;
     for (int l = 0; l < n_layers; ++l) {
       float* y = l == n_layers - 1 ? y_last : ytmp;
       hipError_t e;
       if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[2 * l], s)) != hipSuccess)
         return hip_fail(e, "probe event record");
+      const GroupedWs gl = same_e ? grouped_layer(g, Lw, n_tokens, l) : g;
       int rc = run_layer_grouped(&layers[l], x, n_tokens, topk_ids + (size_t)l * n_tokens * k,
-                                 topk_w + (size_t)l * n_tokens * k, y, nullptr, g, false, s);
+                                 topk_w + (size_t)l * n_tokens * k, y, nullptr, gl, false, s, same_e);
       if (rc) return rc;
       if (l + 1 < n_layers) {
         uint16_t* next = x_chain ? x_chain + (size_t)(l + 1) * xs : xbuf[l & 1];

@@ -63,6 +63,12 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
                                                      int32_t* __restrict__ n_tiles) {
   __shared__ int32_t scan[1024];
   const int e = threadIdx.x;
+  const size_t ly = blockIdx.y;  // layer of a batch of tile lists
+  offsets += ly * (E + 1);
+  t_expert += ly * max_tiles;
+  t_row0 += ly * max_tiles;
+  t_rows += ly * max_tiles;
+  n_tiles += ly;
   int32_t cnt = 0, nt = 0;
   if (e < E) {
     cnt = offsets[e + 1] - offsets[e];
@@ -647,9 +653,10 @@ __global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
 // Launchers.
 // ------------------------------------------------------------------------
 hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tiles, int32_t* t_expert,
-                             int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s) {
-  hipLaunchKernelGGL(k_make_tiles, dim3(1), dim3(1024), 0, s, offsets, E, tm, max_tiles, t_expert,
-                     t_row0, t_rows, n_tiles);
+                             int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s,
+                             int n_layers) {
+  hipLaunchKernelGGL(k_make_tiles, dim3(1, (unsigned)n_layers), dim3(1024), 0, s, offsets, E, tm,
+                     max_tiles, t_expert, t_row0, t_rows, n_tiles);
   return hipGetLastError();
 }
 

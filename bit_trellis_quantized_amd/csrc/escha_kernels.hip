@@ -409,6 +409,11 @@ __global__ __launch_bounds__(64) void k_group_count(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ rank) {
   const int chunk = blockIdx.x;
   const int lane = threadIdx.x;
+  // layer blockIdx.y of a batch of groupings (gridDim.x = chunks per layer)
+  const size_t ly = blockIdx.y;
+  ids += ly * P;
+  hist += ly * gridDim.x * E;
+  rank += ly * P;
   const int i = chunk * 64 + lane;
   const int e = i < P ? ids[i] : -1;
   const bool valid = e >= 0 && e < E;
@@ -437,6 +442,10 @@ __global__ __launch_bounds__(256) void k_group_scan(const int32_t* __restrict__ 
   __shared__ int32_t part[256];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
+  const size_t ly = blockIdx.y;  // layer of a batch of groupings
+  hist += ly * n_chunks * E;
+  base += ly * n_chunks * E;
+  counts += ly * E;
   // each thread owns a contiguous run of chunks
   const int per = (n_chunks + 255) / 256;
   const int c0 = tid * per;
@@ -463,6 +472,9 @@ __global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restric
                                                         int32_t* __restrict__ offsets) {
   __shared__ int32_t scan[1024];
   const int e = threadIdx.x;
+  const size_t ly = blockIdx.y;  // layer of a batch of groupings
+  counts += ly * E;
+  offsets += ly * (E + 1);
   const int32_t v0 = e < E ? counts[e] : 0;
   scan[e] = v0;
   __syncthreads();
@@ -482,6 +494,13 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
                                                       const int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm,
                                                       int32_t* __restrict__ inv) {
+  const size_t ly = blockIdx.y;  // layer of a batch of groupings
+  ids += ly * P;
+  base += ly * gridDim.x * E;
+  rank += ly * P;
+  offsets += ly * (E + 1);
+  perm += ly * P;
+  if (inv) inv += ly * P;
   const int i = blockIdx.x * 64 + threadIdx.x;
   if (i >= P) return;
   const int e = ids[i];
@@ -577,20 +596,21 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                         int32_t* perm, int32_t* inv, int32_t* hist, int32_t* base, int32_t* rank,
-                        hipStream_t s) {
+                        hipStream_t s, int n_layers) {
   const int n_chunks = (P + 63) / 64;
+  const unsigned L = (unsigned)n_layers;
   if (n_chunks > 0) {
-    hipLaunchKernelGGL(k_group_count, dim3(n_chunks), dim3(64), 0, s, ids, P, E, hist, rank);
+    hipLaunchKernelGGL(k_group_count, dim3(n_chunks, L), dim3(64), 0, s, ids, P, E, hist, rank);
     hipError_t err = last_launch();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(k_group_scan, dim3(E), dim3(256), 0, s, hist, n_chunks, E, base, counts);
+  hipLaunchKernelGGL(k_group_scan, dim3(E, L), dim3(256), 0, s, hist, n_chunks, E, base, counts);
   hipError_t err = last_launch();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_group_offsets, dim3(1), dim3(1024), 0, s, counts, E, offsets);
+  hipLaunchKernelGGL(k_group_offsets, dim3(1, L), dim3(1024), 0, s, counts, E, offsets);
   err = last_launch();
   if (err != hipSuccess || n_chunks == 0) return err;
-  hipLaunchKernelGGL(k_group_scatter, dim3(n_chunks), dim3(64), 0, s, ids, P, E, base, rank,
+  hipLaunchKernelGGL(k_group_scatter, dim3(n_chunks, L), dim3(64), 0, s, ids, P, E, base, rank,
                      offsets, perm, inv);
   return last_launch();
 }

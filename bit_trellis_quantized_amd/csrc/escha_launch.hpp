@@ -151,8 +151,11 @@ hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t 
 // Work-groups of the one-launch kernel that one compute unit holds at once.
 hipError_t flow_groups_per_cu(int k_gu, int k_dn, int* n);
 
+// n_layers tile lists at once (layer l: offsets + l (E + 1), t_* + l max_tiles,
+// n_tiles + l).
 hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tiles, int32_t* t_expert,
-                             int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s);
+                             int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s,
+                             int n_layers = 1);
 hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s);
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
@@ -174,8 +177,10 @@ hipError_t launch_hadamard128(const float* x, int64_t rows, int n, float* y, hip
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
 // inv (nullable): pair -> sorted index, -1 for a pair with an out-of-range id
+// n_layers groupings at once: layer l reads ids + l P and uses counts + l E,
+// offsets + l (E + 1), perm / inv / rank + l P, hist / base + l chunks E.
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                         int32_t* perm, int32_t* inv, int32_t* hist, int32_t* base, int32_t* rank,
-                        hipStream_t s);
+                        hipStream_t s, int n_layers = 1);
 
 }  // namespace escha
