@@ -470,8 +470,8 @@ struct SmallLds {
 };
 
 // The wave's partial sums over chunks c0 .. c0 + nch - 1 of the 16 output
-// columns nt0 .. nt0 + 3 (x: the token rows, row n of the tile at xr(n),
-// tokens >= rows contribute zero); lane (n, g) ends with outputs
+// columns nt0 .. nt0 + 3 (x: the token rows, row n of the tile at xr(n);
+// the columns of tokens >= rows are never stored); lane (n, g) ends with outputs
 // 16j + 4g + q of tile j for token n in D[j][q].
 template <int K, class XRow>
 __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code_e, int n_nt, int c0,
@@ -479,8 +479,9 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
                                                int lane, f32x4 (&D)[4]) {
   const int n = lane & 15;
   const int gq = lane >> 4;
-  const bool live = n < rows;
-  const _Float16* xrow = xr(live ? n : 0);
+  // a token column past the tile's rows reads row 0: its outputs (column n
+  // of D) are never stored
+  const _Float16* xrow = xr(n < rows ? n : 0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   u32x4 cv[Stage<K>::kPerLane];
@@ -488,17 +489,32 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
   for (int ch = 0; ch < nch; ++ch) {
     const int c = c0 + ch;
     stage_store<K>(stage, lane, cv);
-    if (ch + 1 < nch) stage_issue<K>(code_e, n_nt, 8 * (c + 1), nt0, lane, cv);  // during the decode
-    h16x8 A[4][4];
-    decode_stage_mfma<K>(stage, lane, A);
-    pin_operands(A);
+    // the chunk's activations, then the next chunk's codes (past the last
+    // chunk: this chunk's again, never used), all in flight during the
+    // decode; issued unconditionally, so that the wait before the MFMAs
+    // leaves the codes outstanding
+    h16x8 B[4];
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
-      h16x8 B = h16x8{};
-      if (live) B = *reinterpret_cast<const h16x8*>(xrow + 128 * c + 32 * pp + 8 * gq);
+    for (int pp = 0; pp < 4; ++pp)
+      B[pp] = *reinterpret_cast<const h16x8*>(xrow + 128 * c + 32 * pp + 8 * gq);
+    stage_issue<K>(code_e, n_nt, 8 * (ch + 1 < nch ? c + 1 : c), nt0, lane, cv);
+    // tile-row pairs decoded one ahead of their MFMAs into two operand sets
+    // (32 VGPRs instead of 64): pair pp's MFMAs run on the matrix core while
+    // pair pp + 1 (then pp + 2, into pp's freed set) is decoded
+    const OperandDecoder<K> dec(stage, lane);
+    h16x8 A0[4], A1[4];
+    dec.template decode<0>(A0);
+    dec.template decode<1>(A1);
+    auto mfma4 = [&](const h16x8 (&A)[4], const h16x8& b) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B, D[j], 0, 0, 0);
-    }
+      for (int j = 0; j < 4; ++j) D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], b, D[j], 0, 0, 0);
+    };
+    mfma4(A0, B[0]);
+    dec.template decode<2>(A0);
+    mfma4(A1, B[1]);
+    dec.template decode<3>(A1);
+    mfma4(A0, B[2]);
+    mfma4(A1, B[3]);
   }
 }
 

@@ -61,10 +61,13 @@ __device__ __forceinline__ void stage_issue(const uint16_t* __restrict__ code_e,
   }
 }
 
-// LDS position (in tiles) of tile-row r, tile j of a wave's region: the odd
-// tile-rows after the even ones, so that the 16 tiles a lane decodes (rows
-// of one parity) are contiguous.
-__device__ __forceinline__ int stage_slot(int r, int j) { return (r & 1) * 16 + (r >> 1) * 4 + j; }
+// LDS position (in tiles) of tile-row r, tile j of a wave's region of NT
+// tiles per row: the odd tile-rows after the even ones, so that the 4 NT
+// tiles a lane decodes (rows of one parity) are contiguous.
+template <int NT = 4>
+__device__ __forceinline__ int stage_slot(int r, int j) {
+  return (r & 1) * (4 * NT) + (r >> 1) * NT + j;
+}
 
 // Store the loaded chunks to the wave's LDS region (tile (r, j) at dword
 // stage_slot(r, j) * kStride) with each tile's wrap dword; the wave can read
@@ -91,44 +94,51 @@ __device__ __forceinline__ void stage_store(uint32_t* lds, int lane,
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
-// Decode, for every pair pp of adjacent tile-rows (2pp, 2pp+1) and tile j of
-// the staged region, this lane's 8 weights into A[pp][j] (A-operand layout).
-template <int K>
-__device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
-                                                  h16x8 (&A)[4][4]) {
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  const int h = g & 1;
-  // tile of the pair: rows 2pp + (g >> 1); lane-dependent part of the
-  // window positions
-  const uint32_t* base = lds + stage_slot(g >> 1, 0) * Stage<K>::kStride;
-  int a0, a1;
+// Lane-dependent part of the operand decode of a staged region (NT tiles per
+// row, at stage_slot<NT>): the two window base addresses of each half of the
+// tile-row pairs and the two window shifts.
+template <int K, int NT = 4>
+struct OperandDecoder {
+  const uint32_t* base;
+  int a0, a1, a0h, a1h;
   uint32_t s0, s1;
-  if constexpr (K == 2) {
-    // window i at bit 256h + 32i + 2n: dword 8h + i, shift 2n
-    a0 = a1 = 8 * h;
-    s0 = s1 = 2 * n;
-  } else {
-    // window i at bit 384h + 48i + 3n; for i = 2m: dword 12h + 3m + (3n >> 5),
-    // shift 3n & 31; for i = 2m + 1: dword 12h + 3m + ((48 + 3n) >> 5),
-    // shift (16 + 3n) & 31
-    a0 = 12 * h + ((3 * n) >> 5);
-    a1 = 12 * h + ((48 + 3 * n) >> 5);
-    s0 = (3 * n) & 31;
-    s1 = (16 + 3 * n) & 31;
+
+  __device__ __forceinline__ OperandDecoder(const uint32_t* lds, int lane) {
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int h = g & 1;
+    // tile of the pair: rows 2pp + (g >> 1)
+    base = lds + stage_slot<NT>(g >> 1, 0) * Stage<K>::kStride;
+    if constexpr (K == 2) {
+      // window i at bit 256h + 32i + 2n: dword 8h + i, shift 2n
+      a0 = a1 = 8 * h;
+      s0 = s1 = 2 * n;
+    } else {
+      // window i at bit 384h + 48i + 3n; for i = 2m: dword 12h + 3m + (3n >> 5),
+      // shift 3n & 31; for i = 2m + 1: dword 12h + 3m + ((48 + 3n) >> 5),
+      // shift (16 + 3n) & 31
+      a0 = 12 * h + ((3 * n) >> 5);
+      a1 = 12 * h + ((48 + 3 * n) >> 5);
+      s0 = (3 * n) & 31;
+      s1 = (16 + 3 * n) & 31;
+    }
+    // the tiles of pairs 2 and 3 through second base addresses (opaque to
+    // the compiler, so that it keeps them instead of adding a constant
+    // before every read: LDS read offsets reach 255 dwords)
+    a0h = a0 + 2 * NT * Stage<K>::kStride;
+    a1h = a1 + 2 * NT * Stage<K>::kStride;
+    asm volatile("" : "+v"(a0h), "+v"(a1h));
   }
-  // the tiles of pairs 2 and 3 through second base addresses (opaque to the
-  // compiler, so that it keeps them instead of adding a constant before
-  // every read: LDS read offsets reach 255 dwords)
-  int a0h = a0 + 8 * Stage<K>::kStride, a1h = a1 + 8 * Stage<K>::kStride;
-  asm volatile("" : "+v"(a0h), "+v"(a1h));
+
+  // This lane's 8 weights of tile j of tile-row pair PP (rows 2PP, 2PP+1)
+  // in the A-operand layout, for every j.
+  template <int PP>
+  __device__ __forceinline__ void decode(h16x8 (&A)[NT]) const {
+    const uint32_t* p0 = base + (PP < 2 ? a0 : a0h);
+    const uint32_t* p1 = base + (PP < 2 ? a1 : a1h);
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) {
-    const uint32_t* p0 = base + (pp < 2 ? a0 : a0h);
-    const uint32_t* p1 = base + (pp < 2 ? a1 : a1h);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int toff = (stage_slot(2 * (pp & 1), j) - stage_slot(0, 0)) * Stage<K>::kStride;
+    for (int j = 0; j < NT; ++j) {
+      const int toff = (stage_slot<NT>(2 * (PP & 1), j) - stage_slot<NT>(0, 0)) * Stage<K>::kStride;
       uint32_t win[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -144,19 +154,33 @@ __device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
         a[i] = w.x;
         a[i + 1] = w.y;
       }
-      A[pp][j] = a;
+      A[j] = a;
     }
   }
+};
+
+// Decode, for every pair pp of adjacent tile-rows (2pp, 2pp+1) and tile j of
+// the staged region (NT tiles per row, at stage_slot<NT>), this lane's 8
+// weights into A[pp][j] (A-operand layout).
+template <int K, int NT = 4>
+__device__ __forceinline__ void decode_stage_mfma(const uint32_t* lds, int lane,
+                                                  h16x8 (&A)[4][NT]) {
+  const OperandDecoder<K, NT> dec(lds, lane);
+  dec.template decode<0>(A[0]);
+  dec.template decode<1>(A[1]);
+  dec.template decode<2>(A[2]);
+  dec.template decode<3>(A[3]);
 }
 
 // Keep decoded operands where they are: an empty asm that claims to modify
 // each register, so the compiler neither sinks the decode past a later
 // point (a wait, the contraction) nor recomputes it there.
-__device__ __forceinline__ void pin_operands(h16x8 (&A)[4][4]) {
+template <int NT>
+__device__ __forceinline__ void pin_operands(h16x8 (&A)[4][NT]) {
 #pragma unroll
   for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(A[pp][j]));
+    for (int j = 0; j < NT; ++j) asm volatile("" : "+v"(A[pp][j]));
 }
 
 static __device__ __noinline__ float2 scale_block(float m);
