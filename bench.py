@@ -73,8 +73,8 @@ def parse():
     ap.add_argument("--pool", type=int, default=8, help="independent steps cycled")
     ap.add_argument("--path", choices=["auto", "flow", "layered"], default="auto",
                     help="stack: one launch for all layers (flow), the layer-by-layer path "
-                         "(layered: per-pair streaming below 32 tokens, grouped kernels from 32 "
-                         "on), or auto: flow below 32 tokens, layered from 32 on")
+                         "(layered: per-pair streaming below 16 tokens, grouped kernels from 16 "
+                         "on), or auto: flow below 16 tokens, layered from 16 on")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -300,7 +300,7 @@ def main():
     stack = escha.Stack(layers)
     hip = Hip()
 
-    path = args.path if args.path != "auto" else ("flow" if T < 32 else "layered")
+    path = args.path if args.path != "auto" else ("flow" if T < 16 else "layered")
     one_launch = path == "flow"
     stack_fn = (escha.escha_moe_stack_decode_persistent if one_launch
                 else escha.escha_moe_stack_decode)
@@ -394,7 +394,7 @@ def main():
         achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
         kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
                   "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
-                  if T < 32 else
+                  if T < 16 else
                   "one layer's grouped launches (grouping + k_small_gate_up + k_small_down + "
                   "k_combine_sorted + RMSNorm)")
         roofline = {"kernel": kernel, "bound": "hbm",

@@ -178,7 +178,7 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
 // Decode calls (single layers and the layer-by-layer stack) with at least
 // this many tokens take the grouped path: pairs sorted by expert, each
 // weight tile decoded once for all of an expert's tokens in a tile.
-constexpr int32_t kGroupedDecodeTokens = 32;
+constexpr int32_t kGroupedDecodeTokens = 16;
 constexpr int32_t kTileTokens = 128;      // tokens per grouped tile (escha_grouped.hip)
 constexpr int32_t kSmallTileTokens = 16;  // tokens per small tile
 

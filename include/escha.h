@@ -158,8 +158,8 @@ ESCHA_API int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uin
  * x bf16 [n_tokens][hidden]; topk_ids int32 / topk_w fp32 [n_tokens][top_k];
  * y fp32 [n_tokens][hidden]; inter_out (nullable) fp32
  * [n_tokens*top_k][inter] receives h per pair, in pair order t*top_k+j.
- * _decode streams every pair's expert weights for fewer than 32 tokens,
- * and from 32 tokens on groups the pairs by expert like _prefill: with at
+ * _decode streams every pair's expert weights for fewer than 16 tokens,
+ * and from 16 tokens on groups the pairs by expert like _prefill: with at
  * most 16 tokens per expert on average (and hidden, inter multiples of
  * 256) in tiles of up to 16 tokens whose weights are decoded straight into
  * matrix-core operands, otherwise in the 128-token tiles of _prefill;

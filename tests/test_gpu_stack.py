@@ -42,7 +42,7 @@ def _route(escha, logits):
     return ids.view(L, T, 8), w.view(L, T, 8)
 
 
-@pytest.mark.parametrize("T", [1, 8, 64])
+@pytest.mark.parametrize("T", [1, 8, 16, 64])
 def test_stack_equals_chained_layers(escha, stack, T):
     announce(f"stack vs chained single-layer calls, T={T}")
     x0, logits = synth.stack_token_inputs(SEED, NL, T, 0)
