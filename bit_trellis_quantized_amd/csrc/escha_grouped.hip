@@ -101,20 +101,46 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
 __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
   const int i = blockIdx.x;
   if (i >= a.offsets[a.n_experts]) return;
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
   const int p = a.perm[i];
   const int e = a.ids[p];
   const int t = p / a.top_k;
-  for (int b = wave; b < a.hidden / 128; b += 4) {
-    const uint16_t* xr = a.x_bf16 + (size_t)t * a.hidden + 128 * b;
-    const uint16_t* rr = a.rin + (size_t)e * a.hidden + 128 * b;
-    float v0 = bf16_to_f32(xr[lane]) * f16_to_f32(rr[lane]);
-    float v1 = bf16_to_f32(xr[lane + 64]) * f16_to_f32(rr[lane + 64]);
-    fwht128(v0, v1);
-    _Float16* xo = reinterpret_cast<_Float16*>(a.xg) + (size_t)i * a.hidden + 128 * b;
-    xo[lane] = (_Float16)(v0 * kInvSqrt128);
-    xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+  // 16 lanes per 128-input block, 8 consecutive inputs per lane (16-byte
+  // loads and stores). The butterflies run in fwht128's order (bit 6, then
+  // bits 0-5), so the rounded results are the same: bit 6 and bits 3-5
+  // across lanes, bits 0-2 inside the lane.
+  const int lane = threadIdx.x & 63;
+  const float s1 = lane_sign(lane, 1), s2 = lane_sign(lane, 2), s4 = lane_sign(lane, 4);
+  const float s8 = lane_sign(lane, 8);
+  for (int base = 8 * threadIdx.x; base < a.hidden; base += 8 * 256) {
+    const u32x4 xq = *reinterpret_cast<const u32x4*>(a.x_bf16 + (size_t)t * a.hidden + base);
+    const u32x4 rq = *reinterpret_cast<const u32x4*>(a.rin + (size_t)e * a.hidden + base);
+    float v[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_to_f32((uint16_t)(xq[q] & 0xFFFFu)) * f16_to_f32((uint16_t)(rq[q] & 0xFFFFu));
+      v[2 * q + 1] = bf16_to_f32((uint16_t)(xq[q] >> 16)) * f16_to_f32((uint16_t)(rq[q] >> 16));
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = butterfly<8>(v[q], s8);  // bit 6
+#pragma unroll
+    for (int h = 1; h <= 4; h <<= 1)  // bits 0-2
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (!(q & h)) {
+          const float lo = v[q], hi = v[q + h];
+          v[q] = lo + hi;
+          v[q + h] = lo - hi;
+        }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = butterfly<4>(butterfly<2>(butterfly<1>(v[q], s1), s2), s4);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const _Float16 lo = (_Float16)(v[2 * q] * kInvSqrt128);
+      const _Float16 hi = (_Float16)(v[2 * q + 1] * kInvSqrt128);
+      o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<u32x4*>(a.xg + (size_t)i * a.hidden + base) = o;
   }
 }
 

@@ -342,12 +342,13 @@ __global__ __launch_bounds__(64) void k_hadamard128(const float* x, int n, float
 }
 
 // ------------------------------------------------------------------------
-// Router: softmax + top-k per token. grid.x = n_tokens, block = 64.
+// Router: softmax + top-k per token. grid.x = n_tokens, block = 64; each
+// lane holds kMaxPer logits (E <= 64 kMaxPer).
 // ------------------------------------------------------------------------
+template <int kMaxPer>
 __global__ __launch_bounds__(64) void k_route_topk(const float* __restrict__ logits, int E, int k,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
-  constexpr int kMaxPer = 16;  // E <= 1024
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
   const float* l = logits + (size_t)t * E;
@@ -590,7 +591,12 @@ hipError_t launch_hadamard128(const float* x, int64_t rows, int n, float* y, hip
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s) {
-  hipLaunchKernelGGL(k_route_topk, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
+  if (E <= 256)
+    hipLaunchKernelGGL(k_route_topk<4>, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
+  else if (E <= 512)
+    hipLaunchKernelGGL(k_route_topk<8>, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
+  else
+    hipLaunchKernelGGL(k_route_topk<16>, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
   return last_launch();
 }
 
