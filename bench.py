@@ -3,8 +3,9 @@
 
 Workload: the full expert stack streaming from HBM -- 40 MoE layers x 256
 experts at the Qwen3.6-35B-A3B expert shapes (gate_up 2048->1024 at K=2,
-down 512->2048 at K=3, 9.40 GB of packed codes), decode at batch 1 (default)
-or 8. One step = one batch of tokens through every layer: router top-8 for
+down 512->2048 at K=3, 9.40 GB of packed codes), decode at batch 1 (default,
+the line's ``value``), then batches 8 and 64 on the same resident stack
+(``batches``). One step = one batch of tokens through every layer: router top-8 for
 all layers, then per layer gate_up -> SiLU*up -> down -> weighted combine ->
 RMSNorm -> bf16 input of the next layer. Inputs are seeded synthetic data
 (random code words, sign/scale vectors with prune masks, N(0,1) activations
@@ -39,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 # The one-launch kernel's measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE,
 # scaled by a plain copy's readings) and the hash of the sources it was taken
 # with; reported only while the sources still hash to that value.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "stack_decode_b1_flow_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "stack_decode_b1_flow_traffic.txt")
 KERNEL_SOURCES = ["escha_stack.hip", "escha_mfma.hpp", "escha_device.hpp", "escha_stream.hpp",
                   "escha_launch.hpp"]
 
@@ -75,6 +76,10 @@ def parse():
                     help="stack: one launch for all layers (flow), the layer-by-layer path "
                          "(layered: per-pair streaming below 16 tokens, grouped kernels from 16 "
                          "on), or auto: flow below 16 tokens, layered from 16 on")
+    ap.add_argument("--also-batches", default="8,64",
+                    help="stack: further decode batches timed after the main one on the same "
+                         "resident stack and reported under 'batches' (empty: none)")
+    ap.add_argument("--also-steps", type=int, default=20, help="timed steps of each further batch")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -293,117 +298,131 @@ def main():
     if args.workload == "layer":
         layer_workload(args, log)
         return
-    T, NL, R = args.batch, args.layers, args.pool
+    NL, R = args.layers, args.pool
     hidden, E, k = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K
 
     layers = build_stack(escha, synth, NL, log)
     stack = escha.Stack(layers)
     hip = Hip()
 
-    path = args.path if args.path != "auto" else ("flow" if T < 16 else "layered")
-    one_launch = path == "flow"
-    stack_fn = (escha.escha_moe_stack_decode_persistent if one_launch
-                else escha.escha_moe_stack_decode)
-    n_probe = 2 if one_launch else 2 * NL
+    def time_stack(T, steps, warmup):
+        """Time `steps` decode steps of batch T through the stack (after
+        `warmup` untimed ones); returns the measurements and the pool."""
+        path = args.path if args.path != "auto" else ("flow" if T < 16 else "layered")
+        one_launch = path == "flow"
+        stack_fn = (escha.escha_moe_stack_decode_persistent if one_launch
+                    else escha.escha_moe_stack_decode)
+        n_probe = 2 if one_launch else 2 * NL
 
-    # a pool of independent steps, each with its own buffers (so each can be
-    # captured in its own graph)
-    pool = []
-    for r in range(R):
-        x0, logits = synth.stack_token_inputs(SEED, NL, T, r)
-        pool.append(dict(
-            x0_host=x0, logits_host=logits,
-            x0=torch.from_numpy(x0.view(np.int16).copy()).cuda(),
-            logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
-            y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
-            ws=torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
-            probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
-        ))
+        # a pool of independent steps, each with its own buffers (so each can be
+        # captured in its own graph)
+        pool = []
+        for r in range(R):
+            x0, logits = synth.stack_token_inputs(SEED, NL, T, r)
+            pool.append(dict(
+                x0_host=x0, logits_host=logits,
+                x0=torch.from_numpy(x0.view(np.int16).copy()).cuda(),
+                logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
+                y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
+                ws=torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
+                probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
+            ))
 
-    def step(p):
-        ids, w = escha.escha_route_topk(p["logits"], k)
-        p["ids"], p["w"] = ids, w  # keep the graph's buffers alive
-        stack_fn(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
-                 out=p["y"], workspace=p["ws"], probe_events=p["probes"])
+        def step(p):
+            ids, w = escha.escha_route_topk(p["logits"], k)
+            p["ids"], p["w"] = ids, w  # keep the graph's buffers alive
+            stack_fn(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
+                     out=p["y"], workspace=p["ws"], probe_events=p["probes"])
 
-    use_graph = not args.no_graph
-    graphs = []
-    if use_graph:
-        try:
-            for p in pool:
-                step(p)  # warm the allocator outside capture
-            torch.cuda.synchronize()
-            for p in pool:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    step(p)
-                graphs.append(g)
-            torch.cuda.synchronize()
-        except Exception as exc:  # capture unsupported: measure eagerly
-            log(f"graph capture failed ({exc}); timing eager launches")
-            use_graph, graphs = False, []
-
-    def run(i):
+        use_graph = not args.no_graph
+        graphs = []
         if use_graph:
-            graphs[i % R].replay()
-        else:
-            step(pool[i % R])
+            try:
+                for p in pool:
+                    step(p)  # warm the allocator outside capture
+                torch.cuda.synchronize()
+                for p in pool:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        step(p)
+                    graphs.append(g)
+                torch.cuda.synchronize()
+            except Exception as exc:  # capture unsupported: measure eagerly
+                log(f"graph capture failed ({exc}); timing eager launches")
+                use_graph, graphs = False, []
 
-    for i in range(args.warmup):
-        run(i)
-    torch.cuda.synchronize()
-    start, stop = hip.event(), hip.event()
-    stream = torch.cuda.current_stream().cuda_stream
-    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    t_wall = time.perf_counter()
-    hip.lib.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream))
-    for i in range(args.steps):
-        run(i)
-    hip.lib.hipEventRecord(ctypes.c_void_p(stop), ctypes.c_void_p(stream))
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_total = hip.elapsed_ms(start, stop)
-    ms_per_step = ms_total / args.steps
+        def run(i):
+            if use_graph:
+                graphs[i % R].replay()
+            else:
+                step(pool[i % R])
 
-    # probe durations of each pool entry's last step: the one-launch kernel
-    # (one per step) or each layer's three launches
-    probe_ms = []
-    if not args.no_probe:
+        for i in range(warmup):
+            run(i)
+        torch.cuda.synchronize()
+        start, stop = hip.event(), hip.event()
+        stream = torch.cuda.current_stream().cuda_stream
+        hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        t_wall = time.perf_counter()
+        hip.lib.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream))
+        for i in range(steps):
+            run(i)
+        hip.lib.hipEventRecord(ctypes.c_void_p(stop), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        ms_total = hip.elapsed_ms(start, stop)
+        ms_per_step = ms_total / steps
+
+        # probe durations of each pool entry's last step: the one-launch kernel
+        # (one per step) or each layer's three launches
+        probe_ms = []
+        if not args.no_probe:
+            for p in pool:
+                if "ids" not in p:
+                    continue
+                for j in range(n_probe // 2):
+                    probe_ms.append(hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]))
+        probe_avg_ms = float(np.mean(probe_ms)) if probe_ms else None
+
+        # algorithmic bytes: the packed codes of the distinct experts each layer
+        # routes to (at batch 1 every one of the 8 is distinct), averaged over the pool
+        distinct = []
         for p in pool:
-            if "ids" not in p:
+            if "ids" not in p:  # a pool entry no step reached (fewer steps than entries)
                 continue
-            for j in range(n_probe // 2):
-                probe_ms.append(hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]))
-    probe_avg_ms = float(np.mean(probe_ms)) if probe_ms else None
+            ids = p["ids"].view(NL, T * k).cpu().numpy()
+            distinct.append(sum(len(set(row.tolist())) for row in ids))
+        code_bytes_step = int(np.mean(distinct) * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR))
+        tok_s = T / (ms_per_step / 1e3)
+        gbs = code_bytes_step / (ms_per_step / 1e3) / 1e9
 
-    # algorithmic bytes: the packed codes of the distinct experts each layer
-    # routes to (at batch 1 every one of the 8 is distinct), averaged over the pool
-    distinct = []
-    for p in pool:
-        if "ids" not in p:  # a pool entry no step reached (fewer steps than entries)
-            continue
-        ids = p["ids"].view(NL, T * k).cpu().numpy()
-        distinct.append(sum(len(set(row.tolist())) for row in ids))
-    code_bytes_step = int(np.mean(distinct) * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR))
-    tok_s = T / (ms_per_step / 1e3)
-    gbs = code_bytes_step / (ms_per_step / 1e3) / 1e9
+        roofline = None
+        if probe_avg_ms:
+            launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
+            achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
+            kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
+                      "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
+                      if T < 16 else
+                      "one layer's grouped launches (grouping + k_small_gate_up + k_small_down + "
+                      "k_combine_sorted + RMSNorm)")
+            roofline = {"kernel": kernel, "bound": "hbm",
+                        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic() if (one_launch and T == 1) else None,
+                        "bytes_per_launch": int(launch_bytes),
+                        "avg_launch_us": round(probe_avg_ms * 1e3, 3),
+                        "samples": len(probe_ms)}
 
-    roofline = None
-    if probe_avg_ms:
-        launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
-        achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
-        kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
-                  "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
-                  if T < 16 else
-                  "one layer's grouped launches (grouping + k_small_gate_up + k_small_down + "
-                  "k_combine_sorted + RMSNorm)")
-        roofline = {"kernel": kernel, "bound": "hbm",
-                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic() if (one_launch and T == 1) else None,
-                    "bytes_per_launch": int(launch_bytes),
-                    "avg_launch_us": round(probe_avg_ms * 1e3, 3),
-                    "samples": len(probe_ms)}
+        res = dict(T=T, path=path, one_launch=one_launch, use_graph=use_graph,
+                   ms_per_step=ms_per_step, tok_s=tok_s, gbs=gbs, t_wall=t_wall, steps=steps,
+                   code_bytes_step=code_bytes_step, roofline=roofline)
+        return res, pool
+
+    T = args.batch
+    main_res, pool = time_stack(T, args.steps, args.warmup)
+    path, one_launch, use_graph = main_res["path"], main_res["one_launch"], main_res["use_graph"]
+    ms_per_step, tok_s, gbs = main_res["ms_per_step"], main_res["tok_s"], main_res["gbs"]
+    t_wall, code_bytes_step, roofline = main_res["t_wall"], main_res["code_bytes_step"], main_res["roofline"]
 
     checks = {}
     if one_launch:  # every timed call completed (no wait gave up)
@@ -424,6 +443,26 @@ def main():
                "kind": "oracle",
                "sample": f"1 token through all {NL} layers (8 experts/layer, fp64 reconstruct-"
                          f"then-matmul); {t_cpu:.1f}s"}
+
+    # the metric's other batch sizes, on the same resident stack
+    batches = {}
+    del pool
+    for Tb in [int(v) for v in args.also_batches.split(",") if v.strip()]:
+        if Tb == T or Tb < 1:
+            continue
+        log(f"batch {Tb}: {args.also_steps} timed steps")
+        rb, pb = time_stack(Tb, args.also_steps, min(args.warmup, 3))
+        entry = {"value": round(rb["tok_s"], 2), "unit": "tokens/s",
+                 "ms_per_step": round(rb["ms_per_step"], 5), "steps": rb["steps"],
+                 "path": rb["path"], "graph": rb["use_graph"],
+                 "code_gbs_step": round(rb["gbs"], 1), "code_bytes_per_step": rb["code_bytes_step"],
+                 "roofline": rb["roofline"]}
+        if rb["one_launch"]:
+            entry["status"] = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pb))
+        batches[str(Tb)] = entry
+        del pb
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
     out = {
         "metric": "MoE-layer decode tokens/s at batch 1/8/64 + achieved HBM GB/s vs peak",
@@ -449,6 +488,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "checks": checks,
+        "batches": batches,
     }
     print(json.dumps(out), flush=True)
 
