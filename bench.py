@@ -35,6 +35,13 @@ SEED = 4  # the stack workload's seed
 GU_BYTES_PER_PAIR = 2048 // 16 * 1024 // 16 * 32 * 2   # 524,288
 DN_BYTES_PER_PAIR = 512 // 16 * 2048 // 16 * 48 * 2    # 393,216
 HBM_PEAK_GBS = 8000.0
+# VALU view of the same launches: decode costs 5.6 VALU lane-operations per
+# weight (721 VALU instructions per wave and 128 weights per lane in the
+# gfx950 ISA of the operand decoder); MI355X issues 256 CUs x 4 SIMDs x 16
+# lanes per clock at 2.4 GHz = 39.32 T lane-operations/s (non-packed).
+DECODE_OPS_PER_WEIGHT = 5.6
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+WEIGHTS_PER_PAIR = 2048 * 1024 + 512 * 2048  # 3,145,728
 
 
 # The one-launch kernel's measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE,
@@ -412,6 +419,12 @@ def main():
                         "bytes_per_launch": int(launch_bytes),
                         "avg_launch_us": round(probe_avg_ms * 1e3, 3),
                         "samples": len(probe_ms)}
+            decodes = launch_bytes / (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR) * WEIGHTS_PER_PAIR
+            valu = decodes * DECODE_OPS_PER_WEIGHT / (probe_avg_ms / 1e3) / 1e12
+            roofline["valu"] = {"bound": "alu", "achieved": round(valu, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                                "unit": "T lane-op/s", "frac": round(valu / VALU_PEAK_TOPS, 4),
+                                "decodes_per_launch": int(decodes),
+                                "ops_per_weight": DECODE_OPS_PER_WEIGHT}
 
         res = dict(T=T, path=path, one_launch=one_launch, use_graph=use_graph,
                    ms_per_step=ms_per_step, tok_s=tok_s, gbs=gbs, t_wall=t_wall, steps=steps,

@@ -288,9 +288,13 @@ int group_layers(const escha_moe_layer_t* L, int T, const int32_t* ids, const Gr
 // expert (unless `grouped`: g then already holds this layer's grouping),
 // decode every weight tile once per tile of its expert's tokens, contract
 // on the matrix cores, combine in slot order.
+// grouped: the pairs are already grouped (by an up-front call for all
+// layers); gather: rotate x into g.xg here (else it is already there);
+// combine: add the pair outputs into y here (else the caller does).
 int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
                       const float* w, float* y, float* inter_out, const GroupedWs& g,
-                      bool prefill, hipStream_t s, bool grouped = false) {
+                      bool prefill, hipStream_t s, bool grouped = false, bool gather = true,
+                      bool combine = true) {
   const int P = T * L->top_k;
   const int E = L->gate_up.n_experts;
   const bool small = grouped_small(L, T, prefill);
@@ -302,10 +306,12 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
     const int rc = group_layers(L, T, ids, g, prefill, 1, s);
     if (rc) return rc;
   }
-  escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
-                       L->top_k, g.xg};
-  e = escha::launch_xin_gather(ga, P, s);
-  if (e != hipSuccess) return hip_fail(e, "input gather launch");
+  if (gather) {
+    escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
+                         L->top_k, g.xg};
+    e = escha::launch_xin_gather(ga, P, s);
+    if (e != hipSuccess) return hip_fail(e, "input gather launch");
+  }
   escha::GroupedArgs gu{};
   gu.code = (const uint16_t*)L->gate_up.code;
   gu.rout = (const uint16_t*)L->gate_up.rout;
@@ -335,6 +341,7 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   e = small ? escha::launch_small_down(dn, max_tiles, L->down.k_bits, s)
             : escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "grouped down launch");
+  if (!combine) return ESCHA_OK;
   escha::SortedCombineArgs c{g.yd, g.inv, L->hidden, L->top_k, T, y, nullptr};
   e = escha::launch_combine_sorted(c, s);
   if (e != hipSuccess) return hip_fail(e, "sorted combine launch");
@@ -651,6 +658,9 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
       const int rc = group_layers(L0, n_tokens, topk_ids, g, false, n_layers, s);
       if (rc) return rc;
     }
+    // with the pairs grouped up front, one kernel per token links two
+    // layers: combine, RMSNorm and the next layer's input gather/rotation
+    const bool linked = same_e && H <= 2048;
     const uint16_t* x = x0_bf16;
     for (int l = 0; l < n_layers; ++l) {
       float* y = l == n_layers - 1 ? y_last : ytmp;
@@ -658,10 +668,29 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
       if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[2 * l], s)) != hipSuccess)
         return hip_fail(e, "probe event record");
       const GroupedWs gl = same_e ? grouped_layer(g, Lw, n_tokens, l) : g;
+      const bool link = linked && l + 1 < n_layers;
       int rc = run_layer_grouped(&layers[l], x, n_tokens, topk_ids + (size_t)l * n_tokens * k,
-                                 topk_w + (size_t)l * n_tokens * k, y, nullptr, gl, false, s, same_e);
+                                 topk_w + (size_t)l * n_tokens * k, y, nullptr, gl, false, s, same_e,
+                                 !linked || l == 0, !link);
       if (rc) return rc;
-      if (l + 1 < n_layers) {
+      if (link) {
+        const GroupedWs gn = grouped_layer(g, Lw, n_tokens, l + 1);
+        escha::CombineNextArgs cn{};
+        cn.rows = gl.yd;
+        cn.inv = gl.inv;
+        cn.hidden = H;
+        cn.top_k = k;
+        cn.n_tokens = n_tokens;
+        cn.y = y;
+        cn.eps = eps;
+        cn.x_out = x_chain ? x_chain + (size_t)(l + 1) * xs : nullptr;
+        cn.rin_next = (const uint16_t*)layers[l + 1].gate_up.rin;
+        cn.ids_next = topk_ids + (size_t)(l + 1) * n_tokens * k;
+        cn.inv_next = gn.inv;
+        cn.xg_next = gn.xg;
+        e = escha::launch_combine_next(cn, s);
+        if (e != hipSuccess) return hip_fail(e, "combine/RMSNorm/gather launch");
+      } else if (l + 1 < n_layers) {
         uint16_t* next = x_chain ? x_chain + (size_t)(l + 1) * xs : xbuf[l & 1];
         e = escha::launch_rmsnorm_bf16(y, n_tokens, H, eps, next, s);
         if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");

@@ -692,6 +692,64 @@ __global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
 }
 
 // ------------------------------------------------------------------------
+// Stack chain between two grouped layers, one work-group per token (wave b
+// = 128-input block b, hidden <= 2048): the slot-ordered combine of the
+// token's sorted pair outputs (as k_combine_sorted), the RMSNorm to bf16 (as
+// k_rmsnorm_bf16: per-block sums of squares over the wave, blocks added in
+// order), then, for each of the token's pairs in the next layer, that
+// pair's rotated fp16 input H_n(rin (.) x) at its sorted index (as
+// k_xin_gather). Each step keeps the arithmetic and order of the kernel it
+// replaces, so the chain's values are the same bits.
+// ------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
+  __shared__ float block_ss[16];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int b = threadIdx.x >> 6;
+  const int nb = a.hidden / 128;
+  const bool mine = b < nb;
+  float acc0 = 0.f, acc1 = 0.f;
+  if (mine) {
+    for (int j = 0; j < a.top_k; ++j) {
+      const int i = a.inv[t * a.top_k + j];
+      if (i < 0) continue;
+      const float* yr = a.rows + (size_t)i * a.hidden + 128 * b;
+      acc0 += yr[lane];
+      acc1 += yr[lane + 64];
+    }
+    float* y = a.y + (size_t)t * a.hidden + 128 * b;
+    y[lane] = acc0;
+    y[lane + 64] = acc1;
+    const float ss = wave_sum(__builtin_fmaf(acc0, acc0, acc1 * acc1));
+    if (lane == 0) block_ss[b] = ss;
+  }
+  __syncthreads();
+  if (!mine) return;
+  float tot = 0.f;
+  for (int q = 0; q < nb; ++q) tot += block_ss[q];
+  const float rs = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
+  const uint16_t x0 = f32_to_bf16_rne(acc0 * rs), x1 = f32_to_bf16_rne(acc1 * rs);
+  if (a.x_out) {
+    uint16_t* xr = a.x_out + (size_t)t * a.hidden + 128 * b;
+    xr[lane] = x0;
+    xr[lane + 64] = x1;
+  }
+  const float xf0 = bf16_to_f32(x0), xf1 = bf16_to_f32(x1);
+  for (int j = 0; j < a.top_k; ++j) {
+    const int i = a.inv_next[t * a.top_k + j];
+    if (i < 0) continue;  // uniform over the work-group
+    const int e = a.ids_next[t * a.top_k + j];
+    const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * b;
+    float v0 = xf0 * f16_to_f32(rr[lane]);
+    float v1 = xf1 * f16_to_f32(rr[lane + 64]);
+    fwht128(v0, v1);
+    _Float16* xo = reinterpret_cast<_Float16*>(a.xg_next) + (size_t)i * a.hidden + 128 * b;
+    xo[lane] = (_Float16)(v0 * kInvSqrt128);
+    xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+  }
+}
+
+// ------------------------------------------------------------------------
 // Launchers.
 // ------------------------------------------------------------------------
 hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tiles, int32_t* t_expert,
@@ -740,6 +798,11 @@ hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hi
     hipLaunchKernelGGL(k_small_down<2>, dim3(grid), dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL(k_small_down<3>, dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_next(const CombineNextArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_combine_next, dim3((unsigned)a.n_tokens), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

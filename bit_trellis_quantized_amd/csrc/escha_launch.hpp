@@ -95,6 +95,21 @@ struct GroupedArgs {
   const int32_t* n_tiles;
 };
 
+// Combine of a layer's sorted pair outputs fused with the RMSNorm of the
+// stack chain and the next layer's input gather/rotation (escha_grouped.hip).
+struct CombineNextArgs {
+  const float* rows;         // this layer's weighted pair outputs [P][hidden], sorted
+  const int32_t* inv;        // this layer: pair -> sorted index (-1: none)
+  int32_t hidden, top_k, n_tokens;
+  float* y;                  // fp32 [T][hidden]
+  float eps;
+  uint16_t* x_out;           // nullable: bf16 RMSNorm(y) [T][hidden]
+  const uint16_t* rin_next;  // next layer's gate_up rin [E][hidden]
+  const int32_t* ids_next;   // next layer's [T][top_k]
+  const int32_t* inv_next;   // next layer: pair -> sorted index
+  uint16_t* xg_next;         // next layer's fp16 rotated inputs [P][hidden], sorted
+};
+
 struct SortedCombineArgs {
   const float* rows;   // [P][hidden] at the sorted index
   const int32_t* inv;  // pair -> sorted index, -1 if the pair has none
@@ -164,6 +179,7 @@ hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, 
 hipError_t launch_small_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
 hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
 hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s);
+hipError_t launch_combine_next(const CombineNextArgs& a, hipStream_t s);
 
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s);
 hipError_t launch_down_partial(const DownPartialArgs& a, int k_bits, hipStream_t s);
