@@ -410,8 +410,9 @@ def main():
             kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
                       "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
                       if T < 16 else
-                      "one layer's grouped launches (grouping + k_small_gate_up + k_small_down + "
-                      "k_combine_sorted + RMSNorm)")
+                      "one layer's grouped launches (k_small_gate_up + k_small_down + "
+                      "k_combine_next: combine, RMSNorm and the next layer's input rotation; "
+                      "the pairs of all layers are grouped once per step)")
             roofline = {"kernel": kernel, "bound": "hbm",
                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4),
