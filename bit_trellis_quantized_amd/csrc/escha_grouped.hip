@@ -707,15 +707,32 @@ __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
   const int lane = threadIdx.x & 63;
   const int b = threadIdx.x >> 6;
   const int nb = a.hidden / 128;
+  const int k = a.top_k;
   const bool mine = b < nb;
+  const int32_t* __restrict__ inv = a.inv + (size_t)t * k;
+  const int32_t* __restrict__ inv_next = a.inv_next + (size_t)t * k;
+  const int32_t* __restrict__ ids_next = a.ids_next + (size_t)t * k;
+  // slots in groups of 8: every load of a group issued before its use (a
+  // slot without a row reads row 0 and adds nothing)
   float acc0 = 0.f, acc1 = 0.f;
   if (mine) {
-    for (int j = 0; j < a.top_k; ++j) {
-      const int i = a.inv[t * a.top_k + j];
-      if (i < 0) continue;
-      const float* yr = a.rows + (size_t)i * a.hidden + 128 * b;
-      acc0 += yr[lane];
-      acc1 += yr[lane + 64];
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float v0[8], v1[8];
+      bool ok[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = j0 + q < k ? inv[j0 + q] : -1;
+        ok[q] = i >= 0;
+        const float* yr = a.rows + (size_t)(ok[q] ? i : 0) * a.hidden + 128 * b;
+        v0[q] = yr[lane];
+        v1[q] = yr[lane + 64];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (ok[q]) {
+          acc0 += v0[q];
+          acc1 += v1[q];
+        }
     }
     float* y = a.y + (size_t)t * a.hidden + 128 * b;
     y[lane] = acc0;
@@ -735,17 +752,27 @@ __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
     xr[lane + 64] = x1;
   }
   const float xf0 = bf16_to_f32(x0), xf1 = bf16_to_f32(x1);
-  for (int j = 0; j < a.top_k; ++j) {
-    const int i = a.inv_next[t * a.top_k + j];
-    if (i < 0) continue;  // uniform over the work-group
-    const int e = a.ids_next[t * a.top_k + j];
-    const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * b;
-    float v0 = xf0 * f16_to_f32(rr[lane]);
-    float v1 = xf1 * f16_to_f32(rr[lane + 64]);
-    fwht128(v0, v1);
-    _Float16* xo = reinterpret_cast<_Float16*>(a.xg_next) + (size_t)i * a.hidden + 128 * b;
-    xo[lane] = (_Float16)(v0 * kInvSqrt128);
-    xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int dst[8];
+    uint16_t r0[8], r1[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      dst[q] = j0 + q < k ? inv_next[j0 + q] : -1;
+      const int e = dst[q] >= 0 ? ids_next[j0 + q] : 0;
+      const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * b;
+      r0[q] = rr[lane];
+      r1[q] = rr[lane + 64];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (dst[q] < 0) continue;  // uniform over the work-group
+      float v0 = xf0 * f16_to_f32(r0[q]);
+      float v1 = xf1 * f16_to_f32(r1[q]);
+      fwht128(v0, v1);
+      _Float16* xo = reinterpret_cast<_Float16*>(a.xg_next) + (size_t)dst[q] * a.hidden + 128 * b;
+      xo[lane] = (_Float16)(v0 * kInvSqrt128);
+      xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+    }
   }
 }
 
