@@ -1,8 +1,12 @@
 // escha_grouped.hip -- the grouped path: pairs sorted by expert, each weight
-// tile decoded once per tile of up to 64 tokens of the same expert (into
-// LDS, as fp16) and contracted on the matrix cores (v_mfma_f32_32x32x16_f16,
-// fp32 accumulate). Used by the prefill entry point and by decode calls
-// with enough tokens.
+// tile decoded once per tile of tokens of the same expert and contracted on
+// the matrix cores with fp32 accumulation. Used by the prefill entry point
+// and by decode calls with enough tokens. Kernels: the rotated-input gather;
+// the 128-token tile kernels below (weights decoded into LDS as fp16,
+// v_mfma_f32_32x32x16_f16); the small-tile kernels (<= 16 tokens, weights
+// decoded straight into v_mfma_f32_16x16x32_f16 operands); the sorted
+// combine, and the kernel that links two layers of the stack (combine,
+// RMSNorm, next layer's gather).
 //
 // Sources: hipfire PR "Escha-W2 port: 2-bit trellis decoded in the GEMV",
 // grouped-GEMM notes (expert_offsets + permutation; each weight tile
