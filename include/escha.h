@@ -191,9 +191,11 @@ ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, fl
 /*
  * A stack of n_layers MoE layers applied in turn to n_tokens tokens:
  *   x_0 = x0_bf16; y_l = layer_l(x_l); x_{l+1} = rmsnorm_bf16(y_l).
- * Each layer runs the kernels escha_moe_layer_decode would run for
- * n_tokens tokens, and the normalisation is escha_rmsnorm_bf16's, so the
- * result equals those calls chained, bit for bit.
+ * Each layer does what escha_moe_layer_decode does for n_tokens tokens,
+ * with the same arithmetic in the same order, and the normalisation is
+ * escha_rmsnorm_bf16's, so the result equals those calls chained, bit for
+ * bit (from 16 tokens on, one kernel per token links two layers: the
+ * combine, the normalisation and the next layer's input rotation).
  * `layers` is a HOST array of n_layers descriptors (their tensors are on
  * the device). topk_ids int32 / topk_w fp32 [n_layers][n_tokens][top_k];
  * y_last fp32 [n_tokens][hidden] = y_{n_layers-1}; x_chain (nullable) bf16
