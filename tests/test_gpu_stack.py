@@ -167,6 +167,37 @@ def test_flow_every_layer_vs_oracle_batch1(escha, stack):
                       range(NL), SEED, "T=1")
 
 
+def test_grouped_stack_graph_replay(escha, stack):
+    """Batch 64 through the layer-by-layer grouped path (the pairs of all
+    layers grouped up front, small-tile kernels, one kernel per token linking
+    two layers): every replay of a captured graph equals the eager call, with
+    eager work and synchronisation between replays."""
+    T = 64
+    announce(f"grouped stack: graph replays vs eager, T={T}")
+    x0, logits = synth.stack_token_inputs(SEED, NL, T, 7)
+    ids, w = _route(escha, logits)
+    x0d = to_dev(x0)
+    ws = torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    c1 = torch.empty(NL, T, synth.HIDDEN, dtype=torch.int16, device="cuda")
+    y1 = escha.escha_moe_stack_decode(stack, x0d, ids, w, x_chain=c1, workspace=ws)
+    torch.cuda.synchronize()
+    y = torch.empty_like(y1)
+    chain = torch.empty_like(c1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        escha.escha_moe_stack_decode(stack, x0d, ids, w, x_chain=chain, workspace=ws, out=y)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.zero_()
+        chain.zero_()
+        escha.escha_moe_stack_decode(stack, x0d, ids, w)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y1), f"replay {rep}: output differs"
+        assert torch.equal(chain, c1), f"replay {rep}: layer inputs differ"
+
+
 @pytest.mark.parametrize("T", [8, 64])
 def test_flow_sampled_vs_oracle(escha, stack, T):
     """Larger batches: two sampled tokens on a spread of layers (tokens are
