@@ -352,7 +352,25 @@ __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el,
 }
 
 // ------------------------------------------------------------------------
-// gate_up, grouped. grid.x = max_tiles * (inter / 128), block = 256.
+// Work-group -> (tile, output block) so that all nb blocks of a tile run on
+// one XCD, one after another in its dispatch order: the hardware deals
+// work-groups to the 8 XCDs in turn (block b to XCD b % 8), so XCD x takes
+// tiles x, x + 8, ... and each tile's activations come from HBM into that
+// XCD's L2 once, not once per block. The grid is a multiple of 8 nb
+// covering every tile (grouped_grid).
+// ------------------------------------------------------------------------
+__device__ __forceinline__ void xcd_tile_block(int nb, int& tile, int& blk) {
+  const int b = blockIdx.x;
+  const int slot = b >> 3;  // the slot-th work-group of XCD b % 8
+  tile = 8 * (slot / nb) + (b & 7);
+  blk = slot % nb;
+}
+__host__ __device__ constexpr unsigned grouped_grid(int max_tiles, int nb) {
+  return (unsigned)(((max_tiles + 7) / 8) * 8 * nb);
+}
+
+// ------------------------------------------------------------------------
+// gate_up, grouped. grid.x = grouped_grid(max_tiles, inter / 128), block = kThreads.
 // A work-group takes the gate rows and the up rows of one 128-channel block
 // c (256 outputs) for one tile; its epilogue finishes h = SiLU(gate) * up
 // for those channels and writes down's rotated fp16 input block c.
@@ -360,8 +378,8 @@ __device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el,
 template <int K>
 __global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
   const int nb = a.inter / 128;
-  const int c = blockIdx.x % nb;
-  const int tile = blockIdx.x / nb;
+  int c, tile;
+  xcd_tile_block(nb, tile, c);
   if (tile >= *a.n_tiles) return;  // uniform
   const int e = a.t_expert[tile];
   const int row0 = a.t_row0[tile];
@@ -426,15 +444,15 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
 }
 
 // ------------------------------------------------------------------------
-// down, grouped. grid.x = max_tiles * (hidden / 256), block = 256. The
+// down, grouped. grid.x = grouped_grid(max_tiles, hidden / 256), block = kThreads. The
 // epilogue applies H_n, rout and the pair's router weight and stores the
 // pair's 256 outputs (fp32) at its sorted index.
 // ------------------------------------------------------------------------
 template <int K>
 __global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
   const int ng = a.hidden / 256;
-  const int r = blockIdx.x % ng;
-  const int tile = blockIdx.x / ng;
+  int r, tile;
+  xcd_tile_block(ng, tile, r);
   if (tile >= *a.n_tiles) return;
   const int e = a.t_expert[tile];
   const int row0 = a.t_row0[tile];
@@ -797,7 +815,7 @@ hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s) {
 }
 
 hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
-  const unsigned grid = (unsigned)((size_t)max_tiles * (a.inter / 128));
+  const unsigned grid = grouped_grid(max_tiles, a.inter / 128);
   if (k_bits == 2)
     hipLaunchKernelGGL(k_grouped_gate_up<2>, dim3(grid), dim3(kThreads), 0, s, a);
   else
@@ -806,7 +824,7 @@ hipError_t launch_grouped_gate_up(const GroupedArgs& a, int max_tiles, int k_bit
 }
 
 hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s) {
-  const unsigned grid = (unsigned)((size_t)max_tiles * (a.hidden / 256));
+  const unsigned grid = grouped_grid(max_tiles, a.hidden / 256);
   if (k_bits == 2)
     hipLaunchKernelGGL(k_grouped_down<2>, dim3(grid), dim3(kThreads), 0, s, a);
   else
