@@ -100,7 +100,7 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
 
 // ------------------------------------------------------------------------
 // Rotated gate_up inputs per sorted pair: Xg[i] = fp16(H_n(rin_e (.) x_t)).
-// grid.x = n_pairs, block = 256 (wave w handles blocks w, w+4, ..).
+// grid.x = n_pairs, block = 256 (each 16 lanes one 128-input block).
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
   const int i = blockIdx.x;
