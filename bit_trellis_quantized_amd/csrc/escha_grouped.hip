@@ -47,12 +47,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDecWaves = 8;     // decoder waves per work-group
 constexpr int kThreads = 64 * (kDecWaves + 4);  // + four matrix waves
+constexpr int kWaves = kThreads / 64;
 constexpr int kTM = 128;         // tokens per tile
 constexpr int kStep = 64;        // inputs per step (4 tile-rows)
 constexpr int kWBuf = 256 * kStep;  // halves per W buffer (32 KiB)
 constexpr int kXBuf = kTM * kStep;  // halves per activation buffer (16 KiB)
-constexpr int kSmemBytes = 2 * (kWBuf + kXBuf) * 2;  // 96 KiB; the epilogue reuses it
-constexpr int kEPitch = 257;     // LDS row pitch of the epilogue (floats)
+constexpr int kEPitch = 260;     // LDS row pitch of the epilogue (floats; rows 16-byte aligned)
+constexpr int kMainBytes = 2 * (kWBuf + kXBuf) * 2;  // 96 KiB of main-loop buffers
+constexpr int kEpiBytes = kTM * kEPitch * 4;        // 130 KiB: the whole tile's outputs
+constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
 
 // ------------------------------------------------------------------------
 // Tile list: for every expert, ceil(count / tm) tiles of consecutive sorted
@@ -331,23 +334,25 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
   }
 }
 
-// Accumulators of the matrix waves with token half wt == h -> LDS E[64
-// tokens][256 outputs] (fp32).
-__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el, int h) {
+// Accumulators of every matrix wave -> LDS E[128 tokens][256 outputs]
+// (fp32; token 64 wt + 32 tt + column).
+__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wave < kDecWaves) return;
   const int wo = (wave - kDecWaves) >> 1, wt = (wave - kDecWaves) & 1;
-  if (wt != h) return;
+  const int j = 64 * wt + (lane & 31);  // token of column lane & 31
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);  // row in the 32x32 tile
-        const int j = lane & 31;                                  // column (token)
-        el[(32 * tt + j) * kEPitch + 128 * wo + 32 * mt + i] = acc[mt][tt][r];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        // rows 8 r4 + 4 (lane >> 5) .. + 3 of the 32x32 tile: one 16-byte store
+        const int i = 8 * r4 + 4 * (lane >> 5);
+        *reinterpret_cast<f32x4*>(&el[(32 * tt + j) * kEPitch + 128 * wo + 32 * mt + i]) =
+            f32x4{acc[mt][tt][4 * r4], acc[mt][tt][4 * r4 + 1], acc[mt][tt][4 * r4 + 2],
+                  acc[mt][tt][4 * r4 + 3]};
       }
 }
 
@@ -411,36 +416,53 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
   const float ru0 = f16_to_f32(ru[lane]), ru1 = f16_to_f32(ru[lane + 64]);
   const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
   float* el = reinterpret_cast<float*>(smem);
-  for (int h = 0; h < 2; ++h) {  // token halves of the tile
-    acc_to_lds(acc, el, h);
-    __syncthreads();
-    for (int tl = 8 * wave; tl < 8 * wave + 8 && wave < 8; ++tl) {  // waves 0-7: 8 tokens each
-      const int tok = 64 * h + tl;
-      if (tok >= rows) break;  // uniform over the wave
-      const float* er = el + tl * kEPitch;
-      float g0 = er[lane], g1 = er[lane + 64], u0 = er[128 + lane], u1 = er[192 + lane];
-      fwht128(g0, g1);
-      fwht128(u0, u1);
-      g0 *= kInvSqrt128 * rg0;
-      g1 *= kInvSqrt128 * rg1;
-      u0 *= kInvSqrt128 * ru0;
-      u1 *= kInvSqrt128 * ru1;
-      const float h0 = silu(g0) * u0;
-      const float h1 = silu(g1) * u1;
-      const int i = row0 + tok;
-      if (a.inter_out) {
-        float* io = a.inter_out + (size_t)a.perm[i] * a.inter + 128 * c;
+  // every wave takes tokens wave, wave + 12, ... of the tile, two at a time
+  // (two independent butterfly chains in flight)
+  auto two_tokens = [&](int tla) {
+    bool ok[2];
+    float g0[2], g1[2], u0[2], u1[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int tl = tla + kWaves * q;
+      ok[q] = tl < kTM && tl < rows;  // uniform over the wave
+      const float* er = el + (ok[q] ? tl : 0) * kEPitch;
+      g0[q] = er[lane];
+      g1[q] = er[lane + 64];
+      u0[q] = er[128 + lane];
+      u1[q] = er[192 + lane];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      fwht128(g0[q], g1[q]);
+      fwht128(u0[q], u1[q]);
+    }
+    float v0[2], v1[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float h0 = silu(g0[q] * (kInvSqrt128 * rg0)) * (u0[q] * (kInvSqrt128 * ru0));
+      const float h1 = silu(g1[q] * (kInvSqrt128 * rg1)) * (u1[q] * (kInvSqrt128 * ru1));
+      if (ok[q] && a.inter_out) {
+        float* io = a.inter_out + (size_t)a.perm[row0 + tla + kWaves * q] * a.inter + 128 * c;
         io[lane] = h0;
         io[lane + 64] = h1;
       }
-      float v0 = h0 * rd0, v1 = h1 * rd1;
-      fwht128(v0, v1);
-      _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
-      xo[lane] = (_Float16)(v0 * kInvSqrt128);
-      xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+      v0[q] = h0 * rd0;
+      v1[q] = h1 * rd1;
     }
-    __syncthreads();
-  }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) fwht128(v0[q], v1[q]);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!ok[q]) continue;
+      const int i = row0 + tla + kWaves * q;
+      _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
+      xo[lane] = (_Float16)(v0[q] * kInvSqrt128);
+      xo[lane + 64] = (_Float16)(v1[q] * kInvSqrt128);
+    }
+  };
+  acc_to_lds(acc, el);
+  __syncthreads();
+  for (int tla = wave; tla < kTM; tla += 2 * kWaves) two_tokens(tla);
 }
 
 // ------------------------------------------------------------------------
@@ -479,26 +501,40 @@ __global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
   const float r00 = f16_to_f32(ro[lane]), r01 = f16_to_f32(ro[lane + 64]);
   const float r10 = f16_to_f32(ro[128 + lane]), r11 = f16_to_f32(ro[192 + lane]);
   float* el = reinterpret_cast<float*>(smem);
-  for (int h = 0; h < 2; ++h) {
-    acc_to_lds(acc, el, h);
-    __syncthreads();
-    for (int tl = 8 * wave; tl < 8 * wave + 8 && wave < 8; ++tl) {  // waves 0-7: 8 tokens each
-      const int tok = 64 * h + tl;
-      if (tok >= rows) break;
-      const int i = row0 + tok;
-      const float wt = a.w[a.perm[i]];
-      const float* er = el + tl * kEPitch;
-      float z0 = er[lane], z1 = er[lane + 64], z2 = er[128 + lane], z3 = er[192 + lane];
-      fwht128(z0, z1);
-      fwht128(z2, z3);
-      float* yo = a.y_out + (size_t)i * a.hidden + 256 * r;
-      yo[lane] = z0 * kInvSqrt128 * r00 * wt;
-      yo[lane + 64] = z1 * kInvSqrt128 * r01 * wt;
-      yo[128 + lane] = z2 * kInvSqrt128 * r10 * wt;
-      yo[192 + lane] = z3 * kInvSqrt128 * r11 * wt;
+  // every wave takes tokens wave, wave + 12, ... of the tile, two at a time
+  auto two_tokens = [&](int tla) {
+    bool ok[2];
+    float z0[2], z1[2], z2[2], z3[2], wt[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int tl = tla + kWaves * q;
+      ok[q] = tl < kTM && tl < rows;  // uniform over the wave
+      const float* er = el + (ok[q] ? tl : 0) * kEPitch;
+      z0[q] = er[lane];
+      z1[q] = er[lane + 64];
+      z2[q] = er[128 + lane];
+      z3[q] = er[192 + lane];
+      wt[q] = ok[q] ? a.w[a.perm[row0 + tl]] : 0.f;
     }
-    __syncthreads();
-  }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      fwht128(z0[q], z1[q]);
+      fwht128(z2[q], z3[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (!ok[q]) continue;
+      const int i = row0 + tla + kWaves * q;
+      float* yo = a.y_out + (size_t)i * a.hidden + 256 * r;
+      yo[lane] = z0[q] * kInvSqrt128 * r00 * wt[q];
+      yo[lane + 64] = z1[q] * kInvSqrt128 * r01 * wt[q];
+      yo[128 + lane] = z2[q] * kInvSqrt128 * r10 * wt[q];
+      yo[192 + lane] = z3[q] * kInvSqrt128 * r11 * wt[q];
+    }
+  };
+  acc_to_lds(acc, el);
+  __syncthreads();
+  for (int tla = wave; tla < kTM; tla += 2 * kWaves) two_tokens(tla);
 }
 
 // ------------------------------------------------------------------------
