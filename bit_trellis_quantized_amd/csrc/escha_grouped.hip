@@ -13,7 +13,7 @@
 // decoded once and reused by several activation tiles). Activations enter
 // the contraction as fp16 (the decoded weights are exactly fp16).
 //
-// Layout in one work-group (12 waves, three per SIMD):
+// Layout in one work-group (16 waves, four per SIMD):
 //  - waves 0-7 decode: lane = 8*tile + o, tile = 16*kt_local + nt_local: 64
 //    tiles (4 tile-rows x 16 output tiles) = one 64-input step for 256
 //    outputs, written to LDS one step ahead of the matrix waves; lane o of a
@@ -28,10 +28,12 @@
 //  - the decoder waves also stage the step's activation tile (fp16,
 //    [k/8][token][8]) in LDS; codes and activations are issued two steps
 //    ahead of their use;
-//  - waves 8-11 run the matrix cores on the current step from LDS, so decode
-//    (VALU) and contraction (MFMA) overlap on every SIMD;
-//  - matrix wave (wo, wt) owns outputs 128wo..128wo+127 (four 32-row MFMA
-//    tiles) for tokens 64wt..64wt+63 (two 32-token MFMA tiles): 8
+//  - waves 8-15 run the matrix cores on the current step from LDS, so decode
+//    (VALU) and contraction (MFMA) overlap on every SIMD, and each SIMD has
+//    two matrix waves, one issuing MFMAs while the other waits for its LDS
+//    operands;
+//  - matrix wave (wo, wt) owns outputs 64wo..64wo+63 (two 32-row MFMA
+//    tiles) for tokens 64wt..64wt+63 (two 32-token MFMA tiles): 4
 //    accumulators of 16 fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,7 +48,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kDecWaves = 8;     // decoder waves per work-group
-constexpr int kThreads = 64 * (kDecWaves + 4);  // + four matrix waves
+constexpr int kMatWaves = 8;    // matrix waves per work-group
+constexpr int kMT = 16 / kMatWaves;  // 32-row output tiles of a matrix wave
+constexpr int kThreads = 64 * (kDecWaves + kMatWaves);
 constexpr int kWaves = kThreads / 64;
 constexpr int kTM = 128;         // tokens per tile
 constexpr int kStep = 64;        // inputs per step (4 tile-rows)
@@ -153,7 +157,7 @@ __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
 
 // ------------------------------------------------------------------------
 // Shared main loop: acc[mt][tt] += W[256 outputs][K] * X[128 tokens][K]^T.
-// Wave (wo, wt) = (wave >> 1, wave & 1) owns outputs 128*wo + 32*mt (mt 0..3)
+// Wave (wo, wt) = (wave >> 1, wave & 1) owns outputs 32*kMT*wo + 32*mt (mt < kMT)
 // and tokens 64*wt + 32*tt (tt 0..1). Step s's matrix-core work is issued
 // in the same loop body as the decode of step s+1 (into the other LDS
 // buffer), so the VALU decode and the MFMAs overlap; codes run two steps
@@ -212,45 +216,51 @@ struct StepLoads {
 };
 
 // The matrix waves' part of every step: NT live 32-token sub-tiles (1 or 2)
-// against four 32-row output tiles; operands of sub-step ks+1 are read from
+// against kMT 32-row output tiles; operands of sub-step ks+1 are read from
 // LDS while sub-step ks's MFMAs issue. One barrier per step, matching the
 // decoder waves'.
 template <int NT>
 __device__ __forceinline__ void mma_steps(const _Float16* wl, const _Float16* xl, int n_steps, int wo,
-                                          int wt, int lane, f32x16 (&acc)[4][2]) {
+                                          int wt, int lane, f32x16 (&acc)[kMT][2]) {
   constexpr int kKs = kStep / 16;
   const int l32 = lane & 31;
   const int khi = lane >> 5;
-  int prow[4];
+  int prow[kMT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    const int row = 128 * wo + 32 * mt + l32;
+  for (int mt = 0; mt < kMT; ++mt) {
+    const int row = 32 * kMT * wo + 32 * mt + l32;
     prow[mt] = row ^ ((row >> 4) & 15);
   }
   for (int s = 0; s < n_steps; ++s) {
     const _Float16* wb = wl + (s & 1) * kWBuf;
     const _Float16* xb = xl + (s & 1) * kXBuf;
-    auto load_ops = [&](int ks, h8 (&a)[4], h8 (&b)[2]) {
+    auto load_ops = [&](int ks, h8 (&a)[kMT], h8 (&b)[2]) {
       const int kc = 2 * ks + khi;
 #pragma unroll
       for (int tt = 0; tt < NT; ++tt)
         b[tt] = *reinterpret_cast<const h8*>(xb + (kc * kTM + 64 * wt + 32 * tt + l32) * 8);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) a[mt] = *reinterpret_cast<const h8*>(wb + (kc * 256 + prow[mt]) * 8);
+      for (int mt = 0; mt < kMT; ++mt) a[mt] = *reinterpret_cast<const h8*>(wb + (kc * 256 + prow[mt]) * 8);
     };
-    h8 a0[4], b0[2], a1[4], b1[2];
+    h8 a0[kMT], b0[2], a1[kMT], b1[2];
     load_ops(0, a0, b0);
+    // the scheduling barriers keep each sub-step's reads ahead of the
+    // previous sub-step's MFMAs (left alone, the compiler sinks them to just
+    // before their use to save registers and exposes every read's latency)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kKs; ks += 2) {
       load_ops(ks + 1, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
           acc[mt][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0[mt], b0[tt], acc[mt][tt], 0, 0, 0);
       if (ks + 2 < kKs) load_ops(ks + 2, a0, b0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
           acc[mt][tt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1[mt], b1[tt], acc[mt][tt], 0, 0, 0);
@@ -264,7 +274,7 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
                                                  int in_f, const _Float16* __restrict__ X,
                                                  int x_pitch, int row0, int rows, OutTile out_tile,
                                                  _Float16* wl, _Float16* xl,
-                                                 f32x16 (&acc)[4][2]) {
+                                                 f32x16 (&acc)[kMT][2]) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform per wave
   const int lane = tid & 63;
@@ -317,8 +327,8 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
       }
     }
   } else {
-    // waves 8-11: matrix cores on step s from LDS. (wo, wt): outputs
-    // 128*wo + 32*mt, tokens 64*wt + 32*tt. Token sub-tiles without a real
+    // the other waves: matrix cores on step s from LDS. (wo, wt): outputs
+    // 32*kMT*wo + 32*mt, tokens 64*wt + 32*tt. Token sub-tiles without a real
     // token are skipped (uniform per wave); padded columns of a live
     // sub-tile hold a clamped row and are never stored.
     const int mw = wave - kDecWaves;
@@ -336,21 +346,21 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
 
 // Accumulators of every matrix wave -> LDS E[128 tokens][256 outputs]
 // (fp32; token 64 wt + 32 tt + column).
-__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[4][2], float* el) {
+__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[kMT][2], float* el) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (wave < kDecWaves) return;
   const int wo = (wave - kDecWaves) >> 1, wt = (wave - kDecWaves) & 1;
   const int j = 64 * wt + (lane & 31);  // token of column lane & 31
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         // rows 8 r4 + 4 (lane >> 5) .. + 3 of the 32x32 tile: one 16-byte store
         const int i = 8 * r4 + 4 * (lane >> 5);
-        *reinterpret_cast<f32x4*>(&el[(32 * tt + j) * kEPitch + 128 * wo + 32 * mt + i]) =
+        *reinterpret_cast<f32x4*>(&el[(32 * tt + j) * kEPitch + 32 * kMT * wo + 32 * mt + i]) =
             f32x4{acc[mt][tt][4 * r4], acc[mt][tt][4 * r4 + 1], acc[mt][tt][4 * r4 + 2],
                   acc[mt][tt][4 * r4 + 3]};
       }
@@ -381,7 +391,7 @@ __host__ __device__ constexpr unsigned grouped_grid(int max_tiles, int nb) {
 // for those channels and writes down's rotated fp16 input block c.
 // ------------------------------------------------------------------------
 template <int K>
-__global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_gate_up(GroupedArgs a) {
   const int nb = a.inter / 128;
   int c, tile;
   xcd_tile_block(nb, tile, c);
@@ -396,9 +406,9 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   _Float16* wl = reinterpret_cast<_Float16*>(smem);
   _Float16* xl = wl + 2 * kWBuf;
-  f32x16 acc[4][2];
+  f32x16 acc[kMT][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
   const float ru0 = f16_to_f32(ru[lane]), ru1 = f16_to_f32(ru[lane + 64]);
   const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
   float* el = reinterpret_cast<float*>(smem);
-  // every wave takes tokens wave, wave + 12, ... of the tile, two at a time
+  // every wave takes tokens wave, wave + kWaves, ... of the tile, two at a time
   // (two independent butterfly chains in flight)
   auto two_tokens = [&](int tla) {
     bool ok[2];
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_gate_up(GroupedArgs a) {
 // pair's 256 outputs (fp32) at its sorted index.
 // ------------------------------------------------------------------------
 template <int K>
-__global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_down(GroupedArgs a) {
   const int ng = a.hidden / 256;
   int r, tile;
   xcd_tile_block(ng, tile, r);
@@ -485,9 +495,9 @@ __global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   _Float16* wl = reinterpret_cast<_Float16*>(smem);
   _Float16* xl = wl + 2 * kWBuf;
-  f32x16 acc[4][2];
+  f32x16 acc[kMT][2];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_down(GroupedArgs a) {
   const float r00 = f16_to_f32(ro[lane]), r01 = f16_to_f32(ro[lane + 64]);
   const float r10 = f16_to_f32(ro[128 + lane]), r11 = f16_to_f32(ro[192 + lane]);
   float* el = reinterpret_cast<float*>(smem);
-  // every wave takes tokens wave, wave + 12, ... of the tile, two at a time
+  // every wave takes tokens wave, wave + kWaves, ... of the tile, two at a time
   auto two_tokens = [&](int tla) {
     bool ok[2];
     float z0[2], z1[2], z2[2], z3[2], wt[2];
