@@ -284,3 +284,29 @@ def test_grouped_one_hot_expert(escha, layer2, layer2_dev):
     ids = np.tile(np.array([[3, 9, 27, 81, 100, 200, 250, 7]], dtype=np.int32), (T, 1))
     w = np.full((T, 8), 0.125, dtype=np.float32)
     _check_layer(escha, layer2, layer2_dev, x, ids, w, escha.escha_moe_layer_prefill, "hot experts")
+
+
+def test_prefill_partial_tiles(escha, layer2, layer2_dev):
+    """128-token tiles whose token counts end inside every 32-token sub-tile
+    of both token halves (1, 20, 29, 32, 33, 40, 59, 64, 65, 69, 70, 96, 97,
+    100, 128 and 129 = a full tile plus one): every matrix wave meets no,
+    one or two live sub-tiles, and the padded columns are never stored."""
+    announce("prefill partial tiles T=129")
+    T = 129
+    # slot j: expert experts[i] for tokens bounds[i - 1] .. bounds[i] - 1 of plan[j]
+    plan = [((20, 60, 129), (10, 11, 12)), ((70, 129), (13, 14)), ((100, 129), (15, 16)),
+            ((128, 129), (17, 18)), ((129,), (19,)), ((64, 129), (20, 21)),
+            ((96, 129), (22, 23)), ((97, 129), (24, 25))]
+    ids = np.empty((T, 8), dtype=np.int32)
+    for j, (bounds, experts) in enumerate(plan):
+        lo = 0
+        for hi, e in zip(bounds, experts):
+            ids[lo:hi, j] = e
+            lo = hi
+    counts = sorted(np.bincount(ids.ravel())[10:26].tolist())
+    assert counts == [1, 20, 29, 32, 33, 40, 59, 64, 65, 69, 70, 96, 97, 100, 128, 129]
+    x = synth.activations(51, T, 2048)
+    rng = np.random.default_rng(51)
+    w = rng.random((T, 8)).astype(np.float32)
+    w /= w.sum(axis=1, keepdims=True)
+    _check_layer(escha, layer2, layer2_dev, x, ids, w, escha.escha_moe_layer_prefill, "partial tiles")
