@@ -31,7 +31,7 @@ CODEBOOK_SECOND_MOMENT = 1.5478
 # tensor ids inside one (layer, expert) stream family
 _T_CODE, _T_RIN, _T_ROUT, _T_MASK = 0, 1, 2, 3
 _GU, _DN = 0, 10
-_T_X, _T_LOGITS, _T_POP = 100, 101, 102
+_T_X, _T_LOGITS, _T_POP, _T_GATE = 100, 101, 102, 103
 
 F16_ONE = 0x3C00
 F16_MINUS_ONE = 0xBC00
@@ -93,6 +93,13 @@ def activations(seed: int, T: int, n: int, layer: int = 0) -> np.ndarray:
     """bf16 bits [T][n] of N(0, 1)."""
     x = rng(seed, layer, 0, _T_X).standard_normal((T, n)).astype(np.float32)
     return to_bf16_bits(x)
+
+
+def router_gate(seed: int, E: int = N_EXPERTS, n: int = HIDDEN, layer: int = 0) -> np.ndarray:
+    """fp16 bits [E][n] of N(0, 1/n): a router gate whose logits on N(0, 1)
+    hidden states are about N(0, 1), like the routing workloads' logits."""
+    g = rng(seed, layer, 0, _T_GATE).standard_normal((E, n)) / np.sqrt(n)
+    return g.astype(np.float16).view(np.uint16).copy()
 
 
 def normal_logits(seed: int, T: int, E: int = N_EXPERTS, layer: int = 0) -> np.ndarray:

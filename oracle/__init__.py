@@ -90,6 +90,9 @@ def lib():
         L.eo_swiglu.restype = None
         L.eo_route_topk.argtypes = [_f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _f64p]
         L.eo_route_topk.restype = None
+        L.eo_router_logits.argtypes = [_u16p, ctypes.c_int, ctypes.c_int, _u16p, ctypes.c_int, _f32p,
+                                       _f64p]
+        L.eo_router_logits.restype = None
         L.eo_group.argtypes = [_i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, _i32p, _i32p, _i32p]
         L.eo_group.restype = None
         L.eo_moe_layer.argtypes = [ctypes.POINTER(_Layer), _u16p, ctypes.c_int, _i32p, _f32p,
@@ -224,6 +227,20 @@ def route_topk(logits, top_k: int):
     w = np.zeros((T, top_k), dtype=np.float64)
     lib().eo_route_topk(_p(l, _f32p), T, E, top_k, _p(ids, _i32p), _p(w, _f64p))
     return ids, w
+
+
+def router_logits(x_bf16, gate_f16, *, want_raw=False):
+    """x bf16 bits [T][H], gate fp16 bits [E][H] -> logits fp32 [T][E] (each
+    an fp16 value: the rounded exact dot product), and the fp64 sums."""
+    x = _c(x_bf16, np.uint16)
+    g = _c(gate_f16, np.uint16)
+    T, H = x.shape
+    E = g.shape[0]
+    assert g.shape[1] == H
+    logits = np.zeros((T, E), dtype=np.float32)
+    raw = np.zeros((T, E), dtype=np.float64)
+    lib().eo_router_logits(_p(x, _u16p), T, H, _p(g, _u16p), E, _p(logits, _f32p), _p(raw, _f64p))
+    return (logits, raw) if want_raw else logits
 
 
 def group(ids, n_experts: int):

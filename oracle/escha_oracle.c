@@ -30,7 +30,10 @@
  *  A4  weight i of a tile sits at input row k = i/16, output column n = i%16;
  *  A8  input side: rin first, then H; output side: H first, then rout;
  *  A10 router weights are softmax probabilities over all experts, not
- *      renormalised over the selected k; ties go to the lower expert index.
+ *      renormalised over the selected k; ties go to the lower expert index;
+ *  A17 router logits: the fp16 rounding of the exact gate . x dot product
+ *      (the pages fix the fp16 gate and the rounding, not the precision of
+ *      the sum; the exact sum is the plainest reading).
  * Real-checkpoint parity of A1-A4 is unpinned: the pages print no decoded
  * tile of real data.
  */
@@ -321,6 +324,30 @@ EO_EXPORT void eo_route_topk(const float* logits, int T, int E, int k, int32_t* 
   }
   free(p);
   free(taken);
+}
+
+/*
+ * Router logits, the step before routing: logit[t][e] = the fp16 rounding
+ * (round to nearest even) of the dot product of gate row e (fp16, [E][H])
+ * with the hidden state of token t (bf16, [T][H]). The model card's
+ * exactness table keeps the router gate in fp16; the port's review notes
+ * state that the logits are rounded to f16 before the top-k, which makes
+ * exact ties that fp32 logits would not have. Every product of an fp16 and
+ * a bf16 value is exact in fp64, and the sum is taken in fp64 (error far
+ * below half an f16 ulp unless the sum cancels), then rounded once.
+ * logits: fp32 holding the f16 value; raw (may be NULL): the fp64 sum.
+ */
+EO_EXPORT void eo_router_logits(const uint16_t* x_bf16, int T, int H, const uint16_t* gate_f16,
+                                int E, float* logits, double* raw) {
+  for (int t = 0; t < T; t++)
+    for (int e = 0; e < E; e++) {
+      double acc = 0.0;
+      for (int i = 0; i < H; i++)
+        acc += eo_f16_to_double(gate_f16[(size_t)e * H + i]) *
+               eo_bf16_to_double(x_bf16[(size_t)t * H + i]);
+      logits[(size_t)t * E + e] = (float)eo_f16_to_double(eo_double_to_f16_rne(acc));
+      if (raw) raw[(size_t)t * E + e] = acc;
+    }
 }
 
 /*

@@ -430,3 +430,55 @@ def test_rmsnorm_closed_forms(oracle_lib):
     assert np.all(x[0] == oracle.double_to_bf16_rne(c0))
     assert np.all(x[1, 0::2] == oracle.double_to_bf16_rne(c1))
     assert np.all(x[1, 1::2] == oracle.double_to_bf16_rne(-2 * c1))
+
+
+# ------------------------------------------------------------ router logits
+
+def _bf16_as_f32(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def test_router_logits_one_hot_rows(oracle_lib):
+    """Gate row e = 2^-3 at input e, zero elsewhere: the logit is the fp16
+    rounding of x_e / 8 (numpy's float16 cast rounds to nearest even)."""
+    T, H, E = 5, 64, 16
+    x = synth.activations(61, T, H)
+    gate = np.zeros((E, H), dtype=np.uint16)
+    gate[np.arange(E), np.arange(E)] = np.float16(0.125).view(np.uint16)
+    got = oracle.router_logits(x, gate)
+    want = (_bf16_as_f32(x)[:, :E].astype(np.float64) / 8).astype(np.float16).astype(np.float32)
+    assert np.array_equal(got, want)
+
+
+def test_router_logits_vs_numpy_matmul(oracle_lib):
+    """Random gate and states against numpy's fp64 matmul and float16 cast."""
+    T, H, E = 6, 256, 40
+    x = synth.activations(62, T, H)
+    gate = synth.router_gate(62, E, H)
+    got, raw = oracle.router_logits(x, gate, want_raw=True)
+    ref = _bf16_as_f32(x).astype(np.float64) @ gate.view(np.float16).astype(np.float64).T
+    assert np.allclose(raw, ref, rtol=0, atol=1e-12)
+    assert np.array_equal(got, ref.astype(np.float16).astype(np.float32))
+    assert np.abs(got).max() > 0.5  # logits of order one, not all rounded to zero
+
+
+def test_router_f16_rounding_makes_ties(oracle_lib):
+    """Exact sums 1 + 2^-12 (expert 5) and 1 (expert 2) both round to the
+    fp16 value 1 (half an ulp at 1 is 2^-11): the logits tie and the top-1
+    goes to the lower index, although the exact sums order them the other
+    way."""
+    H, E = 16, 8
+    x = np.zeros((1, H), dtype=np.uint16)
+    x[0, 0] = 0x3F80  # 1.0
+    x[0, 1] = 0x3980  # 2^-12
+    gate = np.zeros((E, H), dtype=np.uint16)
+    gate[:, 0] = np.float16(0.25).view(np.uint16)
+    gate[5, 0] = gate[2, 0] = np.float16(1.0).view(np.uint16)
+    gate[5, 1] = np.float16(1.0).view(np.uint16)
+    logits, raw = oracle.router_logits(x, gate, want_raw=True)
+    assert raw[0, 5] == 1.0 + 2.0 ** -12 and raw[0, 2] == 1.0
+    assert logits[0, 5] == logits[0, 2] == 1.0
+    ids, _ = oracle.route_topk(logits, 2)
+    assert list(ids[0]) == [2, 5]
+    ids_exact, _ = oracle.route_topk(raw.astype(np.float32), 2)
+    assert list(ids_exact[0]) == [5, 2]
