@@ -35,6 +35,7 @@ SEED = 4  # the stack workload's seed
 GU_BYTES_PER_PAIR = 2048 // 16 * 1024 // 16 * 32 * 2   # 524,288
 DN_BYTES_PER_PAIR = 512 // 16 * 2048 // 16 * 48 * 2    # 393,216
 HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (FMA = 2 flops)
 # VALU view of the same launches: decode costs 5.6 VALU lane-operations per
 # weight (721 VALU instructions per wave and 128 weights per lane in the
 # gfx950 ISA of the operand decoder); MI355X issues 256 CUs x 4 SIMDs x 16
@@ -91,7 +92,7 @@ def parse():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
-    ap.add_argument("--workload", choices=["stack", "layer", "copy"], default="stack",
+    ap.add_argument("--workload", choices=["stack", "layer", "copy", "router"], default="stack",
                     help="stack: the 40-layer decode (default); layer: one MoE layer call; "
                          "copy: a plain device copy (HBM calibration and counter scale)")
     ap.add_argument("--copy-mib", type=int, default=2048, help="copy workload: bytes per copy")
@@ -285,6 +286,46 @@ def copy_workload(args, log):
                       "steps": args.steps, "warmup": args.warmup}), flush=True)
 
 
+def router_workload(args, log):
+    """Router logits (fp16 gate [256][2048] . bf16 states) at 1, 64 and 4096
+    tokens (fp32 FMAs on the vector units), timed with HIP events around the
+    launches."""
+    import torch
+    from bit_trellis_quantized_amd import escha, synth
+    hip = Hip()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    H, E = synth.HIDDEN, synth.N_EXPERTS
+    out = {"workload": "router logits", "hidden": H, "experts": E, "steps": args.steps,
+           "warmup": args.warmup, "cases": {}}
+    for T in (1, 64, 4096):
+        x = torch.from_numpy(synth.activations(80, T, H).view(np.int16)).cuda()
+        gates = [torch.from_numpy(synth.router_gate(80, E, H, layer=l).view(np.int16)).cuda()
+                 for l in range(args.distinct_layers)]
+        logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
+        nbytes = escha._lib.escha_router_workspace_bytes(T, H, E)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+        for i in range(args.warmup):
+            escha.escha_router_logits(x, gates[i % len(gates)], out=logits, workspace=ws)
+        torch.cuda.synchronize()
+        start, stop = hip.event(), hip.event()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        hip.lib.hipEventRecord(ctypes.c_void_p(start), stream)
+        for i in range(args.steps):
+            escha.escha_router_logits(x, gates[i % len(gates)], out=logits, workspace=ws)
+        hip.lib.hipEventRecord(ctypes.c_void_p(stop), stream)
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(start, stop) / args.steps * 1e3
+        byts = E * H * 2 + T * H * 2 + T * E * 4
+        flops = 2.0 * T * E * H
+        out["cases"][str(T)] = {
+            "us_per_call": round(us, 3),
+            "gbs": round(byts / (us / 1e6) / 1e9, 1), "hbm_frac": round(byts / (us / 1e6) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(flops / (us / 1e6) / 1e12, 2),
+            "fp32_frac": round(flops / (us / 1e6) / 1e12 / FP32_PEAK_TFLOPS, 4)}
+        log(f"router T={T}: {us:.2f} us")
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -304,6 +345,9 @@ def main():
         return
     if args.workload == "layer":
         layer_workload(args, log)
+        return
+    if args.workload == "router":
+        router_workload(args, log)
         return
     NL, R = args.layers, args.pool
     hidden, E, k = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K

@@ -483,6 +483,40 @@ int escha_route_topk(const float* logits, int32_t n_tokens, int32_t n_experts, i
   return e == hipSuccess ? ESCHA_OK : hip_fail(e, "route_topk launch");
 }
 
+size_t escha_router_workspace_bytes(int32_t n_tokens, int32_t hidden, int32_t n_experts) {
+  if (n_tokens <= 0 || hidden < 32 || hidden % 32 || n_experts < 1 || n_experts > kMaxExpertsRoute)
+    return 0;
+  const int ks = escha::router_ksplit(n_tokens, hidden, n_experts);
+  return ks > 1 ? round_up((size_t)ks * n_tokens * n_experts * sizeof(float)) : 0;
+}
+
+int escha_router_logits(const uint16_t* x_bf16, int32_t n_tokens, int32_t hidden,
+                        const uint16_t* gate_f16, int32_t n_experts, float* logits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (hidden < 32 || hidden % 32) return fail(ESCHA_E_SHAPE, "hidden=%d is not a positive multiple of 32", hidden);
+  if (n_experts < 1 || n_experts > kMaxExpertsRoute)
+    return fail(ESCHA_E_ARG, "n_experts=%d out of [1, %d]", n_experts, kMaxExpertsRoute);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!x_bf16 || !gate_f16 || !logits) return fail(ESCHA_E_NULL, "x_bf16/gate_f16/logits is NULL");
+  if (!aligned(x_bf16, 16) || !aligned(gate_f16, 16))
+    return fail(ESCHA_E_ARG, "x_bf16/gate_f16 is not 16-byte aligned");
+  const size_t need = escha_router_workspace_bytes(n_tokens, hidden, n_experts);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu bytes < %zu", workspace ? workspace_bytes : 0, need);
+  escha::RouterArgs a;
+  a.x = x_bf16;
+  a.gate = gate_f16;
+  a.T = n_tokens;
+  a.H = hidden;
+  a.E = n_experts;
+  a.ksplit = escha::router_ksplit(n_tokens, hidden, n_experts);
+  a.logits = logits;
+  a.part = (float*)workspace;
+  hipError_t e = escha::launch_router_logits(a, (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "router_logits launch");
+}
+
 size_t escha_moe_group_workspace_bytes(int32_t n_tokens, int32_t top_k, int32_t n_experts) {
   if (n_tokens < 0 || top_k < 1 || n_experts < 1) return 0;
   const size_t P = (size_t)n_tokens * top_k;

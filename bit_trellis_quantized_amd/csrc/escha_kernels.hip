@@ -342,6 +342,119 @@ __global__ __launch_bounds__(64) void k_hadamard128(const float* x, int n, float
 }
 
 // ------------------------------------------------------------------------
+// Router logits: logit[t][e] = fp16(gate[e] . x[t]) (gate fp16 [E][H], x
+// bf16 [T][H]; the model card's exactness table keeps the router gate in
+// fp16, and the port's review notes round the logits to f16 before the
+// top-k). The product of an fp16 and a bf16 value is exact in fp32; each
+// lane adds its products with IEEE fp32 FMAs in input order, so the sum's
+// error follows the textbook bound of sequential summation (the order of
+// additions inside a matrix-core instruction is not specified).
+// One wave per (32-expert tile, 32-token tile, input slice): lane (r, h)
+// loads inputs 32c + 16q + 8h .. + 7 (q = 0, 1) of gate row 32et + r and of
+// token 32tt + r for chunk c (16-byte loads, one chunk ahead of its use;
+// rows past the end are clamped to the last row and their results
+// dropped), converts them to fp32 into LDS ([input][row]), and then
+// accumulates token r against experts 8p + 4h + m (p, m = 0..3) of the
+// tile. With one slice the kernel rounds and stores the logits; otherwise
+// it stores fp32 partial sums [slice][T][E], which k_router_reduce adds in
+// slice order. grid.x = n_tiles * ksplit (slice fastest), block = 64.
+// ------------------------------------------------------------------------
+
+// A lane's operands of one 32-input chunk.
+struct RouterChunk {
+  u32x4 g[2], x[2];
+};
+
+__device__ __forceinline__ void router_load(const uint16_t* gp, const uint16_t* xp, int c,
+                                            RouterChunk& o) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    o.g[q] = *reinterpret_cast<const u32x4*>(gp + 32 * c + 16 * q);
+    o.x[q] = *reinterpret_cast<const u32x4*>(xp + 32 * c + 16 * q);
+  }
+}
+
+__global__ __launch_bounds__(64) void k_router_logits(RouterArgs a) {
+  __shared__ __attribute__((aligned(16))) float gs[32][32];  // [input][expert of the tile]
+  __shared__ float xs[32][32];                               // [input][token of the tile]
+  const int lane = threadIdx.x;
+  const int ne = (a.E + 31) / 32;
+  int b = blockIdx.x;
+  const int ks = b % a.ksplit;
+  b /= a.ksplit;
+  const int et = b % ne, tt = b / ne;
+  const int r = lane & 31, h = lane >> 5;
+  const int er = 32 * et + r < a.E ? 32 * et + r : a.E - 1;
+  const int tr = 32 * tt + r < a.T ? 32 * tt + r : a.T - 1;
+  const int per = (a.H / 32) / a.ksplit;
+  const int c0 = ks * per, c1 = c0 + per;
+  const uint16_t* gp = a.gate + (size_t)er * a.H + 8 * h;
+  const uint16_t* xp = a.x + (size_t)tr * a.H + 8 * h;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  RouterChunk cur;
+  router_load(gp, xp, c0, cur);
+  for (int c = c0; c < c1; ++c) {
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int k = 16 * q + 8 * h + j;
+        gs[k][r] = f16_to_f32((uint16_t)(cur.g[q][j >> 1] >> (16 * (j & 1))));
+        xs[k][r] = bf16_to_f32((uint16_t)(cur.x[q][j >> 1] >> (16 * (j & 1))));
+      }
+    // the next chunk's loads (past the slice: this chunk's again, unused)
+    router_load(gp, xp, c + 1 < c1 ? c + 1 : c, cur);
+    __syncthreads();
+#pragma unroll 8
+    for (int k = 0; k < 32; ++k) {
+      const float xv = xs[k][r];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float4 g4 = *reinterpret_cast<const float4*>(&gs[k][8 * p + 4 * h]);
+        acc[4 * p + 0] = __builtin_fmaf(g4.x, xv, acc[4 * p + 0]);
+        acc[4 * p + 1] = __builtin_fmaf(g4.y, xv, acc[4 * p + 1]);
+        acc[4 * p + 2] = __builtin_fmaf(g4.z, xv, acc[4 * p + 2]);
+        acc[4 * p + 3] = __builtin_fmaf(g4.w, xv, acc[4 * p + 3]);
+      }
+    }
+  }
+  // lane holds token r, experts 8p + 4h + m (i = 4p + m) of the tile
+  const int t = 32 * tt + r;
+  if (t >= a.T) return;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int e = 32 * et + 8 * (i >> 2) + 4 * h + (i & 3);
+    if (e < a.E) {
+      if (a.ksplit == 1)
+        a.logits[(size_t)t * a.E + e] = (float)(_Float16)acc[i];
+      else
+        a.part[((size_t)ks * a.T + t) * a.E + e] = acc[i];
+    }
+  }
+}
+
+// Partial sums of the input slices added in slice order, then rounded to
+// fp16 (round to nearest even). One thread per logit.
+__global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ part, int ksplit,
+                                                       size_t n, float* __restrict__ logits) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  // every slice's partial in flight at once (ksplit <= 32), then added in
+  // slice order
+  float v[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) v[k] = k < ksplit ? part[(size_t)k * n + i] : 0.f;
+  float s = v[0];
+#pragma unroll
+  for (int k = 1; k < 32; ++k)
+    if (k < ksplit) s += v[k];
+  logits[i] = (float)(_Float16)s;
+}
+
+// ------------------------------------------------------------------------
 // Router: softmax + top-k per token. grid.x = n_tokens, block = 64; each
 // lane holds kMaxPer logits (E <= 64 kMaxPer).
 // ------------------------------------------------------------------------
@@ -597,6 +710,25 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     hipLaunchKernelGGL(k_route_topk<8>, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
   else
     hipLaunchKernelGGL(k_route_topk<16>, dim3(T), dim3(64), 0, s, logits, E, k, ids, w);
+  return last_launch();
+}
+
+int router_ksplit(int T, int H, int E) {
+  const int tiles = ((E + 31) / 32) * ((T + 31) / 32);
+  const int nch = H / 32;
+  int ks = 1;
+  while (ks < 32 && nch % (2 * ks) == 0 && tiles * 2 * ks <= 2048) ks *= 2;
+  return ks;
+}
+
+hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s) {
+  const unsigned grid = (unsigned)(((a.E + 31) / 32) * ((a.T + 31) / 32) * a.ksplit);
+  hipLaunchKernelGGL(k_router_logits, dim3(grid), dim3(64), 0, s, a);
+  hipError_t err = last_launch();
+  if (err != hipSuccess || a.ksplit == 1) return err;
+  const size_t n = (size_t)a.T * a.E;
+  hipLaunchKernelGGL(k_router_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.part,
+                     a.ksplit, n, a.logits);
   return last_launch();
 }
 

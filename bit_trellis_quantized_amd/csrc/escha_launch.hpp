@@ -192,6 +192,21 @@ hipError_t launch_decode_tiles(const uint16_t* code_e, int in_f, int out_f, int 
 hipError_t launch_hadamard128(const float* x, int64_t rows, int n, float* y, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);
+// Router logits (k_router_logits / k_router_reduce): x bf16 [T][H], gate
+// fp16 [E][H], logits fp32 [T][E]; part: ksplit * T * E floats when
+// ksplit > 1. H % 32 == 0 and (H / 32) % ksplit == 0.
+struct RouterArgs {
+  const uint16_t* x;
+  const uint16_t* gate;
+  int T, H, E;
+  int ksplit;
+  float* logits;
+  float* part;
+};
+// input slices for a call: a power of two <= 32 dividing H / 32, as many as
+// keep the grid within 2048 waves
+int router_ksplit(int T, int H, int E);
+hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s);
 // inv (nullable): pair -> sorted index, -1 for a pair with an out-of-range id
 // n_layers groupings at once: layer l reads ids + l P and uses counts + l E,
 // offsets + l (E + 1), perm / inv / rank + l P, hist / base + l chunks E.

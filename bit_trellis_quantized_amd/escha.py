@@ -54,6 +54,8 @@ _SIGS = {
     "escha_decode_tiles": ([_P(escha_proj_t), _i32, _vp, _vp], ctypes.c_int),
     "escha_hadamard128": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
     "escha_route_topk": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
+    "escha_router_workspace_bytes": ([_i32, _i32, _i32], _sz),
+    "escha_router_logits": ([_vp, _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
     "escha_moe_group_workspace_bytes": ([_i32, _i32, _i32], _sz),
     "escha_moe_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "escha_expert_gemv_workspace_bytes": ([_P(escha_proj_t), _i32], _sz),
@@ -225,6 +227,25 @@ def escha_route_topk(logits: torch.Tensor, top_k: int, stream=None):
     _check(_lib.escha_route_topk(_ptr(logits, torch.float32, "logits"), T, E, top_k,
                                  _ptr(ids), _ptr(w), _stream(stream)))
     return ids, w
+
+
+def escha_router_logits(x_bf16: torch.Tensor, gate_f16: torch.Tensor, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None):
+    """x bf16 [T][H] (bf16 or 16-bit integer view), gate fp16 [E][H] -> fp32
+    logits [T][E], each an fp16 value."""
+    T, H = x_bf16.shape
+    E, H2 = gate_f16.shape
+    if H2 != H:
+        raise ValueError(f"gate has {H2} inputs, x has {H}")
+    if out is None:
+        out = torch.empty(T, E, dtype=torch.float32, device=x_bf16.device)
+    nbytes = _lib.escha_router_workspace_bytes(T, H, E)
+    if workspace is None and nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_bf16.device)
+    _check(_lib.escha_router_logits(_ptr(x_bf16, _U16, "x_bf16"), T, H, _ptr(gate_f16, _U16, "gate_f16"),
+                                    E, _ptr(out, torch.float32, "logits"), _ptr(workspace),
+                                    workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out
 
 
 def escha_moe_group(topk_ids: torch.Tensor, n_experts: int, stream=None):

@@ -126,6 +126,29 @@ ESCHA_API int escha_route_topk(const float* logits, int32_t n_tokens, int32_t n_
                      int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
+ * Router logits, the step before escha_route_topk: logits[t][e] = the fp16
+ * value nearest (ties to even) to the dot product of gate row e with the
+ * hidden state of token t, returned as fp32. [trellis-mlx] exactness table:
+ * the router gate (mlp.gate) is kept in fp16; [hipfire] review notes: the
+ * logits are rounded to f16 before the top-k, which creates exact ties that
+ * escha_route_topk then breaks to the lower expert index. The products are
+ * exact and summed with IEEE fp32 FMAs in input order, so a logit can differ from
+ * the rounding of the exact sum by one f16 step only where that sum lies
+ * within fp32 rounding error of the midpoint between two f16 values. The
+ * same call (sizes) always sums in the same order: results are reproducible.
+ *   x_bf16    bf16 [n_tokens][hidden], 16-byte aligned
+ *   gate_f16  fp16 [n_experts][hidden], 16-byte aligned
+ *   logits    out: fp32 [n_tokens][n_experts]
+ * hidden % 32 == 0; 1 <= n_experts <= 1024; n_tokens >= 0 (0: no-op).
+ * workspace >= escha_router_workspace_bytes(n_tokens, hidden, n_experts)
+ * (partial sums when small calls split the inputs; may be 0 bytes).
+ */
+ESCHA_API size_t escha_router_workspace_bytes(int32_t n_tokens, int32_t hidden, int32_t n_experts);
+ESCHA_API int escha_router_logits(const uint16_t* x_bf16, int32_t n_tokens, int32_t hidden,
+                                  const uint16_t* gate_f16, int32_t n_experts, float* logits,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Group the n_tokens*top_k (token, slot) pairs by expert ([hipfire] grouped
  * GEMM notes: expert_offsets and a permutation). counts int32 [n_experts];
  * offsets int32 [n_experts+1] exclusive prefix sums; perm int32

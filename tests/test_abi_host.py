@@ -136,6 +136,28 @@ def test_route_and_group_validation(lib):
     assert g(FAKE, 4, 8, 256, FAKE, FAKE, FAKE, FAKE, 0, None) == -4
 
 
+def test_router_logits_validation(lib):
+    f = lib.escha_router_logits
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    wsb = lib.escha_router_workspace_bytes
+    wsb.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    wsb.restype = ctypes.c_size_t
+    assert f(FAKE, 1, 48, FAKE, 256, FAKE, None, 0, None) == -2     # hidden not a multiple of 32
+    assert f(FAKE, 1, 2048, FAKE, 0, FAKE, None, 0, None) == -7     # no experts
+    assert f(FAKE, 1, 2048, FAKE, 1025, FAKE, None, 0, None) == -7
+    assert f(FAKE, -1, 2048, FAKE, 256, FAKE, None, 0, None) == -7
+    assert f(None, 1, 2048, FAKE, 256, FAKE, None, 0, None) == -1
+    assert f(FAKE + 2, 1, 2048, FAKE, 256, FAKE, None, 0, None) == -7  # misaligned x
+    assert f(None, 0, 2048, None, 256, None, None, 0, None) == 0     # zero tokens: no-op
+    # a single token splits the inputs: partial sums need the workspace
+    need = wsb(1, 2048, 256)
+    assert need >= 32 * 256 * 4
+    assert f(FAKE, 1, 2048, FAKE, 256, FAKE, FAKE, need - 1, None) == -4
+    assert wsb(4096, 2048, 256) >= 2 * 4096 * 256 * 4
+    assert wsb(1, 48, 256) == 0
+
+
 def test_stack_validation(lib):
     f = lib.escha_moe_stack_decode
     f.argtypes = [ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,

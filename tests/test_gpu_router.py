@@ -1,0 +1,118 @@
+"""GPU parity of the router logits (the step before routing) against the oracle.
+
+The kernel sums exact products in fp32, the oracle in fp64; both round once
+to fp16. A logit must be the fp16 rounding of a value within the fp32
+summation error bound of the exact sum: equal to the oracle's logit except
+near a rounding midpoint or for logits so small that fp16 steps are finer
+than that bound. The top-k is an
+integer decision taken on fp16 logits, so it is checked on the kernel's own
+logits (the same values on both sides), bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_trellis_quantized_amd import synth
+from tests._gpu_util import announce, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def escha():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from bit_trellis_quantized_amd import escha as mod
+    return mod
+
+
+def _f32(bits_bf16):
+    return (np.asarray(bits_bf16, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _check_logits(got, x, gate, rows=None):
+    """got: the kernel's logits [T][E] (or the rows `rows` of them).
+
+    The kernel sums exact products in fp32 in input order (in slices, then
+    the slices in order). Each addition errs by at most 2^-24 times the
+    partial sum, and the errors add up like a random walk over the H
+    additions, so the fp32 sum lies within delta = 8 * 2^-24 * sqrt(H) *
+    max|prefix sum| (the factor 8 covers slices starting from zero and the
+    statistical margin) of the exact sum. A logit must therefore lie between
+    the fp16 roundings of raw - delta and raw + delta: equal to the oracle's
+    logit unless the exact sum is within delta of a rounding midpoint (or so
+    small that fp16 steps are finer than delta)."""
+    xs = x if rows is None else x[rows]
+    g = got if rows is None else got[rows]
+    ref, raw = oracle.router_logits(xs, gate, want_raw=True)
+    assert np.array_equal(g.astype(np.float16).astype(np.float32), g), "logits are not fp16 values"
+    H = x.shape[1]
+    g64 = gate.view(np.float16).astype(np.float64)
+    xf = _f32(xs).astype(np.float64)
+    max_prefix = np.stack([np.abs(np.cumsum(g64 * xf[t], axis=1)).max(axis=1) for t in range(len(xs))])
+    delta = 8.0 * 2.0 ** -24 * np.sqrt(H) * max_prefix
+    lo = (raw - delta).astype(np.float16).astype(np.float32)
+    hi = (raw + delta).astype(np.float16).astype(np.float32)
+    bad = (g < lo) | (g > hi)
+    assert not bad.any(), (f"{bad.sum()} logits outside the fp32 error bound, e.g. got "
+                           f"{g[bad][:4]} for exact sums {raw[bad][:4]}")
+    assert np.mean(g != ref) < 0.05, f"{np.mean(g != ref):.3%} of the logits differ"
+    return ref
+
+
+@pytest.mark.parametrize("T,H,E", [(1, 2048, 256), (3, 2048, 256), (64, 2048, 256),
+                                   (37, 2048, 200), (5, 64, 8), (300, 96, 33)])
+def test_router_logits_vs_oracle(escha, T, H, E):
+    announce(f"router_logits T={T} H={H} E={E}")
+    x = synth.activations(70 + T, T, H)
+    gate = synth.router_gate(70 + T, E, H)
+    got = escha.escha_router_logits(to_dev(x), to_dev(gate)).cpu().numpy()
+    assert got.shape == (T, E)
+    _check_logits(got, x, gate)
+    again = escha.escha_router_logits(to_dev(x), to_dev(gate)).cpu().numpy()
+    assert np.array_equal(got, again), "router logits are not reproducible"
+
+
+def test_router_logits_prefill_sampled(escha):
+    """4096 tokens (the prefill workload's launch), every 16th token and the
+    last one checked against the oracle."""
+    T, H, E = 4096, 2048, 256
+    announce(f"router_logits T={T} sampled")
+    x = synth.activations(75, T, H)
+    gate = synth.router_gate(75, E, H)
+    got = escha.escha_router_logits(to_dev(x), to_dev(gate)).cpu().numpy()
+    rows = np.r_[np.arange(0, T, 16), T - 1]
+    _check_logits(got, x, gate, rows)
+
+
+def test_router_topk_on_kernel_logits(escha):
+    """Routing the kernel's logits: ids bit-exact with the oracle's top-k of
+    the same logits, weights within fp32 rounding."""
+    T, H, E = 64, 2048, 256
+    announce("router_logits -> route_topk T=64")
+    x = synth.activations(76, T, H)
+    gate = synth.router_gate(76, E, H)
+    logits = escha.escha_router_logits(to_dev(x), to_dev(gate))
+    ids, w = escha.escha_route_topk(logits, 8)
+    ref_ids, ref_w = oracle.route_topk(logits.cpu().numpy(), 8)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    assert np.allclose(w.cpu().numpy(), ref_w, rtol=2e-6, atol=0)
+
+
+def test_router_f16_tie_breaks_to_lower_index(escha):
+    """Exact sums 1 + 2^-12 (expert 5) and 1 (expert 2) round to the same
+    fp16 logit; the top-1 then goes to expert 2."""
+    H, E = 32, 8
+    announce("router_logits tie")
+    x = np.zeros((1, H), dtype=np.uint16)
+    x[0, 0] = 0x3F80  # 1.0
+    x[0, 1] = 0x3980  # 2^-12
+    gate = np.zeros((E, H), dtype=np.uint16)
+    gate[:, 0] = np.float16(0.25).view(np.uint16)
+    gate[5, 0] = gate[2, 0] = np.float16(1.0).view(np.uint16)
+    gate[5, 1] = np.float16(1.0).view(np.uint16)
+    logits = escha.escha_router_logits(to_dev(x), to_dev(gate))
+    lg = logits.cpu().numpy()
+    assert lg[0, 2] == lg[0, 5] == 1.0
+    ids, _ = escha.escha_route_topk(logits, 2)
+    assert ids.cpu().numpy()[0].tolist() == [2, 5]
