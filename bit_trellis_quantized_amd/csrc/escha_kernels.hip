@@ -436,6 +436,53 @@ __global__ __launch_bounds__(64) void k_router_logits(RouterArgs a) {
   }
 }
 
+// Router logits for a few tokens (T <= 8): one wave per expert; lane l
+// sums inputs 32c .. 32c + 31 (c = l, l + 64, ...) of every token in input
+// order with IEEE fp32 FMAs, and the wave adds its 64 lane sums in a fixed
+// butterfly order; one RNE rounding to f16. No partial sums in memory.
+// grid.x = ceil(E / 4), block = 256.
+constexpr int kRouterGemvTokens = 8;
+
+__global__ __launch_bounds__(256) void k_router_gemv(RouterArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = 4 * blockIdx.x + wave;
+  if (e >= a.E) return;  // uniform over the wave
+  float acc[kRouterGemvTokens];
+#pragma unroll
+  for (int t = 0; t < kRouterGemvTokens; ++t) acc[t] = 0.f;
+  for (int c = lane; c < a.H / 32; c += 64) {
+    const u32x4* gp = reinterpret_cast<const u32x4*>(a.gate + (size_t)e * a.H + 32 * c);
+    float gf[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 g = gp[q];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) gf[8 * q + j] = f16_to_f32((uint16_t)(g[j >> 1] >> (16 * (j & 1))));
+    }
+#pragma unroll
+    for (int t = 0; t < kRouterGemvTokens; ++t) {
+      if (t < a.T) {  // uniform
+        const u32x4* xp = reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.H + 32 * c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 xv = xp[q];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            acc[t] = __builtin_fmaf(gf[8 * q + j], bf16_to_f32((uint16_t)(xv[j >> 1] >> (16 * (j & 1)))),
+                                    acc[t]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouterGemvTokens; ++t) {
+    if (t < a.T) {
+      const float s = wave_sum(acc[t]);
+      if (lane == 0) a.logits[(size_t)t * a.E + e] = (float)(_Float16)s;
+    }
+  }
+}
+
 // Partial sums of the input slices added in slice order, then rounded to
 // fp16 (round to nearest even). One thread per logit.
 __global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__ part, int ksplit,
@@ -714,6 +761,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 }
 
 int router_ksplit(int T, int H, int E) {
+  if (T <= kRouterGemvTokens) return 1;  // k_router_gemv
   const int tiles = ((E + 31) / 32) * ((T + 31) / 32);
   const int nch = H / 32;
   int ks = 1;
@@ -722,6 +770,10 @@ int router_ksplit(int T, int H, int E) {
 }
 
 hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s) {
+  if (a.T <= kRouterGemvTokens) {
+    hipLaunchKernelGGL(k_router_gemv, dim3((unsigned)((a.E + 3) / 4)), dim3(256), 0, s, a);
+    return last_launch();
+  }
   const unsigned grid = (unsigned)(((a.E + 31) / 32) * ((a.T + 31) / 32) * a.ksplit);
   hipLaunchKernelGGL(k_router_logits, dim3(grid), dim3(64), 0, s, a);
   hipError_t err = last_launch();

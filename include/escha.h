@@ -141,7 +141,8 @@ ESCHA_API int escha_route_topk(const float* logits, int32_t n_tokens, int32_t n_
  *   logits    out: fp32 [n_tokens][n_experts]
  * hidden % 32 == 0; 1 <= n_experts <= 1024; n_tokens >= 0 (0: no-op).
  * workspace >= escha_router_workspace_bytes(n_tokens, hidden, n_experts)
- * (partial sums when small calls split the inputs; may be 0 bytes).
+ * (partial sums when calls of more than 8 tokens split the inputs; 0 bytes
+ * up to 8 tokens).
  */
 ESCHA_API size_t escha_router_workspace_bytes(int32_t n_tokens, int32_t hidden, int32_t n_experts);
 ESCHA_API int escha_router_logits(const uint16_t* x_bf16, int32_t n_tokens, int32_t hidden,

@@ -150,10 +150,11 @@ def test_router_logits_validation(lib):
     assert f(None, 1, 2048, FAKE, 256, FAKE, None, 0, None) == -1
     assert f(FAKE + 2, 1, 2048, FAKE, 256, FAKE, None, 0, None) == -7  # misaligned x
     assert f(None, 0, 2048, None, 256, None, None, 0, None) == 0     # zero tokens: no-op
-    # a single token splits the inputs: partial sums need the workspace
-    need = wsb(1, 2048, 256)
-    assert need >= 32 * 256 * 4
-    assert f(FAKE, 1, 2048, FAKE, 256, FAKE, FAKE, need - 1, None) == -4
+    # 64 tokens split the inputs: partial sums need the workspace
+    need = wsb(64, 2048, 256)
+    assert need >= 32 * 64 * 256 * 4
+    assert f(FAKE, 64, 2048, FAKE, 256, FAKE, FAKE, need - 1, None) == -4
+    assert wsb(8, 2048, 256) == 0  # up to 8 tokens: one wave per expert, no partial sums
     assert wsb(4096, 2048, 256) >= 2 * 4096 * 256 * 4
     assert wsb(1, 48, 256) == 0
 

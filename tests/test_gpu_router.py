@@ -60,7 +60,7 @@ def _check_logits(got, x, gate, rows=None):
     return ref
 
 
-@pytest.mark.parametrize("T,H,E", [(1, 2048, 256), (3, 2048, 256), (64, 2048, 256),
+@pytest.mark.parametrize("T,H,E", [(1, 2048, 256), (3, 2048, 256), (8, 2048, 256), (9, 2048, 256), (64, 2048, 256),
                                    (37, 2048, 200), (5, 64, 8), (300, 96, 33)])
 def test_router_logits_vs_oracle(escha, T, H, E):
     announce(f"router_logits T={T} H={H} E={E}")
