@@ -302,7 +302,7 @@ def router_workload(args, log):
         gates = [torch.from_numpy(synth.router_gate(80, E, H, layer=l).view(np.int16)).cuda()
                  for l in range(args.distinct_layers)]
         logits = torch.empty(T, E, dtype=torch.float32, device="cuda")
-        nbytes = escha._lib.escha_router_workspace_bytes(T, H, E)
+        nbytes = escha.escha_router_workspace_bytes(T, H, E)
         ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
         for i in range(args.warmup):
             escha.escha_router_logits(x, gates[i % len(gates)], out=logits, workspace=ws)

@@ -229,6 +229,10 @@ def escha_route_topk(logits: torch.Tensor, top_k: int, stream=None):
     return ids, w
 
 
+def escha_router_workspace_bytes(n_tokens: int, hidden: int, n_experts: int) -> int:
+    return int(_lib.escha_router_workspace_bytes(n_tokens, hidden, n_experts))
+
+
 def escha_router_logits(x_bf16: torch.Tensor, gate_f16: torch.Tensor, out: torch.Tensor | None = None,
                         workspace: torch.Tensor | None = None, stream=None):
     """x bf16 [T][H] (bf16 or 16-bit integer view), gate fp16 [E][H] -> fp32
@@ -239,7 +243,7 @@ def escha_router_logits(x_bf16: torch.Tensor, gate_f16: torch.Tensor, out: torch
         raise ValueError(f"gate has {H2} inputs, x has {H}")
     if out is None:
         out = torch.empty(T, E, dtype=torch.float32, device=x_bf16.device)
-    nbytes = _lib.escha_router_workspace_bytes(T, H, E)
+    nbytes = escha_router_workspace_bytes(T, H, E)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_bf16.device)
     _check(_lib.escha_router_logits(_ptr(x_bf16, _U16, "x_bf16"), T, H, _ptr(gate_f16, _U16, "gate_f16"),
