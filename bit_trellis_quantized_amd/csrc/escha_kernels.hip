@@ -765,7 +765,7 @@ int router_ksplit(int T, int H, int E) {
   const int tiles = ((E + 31) / 32) * ((T + 31) / 32);
   const int nch = H / 32;
   int ks = 1;
-  while (ks < 32 && nch % (2 * ks) == 0 && tiles * 2 * ks <= 2048) ks *= 2;
+  while (ks < 32 && nch % (2 * ks) == 0 && tiles * 2 * ks <= 4096) ks *= 2;
   return ks;
 }
 

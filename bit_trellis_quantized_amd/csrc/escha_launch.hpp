@@ -203,8 +203,9 @@ struct RouterArgs {
   float* logits;
   float* part;
 };
-// input slices for a call: a power of two <= 32 dividing H / 32, as many as
-// keep the grid within 2048 waves
+// input slices for a call: 1 up to 8 tokens (one wave per expert); else a
+// power of two <= 32 dividing H / 32, as many as keep the grid within 4096
+// waves
 int router_ksplit(int T, int H, int E);
 hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s);
 // inv (nullable): pair -> sorted index, -1 for a pair with an out-of-range id
