@@ -5,15 +5,21 @@ Workload: the full expert stack streaming from HBM -- 40 MoE layers x 256
 experts at the Qwen3.6-35B-A3B expert shapes (gate_up 2048->1024 at K=2,
 down 512->2048 at K=3, 9.40 GB of packed codes), decode at batch 1 (default,
 the line's ``value``), then batches 8 and 64 on the same resident stack
-(``batches``). One step = one batch of tokens through every layer: router top-8 for
-all layers, then per layer gate_up -> SiLU*up -> down -> weighted combine ->
-RMSNorm -> bf16 input of the next layer. Inputs are seeded synthetic data
-(random code words, sign/scale vectors with prune masks, N(0,1) activations
-and router logits); a pool of independent steps is cycled so that no step
-reuses the previous steps' experts out of the 256 MB Infinity Cache.
+(``batches``). One step = one batch of tokens through every layer: router
+top-8 for all layers, then per layer gate_up -> SiLU*up -> down -> weighted
+combine -> RMSNorm -> bf16 input of the next layer. Inputs are seeded
+synthetic data (random code words, sign/scale vectors with prune masks,
+N(0,1) activations and router logits); a pool of independent steps is cycled
+so that no step reuses the previous steps' experts out of the 256 MB
+Infinity Cache.
+
+The single-layer configurations run next on the same resident layers (each
+call on another of the 40 layers): one layer at batch 1, one layer at 64
+tokens with Zipf(1.1) routing, and a 4096-token prefill chunk (``configs``).
 
 Prints one JSON line. ``cpu_baseline`` times the CPU oracle (test
-infrastructure, fp64, plain loops) on one token of the same workload.
+infrastructure, fp64, plain loops) on one token of the stack, and on the
+single-layer configurations (config 5 on its first 256 tokens).
 """
 from __future__ import annotations
 
@@ -45,29 +51,44 @@ VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 WEIGHTS_PER_PAIR = 2048 * 1024 + 512 * 2048  # 3,145,728
 
 
-# The one-launch kernel's measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE,
-# scaled by a plain copy's readings) and the hash of the sources it was taken
-# with; reported only while the sources still hash to that value.
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "stack_decode_b1_flow_traffic.txt")
-KERNEL_SOURCES = ["escha_stack.hip", "escha_mfma.hpp", "escha_device.hpp", "escha_stream.hpp",
-                  "escha_launch.hpp"]
+# Measured HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE per
+# dispatch, scaled by what the counters read for a plain copy of known size)
+# and the hash of the kernel sources it was taken with; a figure is reported
+# only while the sources still hash to the recorded value.
+STACK_SOURCES = ["escha_stack.hip", "escha_mfma.hpp", "escha_device.hpp", "escha_stream.hpp",
+                 "escha_launch.hpp"]
+GROUPED_SOURCES = ["escha_grouped.hip", "escha_mfma.hpp", "escha_device.hpp", "escha_launch.hpp"]
+STREAM_SOURCES = ["escha_kernels.hip", "escha_stream.hpp", "escha_device.hpp", "escha_launch.hpp"]
+TRAFFIC_PROFILES = {
+    "stack_b1": ("stack_decode_b1_flow_traffic.txt", STACK_SOURCES),
+    "stack_b8": ("stack_decode_b8_flow_traffic.txt", STACK_SOURCES),
+    "stack_b64": ("stack_decode_b64_grouped_traffic.txt", GROUPED_SOURCES),
+    "layer_cfg2": ("layer_cfg2_stream_traffic.txt", STREAM_SOURCES),
+    "layer_cfg3": ("layer_cfg3_small_traffic.txt", GROUPED_SOURCES),
+    "layer_cfg5": ("prefill_4096_grouped_traffic.txt", GROUPED_SOURCES),
+}
 
 
-def measured_traffic():
+def sources_hash(files) -> str:
     import hashlib
-    import re
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "bit_trellis_quantized_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(key: str):
+    import re
+    name, files = TRAFFIC_PROFILES[key]
     try:
-        with open(TRAFFIC_PROFILE) as fh:
+        with open(os.path.join(ROOT, "profiles", name)) as fh:
             text = fh.read()
     except OSError:
         return None
     want = re.search(r"kernel_sources_sha256_16: ([0-9a-f]+)", text)
     val = re.search(r"traffic_bytes_per_launch: ([0-9]+)", text)
-    if not want or not val or want.group(1) != h.hexdigest()[:16]:
+    if not want or not val or want.group(1) != sources_hash(files):
         return None
     return int(val.group(1))
 
@@ -88,6 +109,9 @@ def parse():
                     help="stack: further decode batches timed after the main one on the same "
                          "resident stack and reported under 'batches' (empty: none)")
     ap.add_argument("--also-steps", type=int, default=20, help="timed steps of each further batch")
+    ap.add_argument("--configs", default="2,3,5",
+                    help="single-layer configurations timed after the stack on its resident layers "
+                         "(2: batch-1 decode, 3: 64 tokens Zipf, 5: 4096-token prefill; empty: none)")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -121,6 +145,7 @@ class Hip:
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def event(self) -> int:
         ev = ctypes.c_void_p()
@@ -128,6 +153,11 @@ class Hip:
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         return ev.value
+
+    def record(self, ev: int, stream: int):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = ctypes.c_float()
@@ -159,102 +189,73 @@ def build_stack(escha, synth, n_layers, log):
     return layers
 
 
+def cpu_info():
+    """Host cores and CPU model of the machine the bench runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count() or 1, model
+
+
 def cpu_baseline(synth, n_layers, x0, logits, threads, log):
-    """The oracle on one token through every layer (timed: oracle calls only)."""
+    """The oracle (fp64 reconstruct-then-matmul, as it stands) timed on the
+    host: config 4 at batch 1 (one token through every layer: the line's
+    unit), and configs 1, 2, 3 and config 5's 256-token subset. Timed: the
+    oracle calls only (input generation is not)."""
     import oracle
     oracle.lib()
-    x = x0[:1]
-    t_oracle = 0.0
-    first = None
+    k = synth.TOP_K
+    out = {}
     used = 0
-    for l in range(n_layers):
-        ids, w = oracle.route_topk(logits[l, :1], synth.TOP_K)
-        L = synth.layer_tensors(SEED, l, experts=ids.ravel())
+
+    def timed(fn):
         t = time.perf_counter()
-        y = oracle.moe_layer(L, x, ids, w.astype(np.float32), n_threads=threads)
-        x_next = oracle.rmsnorm_bf16(y) if l < n_layers - 1 else x
-        t_oracle += time.perf_counter() - t
+        r = fn()
+        return r, time.perf_counter() - t
+
+    # config 4, batch 1: the 40-layer chain
+    x = x0[:1]
+    t4 = 0.0
+    first = None
+    for l in range(n_layers):
+        ids, w = oracle.route_topk(logits[l, :1], k)
+        L = synth.layer_tensors(SEED, l, experts=ids.ravel())
+        (y, dt) = timed(lambda: oracle.moe_layer(L, x, ids, w.astype(np.float32), n_threads=threads))
+        xn, dt2 = timed(lambda: oracle.rmsnorm_bf16(y) if l < n_layers - 1 else x)
+        t4 += dt + dt2
         if first is None:
             first = (x, ids, w.astype(np.float32), y)
-        x = x_next
+        x = xn
         used = max(used, min(threads, len(set(ids.ravel().tolist()))))
-    log(f"oracle: {n_layers} layers x 1 token in {t_oracle:.2f}s")
-    return t_oracle, used, first
+    out["4"] = {"tokens_per_s": round(1.0 / t4, 4), "s": round(t4, 2),
+                "sample": f"1 token through all {n_layers} layers"}
+    log(f"oracle config 4: {n_layers} layers x 1 token in {t4:.2f}s")
 
+    # config 1: one 256x256 K=2 matrix, one token
+    code, rin, rout = synth.single_proj(1, 256, 256, 2)
+    x1 = synth.activations(1, 1, 256)
+    reps = 20
+    _, t1 = timed(lambda: [oracle.expert_gemv(code, rin, rout, 256, 256, 2, x1) for _ in range(reps)])
+    out["1"] = {"us_per_call": round(t1 / reps * 1e6, 1), "sample": f"{reps} calls"}
 
-def layer_workload(args, log):
-    """One MoE layer per step (configs 2, 3 or 5), cycling over distinct layers."""
-    import torch
-    from bit_trellis_quantized_amd import escha, synth
-
-    cfg = args.config
-    T = {2: 1, 3: 64, 5: 4096}[cfg]
-    entry = args.entry or ("prefill" if cfg == 5 else "decode")
-    fn = escha.escha_moe_layer_prefill if entry == "prefill" else escha.escha_moe_layer_decode
-    NLw, k = args.distinct_layers, synth.TOP_K
-    hip = Hip()
-
-    def dev(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
-
-    layers = []
-    for l in range(NLw):
-        L = synth.layer_tensors(cfg, l)
-        layers.append(escha.MoeLayer(escha.Proj(dev(L["gu_code"]), dev(L["gu_rin"]), dev(L["gu_rout"])),
-                                     escha.Proj(dev(L["dn_code"]), dev(L["dn_rin"]), dev(L["dn_rout"])), k))
-    log(f"{NLw} layers resident")
-    ws = torch.empty(escha.escha_moe_workspace_bytes(layers[0], T, entry == "prefill"),
-                     dtype=torch.uint8, device="cuda")
-    pool = []
-    for l in range(NLw):
-        x = synth.activations(cfg, T, synth.HIDDEN, layer=l)
-        logits = (synth.zipf_logits(cfg, T, layer=l) if cfg == 3 else synth.normal_logits(cfg, T, layer=l))
-        pool.append(dict(x=dev(x), logits=torch.from_numpy(logits).cuda(),
-                         y=torch.empty(T, synth.HIDDEN, dtype=torch.float32, device="cuda"),
-                         ev=(hip.event(), hip.event())))
-
-    def step(i):
-        p = pool[i % NLw]
-        ids, w = escha.escha_route_topk(p["logits"], k)
-        p["ids"], p["w"] = ids, w
-        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        hip.lib.hipEventRecord(ctypes.c_void_p(p["ev"][0]), stream)
-        fn(layers[i % NLw], p["x"], ids, w, out=p["y"], workspace=ws)
-        hip.lib.hipEventRecord(ctypes.c_void_p(p["ev"][1]), stream)
-
-    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start, stop = hip.event(), hip.event()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    t_wall = time.perf_counter()
-    hip.lib.hipEventRecord(ctypes.c_void_p(start), stream)
-    for i in range(args.steps):
-        step(i)
-    hip.lib.hipEventRecord(ctypes.c_void_p(stop), stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = hip.elapsed_ms(start, stop) / args.steps
-    ran = [p for p in pool if "ids" in p]  # entries some step reached
-    layer_ms = float(np.mean([hip.elapsed_ms(*p["ev"]) for p in ran]))
-    distinct = np.mean([len(set(p["ids"].cpu().numpy().ravel().tolist())) for p in ran])
-    code_bytes = distinct * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR)
-    flops = 2.0 * T * k * (2048 * 1024 + 512 * 2048)
-    out = {
-        "metric": "MoE-layer decode tokens/s at batch 1/8/64 + achieved HBM GB/s vs peak",
-        "value": round(T / (ms / 1e3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp16-decode/fp32-acc",
-        "data": "synthetic", "config": {"workload": f"one MoE layer, config {cfg}, T={T}, entry={entry}, "
-                                                    f"{NLw} distinct layers cycled"},
-        "layer_us": round(layer_ms * 1e3, 2),
-        "code_gbs": round(code_bytes / (layer_ms / 1e3) / 1e9, 1),
-        "distinct_experts": float(distinct),
-        "tflops": round(flops / (layer_ms / 1e3) / 1e12, 2),
-        "wall_ms_per_step": round(t_wall / args.steps * 1e3, 4),
-    }
-    print(json.dumps(out), flush=True)
+    # configs 2, 3 and config 5's first 256 tokens: one layer each
+    for cfg, T, name in ((2, 1, "2"), (3, 64, "3"), (5, 256, "5_subset256")):
+        lg = synth.zipf_logits(cfg, T) if cfg == 3 else synth.normal_logits(cfg, 4096 if cfg == 5 else T)[:T]
+        ids, w = oracle.route_topk(lg, k)
+        L = synth.layer_tensors(cfg, 0, experts=ids.ravel())
+        xc = synth.activations(cfg, 4096 if cfg == 5 else T, synth.HIDDEN)[:T]
+        _, dt = timed(lambda: oracle.moe_layer(L, xc, ids, w.astype(np.float32), n_threads=threads))
+        used = max(used, min(threads, len(set(ids.ravel().tolist()))))
+        out[name] = {"tokens_per_s": round(T / dt, 3), "s": round(dt, 2), "tokens": T,
+                     "distinct_experts": len(set(ids.ravel().tolist()))}
+        log(f"oracle config {name}: {T} tokens in {dt:.2f}s")
+    return t4, used, first, out
 
 
 def copy_workload(args, log):
@@ -263,7 +264,6 @@ def copy_workload(args, log):
     counters (a copy of B bytes reads B and writes B)."""
     import torch
     hip = Hip()
-    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     n = args.copy_mib << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     src.random_(0, 256)
@@ -293,7 +293,6 @@ def router_workload(args, log):
     import torch
     from bit_trellis_quantized_amd import escha, synth
     hip = Hip()
-    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     H, E = synth.HIDDEN, synth.N_EXPERTS
     out = {"workload": "router logits", "hidden": H, "experts": E, "steps": args.steps,
            "warmup": args.warmup, "cases": {}}
@@ -326,6 +325,287 @@ def router_workload(args, log):
     print(json.dumps(out), flush=True)
 
 
+def roofline_hbm(kernel, launch_bytes, launch_ms, traffic, samples):
+    achieved = launch_bytes / (launch_ms / 1e3) / 1e9
+    decodes = launch_bytes / (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR) * WEIGHTS_PER_PAIR
+    valu = decodes * DECODE_OPS_PER_WEIGHT / (launch_ms / 1e3) / 1e12
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "bytes_per_launch": int(launch_bytes), "avg_launch_us": round(launch_ms * 1e3, 3),
+            "samples": samples,
+            "valu": {"bound": "alu", "achieved": round(valu, 2), "peak": round(VALU_PEAK_TOPS, 2),
+                     "unit": "T lane-op/s", "frac": round(valu / VALU_PEAK_TOPS, 4),
+                     "decodes_per_launch": int(decodes), "ops_per_weight": DECODE_OPS_PER_WEIGHT}}
+
+
+def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
+    """Time `steps` decode steps of batch T through the resident stack (after
+    `warmup` untimed ones). Probe events around the measured kernels are
+    recorded inside the timed graph replays (external event nodes)."""
+    import torch
+    NL, R = len(stack.layers), args.pool
+    hidden, E, k = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K
+    path = args.path if args.path != "auto" else ("flow" if T < 16 else "layered")
+    one_launch = path == "flow"
+    n_probe = 2 if one_launch else 2 * NL
+
+    pool = []
+    for r in range(R):
+        x0, logits = synth.stack_token_inputs(SEED, NL, T, r)
+        pool.append(dict(
+            x0_host=x0, logits_host=logits,
+            x0=torch.from_numpy(x0.view(np.int16).copy()).cuda(),
+            logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
+            y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
+            ws=torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
+            probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
+        ))
+
+    def step(p, probes=True):
+        ids, w = escha.escha_route_topk(p["logits"], k)
+        p["ids"], p["w"] = ids, w  # keep the graph's buffers alive
+        ev = p["probes"] if probes else None
+        if one_launch:
+            escha.escha_moe_stack_decode_persistent(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
+                                                    out=p["y"], workspace=p["ws"],
+                                                    probe_events=ev, check_status=False)
+        else:
+            escha.escha_moe_stack_decode(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
+                                         out=p["y"], workspace=p["ws"], probe_events=ev)
+
+    # probe events go into the captured graphs as event-record nodes; if the
+    # runtime refuses that, the graphs are captured without them and the
+    # probes are timed on eager steps after the timed region
+    use_graph = not args.no_graph
+    graphs = []
+    probe_in_graph = use_graph and not args.no_probe
+    if use_graph:
+        for p in pool:
+            step(p)  # warm the allocator outside capture
+        torch.cuda.synchronize()
+        for attempt in ((True, False) if probe_in_graph else (False,)):
+            try:
+                graphs = []
+                for p in pool:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        step(p, probes=attempt)
+                    graphs.append(g)
+                torch.cuda.synchronize()
+                probe_in_graph = attempt
+                break
+            except Exception as exc:
+                log(f"graph capture {'with' if attempt else 'without'} probe nodes failed ({exc})")
+                graphs = []
+        if not graphs:
+            use_graph = probe_in_graph = False
+            log("timing eager launches")
+
+    def run(i):
+        if use_graph:
+            graphs[i % R].replay()
+        else:
+            step(pool[i % R])
+
+    for i in range(warmup):
+        run(i)
+    torch.cuda.synchronize()
+    start, stop = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    t_wall = time.perf_counter()
+    hip.record(start, stream)
+    for i in range(steps):
+        run(i)
+        pool[i % R]["ran"] = True  # its probes were stamped by a timed step
+    hip.record(stop, stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = hip.elapsed_ms(start, stop) / steps
+    ran = [p for p in pool if p.get("ran")]
+    if use_graph and not probe_in_graph and not args.no_probe:
+        # eager steps with plain probe records, after the timed region
+        for p in ran:
+            step(p)
+        torch.cuda.synchronize()
+
+    # probe durations of each pool entry's last timed step: the one-launch
+    # kernel, or each layer's launches
+    probe_ms, per_step_probe = [], []
+    if not args.no_probe:
+        for p in ran:
+            ms = [hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]) for j in range(n_probe // 2)]
+            probe_ms += ms
+            per_step_probe.append(sum(ms))
+    probe_avg_ms = float(np.mean(probe_ms)) if probe_ms else None
+    # the probed kernels run inside the step, so their time cannot exceed it
+    probe_ok = bool(per_step_probe) and max(per_step_probe) <= ms_per_step * 1.02
+
+    distinct = []
+    for p in ran:
+        ids = p["ids"].view(NL, T * k).cpu().numpy()
+        distinct.append(sum(len(set(row.tolist())) for row in ids))
+    code_bytes_step = int(np.mean(distinct) * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR))
+    tok_s = T / (ms_per_step / 1e3)
+
+    roofline = None
+    if probe_avg_ms and probe_ok:
+        launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
+        if one_launch:
+            kernel = "k_stack_flow<2,3> (one launch: every layer's tasks)"
+        elif T < 16:
+            kernel = "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
+        else:
+            kernel = ("one layer's grouped launches (k_small_gate_up + k_small_down + k_combine_next: "
+                      "combine, RMSNorm and the next layer's input rotation; the pairs of all layers "
+                      "are grouped once per step)")
+        key = {1: "stack_b1", 8: "stack_b8", 64: "stack_b64"}.get(T)
+        traffic = measured_traffic(key) if key else None
+        roofline = roofline_hbm(kernel, launch_bytes, probe_avg_ms, traffic, len(probe_ms))
+    status = None
+    if one_launch:  # every timed call completed (no wait gave up)
+        status = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pool))
+    if roofline is not None:
+        roofline["probe"] = ("HIP events recorded as graph nodes in the timed replays" if probe_in_graph
+                             else "HIP events around eager launches after the timed replays"
+                             if use_graph else "HIP events in the timed (eager) steps")
+    res = dict(T=T, path=path, one_launch=one_launch, use_graph=use_graph, ms_per_step=ms_per_step,
+               tok_s=tok_s, gbs=code_bytes_step / (ms_per_step / 1e3) / 1e9, t_wall=t_wall,
+               steps=steps, code_bytes_step=code_bytes_step, roofline=roofline, status=status,
+               probe_ok=probe_ok,
+               probe_step_ms=round(float(max(per_step_probe)), 5) if per_step_probe else None)
+    return res, pool
+
+
+LAYER_CONFIGS = {
+    2: dict(T=1, prefill=False, logits="normal",
+            name="one MoE layer, batch-1 decode (streaming kernels)"),
+    3: dict(T=64, prefill=False, logits="zipf",
+            name="one MoE layer, 64 tokens, Zipf s=1.1 routing (grouped small-tile kernels)"),
+    5: dict(T=4096, prefill=True, logits="normal",
+            name="one MoE layer, 4096-token prefill chunk (grouped MFMA GEMMs)"),
+}
+
+
+def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, n_inputs=8):
+    """One MoE layer call per step (config 2, 3 or 5), each step on the next
+    of the given resident layers; the calls of a sweep over the layers are
+    captured in one graph. Probe events around each call's gate_up and down
+    projection kernels (escha_probe_events_set) give the kernels' time."""
+    import torch
+    c = LAYER_CONFIGS[cfg]
+    T, prefill = c["T"], c["prefill"]
+    k = synth.TOP_K
+    fn = escha.escha_moe_layer_prefill if prefill else escha.escha_moe_layer_decode
+    NLc = len(layers)
+    inputs = []
+    for i in range(n_inputs):
+        x = synth.activations(cfg, T, synth.HIDDEN, layer=i)
+        lg = synth.zipf_logits(cfg, T, layer=i) if c["logits"] == "zipf" else synth.normal_logits(cfg, T, layer=i)
+        inputs.append(dict(x=torch.from_numpy(x.view(np.int16).copy()).cuda(),
+                           logits=torch.from_numpy(lg).cuda()))
+    ws = torch.zeros(max(escha.escha_moe_workspace_bytes(layers[0], T, prefill), 1), dtype=torch.uint8,
+                     device="cuda")
+    y = torch.empty(T, synth.HIDDEN, dtype=torch.float32, device="cuda")
+    probe_ev = [(hip.event(), hip.event()) for _ in range(NLc)]
+    routed = [None] * NLc
+
+    def sweep(probes=True):
+        for l in range(NLc):
+            inp = inputs[l % n_inputs]
+            ids, w = escha.escha_route_topk(inp["logits"], k)
+            routed[l] = (ids, w)
+            escha.escha_probe_events_set(probe_ev[l] if probes else None)
+            try:
+                fn(layers[l], inp["x"], ids, w, out=y, workspace=ws)
+            finally:
+                escha.escha_probe_events_set(None)
+
+    sweep()  # warm the allocator outside capture
+    torch.cuda.synchronize()
+    use_graph = not args.no_graph
+    probe_in_graph = use_graph
+    g = None
+    if use_graph:
+        for attempt in (True, False):
+            try:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    sweep(probes=attempt)
+                torch.cuda.synchronize()
+                probe_in_graph = attempt
+                break
+            except Exception as exc:
+                log(f"config {cfg}: graph capture {'with' if attempt else 'without'} probe nodes "
+                    f"failed ({exc})")
+                g = None
+        if g is None:
+            use_graph = probe_in_graph = False
+    n_sweeps = max(1, -(-steps // NLc))
+    for _ in range(max(1, warmup // NLc)):
+        g.replay() if use_graph else sweep()
+    torch.cuda.synchronize()
+    start, stop = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    hip.record(start, stream)
+    for _ in range(n_sweeps):
+        g.replay() if use_graph else sweep()
+    hip.record(stop, stream)
+    torch.cuda.synchronize()
+    calls = n_sweeps * NLc
+    ms = hip.elapsed_ms(start, stop) / calls
+    if use_graph and not probe_in_graph:
+        sweep()  # eager calls with plain probe records, after the timed region
+        torch.cuda.synchronize()
+    proj_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in probe_ev]))
+    distinct = float(np.mean([len(set(ids.cpu().numpy().ravel().tolist())) for ids, _ in routed]))
+    code_bytes = distinct * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR)
+    entry = {"workload": c["name"], "tokens": T, "value": round(T / (ms / 1e3), 2), "unit": "tokens/s",
+             "us_per_layer": round(ms * 1e3, 3), "calls": calls, "graph": use_graph,
+             "distinct_experts": round(distinct, 2), "layers_cycled": NLc,
+             "probe_ok": proj_ms <= ms * 1.02,
+             "probe": ("HIP events recorded as graph nodes in the timed replays" if probe_in_graph
+                       else "HIP events around eager calls after the timed replays" if use_graph
+                       else "HIP events in the timed (eager) calls")}
+    if not entry["probe_ok"]:
+        return entry
+    if prefill:
+        flops = 2.0 * T * k * WEIGHTS_PER_PAIR
+        achieved = flops / (proj_ms / 1e3) / 1e12
+        entry["roofline"] = {
+            "kernel": "k_grouped_gate_up + k_grouped_down (fp16 MFMA 32x32x16, fp32 accumulate)",
+            "bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
+            "frac": round(achieved / 2500.0, 4), "traffic": measured_traffic("layer_cfg5"),
+            "flops_per_launch": flops, "avg_launch_us": round(proj_ms * 1e3, 3), "samples": NLc,
+            "code_bytes": int(code_bytes), "code_gbs": round(code_bytes / (proj_ms / 1e3) / 1e9, 1)}
+    else:
+        kernel = ("k_in_partial + k_down_partial (streaming decode)" if T < 16 else
+                  "k_small_gate_up + k_small_down (small-tile grouped decode, MFMA 16x16x32)")
+        entry["roofline"] = roofline_hbm(kernel, code_bytes, proj_ms,
+                                         measured_traffic("layer_cfg2" if T < 16 else "layer_cfg3"), NLc)
+    return entry
+
+
+def layer_workload(args, log):
+    """One configuration alone, on freshly generated layers (for profiling)."""
+    import torch
+    from bit_trellis_quantized_amd import escha, synth
+    hip = Hip()
+    cfg = args.config
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    layers = []
+    for l in range(args.distinct_layers):
+        L = synth.layer_tensors(cfg, l)
+        layers.append(escha.MoeLayer(escha.Proj(dev(L["gu_code"]), dev(L["gu_rin"]), dev(L["gu_rout"])),
+                                     escha.Proj(dev(L["dn_code"]), dev(L["dn_rin"]), dev(L["dn_rout"])),
+                                     synth.TOP_K))
+    log(f"{len(layers)} layers resident")
+    entry = time_layer_config(args, escha, synth, hip, layers, cfg, args.steps, args.warmup, log)
+    print(json.dumps(entry), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -349,204 +629,95 @@ def main():
     if args.workload == "router":
         router_workload(args, log)
         return
-    NL, R = args.layers, args.pool
+    NL = args.layers
     hidden, E, k = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K
 
     layers = build_stack(escha, synth, NL, log)
     stack = escha.Stack(layers)
     hip = Hip()
 
-    def time_stack(T, steps, warmup):
-        """Time `steps` decode steps of batch T through the stack (after
-        `warmup` untimed ones); returns the measurements and the pool."""
-        path = args.path if args.path != "auto" else ("flow" if T < 16 else "layered")
-        one_launch = path == "flow"
-        stack_fn = (escha.escha_moe_stack_decode_persistent if one_launch
-                    else escha.escha_moe_stack_decode)
-        n_probe = 2 if one_launch else 2 * NL
-
-        # a pool of independent steps, each with its own buffers (so each can be
-        # captured in its own graph)
-        pool = []
-        for r in range(R):
-            x0, logits = synth.stack_token_inputs(SEED, NL, T, r)
-            pool.append(dict(
-                x0_host=x0, logits_host=logits,
-                x0=torch.from_numpy(x0.view(np.int16).copy()).cuda(),
-                logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
-                y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
-                ws=torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
-                probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
-            ))
-
-        def step(p):
-            ids, w = escha.escha_route_topk(p["logits"], k)
-            p["ids"], p["w"] = ids, w  # keep the graph's buffers alive
-            stack_fn(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
-                     out=p["y"], workspace=p["ws"], probe_events=p["probes"])
-
-        use_graph = not args.no_graph
-        graphs = []
-        if use_graph:
-            try:
-                for p in pool:
-                    step(p)  # warm the allocator outside capture
-                torch.cuda.synchronize()
-                for p in pool:
-                    g = torch.cuda.CUDAGraph()
-                    with torch.cuda.graph(g):
-                        step(p)
-                    graphs.append(g)
-                torch.cuda.synchronize()
-            except Exception as exc:  # capture unsupported: measure eagerly
-                log(f"graph capture failed ({exc}); timing eager launches")
-                use_graph, graphs = False, []
-
-        def run(i):
-            if use_graph:
-                graphs[i % R].replay()
-            else:
-                step(pool[i % R])
-
-        for i in range(warmup):
-            run(i)
-        torch.cuda.synchronize()
-        start, stop = hip.event(), hip.event()
-        stream = torch.cuda.current_stream().cuda_stream
-        hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-        t_wall = time.perf_counter()
-        hip.lib.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream))
-        for i in range(steps):
-            run(i)
-        hip.lib.hipEventRecord(ctypes.c_void_p(stop), ctypes.c_void_p(stream))
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
-        ms_total = hip.elapsed_ms(start, stop)
-        ms_per_step = ms_total / steps
-
-        # probe durations of each pool entry's last step: the one-launch kernel
-        # (one per step) or each layer's three launches
-        probe_ms = []
-        if not args.no_probe:
-            for p in pool:
-                if "ids" not in p:
-                    continue
-                for j in range(n_probe // 2):
-                    probe_ms.append(hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]))
-        probe_avg_ms = float(np.mean(probe_ms)) if probe_ms else None
-
-        # algorithmic bytes: the packed codes of the distinct experts each layer
-        # routes to (at batch 1 every one of the 8 is distinct), averaged over the pool
-        distinct = []
-        for p in pool:
-            if "ids" not in p:  # a pool entry no step reached (fewer steps than entries)
-                continue
-            ids = p["ids"].view(NL, T * k).cpu().numpy()
-            distinct.append(sum(len(set(row.tolist())) for row in ids))
-        code_bytes_step = int(np.mean(distinct) * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR))
-        tok_s = T / (ms_per_step / 1e3)
-        gbs = code_bytes_step / (ms_per_step / 1e3) / 1e9
-
-        roofline = None
-        if probe_avg_ms:
-            launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
-            achieved = launch_bytes / (probe_avg_ms / 1e3) / 1e9
-            kernel = ("k_stack_flow<2,3> (one launch: every layer's tasks)" if one_launch else
-                      "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
-                      if T < 16 else
-                      "one layer's grouped launches (k_small_gate_up + k_small_down + "
-                      "k_combine_next: combine, RMSNorm and the next layer's input rotation; "
-                      "the pairs of all layers are grouped once per step)")
-            roofline = {"kernel": kernel, "bound": "hbm",
-                        "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic() if (one_launch and T == 1) else None,
-                        "bytes_per_launch": int(launch_bytes),
-                        "avg_launch_us": round(probe_avg_ms * 1e3, 3),
-                        "samples": len(probe_ms)}
-            decodes = launch_bytes / (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR) * WEIGHTS_PER_PAIR
-            valu = decodes * DECODE_OPS_PER_WEIGHT / (probe_avg_ms / 1e3) / 1e12
-            roofline["valu"] = {"bound": "alu", "achieved": round(valu, 2), "peak": round(VALU_PEAK_TOPS, 2),
-                                "unit": "T lane-op/s", "frac": round(valu / VALU_PEAK_TOPS, 4),
-                                "decodes_per_launch": int(decodes),
-                                "ops_per_weight": DECODE_OPS_PER_WEIGHT}
-
-        res = dict(T=T, path=path, one_launch=one_launch, use_graph=use_graph,
-                   ms_per_step=ms_per_step, tok_s=tok_s, gbs=gbs, t_wall=t_wall, steps=steps,
-                   code_bytes_step=code_bytes_step, roofline=roofline)
-        return res, pool
-
     T = args.batch
-    main_res, pool = time_stack(T, args.steps, args.warmup)
-    path, one_launch, use_graph = main_res["path"], main_res["one_launch"], main_res["use_graph"]
-    ms_per_step, tok_s, gbs = main_res["ms_per_step"], main_res["tok_s"], main_res["gbs"]
-    t_wall, code_bytes_step, roofline = main_res["t_wall"], main_res["code_bytes_step"], main_res["roofline"]
+    main_res, pool = time_stack(args, escha, synth, hip, stack, T, args.steps, args.warmup, log)
+    log(f"batch {T}: {main_res['tok_s']:.1f} tokens/s")
+    checks = {"probe_ok": main_res["probe_ok"], "probe_step_ms": main_res["probe_step_ms"]}
+    if main_res["status"] is not None:
+        checks["status"] = main_res["status"]
 
-    checks = {}
-    if one_launch:  # every timed call completed (no wait gave up)
-        checks["status"] = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pool))
     cpu = None
     if not args.no_cpu_baseline:
         p0 = pool[0]
-        t_cpu, cores, (x_l0, ids_l0, w_l0, y_l0) = cpu_baseline(
-            synth, NL, p0["x0_host"], p0["logits_host"], args.cpu_threads, log)
+        nproc, model = cpu_info()
+        threads = max(1, min(args.cpu_threads, nproc))
+        t_cpu, used, (x_l0, ids_l0, w_l0, y_l0), cfgs = cpu_baseline(
+            synth, NL, p0["x0_host"], p0["logits_host"], threads, log)
         # layer 0 of the same token on the GPU (the 40-layer chain itself is
         # chaotic, so outputs are compared layer by layer, not end to end)
         y_gpu = escha.escha_moe_layer_decode(
             layers[0], torch.from_numpy(x_l0.view(np.int16).copy()).cuda(),
             torch.from_numpy(ids_l0).cuda(), torch.from_numpy(w_l0).cuda()).cpu().numpy()
-        rel = float(np.linalg.norm(y_gpu - y_l0) / np.linalg.norm(y_l0))
-        checks["layer0_vs_oracle_rel_l2"] = rel
-        cpu = {"value": round(1.0 / t_cpu, 4), "unit": "tokens/s", "cores": int(cores),
+        checks["layer0_vs_oracle_rel_l2"] = float(np.linalg.norm(y_gpu - y_l0) / np.linalg.norm(y_l0))
+        cpu = {"value": round(1.0 / t_cpu, 4), "unit": "tokens/s", "cores": int(used),
                "kind": "oracle",
                "sample": f"1 token through all {NL} layers (8 experts/layer, fp64 reconstruct-"
-                         f"then-matmul); {t_cpu:.1f}s"}
+                         f"then-matmul, {threads} threads requested); {t_cpu:.1f}s",
+               "host_cpus": nproc, "cpu_model": model, "configs": cfgs}
+    del pool
 
     # the metric's other batch sizes, on the same resident stack
     batches = {}
-    del pool
     for Tb in [int(v) for v in args.also_batches.split(",") if v.strip()]:
         if Tb == T or Tb < 1:
             continue
         log(f"batch {Tb}: {args.also_steps} timed steps")
-        rb, pb = time_stack(Tb, args.also_steps, min(args.warmup, 3))
+        rb, pb = time_stack(args, escha, synth, hip, stack, Tb, args.also_steps, min(args.warmup, 3), log)
         entry = {"value": round(rb["tok_s"], 2), "unit": "tokens/s",
                  "ms_per_step": round(rb["ms_per_step"], 5), "steps": rb["steps"],
                  "path": rb["path"], "graph": rb["use_graph"],
                  "code_gbs_step": round(rb["gbs"], 1), "code_bytes_per_step": rb["code_bytes_step"],
+                 "probe_ok": rb["probe_ok"], "probe_step_ms": rb["probe_step_ms"],
                  "roofline": rb["roofline"]}
-        if rb["one_launch"]:
-            entry["status"] = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pb))
+        if rb["status"] is not None:
+            entry["status"] = rb["status"]
         batches[str(Tb)] = entry
         del pb
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
 
+    # the single-layer configurations on the same resident layers
+    configs = {}
+    for cfg in [int(v) for v in args.configs.split(",") if v.strip()]:
+        steps = {2: 400, 3: 200, 5: 40}[cfg]
+        log(f"config {cfg}: {steps} layer calls")
+        configs[str(cfg)] = time_layer_config(args, escha, synth, hip, layers, cfg, steps, NL, log)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
     out = {
         "metric": "MoE-layer decode tokens/s at batch 1/8/64 + achieved HBM GB/s vs peak",
-        "value": round(tok_s, 2),
+        "value": round(main_res["tok_s"], 2),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(main_res["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16-decode/fp32-acc",
         "data": "synthetic (seeded random trellis codes, +-1/U(0.5,2) scales with prune masks, "
-                "N(0,1) activations and router logits)",
+                "N(0,1) activations and router logits; Zipf s=1.1 routing for the 64-token layer)",
         "config": {"workload": f"expert stack streaming: {NL} layers x {E} experts, "
                                f"decode batch {T}, top-{k}, hidden {hidden}, inter 512, "
                                f"gate_up K=2 / down K=3, codes {NL * E * 917504 / 1e9:.2f} GB in HBM",
-                   "batch": T, "layers": NL, "graph": use_graph, "path": path},
-        "code_gbs_step": round(gbs, 1),
-        "code_bytes_per_step": code_bytes_step,
-        "wall_ms_per_step": round(t_wall / args.steps * 1e3, 4),
-        "roofline": roofline,
+                   "batch": T, "layers": NL, "graph": main_res["use_graph"], "path": main_res["path"]},
+        "code_gbs_step": round(main_res["gbs"], 1),
+        "code_bytes_per_step": main_res["code_bytes_step"],
+        "wall_ms_per_step": round(main_res["t_wall"] / args.steps * 1e3, 4),
+        "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "checks": checks,
         "batches": batches,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
 

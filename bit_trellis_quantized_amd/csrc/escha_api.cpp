@@ -28,6 +28,42 @@ int hip_fail(hipError_t e, const char* where) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// A probe event recorded on the stream. Under stream capture a plain record
+// is not a node of the graph (a replay would never stamp the event), so an
+// event-record node is added to the graph being captured, after the
+// stream's current capture dependencies, and becomes the new dependency.
+// A failure is returned and also cleared from the runtime's last-error
+// state, so that later launch checks do not report it again.
+hipError_t record_probe(hipEvent_t ev, hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  hipGraph_t graph = nullptr;
+  const hipGraphNode_t* deps = nullptr;
+  size_t n_deps = 0;
+  hipError_t e = hipStreamGetCaptureInfo_v2(s, &st, nullptr, &graph, &deps, &n_deps);
+  if (e == hipSuccess) {
+    if (st != hipStreamCaptureStatusActive) {
+      e = hipEventRecord(ev, s);
+    } else {
+      hipGraphNode_t node = nullptr;
+      e = hipGraphAddEventRecordNode(&node, graph, deps, n_deps, ev);
+      if (e == hipSuccess) e = hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies);
+    }
+  }
+  if (e != hipSuccess) (void)hipGetLastError();
+  return e;
+}
+
+// Events that escha_probe_events_set installs for this thread: recorded
+// right before a layer call's gate_up projection kernel and right after its
+// down projection kernel.
+thread_local hipEvent_t g_proj_probe[2] = {nullptr, nullptr};
+
+int probe_proj(int which, hipStream_t s) {
+  if (!g_proj_probe[which]) return ESCHA_OK;
+  const hipError_t e = record_probe(g_proj_probe[which], s);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "projection probe record");
+}
+
 size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 constexpr int32_t kMaxTopK = 64;
@@ -137,8 +173,10 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   a.x_out = in.x_out;
   a.partial = ws.gu_part;
   hipError_t e;
-  if (probe_before && (e = hipEventRecord(probe_before, s)) != hipSuccess)
+  if (probe_before && (e = record_probe(probe_before, s)) != hipSuccess)
     return hip_fail(e, "probe event record");
+  int rc = probe_proj(0, s);
+  if (rc) return rc;
   e = escha::launch_in_partial(a, L->gate_up.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "gate_up partial launch");
 
@@ -158,6 +196,8 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   d.partial = ws.dn_part;
   e = escha::launch_down_partial(d, L->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "down partial launch");
+  rc = probe_proj(1, s);
+  if (rc) return rc;
 
   escha::CombineArgs c{};
   c.partial = ws.dn_part;
@@ -169,7 +209,7 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   c.ss = ws.ss;
   e = escha::launch_combine(c, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
-  if (probe_after && (e = hipEventRecord(probe_after, s)) != hipSuccess)
+  if (probe_after && (e = record_probe(probe_after, s)) != hipSuccess)
     return hip_fail(e, "probe event record");
   return ESCHA_OK;
 }
@@ -203,9 +243,11 @@ struct GroupedWs {
   int32_t *hist, *base, *rank;          // grouping scratch
   int32_t *counts, *offsets, *perm, *inv;
   int32_t *t_expert, *t_row0, *t_rows, *n_tiles;
-  uint16_t* xg;  // fp16 [P][hidden]
-  uint16_t* xd;  // fp16 [P][inter]
-  float* yd;     // fp32 [P][hidden]
+  uint16_t* xg;     // fp16 [P][hidden], row i scaled by 2^xg_exp[i]
+  uint16_t* xd;     // fp16 [P][inter], 128-block c of row i scaled by 2^xd_exp[i][c]
+  float* yd;        // fp32 [P][hidden]
+  int32_t* xg_exp;  // [P]
+  int32_t* xd_exp;  // [P][inter/128]
 };
 
 // Carves the grouped workspace; with ws == nullptr only sizes it. The
@@ -241,6 +283,8 @@ size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* ou
   g.xg = (uint16_t*)take((size_t)P * L->hidden * sizeof(uint16_t));
   g.xd = (uint16_t*)take((size_t)P * L->inter * sizeof(uint16_t));
   g.yd = (float*)take((size_t)P * L->hidden * sizeof(float));
+  g.xg_exp = (int32_t*)take((size_t)P * sizeof(int32_t));
+  g.xd_exp = (int32_t*)take((size_t)P * (L->inter / 128) * sizeof(int32_t));
   if (out) *out = g;
   return off;
 }
@@ -308,7 +352,7 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   }
   if (gather) {
     escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
-                         L->top_k, g.xg};
+                         L->top_k, g.xg, g.xg_exp};
     e = escha::launch_xin_gather(ga, P, s);
     if (e != hipSuccess) return hip_fail(e, "input gather launch");
   }
@@ -319,6 +363,8 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   gu.hidden = L->hidden;
   gu.inter = L->inter;
   gu.x_in = g.xg;
+  gu.x_exp_in = g.xg_exp;
+  gu.x_exp_out = g.xd_exp;
   gu.x_out = g.xd;
   gu.inter_out = inter_out;
   gu.perm = g.perm;
@@ -327,6 +373,8 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   gu.t_row0 = g.t_row0;
   gu.t_rows = g.t_rows;
   gu.n_tiles = g.n_tiles;
+  int rc = probe_proj(0, s);
+  if (rc) return rc;
   e = small ? escha::launch_small_gate_up(gu, max_tiles, L->gate_up.k_bits, s)
             : escha::launch_grouped_gate_up(gu, max_tiles, L->gate_up.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "grouped gate_up launch");
@@ -335,12 +383,16 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   dn.rout = (const uint16_t*)L->down.rout;
   dn.rin2 = nullptr;
   dn.x_in = g.xd;
+  dn.x_exp_in = g.xd_exp;
+  dn.x_exp_out = nullptr;
   dn.x_out = nullptr;
   dn.y_out = g.yd;
   dn.inter_out = nullptr;
   e = small ? escha::launch_small_down(dn, max_tiles, L->down.k_bits, s)
             : escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "grouped down launch");
+  rc = probe_proj(1, s);
+  if (rc) return rc;
   if (!combine) return ESCHA_OK;
   escha::SortedCombineArgs c{g.yd, g.inv, L->hidden, L->top_k, T, y, nullptr};
   e = escha::launch_combine_sorted(c, s);
@@ -448,6 +500,18 @@ extern "C" {
 
 const char* escha_last_error(void) { return g_err; }
 
+int escha_probe_events_set(void* const* events, int32_t n_events) {
+  if (!events || n_events == 0) {
+    g_proj_probe[0] = g_proj_probe[1] = nullptr;
+    return ESCHA_OK;
+  }
+  if (n_events != 2) return fail(ESCHA_E_ARG, "n_events=%d, must be 0 or 2", n_events);
+  if (!events[0] || !events[1]) return fail(ESCHA_E_NULL, "a probe event is NULL");
+  g_proj_probe[0] = (hipEvent_t)events[0];
+  g_proj_probe[1] = (hipEvent_t)events[1];
+  return ESCHA_OK;
+}
+
 int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t* w_f16, void* stream) {
   int rc = check_proj(w, "decode_tiles");
   if (rc) return rc;
@@ -460,6 +524,24 @@ int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t* w_f16, v
   hipError_t e = escha::launch_decode_tiles(code_e, w->in_features, w->out_features, w->k_bits,
                                             w_f16, (hipStream_t)stream);
   return e == hipSuccess ? ESCHA_OK : hip_fail(e, "decode_tiles launch");
+}
+
+int escha_decode_tiles_layout(const escha_proj_t* w, int32_t expert, int32_t layout, uint16_t* w_f16,
+                              void* stream) {
+  if (layout == ESCHA_LAYOUT_QUARTER) return escha_decode_tiles(w, expert, w_f16, stream);
+  int rc = check_proj(w, "decode_tiles_layout");
+  if (rc) return rc;
+  if (layout != ESCHA_LAYOUT_MFMA_OPERAND && layout != ESCHA_LAYOUT_LDS_TILE)
+    return fail(ESCHA_E_ARG, "layout=%d is not one of the ESCHA_LAYOUT_* values", layout);
+  if (expert < 0 || expert >= w->n_experts)
+    return fail(ESCHA_E_ARG, "expert=%d out of [0, %d)", expert, w->n_experts);
+  if (!w_f16) return fail(ESCHA_E_NULL, "w_f16 is NULL");
+  if (!aligned(w_f16, 16)) return fail(ESCHA_E_ARG, "w_f16 is not 16-byte aligned");
+  const size_t per_expert = (size_t)(w->in_features / 16) * (w->out_features / 16) * 16 * w->k_bits;
+  const uint16_t* code_e = (const uint16_t*)w->code + (size_t)expert * per_expert;
+  hipError_t e = escha::launch_decode_operands(code_e, w->in_features, w->out_features, w->k_bits, layout,
+                                               w_f16, (hipStream_t)stream);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "decode_tiles_layout launch");
 }
 
 int escha_hadamard128(const float* x, int64_t rows, int32_t n, float* y, void* stream) {
@@ -699,7 +781,7 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
     for (int l = 0; l < n_layers; ++l) {
       float* y = l == n_layers - 1 ? y_last : ytmp;
       hipError_t e;
-      if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[2 * l], s)) != hipSuccess)
+      if (probe_events && (e = record_probe((hipEvent_t)probe_events[2 * l], s)) != hipSuccess)
         return hip_fail(e, "probe event record");
       const GroupedWs gl = same_e ? grouped_layer(g, Lw, n_tokens, l) : g;
       const bool link = linked && l + 1 < n_layers;
@@ -722,6 +804,7 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
         cn.ids_next = topk_ids + (size_t)(l + 1) * n_tokens * k;
         cn.inv_next = gn.inv;
         cn.xg_next = gn.xg;
+        cn.xg_exp_next = gn.xg_exp;
         e = escha::launch_combine_next(cn, s);
         if (e != hipSuccess) return hip_fail(e, "combine/RMSNorm/gather launch");
       } else if (l + 1 < n_layers) {
@@ -730,7 +813,7 @@ int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_layers,
         if (e != hipSuccess) return hip_fail(e, "rmsnorm launch");
         x = next;
       }
-      if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[2 * l + 1], s)) != hipSuccess)
+      if (probe_events && (e = record_probe((hipEvent_t)probe_events[2 * l + 1], s)) != hipSuccess)
         return hip_fail(e, "probe event record");
     }
     return ESCHA_OK;
@@ -847,11 +930,11 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   // status, tickets and flags to zero, the call number one further
   e = escha::launch_flow_prepare(ctl, (size_t)f.ctl_ints, s);
   if (e != hipSuccess) return hip_fail(e, "flag clear launch");
-  if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[0], s)) != hipSuccess)
+  if (probe_events && (e = record_probe((hipEvent_t)probe_events[0], s)) != hipSuccess)
     return hip_fail(e, "probe event record");
   e = escha::launch_stack_flow(a, L0->gate_up.k_bits, L0->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "one-launch stack launch");
-  if (probe_events && (e = hipEventRecord((hipEvent_t)probe_events[1], s)) != hipSuccess)
+  if (probe_events && (e = record_probe((hipEvent_t)probe_events[1], s)) != hipSuccess)
     return hip_fail(e, "probe event record");
   return ESCHA_OK;
 }

@@ -249,6 +249,91 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Largest value over the 64 lanes (NaN lanes are ignored by fmaxf); every
+// lane gets the same result.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, xor_lane<1>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  {
+    const unsigned u = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  }
+  return v;
+}
+
+// ---- power-of-two scaling of activations rounded to fp16 ---------------
+//
+// Activations that enter a matrix-core contraction as fp16 are first
+// multiplied by 2^e, e chosen from the largest magnitude m of the block
+// they belong to so that m 2^e lies in [2^13, 2^14): far from fp16's
+// overflow (65504) and from its subnormals (below 2^-14), whatever the
+// magnitude of the input. The fp32 result is multiplied by 2^-e. A power of
+// two scales exactly, so wherever the unscaled values would have been
+// normal fp16 numbers the results carry the same bits as without scaling.
+
+// Exponent marker of a block whose values are all exactly zero (+0 or -0,
+// no NaN): the block contributes exactly zero to any contraction.
+constexpr int kExpZeroBlock = 1 << 20;
+
+// 2^e for |e| < 126 (exact).
+__device__ __forceinline__ float exp2i(int e) { return __int_as_float((e + 127) << 23); }
+
+// e with 2^13 <= m 2^e < 2^14 for a finite m > 0; 0 for an infinite or NaN
+// m (no scaling); kExpZeroBlock for m == 0. Clamped to |e| <= 100.
+__device__ __forceinline__ int fp16_block_exp(float m) {
+  if (m == 0.0f) return kExpZeroBlock;
+  if (!(m <= 3.0e38f)) return 0;
+  int ex;
+  frexpf(m, &ex);  // 2^(ex - 1) <= m < 2^ex
+  int e = 14 - ex;
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+
+// The exponent of a row whose blocks carry exponents ex[0..n): the
+// smallest (the scale of its largest block); zero blocks do not count, and a
+// row of zero blocks gets 0.
+__device__ __forceinline__ int row_exp(const int32_t* __restrict__ ex, int n) {
+  int e = kExpZeroBlock;
+  for (int c = 0; c < n; ++c) e = ex[c] < e ? ex[c] : e;
+  return e == kExpZeroBlock ? 0 : e;
+}
+
+// Shift that brings fp16 values of a block with exponent eb to the exponent
+// er of their row (er <= eb, so the shift is <= 0); 0 for a zero block.
+__device__ __forceinline__ int block_shift(int er, int eb) {
+  return eb == kExpZeroBlock ? 0 : er - eb;
+}
+
+// 8 fp16 values times 2^sh (sh <= 0): one packed multiply per pair by
+// 2^sh, an fp16 number for sh >= -24 (subnormal below -14), so the result
+// is rounded once to nearest even. Further shifts (a block more than 2^24
+// below its row's largest, whose values then fall below 2^-10 of a row
+// maximum of at most 2^14) take two multiplies, by 2^(sh + 24) and 2^-24,
+// and may round twice; below -48 every value rounds to zero.
+typedef _Float16 h16x8v __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ _Float16 f16_pow2(int sh) {  // -24 <= sh <= 0
+  return __builtin_bit_cast(_Float16, sh >= -14 ? (uint16_t)((sh + 15) << 10)
+                                                : (uint16_t)(1u << (sh + 24)));
+}
+__device__ __forceinline__ h16x8v rescale_h8(h16x8v v, int sh) {
+  if (sh == 0) return v;
+  if (sh >= -24) {
+    const _Float16 f = f16_pow2(sh);
+    return v * h16x8v{f, f, f, f, f, f, f, f};
+  }
+  if (sh < -48) return h16x8v{};
+  const _Float16 f = f16_pow2(sh + 24), g = f16_pow2(-24);
+  return (v * h16x8v{f, f, f, f, f, f, f, f}) * h16x8v{g, g, g, g, g, g, g, g};
+}
+
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
 }  // namespace escha

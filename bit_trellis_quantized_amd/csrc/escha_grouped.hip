@@ -106,31 +106,57 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
 }
 
 // ------------------------------------------------------------------------
-// Rotated gate_up inputs per sorted pair: Xg[i] = fp16(H_n(rin_e (.) x_t)).
-// grid.x = n_pairs, block = 256 (each 16 lanes one 128-input block).
+// Rotated gate_up inputs per sorted pair: Xg[i] = fp16(2^e H_n(rin_e (.) x_t))
+// with the row's power-of-two exponent e (xg_exp[i]). Every rotated value
+// is at most 16 max|rin (.) x| in magnitude (the 128 terms of a row of
+// H_n each have magnitude 1/sqrt(128) < 16/128), so e is taken from that
+// bound: 2^13 <= 16 max|rin (.) x| 2^e < 2^14, and the rotated values stay
+// below 2^14. grid.x = n_pairs, block = 256 (each 16 lanes one 128-input
+// block, 8 consecutive inputs per lane).
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
+  __shared__ float wmax[4];
   const int i = blockIdx.x;
   if (i >= a.offsets[a.n_experts]) return;
   const int p = a.perm[i];
   const int e = a.ids[p];
   const int t = p / a.top_k;
-  // 16 lanes per 128-input block, 8 consecutive inputs per lane (16-byte
-  // loads and stores). The butterflies run in fwht128's order (bit 6, then
-  // bits 0-5), so the rounded results are the same: bit 6 and bits 3-5
-  // across lanes, bits 0-2 inside the lane.
   const int lane = threadIdx.x & 63;
-  const float s1 = lane_sign(lane, 1), s2 = lane_sign(lane, 2), s4 = lane_sign(lane, 4);
-  const float s8 = lane_sign(lane, 8);
-  for (int base = 8 * threadIdx.x; base < a.hidden; base += 8 * 256) {
-    const u32x4 xq = *reinterpret_cast<const u32x4*>(a.x_bf16 + (size_t)t * a.hidden + base);
-    const u32x4 rq = *reinterpret_cast<const u32x4*>(a.rin + (size_t)e * a.hidden + base);
-    float v[8];
+  const uint16_t* xrow = a.x_bf16 + (size_t)t * a.hidden;
+  const uint16_t* rrow = a.rin + (size_t)e * a.hidden;
+  auto load8 = [&](int base, float (&v)[8]) {
+    const u32x4 xq = *reinterpret_cast<const u32x4*>(xrow + base);
+    const u32x4 rq = *reinterpret_cast<const u32x4*>(rrow + base);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v[2 * q] = bf16_to_f32((uint16_t)(xq[q] & 0xFFFFu)) * f16_to_f32((uint16_t)(rq[q] & 0xFFFFu));
       v[2 * q + 1] = bf16_to_f32((uint16_t)(xq[q] >> 16)) * f16_to_f32((uint16_t)(rq[q] >> 16));
     }
+  };
+  // the row's largest |rin (.) x| -> its exponent
+  float m = 0.f;
+  for (int base = 8 * threadIdx.x; base < a.hidden; base += 8 * 256) {
+    float v[8];
+    load8(base, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+  }
+  m = wave_max(m);
+  if (lane == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  int ex = fp16_block_exp(16.0f * m);
+  if (ex == kExpZeroBlock) ex = 0;
+  if (threadIdx.x == 0) a.xg_exp[i] = ex;
+  const float scale = kInvSqrt128 * exp2i(ex);
+  // The butterflies run in fwht128's order (bit 6, then bits 0-5), so the
+  // rounded results are the same: bit 6 and bits 3-5 across lanes, bits
+  // 0-2 inside the lane.
+  const float s1 = lane_sign(lane, 1), s2 = lane_sign(lane, 2), s4 = lane_sign(lane, 4);
+  const float s8 = lane_sign(lane, 8);
+  for (int base = 8 * threadIdx.x; base < a.hidden; base += 8 * 256) {
+    float v[8];
+    load8(base, v);
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = butterfly<8>(v[q], s8);  // bit 6
 #pragma unroll
@@ -147,8 +173,8 @@ __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
     u32x4 o;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const _Float16 lo = (_Float16)(v[2 * q] * kInvSqrt128);
-      const _Float16 hi = (_Float16)(v[2 * q + 1] * kInvSqrt128);
+      const _Float16 lo = (_Float16)(v[2 * q] * scale);
+      const _Float16 hi = (_Float16)(v[2 * q + 1] * scale);
       o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
     *reinterpret_cast<u32x4*>(a.xg + (size_t)i * a.hidden + base) = o;
@@ -180,8 +206,16 @@ __device__ __forceinline__ void load_eighth(const uint16_t* te, uint32_t (&d)[K]
   }
 }
 
+// Offset (in halves) of the 16-byte chunk holding inputs 8kc .. 8kc + 7 of
+// row `row` (0..255) of a step's W buffer: chunks of one kc are 256 rows
+// apart, and rows are permuted as row ^ ((row >> 4) & 15) (see the header).
+__device__ __forceinline__ int w_slot(int kc, int row) {
+  return (kc * 256 + (row ^ ((row >> 4) & 15))) * 8;
+}
+
 // Decode the lane's 32 weights (input rows 2o, 2o+1 of tile (dkt, dnt) of
-// the step, all 16 output columns) and store them to the W buffer.
+// the step, all 16 output columns) and store them to the W buffer at
+// w_slot's positions.
 template <int K>
 __device__ __forceinline__ void decode_to_lds(const uint32_t (&raw)[K], int dkt, int dnt, int o,
                                               int lane, _Float16* wb) {
@@ -213,6 +247,7 @@ template <int K>
 struct StepLoads {
   uint32_t raw[K];
   h8 x[2];
+  int eb;  // exponent of the activations' 128-input block (rescaling loops)
 };
 
 // The matrix waves' part of every step: NT live 32-token sub-tiles (1 or 2)
@@ -225,12 +260,9 @@ __device__ __forceinline__ void mma_steps(const _Float16* wl, const _Float16* xl
   constexpr int kKs = kStep / 16;
   const int l32 = lane & 31;
   const int khi = lane >> 5;
-  int prow[kMT];
+  int wrow[kMT];
 #pragma unroll
-  for (int mt = 0; mt < kMT; ++mt) {
-    const int row = 32 * kMT * wo + 32 * mt + l32;
-    prow[mt] = row ^ ((row >> 4) & 15);
-  }
+  for (int mt = 0; mt < kMT; ++mt) wrow[mt] = 32 * kMT * wo + 32 * mt + l32;
   for (int s = 0; s < n_steps; ++s) {
     const _Float16* wb = wl + (s & 1) * kWBuf;
     const _Float16* xb = xl + (s & 1) * kXBuf;
@@ -240,7 +272,7 @@ __device__ __forceinline__ void mma_steps(const _Float16* wl, const _Float16* xl
       for (int tt = 0; tt < NT; ++tt)
         b[tt] = *reinterpret_cast<const h8*>(xb + (kc * kTM + 64 * wt + 32 * tt + l32) * 8);
 #pragma unroll
-      for (int mt = 0; mt < kMT; ++mt) a[mt] = *reinterpret_cast<const h8*>(wb + (kc * 256 + prow[mt]) * 8);
+      for (int mt = 0; mt < kMT; ++mt) a[mt] = *reinterpret_cast<const h8*>(wb + w_slot(kc, wrow[mt]));
     };
     h8 a0[kMT], b0[2], a1[kMT], b1[2];
     load_ops(0, a0, b0);
@@ -269,21 +301,29 @@ __device__ __forceinline__ void mma_steps(const _Float16* wl, const _Float16* xl
   }
 }
 
-template <int K, class OutTile>
+// The main loop runs over n_steps of the projection's 64-input steps:
+// step i of the loop is input step step_of(i) (all steps in order for
+// gate_up; the down kernel leaves out steps whose 128-channel block is zero
+// for every token of the tile). RESCALE: the activation rows are stored
+// with a power-of-two exponent per 128-input block (xexp [row][nblk]); each
+// 16-byte chunk is rescaled to its row's exponent (row_exp) before it goes
+// to LDS, so that a whole row enters the contraction at one scale.
+template <int K, bool RESCALE, class OutTile, class StepOf>
 __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ code_e, int n_nt,
-                                                 int in_f, const _Float16* __restrict__ X,
-                                                 int x_pitch, int row0, int rows, OutTile out_tile,
+                                                 int n_steps, StepOf step_of,
+                                                 const _Float16* __restrict__ X, int x_pitch,
+                                                 const int32_t* __restrict__ xexp, int nblk,
+                                                 int row0, int rows, OutTile out_tile,
                                                  _Float16* wl, _Float16* xl,
                                                  f32x16 (&acc)[kMT][2]) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform per wave
   const int lane = tid & 63;
   const bool decoder = wave < kDecWaves;
-  const int n_steps = in_f / kStep;
 
   if (decoder) {
-    // waves 0-7: codes and activations of step s+2 are issued at step s
-    // (two steps of latency cover); at step s the lane decodes step s+1's
+    // waves 0-7: codes and activations of step i+2 are issued at step i
+    // (two steps of latency cover); at step i the lane decodes step i+1's
     // eighth of a tile into W and copies its activation chunks into the X
     // tile.
     const int o = tid & 7;
@@ -293,41 +333,52 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
     const int gnt = out_tile(dnt);
     const int xtok = tid & 127;        // activation row of this lane
     const int xkc0 = 2 * (tid >> 7);   // first of its two 16-byte k-chunks
-    const _Float16* xrow = X + (size_t)(row0 + (xtok < rows ? xtok : rows - 1)) * x_pitch + 8 * xkc0;
-    auto issue = [&](int s, StepLoads<K>& L) {
-      load_eighth<K>(code_e + ((size_t)(4 * s + dkt) * n_nt + gnt) * (16 * K) + o * (2 * K), L.raw);
+    const int xr = row0 + (xtok < rows ? xtok : rows - 1);
+    const _Float16* xrow = X + (size_t)xr * x_pitch + 8 * xkc0;
+    const int32_t* erow = RESCALE ? xexp + (size_t)xr * nblk : nullptr;
+    const int e_row = RESCALE ? row_exp(erow, nblk) : 0;
+    auto issue = [&](int i, StepLoads<K>& L) {
+      const int st = step_of(i);
+      load_eighth<K>(code_e + ((size_t)(4 * st + dkt) * n_nt + gnt) * (16 * K) + o * (2 * K), L.raw);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) L.x[j] = *reinterpret_cast<const h8*>(xrow + s * kStep + 8 * j);
+      for (int j = 0; j < 2; ++j) L.x[j] = *reinterpret_cast<const h8*>(xrow + st * kStep + 8 * j);
+      if constexpr (RESCALE) L.eb = erow[(st * kStep) >> 7];
     };
-    auto consume = [&](int s, const StepLoads<K>& L) {
-      decode_to_lds<K>(L.raw, dkt, dnt, o, lane, wl + (s & 1) * kWBuf);
-      _Float16* xb = xl + (s & 1) * kXBuf;
+    auto consume = [&](int i, StepLoads<K>& L) {
+      decode_to_lds<K>(L.raw, dkt, dnt, o, lane, wl + (i & 1) * kWBuf);
+      _Float16* xb = xl + (i & 1) * kXBuf;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) *reinterpret_cast<h8*>(xb + ((xkc0 + j) * kTM + xtok) * 8) = L.x[j];
+      for (int j = 0; j < 2; ++j) {
+        h8 v = L.x[j];
+        if constexpr (RESCALE) v = rescale_h8(v, block_shift(e_row, L.eb));
+        *reinterpret_cast<h8*>(xb + ((xkc0 + j) * kTM + xtok) * 8) = v;
+      }
     };
     StepLoads<K> ring[2];
-    issue(0, ring[0]);
-    if (n_steps > 1) issue(1, ring[1]);
-    consume(0, ring[0]);
-    if (n_steps > 2) issue(2, ring[0]);
+    if (n_steps > 0) {
+      issue(0, ring[0]);
+      if (n_steps > 1) issue(1, ring[1]);
+      consume(0, ring[0]);
+      if (n_steps > 2) issue(2, ring[0]);
+    }
     __syncthreads();
-    // step s consumes ring[(s+1)&1] (issued two steps earlier) and reuses it
-    for (int s = 0; s < n_steps; s += 2) {
-      if (s + 1 < n_steps) {
-        consume(s + 1, ring[1]);
-        if (s + 3 < n_steps) issue(s + 3, ring[1]);
+    // step i consumes ring[(i+1)&1] (issued two steps earlier) and reuses it
+    for (int i = 0; i < n_steps; i += 2) {
+      if (i + 1 < n_steps) {
+        consume(i + 1, ring[1]);
+        if (i + 3 < n_steps) issue(i + 3, ring[1]);
       }
       __syncthreads();
-      if (s + 1 < n_steps) {
-        if (s + 2 < n_steps) {
-          consume(s + 2, ring[0]);
-          if (s + 4 < n_steps) issue(s + 4, ring[0]);
+      if (i + 1 < n_steps) {
+        if (i + 2 < n_steps) {
+          consume(i + 2, ring[0]);
+          if (i + 4 < n_steps) issue(i + 4, ring[0]);
         }
         __syncthreads();
       }
     }
   } else {
-    // the other waves: matrix cores on step s from LDS. (wo, wt): outputs
+    // the other waves: matrix cores on step i from LDS. (wo, wt): outputs
     // 32*kMT*wo + 32*mt, tokens 64*wt + 32*tt. Token sub-tiles without a real
     // token are skipped (uniform per wave); padded columns of a live
     // sub-tile hold a clamped row and are never stored.
@@ -340,7 +391,7 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
     else if (live == 1)
       mma_steps<1>(wl, xl, n_steps, wo, wt, lane, acc);
     else
-      for (int s = 0; s < n_steps; ++s) __syncthreads();
+      for (int i = 0; i < n_steps; ++i) __syncthreads();
   }
 }
 
@@ -387,9 +438,26 @@ __host__ __device__ constexpr unsigned grouped_grid(int max_tiles, int nb) {
 // ------------------------------------------------------------------------
 // gate_up, grouped. grid.x = grouped_grid(max_tiles, inter / 128), block = kThreads.
 // A work-group takes the gate rows and the up rows of one 128-channel block
-// c (256 outputs) for one tile; its epilogue finishes h = SiLU(gate) * up
-// for those channels and writes down's rotated fp16 input block c.
+// c (256 outputs) for one tile; its epilogue undoes the input rows'
+// exponents, finishes h = SiLU(gate) * up for those channels and writes
+// down's rotated fp16 input block c with the block's own exponent.
 // ------------------------------------------------------------------------
+
+// Down's rotated input block (v0 at channel lane, v1 at lane + 64, before
+// the 1/sqrt(128) of H_n) of sorted row i, as fp16 scaled by the block's
+// exponent, and the exponent. Whole wave.
+__device__ __forceinline__ void store_down_input(const GroupedArgs& a, int i, int c, float v0, float v1,
+                                                 int lane) {
+  const bool nan = __ballot(v0 != v0 || v1 != v1) != 0;
+  const float m = wave_max(fmaxf(fabsf(v0), fabsf(v1))) * kInvSqrt128;
+  int ex = nan ? 0 : fp16_block_exp(m);
+  const float scale = kInvSqrt128 * exp2i(ex == kExpZeroBlock ? 0 : ex);
+  _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
+  xo[lane] = (_Float16)(v0 * scale);
+  xo[lane + 64] = (_Float16)(v1 * scale);
+  if (lane == 0) a.x_exp_out[(size_t)i * (a.inter / 128) + c] = ex;
+}
+
 template <int K>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_gate_up(GroupedArgs a) {
   const int nb = a.inter / 128;
@@ -413,9 +481,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][tt][r] = 0.f;
-  grouped_mainloop<K>(code_e, n_nt, a.hidden, reinterpret_cast<const _Float16*>(a.x_in), a.hidden,
-                      row0, rows,
-                      [&](int j) { return j < 8 ? gate_nt0 + j : up_nt0 + j - 8; }, wl, xl, acc);
+  grouped_mainloop<K, false>(code_e, n_nt, a.hidden / kStep, [](int i) { return i; },
+                             reinterpret_cast<const _Float16*>(a.x_in), a.hidden, nullptr, 0, row0,
+                             rows, [&](int j) { return j < 8 ? gate_nt0 + j : up_nt0 + j - 8; }, wl,
+                             xl, acc);
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -430,7 +499,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   // (two independent butterfly chains in flight)
   auto two_tokens = [&](int tla) {
     bool ok[2];
-    float g0[2], g1[2], u0[2], u1[2];
+    float g0[2], g1[2], u0[2], u1[2], us[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int tl = tla + kWaves * q;
@@ -440,6 +509,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       g1[q] = er[lane + 64];
       u0[q] = er[128 + lane];
       u1[q] = er[192 + lane];
+      us[q] = exp2i(-a.x_exp_in[row0 + (ok[q] ? tl : 0)]);  // undo the input row's scale
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -449,8 +519,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     float v0[2], v1[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const float h0 = silu(g0[q] * (kInvSqrt128 * rg0)) * (u0[q] * (kInvSqrt128 * ru0));
-      const float h1 = silu(g1[q] * (kInvSqrt128 * rg1)) * (u1[q] * (kInvSqrt128 * ru1));
+      const float h0 = silu(g0[q] * (kInvSqrt128 * rg0) * us[q]) * (u0[q] * (kInvSqrt128 * ru0) * us[q]);
+      const float h1 = silu(g1[q] * (kInvSqrt128 * rg1) * us[q]) * (u1[q] * (kInvSqrt128 * ru1) * us[q]);
       if (ok[q] && a.inter_out) {
         float* io = a.inter_out + (size_t)a.perm[row0 + tla + kWaves * q] * a.inter + 128 * c;
         io[lane] = h0;
@@ -464,10 +534,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       if (!ok[q]) continue;
-      const int i = row0 + tla + kWaves * q;
-      _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
-      xo[lane] = (_Float16)(v0[q] * kInvSqrt128);
-      xo[lane + 64] = (_Float16)(v1[q] * kInvSqrt128);
+      store_down_input(a, row0 + tla + kWaves * q, c, v0[q], v1[q], lane);
     }
   };
   acc_to_lds(acc, el);
@@ -475,11 +542,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   for (int tla = wave; tla < kTM; tla += 2 * kWaves) two_tokens(tla);
 }
 
+// The 128-channel blocks of down's input that are nonzero for some token
+// of the tile (rows row0 .. row0 + rows - 1), as the list of their 64-input
+// steps in order: steps[0 .. n) in LDS; returns n. A block that is exactly
+// zero for every token contributes exactly zero, so its codes are neither
+// loaded nor decoded. Whole work-group (ends with a barrier).
+__device__ __forceinline__ int live_down_steps(const int32_t* __restrict__ xexp, int nblk, int row0,
+                                               int rows, int* live_blk, int* steps) {
+  for (int c = threadIdx.x; c < nblk; c += blockDim.x) live_blk[c] = 0;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * nblk; idx += blockDim.x)
+    if (xexp[(size_t)(row0 + idx / nblk) * nblk + idx % nblk] != kExpZeroBlock) live_blk[idx % nblk] = 1;
+  __syncthreads();
+  int n = 0;
+  for (int c = 0; c < nblk; ++c)
+    if (live_blk[c]) n += 128 / kStep;
+  if (threadIdx.x == 0) {
+    int j = 0;
+    for (int c = 0; c < nblk; ++c)
+      if (live_blk[c])
+        for (int q = 0; q < 128 / kStep; ++q) steps[j++] = c * (128 / kStep) + q;
+  }
+  __syncthreads();
+  return n;
+}
+
 // ------------------------------------------------------------------------
 // down, grouped. grid.x = grouped_grid(max_tiles, hidden / 256), block = kThreads. The
-// epilogue applies H_n, rout and the pair's router weight and stores the
-// pair's 256 outputs (fp32) at its sorted index.
+// epilogue undoes the row's exponent, applies H_n, rout and the pair's
+// router weight and stores the pair's 256 outputs (fp32) at its sorted index.
 // ------------------------------------------------------------------------
+constexpr int kMaxDownBlocks = 64;  // inter <= 8192 for the zero-block skip
+
 template <int K>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_grouped_down(GroupedArgs a) {
   const int ng = a.hidden / 256;
@@ -490,9 +584,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const int row0 = a.t_row0[tile];
   const int rows = a.t_rows[tile];
   const int n_nt = a.hidden / 16;
+  const int nblk = a.inter / 128;
   const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.inter / 16) * n_nt * (16 * K);
 
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ int live_blk[kMaxDownBlocks];
+  __shared__ int steps[kMaxDownBlocks * (128 / kStep)];
+  int n_steps = a.inter / kStep;
+  const bool skip = nblk <= kMaxDownBlocks;  // uniform
+  if (skip) n_steps = live_down_steps(a.x_exp_in, nblk, row0, rows, live_blk, steps);
   _Float16* wl = reinterpret_cast<_Float16*>(smem);
   _Float16* xl = wl + 2 * kWBuf;
   f32x16 acc[kMT][2];
@@ -502,8 +602,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[mt][tt][q] = 0.f;
-  grouped_mainloop<K>(code_e, n_nt, a.inter, reinterpret_cast<const _Float16*>(a.x_in), a.inter,
-                      row0, rows, [&](int j) { return 16 * r + j; }, wl, xl, acc);
+  grouped_mainloop<K, true>(code_e, n_nt, n_steps, [&](int i) { return skip ? steps[i] : i; },
+                            reinterpret_cast<const _Float16*>(a.x_in), a.inter, a.x_exp_in, nblk, row0,
+                            rows, [&](int j) { return 16 * r + j; }, wl, xl, acc);
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -524,7 +625,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       z1[q] = er[lane + 64];
       z2[q] = er[128 + lane];
       z3[q] = er[192 + lane];
-      wt[q] = ok[q] ? a.w[a.perm[row0 + tl]] : 0.f;
+      // the router weight, with the row's input exponent undone
+      wt[q] = ok[q] ? a.w[a.perm[row0 + tl]] *
+                          exp2i(-row_exp(a.x_exp_in + (size_t)(row0 + tl) * nblk, nblk))
+                    : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -559,29 +663,44 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 constexpr int kSmallTM = 16;
 
 struct SmallLds {
-  uint32_t stage[8 * Stage<3>::kDw];  // each wave's staged codes
-  float red[2][kSmallTM][256];        // per input half: [token][output]
+  uint32_t stage[8 * Stage<3>::kDw];    // each wave's staged codes
+  float red[2][kSmallTM][256];          // per input half: [token][output]
+  int live[kMaxDownBlocks];             // down: 128-channel blocks nonzero for some token
+  int shift[kSmallTM][kMaxDownBlocks];  // down: block_shift of token n's block c
 };
 
-// The wave's partial sums over chunks c0 .. c0 + nch - 1 of the 16 output
-// columns nt0 .. nt0 + 3 (x: the token rows, row n of the tile at xr(n);
-// the columns of tokens >= rows are never stored); lane (n, g) ends with outputs
-// 16j + 4g + q of tile j for token n in D[j][q].
-template <int K, class XRow>
+// The wave's partial sums over the live chunks among c0 .. c0 + nch - 1 of
+// the 16 output columns nt0 .. nt0 + 3; the tile's token rows are rows
+// row0 .. row0 + rows - 1 of X (pitch x_pitch; the columns of tokens >=
+// rows read row row0 and are never stored); lane (n, g) ends with outputs
+// 16j + 4g + q of tile j for token n in D[j][q]. RESCALE: X carries an
+// exponent per 128-input block, and shift(n, c) is the shift that takes
+// token n's chunk c to its row's exponent; the chunk's activations are
+// rescaled with it right before their contraction.
+template <int K, bool RESCALE, class Live, class Shift>
 __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code_e, int n_nt, int c0,
-                                               int nch, int nt0, XRow xr, int rows, uint32_t* stage,
-                                               int lane, f32x4 (&D)[4]) {
+                                               int nch, int nt0, const _Float16* __restrict__ X,
+                                               int x_pitch, int row0, int rows, Live live,
+                                               Shift shift, uint32_t* stage, int lane,
+                                               f32x4 (&D)[4]) {
   const int n = lane & 15;
   const int gq = lane >> 4;
-  // a token column past the tile's rows reads row 0: its outputs (column n
-  // of D) are never stored
-  const _Float16* xrow = xr(n < rows ? n : 0);
+  const int xr = row0 + (n < rows ? n : 0);
+  const _Float16* xrow = X + (size_t)xr * x_pitch;
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int cend = c0 + nch;
+  auto next_live = [&](int c) {  // first live chunk after c, or cend
+    for (++c; c < cend && !live(c); ++c) {
+    }
+    return c;
+  };
+  int c = next_live(c0 - 1);
+  if (c >= cend) return;  // uniform: every chunk of this half is zero
   u32x4 cv[Stage<K>::kPerLane];
-  stage_issue<K>(code_e, n_nt, 8 * c0, nt0, lane, cv);
-  for (int ch = 0; ch < nch; ++ch) {
-    const int c = c0 + ch;
+  stage_issue<K>(code_e, n_nt, 8 * c, nt0, lane, cv);
+  while (c < cend) {
+    const int cn = next_live(c);
     stage_store<K>(stage, lane, cv);
     // the chunk's activations, then the next chunk's codes (past the last
     // chunk: this chunk's again, never used), all in flight during the
@@ -591,7 +710,14 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
       B[pp] = *reinterpret_cast<const h16x8*>(xrow + 128 * c + 32 * pp + 8 * gq);
-    stage_issue<K>(code_e, n_nt, 8 * (ch + 1 < nch ? c + 1 : c), nt0, lane, cv);
+    const int sh = RESCALE ? shift(n, c) : 0;
+    stage_issue<K>(code_e, n_nt, 8 * (cn < cend ? cn : c), nt0, lane, cv);
+    // the chunk's activations at the row's exponent (this waits for their
+    // loads only: the next chunk's codes stay in flight)
+    if constexpr (RESCALE) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) B[pp] = rescale_h8(B[pp], sh);
+    }
     // tile-row pairs decoded one ahead of their MFMAs into two operand sets
     // (32 VGPRs instead of 64): pair pp's MFMAs run on the matrix core while
     // pair pp + 1 (then pp + 2, into pp's freed set) is decoded
@@ -609,6 +735,7 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
     dec.template decode<3>(A1);
     mfma4(A0, B[2]);
     mfma4(A1, B[3]);
+    c = cn;
   }
 }
 
@@ -625,8 +752,9 @@ __device__ __forceinline__ void small_to_lds(const f32x4 (&D)[4], SmallLds& sh, 
 
 // gate_up, small tiles. grid.x = max_tiles * (inter / 128), block = 512.
 // A work-group takes gate block c and up block c (256 outputs, quads 0-1
-// and 2-3) of one tile; its epilogue is the big tile kernel's: h =
-// SiLU(gate) * up for the block's channels, then down's rotated input.
+// and 2-3) of one tile; its epilogue is the big tile kernel's: the input
+// rows' exponents undone, h = SiLU(gate) * up for the block's channels,
+// then down's rotated input with the block's exponent.
 template <int K>
 __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const int nb = a.inter / 128;
@@ -644,11 +772,11 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const int nt0 = nq < 2 ? 8 * c + 4 * nq : a.inter / 16 + 8 * c + 4 * (nq - 2);
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncg * 8 * n_nt * (16 * K);
   __shared__ SmallLds sh;
-  const _Float16* X = reinterpret_cast<const _Float16*>(a.x_in);
   f32x4 D[4];
-  small_mainloop<K>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
-                    [&](int r) { return X + (size_t)(row0 + r) * a.hidden; }, rows,
-                    sh.stage + wave * Stage<K>::kDw, lane, D);
+  small_mainloop<K, false>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
+                           reinterpret_cast<const _Float16*>(a.x_in), a.hidden, row0, rows,
+                           [](int) { return true; }, [](int, int) { return 0; },
+                           sh.stage + wave * Stage<K>::kDw, lane, D);
   small_to_lds(D, sh, kh, nq, lane);
   __syncthreads();
   const uint16_t* rg = a.rout + (size_t)e * (2 * a.inter) + 128 * c;
@@ -659,19 +787,20 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
   for (int tok = 2 * wave; tok < 2 * wave + 2; ++tok) {
     if (tok >= rows) break;  // uniform over the wave
+    const int i = row0 + tok;
+    const float us = exp2i(-a.x_exp_in[i]);  // undo the input row's scale
     const float* r0 = sh.red[0][tok];
     const float* r1 = sh.red[1][tok];
     float g0 = r0[lane] + r1[lane], g1 = r0[lane + 64] + r1[lane + 64];
     float u0 = r0[128 + lane] + r1[128 + lane], u1 = r0[192 + lane] + r1[192 + lane];
     fwht128(g0, g1);
     fwht128(u0, u1);
-    g0 *= kInvSqrt128 * rg0;
-    g1 *= kInvSqrt128 * rg1;
-    u0 *= kInvSqrt128 * ru0;
-    u1 *= kInvSqrt128 * ru1;
+    g0 = g0 * (kInvSqrt128 * rg0) * us;
+    g1 = g1 * (kInvSqrt128 * rg1) * us;
+    u0 = u0 * (kInvSqrt128 * ru0) * us;
+    u1 = u1 * (kInvSqrt128 * ru1) * us;
     const float h0 = silu(g0) * u0;
     const float h1 = silu(g1) * u1;
-    const int i = row0 + tok;
     if (a.inter_out) {
       float* io = a.inter_out + (size_t)a.perm[i] * a.inter + 128 * c;
       io[lane] = h0;
@@ -679,15 +808,15 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
     }
     float v0 = h0 * rd0, v1 = h1 * rd1;
     fwht128(v0, v1);
-    _Float16* xo = reinterpret_cast<_Float16*>(a.x_out) + (size_t)i * a.inter + 128 * c;
-    xo[lane] = (_Float16)(v0 * kInvSqrt128);
-    xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+    store_down_input(a, i, c, v0, v1, lane);
   }
 }
 
 // down, small tiles. grid.x = max_tiles * (hidden / 256), block = 512. The
-// epilogue applies H_n, rout and the pair's router weight and stores the
-// pair's 256 outputs (fp32) at its sorted index.
+// epilogue undoes the row's exponent, applies H_n, rout and the pair's
+// router weight and stores the pair's 256 outputs (fp32) at its sorted
+// index. 128-channel blocks that are zero for every token of the tile are
+// skipped.
 template <int K>
 __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
   const int ng = a.hidden / 256;
@@ -704,11 +833,30 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
   const int ncd = a.inter / 128;
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncd * 8 * n_nt * (16 * K);
   __shared__ SmallLds sh;
-  const _Float16* X = reinterpret_cast<const _Float16*>(a.x_in);
+  // the blocks nonzero for some token of the tile, and each token's shift
+  // per block (columns past the tile's rows read row 0: never stored)
+  const bool table = ncd <= kMaxDownBlocks;  // uniform
+  if (table) {
+    for (int c = threadIdx.x; c < ncd; c += blockDim.x) sh.live[c] = 0;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kSmallTM * ncd; idx += blockDim.x) {
+      const int n = idx / ncd, c = idx % ncd;
+      const int32_t* ex = a.x_exp_in + (size_t)(row0 + (n < rows ? n : 0)) * ncd;
+      sh.shift[n][c] = block_shift(row_exp(ex, ncd), ex[c]);
+      if (n < rows && ex[c] != kExpZeroBlock) sh.live[c] = 1;
+    }
+    __syncthreads();
+  }
   f32x4 D[4];
-  small_mainloop<K>(code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq,
-                    [&](int rr) { return X + (size_t)(row0 + rr) * a.inter; }, rows,
-                    sh.stage + wave * Stage<K>::kDw, lane, D);
+  small_mainloop<K, true>(
+      code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq, reinterpret_cast<const _Float16*>(a.x_in),
+      a.inter, row0, rows, [&](int c) { return !table || sh.live[c] != 0; },
+      [&](int n, int c) {
+        if (table) return sh.shift[n][c];
+        const int32_t* ex = a.x_exp_in + (size_t)(row0 + (n < rows ? n : 0)) * ncd;
+        return block_shift(row_exp(ex, ncd), ex[c]);
+      },
+      sh.stage + wave * Stage<K>::kDw, lane, D);
   small_to_lds(D, sh, kh, nq, lane);
   __syncthreads();
   const uint16_t* ro = a.rout + (size_t)e * a.hidden + 256 * r;
@@ -717,7 +865,8 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
   for (int tok = 2 * wave; tok < 2 * wave + 2; ++tok) {
     if (tok >= rows) break;
     const int i = row0 + tok;
-    const float wt = a.w[a.perm[i]];
+    // the router weight, with the row's input exponent undone
+    const float wt = a.w[a.perm[i]] * exp2i(-row_exp(a.x_exp_in + (size_t)i * ncd, ncd));
     const float* q0 = sh.red[0][tok];
     const float* q1 = sh.red[1][tok];
     float z0 = q0[lane] + q1[lane], z1 = q0[lane + 64] + q1[lane + 64];
@@ -771,6 +920,7 @@ __global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
   __shared__ float block_ss[16];
+  __shared__ float pmax[16][8];  // [block][pair of a group]: largest |rin (.) x|
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int b = threadIdx.x >> 6;
@@ -809,39 +959,146 @@ __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
     if (lane == 0) block_ss[b] = ss;
   }
   __syncthreads();
-  if (!mine) return;
   float tot = 0.f;
   for (int q = 0; q < nb; ++q) tot += block_ss[q];
   const float rs = 1.0f / sqrtf(tot / (float)a.hidden + a.eps);
   const uint16_t x0 = f32_to_bf16_rne(acc0 * rs), x1 = f32_to_bf16_rne(acc1 * rs);
-  if (a.x_out) {
+  if (mine && a.x_out) {
     uint16_t* xr = a.x_out + (size_t)t * a.hidden + 128 * b;
     xr[lane] = x0;
     xr[lane + 64] = x1;
   }
   const float xf0 = bf16_to_f32(x0), xf1 = bf16_to_f32(x1);
+  // the next layer's inputs of the token's pairs, as k_xin_gather forms
+  // them: each pair's row scaled by the power of two taken from 16 times
+  // its largest |rin (.) x| (the blocks' maxima meet in LDS)
   for (int j0 = 0; j0 < k; j0 += 8) {
     int dst[8];
-    uint16_t r0[8], r1[8];
+    float v0[8], v1[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       dst[q] = j0 + q < k ? inv_next[j0 + q] : -1;
       const int e = dst[q] >= 0 ? ids_next[j0 + q] : 0;
-      const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * b;
-      r0[q] = rr[lane];
-      r1[q] = rr[lane + 64];
+      v0[q] = v1[q] = 0.f;
+      if (mine) {
+        const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * b;
+        v0[q] = xf0 * f16_to_f32(rr[lane]);
+        v1[q] = xf1 * f16_to_f32(rr[lane + 64]);
+      }
     }
+    __syncthreads();  // pmax of the previous group has been read
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float m = wave_max(fmaxf(fabsf(v0[q]), fabsf(v1[q])));
+      if (mine && lane == 0) pmax[b][q] = m;
+    }
+    __syncthreads();
+    if (!mine) continue;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (dst[q] < 0) continue;  // uniform over the work-group
-      float v0 = xf0 * f16_to_f32(r0[q]);
-      float v1 = xf1 * f16_to_f32(r1[q]);
-      fwht128(v0, v1);
+      float m = 0.f;
+      for (int bb = 0; bb < nb; ++bb) m = fmaxf(m, pmax[bb][q]);
+      int ex = fp16_block_exp(16.0f * m);
+      if (ex == kExpZeroBlock) ex = 0;
+      if (b == 0 && lane == 0) a.xg_exp_next[dst[q]] = ex;
+      const float scale = kInvSqrt128 * exp2i(ex);
+      fwht128(v0[q], v1[q]);
       _Float16* xo = reinterpret_cast<_Float16*>(a.xg_next) + (size_t)dst[q] * a.hidden + 128 * b;
-      xo[lane] = (_Float16)(v0 * kInvSqrt128);
-      xo[lane + 64] = (_Float16)(v1 * kInvSqrt128);
+      xo[lane] = (_Float16)(v0[q] * scale);
+      xo[lane + 64] = (_Float16)(v1[q] * scale);
     }
   }
+}
+
+// ------------------------------------------------------------------------
+// The decoders of the fused kernels, with their results written back in
+// [out][in] order, so that every decode layout can be checked bit for bit
+// against the format (escha_decode_tiles_layout).
+//
+// MFMA-operand layout (the one-launch stack and the small-tile kernels):
+// one wave per region of 8 tile-rows x 4 output tiles, staged and decoded
+// by exactly the routines those kernels run (stage_issue, stage_store,
+// decode_stage_mfma). Lane (n, g) holds in A[pp][j] the weights of output
+// column n of tile nt0 + j, input rows 8 (g & 1) + i (i = 0..7) of
+// tile-row kt0 + 2 pp + (g >> 1). grid.x = (in/128) * (out/64), block = 64.
+// ------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(64) void k_decode_operands_mfma(const uint16_t* __restrict__ code_e,
+                                                             int in_f, int out_f,
+                                                             uint16_t* __restrict__ w) {
+  __shared__ uint32_t stage[Stage<K>::kDw];
+  const int n_nt = out_f / 16;
+  const int nq = n_nt / 4;
+  const int kt0 = 8 * (blockIdx.x / nq);
+  const int nt0 = 4 * (blockIdx.x % nq);
+  const int lane = threadIdx.x;
+  u32x4 cv[Stage<K>::kPerLane];
+  stage_issue<K>(code_e, n_nt, kt0, nt0, lane, cv);
+  stage_store<K>(stage, lane, cv);
+  h16x8 A[4][4];
+  decode_stage_mfma<K>(stage, lane, A);
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * (nt0 + j) + n;
+      const int col = 16 * (kt0 + 2 * pp + (g >> 1)) + 8 * (g & 1);
+      *reinterpret_cast<h16x8*>(w + (size_t)row * in_f + col) = A[pp][j];
+    }
+}
+
+// LDS-tile layout (the 128-token grouped kernels): one work-group of eight
+// waves -- the decoder waves of those kernels -- per 64-input step and
+// group of 16 output tiles; each lane loads and decodes its eighth of a
+// tile with load_eighth and decode_to_lds, and the W buffer is then read
+// back through w_slot, the addressing of the matrix waves' operand reads.
+// grid.x = (in/64) * (out/256), block = 512.
+template <int K>
+__global__ __launch_bounds__(512) void k_decode_operands_lds(const uint16_t* __restrict__ code_e,
+                                                             int in_f, int out_f,
+                                                             uint16_t* __restrict__ w) {
+  __shared__ __attribute__((aligned(16))) _Float16 wb[kWBuf];
+  const int n_nt = out_f / 16;
+  const int ng = out_f / 256;
+  const int s = blockIdx.x / ng;
+  const int grp = blockIdx.x % ng;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int o = tid & 7;
+  const int dtile = tid >> 3;
+  const int dkt = dtile >> 4, dnt = dtile & 15;
+  uint32_t raw[K];
+  load_eighth<K>(code_e + ((size_t)(4 * s + dkt) * n_nt + 16 * grp + dnt) * (16 * K) + o * (2 * K), raw);
+  decode_to_lds<K>(raw, dkt, dnt, o, lane, wb);
+  __syncthreads();
+  for (int idx = tid; idx < 256 * (kStep / 8); idx += 512) {
+    const int row = idx / (kStep / 8);
+    const int kc = idx % (kStep / 8);
+    const h8 v = *reinterpret_cast<const h8*>(wb + w_slot(kc, row));
+    *reinterpret_cast<h8*>(w + (size_t)(256 * grp + row) * in_f + kStep * s + 8 * kc) = v;
+  }
+}
+
+hipError_t launch_decode_operands(const uint16_t* code_e, int in_f, int out_f, int k_bits, int layout,
+                                  uint16_t* w, hipStream_t s) {
+  if (layout == 1) {
+    const unsigned grid = (unsigned)((in_f / 128) * (out_f / 64));
+    if (k_bits == 2)
+      hipLaunchKernelGGL(k_decode_operands_mfma<2>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+    else
+      hipLaunchKernelGGL(k_decode_operands_mfma<3>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+  } else if (layout == 2) {
+    const unsigned grid = (unsigned)((in_f / kStep) * (out_f / 256));
+    if (k_bits == 2)
+      hipLaunchKernelGGL(k_decode_operands_lds<2>, dim3(grid), dim3(512), 0, s, code_e, in_f, out_f, w);
+    else
+      hipLaunchKernelGGL(k_decode_operands_lds<3>, dim3(grid), dim3(512), 0, s, code_e, in_f, out_f, w);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------------

@@ -75,15 +75,22 @@ struct GatherArgs {
   const int32_t* perm;     // sorted index -> pair
   const int32_t* offsets;  // [E+1]; offsets[E] = number of sorted pairs
   int32_t n_experts, hidden, top_k;
-  uint16_t* xg;            // fp16 [P][hidden] at the sorted index
+  uint16_t* xg;            // fp16 [P][hidden] at the sorted index, row i scaled by 2^xg_exp[i]
+  int32_t* xg_exp;         // [P]: each row's power-of-two exponent
 };
 
+// Activations enter the grouped kernels as fp16 with power-of-two
+// exponents: gate_up's input rows one per row (x_exp_in [P]), down's input
+// one per 128-channel block (x_exp_in [P][inter/128], written by gate_up
+// into x_exp_out); the kernels undo them in their fp32 epilogues.
 struct GroupedArgs {
   const uint16_t* code;     // this projection's codes
   const uint16_t* rout;     // this projection's rout
   const uint16_t* rin2;     // gate_up kernel: down's rin (for its epilogue)
   int32_t hidden, inter;
   const uint16_t* x_in;     // fp16 rows at the sorted index
+  const int32_t* x_exp_in;  // their exponents (see above)
+  int32_t* x_exp_out;       // gate_up: exponents of x_out's blocks [P][inter/128]
   uint16_t* x_out;          // gate_up: fp16 rotated down input [P][inter]
   float* y_out;             // down: fp32 weighted outputs [P][hidden]
   float* inter_out;         // nullable: h per pair, pair order
@@ -108,6 +115,7 @@ struct CombineNextArgs {
   const int32_t* ids_next;   // next layer's [T][top_k]
   const int32_t* inv_next;   // next layer: pair -> sorted index
   uint16_t* xg_next;         // next layer's fp16 rotated inputs [P][hidden], sorted
+  int32_t* xg_exp_next;      // their row exponents [P]
 };
 
 struct SortedCombineArgs {
@@ -189,6 +197,12 @@ hipError_t launch_rmsnorm_bf16(const float* y, int n_tokens, int n, float eps, u
                                hipStream_t s);
 hipError_t launch_decode_tiles(const uint16_t* code_e, int in_f, int out_f, int k_bits,
                                uint16_t* w, hipStream_t s);
+// The fused kernels' decoders with their results written in [out][in] order:
+// layout 1 = matrix-operand decode (decode_stage_mfma), 2 = LDS tiles
+// (decode_to_lds read back through the matrix waves' addressing).
+// in_f % 128 == 0, out_f % 256 == 0.
+hipError_t launch_decode_operands(const uint16_t* code_e, int in_f, int out_f, int k_bits, int layout,
+                                  uint16_t* w, hipStream_t s);
 hipError_t launch_hadamard128(const float* x, int64_t rows, int n, float* y, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
                              hipStream_t s);

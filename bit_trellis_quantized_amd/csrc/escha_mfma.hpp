@@ -187,13 +187,15 @@ static __device__ __noinline__ float2 scale_block(float m);
 
 // Split a wave's 128 rotated activations (v0 at position lane, v1 at
 // lane + 64) into fp16 high and low parts for B, scaled by a power of two
-// that keeps the high part inside the fp16 range (1 unless the largest
-// magnitude exceeds 2^14). Returns the factor that undoes the scale.
+// that keeps both parts inside fp16's normal range: 1 unless the largest
+// magnitude exceeds 2^14 or is below 2^-8 (then it is brought into
+// [2^13, 2^14)). Returns the factor that undoes the scale.
 __device__ __forceinline__ float split_hilo(float v0, float v1, _Float16* xh, _Float16* xl,
                                             int lane) {
   float m = fmaxf(fabsf(v0), fabsf(v1));
   float scale = 1.0f, unscale = 1.0f;
-  if (__ballot(!(m <= 16384.0f)) != 0) {  // rare: large values
+  // rare: large values, or a block whose values are all small
+  if (__ballot(!(m <= 16384.0f)) != 0 || __ballot(m >= 0.00390625f) == 0) {
     const float2 su = scale_block(m);
     scale = su.x;
     unscale = su.y;
@@ -208,8 +210,9 @@ __device__ __forceinline__ float split_hilo(float v0, float v1, _Float16* xh, _F
 }
 
 // The power-of-two scale of split_hilo for a block whose largest magnitude
-// exceeds 2^14 (m: this lane's largest magnitude; NaN and infinity leave the
-// scale at 1): {scale, its inverse}.
+// exceeds 2^14 or lies below 2^-8 (m: this lane's largest magnitude; NaN,
+// infinity and an all-zero block leave the scale at 1): {scale, its
+// inverse}.
 static __device__ __noinline__ float2 scale_block(float m) {
   m = fmaxf(m, xor_lane<1>(m));
   m = fmaxf(m, xor_lane<2>(m));
@@ -226,7 +229,7 @@ static __device__ __noinline__ float2 scale_block(float m) {
     m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
   float scale = 1.0f, unscale = 1.0f;
-  if (m > 16384.0f && m <= 3.0e38f) {
+  if ((m > 16384.0f && m <= 3.0e38f) || (m < 0.00390625f && m > 0.0f)) {
     int ex;
     frexpf(m * (1.0f / 16384.0f), &ex);
     scale = ldexpf(1.0f, -ex);

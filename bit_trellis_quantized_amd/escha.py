@@ -24,6 +24,7 @@ if not _LIB_PATH.exists():
 _lib = ctypes.CDLL(str(_LIB_PATH))
 
 ESCHA_OK = 0
+STATUS_INCOMPLETE = 1  # escha_moe_stack_status: a dependency wait gave up
 STATUS = {
     -1: "ESCHA_E_NULL", -2: "ESCHA_E_SHAPE", -3: "ESCHA_E_KBITS", -4: "ESCHA_E_WORKSPACE",
     -5: "ESCHA_E_HIP", -6: "ESCHA_E_UNSUPPORTED", -7: "ESCHA_E_ARG",
@@ -52,6 +53,7 @@ _P = ctypes.POINTER
 
 _SIGS = {
     "escha_decode_tiles": ([_P(escha_proj_t), _i32, _vp, _vp], ctypes.c_int),
+    "escha_decode_tiles_layout": ([_P(escha_proj_t), _i32, _i32, _vp, _vp], ctypes.c_int),
     "escha_hadamard128": ([_vp, _i64, _i32, _vp, _vp], ctypes.c_int),
     "escha_route_topk": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
     "escha_router_workspace_bytes": ([_i32, _i32, _i32], _sz),
@@ -72,6 +74,7 @@ _SIGS = {
     "escha_moe_stack_decode_persistent": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32,
                                            _vp, _vp, _vp, _sz, _vp, _vp], ctypes.c_int),
     "escha_moe_stack_status": ([_vp, _P(_i32), _vp], ctypes.c_int),
+    "escha_probe_events_set": ([_vp, _i32], ctypes.c_int),
     "escha_last_error": ([], ctypes.c_char_p),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -107,7 +110,20 @@ def _ptr(t: torch.Tensor | None, dtype=None, name="tensor"):
     return ctypes.c_void_p(t.data_ptr())
 
 
-_U16 = (torch.int16, torch.uint16, torch.float16, torch.bfloat16)
+# 16-bit tensors are passed as their bit patterns: a raw int16/uint16 view,
+# or the matching float type (bf16 for activations, fp16 for scales and
+# gates); the other float type is rejected rather than reinterpreted.
+_U16_BITS = (torch.int16, torch.uint16)
+_BF16 = _U16_BITS + (torch.bfloat16,)
+_F16 = _U16_BITS + (torch.float16,)
+
+
+def _check_out(t: torch.Tensor, shape, dtypes, name: str):
+    """A caller-provided tensor must have exactly the shape the call reads or writes."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in (dtypes if isinstance(dtypes, tuple) else (dtypes,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtypes}")
 
 
 # ------------------------------------------------------------------ descriptors
@@ -156,8 +172,8 @@ class Proj:
         E = self.n_experts
         if tuple(self.rin.shape) != (E, self.in_features) or tuple(self.rout.shape) != (E, self.out_features):
             raise ValueError("rin/rout shapes do not match the code tensor")
-        return escha_proj_t(_ptr(self.code, _U16, "code").value, _ptr(self.rin, _U16, "rin").value,
-                            _ptr(self.rout, _U16, "rout").value, E, self.in_features,
+        return escha_proj_t(_ptr(self.code, _U16_BITS, "code").value, _ptr(self.rin, _F16, "rin").value,
+                            _ptr(self.rout, _F16, "rout").value, E, self.in_features,
                             self.out_features, self.k_bits)
 
     @classmethod
@@ -205,8 +221,24 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 def escha_decode_tiles(w: Proj, expert: int, out: torch.Tensor | None = None, stream=None):
     if out is None:
         out = torch.empty(w.out_features, w.in_features, dtype=torch.int16, device=w.code.device)
+    _check_out(out, (w.out_features, w.in_features), _U16_BITS, "out")
     wc = w.c()
-    _check(_lib.escha_decode_tiles(ctypes.byref(wc), expert, _ptr(out, _U16, "out"), _stream(stream)))
+    _check(_lib.escha_decode_tiles(ctypes.byref(wc), expert, _ptr(out, _U16_BITS, "out"), _stream(stream)))
+    return out
+
+
+LAYOUT_QUARTER, LAYOUT_MFMA_OPERAND, LAYOUT_LDS_TILE = 0, 1, 2
+
+
+def escha_decode_tiles_layout(w: Proj, expert: int, layout: int, out: torch.Tensor | None = None,
+                              stream=None):
+    """Decode through one fused kernel's decoder (LAYOUT_*); fp16 bits [out][in]."""
+    if out is None:
+        out = torch.empty(w.out_features, w.in_features, dtype=torch.int16, device=w.code.device)
+    _check_out(out, (w.out_features, w.in_features), _U16_BITS, "out")
+    wc = w.c()
+    _check(_lib.escha_decode_tiles_layout(ctypes.byref(wc), expert, layout, _ptr(out, _U16_BITS, "out"),
+                                          _stream(stream)))
     return out
 
 
@@ -215,6 +247,7 @@ def escha_hadamard128(x: torch.Tensor, out: torch.Tensor | None = None, stream=N
     rows = x.numel() // n if n else 0
     if out is None:
         out = torch.empty_like(x)
+    _check_out(out, tuple(x.shape), torch.float32, "out")
     _check(_lib.escha_hadamard128(_ptr(x, torch.float32, "x"), rows, n, _ptr(out, torch.float32, "y"),
                                   _stream(stream)))
     return out
@@ -243,10 +276,11 @@ def escha_router_logits(x_bf16: torch.Tensor, gate_f16: torch.Tensor, out: torch
         raise ValueError(f"gate has {H2} inputs, x has {H}")
     if out is None:
         out = torch.empty(T, E, dtype=torch.float32, device=x_bf16.device)
+    _check_out(out, (T, E), torch.float32, "out")
     nbytes = escha_router_workspace_bytes(T, H, E)
     if workspace is None and nbytes:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x_bf16.device)
-    _check(_lib.escha_router_logits(_ptr(x_bf16, _U16, "x_bf16"), T, H, _ptr(gate_f16, _U16, "gate_f16"),
+    _check(_lib.escha_router_logits(_ptr(x_bf16, _BF16, "x_bf16"), T, H, _ptr(gate_f16, _F16, "gate_f16"),
                                     E, _ptr(out, torch.float32, "logits"), _ptr(workspace),
                                     workspace.numel() if workspace is not None else 0, _stream(stream)))
     return out
@@ -272,11 +306,12 @@ def escha_expert_gemv(w: Proj, expert: int, x_bf16: torch.Tensor, out: torch.Ten
     T = x2.shape[0]
     if out is None:
         out = torch.empty(T, w.out_features, dtype=torch.float32, device=x_bf16.device)
+    _check_out(out, (T, w.out_features), torch.float32, "out")
     wc = w.c()
     nbytes = _lib.escha_expert_gemv_workspace_bytes(ctypes.byref(wc), T)
     if workspace is None:
         workspace = _ws(nbytes, x_bf16.device)
-    _check(_lib.escha_expert_gemv(ctypes.byref(wc), expert, _ptr(x2, _U16, "x"), T,
+    _check(_lib.escha_expert_gemv(ctypes.byref(wc), expert, _ptr(x2, _BF16, "x"), T,
                                   _ptr(out, torch.float32, "y"), _ptr(workspace),
                                   workspace.numel(), _stream(stream)))
     return out
@@ -292,10 +327,16 @@ def _moe_call(fn, layer, x_bf16, topk_ids, topk_w, out, inter_out, workspace, st
     lc = layer.c()
     if out is None:
         out = torch.empty(T, layer.hidden, dtype=torch.float32, device=x_bf16.device)
+    _check_out(x_bf16, (T, layer.hidden), _BF16, "x_bf16")
+    _check_out(out, (T, layer.hidden), torch.float32, "out")
+    _check_out(topk_ids, (T, layer.top_k), torch.int32, "topk_ids")
+    _check_out(topk_w, (T, layer.top_k), torch.float32, "topk_w")
+    if inter_out is not None:
+        _check_out(inter_out, (T * layer.top_k, layer.inter), torch.float32, "inter_out")
     nbytes = _lib.escha_moe_workspace_bytes(ctypes.byref(lc), T, int(prefill))
     if workspace is None:
         workspace = _ws(nbytes, x_bf16.device)
-    _check(fn(ctypes.byref(lc), _ptr(x_bf16, _U16, "x"), T, _ptr(topk_ids, torch.int32, "topk_ids"),
+    _check(fn(ctypes.byref(lc), _ptr(x_bf16, _BF16, "x"), T, _ptr(topk_ids, torch.int32, "topk_ids"),
               _ptr(topk_w, torch.float32, "topk_w"), _ptr(out, torch.float32, "y"),
               _ptr(inter_out, torch.float32, "inter_out"), _ptr(workspace), workspace.numel(),
               _stream(stream)))
@@ -318,7 +359,8 @@ def escha_rmsnorm_bf16(y: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | N
     T, n = y.shape
     if out is None:
         out = torch.empty(T, n, dtype=torch.int16, device=y.device)
-    _check(_lib.escha_rmsnorm_bf16(_ptr(y, torch.float32, "y"), T, n, eps, _ptr(out, _U16, "x"),
+    _check_out(out, (T, n), _BF16, "out")
+    _check(_lib.escha_rmsnorm_bf16(_ptr(y, torch.float32, "y"), T, n, eps, _ptr(out, _BF16, "x"),
                                    _stream(stream)))
     return out
 
@@ -337,32 +379,54 @@ class Stack:
 def _stack_call(fn, n_events, stack, x0_bf16, topk_ids, topk_w, eps, out, x_chain, workspace,
                 probe_events, stream):
     T = x0_bf16.shape[0]
+    NL = len(stack.layers)
     hidden = stack.layers[0].hidden
+    k = stack.layers[0].top_k
     if out is None:
         out = torch.empty(T, hidden, dtype=torch.float32, device=x0_bf16.device)
+    _check_out(x0_bf16, (T, hidden), _BF16, "x0_bf16")
+    _check_out(out, (T, hidden), torch.float32, "out")
+    _check_out(topk_ids, (NL, T, k), torch.int32, "topk_ids")
+    _check_out(topk_w, (NL, T, k), torch.float32, "topk_w")
+    if x_chain is not None:
+        _check_out(x_chain, (NL, T, hidden), _BF16, "x_chain")
     nbytes = stack.workspace_bytes(T)
     if workspace is None:
         workspace = _ws(nbytes, x0_bf16.device)
-    _check(fn(stack.arr, len(stack.layers), _ptr(x0_bf16, _U16, "x0"), T,
+    _check(fn(stack.arr, NL, _ptr(x0_bf16, _BF16, "x0"), T,
               _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"), eps,
-              _ptr(out, torch.float32, "y"), _ptr(x_chain, _U16, "x_chain"), _ptr(workspace),
+              _ptr(out, torch.float32, "y"), _ptr(x_chain, _BF16, "x_chain"), _ptr(workspace),
               workspace.numel(), _events(probe_events, n_events), _stream(stream)))
-    return out
+    return out, workspace
 
 
 def escha_moe_stack_decode(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6, out=None,
                            x_chain=None, workspace=None, probe_events=None, stream=None):
     """probe_events: optional sequence of 2*n_layers raw hipEvent_t handles (ints)."""
     return _stack_call(_lib.escha_moe_stack_decode, 2 * len(stack.layers), stack, x0_bf16, topk_ids,
-                       topk_w, eps, out, x_chain, workspace, probe_events, stream)
+                       topk_w, eps, out, x_chain, workspace, probe_events, stream)[0]
 
 
 def escha_moe_stack_decode_persistent(stack: Stack, x0_bf16, topk_ids, topk_w, eps: float = 1e-6,
                                       out=None, x_chain=None, workspace=None, probe_events=None,
-                                      stream=None):
-    """One persistent launch for the whole stack; probe_events: 2 raw hipEvent_t handles."""
-    return _stack_call(_lib.escha_moe_stack_decode_persistent, 2, stack, x0_bf16, topk_ids, topk_w,
-                       eps, out, x_chain, workspace, probe_events, stream)
+                                      stream=None, check_status: bool = True):
+    """One persistent launch for the whole stack; probe_events: 2 raw hipEvent_t handles.
+
+    The C call returns before the kernel has run, so a dependency wait that
+    gave up (its outputs then incomplete) shows only in the status word. With
+    ``check_status`` (the default) this waits for the stream, reads the word
+    and raises ``EschaError`` when it is set; pass False to keep the call
+    asynchronous (inside graph capture it must be False) and check
+    ``escha_moe_stack_status`` later.
+    """
+    if check_status and torch.cuda.is_current_stream_capturing():
+        raise ValueError("check_status=True needs a synchronising read; pass False under graph capture")
+    out, ws = _stack_call(_lib.escha_moe_stack_decode_persistent, 2, stack, x0_bf16, topk_ids, topk_w,
+                          eps, out, x_chain, workspace, probe_events, stream)
+    if check_status and escha_moe_stack_status(ws, stream) != 0:
+        raise EschaError(STATUS_INCOMPLETE, "a dependency wait of the one-launch stack gave up; "
+                                            "the outputs are incomplete")
+    return out
 
 
 def escha_moe_stack_status(workspace: torch.Tensor, stream=None) -> int:
@@ -370,6 +434,16 @@ def escha_moe_stack_status(workspace: torch.Tensor, stream=None) -> int:
     v = ctypes.c_int32(-1)
     _check(_lib.escha_moe_stack_status(_ptr(workspace), ctypes.byref(v), _stream(stream)))
     return int(v.value)
+
+
+def escha_probe_events_set(handles=None):
+    """Install (two raw hipEvent_t handles) or remove (None) this thread's
+    projection probes: later layer calls record them around their gate_up
+    and down projection kernels."""
+    if handles is None:
+        _check(_lib.escha_probe_events_set(None, 0))
+    else:
+        _check(_lib.escha_probe_events_set(_events(handles, 2), 2))
 
 
 def _events(handles, n):

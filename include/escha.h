@@ -108,6 +108,31 @@ typedef struct escha_moe_layer {
 ESCHA_API int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t* w_f16, void* stream);
 
 /*
+ * The same decode as escha_decode_tiles, run through the decoder of one of
+ * the fused kernels and written back in [out_features][in_features] order,
+ * so that each kernel's decoder can be checked bit for bit against the
+ * format ([trellis-mlx] exactness table; [hipfire] "What it is"):
+ *   ESCHA_LAYOUT_QUARTER        the streaming kernels' decoder (four lanes
+ *                               per tile); identical to escha_decode_tiles;
+ *   ESCHA_LAYOUT_MFMA_OPERAND   the decoder of the one-launch stack and the
+ *                               small-tile kernels (tiles staged in LDS,
+ *                               weights decoded into matrix-core A operands);
+ *   ESCHA_LAYOUT_LDS_TILE       the decoder of the 128-token grouped kernels
+ *                               (an eighth of a tile per lane, fp16 tiles in
+ *                               LDS, read back with the matrix waves'
+ *                               addressing).
+ * w_f16 is 16-byte aligned (8 for ESCHA_LAYOUT_QUARTER). An unknown layout
+ * returns ESCHA_E_ARG.
+ */
+enum escha_decode_layout {
+  ESCHA_LAYOUT_QUARTER = 0,
+  ESCHA_LAYOUT_MFMA_OPERAND = 1,
+  ESCHA_LAYOUT_LDS_TILE = 2,
+};
+ESCHA_API int escha_decode_tiles_layout(const escha_proj_t* w, int32_t expert, int32_t layout,
+                                        uint16_t* w_f16, void* stream);
+
+/*
  * y = H_n x on each consecutive block of 128 values of every row, with H the
  * Sylvester-ordered 128-point Hadamard matrix and H_n = H / sqrt(128)
  * ([trellis-mlx] Hadamard note). x, y fp32 [rows][n]; n % 128 == 0; x and y
@@ -131,11 +156,21 @@ ESCHA_API int escha_route_topk(const float* logits, int32_t n_tokens, int32_t n_
  * hidden state of token t, returned as fp32. [trellis-mlx] exactness table:
  * the router gate (mlp.gate) is kept in fp16; [hipfire] review notes: the
  * logits are rounded to f16 before the top-k, which creates exact ties that
- * escha_route_topk then breaks to the lower expert index. The products are
- * exact and summed with IEEE fp32 FMAs in input order, so a logit can differ from
- * the rounding of the exact sum by one f16 step only where that sum lies
- * within fp32 rounding error of the midpoint between two f16 values. The
- * same call (sizes) always sums in the same order: results are reproducible.
+ * escha_route_topk then breaks to the lower expert index. The products of an
+ * fp16 and a bf16 value are exact in fp32 and are added with IEEE fp32
+ * operations in a fixed order that depends on the number of tokens:
+ *   - up to 8 tokens: lane l of a 64-lane wave adds, with FMAs in input
+ *     order, the inputs of 32-input chunks l, l + 64, l + 128, ...; the 64
+ *     lane sums are then added pairwise in a butterfly (lanes 1, 2, 4, 8,
+ *     16, 32 apart);
+ *   - more tokens: the inputs are cut into ksplit consecutive slices (ksplit
+ *     a power of two <= 32 chosen from the sizes); each slice is summed from
+ *     zero with FMAs in input order, and the slice sums are then added in
+ *     slice order.
+ * A logit can therefore differ from the rounding of the exact sum by one f16
+ * step only where that sum lies within the fp32 error of these orders of a
+ * midpoint between two f16 values. The same call (sizes) always sums in the
+ * same order: results are reproducible.
  *   x_bf16    bf16 [n_tokens][hidden], 16-byte aligned
  *   gate_f16  fp16 [n_experts][hidden], 16-byte aligned
  *   logits    out: fp32 [n_tokens][n_experts]
@@ -229,6 +264,8 @@ ESCHA_API int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, fl
  * events[2l] and events[2l+1] are recorded on `stream` right before layer
  * l's first kernel and right after its last one, so a caller can time each
  * layer inside a longer run. The library does not create or destroy them.
+ * Under stream capture they are recorded as external event nodes, so every
+ * replay of the graph stamps them.
  */
 ESCHA_API size_t escha_moe_stack_workspace_bytes(const escha_moe_layer_t* layers, int32_t n_layers,
                                        int32_t n_tokens);
@@ -257,10 +294,16 @@ ESCHA_API int escha_moe_stack_decode(const escha_moe_layer_t* layers, int32_t n_
  * data handed between tasks carries a per-call tag kept in the workspace);
  * afterwards the library keeps it consistent from call to call.
  * probe_events (nullable): a HOST array of 2 hipEvent_t handles, recorded
- * right before and right after the kernel.
+ * right before and right after the kernel (external event nodes under
+ * stream capture).
  * A dependency wait that exceeds its bound (half a second; it cannot happen
  * while the device makes progress) makes every work-group stop at its next
  * wait; the outputs are then incomplete and escha_moe_stack_status reports 1.
+ * The return value cannot show this: ESCHA_OK only means the launch was
+ * enqueued, before the kernel has run. A caller must read the status word
+ * with escha_moe_stack_status after the stream has reached the call; the
+ * Python binding does so by default (a synchronising read) and raises when
+ * it is set.
  * Calls sharing one workspace must be ordered (same stream or synchronised).
  */
 ESCHA_API int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n_layers,
@@ -276,6 +319,18 @@ ESCHA_API int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers,
  * up) in *status (a HOST pointer).
  */
 ESCHA_API int escha_moe_stack_status(const void* workspace, int32_t* status, void* stream);
+
+/*
+ * Measurement hook. With n_events == 2, every later layer call of the
+ * calling thread (escha_moe_layer_decode / _prefill, and each layer of
+ * escha_moe_stack_decode) records events[0] on its stream right before its
+ * gate_up projection kernel and events[1] right after its down projection
+ * kernel, so a caller can time the two projection kernels alone; events
+ * NULL or n_events == 0 removes the hook. The handles are hipEvent_t
+ * created by the caller, who keeps them alive while the hook is set. Under
+ * stream capture the records become external event nodes of the graph.
+ */
+ESCHA_API int escha_probe_events_set(void* const* events, int32_t n_events);
 
 /* Message for the calling thread's last failed call ("" if none). */
 ESCHA_API const char* escha_last_error(void);

@@ -234,3 +234,23 @@ def test_leaf_contract():
         escha.Proj.from_leaves({k: v for k, v in leaves.items() if "rout" not in k}, "x.")
     with pytest.raises(ValueError, match="escha_rotation_theta"):
         escha.Proj.from_leaves(dict(leaves, **{"x.escha_rotation_theta": t}), "x.")
+
+
+def test_decode_tiles_layout_rejects_unknown_layout(lib):
+    f = lib.escha_decode_tiles_layout
+    f.argtypes = [ctypes.POINTER(Proj), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    p = _proj()
+    assert f(ctypes.byref(p), 0, 3, ctypes.c_void_p(FAKE), None) == -7
+    assert "layout" in _err(lib)
+    assert f(ctypes.byref(p), 256, 1, ctypes.c_void_p(FAKE), None) == -7  # expert out of range
+    assert f(ctypes.byref(p), 0, 2, None, None) == -1
+    assert f(ctypes.byref(p), 0, 1, ctypes.c_void_p(FAKE + 8), None) == -7  # not 16-byte aligned
+
+
+def test_probe_events_set_validates(lib):
+    f = lib.escha_probe_events_set
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    arr = (ctypes.c_void_p * 2)(FAKE, None)
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 2) == -1
+    assert f(ctypes.cast(arr, ctypes.c_void_p), 3) == -7
+    assert f(None, 0) == 0

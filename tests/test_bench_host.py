@@ -16,19 +16,25 @@ def _bench():
     return mod
 
 
-def test_traffic_record_matches_the_kernel_sources():
-    """bench.py reports the counted HBM traffic only while the one-launch
-    kernel's sources hash to the value recorded with the counters."""
+def test_traffic_records_match_the_kernel_sources():
+    """bench.py reports a counted HBM traffic figure only while the kernel
+    sources hash to the value recorded with the counters."""
     bench = _bench()
-    text = Path(bench.TRAFFIC_PROFILE).read_text()
-    want = re.search(r"kernel_sources_sha256_16: ([0-9a-f]+)", text).group(1)
-    h = hashlib.sha256()
-    for f in bench.KERNEL_SOURCES:
-        h.update((ROOT / "bit_trellis_quantized_amd" / "csrc" / f).read_bytes())
-    if h.hexdigest()[:16] == want:
-        assert bench.measured_traffic() == int(re.search(r"traffic_bytes_per_launch: (\d+)", text).group(1))
-    else:
-        assert bench.measured_traffic() is None
+    for key, (name, files) in bench.TRAFFIC_PROFILES.items():
+        path = ROOT / "profiles" / name
+        if not path.exists():
+            assert bench.measured_traffic(key) is None
+            continue
+        text = path.read_text()
+        want = re.search(r"kernel_sources_sha256_16: ([0-9a-f]+)", text).group(1)
+        h = hashlib.sha256()
+        for f in files:
+            h.update((ROOT / "bit_trellis_quantized_amd" / "csrc" / f).read_bytes())
+        if h.hexdigest()[:16] == want:
+            got = int(re.search(r"traffic_bytes_per_launch: (\d+)", text).group(1))
+            assert bench.measured_traffic(key) == got
+        else:
+            assert bench.measured_traffic(key) is None
 
 
 def _ignored(rel: str, patterns) -> bool:
@@ -50,8 +56,9 @@ def test_gpu_runs_ship_what_bench_and_tests_load():
     ign = ROOT / ".gpurunignore"
     patterns = [ln.strip() for ln in ign.read_text().splitlines() if ln.strip()] if ign.exists() else []
     bench = _bench()
-    needed = [Path(bench.TRAFFIC_PROFILE).relative_to(ROOT).as_posix(),
-              "bench.py", "__graft_entry__.py", "bit_trellis_quantized_amd/escha.py",
+    needed = ["profiles/" + name for name, _ in bench.TRAFFIC_PROFILES.values()
+              if (ROOT / "profiles" / name).exists()]
+    needed += ["bench.py", "__graft_entry__.py", "bit_trellis_quantized_amd/escha.py",
               "bit_trellis_quantized_amd/synth.py", "bit_trellis_quantized_amd/libescha.so"]
     needed += [p.relative_to(ROOT).as_posix() for p in (ROOT / "tests").rglob("*") if p.is_file()
                and "__pycache__" not in p.parts]

@@ -70,6 +70,56 @@ def test_decode_tiles_special_words(escha, K):
         assert np.array_equal(got, oracle.reconstruct(code, in_f, out_f, K)), hex(fill)
 
 
+# The decoders of the fused kernels, written back in [out][in] order: the
+# matrix-operand decoder (one-launch stack, small tiles) and the LDS-tile
+# decoder (128-token grouped kernels) must give the format's bits exactly.
+FUSED_LAYOUTS = [1, 2]  # LAYOUT_MFMA_OPERAND, LAYOUT_LDS_TILE
+
+
+@pytest.mark.parametrize("layout", FUSED_LAYOUTS)
+@pytest.mark.parametrize("K", [2, 3])
+def test_decode_layouts_single_matrix_bit_exact(escha, layout, K):
+    announce(f"decode layout {layout} 256x256 K={K}")
+    code, rin, rout = synth.single_proj(1, 256, 256, K)
+    w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
+    got = u16(escha.escha_decode_tiles_layout(w, 0, layout))
+    ref = oracle.reconstruct(code, 256, 256, K)
+    assert np.count_nonzero(got != ref) == 0
+
+
+@pytest.mark.parametrize("layout", FUSED_LAYOUTS)
+@pytest.mark.parametrize("expert", [0, 1, 137, 255])
+def test_decode_layouts_layer_experts_bit_exact(escha, layer2, layer2_dev, layout, expert):
+    announce(f"decode layout {layout} layer2 expert {expert}")
+    got_gu = u16(escha.escha_decode_tiles_layout(layer2_dev.gate_up, expert, layout))
+    got_dn = u16(escha.escha_decode_tiles_layout(layer2_dev.down, expert, layout))
+    ref_gu = oracle.reconstruct(layer2["gu_code"][expert], 2048, 1024, 2)
+    ref_dn = oracle.reconstruct(layer2["dn_code"][expert], 512, 2048, 3)
+    assert np.count_nonzero(got_gu != ref_gu) == 0
+    assert np.count_nonzero(got_dn != ref_dn) == 0
+
+
+@pytest.mark.parametrize("layout", [0] + FUSED_LAYOUTS)
+@pytest.mark.parametrize("K", [2, 3])
+def test_decode_layouts_special_words(escha, layout, K):
+    """Constant words (all-zero, all-one, alternating, end bits) and a
+    mixture with one constant word per tile position, so that every window,
+    the wrapping ones included, sees distinct neighbours."""
+    announce(f"decode layout {layout} special words K={K}")
+    in_f, out_f = 128, 256
+    shape = (in_f // 16, out_f // 16, 16 * K)
+    _, rin, rout = synth.single_proj(3, in_f, out_f, K)
+    cases = [np.full(shape, f, dtype=np.uint16) for f in (0x0000, 0xFFFF, 0xAAAA, 0x8001)]
+    mixed = np.random.default_rng(K).integers(0, 65536, size=shape, dtype=np.uint16)
+    mixed[..., 0] = 0xFFFF   # first word of every tile (the wrap target)
+    mixed[..., -1] = 0x8001  # last word of every tile (the wrap source)
+    cases.append(mixed)
+    for code in cases:
+        w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
+        got = u16(escha.escha_decode_tiles_layout(w, 0, layout))
+        assert np.array_equal(got, oracle.reconstruct(code, in_f, out_f, K)), hex(int(code.flat[1]))
+
+
 # ------------------------------------------------------------------ Hadamard
 
 def test_hadamard128(escha):
