@@ -701,6 +701,27 @@ int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, i
                           (hipStream_t)stream);
 }
 
+int escha_moe_layer_decode_static(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
+                                  const int32_t* topk_ids, const float* topk_w, float* y,
+                                  float* inter_out, void* stream) {
+  int rc = check_layer_call(L, x_bf16, n_tokens, topk_ids, topk_w, y);
+  if (rc) return rc;
+  if (n_tokens == 0) return ESCHA_OK;
+  const size_t need = escha_moe_workspace_bytes(L, n_tokens, 0);
+  if (need > escha::kStaticScratchBytes)
+    return fail(ESCHA_E_WORKSPACE,
+                "decode_static: %d tokens need %zu bytes of scratch, more than the library's "
+                "%zu-byte array (call escha_moe_layer_decode with a workspace instead)",
+                n_tokens, need, escha::kStaticScratchBytes);
+  void* scratch = nullptr;
+  const hipError_t e = escha::static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  // the same kernels, in the same order, as escha_moe_layer_decode with this
+  // scratch as its workspace (nothing in it needs to start at zero)
+  return escha_moe_layer_decode(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, scratch,
+                                escha::kStaticScratchBytes, stream);
+}
+
 int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
                             const int32_t* topk_ids, const float* topk_w, float* y,
                             float* inter_out, void* workspace, size_t workspace_bytes,

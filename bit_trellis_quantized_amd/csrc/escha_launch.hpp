@@ -189,6 +189,12 @@ hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hi
 hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s);
 hipError_t launch_combine_next(const CombineNextArgs& a, hipStream_t s);
 
+// The device-resident scratch array of escha_static.hip (one per device,
+// kStaticScratchBytes): its device address on the current device, looked up
+// on the first call there and kept for the process.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+hipError_t static_scratch(void** ptr);
+
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s);
 hipError_t launch_down_partial(const DownPartialArgs& a, int k_bits, hipStream_t s);
 hipError_t launch_proj_finish(const FinishArgs& a, hipStream_t s);

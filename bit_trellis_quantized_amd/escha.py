@@ -67,6 +67,8 @@ _SIGS = {
                                ctypes.c_int),
     "escha_moe_layer_prefill": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                                 ctypes.c_int),
+    "escha_moe_layer_decode_static": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp],
+                                      ctypes.c_int),
     "escha_rmsnorm_bf16": ([_vp, _i32, _i32, _f32, _vp, _vp], ctypes.c_int),
     "escha_moe_stack_workspace_bytes": ([_P(escha_moe_layer_t), _i32, _i32], _sz),
     "escha_moe_stack_decode": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp,
@@ -353,6 +355,28 @@ def escha_moe_layer_prefill(layer: MoeLayer, x_bf16, topk_ids, topk_w, out=None,
                             workspace=None, stream=None):
     return _moe_call(_lib.escha_moe_layer_prefill, layer, x_bf16, topk_ids, topk_w, out, inter_out,
                      workspace, stream, True)
+
+
+def escha_moe_layer_decode_static(layer: MoeLayer, x_bf16, topk_ids, topk_w, out=None, inter_out=None,
+                                  stream=None):
+    """escha_moe_layer_decode with the library's own device scratch (no
+    workspace, no allocation in the library; ``out`` may be passed so that
+    the call allocates nothing at all)."""
+    T = x_bf16.shape[0]
+    lc = layer.c()
+    if out is None:
+        out = torch.empty(T, layer.hidden, dtype=torch.float32, device=x_bf16.device)
+    _check_out(x_bf16, (T, layer.hidden), _BF16, "x_bf16")
+    _check_out(out, (T, layer.hidden), torch.float32, "out")
+    _check_out(topk_ids, (T, layer.top_k), torch.int32, "topk_ids")
+    _check_out(topk_w, (T, layer.top_k), torch.float32, "topk_w")
+    if inter_out is not None:
+        _check_out(inter_out, (T * layer.top_k, layer.inter), torch.float32, "inter_out")
+    _check(_lib.escha_moe_layer_decode_static(
+        ctypes.byref(lc), _ptr(x_bf16, _BF16, "x"), T, _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_w, torch.float32, "topk_w"), _ptr(out, torch.float32, "y"),
+        _ptr(inter_out, torch.float32, "inter_out"), _stream(stream)))
+    return out
 
 
 def escha_rmsnorm_bf16(y: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | None = None, stream=None):

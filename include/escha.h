@@ -239,6 +239,25 @@ ESCHA_API int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t
                             void* stream);
 
 /*
+ * escha_moe_layer_decode for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument. Its scratch is one array of
+ * 8 MiB that the library holds on every device it runs on until the process
+ * ends (escha_moe_workspace_bytes(L, n_tokens, 0) must not exceed it: with
+ * hidden 2048, inter 512, top_k 8 that is 1 to 10 tokens, and 16 to 78
+ * tokens through the grouped kernels; a larger request returns
+ * ESCHA_E_WORKSPACE and launches nothing). The device address of that array
+ * is looked up on the first call on a device. Same kernels, same results
+ * as escha_moe_layer_decode. Every call on one device shares the one array:
+ * calls that overlap on a device (different streams, not ordered) race and
+ * must be serialised by the caller.
+ */
+ESCHA_API int escha_moe_layer_decode_static(const escha_moe_layer_t* L, const uint16_t* x_bf16,
+                                            int32_t n_tokens, const int32_t* topk_ids,
+                                            const float* topk_w, float* y, float* inter_out,
+                                            void* stream);
+
+/*
  * Between stacked layers: x = bf16( y / sqrt(mean(y^2) + eps) ) per row,
  * unit weight, no residual. y fp32 [n_tokens][n]; x_bf16 [n_tokens][n];
  * n a multiple of 128, at most 16384. Bit-identical to the normalisation
