@@ -166,6 +166,32 @@ def layer_tensors(seed: int, layer: int, n_experts: int = N_EXPERTS, experts=Non
     return out
 
 
+# ---------------------------------------------------------------- shared expert
+
+SHARED_INTER = 512
+_SH = 20  # tensor ids of the shared expert: _SH + 0..4
+# second moment of a uniform int8 value over [-128, 127]
+INT8_SECOND_MOMENT = (sum(q * q for q in range(-128, 128)) / 256.0)
+
+
+def shared_expert_tensors(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = SHARED_INTER):
+    """The shared expert of a layer in the w8a16 form: int8 weights uniform
+    over [-128, 127] (gate_up [2*inter][hidden], gate rows first; down
+    [hidden][inter]), f32 scales per group of 128 inputs of
+    U(0.5, 2) / (sqrt(E[q^2]) sqrt(in)) (outputs stay O(1)), and the fp16
+    shared_expert_gate row [hidden] of N(0, 1/hidden)."""
+    def q8(tid, out_f, in_f):
+        g = rng(seed, layer, 0, _SH + tid)
+        w = g.integers(-128, 128, size=(out_f, in_f), dtype=np.int16).astype(np.int8)
+        sc = (g.uniform(0.5, 2.0, size=(out_f, in_f // 128)) /
+              (np.sqrt(INT8_SECOND_MOMENT) * np.sqrt(in_f))).astype(np.float32)
+        return w, sc
+    gu_w, gu_s = q8(0, 2 * inter, hidden)
+    dn_w, dn_s = q8(1, hidden, inter)
+    gate = (rng(seed, layer, 0, _SH + 2).standard_normal(hidden) / np.sqrt(hidden)).astype(np.float16)
+    return dict(gu_w=gu_w, gu_s=gu_s, dn_w=dn_w, dn_s=dn_s, gate=gate.view(np.uint16).copy())
+
+
 # ---------------------------------------------------------------- workloads
 
 def stack_token_inputs(seed: int, n_layers: int, T: int, entry: int, E: int = N_EXPERTS,

@@ -26,6 +26,7 @@ _u16p = ctypes.POINTER(ctypes.c_uint16)
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
+_i8p = ctypes.POINTER(ctypes.c_int8)
 
 
 def build(force: bool = True) -> Path:
@@ -101,6 +102,13 @@ def lib():
         L.eo_expert_gemv.argtypes = [_u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _u16p, ctypes.c_int, _f64p]
         L.eo_expert_gemv.restype = ctypes.c_int
+        L.eo_q8_weight.argtypes = [ctypes.c_int8, ctypes.c_float]
+        L.eo_q8_weight.restype = ctypes.c_double
+        L.eo_q8_linear.argtypes = [_i8p, _f32p, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
+        L.eo_q8_linear.restype = None
+        L.eo_shared_expert.argtypes = [_i8p, _f32p, _i8p, _f32p, _u16p, ctypes.c_int, ctypes.c_int,
+                                       _u16p, ctypes.c_int, _f64p, _f64p, _f64p]
+        L.eo_shared_expert.restype = ctypes.c_int
         L.eo_rmsnorm_bf16.argtypes = [_f64p, ctypes.c_int, ctypes.c_int, ctypes.c_double, _u16p]
         L.eo_rmsnorm_bf16.restype = None
         _lib = L
@@ -316,3 +324,49 @@ def rmsnorm_bf16(y, eps: float = 1e-6) -> np.ndarray:
     x = np.zeros((T, n), dtype=np.uint16)
     lib().eo_rmsnorm_bf16(_p(yc, _f64p), T, n, float(eps), _p(x, _u16p))
     return x
+
+
+# ---------------------------------------------------------------- shared expert
+
+def q8_weight(q: int, scale: float) -> float:
+    """The f32 dequantised int8 weight scale * q."""
+    return float(lib().eo_q8_weight(int(q), float(scale)))
+
+
+def q8_linear(W, scales, x) -> np.ndarray:
+    """y = dequant(W) x in fp64: W int8 [out][in], scales f32 [out][in/128], x [in]."""
+    Wc = _c(W, np.int8)
+    out_f, in_f = Wc.shape
+    sc = _c(scales, np.float32)
+    xc = _c(x, np.float64)
+    y = np.zeros(out_f, dtype=np.float64)
+    lib().eo_q8_linear(_p(Wc, _i8p), _p(sc, _f32p), in_f, out_f, _p(xc, _f64p), _p(y, _f64p))
+    return y
+
+
+def shared_expert(S: dict, x_bf16, *, want_gate=False, want_inter=False):
+    """Shared expert + sigmoid gate of every token: S holds ``gu_w`` int8
+    [2I][H], ``gu_s`` f32 [2I][H/128], ``dn_w`` int8 [H][I], ``dn_s`` f32
+    [H][I/128], ``gate`` fp16 bits [H]. Returns out double [T][H] (and the
+    gates [T], the intermediate h [T][I] on request)."""
+    gu_w, gu_s = _c(S["gu_w"], np.int8), _c(S["gu_s"], np.float32)
+    dn_w, dn_s = _c(S["dn_w"], np.int8), _c(S["dn_s"], np.float32)
+    gate = _c(S["gate"], np.uint16)
+    H = gu_w.shape[1]
+    I = dn_w.shape[1]
+    x = _c(x_bf16, np.uint16).reshape(-1, H)
+    T = x.shape[0]
+    out = np.zeros((T, H), dtype=np.float64)
+    g = np.zeros(T, dtype=np.float64)
+    h = np.zeros((T, I), dtype=np.float64)
+    rc = lib().eo_shared_expert(_p(gu_w, _i8p), _p(gu_s, _f32p), _p(dn_w, _i8p), _p(dn_s, _f32p),
+                                _p(gate, _u16p), H, I, _p(x, _u16p), T, _p(out, _f64p), _p(g, _f64p),
+                                _p(h, _f64p))
+    if rc:
+        raise ValueError("shared_expert: bad shape")
+    res = [out]
+    if want_gate:
+        res.append(g)
+    if want_inter:
+        res.append(h)
+    return res[0] if len(res) == 1 else tuple(res)

@@ -516,6 +516,81 @@ EO_EXPORT int eo_expert_gemv(const uint16_t* code, const uint16_t* rin, const ui
   return rc;
 }
 
+/* ------------------------------------------------------------------------ */
+/* The shared expert: int8 weights with f32 group scales (w8a16) and its    */
+/* fp16 gate.                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Model card "...-trellis-mlx", exactness table: the shared expert (like
+ * the attention and embedding weights) is kept as int8 with f32 scales per
+ * group of 128, and its dequantised weight is the f32 product scale * w8;
+ * the activations are the 16-bit hidden state (w8a16). The router gates,
+ * shared_expert_gate among them, are fp16. Readings (S1-S4 in the design
+ * notes): weights int8 [out][in] with scales f32 [out][in/128], weight
+ * (o, i) scaled by scales[o][i/128]; the product is rounded once to binary32
+ * (it is what the f32 dequantisation computes) and everything after it is
+ * exact here (fp64).
+ */
+EO_EXPORT double eo_q8_weight(int8_t q, float scale) {
+  float w = scale * (float)q; /* one binary32 multiply, round to nearest even */
+  return (double)w;
+}
+
+/* y[o] = sum_i w(o, i) x[i]: W int8 [out][in], scales f32 [out][in/128]. */
+EO_EXPORT void eo_q8_linear(const int8_t* W, const float* scales, int in_f, int out_f,
+                            const double* x, double* y) {
+  int ng = in_f / 128;
+  for (int o = 0; o < out_f; o++) {
+    double acc = 0.0;
+    for (int i = 0; i < in_f; i++)
+      acc += eo_q8_weight(W[(size_t)o * in_f + i], scales[(size_t)o * ng + i / 128]) * x[i];
+    y[o] = acc;
+  }
+}
+
+/*
+ * The shared expert of one token, added to the routed experts' output:
+ *   gu = Wgu x (gate rows [0, inter), up rows [inter, 2 inter));
+ *   h = SiLU(gate) * up;  s = Wdn h;
+ *   g = sigmoid(gate_f16 . x);  out = g * s.
+ * Reading S2: the shared_expert_gate (a single fp16 row over the hidden
+ * state) scales the shared expert's output through a sigmoid before it is
+ * added to the routed output, as the Qwen MoE blocks do; S3: the gate's dot
+ * product is not rounded (unlike the router logits, for which the pages
+ * state the f16 rounding). x bf16 bits [T][hidden]; out double [T][hidden];
+ * gate_out (nullable) double [T] the sigmoid; h_out (nullable) double
+ * [T][inter]. Returns 0, or -1 on a bad shape.
+ */
+EO_EXPORT int eo_shared_expert(const int8_t* gu_w, const float* gu_s, const int8_t* dn_w,
+                               const float* dn_s, const uint16_t* gate_f16, int hidden, int inter,
+                               const uint16_t* x_bf16, int T, double* out, double* gate_out,
+                               double* h_out) {
+  if (hidden % 128 || inter % 128 || hidden <= 0 || inter <= 0 || T < 0) return -1;
+  double* x = (double*)malloc(sizeof(double) * hidden);
+  double* gu = (double*)malloc(sizeof(double) * 2 * inter);
+  double* h = (double*)malloc(sizeof(double) * inter);
+  double* sh = (double*)malloc(sizeof(double) * hidden);
+  for (int t = 0; t < T; t++) {
+    for (int i = 0; i < hidden; i++) x[i] = eo_bf16_to_double(x_bf16[(size_t)t * hidden + i]);
+    eo_q8_linear(gu_w, gu_s, hidden, 2 * inter, x, gu);
+    eo_swiglu(gu, inter, h);
+    eo_q8_linear(dn_w, dn_s, inter, hidden, h, sh);
+    double logit = 0.0;
+    for (int i = 0; i < hidden; i++) logit += eo_f16_to_double(gate_f16[i]) * x[i];
+    double g = 1.0 / (1.0 + exp(-logit));
+    for (int i = 0; i < hidden; i++) out[(size_t)t * hidden + i] = g * sh[i];
+    if (gate_out) gate_out[t] = g;
+    if (h_out)
+      for (int c = 0; c < inter; c++) h_out[(size_t)t * inter + c] = h[c];
+  }
+  free(x);
+  free(gu);
+  free(h);
+  free(sh);
+  return 0;
+}
+
 /*
  * Between stacked layers: x' = bf16( v / sqrt(mean(v^2) + eps) ), unit
  * weight, no residual. y double [T][n] -> x_out bf16 bits [T][n].

@@ -482,3 +482,99 @@ def test_router_f16_rounding_makes_ties(oracle_lib):
     assert list(ids[0]) == [2, 5]
     ids_exact, _ = oracle.route_topk(raw.astype(np.float32), 2)
     assert list(ids_exact[0]) == [5, 2]
+
+
+# ------------------------------------------------------------ shared expert (w8a16)
+
+def test_q8_dequant_is_one_binary32_product(oracle_lib):
+    """The exactness table's dequantisation, scale * w8 in f32: numpy's
+    float32 multiply (IEEE, round to nearest even) gives the same values,
+    over the whole int8 range and random scales."""
+    rs = np.random.default_rng(3)
+    q = np.arange(-128, 128, dtype=np.int8)
+    for scale in rs.uniform(1e-4, 1.0, size=6).astype(np.float32):
+        ref = (np.float32(scale) * q.astype(np.float32)).astype(np.float64)
+        got = np.array([oracle.q8_weight(int(v), float(scale)) for v in q])
+        assert np.array_equal(got, ref)
+    # a product that is not exact in binary32 is rounded, not kept in fp64
+    s = np.float32(1.0 + 2.0 ** -23)
+    assert oracle.q8_weight(3, float(s)) == float(np.float32(s * np.float32(3.0)))
+    assert oracle.q8_weight(3, float(s)) != 3.0 * float(s)
+
+
+def test_q8_linear_vs_numpy_matmul(oracle_lib):
+    """Against a numpy fp64 matmul of the numpy-dequantised matrix."""
+    S = synth.shared_expert_tensors(5, hidden=256, inter=128)
+    W, sc = S["gu_w"], S["gu_s"]
+    x = np.random.default_rng(1).standard_normal(W.shape[1])
+    deq = (np.repeat(sc, 128, axis=1) * W.astype(np.float32)).astype(np.float64)
+    ref = deq @ x
+    got = oracle.q8_linear(W, sc, x)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_q8_group_index_is_input_over_128(oracle_lib):
+    """Scales 2^g on group g, unit weights: a one-hot input at i returns
+    2^(i // 128) on every row (a per-row or i % 128 indexing would not)."""
+    out_f, in_f = 4, 512
+    W = np.ones((out_f, in_f), dtype=np.int8)
+    sc = np.tile(2.0 ** np.arange(in_f // 128), (out_f, 1)).astype(np.float32)
+    for i in (0, 127, 128, 300, 511):
+        x = np.zeros(in_f)
+        x[i] = 1.0
+        assert np.all(oracle.q8_linear(W, sc, x) == 2.0 ** (i // 128))
+
+
+def _tiny_shared(H=128, I=128, q=1, scale=1.0, gate=0.0):
+    return dict(gu_w=np.full((2 * I, H), q, np.int8), gu_s=np.full((2 * I, H // 128), scale, np.float32),
+                dn_w=np.full((H, I), q, np.int8), dn_s=np.full((H, I // 128), scale, np.float32),
+                gate=np.full(H, gate, np.float16).view(np.uint16))
+
+
+def test_shared_expert_closed_form(oracle_lib):
+    """Unit weights and scales s, a constant input a, a zero gate: gate and
+    up are s H a, h = SiLU(s H a) s H a, the down output is s I h, and the
+    sigmoid of a zero logit is exactly 1/2."""
+    H, I, s, a = 128, 128, 0.001, 0.5
+    S = _tiny_shared(H, I, 1, s, 0.0)
+    x = np.full((1, H), 0x3F00, np.uint16)  # bf16 0.5
+    out, g = oracle.shared_expert(S, x, want_gate=True)
+    gu = np.float64(np.float32(s)) * H * a
+    h = gu / (1.0 + np.exp(-gu)) * gu
+    assert g[0] == 0.5
+    assert np.allclose(out, 0.5 * np.float64(np.float32(s)) * I * h, rtol=1e-13, atol=0)
+
+
+def test_shared_expert_gate_is_sigmoid_of_fp16_dot(oracle_lib):
+    """Gate row fp16, input one-hot: the logit is that fp16 entry times the
+    bf16 input, and the output scales by its logistic function (scipy)."""
+    import scipy.special
+    H, I = 128, 128
+    S = _tiny_shared(H, I, 1, 0.001, 0.0)
+    gate = np.zeros(H, np.float16)
+    gate[17] = np.float16(-1.375)
+    S["gate"] = gate.view(np.uint16)
+    x = np.zeros((1, H), np.uint16)
+    x[0, 17] = 0x4000  # bf16 2.0
+    out, g = oracle.shared_expert(S, x, want_gate=True)
+    assert np.isclose(g[0], scipy.special.expit(-2.75), rtol=1e-15)
+    S0 = dict(S, gate=np.zeros(H, np.uint16))
+    out0 = oracle.shared_expert(S0, x)
+    assert np.allclose(out, out0 / 0.5 * g[0], rtol=1e-14, atol=0)
+
+
+def test_shared_expert_gate_rows_first(oracle_lib):
+    """h is SiLU of the first half of gate_up times the second half (the
+    halves taken from the int8 product), and swapping the halves changes h."""
+    H, I = 128, 128
+    S = synth.shared_expert_tensors(9, hidden=H, inter=I)
+    x = synth.activations(9, 1, H)
+    _, h = oracle.shared_expert(S, x, want_inter=True)
+    Sw = dict(S, gu_w=np.concatenate([S["gu_w"][I:], S["gu_w"][:I]]),
+              gu_s=np.concatenate([S["gu_s"][I:], S["gu_s"][:I]]))
+    _, hw = oracle.shared_expert(Sw, x, want_inter=True)
+    xd = np.array([oracle.bf16_to_double(int(v)) for v in x[0]])
+    gu = oracle.q8_linear(S["gu_w"], S["gu_s"], xd)
+    g, u = gu[:I], gu[I:]
+    assert np.allclose(h[0], g / (1 + np.exp(-g)) * u, rtol=1e-12, atol=1e-15)
+    assert not np.allclose(h, hw)
