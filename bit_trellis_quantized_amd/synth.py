@@ -166,6 +166,23 @@ def layer_tensors(seed: int, layer: int, n_experts: int = N_EXPERTS, experts=Non
     return out
 
 
+# ---------------------------------------------------------------- dense projections
+
+_BIAS = 30  # tensor ids of dense biases: _BIAS + 0 (gate_up), + 1 (down)
+
+
+def dense_mlp_tensors(seed: int, layer: int = 0, hidden: int = HIDDEN, inter: int = INTER,
+                      k_gu: int = K_GU, k_dn: int = K_DN, bias_scale: float = 0.25):
+    """A dense MLP of coded projections (the one-expert case, no prune mask):
+    the leaves of expert 0 at [1][...] plus f32 output biases of
+    N(0, bias_scale^2) on gate_up [2*inter] and down [hidden]."""
+    t = expert_tensors(seed, layer, 0, hidden=hidden, inter=inter, k_gu=k_gu, k_dn=k_dn, masks=False)
+    out = {k: v[None] for k, v in t.items() if k != "mask"}
+    out["gu_bias"] = (rng(seed, layer, 0, _BIAS).standard_normal(2 * inter) * bias_scale).astype(np.float32)
+    out["dn_bias"] = (rng(seed, layer, 0, _BIAS + 1).standard_normal(hidden) * bias_scale).astype(np.float32)
+    return out
+
+
 # ---------------------------------------------------------------- shared expert
 
 SHARED_INTER = 512

@@ -102,6 +102,13 @@ def lib():
         L.eo_expert_gemv.argtypes = [_u16p, _u16p, _u16p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                      _u16p, ctypes.c_int, _f64p]
         L.eo_expert_gemv.restype = ctypes.c_int
+        L.eo_dense_gemv.argtypes = [_u16p, _u16p, _u16p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    _u16p, ctypes.c_int, _f64p]
+        L.eo_dense_gemv.restype = ctypes.c_int
+        L.eo_dense_mlp.argtypes = [_u16p, _u16p, _u16p, _f32p, _u16p, _u16p, _u16p, _f32p, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, _u16p, ctypes.c_int, _f64p,
+                                   _f64p]
+        L.eo_dense_mlp.restype = ctypes.c_int
         L.eo_q8_weight.argtypes = [ctypes.c_int8, ctypes.c_float]
         L.eo_q8_weight.restype = ctypes.c_double
         L.eo_q8_linear.argtypes = [_i8p, _f32p, ctypes.c_int, ctypes.c_int, _f64p, _f64p]
@@ -370,3 +377,45 @@ def shared_expert(S: dict, x_bf16, *, want_gate=False, want_inter=False):
     if want_inter:
         res.append(h)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+# ---------------------------------------------------------------- dense projections with bias
+
+def dense_gemv(code, rin, rout, bias, in_f: int, out_f: int, K: int, x_bf16) -> np.ndarray:
+    """One coded projection (the one-expert case) plus an f32 output bias (or None)."""
+    c, ri, ro = _c(code, np.uint16), _c(rin, np.uint16), _c(rout, np.uint16)
+    b = None if bias is None else _c(bias, np.float32)
+    x = _c(x_bf16, np.uint16).reshape(-1, in_f)
+    T = x.shape[0]
+    y = np.zeros((T, out_f), dtype=np.float64)
+    rc = lib().eo_dense_gemv(_p(c, _u16p), _p(ri, _u16p), _p(ro, _u16p), _p(b, _f32p) if b is not None else None,
+                             in_f, out_f, K, _p(x, _u16p), T, _p(y, _f64p))
+    if rc:
+        raise ValueError("dense_gemv: bad shape")
+    return y
+
+
+def dense_mlp(M: dict, x_bf16, *, want_inter=False):
+    """A dense MLP of coded projections with f32 biases: M holds ``gu_code``
+    [H/16][2I/16][16Kgu], ``gu_rin``, ``gu_rout``, ``gu_bias`` (f32 [2I] or
+    None), ``dn_code``, ``dn_rin``, ``dn_rout``, ``dn_bias`` (f32 [H] or None).
+    Returns y double [T][H] (and h [T][I])."""
+    a = {n: _c(M[n], np.uint16) for n in ("gu_code", "gu_rin", "gu_rout", "dn_code", "dn_rin", "dn_rout")}
+    gb = None if M.get("gu_bias") is None else _c(M["gu_bias"], np.float32)
+    db = None if M.get("dn_bias") is None else _c(M["dn_bias"], np.float32)
+    H = a["gu_rin"].shape[-1]
+    I = a["dn_rin"].shape[-1]
+    k_gu = a["gu_code"].shape[-1] // 16
+    k_dn = a["dn_code"].shape[-1] // 16
+    x = _c(x_bf16, np.uint16).reshape(-1, H)
+    T = x.shape[0]
+    y = np.zeros((T, H), dtype=np.float64)
+    h = np.zeros((T, I), dtype=np.float64)
+    rc = lib().eo_dense_mlp(_p(a["gu_code"], _u16p), _p(a["gu_rin"], _u16p), _p(a["gu_rout"], _u16p),
+                            _p(gb, _f32p) if gb is not None else None, _p(a["dn_code"], _u16p),
+                            _p(a["dn_rin"], _u16p), _p(a["dn_rout"], _u16p),
+                            _p(db, _f32p) if db is not None else None, H, I, k_gu, k_dn, _p(x, _u16p), T,
+                            _p(y, _f64p), _p(h, _f64p))
+    if rc:
+        raise ValueError("dense_mlp: bad shape")
+    return (y, h) if want_inter else y

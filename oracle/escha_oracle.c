@@ -517,6 +517,71 @@ EO_EXPORT int eo_expert_gemv(const uint16_t* code, const uint16_t* rin, const ui
 }
 
 /* ------------------------------------------------------------------------ */
+/* Dense coded projections: the one-expert case, with additive biases.      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * hipfire PR, commit notes on the dense export: every coded projection of an
+ * Escha dense export carries an additive output bias, which no weight can
+ * absorb; the gate and up biases are added before the SwiGLU, and the down
+ * (and out_proj) bias lands on the output (the residual stream). A dense
+ * linear is the routed path with one expert, id 0, weight 1. Reading D1:
+ * the biases are f32 vectors added to the projection's output after rout
+ * (the output side of the coded projection is rout (.) H_n(z)).
+ * One projection: y[t] = proj(x[t]) + bias (bias may be NULL).
+ */
+EO_EXPORT int eo_dense_gemv(const uint16_t* code, const uint16_t* rin, const uint16_t* rout,
+                            const float* bias, int in_f, int out_f, int K, const uint16_t* x_bf16,
+                            int T, double* y) {
+  int rc = eo_expert_gemv(code, rin, rout, in_f, out_f, K, x_bf16, T, y);
+  if (rc || !bias) return rc;
+  for (int t = 0; t < T; t++)
+    for (int n = 0; n < out_f; n++) y[(size_t)t * out_f + n] += (double)bias[n];
+  return 0;
+}
+
+/*
+ * A dense MLP of coded projections: gu = gate_up(x) + gu_bias; g, u = the
+ * first and second halves; h = SiLU(g) * u; y = down(h) + dn_bias. Biases
+ * f32 (nullable). x bf16 bits [T][hidden]; y double [T][hidden]; h_out
+ * (nullable) double [T][inter]. Returns 0 or -1 on a bad shape.
+ */
+EO_EXPORT int eo_dense_mlp(const uint16_t* gu_code, const uint16_t* gu_rin, const uint16_t* gu_rout,
+                           const float* gu_bias, const uint16_t* dn_code, const uint16_t* dn_rin,
+                           const uint16_t* dn_rout, const float* dn_bias, int hidden, int inter,
+                           int k_gu, int k_dn, const uint16_t* x_bf16, int T, double* y,
+                           double* h_out) {
+  if (hidden % 128 || inter % 128 || T < 0) return -1;
+  int G = 2 * inter;
+  uint16_t* Wgu = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)G * hidden);
+  uint16_t* Wdn = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)hidden * inter);
+  double* x = (double*)malloc(sizeof(double) * hidden);
+  double* gu = (double*)malloc(sizeof(double) * G);
+  double* h = (double*)malloc(sizeof(double) * inter);
+  int rc = eo_reconstruct(gu_code, hidden, G, k_gu, Wgu);
+  if (!rc) rc = eo_reconstruct(dn_code, inter, hidden, k_dn, Wdn);
+  for (int t = 0; rc == 0 && t < T; t++) {
+    for (int c = 0; c < hidden; c++) x[c] = eo_bf16_to_double(x_bf16[(size_t)t * hidden + c]);
+    eo_proj(Wgu, gu_rin, gu_rout, hidden, G, x, gu);
+    if (gu_bias)
+      for (int c = 0; c < G; c++) gu[c] += (double)gu_bias[c];
+    eo_swiglu(gu, inter, h);
+    if (h_out)
+      for (int c = 0; c < inter; c++) h_out[(size_t)t * inter + c] = h[c];
+    double* yt = y + (size_t)t * hidden;
+    eo_proj(Wdn, dn_rin, dn_rout, inter, hidden, h, yt);
+    if (dn_bias)
+      for (int c = 0; c < hidden; c++) yt[c] += (double)dn_bias[c];
+  }
+  free(Wgu);
+  free(Wdn);
+  free(x);
+  free(gu);
+  free(h);
+  return rc;
+}
+
+/* ------------------------------------------------------------------------ */
 /* The shared expert: int8 weights with f32 group scales (w8a16) and its    */
 /* fp16 gate.                                                                 */
 /* ------------------------------------------------------------------------ */

@@ -578,3 +578,55 @@ def test_shared_expert_gate_rows_first(oracle_lib):
     g, u = gu[:I], gu[I:]
     assert np.allclose(h[0], g / (1 + np.exp(-g)) * u, rtol=1e-12, atol=1e-15)
     assert not np.allclose(h, hw)
+
+
+# ------------------------------------------------------------ dense projections with bias
+
+def _dense_unbatched(M):
+    return {k: (v[0] if k in ("gu_code", "gu_rin", "gu_rout", "dn_code", "dn_rin", "dn_rout") else v)
+            for k, v in M.items()}
+
+
+def test_dense_gemv_bias_vs_weff_matmul(oracle_lib):
+    """One coded projection plus its bias against numpy: W_eff @ x + b."""
+    M = synth.dense_mlp_tensors(3, hidden=256, inter=128)
+    D = _dense_unbatched(M)
+    x = synth.activations(3, 2, 256)
+    xd = np.array([[oracle.bf16_to_double(int(v)) for v in row] for row in x])
+    W = oracle.reconstruct(D["gu_code"], 256, 256, 2)
+    Weff = oracle.proj_weff(W, D["gu_rin"], D["gu_rout"])
+    ref = xd @ Weff.T + M["gu_bias"].astype(np.float64)
+    got = oracle.dense_gemv(D["gu_code"], D["gu_rin"], D["gu_rout"], M["gu_bias"], 256, 256, 2, x)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_dense_mlp_zero_input_isolates_the_biases(oracle_lib):
+    """x = 0 makes gate_up's coded output exactly zero, so the MLP reduces to
+    h = SiLU(b_gate) * b_up (the gate/up bias before the SwiGLU) and
+    y = down(h) + b_down; a bias added after the SwiGLU would give another h."""
+    H, I = 256, 128
+    M = synth.dense_mlp_tensors(4, hidden=H, inter=I)
+    D = _dense_unbatched(M)
+    x = np.zeros((1, H), np.uint16)
+    y, h = oracle.dense_mlp(M, x, want_inter=True)
+    bg, bu = M["gu_bias"][:I].astype(np.float64), M["gu_bias"][I:].astype(np.float64)
+    h_ref = bg / (1.0 + np.exp(-bg)) * bu
+    assert np.allclose(h[0], h_ref, rtol=1e-14, atol=0)
+    Wd = oracle.reconstruct(D["dn_code"], I, H, 3)
+    y_ref = oracle.proj_weff(Wd, D["dn_rin"], D["dn_rout"]) @ h_ref + M["dn_bias"].astype(np.float64)
+    assert np.allclose(y[0], y_ref, rtol=1e-12, atol=1e-12 * np.abs(y_ref).max())
+    h_after = np.zeros(I) + M["gu_bias"][:I]  # SiLU(0) * 0 + bias: the wrong placement
+    assert not np.allclose(h[0], h_after)
+
+
+def test_dense_mlp_without_bias_is_the_one_expert_layer(oracle_lib):
+    """A dense MLP is the routed layer with one expert, id 0, weight 1."""
+    H, I = 256, 128
+    M = synth.dense_mlp_tensors(5, hidden=H, inter=I)
+    M0 = dict(M, gu_bias=None, dn_bias=None)
+    x = synth.activations(5, 3, H)
+    y = oracle.dense_mlp(M0, x)
+    ids = np.zeros((3, 1), np.int32)
+    w = np.ones((3, 1), np.float32)
+    ref = oracle.moe_layer(M, x, ids, w)
+    assert np.array_equal(y, ref)
