@@ -112,6 +112,7 @@ def parse():
     ap.add_argument("--configs", default="2,3,5",
                     help="single-layer configurations timed after the stack on its resident layers "
                          "(2: batch-1 decode, 3: 64 tokens Zipf, 5: 4096-token prefill; empty: none)")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert timing")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -585,6 +586,77 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
     return entry
 
 
+def time_shared_expert(args, escha, synth, hip, log, n_distinct=96):
+    """The shared expert (w8a16) at 1 and 64 tokens, each call on the next of
+    n_distinct resident shared experts (96 x 3.1 MB, past the 256 MB
+    Infinity Cache), the calls of a sweep captured in one graph, probe
+    events around each call's two kernels (escha_probe_events_set)."""
+    import torch
+    H, I = synth.HIDDEN, synth.SHARED_INTER
+    experts = []
+    for i in range(n_distinct):
+        S = synth.shared_expert_tensors(70, layer=i)
+        experts.append(escha.SharedExpert(*(torch.from_numpy(S[k]).cuda() for k in ("gu_w", "gu_s", "dn_w", "dn_s")),
+                                          torch.from_numpy(S["gate"].view(np.int16)).cuda()))
+    wbytes = 3 * H * I + 4 * (3 * H * I // 128)  # int8 weights + f32 scales per call
+    out = {}
+    for T in (1, 64):
+        x = torch.from_numpy(synth.activations(71, T, H).view(np.int16)).cuda()
+        y = torch.zeros(T, H, dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(int(escha._lib.escha_shared_expert_workspace_bytes(
+            ctypes.byref(experts[0].c()), T)), 1), dtype=torch.uint8, device="cuda")
+        ev = [(hip.event(), hip.event()) for _ in range(n_distinct)]
+
+        def sweep(probes=True):
+            for i, S in enumerate(experts):
+                escha.escha_probe_events_set(ev[i] if probes else None)
+                try:
+                    escha.escha_shared_expert(S, x, out=y, accumulate=True, workspace=ws)
+                finally:
+                    escha.escha_probe_events_set(None)
+
+        sweep()
+        torch.cuda.synchronize()
+        g, in_graph = None, False
+        if not args.no_graph:
+            for attempt in (True, False):
+                try:
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        sweep(probes=attempt)
+                    torch.cuda.synchronize()
+                    in_graph = attempt
+                    break
+                except Exception as exc:
+                    log(f"shared expert: capture failed ({exc})")
+                    g = None
+        reps = 4
+        start, stop = hip.event(), hip.event()
+        stream = torch.cuda.current_stream().cuda_stream
+        hip.record(start, stream)
+        for _ in range(reps):
+            g.replay() if g is not None else sweep()
+        hip.record(stop, stream)
+        torch.cuda.synchronize()
+        if g is not None and not in_graph:
+            sweep()
+            torch.cuda.synchronize()
+        us = hip.elapsed_ms(start, stop) / (reps * n_distinct) * 1e3
+        call_us = float(np.mean([hip.elapsed_ms(a, b) for a, b in ev])) * 1e3
+        achieved = wbytes / (call_us / 1e6) / 1e9
+        out[str(T)] = {"us_per_call": round(us, 3), "tokens_per_s": round(T / (us / 1e6), 1),
+                       "graph": g is not None, "probe_ok": call_us <= us * 1.02,
+                       "roofline": {"kernel": "k_shared_gate_up + k_shared_down (int8 dequant in registers, "
+                                              "fp32 accumulate)", "bound": "hbm",
+                                    "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                    "bytes_per_launch": wbytes, "avg_launch_us": round(call_us, 3),
+                                    "samples": n_distinct}}
+        log(f"shared expert T={T}: {us:.2f} us per call")
+    return {"workload": f"shared expert w8a16 (hidden {H}, inter {I}), {n_distinct} distinct cycled",
+            "cases": out}
+
+
 def layer_workload(args, log):
     """One configuration alone, on freshly generated layers (for profiling)."""
     import torch
@@ -690,6 +762,10 @@ def main():
         log(f"config {cfg}: {steps} layer calls")
         configs[str(cfg)] = time_layer_config(args, escha, synth, hip, layers, cfg, steps, NL, log)
         torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    if not args.no_shared:
+        configs["shared_expert"] = time_shared_expert(args, escha, synth, hip, log)
         torch.cuda.empty_cache()
 
     out = {

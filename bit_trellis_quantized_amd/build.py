@@ -18,8 +18,8 @@ CSRC = PKG / "csrc"
 LIB = PKG / "libescha.so"
 ARCH = "gfx950"
 
-SOURCES = ["escha_kernels.hip", "escha_grouped.hip", "escha_stack.hip", "escha_static.hip",
-           "escha_api.cpp"]
+SOURCES = ["escha_kernels.hip", "escha_grouped.hip", "escha_stack.hip", "escha_shared.hip",
+           "escha_static.hip", "escha_api.cpp"]
 
 
 def hipcc() -> str:

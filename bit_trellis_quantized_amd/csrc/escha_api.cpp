@@ -150,10 +150,12 @@ struct LayerInput {
 };
 
 // One layer over T tokens through the streaming kernels.
+// gu_bias / dn_bias (nullable): the dense export's biases (one-expert case).
 int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, const int32_t* ids,
                      const float* w, float* y, float* inter_out, const DecodeWs& ws,
                      hipStream_t s, hipEvent_t probe_before = nullptr,
-                     hipEvent_t probe_after = nullptr) {
+                     hipEvent_t probe_after = nullptr, const float* gu_bias = nullptr,
+                     const float* dn_bias = nullptr) {
   const int P = T * L->top_k;
   escha::InPartialArgs a{};
   a.code = (const uint16_t*)L->gate_up.code;
@@ -194,6 +196,7 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   d.gu_chunks = L->hidden / 128;
   d.inter_out = inter_out;
   d.partial = ws.dn_part;
+  d.gu_bias = gu_bias;
   e = escha::launch_down_partial(d, L->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "down partial launch");
   rc = probe_proj(1, s);
@@ -207,6 +210,7 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   c.n_tokens = T;
   c.y = y;
   c.ss = ws.ss;
+  c.bias = dn_bias;
   e = escha::launch_combine(c, s);
   if (e != hipSuccess) return hip_fail(e, "combine launch");
   if (probe_after && (e = record_probe(probe_after, s)) != hipSuccess)
@@ -228,7 +232,7 @@ constexpr int32_t kSmallTileTokens = 16;  // tokens per small tile
 // weights once for up to 128 of its tokens.
 bool grouped_small(const escha_moe_layer_t* L, int64_t T, bool prefill) {
   const int64_t P = T * L->top_k;
-  return !prefill && L->inter % 256 == 0 && L->hidden % 256 == 0 &&
+  return !prefill && L->inter % 256 == 0 && L->hidden % 256 == 0 && L->inter <= 2048 &&
          P <= (int64_t)kSmallTileTokens * L->gate_up.n_experts;
 }
 
@@ -338,7 +342,8 @@ int group_layers(const escha_moe_layer_t* L, int T, const int32_t* ids, const Gr
 int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, const int32_t* ids,
                       const float* w, float* y, float* inter_out, const GroupedWs& g,
                       bool prefill, hipStream_t s, bool grouped = false, bool gather = true,
-                      bool combine = true) {
+                      bool combine = true, const float* gu_bias = nullptr,
+                      const float* dn_bias = nullptr) {
   const int P = T * L->top_k;
   const int E = L->gate_up.n_experts;
   const bool small = grouped_small(L, T, prefill);
@@ -373,6 +378,7 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   gu.t_row0 = g.t_row0;
   gu.t_rows = g.t_rows;
   gu.n_tiles = g.n_tiles;
+  gu.bias = gu_bias;
   int rc = probe_proj(0, s);
   if (rc) return rc;
   e = small ? escha::launch_small_gate_up(gu, max_tiles, L->gate_up.k_bits, s)
@@ -388,13 +394,14 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   dn.x_out = nullptr;
   dn.y_out = g.yd;
   dn.inter_out = nullptr;
+  dn.bias = nullptr;
   e = small ? escha::launch_small_down(dn, max_tiles, L->down.k_bits, s)
             : escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
   if (e != hipSuccess) return hip_fail(e, "grouped down launch");
   rc = probe_proj(1, s);
   if (rc) return rc;
   if (!combine) return ESCHA_OK;
-  escha::SortedCombineArgs c{g.yd, g.inv, L->hidden, L->top_k, T, y, nullptr};
+  escha::SortedCombineArgs c{g.yd, g.inv, L->hidden, L->top_k, T, y, nullptr, dn_bias};
   e = escha::launch_combine_sorted(c, s);
   if (e != hipSuccess) return hip_fail(e, "sorted combine launch");
   return ESCHA_OK;
@@ -492,6 +499,81 @@ int check_stack_call(const escha_moe_layer_t* layers, int32_t n_layers, const ui
   if (!workspace || workspace_bytes < need)
     return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   return ESCHA_OK;
+}
+
+// One projection of one expert through the streaming kernels (validated
+// arguments), plus an optional output bias.
+int expert_gemv_call(const escha_proj_t* w, int32_t expert, const uint16_t* x_bf16, int32_t n_tokens,
+                     float* y, void* workspace, const float* bias, hipStream_t s) {
+  escha::InPartialArgs a{};
+  a.code = (const uint16_t*)w->code;
+  a.rin = (const uint16_t*)w->rin;
+  a.rout = (const uint16_t*)w->rout;
+  a.n_experts = w->n_experts;
+  a.in_f = w->in_features;
+  a.out_f = w->out_features;
+  a.n_pairs = n_tokens;
+  a.top_k = 1;
+  a.ids = nullptr;
+  a.fixed_expert = expert;
+  a.x_bf16 = x_bf16;
+  a.partial = (float*)workspace;
+  hipError_t e = escha::launch_in_partial(a, w->k_bits, s);
+  if (e != hipSuccess) return hip_fail(e, "expert_gemv partial launch");
+  escha::FinishArgs f{};
+  f.partial = (const float*)workspace;
+  f.n_chunks = w->in_features / 128;
+  f.out_f = w->out_features;
+  f.n_pairs = n_tokens;
+  f.y = y;
+  f.bias = bias;
+  e = escha::launch_proj_finish(f, s);
+  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "expert_gemv finish launch");
+}
+
+// ---------------------------------------------------------------- dense
+
+// The one-expert layer of a dense MLP, or an error.
+int dense_layer(const escha_dense_mlp_t* M, escha_moe_layer_t* L) {
+  if (!M) return fail(ESCHA_E_NULL, "dense MLP descriptor is NULL");
+  if (M->gate_up.n_experts != 1 || M->down.n_experts != 1)
+    return fail(ESCHA_E_SHAPE, "dense MLP: n_experts must be 1 (gate_up %d, down %d)", M->gate_up.n_experts,
+                M->down.n_experts);
+  *L = escha_moe_layer_t{M->gate_up, M->down, M->hidden, M->inter, 1};
+  return check_layer(L);
+}
+
+size_t dense_route_bytes(int64_t T) { return 2 * round_up((size_t)T * sizeof(int32_t)); }
+
+int dense_mlp_call(const escha_dense_mlp_t* M, const uint16_t* x_bf16, int32_t n_tokens, float* y,
+                   float* inter_out, void* workspace, size_t workspace_bytes, void* stream,
+                   bool prefill) {
+  escha_moe_layer_t L;
+  int rc = dense_layer(M, &L);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!x_bf16 || !y) return fail(ESCHA_E_NULL, "x/y is NULL");
+  const size_t need = escha_dense_mlp_workspace_bytes(M, n_tokens, prefill ? 1 : 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  // the routing of the one-expert case (id 0, weight 1) at the workspace's start
+  int32_t* ids = (int32_t*)workspace;
+  float* w = (float*)((char*)workspace + round_up((size_t)n_tokens * sizeof(int32_t)));
+  void* rest = (char*)workspace + dense_route_bytes(n_tokens);
+  hipError_t e = escha::launch_fill_one_expert(ids, w, n_tokens, s);
+  if (e != hipSuccess) return hip_fail(e, "routing fill launch");
+  if (prefill || n_tokens >= kGroupedDecodeTokens) {
+    GroupedWs g;
+    grouped_ws(&L, n_tokens, rest, &g);
+    return run_layer_grouped(&L, x_bf16, n_tokens, ids, w, y, inter_out, g, prefill, s, false, true, true,
+                             M->gate_up_bias, M->down_bias);
+  }
+  const DecodeWs ws = decode_ws_carve(&L, n_tokens, rest);
+  const LayerInput in{x_bf16, nullptr, nullptr, 0.f, nullptr};
+  return run_layer_decode(&L, in, n_tokens, ids, w, y, inter_out, ws, s, nullptr, nullptr,
+                          M->gate_up_bias, M->down_bias);
 }
 
 }  // namespace
@@ -646,31 +728,9 @@ int escha_expert_gemv(const escha_proj_t* w, int32_t expert, const uint16_t* x_b
   const size_t need = escha_expert_gemv_workspace_bytes(w, n_tokens);
   if (!workspace || workspace_bytes < need)
     return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-  hipStream_t s = (hipStream_t)stream;
-  escha::InPartialArgs a{};
-  a.code = (const uint16_t*)w->code;
-  a.rin = (const uint16_t*)w->rin;
-  a.rout = (const uint16_t*)w->rout;
-  a.n_experts = w->n_experts;
-  a.in_f = w->in_features;
-  a.out_f = w->out_features;
-  a.n_pairs = n_tokens;
-  a.top_k = 1;
-  a.ids = nullptr;
-  a.fixed_expert = expert;
-  a.x_bf16 = x_bf16;
-  a.partial = (float*)workspace;
-  hipError_t e = escha::launch_in_partial(a, w->k_bits, s);
-  if (e != hipSuccess) return hip_fail(e, "expert_gemv partial launch");
-  escha::FinishArgs f{};
-  f.partial = (const float*)workspace;
-  f.n_chunks = w->in_features / 128;
-  f.out_f = w->out_features;
-  f.n_pairs = n_tokens;
-  f.y = y;
-  e = escha::launch_proj_finish(f, s);
-  return e == hipSuccess ? ESCHA_OK : hip_fail(e, "expert_gemv finish launch");
+  return expert_gemv_call(w, expert, x_bf16, n_tokens, y, workspace, nullptr, (hipStream_t)stream);
 }
+
 
 
 size_t escha_moe_workspace_bytes(const escha_moe_layer_t* L, int32_t n_tokens, int32_t prefill) {
@@ -736,6 +796,85 @@ int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t* x_bf16, 
   grouped_ws(L, n_tokens, workspace, &g);
   return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g, true,
                            (hipStream_t)stream);
+}
+
+size_t escha_dense_mlp_workspace_bytes(const escha_dense_mlp_t* M, int32_t n_tokens, int32_t prefill) {
+  if (!M || n_tokens < 0) return 0;
+  const escha_moe_layer_t L{M->gate_up, M->down, M->hidden, M->inter, 1};
+  return dense_route_bytes(n_tokens) + escha_moe_workspace_bytes(&L, n_tokens, prefill);
+}
+
+int escha_dense_mlp_decode(const escha_dense_mlp_t* M, const uint16_t* x_bf16, int32_t n_tokens, float* y,
+                           float* inter_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return dense_mlp_call(M, x_bf16, n_tokens, y, inter_out, workspace, workspace_bytes, stream, false);
+}
+
+int escha_dense_mlp_prefill(const escha_dense_mlp_t* M, const uint16_t* x_bf16, int32_t n_tokens, float* y,
+                            float* inter_out, void* workspace, size_t workspace_bytes, void* stream) {
+  return dense_mlp_call(M, x_bf16, n_tokens, y, inter_out, workspace, workspace_bytes, stream, true);
+}
+
+int escha_dense_gemv(const escha_proj_t* w, const float* bias, const uint16_t* x_bf16, int32_t n_tokens,
+                     float* y, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_proj(w, "dense_gemv");
+  if (rc) return rc;
+  if (w->n_experts != 1) return fail(ESCHA_E_SHAPE, "dense_gemv: n_experts=%d, must be 1", w->n_experts);
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!x_bf16 || !y) return fail(ESCHA_E_NULL, "x/y is NULL");
+  const size_t need = escha_expert_gemv_workspace_bytes(w, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return expert_gemv_call(w, 0, x_bf16, n_tokens, y, workspace, bias, (hipStream_t)stream);
+}
+
+size_t escha_shared_expert_workspace_bytes(const escha_shared_expert_t* S, int32_t n_tokens) {
+  if (!S || n_tokens < 0 || S->inter <= 0) return 0;
+  return round_up((size_t)n_tokens * S->inter * sizeof(float)) + round_up((size_t)n_tokens * sizeof(float));
+}
+
+int escha_shared_expert(const escha_shared_expert_t* S, const uint16_t* x_bf16, int32_t n_tokens,
+                        float* y, int32_t accumulate, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (!S) return fail(ESCHA_E_NULL, "shared expert descriptor is NULL");
+  if (!S->gate_up || !S->gate_up_scale || !S->down || !S->down_scale || !S->gate)
+    return fail(ESCHA_E_NULL, "shared expert: a weight, scale or gate pointer is NULL");
+  const int H = S->hidden, I = S->inter;
+  if (H < 1024 || H % 1024 || H > 16 * 64 * escha::kShMaxChunks)
+    return fail(ESCHA_E_SHAPE, "shared expert: hidden=%d is not a multiple of 1024 in [1024, %d]", H,
+                16 * 64 * escha::kShMaxChunks);
+  if (I < 512 || I % 512 || I > 8 * 64 * escha::kShMaxChunks)
+    return fail(ESCHA_E_SHAPE, "shared expert: inter=%d is not a multiple of 512 in [512, %d]", I,
+                8 * 64 * escha::kShMaxChunks);
+  if (!aligned(S->gate_up, 16) || !aligned(S->down, 16) || !aligned(S->gate_up_scale, 4) ||
+      !aligned(S->down_scale, 4) || !aligned(S->gate, 2))
+    return fail(ESCHA_E_ARG, "shared expert: misaligned weights (int8 16 B, scales 4 B)");
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!x_bf16 || !y) return fail(ESCHA_E_NULL, "x/y is NULL");
+  if (!aligned(x_bf16, 16)) return fail(ESCHA_E_ARG, "x_bf16 is not 16-byte aligned");
+  const size_t need = escha_shared_expert_workspace_bytes(S, n_tokens);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  escha::SharedArgs a{};
+  a.gu_w = S->gate_up;
+  a.gu_s = S->gate_up_scale;
+  a.dn_w = S->down;
+  a.dn_s = S->down_scale;
+  a.gate = S->gate;
+  a.hidden = H;
+  a.inter = I;
+  a.n_tokens = n_tokens;
+  a.x = x_bf16;
+  a.h = (float*)workspace;
+  a.glogit = (float*)((char*)workspace + round_up((size_t)n_tokens * I * sizeof(float)));
+  a.y = y;
+  a.accumulate = accumulate ? 1 : 0;
+  int rc = probe_proj(0, (hipStream_t)stream);
+  if (rc) return rc;
+  const hipError_t e = escha::launch_shared_expert(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "shared expert launch");
+  return probe_proj(1, (hipStream_t)stream);
 }
 
 int escha_rmsnorm_bf16(const float* y, int32_t n_tokens, int32_t n, float eps, uint16_t* x_bf16,

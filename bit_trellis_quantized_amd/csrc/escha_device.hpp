@@ -272,12 +272,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---- power-of-two scaling of activations rounded to fp16 ---------------
 //
 // Activations that enter a matrix-core contraction as fp16 are first
-// multiplied by 2^e, e chosen from the largest magnitude m of the block
-// they belong to so that m 2^e lies in [2^13, 2^14): far from fp16's
-// overflow (65504) and from its subnormals (below 2^-14), whatever the
-// magnitude of the input. The fp32 result is multiplied by 2^-e. A power of
-// two scales exactly, so wherever the unscaled values would have been
-// normal fp16 numbers the results carry the same bits as without scaling.
+// multiplied by 2^e, e a multiple of 8 chosen from the largest magnitude m
+// of the block they belong to so that m 2^e lies in [2^6, 2^14): far from
+// fp16's overflow (65504) and 20 binades above its subnormals (below
+// 2^-14), whatever the magnitude of the input. The fp32 result is
+// multiplied by 2^-e. A power of two scales exactly, so wherever the
+// unscaled values would have been normal fp16 numbers the results carry the
+// same bits as without scaling. The coarse steps make neighbouring blocks of
+// a row share their exponent unless their maxima straddle a step, so the
+// rescaling to a row's common exponent is mostly not needed.
 
 // Exponent marker of a block whose values are all exactly zero (+0 or -0,
 // no NaN): the block contributes exactly zero to any contraction.
@@ -286,15 +289,16 @@ constexpr int kExpZeroBlock = 1 << 20;
 // 2^e for |e| < 126 (exact).
 __device__ __forceinline__ float exp2i(int e) { return __int_as_float((e + 127) << 23); }
 
-// e with 2^13 <= m 2^e < 2^14 for a finite m > 0; 0 for an infinite or NaN
-// m (no scaling); kExpZeroBlock for m == 0. Clamped to |e| <= 100.
+// e, a multiple of 8, with 2^6 <= m 2^e < 2^14 for a finite m > 0; 0 for
+// an infinite or NaN m (no scaling); kExpZeroBlock for m == 0. Clamped to
+// |e| <= 96.
 __device__ __forceinline__ int fp16_block_exp(float m) {
   if (m == 0.0f) return kExpZeroBlock;
   if (!(m <= 3.0e38f)) return 0;
   int ex;
-  frexpf(m, &ex);  // 2^(ex - 1) <= m < 2^ex
-  int e = 14 - ex;
-  return e < -100 ? -100 : (e > 100 ? 100 : e);
+  frexpf(m, &ex);                 // 2^(ex - 1) <= m < 2^ex
+  int e = (14 - ex) & ~7;         // floor to a multiple of 8: m 2^e in [2^6, 2^14)
+  return e < -96 ? -96 : (e > 96 ? 96 : e);
 }
 
 // The exponent of a row whose blocks carry exponents ex[0..n): the
@@ -302,7 +306,14 @@ __device__ __forceinline__ int fp16_block_exp(float m) {
 // row of zero blocks gets 0.
 __device__ __forceinline__ int row_exp(const int32_t* __restrict__ ex, int n) {
   int e = kExpZeroBlock;
-  for (int c = 0; c < n; ++c) e = ex[c] < e ? ex[c] : e;
+  for (int c0 = 0; c0 < n; c0 += 8) {
+    // eight loads in flight at once (clamped indices: no load under a branch)
+    int v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = ex[c0 + q < n ? c0 + q : n - 1];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) e = v[q] < e ? v[q] : e;
+  }
   return e == kExpZeroBlock ? 0 : e;
 }
 

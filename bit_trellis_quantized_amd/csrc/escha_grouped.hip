@@ -308,6 +308,7 @@ __device__ __forceinline__ void mma_steps(const _Float16* wl, const _Float16* xl
 // with a power-of-two exponent per 128-input block (xexp [row][nblk]); each
 // 16-byte chunk is rescaled to its row's exponent (row_exp) before it goes
 // to LDS, so that a whole row enters the contraction at one scale.
+// rexp_out (RESCALE, LDS): each token row's exponent, for the epilogue.
 template <int K, bool RESCALE, class OutTile, class StepOf>
 __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ code_e, int n_nt,
                                                  int n_steps, StepOf step_of,
@@ -315,7 +316,7 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
                                                  const int32_t* __restrict__ xexp, int nblk,
                                                  int row0, int rows, OutTile out_tile,
                                                  _Float16* wl, _Float16* xl,
-                                                 f32x16 (&acc)[kMT][2]) {
+                                                 f32x16 (&acc)[kMT][2], int* rexp_out = nullptr) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: uniform per wave
   const int lane = tid & 63;
@@ -337,6 +338,7 @@ __device__ __forceinline__ void grouped_mainloop(const uint16_t* __restrict__ co
     const _Float16* xrow = X + (size_t)xr * x_pitch + 8 * xkc0;
     const int32_t* erow = RESCALE ? xexp + (size_t)xr * nblk : nullptr;
     const int e_row = RESCALE ? row_exp(erow, nblk) : 0;
+    if (RESCALE && rexp_out && tid < kTM) rexp_out[xtok] = e_row;  // for the epilogue
     auto issue = [&](int i, StepLoads<K>& L) {
       const int st = step_of(i);
       load_eighth<K>(code_e + ((size_t)(4 * st + dkt) * n_nt + gnt) * (16 * K) + o * (2 * K), L.raw);
@@ -472,6 +474,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const uint16_t* code_e = a.code + (size_t)e * (size_t)(a.hidden / 16) * n_nt * (16 * K);
 
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  __shared__ int rexp[kTM];  // the tile's input row exponents (read after the main loop's barriers)
+  if (threadIdx.x < rows) rexp[threadIdx.x] = a.x_exp_in[row0 + threadIdx.x];
   _Float16* wl = reinterpret_cast<_Float16*>(smem);
   _Float16* xl = wl + 2 * kWBuf;
   f32x16 acc[kMT][2];
@@ -494,6 +498,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const float rg0 = f16_to_f32(rg[lane]), rg1 = f16_to_f32(rg[lane + 64]);
   const float ru0 = f16_to_f32(ru[lane]), ru1 = f16_to_f32(ru[lane + 64]);
   const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
+  // the dense export's gate/up biases (zero for routed experts)
+  const float* bg = a.bias ? a.bias + 128 * c : nullptr;
+  const float bg0 = bg ? bg[lane] : 0.f, bg1 = bg ? bg[lane + 64] : 0.f;
+  const float bu0 = bg ? bg[a.inter + lane] : 0.f, bu1 = bg ? bg[a.inter + lane + 64] : 0.f;
   float* el = reinterpret_cast<float*>(smem);
   // every wave takes tokens wave, wave + kWaves, ... of the tile, two at a time
   // (two independent butterfly chains in flight)
@@ -509,7 +517,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       g1[q] = er[lane + 64];
       u0[q] = er[128 + lane];
       u1[q] = er[192 + lane];
-      us[q] = exp2i(-a.x_exp_in[row0 + (ok[q] ? tl : 0)]);  // undo the input row's scale
+      us[q] = exp2i(-rexp[ok[q] ? tl : 0]);  // undo the input row's scale
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -519,8 +527,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     float v0[2], v1[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const float h0 = silu(g0[q] * (kInvSqrt128 * rg0) * us[q]) * (u0[q] * (kInvSqrt128 * ru0) * us[q]);
-      const float h1 = silu(g1[q] * (kInvSqrt128 * rg1) * us[q]) * (u1[q] * (kInvSqrt128 * ru1) * us[q]);
+      const float h0 = silu(g0[q] * (kInvSqrt128 * rg0) * us[q] + bg0) * (u0[q] * (kInvSqrt128 * ru0) * us[q] + bu0);
+      const float h1 = silu(g1[q] * (kInvSqrt128 * rg1) * us[q] + bg1) * (u1[q] * (kInvSqrt128 * ru1) * us[q] + bu1);
       if (ok[q] && a.inter_out) {
         float* io = a.inter_out + (size_t)a.perm[row0 + tla + kWaves * q] * a.inter + 128 * c;
         io[lane] = h0;
@@ -590,6 +598,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   __shared__ int live_blk[kMaxDownBlocks];
   __shared__ int steps[kMaxDownBlocks * (128 / kStep)];
+  __shared__ int rexp[kTM];  // the tile's row exponents (written in the main loop)
   int n_steps = a.inter / kStep;
   const bool skip = nblk <= kMaxDownBlocks;  // uniform
   if (skip) n_steps = live_down_steps(a.x_exp_in, nblk, row0, rows, live_blk, steps);
@@ -604,7 +613,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       for (int q = 0; q < 16; ++q) acc[mt][tt][q] = 0.f;
   grouped_mainloop<K, true>(code_e, n_nt, n_steps, [&](int i) { return skip ? steps[i] : i; },
                             reinterpret_cast<const _Float16*>(a.x_in), a.inter, a.x_exp_in, nblk, row0,
-                            rows, [&](int j) { return 16 * r + j; }, wl, xl, acc);
+                            rows, [&](int j) { return 16 * r + j; }, wl, xl, acc, rexp);
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -626,9 +635,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       z2[q] = er[128 + lane];
       z3[q] = er[192 + lane];
       // the router weight, with the row's input exponent undone
-      wt[q] = ok[q] ? a.w[a.perm[row0 + tl]] *
-                          exp2i(-row_exp(a.x_exp_in + (size_t)(row0 + tl) * nblk, nblk))
-                    : 0.f;
+      wt[q] = ok[q] ? a.w[a.perm[row0 + tl]] * exp2i(-rexp[tl]) : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -661,28 +668,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 // (half 0 + half 1) before the epilogue. Work-group: 8 waves.
 // ------------------------------------------------------------------------
 constexpr int kSmallTM = 16;
+constexpr int kSmallMaxBlocks = 16;  // small tiles: inter <= 2048 (the host checks)
 
 struct SmallLds {
-  uint32_t stage[8 * Stage<3>::kDw];    // each wave's staged codes
-  float red[2][kSmallTM][256];          // per input half: [token][output]
-  int live[kMaxDownBlocks];             // down: 128-channel blocks nonzero for some token
-  int shift[kSmallTM][kMaxDownBlocks];  // down: block_shift of token n's block c
+  uint32_t stage[8 * Stage<3>::kDw];  // each wave's staged codes
+  float red[2][kSmallTM][256];        // per input half: [token][output]
+  int rexp[kSmallTM];                 // down: each token's row exponent
 };
 
-// The wave's partial sums over the live chunks among c0 .. c0 + nch - 1 of
-// the 16 output columns nt0 .. nt0 + 3; the tile's token rows are rows
-// row0 .. row0 + rows - 1 of X (pitch x_pitch; the columns of tokens >=
-// rows read row row0 and are never stored); lane (n, g) ends with outputs
-// 16j + 4g + q of tile j for token n in D[j][q]. RESCALE: X carries an
-// exponent per 128-input block, and shift(n, c) is the shift that takes
-// token n's chunk c to its row's exponent; the chunk's activations are
-// rescaled with it right before their contraction.
-template <int K, bool RESCALE, class Live, class Shift>
+// The wave's partial sums over chunks c0 .. c0 + nch - 1 of the 16 output
+// columns nt0 .. nt0 + 3; the tile's token rows are rows row0 .. row0 +
+// rows - 1 of X (pitch x_pitch; the columns of tokens >= rows read row row0
+// and are never stored); lane (n, g) ends with outputs 16j + 4g + q of tile
+// j for token n in D[j][q]. RESCALE: X carries an exponent per 128-input
+// block (xexp [row][nblk]); a chunk that is zero for every token of the
+// tile is skipped, and each chunk's activations are rescaled to the row's
+// exponent before their contraction. The row's exponent comes back in
+// e_row_out.
+template <int K, bool RESCALE>
 __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code_e, int n_nt, int c0,
                                                int nch, int nt0, const _Float16* __restrict__ X,
-                                               int x_pitch, int row0, int rows, Live live,
-                                               Shift shift, uint32_t* stage, int lane,
-                                               f32x4 (&D)[4]) {
+                                               int x_pitch, const int32_t* __restrict__ xexp, int nblk,
+                                               int row0, int rows, uint32_t* stage, int lane,
+                                               f32x4 (&D)[4], int& e_row_out) {
   const int n = lane & 15;
   const int gq = lane >> 4;
   const int xr = row0 + (n < rows ? n : 0);
@@ -690,17 +698,46 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int cend = c0 + nch;
+  // the first chunk's codes go out before anything else
+  u32x4 cv[Stage<K>::kPerLane];
+  stage_issue<K>(code_e, n_nt, 8 * c0, nt0, lane, cv);
+  // the row's block exponents, loaded together once (nblk <= kSmallMaxBlocks):
+  // the row exponent, and which chunks of this half are live for some token
+  // of the tile (a bit per chunk)
+  const int32_t* erow = RESCALE ? xexp + (size_t)xr * nblk : nullptr;
+  int e_row = 0;
+  uint32_t live_bits = 0xFFFFFFFFu;
+  if constexpr (RESCALE) {
+    // clamped indices: every load is issued unconditionally, back to back
+    // (a load under a branch would be waited for before the branch)
+    int eb_all[kSmallMaxBlocks], eb_half[kSmallMaxBlocks / 2];
+#pragma unroll
+    for (int b = 0; b < kSmallMaxBlocks; ++b) eb_all[b] = erow[b < nblk ? b : nblk - 1];
+#pragma unroll
+    for (int ch = 0; ch < kSmallMaxBlocks / 2; ++ch) eb_half[ch] = erow[c0 + (ch < nch ? ch : 0)];
+    int emin = kExpZeroBlock;
+#pragma unroll
+    for (int b = 0; b < kSmallMaxBlocks; ++b) emin = eb_all[b] < emin ? eb_all[b] : emin;
+    e_row = emin == kExpZeroBlock ? 0 : emin;
+    live_bits = 0;
+#pragma unroll
+    for (int ch = 0; ch < kSmallMaxBlocks / 2; ++ch)
+      if (__ballot(ch < nch && n < rows && eb_half[ch] != kExpZeroBlock) != 0) live_bits |= 1u << ch;
+  }
+  e_row_out = e_row;
+  auto live = [&](int c) { return ((live_bits >> (c - c0)) & 1u) != 0; };  // uniform
   auto next_live = [&](int c) {  // first live chunk after c, or cend
     for (++c; c < cend && !live(c); ++c) {
     }
     return c;
   };
-  int c = next_live(c0 - 1);
-  if (c >= cend) return;  // uniform: every chunk of this half is zero
-  u32x4 cv[Stage<K>::kPerLane];
-  stage_issue<K>(code_e, n_nt, 8 * c, nt0, lane, cv);
-  while (c < cend) {
+  // the first chunk is always contracted (its codes are already on the
+  // way; a dead first chunk only adds zeros), later dead chunks are skipped
+  int c = c0;
+  int eb = RESCALE ? erow[c] : 0;  // this chunk's block exponent (the next one's is loaded a chunk ahead)
+  do {
     const int cn = next_live(c);
+    const int eb_next = RESCALE ? erow[cn < cend ? cn : c] : 0;
     stage_store<K>(stage, lane, cv);
     // the chunk's activations, then the next chunk's codes (past the last
     // chunk: this chunk's again, never used), all in flight during the
@@ -710,13 +747,16 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
       B[pp] = *reinterpret_cast<const h16x8*>(xrow + 128 * c + 32 * pp + 8 * gq);
-    const int sh = RESCALE ? shift(n, c) : 0;
+    const int sh = RESCALE ? block_shift(e_row, eb) : 0;
     stage_issue<K>(code_e, n_nt, 8 * (cn < cend ? cn : c), nt0, lane, cv);
-    // the chunk's activations at the row's exponent (this waits for their
-    // loads only: the next chunk's codes stay in flight)
+    // the chunk's activations at the row's exponent, when some token of the
+    // wave needs it (this waits for their loads only: the next chunk's
+    // codes stay in flight)
     if constexpr (RESCALE) {
+      if (__ballot(sh != 0) != 0) {
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) B[pp] = rescale_h8(B[pp], sh);
+        for (int pp = 0; pp < 4; ++pp) B[pp] = rescale_h8(B[pp], sh);
+      }
     }
     // tile-row pairs decoded one ahead of their MFMAs into two operand sets
     // (32 VGPRs instead of 64): pair pp's MFMAs run on the matrix core while
@@ -736,7 +776,8 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
     mfma4(A0, B[2]);
     mfma4(A1, B[3]);
     c = cn;
-  }
+    eb = eb_next;
+  } while (c < cend);
 }
 
 // D of a wave (output quad nq, input half kh) -> sh.red[kh][token][output].
@@ -772,11 +813,12 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const int nt0 = nq < 2 ? 8 * c + 4 * nq : a.inter / 16 + 8 * c + 4 * (nq - 2);
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncg * 8 * n_nt * (16 * K);
   __shared__ SmallLds sh;
+  if (threadIdx.x < rows) sh.rexp[threadIdx.x] = a.x_exp_in[row0 + threadIdx.x];  // read after the barrier below
   f32x4 D[4];
+  int e_row;
   small_mainloop<K, false>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
-                           reinterpret_cast<const _Float16*>(a.x_in), a.hidden, row0, rows,
-                           [](int) { return true; }, [](int, int) { return 0; },
-                           sh.stage + wave * Stage<K>::kDw, lane, D);
+                           reinterpret_cast<const _Float16*>(a.x_in), a.hidden, nullptr, 0, row0, rows,
+                           sh.stage + wave * Stage<K>::kDw, lane, D, e_row);
   small_to_lds(D, sh, kh, nq, lane);
   __syncthreads();
   const uint16_t* rg = a.rout + (size_t)e * (2 * a.inter) + 128 * c;
@@ -785,20 +827,23 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const float rg0 = f16_to_f32(rg[lane]), rg1 = f16_to_f32(rg[lane + 64]);
   const float ru0 = f16_to_f32(ru[lane]), ru1 = f16_to_f32(ru[lane + 64]);
   const float rd0 = f16_to_f32(rd[lane]), rd1 = f16_to_f32(rd[lane + 64]);
+  const float* bg = a.bias ? a.bias + 128 * c : nullptr;  // dense gate/up biases
+  const float bg0 = bg ? bg[lane] : 0.f, bg1 = bg ? bg[lane + 64] : 0.f;
+  const float bu0 = bg ? bg[a.inter + lane] : 0.f, bu1 = bg ? bg[a.inter + lane + 64] : 0.f;
   for (int tok = 2 * wave; tok < 2 * wave + 2; ++tok) {
     if (tok >= rows) break;  // uniform over the wave
     const int i = row0 + tok;
-    const float us = exp2i(-a.x_exp_in[i]);  // undo the input row's scale
+    const float us = exp2i(-sh.rexp[tok]);  // undo the input row's scale
     const float* r0 = sh.red[0][tok];
     const float* r1 = sh.red[1][tok];
     float g0 = r0[lane] + r1[lane], g1 = r0[lane + 64] + r1[lane + 64];
     float u0 = r0[128 + lane] + r1[128 + lane], u1 = r0[192 + lane] + r1[192 + lane];
     fwht128(g0, g1);
     fwht128(u0, u1);
-    g0 = g0 * (kInvSqrt128 * rg0) * us;
-    g1 = g1 * (kInvSqrt128 * rg1) * us;
-    u0 = u0 * (kInvSqrt128 * ru0) * us;
-    u1 = u1 * (kInvSqrt128 * ru1) * us;
+    g0 = g0 * (kInvSqrt128 * rg0) * us + bg0;
+    g1 = g1 * (kInvSqrt128 * rg1) * us + bg1;
+    u0 = u0 * (kInvSqrt128 * ru0) * us + bu0;
+    u1 = u1 * (kInvSqrt128 * ru1) * us + bu1;
     const float h0 = silu(g0) * u0;
     const float h1 = silu(g1) * u1;
     if (a.inter_out) {
@@ -833,30 +878,12 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
   const int ncd = a.inter / 128;
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncd * 8 * n_nt * (16 * K);
   __shared__ SmallLds sh;
-  // the blocks nonzero for some token of the tile, and each token's shift
-  // per block (columns past the tile's rows read row 0: never stored)
-  const bool table = ncd <= kMaxDownBlocks;  // uniform
-  if (table) {
-    for (int c = threadIdx.x; c < ncd; c += blockDim.x) sh.live[c] = 0;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kSmallTM * ncd; idx += blockDim.x) {
-      const int n = idx / ncd, c = idx % ncd;
-      const int32_t* ex = a.x_exp_in + (size_t)(row0 + (n < rows ? n : 0)) * ncd;
-      sh.shift[n][c] = block_shift(row_exp(ex, ncd), ex[c]);
-      if (n < rows && ex[c] != kExpZeroBlock) sh.live[c] = 1;
-    }
-    __syncthreads();
-  }
   f32x4 D[4];
-  small_mainloop<K, true>(
-      code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq, reinterpret_cast<const _Float16*>(a.x_in),
-      a.inter, row0, rows, [&](int c) { return !table || sh.live[c] != 0; },
-      [&](int n, int c) {
-        if (table) return sh.shift[n][c];
-        const int32_t* ex = a.x_exp_in + (size_t)(row0 + (n < rows ? n : 0)) * ncd;
-        return block_shift(row_exp(ex, ncd), ex[c]);
-      },
-      sh.stage + wave * Stage<K>::kDw, lane, D);
+  int e_row;
+  small_mainloop<K, true>(code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq,
+                          reinterpret_cast<const _Float16*>(a.x_in), a.inter, a.x_exp_in, ncd, row0, rows,
+                          sh.stage + wave * Stage<K>::kDw, lane, D, e_row);
+  if (wave == 0 && lane < kSmallTM) sh.rexp[lane] = e_row;  // lane n: token n
   small_to_lds(D, sh, kh, nq, lane);
   __syncthreads();
   const uint16_t* ro = a.rout + (size_t)e * a.hidden + 256 * r;
@@ -866,7 +893,7 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
     if (tok >= rows) break;
     const int i = row0 + tok;
     // the router weight, with the row's input exponent undone
-    const float wt = a.w[a.perm[i]] * exp2i(-row_exp(a.x_exp_in + (size_t)i * ncd, ncd));
+    const float wt = a.w[a.perm[i]] * exp2i(-sh.rexp[tok]);
     const float* q0 = sh.red[0][tok];
     const float* q1 = sh.red[1][tok];
     float z0 = q0[lane] + q1[lane], z1 = q0[lane + 64] + q1[lane + 64];
@@ -899,6 +926,10 @@ __global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
     acc0 += yr[lane];
     acc1 += yr[lane + 64];
   }
+  if (a.bias) {  // the dense export's output bias, after the sum
+    acc0 += a.bias[128 * b + lane];
+    acc1 += a.bias[128 * b + lane + 64];
+  }
   float* y = a.y + (size_t)t * a.hidden + 128 * b;
   y[lane] = acc0;
   y[lane + 64] = acc1;
@@ -930,6 +961,30 @@ __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
   const int32_t* __restrict__ inv = a.inv + (size_t)t * k;
   const int32_t* __restrict__ inv_next = a.inv_next + (size_t)t * k;
   const int32_t* __restrict__ ids_next = a.ids_next + (size_t)t * k;
+  // the next layer's pairs of the first group and their input scales: a
+  // chain of dependent loads that does not depend on the combine, issued
+  // first so that it overlaps it
+  int dst[8];
+  uint16_t r0[8], r1[8];
+  auto load_group = [&](int j0) {
+    // clamped indices: the loads are issued unconditionally, back to back
+    int id[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int jq = j0 + q < k ? j0 + q : k - 1;
+      dst[q] = inv_next[jq];
+      id[q] = ids_next[jq];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      if (j0 + q >= k) dst[q] = -1;
+      const int e = dst[q] >= 0 ? id[q] : 0;  // a pair without a row may carry an invalid id
+      const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * (mine ? b : 0);
+      r0[q] = rr[lane];
+      r1[q] = rr[lane + 64];
+    }
+  };
+  load_group(0);
   // slots in groups of 8: every load of a group issued before its use (a
   // slot without a row reads row 0 and adds nothing)
   float acc0 = 0.f, acc1 = 0.f;
@@ -937,9 +992,12 @@ __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
     for (int j0 = 0; j0 < k; j0 += 8) {
       float v0[8], v1[8];
       bool ok[8];
+      int iv[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) iv[q] = inv[j0 + q < k ? j0 + q : k - 1];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const int i = j0 + q < k ? inv[j0 + q] : -1;
+        const int i = j0 + q < k ? iv[q] : -1;
         ok[q] = i >= 0;
         const float* yr = a.rows + (size_t)(ok[q] ? i : 0) * a.hidden + 128 * b;
         v0[q] = yr[lane];
@@ -973,32 +1031,26 @@ __global__ __launch_bounds__(1024) void k_combine_next(CombineNextArgs a) {
   // them: each pair's row scaled by the power of two taken from 16 times
   // its largest |rin (.) x| (the blocks' maxima meet in LDS)
   for (int j0 = 0; j0 < k; j0 += 8) {
-    int dst[8];
+    if (j0 > 0) load_group(j0);
     float v0[8], v1[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      dst[q] = j0 + q < k ? inv_next[j0 + q] : -1;
-      const int e = dst[q] >= 0 ? ids_next[j0 + q] : 0;
-      v0[q] = v1[q] = 0.f;
-      if (mine) {
-        const uint16_t* rr = a.rin_next + (size_t)e * a.hidden + 128 * b;
-        v0[q] = xf0 * f16_to_f32(rr[lane]);
-        v1[q] = xf1 * f16_to_f32(rr[lane + 64]);
-      }
-    }
-    __syncthreads();  // pmax of the previous group has been read
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
+      v0[q] = xf0 * f16_to_f32(r0[q]);
+      v1[q] = xf1 * f16_to_f32(r1[q]);
       const float m = wave_max(fmaxf(fabsf(v0[q]), fabsf(v1[q])));
       if (mine && lane == 0) pmax[b][q] = m;
     }
     __syncthreads();
+    // lane q < 8: pair q's largest magnitude over the blocks
+    float mq = 0.f;
+    if (lane < 8)
+      for (int bb = 0; bb < nb; ++bb) mq = fmaxf(mq, pmax[bb][lane]);
+    __syncthreads();  // pmax is rewritten by the next group
     if (!mine) continue;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if (dst[q] < 0) continue;  // uniform over the work-group
-      float m = 0.f;
-      for (int bb = 0; bb < nb; ++bb) m = fmaxf(m, pmax[bb][q]);
+      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mq), q));
       int ex = fp16_block_exp(16.0f * m);
       if (ex == kExpZeroBlock) ex = 0;
       if (b == 0 && lane == 0) a.xg_exp_next[dst[q]] = ex;

@@ -176,6 +176,12 @@ __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
       u0 += b[inter + lane];
       u1 += b[inter + lane + 64];
     }
+    if (a.gu_bias) {  // the dense export's gate/up biases, before the SiLU
+      g0 += a.gu_bias[128 * c + lane];
+      g1 += a.gu_bias[128 * c + lane + 64];
+      u0 += a.gu_bias[inter + 128 * c + lane];
+      u1 += a.gu_bias[inter + 128 * c + lane + 64];
+    }
     const float h0 = silu(g0) * u0;
     const float h1 = silu(g1) * u1;
     if (a.inter_out && g == 0) {
@@ -230,6 +236,10 @@ __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
     z0 += pp[(size_t)cc * a.out_f + lane];
     z1 += pp[(size_t)cc * a.out_f + lane + 64];
   }
+  if (a.bias) {
+    z0 += a.bias[128 * b + lane];
+    z1 += a.bias[128 * b + lane + 64];
+  }
   float* y = a.y + (size_t)p * a.out_f + 128 * b;
   y[lane] = z0;
   y[lane + 64] = z1;
@@ -252,6 +262,10 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
   for (int r = 0; r < n; ++r) {
     acc0 += pp[(size_t)r * a.hidden + lane];
     acc1 += pp[(size_t)r * a.hidden + lane + 64];
+  }
+  if (a.bias) {  // the dense export's output bias, after the sum
+    acc0 += a.bias[128 * b + lane];
+    acc1 += a.bias[128 * b + lane + 64];
   }
   float* y = a.y + (size_t)t * a.hidden + 128 * b;
   y[lane] = acc0;
@@ -674,10 +688,25 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
   if (inv) inv[i] = pos;
 }
 
+__global__ __launch_bounds__(256) void k_fill_one_expert(int32_t* __restrict__ ids, float* __restrict__ w,
+                                                        int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) {
+    ids[i] = 0;
+    w[i] = 1.0f;
+  }
+}
+
 // ------------------------------------------------------------------------
 // Host launchers.
 // ------------------------------------------------------------------------
 static hipError_t last_launch() { return hipGetLastError(); }
+
+hipError_t launch_fill_one_expert(int32_t* ids, float* w, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_one_expert, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids, w, n);
+  return last_launch();
+}
 
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s) {
   const unsigned grid = (unsigned)((size_t)a.n_pairs * (a.in_f / 128) * (a.out_f / 256));

@@ -48,6 +48,7 @@ struct DownPartialArgs {
   int32_t gu_chunks;
   float* inter_out;
   float* partial;
+  const float* gu_bias;  // nullable fp32 [2*in_f]: gate and up biases, added before the SiLU
 };
 
 // y[p] = sum over the chunks of a pair's transformed partials.
@@ -55,6 +56,7 @@ struct FinishArgs {
   const float* partial;
   int32_t n_chunks, out_f, n_pairs;
   float* y;
+  const float* bias;  // nullable fp32 [out_f], added to every row
 };
 
 // Per-token sum over slots (in order) and chunks of down's weighted partials.
@@ -65,6 +67,7 @@ struct CombineArgs {
   int32_t n_chunks, hidden, top_k, n_tokens;
   float* y;
   float* ss;
+  const float* bias;  // nullable fp32 [hidden], added after the slot sum
 };
 
 // Grouped path (pairs sorted by expert; see escha_grouped.hip).
@@ -100,6 +103,7 @@ struct GroupedArgs {
   const int32_t* t_row0;
   const int32_t* t_rows;
   const int32_t* n_tiles;
+  const float* bias;        // gate_up kernels: nullable fp32 [2*inter], added before the SiLU
 };
 
 // Combine of a layer's sorted pair outputs fused with the RMSNorm of the
@@ -123,7 +127,8 @@ struct SortedCombineArgs {
   const int32_t* inv;  // pair -> sorted index, -1 if the pair has none
   int32_t hidden, top_k, n_tokens;
   float* y;
-  float* ss;  // nullable
+  float* ss;           // nullable
+  const float* bias;   // nullable fp32 [hidden], added after the slot sum
 };
 
 // Decode of a whole stack of layers in one launch (escha_stack.hip). Every
@@ -189,11 +194,37 @@ hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hi
 hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s);
 hipError_t launch_combine_next(const CombineNextArgs& a, hipStream_t s);
 
+// The shared expert in its w8a16 form (escha_shared.hip): int8 weights with
+// f32 scales per group of 128 inputs; gu_w [2*inter][hidden] (gate rows
+// first), dn_w [hidden][inter]; gate fp16 [hidden]. h fp32 [T][inter] and
+// glogit fp32 [T] are scratch; y fp32 [T][hidden] receives (accumulate: is
+// increased by) sigmoid(gate . x) * down(SiLU(gate_x) * up_x).
+// hidden % 1024 == 0, hidden <= 1024 * kShMaxChunks; inter % 512 == 0,
+// inter <= 512 * kShMaxChunks.
+constexpr int kShMaxChunks = 4;
+struct SharedArgs {
+  const int8_t* gu_w;
+  const float* gu_s;
+  const int8_t* dn_w;
+  const float* dn_s;
+  const uint16_t* gate;
+  int32_t hidden, inter, n_tokens;
+  const uint16_t* x;
+  float* h;
+  float* glogit;
+  float* y;
+  int32_t accumulate;
+};
+hipError_t launch_shared_expert(const SharedArgs& a, hipStream_t s);
+
 // The device-resident scratch array of escha_static.hip (one per device,
 // kStaticScratchBytes): its device address on the current device, looked up
 // on the first call there and kept for the process.
 constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
 hipError_t static_scratch(void** ptr);
+
+// ids = 0 and weights = 1 for n pairs: the routing of the one-expert case.
+hipError_t launch_fill_one_expert(int32_t* ids, float* w, int n, hipStream_t s);
 
 hipError_t launch_in_partial(const InPartialArgs& a, int k_bits, hipStream_t s);
 hipError_t launch_down_partial(const DownPartialArgs& a, int k_bits, hipStream_t s);

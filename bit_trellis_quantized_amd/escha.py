@@ -43,9 +43,20 @@ class escha_proj_t(ctypes.Structure):
                 ("out_features", ctypes.c_int32), ("k_bits", ctypes.c_int32)]
 
 
+class escha_shared_expert_t(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("gate_up_scale", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("down_scale", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32)]
+
+
 class escha_moe_layer_t(ctypes.Structure):
     _fields_ = [("gate_up", escha_proj_t), ("down", escha_proj_t), ("hidden", ctypes.c_int32),
                 ("inter", ctypes.c_int32), ("top_k", ctypes.c_int32)]
+
+
+class escha_dense_mlp_t(ctypes.Structure):
+    _fields_ = [("gate_up", escha_proj_t), ("down", escha_proj_t), ("gate_up_bias", ctypes.c_void_p),
+                ("down_bias", ctypes.c_void_p), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -69,6 +80,12 @@ _SIGS = {
                                 ctypes.c_int),
     "escha_moe_layer_decode_static": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp],
                                       ctypes.c_int),
+    "escha_dense_mlp_workspace_bytes": ([_P(escha_dense_mlp_t), _i32, _i32], _sz),
+    "escha_dense_mlp_decode": ([_P(escha_dense_mlp_t), _vp, _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "escha_dense_mlp_prefill": ([_P(escha_dense_mlp_t), _vp, _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "escha_dense_gemv": ([_P(escha_proj_t), _vp, _vp, _i32, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "escha_shared_expert_workspace_bytes": ([_P(escha_shared_expert_t), _i32], _sz),
+    "escha_shared_expert": ([_P(escha_shared_expert_t), _vp, _i32, _vp, _i32, _vp, _sz, _vp], ctypes.c_int),
     "escha_rmsnorm_bf16": ([_vp, _i32, _i32, _f32, _vp, _vp], ctypes.c_int),
     "escha_moe_stack_workspace_bytes": ([_P(escha_moe_layer_t), _i32, _i32], _sz),
     "escha_moe_stack_decode": ([_P(escha_moe_layer_t), _i32, _vp, _i32, _vp, _vp, _f32, _vp, _vp,
@@ -376,6 +393,126 @@ def escha_moe_layer_decode_static(layer: MoeLayer, x_bf16, topk_ids, topk_w, out
         ctypes.byref(lc), _ptr(x_bf16, _BF16, "x"), T, _ptr(topk_ids, torch.int32, "topk_ids"),
         _ptr(topk_w, torch.float32, "topk_w"), _ptr(out, torch.float32, "y"),
         _ptr(inter_out, torch.float32, "inter_out"), _stream(stream)))
+    return out
+
+
+@dataclass
+class DenseMLP:
+    """A dense MLP of coded projections (one expert each) with fp32 biases."""
+    gate_up: Proj
+    down: Proj
+    gate_up_bias: torch.Tensor | None = None  # fp32 [2*inter]
+    down_bias: torch.Tensor | None = None     # fp32 [hidden]
+
+    @property
+    def hidden(self) -> int:
+        return self.gate_up.in_features
+
+    @property
+    def inter(self) -> int:
+        return self.down.in_features
+
+    def c(self) -> escha_dense_mlp_t:
+        if self.gate_up_bias is not None:
+            _check_out(self.gate_up_bias, (2 * self.inter,), torch.float32, "gate_up_bias")
+        if self.down_bias is not None:
+            _check_out(self.down_bias, (self.hidden,), torch.float32, "down_bias")
+        gb = _ptr(self.gate_up_bias, torch.float32, "gate_up_bias")
+        db = _ptr(self.down_bias, torch.float32, "down_bias")
+        return escha_dense_mlp_t(self.gate_up.c(), self.down.c(), gb.value if gb else None,
+                                 db.value if db else None, self.hidden, self.inter)
+
+
+def _dense_call(fn, M: DenseMLP, x_bf16, out, inter_out, workspace, stream, prefill):
+    T = x_bf16.shape[0]
+    mc = M.c()
+    if out is None:
+        out = torch.empty(T, M.hidden, dtype=torch.float32, device=x_bf16.device)
+    _check_out(x_bf16, (T, M.hidden), _BF16, "x_bf16")
+    _check_out(out, (T, M.hidden), torch.float32, "out")
+    if inter_out is not None:
+        _check_out(inter_out, (T, M.inter), torch.float32, "inter_out")
+    nbytes = _lib.escha_dense_mlp_workspace_bytes(ctypes.byref(mc), T, int(prefill))
+    if workspace is None:
+        workspace = _ws(nbytes, x_bf16.device)
+    _check(fn(ctypes.byref(mc), _ptr(x_bf16, _BF16, "x"), T, _ptr(out, torch.float32, "y"),
+              _ptr(inter_out, torch.float32, "inter_out"), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def escha_dense_mlp_decode(M: DenseMLP, x_bf16, out=None, inter_out=None, workspace=None, stream=None):
+    return _dense_call(_lib.escha_dense_mlp_decode, M, x_bf16, out, inter_out, workspace, stream, False)
+
+
+def escha_dense_mlp_prefill(M: DenseMLP, x_bf16, out=None, inter_out=None, workspace=None, stream=None):
+    return _dense_call(_lib.escha_dense_mlp_prefill, M, x_bf16, out, inter_out, workspace, stream, True)
+
+
+def escha_dense_gemv(w: Proj, x_bf16: torch.Tensor, bias: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None, stream=None):
+    x2 = x_bf16.reshape(-1, w.in_features)
+    T = x2.shape[0]
+    if out is None:
+        out = torch.empty(T, w.out_features, dtype=torch.float32, device=x_bf16.device)
+    _check_out(out, (T, w.out_features), torch.float32, "out")
+    if bias is not None:
+        _check_out(bias, (w.out_features,), torch.float32, "bias")
+    wc = w.c()
+    nbytes = _lib.escha_expert_gemv_workspace_bytes(ctypes.byref(wc), T)
+    if workspace is None:
+        workspace = _ws(nbytes, x_bf16.device)
+    _check(_lib.escha_dense_gemv(ctypes.byref(wc), _ptr(bias, torch.float32, "bias"), _ptr(x2, _BF16, "x"), T,
+                                 _ptr(out, torch.float32, "y"), _ptr(workspace), workspace.numel(),
+                                 _stream(stream)))
+    return out
+
+
+@dataclass
+class SharedExpert:
+    """The shared expert in its w8a16 form (device tensors): int8 weights,
+    f32 group-128 scales, the fp16 shared_expert_gate row."""
+    gate_up: torch.Tensor        # int8 [2*inter][hidden]
+    gate_up_scale: torch.Tensor  # f32 [2*inter][hidden/128]
+    down: torch.Tensor           # int8 [hidden][inter]
+    down_scale: torch.Tensor     # f32 [hidden][inter/128]
+    gate: torch.Tensor           # fp16 bits [hidden]
+
+    @property
+    def hidden(self) -> int:
+        return self.gate_up.shape[1]
+
+    @property
+    def inter(self) -> int:
+        return self.down.shape[1]
+
+    def c(self) -> escha_shared_expert_t:
+        H, I = self.hidden, self.inter
+        _check_out(self.gate_up, (2 * I, H), torch.int8, "gate_up")
+        _check_out(self.gate_up_scale, (2 * I, H // 128), torch.float32, "gate_up_scale")
+        _check_out(self.down, (H, I), torch.int8, "down")
+        _check_out(self.down_scale, (H, I // 128), torch.float32, "down_scale")
+        _check_out(self.gate, (H,), _F16, "gate")
+        return escha_shared_expert_t(_ptr(self.gate_up).value, _ptr(self.gate_up_scale).value,
+                                     _ptr(self.down).value, _ptr(self.down_scale).value,
+                                     _ptr(self.gate).value, H, I)
+
+
+def escha_shared_expert(S: SharedExpert, x_bf16: torch.Tensor, out: torch.Tensor | None = None,
+                        accumulate: bool = False, workspace: torch.Tensor | None = None, stream=None):
+    """out (+)= sigmoid(gate . x) * shared_expert(x) per token (fp32 [T][hidden])."""
+    T = x_bf16.shape[0]
+    sc = S.c()
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs the output to add into")
+        out = torch.empty(T, S.hidden, dtype=torch.float32, device=x_bf16.device)
+    _check_out(x_bf16, (T, S.hidden), _BF16, "x_bf16")
+    _check_out(out, (T, S.hidden), torch.float32, "out")
+    nbytes = _lib.escha_shared_expert_workspace_bytes(ctypes.byref(sc), T)
+    if workspace is None:
+        workspace = torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=x_bf16.device)
+    _check(_lib.escha_shared_expert(ctypes.byref(sc), _ptr(x_bf16, _BF16, "x"), T, _ptr(out, torch.float32, "y"),
+                                    int(bool(accumulate)), _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
 
 

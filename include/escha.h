@@ -258,6 +258,97 @@ ESCHA_API int escha_moe_layer_decode_static(const escha_moe_layer_t* L, const ui
                                             void* stream);
 
 /*
+ * Dense coded projections: the one-expert case of the routed path, with the
+ * additive output biases of an Escha dense export ([hipfire] commit notes:
+ * a dense linear is served through the indexed contract as one expert, id 0,
+ * weight 1; every coded projection of the dense export carries an additive
+ * bias, which no weight absorbs; the gate/up biases land before the SwiGLU,
+ * the down / out_proj bias on the output). Biases are fp32 and added after
+ * rout, to the projection's output.
+ *   gate_up, down  as in escha_moe_layer_t, each with n_experts == 1
+ *   gate_up_bias   nullable fp32 [2*inter]
+ *   down_bias      nullable fp32 [hidden]
+ */
+typedef struct escha_dense_mlp {
+  escha_proj_t gate_up;
+  escha_proj_t down;
+  const float* gate_up_bias;
+  const float* down_bias;
+  int32_t hidden;
+  int32_t inter;
+} escha_dense_mlp_t;
+
+/*
+ * y[t] = down(SiLU(g + b_g) * (u + b_u)) + b_down with g, u the halves of
+ * gate_up(x[t]); the same kernels as escha_moe_layer_decode / _prefill with
+ * one expert (_decode: the streaming kernels below 16 tokens, the grouped
+ * kernels from 16 on; _prefill: the 128-token grouped GEMMs, the expert's
+ * token list being all n_tokens tokens, i.e. expert_offsets = [0, n]).
+ * x bf16 [n_tokens][hidden]; y fp32 [n_tokens][hidden]; inter_out
+ * (nullable) fp32 [n_tokens][inter] receives h.
+ * workspace >= escha_dense_mlp_workspace_bytes(M, n_tokens, prefill).
+ */
+ESCHA_API size_t escha_dense_mlp_workspace_bytes(const escha_dense_mlp_t* M, int32_t n_tokens,
+                                                 int32_t prefill);
+ESCHA_API int escha_dense_mlp_decode(const escha_dense_mlp_t* M, const uint16_t* x_bf16, int32_t n_tokens,
+                                     float* y, float* inter_out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+ESCHA_API int escha_dense_mlp_prefill(const escha_dense_mlp_t* M, const uint16_t* x_bf16,
+                                      int32_t n_tokens, float* y, float* inter_out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
+ * One dense coded projection (n_experts == 1) plus its bias (nullable fp32
+ * [out_features]): y[t] = rout (.) H_n(W~ H_n(rin (.) x[t])) + bias, through
+ * the streaming kernels of escha_expert_gemv, whose workspace size it takes
+ * (escha_expert_gemv_workspace_bytes).
+ */
+ESCHA_API int escha_dense_gemv(const escha_proj_t* w, const float* bias, const uint16_t* x_bf16,
+                               int32_t n_tokens, float* y, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The MoE block's shared expert in its w8a16 form, and its gate
+ * ([trellis-mlx] exactness table: the shared expert is int8 with f32 scales
+ * per group of 128 inputs, its dequantised weight the f32 product
+ * scale * w8; shared_expert_gate is fp16. [mtplx] improvements table: int8
+ * weights applied by a fused matvec, never dequantised in memory):
+ *   gate_up        int8 [2*inter][hidden]: gate rows [0, inter), up rows
+ *                  [inter, 2*inter)
+ *   gate_up_scale  f32  [2*inter][hidden/128]: row o, inputs 128 g ..
+ *                  128 g + 127 use gate_up_scale[o][g]
+ *   down           int8 [hidden][inter]
+ *   down_scale     f32  [hidden][inter/128]
+ *   gate           fp16 [hidden]: the shared_expert_gate row
+ * hidden % 1024 == 0 and hidden <= 4096; inter % 512 == 0 and inter <= 2048.
+ * int8 tensors 16-byte aligned; scales 4-byte aligned.
+ */
+typedef struct escha_shared_expert {
+  const int8_t* gate_up;
+  const float* gate_up_scale;
+  const int8_t* down;
+  const float* down_scale;
+  const uint16_t* gate;
+  int32_t hidden;
+  int32_t inter;
+} escha_shared_expert_t;
+
+/*
+ * For every token t: y[t] (+)= sigmoid(gate . x[t]) * down(SiLU(g) * u),
+ * g, u = the gate and up halves of gate_up x[t], with weights
+ * scale * w8 (binary32 products) and fp32 accumulation. x bf16
+ * [n_tokens][hidden]; y fp32 [n_tokens][hidden]. accumulate != 0 adds into
+ * y (the routed experts' output of escha_moe_layer_decode/_prefill on the
+ * same stream: the MoE block's sum); 0 overwrites it. The gate's dot product
+ * is not rounded to fp16 (the pages state that rounding for the router
+ * logits only). workspace >= escha_shared_expert_workspace_bytes.
+ */
+ESCHA_API size_t escha_shared_expert_workspace_bytes(const escha_shared_expert_t* S, int32_t n_tokens);
+ESCHA_API int escha_shared_expert(const escha_shared_expert_t* S, const uint16_t* x_bf16,
+                                  int32_t n_tokens, float* y, int32_t accumulate, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Between stacked layers: x = bf16( y / sqrt(mean(y^2) + eps) ) per row,
  * unit weight, no residual. y fp32 [n_tokens][n]; x_bf16 [n_tokens][n];
  * n a multiple of 128, at most 16384. Bit-identical to the normalisation
@@ -344,7 +435,8 @@ ESCHA_API int escha_moe_stack_status(const void* workspace, int32_t* status, voi
  * calling thread (escha_moe_layer_decode / _prefill, and each layer of
  * escha_moe_stack_decode) records events[0] on its stream right before its
  * gate_up projection kernel and events[1] right after its down projection
- * kernel, so a caller can time the two projection kernels alone; events
+ * kernel, so a caller can time the two projection kernels alone (and
+ * escha_shared_expert around its two kernels); events
  * NULL or n_events == 0 removes the hook. The handles are hipEvent_t
  * created by the caller, who keeps them alive while the hook is set. Under
  * stream capture the records become external event nodes of the graph.

@@ -254,3 +254,48 @@ def test_probe_events_set_validates(lib):
     assert f(ctypes.cast(arr, ctypes.c_void_p), 2) == -1
     assert f(ctypes.cast(arr, ctypes.c_void_p), 3) == -7
     assert f(None, 0) == 0
+
+
+class Shared(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("gate_up_scale", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("down_scale", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("hidden", ctypes.c_int32),
+                ("inter", ctypes.c_int32)]
+
+
+def test_shared_expert_validates(lib):
+    f = lib.escha_shared_expert
+    f.argtypes = [ctypes.POINTER(Shared), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    ok = dict(gate_up=FAKE, gate_up_scale=FAKE, down=FAKE, down_scale=FAKE, gate=FAKE, hidden=2048, inter=512)
+    x, y = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE)
+    assert f(ctypes.byref(Shared(**dict(ok, down=None))), x, 1, y, 0, x, 1 << 20, None) == -1
+    assert f(ctypes.byref(Shared(**dict(ok, hidden=2000))), x, 1, y, 0, x, 1 << 20, None) == -2
+    assert f(ctypes.byref(Shared(**dict(ok, hidden=8192))), x, 1, y, 0, x, 1 << 20, None) == -2
+    assert f(ctypes.byref(Shared(**dict(ok, inter=384))), x, 1, y, 0, x, 1 << 20, None) == -2
+    assert f(ctypes.byref(Shared(**dict(ok, gate_up=FAKE + 8))), x, 1, y, 0, x, 1 << 20, None) == -7
+    assert f(ctypes.byref(Shared(**ok)), x, 1, y, 0, x, 16, None) == -4
+    assert f(ctypes.byref(Shared(**ok)), x, 0, y, 0, None, 0, None) == 0
+
+
+class DenseMLP(ctypes.Structure):
+    _fields_ = [("gate_up", Proj), ("down", Proj), ("gate_up_bias", ctypes.c_void_p),
+                ("down_bias", ctypes.c_void_p), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32)]
+
+
+def test_dense_entry_points_validate(lib):
+    f = lib.escha_dense_mlp_decode
+    f.argtypes = [ctypes.POINTER(DenseMLP), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    M = DenseMLP(_proj(n_experts=1), _proj(n_experts=1, in_features=512, out_features=2048, k_bits=3),
+                 None, None, 2048, 512)
+    x = ctypes.c_void_p(FAKE)
+    assert f(ctypes.byref(M), x, 4, x, None, x, 16, None) == -4  # workspace too small
+    M2 = DenseMLP(_proj(n_experts=2), M.down, None, None, 2048, 512)
+    assert f(ctypes.byref(M2), x, 4, x, None, x, 1 << 30, None) == -2  # not the one-expert case
+    M3 = DenseMLP(M.gate_up, M.down, None, None, 2048, 256)
+    assert f(ctypes.byref(M3), x, 4, x, None, x, 1 << 30, None) == -2  # inter disagrees
+    g = lib.escha_dense_gemv
+    g.argtypes = [ctypes.POINTER(Proj), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    p = _proj(n_experts=3)
+    assert g(ctypes.byref(p), None, x, 1, x, x, 1 << 30, None) == -2

@@ -1,12 +1,12 @@
 """GPU parity of the router logits (the step before routing) against the oracle.
 
 The kernel sums exact products in fp32, the oracle in fp64; both round once
-to fp16. A logit must be the fp16 rounding of a value within the fp32
-summation error bound of the exact sum: equal to the oracle's logit except
-near a rounding midpoint or for logits so small that fp16 steps are finer
-than that bound. The top-k is an
-integer decision taken on fp16 logits, so it is checked on the kernel's own
-logits (the same values on both sides), bit for bit.
+to fp16. A logit must be the fp16 rounding of a value within the worst-case
+fp32 error of the kernel's summation order: equal to the oracle's logit
+except near a rounding midpoint or for logits so small that fp16 steps are
+finer than that bound. The top-k is an integer decision taken on fp16
+logits, so it is checked on the kernel's own logits (the same values on both
+sides), bit for bit.
 """
 import numpy as np
 import pytest
@@ -30,27 +30,42 @@ def _f32(bits_bf16):
     return (np.asarray(bits_bf16, dtype=np.uint32) << 16).view(np.float32)
 
 
-def _check_logits(got, x, gate, rows=None):
+def _sum_depth(T, H, E):
+    """Most additions any logit's fp32 sum goes through, from the orders the
+    header documents: up to 8 tokens, each lane adds 32-input chunks l, l +
+    64, .. with FMAs and the 64 lane sums meet in a 6-level butterfly; more
+    tokens, ksplit slices of H / ksplit inputs summed in order, then the
+    slices in order (ksplit: the largest power of two <= 32 dividing H / 32
+    that keeps ceil(E/32) ceil(T/32) ksplit <= 4096)."""
+    if T <= 8:
+        return 32 * -(-(H // 32) // 64) + 6
+    tiles = -(-E // 32) * -(-T // 32)
+    ks = 1
+    while ks < 32 and (H // 32) % (2 * ks) == 0 and tiles * 2 * ks <= 4096:
+        ks *= 2
+    return H // ks + ks
+
+
+def _check_logits(got, x, gate, rows=None, T=None, E=None):
     """got: the kernel's logits [T][E] (or the rows `rows` of them).
 
-    The kernel sums exact products in fp32 in input order (in slices, then
-    the slices in order). Each addition errs by at most 2^-24 times the
-    partial sum, and the errors add up like a random walk over the H
-    additions, so the fp32 sum lies within delta = 8 * 2^-24 * sqrt(H) *
-    max|prefix sum| (the factor 8 covers slices starting from zero and the
-    statistical margin) of the exact sum. A logit must therefore lie between
-    the fp16 roundings of raw - delta and raw + delta: equal to the oracle's
-    logit unless the exact sum is within delta of a rounding midpoint (or so
-    small that fp16 steps are finer than delta)."""
+    Worst-case bound: a sum of exact products computed with n rounded fp32
+    additions (in any order of depth n) differs from the exact sum by at most
+    gamma_n sum |g_i x_i|, gamma_n = n u / (1 - n u), u = 2^-24. A logit must
+    therefore lie between the fp16 roundings of raw - delta and raw + delta:
+    equal to the oracle's logit unless the exact sum is within delta of a
+    rounding midpoint (or so small that fp16 steps are finer than delta)."""
     xs = x if rows is None else x[rows]
     g = got if rows is None else got[rows]
     ref, raw = oracle.router_logits(xs, gate, want_raw=True)
     assert np.array_equal(g.astype(np.float16).astype(np.float32), g), "logits are not fp16 values"
     H = x.shape[1]
-    g64 = gate.view(np.float16).astype(np.float64)
-    xf = _f32(xs).astype(np.float64)
-    max_prefix = np.stack([np.abs(np.cumsum(g64 * xf[t], axis=1)).max(axis=1) for t in range(len(xs))])
-    delta = 8.0 * 2.0 ** -24 * np.sqrt(H) * max_prefix
+    n = _sum_depth(T if T is not None else len(x), H, E if E is not None else gate.shape[0])
+    u = 2.0 ** -24
+    gamma = n * u / (1 - n * u)
+    g64 = np.abs(gate.view(np.float16).astype(np.float64))
+    xf = np.abs(_f32(xs).astype(np.float64))
+    delta = gamma * (xf @ g64.T)
     lo = (raw - delta).astype(np.float16).astype(np.float32)
     hi = (raw + delta).astype(np.float16).astype(np.float32)
     bad = (g < lo) | (g > hi)
@@ -82,7 +97,7 @@ def test_router_logits_prefill_sampled(escha):
     gate = synth.router_gate(75, E, H)
     got = escha.escha_router_logits(to_dev(x), to_dev(gate)).cpu().numpy()
     rows = np.r_[np.arange(0, T, 16), T - 1]
-    _check_logits(got, x, gate, rows)
+    _check_logits(got, x, gate, rows, T=T, E=E)
 
 
 def test_router_topk_on_kernel_logits(escha):
@@ -120,9 +135,11 @@ def test_router_f16_tie_breaks_to_lower_index(escha):
 
 def test_router_end_to_end_ids(escha):
     """Hidden states -> logits -> top-8 on the GPU against the oracle's
-    logits and top-8: on every token whose logits all equal the oracle's
-    (the rest differ only within the fp32 error bound checked above), the
-    expert ids match exactly; such tokens are the large majority."""
+    logits and top-8. Tokens whose logits all equal the oracle's (about 78%
+    of them) must get exactly the oracle's ids in order; every other token
+    must get the oracle's set of 8 experts unless one of its differing logits
+    lies within one fp16 step of the 8th or 9th largest logit (there the
+    rounding may legitimately move an expert across the boundary)."""
     T, H, E = 256, 2048, 256
     announce("router end to end T=256")
     x = synth.activations(77, T, H)
@@ -133,8 +150,20 @@ def test_router_end_to_end_ids(escha):
     ref_l = oracle.router_logits(x, gate)
     ref_ids, _ = oracle.route_topk(ref_l, 8)
     same = np.all(got_l == ref_l, axis=1)
-    assert same.mean() > 0.5, f"only {same.mean():.1%} of the tokens have identical logits"
+    assert same.mean() > 0.7, f"only {same.mean():.1%} of the tokens have identical logits"
     assert np.array_equal(got_ids[same], ref_ids[same])
+    near_boundary = 0
+    for t in np.nonzero(~same)[0]:
+        srt = np.sort(ref_l[t])[::-1]
+        b8, b9 = srt[7], srt[8]
+        diff = got_l[t] != ref_l[t]
+        step = np.spacing(np.abs(ref_l[t][diff]).astype(np.float16)).astype(np.float64)
+        close = (np.abs(ref_l[t][diff] - b8) <= step) | (np.abs(ref_l[t][diff] - b9) <= step)
+        if close.any():
+            near_boundary += 1
+            continue
+        assert set(got_ids[t].tolist()) == set(ref_ids[t].tolist()), f"token {t}: expert set differs"
     # the f16 rounding creates exact ties among the selected or boundary logits on some tokens
     ties = [len(np.unique(ref_l[t][ref_ids[t]])) < 8 for t in range(T)]
-    print(f"tokens with identical logits {same.mean():.1%}; tokens with a tie in the top-8 {np.mean(ties):.1%}")
+    print(f"tokens with identical logits {same.mean():.1%}; differing near the 8/9 boundary "
+          f"{near_boundary}; tokens with a tie in the top-8 {np.mean(ties):.1%}")
