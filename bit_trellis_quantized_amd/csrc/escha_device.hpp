@@ -323,26 +323,21 @@ __device__ __forceinline__ int block_shift(int er, int eb) {
   return eb == kExpZeroBlock ? 0 : er - eb;
 }
 
-// 8 fp16 values times 2^sh (sh <= 0): one packed multiply per pair by
-// 2^sh, an fp16 number for sh >= -24 (subnormal below -14), so the result
-// is rounded once to nearest even. Further shifts (a block more than 2^24
-// below its row's largest, whose values then fall below 2^-10 of a row
-// maximum of at most 2^14) take two multiplies, by 2^(sh + 24) and 2^-24,
-// and may round twice; below -48 every value rounds to zero.
+// 8 fp16 values times 2^sh (sh <= 0, a multiple of 8): one packed multiply
+// per pair by 2^sh, an fp16 number down to 2^-24 (subnormal below 2^-14), so
+// each value is rounded once to nearest even. A block more than 2^24 below
+// its row (sh < -24) gives zeros: its values are then below 2^-24 of the
+// row's largest, under the resolution of the fp32 sums they would join.
+// Branch-free: the callers run at their register limit, where a branch here
+// costs the LDS pipelining of the loop around it.
 typedef _Float16 h16x8v __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ _Float16 f16_pow2(int sh) {  // -24 <= sh <= 0
   return __builtin_bit_cast(_Float16, sh >= -14 ? (uint16_t)((sh + 15) << 10)
                                                 : (uint16_t)(1u << (sh + 24)));
 }
 __device__ __forceinline__ h16x8v rescale_h8(h16x8v v, int sh) {
-  if (sh == 0) return v;
-  if (sh >= -24) {
-    const _Float16 f = f16_pow2(sh);
-    return v * h16x8v{f, f, f, f, f, f, f, f};
-  }
-  if (sh < -48) return h16x8v{};
-  const _Float16 f = f16_pow2(sh + 24), g = f16_pow2(-24);
-  return (v * h16x8v{f, f, f, f, f, f, f, f}) * h16x8v{g, g, g, g, g, g, g, g};
+  const _Float16 f = sh < -24 ? (_Float16)0 : f16_pow2(sh);
+  return v * h16x8v{f, f, f, f, f, f, f, f};
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }

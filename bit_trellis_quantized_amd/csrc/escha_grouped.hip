@@ -683,14 +683,14 @@ struct SmallLds {
 // j for token n in D[j][q]. RESCALE: X carries an exponent per 128-input
 // block (xexp [row][nblk]); a chunk that is zero for every token of the
 // tile is skipped, and each chunk's activations are rescaled to the row's
-// exponent before their contraction. The row's exponent comes back in
-// e_row_out.
+// exponent before their contraction; the lanes n < 16 store the row
+// exponent of token n at rexp_out[n] when rexp_out is not null.
 template <int K, bool RESCALE>
 __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code_e, int n_nt, int c0,
                                                int nch, int nt0, const _Float16* __restrict__ X,
                                                int x_pitch, const int32_t* __restrict__ xexp, int nblk,
                                                int row0, int rows, uint32_t* stage, int lane,
-                                               f32x4 (&D)[4], int& e_row_out) {
+                                               f32x4 (&D)[4], int* rexp_out) {
   const int n = lane & 15;
   const int gq = lane >> 4;
   const int xr = row0 + (n < rows ? n : 0);
@@ -702,12 +702,16 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
   u32x4 cv[Stage<K>::kPerLane];
   stage_issue<K>(code_e, n_nt, 8 * c0, nt0, lane, cv);
   // the row's block exponents, loaded together once (nblk <= kSmallMaxBlocks):
-  // the row exponent, and which chunks of this half are live for some token
-  // of the tile (a bit per chunk)
-  const int32_t* erow = RESCALE ? xexp + (size_t)xr * nblk : nullptr;
-  int e_row = 0;
+  // the row exponent (stored at rexp_out[n] by the lanes n < 16 when
+  // rexp_out is given), which chunks of this half are live for some token of
+  // the tile (a bit per chunk, uniform), and each chunk's shift to the row
+  // exponent, packed as -shift / 8 in four bits per chunk (7: the block
+  // rounds to zero). Nothing else of the exponents stays live in the loop,
+  // which runs at the register limit.
   uint32_t live_bits = 0xFFFFFFFFu;
+  uint32_t sh_pack = 0;
   if constexpr (RESCALE) {
+    const int32_t* erow = xexp + (size_t)xr * nblk;
     // clamped indices: every load is issued unconditionally, back to back
     // (a load under a branch would be waited for before the branch)
     int eb_all[kSmallMaxBlocks], eb_half[kSmallMaxBlocks / 2];
@@ -718,13 +722,16 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
     int emin = kExpZeroBlock;
 #pragma unroll
     for (int b = 0; b < kSmallMaxBlocks; ++b) emin = eb_all[b] < emin ? eb_all[b] : emin;
-    e_row = emin == kExpZeroBlock ? 0 : emin;
+    const int e_row = emin == kExpZeroBlock ? 0 : emin;
+    if (rexp_out != nullptr && lane < kSmallTM) rexp_out[lane] = e_row;  // lane n: token n
     live_bits = 0;
 #pragma unroll
-    for (int ch = 0; ch < kSmallMaxBlocks / 2; ++ch)
+    for (int ch = 0; ch < kSmallMaxBlocks / 2; ++ch) {
       if (__ballot(ch < nch && n < rows && eb_half[ch] != kExpZeroBlock) != 0) live_bits |= 1u << ch;
+      const int q = -block_shift(e_row, eb_half[ch]) >> 3;  // exponents are multiples of 8
+      sh_pack |= (uint32_t)(q < 7 ? q : 7) << (4 * ch);
+    }
   }
-  e_row_out = e_row;
   auto live = [&](int c) { return ((live_bits >> (c - c0)) & 1u) != 0; };  // uniform
   auto next_live = [&](int c) {  // first live chunk after c, or cend
     for (++c; c < cend && !live(c); ++c) {
@@ -734,10 +741,8 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
   // the first chunk is always contracted (its codes are already on the
   // way; a dead first chunk only adds zeros), later dead chunks are skipped
   int c = c0;
-  int eb = RESCALE ? erow[c] : 0;  // this chunk's block exponent (the next one's is loaded a chunk ahead)
   do {
     const int cn = next_live(c);
-    const int eb_next = RESCALE ? erow[cn < cend ? cn : c] : 0;
     stage_store<K>(stage, lane, cv);
     // the chunk's activations, then the next chunk's codes (past the last
     // chunk: this chunk's again, never used), all in flight during the
@@ -747,16 +752,13 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
       B[pp] = *reinterpret_cast<const h16x8*>(xrow + 128 * c + 32 * pp + 8 * gq);
-    const int sh = RESCALE ? block_shift(e_row, eb) : 0;
+    const int sh = RESCALE ? -8 * (int)((sh_pack >> (4 * (c - c0))) & 7u) : 0;
     stage_issue<K>(code_e, n_nt, 8 * (cn < cend ? cn : c), nt0, lane, cv);
-    // the chunk's activations at the row's exponent, when some token of the
-    // wave needs it (this waits for their loads only: the next chunk's
-    // codes stay in flight)
+    // the chunk's activations at the row's exponent (this waits for their
+    // loads only: the next chunk's codes stay in flight)
     if constexpr (RESCALE) {
-      if (__ballot(sh != 0) != 0) {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) B[pp] = rescale_h8(B[pp], sh);
-      }
+      for (int pp = 0; pp < 4; ++pp) B[pp] = rescale_h8(B[pp], sh);
     }
     // tile-row pairs decoded one ahead of their MFMAs into two operand sets
     // (32 VGPRs instead of 64): pair pp's MFMAs run on the matrix core while
@@ -776,7 +778,6 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
     mfma4(A0, B[2]);
     mfma4(A1, B[3]);
     c = cn;
-    eb = eb_next;
   } while (c < cend);
 }
 
@@ -815,10 +816,9 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   __shared__ SmallLds sh;
   if (threadIdx.x < rows) sh.rexp[threadIdx.x] = a.x_exp_in[row0 + threadIdx.x];  // read after the barrier below
   f32x4 D[4];
-  int e_row;
   small_mainloop<K, false>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
                            reinterpret_cast<const _Float16*>(a.x_in), a.hidden, nullptr, 0, row0, rows,
-                           sh.stage + wave * Stage<K>::kDw, lane, D, e_row);
+                           sh.stage + wave * Stage<K>::kDw, lane, D, nullptr);
   small_to_lds(D, sh, kh, nq, lane);
   __syncthreads();
   const uint16_t* rg = a.rout + (size_t)e * (2 * a.inter) + 128 * c;
@@ -879,11 +879,9 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncd * 8 * n_nt * (16 * K);
   __shared__ SmallLds sh;
   f32x4 D[4];
-  int e_row;
   small_mainloop<K, true>(code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq,
                           reinterpret_cast<const _Float16*>(a.x_in), a.inter, a.x_exp_in, ncd, row0, rows,
-                          sh.stage + wave * Stage<K>::kDw, lane, D, e_row);
-  if (wave == 0 && lane < kSmallTM) sh.rexp[lane] = e_row;  // lane n: token n
+                          sh.stage + wave * Stage<K>::kDw, lane, D, wave == 0 ? sh.rexp : nullptr);
   small_to_lds(D, sh, kh, nq, lane);
   __syncthreads();
   const uint16_t* ro = a.rout + (size_t)e * a.hidden + 256 * r;

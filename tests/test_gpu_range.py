@@ -154,3 +154,49 @@ def test_prefill_pruned_block_skip(escha, pruned_layer):
     ids, w = _route(400, 96)
     ids = _with_expert(ids, 96)
     _check(escha, pruned_layer, Ldev, x, ids, w, escha.escha_moe_layer_prefill, "pruned block prefill")
+
+
+# ------------------------------------------------------- blocks far below their row
+
+# expert 5's (gate, up) rout on three 128-channel blocks, as fp16 bits
+# (None: unchanged): h there ends near 2^-38, 2^-20 and 2^-12 of the row's
+# largest value
+FAR_BLOCKS = {1: (0x0001, 0x0001), 2: (0x0001, None), 3: (0x0100, None)}
+
+
+@pytest.fixture(scope="module")
+def far_layer():
+    """The test layer with expert 5's gate (and on one block up) rout at fp16
+    subnormals: the down kernels see block exponents 8 to 40 above the row
+    exponent, so the rescale to the row exponent lands in fp16 subnormals
+    (2^-12, 2^-20) or below them (2^-38, where the block gives zeros)."""
+    L = {k: v.copy() for k, v in synth.layer_tensors(40, 0, n_experts=E).items()}
+    rs = np.random.default_rng(9)
+    inter = L["mask"].shape[1]
+    for blk, (g_bits, u_bits) in FAR_BLOCKS.items():
+        for off, bits in ((0, g_bits), (inter, u_bits)):
+            if bits is not None:
+                sign = rs.integers(0, 2, 128).astype(np.uint16) << 15
+                pruned = L["mask"][PRUNED_EXPERT, 128 * blk:128 * blk + 128]  # rout stays zero there
+                L["gu_rout"][PRUNED_EXPERT, off + 128 * blk:off + 128 * blk + 128] = np.where(
+                    pruned, np.uint16(0), sign | np.uint16(bits))
+    return L
+
+
+@pytest.mark.parametrize("T", [2, 24, 160])
+def test_decode_far_blocks(escha, far_layer, T):
+    announce(f"decode with blocks far below their row, T={T}")
+    Ldev = layer_to_dev(far_layer)
+    x = _scaled_x(500 + T, T, 1.0)
+    ids, w = _route(500 + T, T)
+    ids = _with_expert(ids, T)
+    _check(escha, far_layer, Ldev, x, ids, w, escha.escha_moe_layer_decode, f"far blocks T={T}")
+
+
+def test_prefill_far_blocks(escha, far_layer):
+    announce("prefill with blocks far below their row, T=96")
+    Ldev = layer_to_dev(far_layer)
+    x = _scaled_x(600, 96, 1.0)
+    ids, w = _route(600, 96)
+    ids = _with_expert(ids, 96)
+    _check(escha, far_layer, Ldev, x, ids, w, escha.escha_moe_layer_prefill, "far blocks prefill")
