@@ -11,6 +11,7 @@
 // input dimension land in a partial buffer that the next kernel reduces in
 // a fixed order, so results are bit-reproducible with no atomics.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "escha_device.hpp"
@@ -517,8 +518,50 @@ __global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__
 
 // ------------------------------------------------------------------------
 // Router: softmax + top-k per token. grid.x = n_tokens, block = 64; each
-// lane holds kMaxPer logits (E <= 64 kMaxPer).
+// lane holds kMaxPer logits (E <= 64 kMaxPer). The wave-wide reductions run
+// on DPP and permlane swaps (no LDS round trips): the max, the sum of the
+// exponentials, and per selected expert an argmax.
 // ------------------------------------------------------------------------
+
+// (ov, oi) replaces (bv, bi) when it ranks higher: larger value, then
+// smaller index.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// The highest-ranking (value, index) pair of the wave, in every lane.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  auto within_rows = [&](auto h) {
+    constexpr int H = decltype(h)::value;
+    const float ov = xor_lane<H>(bv);
+    const int oi = __float_as_int(xor_lane<H>(__int_as_float(bi)));
+    take_better(bv, bi, ov, oi);
+  };
+  within_rows(std::integral_constant<int, 1>{});
+  within_rows(std::integral_constant<int, 2>{});
+  within_rows(std::integral_constant<int, 4>{});
+  within_rows(std::integral_constant<int, 8>{});
+  // rows 16 apart, then halves 32 apart: both lanes of a pair see the same
+  // two candidates (r[0], r[1]) and keep the same one
+  {
+    const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto ri = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    bv = __uint_as_float(rv[0]);
+    bi = (int)ri[0];
+    take_better(bv, bi, __uint_as_float(rv[1]), (int)ri[1]);
+  }
+  {
+    const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto ri = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
+    bv = __uint_as_float(rv[0]);
+    bi = (int)ri[0];
+    take_better(bv, bi, __uint_as_float(rv[1]), (int)ri[1]);
+  }
+}
+
 template <int kMaxPer>
 __global__ __launch_bounds__(64) void k_route_topk(const float* __restrict__ logits, int E, int k,
                                                    int32_t* __restrict__ ids,
@@ -536,35 +579,20 @@ __global__ __launch_bounds__(64) void k_route_topk(const float* __restrict__ log
     m = fmaxf(m, v[j]);
     if (e >= E) taken |= 1u << j;
   }
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
+  m = wave_max(m);
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < kMaxPer; ++j)
     if (lane + 64 * j < E) s += expf(v[j] - m);
-#pragma unroll
-  for (int h = 32; h >= 1; h >>= 1) s += __shfl_xor(s, h, 64);
+  s = wave_sum(s);
   for (int r = 0; r < k; ++r) {
-    // lane-local best untaken: larger value, then lower index
+    // lane-local best untaken, then the wave's
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int e = lane + 64 * j;
-      if (!(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bi))) {
-        bv = v[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) {
-      const float ov = __shfl_xor(bv, h, 64);
-      const int oi = __shfl_xor(bi, h, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    for (int j = 0; j < kMaxPer; ++j)
+      if (!(taken & (1u << j))) take_better(bv, bi, v[j], lane + 64 * j);
+    wave_argmax(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == 0) {
       ids[(size_t)t * k + r] = bi;
