@@ -840,12 +840,12 @@ int escha_shared_expert(const escha_shared_expert_t* S, const uint16_t* x_bf16, 
   if (!S->gate_up || !S->gate_up_scale || !S->down || !S->down_scale || !S->gate)
     return fail(ESCHA_E_NULL, "shared expert: a weight, scale or gate pointer is NULL");
   const int H = S->hidden, I = S->inter;
-  if (H < 1024 || H % 1024 || H > 16 * 64 * escha::kShMaxChunks)
+  if (H < 1024 || H % 1024 || H > escha::kShMaxHidden)
     return fail(ESCHA_E_SHAPE, "shared expert: hidden=%d is not a multiple of 1024 in [1024, %d]", H,
-                16 * 64 * escha::kShMaxChunks);
-  if (I < 512 || I % 512 || I > 8 * 64 * escha::kShMaxChunks)
+                escha::kShMaxHidden);
+  if (I < 512 || I % 512 || I > escha::kShMaxInter)
     return fail(ESCHA_E_SHAPE, "shared expert: inter=%d is not a multiple of 512 in [512, %d]", I,
-                8 * 64 * escha::kShMaxChunks);
+                escha::kShMaxInter);
   if (!aligned(S->gate_up, 16) || !aligned(S->down, 16) || !aligned(S->gate_up_scale, 4) ||
       !aligned(S->down_scale, 4) || !aligned(S->gate, 2))
     return fail(ESCHA_E_ARG, "shared expert: misaligned weights (int8 16 B, scales 4 B)");

@@ -199,9 +199,11 @@ hipError_t launch_combine_next(const CombineNextArgs& a, hipStream_t s);
 // first), dn_w [hidden][inter]; gate fp16 [hidden]. h fp32 [T][inter] and
 // glogit fp32 [T] are scratch; y fp32 [T][hidden] receives (accumulate: is
 // increased by) sigmoid(gate . x) * down(SiLU(gate_x) * up_x).
-// hidden % 1024 == 0, hidden <= 1024 * kShMaxChunks; inter % 512 == 0,
-// inter <= 512 * kShMaxChunks.
-constexpr int kShMaxChunks = 4;
+// hidden % 1024 == 0, hidden <= kShMaxHidden (the gate_up work-group's waves
+// take one or two 128-input groups each, at most 16 waves); inter % 512 == 0,
+// inter <= kShMaxInter (the down work-group's waves take one group each).
+constexpr int kShMaxHidden = 4096;
+constexpr int kShMaxInter = 2048;
 struct SharedArgs {
   const int8_t* gu_w;
   const float* gu_s;
