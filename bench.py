@@ -646,8 +646,8 @@ def time_shared_expert(args, escha, synth, hip, log, n_distinct=96):
         achieved = wbytes / (call_us / 1e6) / 1e9
         out[str(T)] = {"us_per_call": round(us, 3), "tokens_per_s": round(T / (us / 1e6), 1),
                        "graph": g is not None, "probe_ok": call_us <= us * 1.02,
-                       "roofline": {"kernel": "k_shared_gate_up + k_shared_down (int8 dequant in registers, "
-                                              "fp32 accumulate)", "bound": "hbm",
+                       "roofline": {"kernel": "k_shared_gate_up + k_shared_down (bf16 MFMA on exact int8 x bf16 "
+                                              "products, group scales in fp32)", "bound": "hbm",
                                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                                     "bytes_per_launch": wbytes, "avg_launch_us": round(call_us, 3),
