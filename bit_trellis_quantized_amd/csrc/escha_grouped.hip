@@ -1099,6 +1099,45 @@ __global__ __launch_bounds__(64) void k_decode_operands_mfma(const uint16_t* __r
     }
 }
 
+// Column-pair layout (PairDecoder, K = 2: the one-launch kernel's gate_up
+// tasks): the same staged region; lane (m, g) holds in register i of
+// A[pp][j] the weights of output columns c = m & 7 and c + 8 of tile nt0 + j,
+// input row 8 (m >> 3) + 4 (g & 1) + i of tile-row kt0 + 2 pp + (g >> 1).
+// grid.x = (in/128) * (out/64), block = 64.
+__global__ __launch_bounds__(64) void k_decode_operands_pairs(const uint16_t* __restrict__ code_e, int in_f,
+                                                              int out_f, uint16_t* __restrict__ w) {
+  __shared__ uint32_t stage[Stage<2>::kDw];
+  const int n_nt = out_f / 16;
+  const int nq = n_nt / 4;
+  const int kt0 = 8 * (blockIdx.x / nq);
+  const int nt0 = 4 * (blockIdx.x % nq);
+  const int lane = threadIdx.x;
+  u32x4 cv[Stage<2>::kPerLane];
+  stage_issue<2>(code_e, n_nt, kt0, nt0, lane, cv);
+  stage_store<2>(stage, lane, cv);
+  const PairDecoder dec(stage, lane);
+  h16x8 A[4][4];
+  dec.decode<0>(A[0]);
+  dec.decode<1>(A[1]);
+  dec.decode<2>(A[2]);
+  dec.decode<3>(A[3]);
+  const int m = lane & 15, g = lane >> 4;
+  const int c = m & 7;
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * (nt0 + j) + c;  // output c (and c + 8 eight rows on)
+      const int col0 = 16 * (kt0 + 2 * pp + (g >> 1)) + 8 * (m >> 3) + 4 * (g & 1);
+      const u32x4 v = __builtin_bit_cast(u32x4, A[pp][j]);  // register i: (column c, column c + 8)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[(size_t)row * in_f + col0 + i] = (uint16_t)(v[i] & 0xFFFFu);
+        w[(size_t)(row + 8) * in_f + col0 + i] = (uint16_t)(v[i] >> 16);
+      }
+    }
+}
+
 // LDS-tile layout (the 128-token grouped kernels): one work-group of eight
 // waves -- the decoder waves of those kernels -- per 64-input step and
 // group of 16 output tiles; each lane loads and decodes its eighth of a
@@ -1139,6 +1178,10 @@ hipError_t launch_decode_operands(const uint16_t* code_e, int in_f, int out_f, i
       hipLaunchKernelGGL(k_decode_operands_mfma<2>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
     else
       hipLaunchKernelGGL(k_decode_operands_mfma<3>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+  } else if (layout == 3) {
+    if (k_bits != 2) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((in_f / 128) * (out_f / 64));
+    hipLaunchKernelGGL(k_decode_operands_pairs, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
   } else if (layout == 2) {
     const unsigned grid = (unsigned)((in_f / kStep) * (out_f / 256));
     if (k_bits == 2)

@@ -159,6 +159,49 @@ struct OperandDecoder {
   }
 };
 
+// Column-pair operand layout (K = 2 only; the one-launch kernel's gate_up
+// tasks, whose contraction has one token): lane (m, g), c = m & 7, set =
+// m >> 3, decodes of tile j of tile-row pair PP the weights of output
+// columns c and c + 8 in input rows 8 set + 4 (g & 1) + i (i = 0..3) of
+// tile-row 2 PP + (g >> 1). At K = 2 those two states are 16 stream bits
+// apart, so one 32-bit window (one v_alignbit) holds both, packed as the
+// hash wants them: a pair of weights costs the window and the hash, 9
+// VALU operations instead of 11. Register i of A[j] holds (w(row_i, c),
+// w(row_i, c + 8)); the contraction puts each set's activations into its
+// own B columns (mfma_pairs in the one-launch kernel).
+struct PairDecoder {
+  const uint32_t* base;
+  int a0, a0h;
+  uint32_t sh;
+
+  __device__ __forceinline__ PairDecoder(const uint32_t* lds, int lane) {
+    const int m = lane & 15;
+    const int g = lane >> 4;
+    base = lds + stage_slot<4>(g >> 1, 0) * Stage<2>::kStride;
+    // row r of a tile is dword r (16 weights x 2 bits); the window of
+    // columns (c, c + 8) of row r starts at bit 2 c of it
+    a0 = 8 * (m >> 3) + 4 * (g & 1);
+    sh = 2 * (m & 7);
+    a0h = a0 + 2 * 4 * Stage<2>::kStride;  // tile-rows 4..7: second base (see OperandDecoder)
+    asm volatile("" : "+v"(a0h));
+  }
+
+  template <int PP>
+  __device__ __forceinline__ void decode(h16x8 (&A)[4]) const {
+    const uint32_t* p = base + (PP < 2 ? a0 : a0h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int toff = (stage_slot<4>(2 * (PP & 1), j) - stage_slot<4>(0, 0)) * Stage<2>::kStride;
+      uint32_t r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r[i] = __builtin_bit_cast(uint32_t,
+                                  cba_decode_pair(__builtin_amdgcn_alignbit(p[toff + i + 1], p[toff + i], sh)));
+      A[j] = __builtin_bit_cast(h16x8, u32x4{r[0], r[1], r[2], r[3]});
+    }
+  }
+};
+
 // Decode, for every pair pp of adjacent tile-rows (2pp, 2pp+1) and tile j of
 // the staged region (NT tiles per row, at stage_slot<NT>), this lane's 8
 // weights into A[pp][j] (A-operand layout).

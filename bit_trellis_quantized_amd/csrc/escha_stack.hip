@@ -212,7 +212,8 @@ struct Lds {
   _Float16 xh[kChunks][128] __attribute__((aligned(16)));  // rotated inputs (high fp16 parts) per chunk
   _Float16 xl[kChunks][128] __attribute__((aligned(16)));  // and their low parts
   float xe[kChunks];                                       // undo factor of each chunk's scale
-  float red[kChunks * 128] __attribute__((aligned(16)));   // per-chunk sums of the task's outputs
+  float red[2][kChunks * 128] __attribute__((aligned(16)));  // per-chunk sums of the task's outputs
+                                                             // (two input-row sets in the pair layout)
   float rin[kChunks][128];                                 // input scales of the task's chunks
   float rout[128];                                         // output scales of its block
   float4 part[kChunks][64];                                // down: second-half gate_up part sums
@@ -231,7 +232,7 @@ __device__ __forceinline__ bool all_ok(const Lds& sh) {
 
 // Contract a wave's decoded tiles (8 tile-rows of 128-block cl x 4 output
 // tiles 4nq..4nq+3) with the block's activations on the matrix cores and
-// leave the 64 sums in sh.red[stride * cl + 16 (4nq + j) + n] (output
+// leave the 64 sums in sh.red[0][stride * cl + 16 (4nq + j) + n] (output
 // 16 (4nq + j) + n of the task).
 __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq,
                                            int stride, int lane) {
@@ -260,23 +261,74 @@ __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int 
   if ((lane & 15) == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(&sh.red[stride * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) = zr[j];
+      *reinterpret_cast<float4*>(&sh.red[0][stride * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) = zr[j];
+  }
+}
+
+// The same contraction for operands in the column-pair layout (PairDecoder,
+// K = 2): B's column 2 q + h (q = 2 set + parity, h: 0 high, 1 low part)
+// holds the activations of the set's input rows at the B rows of that
+// parity (8 g + 2 i + parity) and zeros at the others, so that
+// D[m][2 q + h] with m = 8 set + c collects output column c (parity 0) or
+// c + 8 (parity 1) over the set's input rows. The two sets' sums go to
+// sh.red[set] and are added in sum_transform_store.
+__device__ __forceinline__ void mfma_pairs(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq, int lane) {
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  h16x8 B[4];
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp) B[pp] = h16x8{};
+  if (col < 8) {
+    const int set = col >> 2, par = (col >> 1) & 1;
+    // input rows 8 set + 4 (g & 1) + i of tile-row 2 pp + (g >> 1): inputs
+    // 32 pp + 16 (g >> 1) + 8 set + 4 (g & 1) + i of the chunk
+    const _Float16* src = ((col & 1) ? sh.xl[cl] : sh.xh[cl]) + 16 * (g >> 1) + 8 * set + 4 * (g & 1);
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src + 32 * pp);
+      const u32x4 d = par == 0 ? u32x4{v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16}
+                               : u32x4{v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u};
+      B[pp] = __builtin_bit_cast(h16x8, d);
+    }
+  }
+  f32x4 D[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B[pp], D[j], 0, 0, 0);
+  // high + low part into the even columns (finish_mfma), then lanes (col
+  // 4 set + 2 parity, g) with set = g >> 1 hold outputs 8 parity + 4 (g &
+  // 1) .. + 3 of each tile for that set
+  float4 zr[4];
+  finish_mfma(D, sh.xe[cl], zr);
+  if ((col & 9) == 0 && (col >> 2) == (g >> 1)) {
+    const int set = col >> 2;
+    const int off = 128 * cl + 8 * ((col >> 1) & 1) + 4 * (g & 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(&sh.red[set][off + 16 * (4 * nq + j)]) = zr[j];
   }
 }
 
 // Output transform of the task's 128 outputs (wave 0): the sum over the
 // first nb input chunks (in chunk order), H_n, rout (sh.rout) and the
 // weight, stored as tagged words (REMOTE: sc1 stores).
-template <bool REMOTE>
+template <bool REMOTE, bool PAIRS = false>
 __device__ __forceinline__ void sum_transform_store(const Lds& sh, int nb, float wt,
                                                     uint64_t* __restrict__ out, uint32_t tag,
                                                     int wave, int lane) {
   if (wave == 0) {
     const int o = lane;
-    float z0 = sh.red[o], z1 = sh.red[o + 64];
+    // chunk by chunk (in order), each chunk's two sets first in the pair layout
+    auto part = [&](int b, int oo) {
+      return PAIRS ? sh.red[0][128 * b + oo] + sh.red[1][128 * b + oo] : sh.red[0][128 * b + oo];
+    };
+    float z0 = part(0, o), z1 = part(0, o + 64);
     for (int b = 1; b < nb; ++b) {
-      z0 += sh.red[128 * b + o];
-      z1 += sh.red[128 * b + o + 64];
+      z0 += part(b, o);
+      z1 += part(b, o + 64);
     }
     fwht128(z0, z1);
     const float o0 = z0 * kInvSqrt128 * sh.rout[o] * wt;
@@ -389,7 +441,15 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
       sd[lane + 64] = f16_to_f32(s1);
     }
     h16x8 A[4][4];
-    decode_stage_mfma<KG>(stage, lane, A);
+    if constexpr (KG == 2) {  // column-pair layout: 9 VALU operations per pair of weights
+      const PairDecoder dec(stage, lane);
+      dec.template decode<0>(A[0]);
+      dec.template decode<1>(A[1]);
+      dec.template decode<2>(A[2]);
+      dec.template decode<3>(A[3]);
+    } else {
+      decode_stage_mfma<KG>(stage, lane, A);
+    }
     pin_operands(A);
     // arguments the normalisation needs, read now rather than after the wait
     float eps = a.eps;
@@ -438,9 +498,12 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
     if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
-      mfma_block(sh, A, cl, nq, 128, lane);
+      if constexpr (KG == 2)
+        mfma_pairs(sh, A, cl, nq, lane);
+      else
+        mfma_block(sh, A, cl, nq, 128, lane);
       __syncthreads();
-      sum_transform_store<false>(sh, kChunks, 1.0f, out, tag, wave, lane);
+      sum_transform_store<false, KG == 2>(sh, kChunks, 1.0f, out, tag, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
       out[lane] = tag_word(0.f, tag);
       out[lane + 64] = tag_word(0.f, tag);
@@ -529,7 +592,7 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
       } else if (active && (lane & 15) == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(&sh.red[128 * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
+          *reinterpret_cast<float4*>(&sh.red[0][128 * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
               make_float4(0.f, 0.f, 0.f, 0.f);
       }
       __syncthreads();
@@ -616,16 +679,16 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
           y1 += v[2 * j + 1];
         }
       if (wave & 1) {  // second half of the slots to LDS
-        sh.red[128 * (wave >> 1) + lane] = y0;
-        sh.red[128 * (wave >> 1) + 64 + lane] = y1;
+        sh.red[0][128 * (wave >> 1) + lane] = y0;
+        sh.red[0][128 * (wave >> 1) + 64 + lane] = y1;
       }
     }
     if (lane == 0 && !ok) sh.ok[wave] = 0;
     __syncthreads();
     if (!all_ok(sh)) return;
     if (!(wave & 1) && b < nb) {
-      y0 += sh.red[128 * (wave >> 1) + lane];
-      y1 += sh.red[128 * (wave >> 1) + 64 + lane];
+      y0 += sh.red[0][128 * (wave >> 1) + lane];
+      y1 += sh.red[0][128 * (wave >> 1) + 64 + lane];
       store_combined(a, last, t, x, b, lane, y0, y1, tag);
     }
   }

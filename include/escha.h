@@ -114,13 +114,19 @@ ESCHA_API int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t
  * format ([trellis-mlx] exactness table; [hipfire] "What it is"):
  *   ESCHA_LAYOUT_QUARTER        the streaming kernels' decoder (four lanes
  *                               per tile); identical to escha_decode_tiles;
- *   ESCHA_LAYOUT_MFMA_OPERAND   the decoder of the one-launch stack and the
- *                               small-tile kernels (tiles staged in LDS,
- *                               weights decoded into matrix-core A operands);
+ *   ESCHA_LAYOUT_MFMA_OPERAND   the decoder of the one-launch stack (its K=3
+ *                               down tasks) and the small-tile kernels (tiles
+ *                               staged in LDS, weights decoded into
+ *                               matrix-core A operands);
  *   ESCHA_LAYOUT_LDS_TILE       the decoder of the 128-token grouped kernels
  *                               (an eighth of a tile per lane, fp16 tiles in
  *                               LDS, read back with the matrix waves'
- *                               addressing).
+ *                               addressing);
+ *   ESCHA_LAYOUT_MFMA_PAIRS     the K=2 decoder of the one-launch stack's
+ *                               gate_up tasks (A operands holding output
+ *                               columns c and c + 8 of one input row, both
+ *                               states from one 32-bit window); K=2 codes
+ *                               only, else ESCHA_E_ARG.
  * w_f16 is 16-byte aligned (8 for ESCHA_LAYOUT_QUARTER). An unknown layout
  * returns ESCHA_E_ARG.
  */
@@ -128,6 +134,7 @@ enum escha_decode_layout {
   ESCHA_LAYOUT_QUARTER = 0,
   ESCHA_LAYOUT_MFMA_OPERAND = 1,
   ESCHA_LAYOUT_LDS_TILE = 2,
+  ESCHA_LAYOUT_MFMA_PAIRS = 3,
 };
 ESCHA_API int escha_decode_tiles_layout(const escha_proj_t* w, int32_t expert, int32_t layout,
                                         uint16_t* w_f16, void* stream);
