@@ -614,10 +614,10 @@ int escha_decode_tiles_layout(const escha_proj_t* w, int32_t expert, int32_t lay
   int rc = check_proj(w, "decode_tiles_layout");
   if (rc) return rc;
   if (layout != ESCHA_LAYOUT_MFMA_OPERAND && layout != ESCHA_LAYOUT_LDS_TILE &&
-      layout != ESCHA_LAYOUT_MFMA_PAIRS)
+      layout != ESCHA_LAYOUT_MFMA_PAIRS && layout != ESCHA_LAYOUT_MFMA_TILE_PAIRS)
     return fail(ESCHA_E_ARG, "layout=%d is not one of the ESCHA_LAYOUT_* values", layout);
-  if (layout == ESCHA_LAYOUT_MFMA_PAIRS && w->k_bits != 2)
-    return fail(ESCHA_E_ARG, "ESCHA_LAYOUT_MFMA_PAIRS decodes K=2 codes only (K=%d)", w->k_bits);
+  if ((layout == ESCHA_LAYOUT_MFMA_PAIRS || layout == ESCHA_LAYOUT_MFMA_TILE_PAIRS) && w->k_bits != 2)
+    return fail(ESCHA_E_ARG, "the column-pair layouts decode K=2 codes only (K=%d)", w->k_bits);
   if (expert < 0 || expert >= w->n_experts)
     return fail(ESCHA_E_ARG, "expert=%d out of [0, %d)", expert, w->n_experts);
   if (!w_f16) return fail(ESCHA_E_NULL, "w_f16 is NULL");

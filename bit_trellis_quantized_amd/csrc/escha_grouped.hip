@@ -38,6 +38,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "escha_device.hpp"
 #include "escha_launch.hpp"
 #include "escha_mfma.hpp"
@@ -792,6 +794,60 @@ __device__ __forceinline__ void small_to_lds(const f32x4 (&D)[4], SmallLds& sh, 
         make_float4(D[j][0], D[j][1], D[j][2], D[j][3]);
 }
 
+// The gate_up main loop for tiles of at most 8 tokens at K = 2, in the
+// tile-pair layout (TilePairDecoder: 9 VALU operations per pair of weights
+// instead of 11): the wave's partial sums over chunks c0 .. c0 + nch - 1 of
+// output tiles nt0 .. nt0 + 3, D[jp] for the tile pair (2 jp, 2 jp + 1). The
+// tile's rows are row0 .. row0 + rows - 1 of X (rows <= 8; the columns of
+// tokens >= rows read row row0 and are never stored).
+__device__ __forceinline__ void small_mainloop_pairs(const uint16_t* __restrict__ code_e, int n_nt, int c0,
+                                                     int nch, int nt0, const _Float16* __restrict__ X,
+                                                     int x_pitch, int row0, int rows, uint32_t* stage,
+                                                     int lane, f32x4 (&D)[2]) {
+  const int tk = lane & 7;          // B column 8 par + tk: token tk
+  const int par = (lane >> 3) & 1;
+  const _Float16* xrow = X + (size_t)(row0 + (tk < rows ? tk : 0)) * x_pitch + 4 * (lane >> 4);
+  D[0] = D[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  u32x4 cv[Stage<2>::kPerLane];
+  stage_issue<2>(code_e, n_nt, 8 * c0, nt0, lane, cv);
+  const TilePairDecoder dec(stage, lane);
+  for (int c = c0; c < c0 + nch; ++c) {
+    stage_store<2>(stage, lane, cv);
+    // the chunk's activations (inputs 16 tr + 4 g .. + 3 of token tk), then
+    // the next chunk's codes, in flight during the decode
+    u32x2 xa[8];
+#pragma unroll
+    for (int tr = 0; tr < 8; ++tr) xa[tr] = *reinterpret_cast<const u32x2*>(xrow + 128 * c + 16 * tr);
+    const int cn = c + 1 < c0 + nch ? c + 1 : c;
+    stage_issue<2>(code_e, n_nt, 8 * cn, nt0, lane, cv);
+    auto step = [&](auto trc) {
+      constexpr int TR = decltype(trc)::value;
+      const h16x8 B = parity_operand(xa[TR], par);
+      D[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec.template decode<TR, 0>(), B, D[0], 0, 0, 0);
+      D[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec.template decode<TR, 1>(), B, D[1], 0, 0, 0);
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    step(std::integral_constant<int, 3>{});
+    step(std::integral_constant<int, 4>{});
+    step(std::integral_constant<int, 5>{});
+    step(std::integral_constant<int, 6>{});
+    step(std::integral_constant<int, 7>{});
+  }
+}
+
+// Accumulators of small_mainloop_pairs -> sh.red[kh][token][output]: lane
+// (8 par + tk, g) holds rows 4 g .. 4 g + 3 of D[jp], i.e. columns 4 (g & 1)
+// + r + 8 par of tile 2 jp + (g >> 1) for token tk.
+__device__ __forceinline__ void small_pairs_to_lds(const f32x4 (&D)[2], SmallLds& sh, int kh, int nq, int lane) {
+  const int tk = lane & 7, par = (lane >> 3) & 1, g = lane >> 4;
+#pragma unroll
+  for (int jp = 0; jp < 2; ++jp)
+    *reinterpret_cast<float4*>(&sh.red[kh][tk][16 * (4 * nq + 2 * jp + (g >> 1)) + 8 * par + 4 * (g & 1)]) =
+        make_float4(D[jp][0], D[jp][1], D[jp][2], D[jp][3]);
+}
+
 // gate_up, small tiles. grid.x = max_tiles * (inter / 128), block = 512.
 // A work-group takes gate block c and up block c (256 outputs, quads 0-1
 // and 2-3) of one tile; its epilogue is the big tile kernel's: the input
@@ -815,11 +871,20 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncg * 8 * n_nt * (16 * K);
   __shared__ SmallLds sh;
   if (threadIdx.x < rows) sh.rexp[threadIdx.x] = a.x_exp_in[row0 + threadIdx.x];  // read after the barrier below
-  f32x4 D[4];
-  small_mainloop<K, false>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
-                           reinterpret_cast<const _Float16*>(a.x_in), a.hidden, nullptr, 0, row0, rows,
-                           sh.stage + wave * Stage<K>::kDw, lane, D, nullptr);
-  small_to_lds(D, sh, kh, nq, lane);
+  bool pairs = false;
+  if constexpr (K == 2) pairs = rows <= 8;  // uniform
+  if (pairs) {
+    f32x4 D[2];
+    small_mainloop_pairs(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0, reinterpret_cast<const _Float16*>(a.x_in),
+                         a.hidden, row0, rows, sh.stage + wave * Stage<K>::kDw, lane, D);
+    small_pairs_to_lds(D, sh, kh, nq, lane);
+  } else {
+    f32x4 D[4];
+    small_mainloop<K, false>(code_e, n_nt, kh * (ncg / 2), ncg / 2, nt0,
+                             reinterpret_cast<const _Float16*>(a.x_in), a.hidden, nullptr, 0, row0, rows,
+                             sh.stage + wave * Stage<K>::kDw, lane, D, nullptr);
+    small_to_lds(D, sh, kh, nq, lane);
+  }
   __syncthreads();
   const uint16_t* rg = a.rout + (size_t)e * (2 * a.inter) + 128 * c;
   const uint16_t* ru = rg + a.inter;
@@ -1138,6 +1203,50 @@ __global__ __launch_bounds__(64) void k_decode_operands_pairs(const uint16_t* __
     }
 }
 
+// Tile-pair layout (TilePairDecoder, K = 2: the small-tile gate_up kernel on
+// tiles of at most 8 tokens): the same staged region; lane (m, g) holds in
+// register i of the operand of tile-row tr and tile pair jp the weights of
+// output columns c = m & 7 and c + 8 of tile nt0 + 2 jp + (m >> 3), input row
+// 4 g + i of tile-row kt0 + tr. grid.x = (in/128) * (out/64), block = 64.
+__global__ __launch_bounds__(64) void k_decode_operands_tilepairs(const uint16_t* __restrict__ code_e,
+                                                                  int in_f, int out_f,
+                                                                  uint16_t* __restrict__ w) {
+  __shared__ uint32_t stage[Stage<2>::kDw];
+  const int n_nt = out_f / 16;
+  const int nq = n_nt / 4;
+  const int kt0 = 8 * (blockIdx.x / nq);
+  const int nt0 = 4 * (blockIdx.x % nq);
+  const int lane = threadIdx.x;
+  u32x4 cv[Stage<2>::kPerLane];
+  stage_issue<2>(code_e, n_nt, kt0, nt0, lane, cv);
+  stage_store<2>(stage, lane, cv);
+  const TilePairDecoder dec(stage, lane);
+  const int m = lane & 15, g = lane >> 4;
+  auto put = [&](int tr, int jp, h16x8 A) {
+    const u32x4 v = __builtin_bit_cast(u32x4, A);  // register i: (column c, column c + 8)
+    const int row = 16 * (nt0 + 2 * jp + (m >> 3)) + (m & 7);
+    const int col0 = 16 * (kt0 + tr) + 4 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[(size_t)row * in_f + col0 + i] = (uint16_t)(v[i] & 0xFFFFu);
+      w[(size_t)(row + 8) * in_f + col0 + i] = (uint16_t)(v[i] >> 16);
+    }
+  };
+  auto both = [&](auto trc) {
+    constexpr int TR = decltype(trc)::value;
+    put(TR, 0, dec.template decode<TR, 0>());
+    put(TR, 1, dec.template decode<TR, 1>());
+  };
+  both(std::integral_constant<int, 0>{});
+  both(std::integral_constant<int, 1>{});
+  both(std::integral_constant<int, 2>{});
+  both(std::integral_constant<int, 3>{});
+  both(std::integral_constant<int, 4>{});
+  both(std::integral_constant<int, 5>{});
+  both(std::integral_constant<int, 6>{});
+  both(std::integral_constant<int, 7>{});
+}
+
 // LDS-tile layout (the 128-token grouped kernels): one work-group of eight
 // waves -- the decoder waves of those kernels -- per 64-input step and
 // group of 16 output tiles; each lane loads and decodes its eighth of a
@@ -1178,10 +1287,13 @@ hipError_t launch_decode_operands(const uint16_t* code_e, int in_f, int out_f, i
       hipLaunchKernelGGL(k_decode_operands_mfma<2>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
     else
       hipLaunchKernelGGL(k_decode_operands_mfma<3>, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
-  } else if (layout == 3) {
+  } else if (layout == 3 || layout == 4) {
     if (k_bits != 2) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((in_f / 128) * (out_f / 64));
-    hipLaunchKernelGGL(k_decode_operands_pairs, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+    if (layout == 3)
+      hipLaunchKernelGGL(k_decode_operands_pairs, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
+    else
+      hipLaunchKernelGGL(k_decode_operands_tilepairs, dim3(grid), dim3(64), 0, s, code_e, in_f, out_f, w);
   } else if (layout == 2) {
     const unsigned grid = (unsigned)((in_f / kStep) * (out_f / 256));
     if (k_bits == 2)

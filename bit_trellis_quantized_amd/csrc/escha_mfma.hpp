@@ -202,6 +202,44 @@ struct PairDecoder {
   }
 };
 
+// Tile-pair operand layout (K = 2 only; the small-tile gate_up kernel on
+// tiles of at most 8 tokens): one A operand covers output tiles 2 jp (A rows
+// 0..7) and 2 jp + 1 (rows 8..15) of one input tile-row tr; lane (m, g), t =
+// m >> 3, c = m & 7, holds in register i the weights of columns c and c + 8
+// of tile 2 jp + t at input row 4 g + i of the tile (one window each, as in
+// PairDecoder). With B column 8 par + tk holding token tk's activation of
+// input row 4 g + i at B row 8 g + 2 i + par (zeros at the other parity),
+// D[m][8 par + tk] is output column c + 8 par of tile 2 jp + t for token tk.
+struct TilePairDecoder {
+  const uint32_t* base;
+  uint32_t sh;
+
+  __device__ __forceinline__ TilePairDecoder(const uint32_t* lds, int lane) {
+    const int m = lane & 15;
+    base = lds + (m >> 3) * Stage<2>::kStride + 4 * (lane >> 4);
+    sh = 2 * (m & 7);
+  }
+
+  // the operand of tile-row tr and tile pair jp (tiles 2 jp, 2 jp + 1)
+  template <int TR, int JP>
+  __device__ __forceinline__ h16x8 decode() const {
+    const uint32_t* p = base + stage_slot<4>(TR, 2 * JP) * Stage<2>::kStride;
+    uint32_t r[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = __builtin_bit_cast(uint32_t, cba_decode_pair(__builtin_amdgcn_alignbit(p[i + 1], p[i], sh)));
+    return __builtin_bit_cast(h16x8, u32x4{r[0], r[1], r[2], r[3]});
+  }
+};
+
+// B operand of the parity layouts from four fp16 activations (two words):
+// at the even B rows of the lane's group (parity 0) or the odd ones.
+__device__ __forceinline__ h16x8 parity_operand(u32x2 v, int par) {
+  const u32x4 d = par == 0 ? u32x4{v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16}
+                           : u32x4{v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u};
+  return __builtin_bit_cast(h16x8, d);
+}
+
 // Decode, for every pair pp of adjacent tile-rows (2pp, 2pp+1) and tile j of
 // the staged region (NT tiles per row, at stage_slot<NT>), this lane's 8
 // weights into A[pp][j] (A-operand layout).

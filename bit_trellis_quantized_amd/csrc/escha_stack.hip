@@ -285,10 +285,7 @@ __device__ __forceinline__ void mfma_pairs(Lds& sh, const h16x8 (&A)[4][4], int 
     const _Float16* src = ((col & 1) ? sh.xl[cl] : sh.xh[cl]) + 16 * (g >> 1) + 8 * set + 4 * (g & 1);
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(src + 32 * pp);
-      const u32x4 d = par == 0 ? u32x4{v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16}
-                               : u32x4{v.x << 16, v.x & 0xFFFF0000u, v.y << 16, v.y & 0xFFFF0000u};
-      B[pp] = __builtin_bit_cast(h16x8, d);
+      B[pp] = parity_operand(*reinterpret_cast<const u32x2*>(src + 32 * pp), par);
     }
   }
   f32x4 D[4];

@@ -246,7 +246,7 @@ def escha_decode_tiles(w: Proj, expert: int, out: torch.Tensor | None = None, st
     return out
 
 
-LAYOUT_QUARTER, LAYOUT_MFMA_OPERAND, LAYOUT_LDS_TILE, LAYOUT_MFMA_PAIRS = 0, 1, 2, 3
+LAYOUT_QUARTER, LAYOUT_MFMA_OPERAND, LAYOUT_LDS_TILE, LAYOUT_MFMA_PAIRS, LAYOUT_MFMA_TILE_PAIRS = 0, 1, 2, 3, 4
 
 
 def escha_decode_tiles_layout(w: Proj, expert: int, layout: int, out: torch.Tensor | None = None,

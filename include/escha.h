@@ -126,7 +126,11 @@ ESCHA_API int escha_decode_tiles(const escha_proj_t* w, int32_t expert, uint16_t
  *                               gate_up tasks (A operands holding output
  *                               columns c and c + 8 of one input row, both
  *                               states from one 32-bit window); K=2 codes
- *                               only, else ESCHA_E_ARG.
+ *                               only, else ESCHA_E_ARG;
+ *   ESCHA_LAYOUT_MFMA_TILE_PAIRS the K=2 decoder of the small-tile gate_up
+ *                               kernel on tiles of at most 8 tokens (A
+ *                               operands covering two output tiles, columns
+ *                               c and c + 8 from one window); K=2 only.
  * w_f16 is 16-byte aligned (8 for ESCHA_LAYOUT_QUARTER). An unknown layout
  * returns ESCHA_E_ARG.
  */
@@ -135,6 +139,7 @@ enum escha_decode_layout {
   ESCHA_LAYOUT_MFMA_OPERAND = 1,
   ESCHA_LAYOUT_LDS_TILE = 2,
   ESCHA_LAYOUT_MFMA_PAIRS = 3,
+  ESCHA_LAYOUT_MFMA_TILE_PAIRS = 4,
 };
 ESCHA_API int escha_decode_tiles_layout(const escha_proj_t* w, int32_t expert, int32_t layout,
                                         uint16_t* w_f16, void* stream);

@@ -240,11 +240,12 @@ def test_decode_tiles_layout_rejects_unknown_layout(lib):
     f = lib.escha_decode_tiles_layout
     f.argtypes = [ctypes.POINTER(Proj), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     p = _proj()
-    assert f(ctypes.byref(p), 0, 4, ctypes.c_void_p(FAKE), None) == -7
+    assert f(ctypes.byref(p), 0, 5, ctypes.c_void_p(FAKE), None) == -7
     assert "layout" in _err(lib)
     p3 = _proj(in_features=512, out_features=2048, k_bits=3)
-    assert f(ctypes.byref(p3), 0, 3, ctypes.c_void_p(FAKE), None) == -7  # the pair layout is K=2 only
-    assert "K=2" in _err(lib)
+    for layout in (3, 4):  # the column-pair layouts are K=2 only
+        assert f(ctypes.byref(p3), 0, layout, ctypes.c_void_p(FAKE), None) == -7
+        assert "K=2" in _err(lib)
     assert f(ctypes.byref(p), 256, 1, ctypes.c_void_p(FAKE), None) == -7  # expert out of range
     assert f(ctypes.byref(p), 0, 2, None, None) == -1
     assert f(ctypes.byref(p), 0, 1, ctypes.c_void_p(FAKE + 8), None) == -7  # not 16-byte aligned

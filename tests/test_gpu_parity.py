@@ -75,7 +75,7 @@ def test_decode_tiles_special_words(escha, K):
 # decoder (128-token grouped kernels) and the K=2 column-pair decoder (the
 # one-launch stack's gate_up tasks) must give the format's bits exactly.
 FUSED_LAYOUTS = [1, 2]  # LAYOUT_MFMA_OPERAND, LAYOUT_LDS_TILE
-LAYOUT_PAIRS = 3        # LAYOUT_MFMA_PAIRS (K=2 only)
+PAIR_LAYOUTS = [3, 4]   # LAYOUT_MFMA_PAIRS, LAYOUT_MFMA_TILE_PAIRS (K=2 only)
 
 
 @pytest.mark.parametrize("layout", FUSED_LAYOUTS)
@@ -122,18 +122,20 @@ def test_decode_layouts_special_words(escha, layout, K):
         assert np.array_equal(got, oracle.reconstruct(code, in_f, out_f, K)), hex(int(code.flat[1]))
 
 
+@pytest.mark.parametrize("layout", PAIR_LAYOUTS)
 @pytest.mark.parametrize("expert", [0, 137])
-def test_decode_pairs_layout_bit_exact(escha, layer2, layer2_dev, expert):
-    announce(f"decode layout pairs layer2 gate_up expert {expert}")
-    got = u16(escha.escha_decode_tiles_layout(layer2_dev.gate_up, expert, LAYOUT_PAIRS))
+def test_decode_pairs_layout_bit_exact(escha, layer2, layer2_dev, layout, expert):
+    announce(f"decode layout {layout} layer2 gate_up expert {expert}")
+    got = u16(escha.escha_decode_tiles_layout(layer2_dev.gate_up, expert, layout))
     assert np.count_nonzero(got != oracle.reconstruct(layer2["gu_code"][expert], 2048, 1024, 2)) == 0
 
 
-def test_decode_pairs_layout_matrix_and_special_words(escha):
-    announce("decode layout pairs 256x256 and special words")
+@pytest.mark.parametrize("layout", PAIR_LAYOUTS)
+def test_decode_pairs_layout_matrix_and_special_words(escha, layout):
+    announce(f"decode layout {layout} 256x256 and special words")
     code, rin, rout = synth.single_proj(1, 256, 256, 2)
     w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
-    assert np.count_nonzero(u16(escha.escha_decode_tiles_layout(w, 0, LAYOUT_PAIRS))
+    assert np.count_nonzero(u16(escha.escha_decode_tiles_layout(w, 0, layout))
                             != oracle.reconstruct(code, 256, 256, 2)) == 0
     in_f, out_f = 128, 256
     shape = (in_f // 16, out_f // 16, 32)
@@ -143,7 +145,7 @@ def test_decode_pairs_layout_matrix_and_special_words(escha):
     mixed[..., -1] = 0x8001  # the wrap source
     for code in [np.full(shape, f, dtype=np.uint16) for f in (0x0000, 0xFFFF, 0xAAAA, 0x8001)] + [mixed]:
         w = escha.Proj(to_dev(code), to_dev(rin), to_dev(rout))
-        got = u16(escha.escha_decode_tiles_layout(w, 0, LAYOUT_PAIRS))
+        got = u16(escha.escha_decode_tiles_layout(w, 0, layout))
         assert np.array_equal(got, oracle.reconstruct(code, in_f, out_f, 2)), hex(int(code.flat[1]))
 
 
