@@ -322,6 +322,12 @@ int group_layers(const escha_moe_layer_t* L, int T, const int32_t* ids, const Gr
   const int P = T * L->top_k;
   const int E = L->gate_up.n_experts;
   const bool small = grouped_small(L, T, prefill);
+  if (escha::group_small_ok(P, E)) {
+    const hipError_t e = escha::launch_group_small(
+        ids, P, E, g.counts, g.offsets, g.perm, g.inv, small ? kSmallTileTokens : kTileTokens,
+        grouped_max_tiles(L, T, true), g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s, n_layers);
+    return e == hipSuccess ? ESCHA_OK : hip_fail(e, "group launch");
+  }
   hipError_t e = escha::launch_group(ids, P, E, g.counts, g.offsets, g.perm, g.inv, g.hist, g.base,
                                      g.rank, s, n_layers);
   if (e != hipSuccess) return hip_fail(e, "group launch");
@@ -708,8 +714,12 @@ int escha_moe_group(const int32_t* topk_ids, int32_t n_tokens, int32_t top_k, in
   int32_t* hist = (int32_t*)b;
   int32_t* base = (int32_t*)(b + round_up(chunks * n_experts * sizeof(int32_t)));
   int32_t* rank = (int32_t*)(b + 2 * round_up(chunks * n_experts * sizeof(int32_t)));
-  hipError_t e = escha::launch_group(topk_ids, P, n_experts, counts, offsets, perm, nullptr, hist,
-                                     base, rank, (hipStream_t)stream);
+  hipError_t e = escha::group_small_ok(P, n_experts)
+                     ? escha::launch_group_small(topk_ids, P, n_experts, counts, offsets, perm, nullptr,
+                                                 0, 0, nullptr, nullptr, nullptr, nullptr,
+                                                 (hipStream_t)stream)
+                     : escha::launch_group(topk_ids, P, n_experts, counts, offsets, perm, nullptr,
+                                           hist, base, rank, (hipStream_t)stream);
   return e == hipSuccess ? ESCHA_OK : hip_fail(e, "group launch");
 }
 

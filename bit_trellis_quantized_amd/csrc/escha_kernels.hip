@@ -716,6 +716,126 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
   if (inv) inv[i] = pos;
 }
 
+// ------------------------------------------------------------------------
+// Grouping of up to kGroupSmallPairs pairs in one work-group of 1024 threads
+// (decode-sized calls: one launch instead of count, scan, offsets, scatter
+// and tile list): the same results as the multi-pass path -- counts,
+// offsets, the stable permutation (sorted index -> pair, ties in pair
+// order), its inverse, and optionally the tile list (tiles of tm
+// consecutive sorted pairs of one expert, experts in order). Pairs are
+// taken 1024 at a time; inside a wave, the lanes holding the same expert
+// are found with one ballot per bit of the expert index; a wave's count per
+// expert goes to LDS, and the rank of a pair is the expert's running count
+// before this chunk + the counts of the earlier waves of the chunk + its
+// rank among the wave's lanes with that expert. grid.y = layer of a batch.
+// ------------------------------------------------------------------------
+constexpr int kGroupSmallPairs = 8192;
+constexpr int kGroupSmallExperts = 256;  // wave-count table in LDS: 16 waves x 256 experts
+
+__global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict__ ids, int P, int E,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm, int32_t* __restrict__ inv,
+                                                      int tm, int max_tiles, int32_t* __restrict__ t_expert,
+                                                      int32_t* __restrict__ t_row0,
+                                                      int32_t* __restrict__ t_rows,
+                                                      int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t cnt[kGroupSmallExperts];       // per expert: running count, then its offset
+  __shared__ int32_t wc[16][kGroupSmallExperts];    // per wave of the chunk and expert: its count
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;  // bits of the largest expert index
+  const size_t ly = blockIdx.y;
+  ids += ly * P;
+  counts += ly * E;
+  offsets += ly * (E + 1);
+  perm += ly * P;
+  if (inv) inv += ly * P;
+  // pass 1: counts (LDS atomics on integers: exact, order-free)
+  if (tid < E) cnt[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < P; i += 1024) {
+    const int e = ids[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // offsets: exclusive scan of the counts
+  const int32_t c0 = tid < E ? cnt[tid] : 0;
+  scan[tid] = c0;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int32_t v = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += v;
+    __syncthreads();
+  }
+  const int32_t off = scan[tid] - c0;
+  if (tid < E) {
+    counts[tid] = c0;
+    offsets[tid] = off;
+    cnt[tid] = off;  // now: the next free sorted index of the expert
+  }
+  if (tid == 0) offsets[E] = scan[1023];
+  // the tile list: ceil(count / tm) tiles per expert, experts in order
+  if (t_expert) {
+    __syncthreads();
+    const int32_t nt = tid < E ? (c0 + tm - 1) / tm : 0;
+    scan[tid] = nt;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {
+      const int32_t v = tid >= d ? scan[tid - d] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    t_expert += ly * max_tiles;
+    t_row0 += ly * max_tiles;
+    t_rows += ly * max_tiles;
+    const int32_t b = scan[tid] - nt;
+    for (int q = 0; q < nt; ++q)
+      if (b + q < max_tiles) {
+        t_expert[b + q] = tid;
+        t_row0[b + q] = off + q * tm;
+        t_rows[b + q] = c0 - q * tm < tm ? c0 - q * tm : tm;
+      }
+    if (tid == 1023) n_tiles[ly] = scan[1023] < max_tiles ? scan[1023] : max_tiles;
+  }
+  // pass 2: the stable scatter, 1024 pairs at a time
+  for (int i0 = 0; i0 < P; i0 += 1024) {
+    for (int q = tid; q < 16 * kGroupSmallExperts; q += 1024) (&wc[0][0])[q] = 0;
+    __syncthreads();
+    const int i = i0 + tid;
+    const int e = i < P ? ids[i] : -1;
+    const bool valid = e >= 0 && e < E;
+    // lanes of this wave holding the same expert: one ballot per index bit
+    uint64_t same = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const uint64_t ones = __ballot(valid && ((e >> bit) & 1));
+      same &= ((e >> bit) & 1) ? ones : ~ones;
+    }
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int r_wave = __popcll(same & below);
+    if (valid && r_wave == __popcll(same) - 1) wc[wave][e] = __popcll(same);  // the last such lane
+    __syncthreads();
+    if (valid) {
+      int pos = cnt[e] + r_wave;
+      for (int w = 0; w < wave; ++w) pos += wc[w][e];
+      perm[pos] = i;
+      if (inv) inv[i] = pos;
+    } else if (i < P && inv) {
+      inv[i] = -1;
+    }
+    __syncthreads();
+    // advance the experts' cursors by this chunk's counts
+    if (tid < E) {
+      int add = 0;
+      for (int w = 0; w < 16; ++w) add += wc[w][tid];
+      cnt[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(256) void k_fill_one_expert(int32_t* __restrict__ ids, float* __restrict__ w,
                                                         int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -838,6 +958,16 @@ hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s) {
   const size_t n = (size_t)a.T * a.E;
   hipLaunchKernelGGL(k_router_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.part,
                      a.ksplit, n, a.logits);
+  return last_launch();
+}
+
+bool group_small_ok(int P, int E) { return P <= kGroupSmallPairs && E <= kGroupSmallExperts; }
+
+hipError_t launch_group_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* inv, int tm, int max_tiles, int32_t* t_expert,
+                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s, int n_layers) {
+  hipLaunchKernelGGL(k_group_small, dim3(1, (unsigned)n_layers), dim3(1024), 0, s, ids, P, E, counts, offsets,
+                     perm, inv, tm, max_tiles, t_expert, t_row0, t_rows, n_tiles);
   return last_launch();
 }
 

@@ -264,6 +264,13 @@ hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s);
 // inv (nullable): pair -> sorted index, -1 for a pair with an out-of-range id
 // n_layers groupings at once: layer l reads ids + l P and uses counts + l E,
 // offsets + l (E + 1), perm / inv / rank + l P, hist / base + l chunks E.
+// One work-group per layer doing all of the grouping (and, with t_expert
+// non-null, the tile list of launch_make_tiles) when group_small_ok(P, E).
+bool group_small_ok(int P, int E);
+hipError_t launch_group_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                              int32_t* perm, int32_t* inv, int tm, int max_tiles, int32_t* t_expert,
+                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s,
+                              int n_layers = 1);
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                         int32_t* perm, int32_t* inv, int32_t* hist, int32_t* base, int32_t* rank,
                         hipStream_t s, int n_layers = 1);

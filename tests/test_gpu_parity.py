@@ -196,6 +196,51 @@ def test_group_vs_oracle(escha, cfg, T):
     assert np.array_equal(perm.cpu().numpy(), rp)
 
 
+def _group_check(escha, ids, E, what):
+    """Grouping of ``ids`` over E experts against the oracle; ids outside
+    [0, E) are left out of the grouping, which is the oracle's grouping over
+    one more expert (index E, taking every bad id) with that expert dropped."""
+    announce(f"moe_group {what}")
+    bad = (ids < 0) | (ids >= E)
+    ids_o = np.where(bad, E, ids).astype(np.int32)
+    rc, ro, rp = oracle.group(ids_o, E + 1)
+    counts, offsets, perm = escha.escha_moe_group(to_dev(ids.astype(np.int32)), E)
+    n = int(ro[E])
+    assert np.array_equal(counts.cpu().numpy(), rc[:E]), what
+    assert np.array_equal(offsets.cpu().numpy(), ro[:E + 1]), what
+    assert np.array_equal(perm.cpu().numpy()[:n], rp[:n]), what
+
+
+@pytest.mark.parametrize("T", [1024, 1025])
+def test_group_one_expert_for_all(escha, T):
+    """Every pair on one expert: 8192 pairs (the most one work-group groups)
+    and 8200 (the multi-pass path); ranks in pair order across all waves and
+    chunks."""
+    _group_check(escha, np.full((T, 8), 77, dtype=np.int32), 256, f"one expert T={T}")
+
+
+@pytest.mark.parametrize("E", [1, 2, 255, 256, 257, 300])
+def test_group_expert_counts(escha, E):
+    """Expert counts around the one-work-group limit (256) and the smallest
+    (one expert: no index bits)."""
+    rng = np.random.default_rng(900 + E)
+    T = 700
+    ids = rng.integers(0, E, size=(T, 8)).astype(np.int32)
+    _group_check(escha, ids, E, f"E={E} T={T}")
+
+
+@pytest.mark.parametrize("T", [37, 1100])
+def test_group_bad_ids(escha, T):
+    """Ids below 0 or at/above E are left out (counts, offsets and the sorted
+    part of perm over the valid pairs only), on both grouping paths."""
+    rng = np.random.default_rng(40 + T)
+    ids = rng.integers(0, 256, size=(T, 8)).astype(np.int32)
+    flat = ids.reshape(-1)
+    pick = rng.choice(flat.size, size=flat.size // 10, replace=False)
+    flat[pick] = rng.choice(np.array([-1, -7, 256, 1000], dtype=np.int32), size=pick.size)
+    _group_check(escha, ids, 256, f"bad ids T={T}")
+
+
 # ------------------------------------------------------------------ projections
 
 @pytest.mark.parametrize("T", [1, 3])
