@@ -510,14 +510,25 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
     probe_ev = [(hip.event(), hip.event()) for _ in range(NLc)]
     routed = [None] * NLc
 
+    # the decode configs route inside the layer call (the router step in the
+    # layer's first kernel); the prefill chunk routes with its own kernel first
+    route_bufs = [(torch.empty(T, k, dtype=torch.int32, device="cuda"),
+                   torch.empty(T, k, dtype=torch.float32, device="cuda")) for _ in range(NLc)]
+
     def sweep(probes=True):
         for l in range(NLc):
             inp = inputs[l % n_inputs]
-            ids, w = escha.escha_route_topk(inp["logits"], k)
+            ids, w = route_bufs[l]
+            if prefill:
+                escha.escha_route_topk(inp["logits"], k, ids=ids, w=w)
             routed[l] = (ids, w)
             escha.escha_probe_events_set(probe_ev[l] if probes else None)
             try:
-                fn(layers[l], inp["x"], ids, w, out=y, workspace=ws)
+                if prefill:
+                    fn(layers[l], inp["x"], ids, w, out=y, workspace=ws)
+                else:
+                    escha.escha_moe_layer_decode_logits(layers[l], inp["x"], inp["logits"], out=y, topk_ids=ids,
+                                                        topk_w=w, workspace=ws)
             finally:
                 escha.escha_probe_events_set(None)
 
@@ -579,7 +590,7 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
             "flops_per_launch": flops, "avg_launch_us": round(proj_ms * 1e3, 3), "samples": NLc,
             "code_bytes": int(code_bytes), "code_gbs": round(code_bytes / (proj_ms / 1e3) / 1e9, 1)}
     else:
-        kernel = ("k_in_partial + k_down_partial (streaming decode)" if T < 16 else
+        kernel = ("k_in_partial (with the router step) + k_down_partial (streaming decode)" if T < 16 else
                   "k_small_gate_up + k_small_down (small-tile grouped decode, MFMA 16x16x32)")
         entry["roofline"] = roofline_hbm(kernel, code_bytes, proj_ms,
                                          measured_traffic("layer_cfg2" if T < 16 else "layer_cfg3"), NLc)

@@ -151,12 +151,19 @@ struct LayerInput {
 
 // One layer over T tokens through the streaming kernels.
 // gu_bias / dn_bias (nullable): the dense export's biases (one-expert case).
+// route (nullable): the router step runs inside the first kernel, from
+// route->logits, and its selections (route->ids_out / w_out) are the
+// routing (ids and w are then unused).
 int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, const int32_t* ids,
                      const float* w, float* y, float* inter_out, const DecodeWs& ws,
                      hipStream_t s, hipEvent_t probe_before = nullptr,
                      hipEvent_t probe_after = nullptr, const float* gu_bias = nullptr,
-                     const float* dn_bias = nullptr) {
+                     const float* dn_bias = nullptr, const escha::RouteOut* route = nullptr) {
   const int P = T * L->top_k;
+  if (route) {
+    ids = route->ids_out;
+    w = route->w_out;
+  }
   escha::InPartialArgs a{};
   a.code = (const uint16_t*)L->gate_up.code;
   a.rin = (const uint16_t*)L->gate_up.rin;
@@ -166,8 +173,13 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
   a.out_f = 2 * L->inter;
   a.n_pairs = P;
   a.top_k = L->top_k;
-  a.ids = ids;
+  a.ids = route ? nullptr : ids;
   a.fixed_expert = 0;
+  if (route) {
+    a.logits = route->logits;
+    a.ids_out = route->ids_out;
+    a.w_out = route->w_out;
+  }
   a.x_bf16 = in.x_bf16;
   a.y_prev = in.y_prev;
   a.ss_prev = in.ss_prev;
@@ -772,6 +784,41 @@ int escha_moe_layer_decode(const escha_moe_layer_t* L, const uint16_t* x_bf16, i
   const LayerInput in{x_bf16, nullptr, nullptr, 0.f, nullptr};
   return run_layer_decode(L, in, n_tokens, topk_ids, topk_w, y, inter_out, ws,
                           (hipStream_t)stream);
+}
+
+int escha_moe_layer_decode_logits(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,
+                                  const float* logits, int32_t* topk_ids, float* topk_w, float* y,
+                                  float* inter_out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  int rc = check_layer(L);
+  if (rc) return rc;
+  if (n_tokens < 0) return fail(ESCHA_E_ARG, "n_tokens=%d", n_tokens);
+  if (n_tokens == 0) return ESCHA_OK;
+  if (!x_bf16 || !logits || !topk_ids || !topk_w || !y)
+    return fail(ESCHA_E_NULL, "x/logits/topk_ids/topk_w/y is NULL");
+  if (L->top_k > 32) return fail(ESCHA_E_ARG, "top_k=%d > 32", L->top_k);
+  const size_t need = escha_moe_workspace_bytes(L, n_tokens, 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(ESCHA_E_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  const int E = L->gate_up.n_experts;
+  const escha::RouteOut route{logits, L->top_k, topk_ids, topk_w};
+  // the router step inside the streaming gate_up kernel (below 16 tokens,
+  // up to 256 experts and 8 slots); otherwise a kernel of its own first
+  const bool fusable = n_tokens < kGroupedDecodeTokens && E <= 64 * escha::kRouteFusedPer && L->top_k <= 8;
+  if (!fusable) {
+    hipError_t e = escha::launch_route_topk(logits, n_tokens, E, L->top_k, topk_ids, topk_w, s);
+    if (e != hipSuccess) return hip_fail(e, "route_topk launch");
+  }
+  if (n_tokens >= kGroupedDecodeTokens) {
+    GroupedWs g;
+    grouped_ws(L, n_tokens, workspace, &g);
+    return run_layer_grouped(L, x_bf16, n_tokens, topk_ids, topk_w, y, inter_out, g, false, s);
+  }
+  const DecodeWs ws = decode_ws_carve(L, n_tokens, workspace);
+  const LayerInput in{x_bf16, nullptr, nullptr, 0.f, nullptr};
+  return run_layer_decode(L, in, n_tokens, topk_ids, topk_w, y, inter_out, ws, s, nullptr, nullptr, nullptr,
+                          nullptr, fusable ? &route : nullptr);
 }
 
 int escha_moe_layer_decode_static(const escha_moe_layer_t* L, const uint16_t* x_bf16, int32_t n_tokens,

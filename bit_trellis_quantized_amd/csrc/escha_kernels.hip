@@ -21,6 +21,92 @@
 namespace escha {
 
 // ------------------------------------------------------------------------
+// Router: softmax + top-k of a row of logits, one wave per row; each lane
+// holds kMaxPer logits (E <= 64 kMaxPer). The wave-wide reductions run on
+// DPP and permlane swaps (no LDS round trips): the max, the sum of the
+// exponentials, and per selected expert an argmax.
+// ------------------------------------------------------------------------
+
+// (ov, oi) replaces (bv, bi) when it ranks higher: larger value, then
+// smaller index.
+__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
+  }
+}
+
+// The highest-ranking (value, index) pair of the wave, in every lane.
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  auto within_rows = [&](auto h) {
+    constexpr int H = decltype(h)::value;
+    const float ov = xor_lane<H>(bv);
+    const int oi = __float_as_int(xor_lane<H>(__int_as_float(bi)));
+    take_better(bv, bi, ov, oi);
+  };
+  within_rows(std::integral_constant<int, 1>{});
+  within_rows(std::integral_constant<int, 2>{});
+  within_rows(std::integral_constant<int, 4>{});
+  within_rows(std::integral_constant<int, 8>{});
+  // rows 16 apart, then halves 32 apart: both lanes of a pair see the same
+  // two candidates (r[0], r[1]) and keep the same one
+  {
+    const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto ri = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
+    bv = __uint_as_float(rv[0]);
+    bi = (int)ri[0];
+    take_better(bv, bi, __uint_as_float(rv[1]), (int)ri[1]);
+  }
+  {
+    const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+    const auto ri = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
+    bv = __uint_as_float(rv[0]);
+    bi = (int)ri[0];
+    take_better(bv, bi, __uint_as_float(rv[1]), (int)ri[1]);
+  }
+}
+
+// The first `rounds` selections of the softmax top-k of row l (E logits),
+// in decreasing-logit order, ties to the lower index: sel(r, expert,
+// probability) is called in every lane for selection r (the same values in
+// every lane; the probability is computed only WITH_W, else 0). Whole wave.
+template <int kMaxPer, bool WITH_W = true, class F>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ l, int E, int rounds, int lane, F&& sel) {
+  float v[kMaxPer];
+  uint32_t taken = 0;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxPer; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? l[e] : -INFINITY;
+    m = fmaxf(m, v[j]);
+    if (e >= E) taken |= 1u << j;
+  }
+  float s = 0.f;
+  if constexpr (WITH_W) {
+    m = wave_max(m);
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+      if (lane + 64 * j < E) s += expf(v[j] - m);
+    s = wave_sum(s);
+  }
+  for (int r = 0; r < rounds; ++r) {
+    // lane-local best untaken, then the wave's
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j)
+      if (!(taken & (1u << j))) take_better(bv, bi, v[j], lane + 64 * j);
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if constexpr (WITH_W)
+      sel(r, bi, expf(bv - m) / s);
+    else
+      sel(r, bi, 0.f);
+  }
+}
+
+// ------------------------------------------------------------------------
 // gate_up (or any single projection): transformed partial sums over one
 // 128-input chunk. grid.x = n_pairs * n_chunks * n_groups; block = 4 waves,
 // wave w streams tile-rows 8c+2w and 8c+2w+1 of the 16 output tiles of
@@ -39,7 +125,35 @@ __global__ __launch_bounds__(256) void k_in_partial(InPartialArgs a) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   float* out = a.partial + ((size_t)p * n_chunks + c) * a.out_f + g * 256;
-  const int e = a.ids ? a.ids[p] : a.fixed_expert;
+  int e;
+  if (a.logits) {
+    // the router step inside: every wave selects the top (j + 1) of the
+    // token's logits for its pair (slot j) as the standalone router step
+    // does; the work-group of slot 0 (first chunk and group) stores all
+    // top_k selections for the kernels that follow
+    const int tt = p / a.top_k, j = p - tt * a.top_k;
+    const bool writer = j == 0 && c == 0 && g == 0 && wave == 0;
+    int32_t* ido = a.ids_out + (size_t)tt * a.top_k;
+    float* wo = a.w_out + (size_t)tt * a.top_k;
+    const float* lt = a.logits + (size_t)tt * a.n_experts;
+    int ej = 0;
+    if (writer) {
+      wave_topk<kRouteFusedPer>(lt, a.n_experts, a.top_k, lane, [&](int r, int er, float wr) {
+        if (r == 0) ej = er;
+        if (lane == 0) {
+          ido[r] = er;
+          wo[r] = wr;
+        }
+      });
+    } else {  // the selection only (no softmax weights)
+      wave_topk<kRouteFusedPer, false>(lt, a.n_experts, j + 1, lane, [&](int r, int er, float) {
+        if (r == j) ej = er;
+      });
+    }
+    e = __builtin_amdgcn_readfirstlane(ej);
+  } else {
+    e = a.ids ? a.ids[p] : a.fixed_expert;
+  }
   const bool valid = e >= 0 && e < a.n_experts;  // uniform over the block
   const int t = p / a.top_k;
   const int q = lane & 3;
@@ -516,89 +630,19 @@ __global__ __launch_bounds__(256) void k_router_reduce(const float* __restrict__
   logits[i] = (float)(_Float16)s;
 }
 
-// ------------------------------------------------------------------------
-// Router: softmax + top-k per token. grid.x = n_tokens, block = 64; each
-// lane holds kMaxPer logits (E <= 64 kMaxPer). The wave-wide reductions run
-// on DPP and permlane swaps (no LDS round trips): the max, the sum of the
-// exponentials, and per selected expert an argmax.
-// ------------------------------------------------------------------------
-
-// (ov, oi) replaces (bv, bi) when it ranks higher: larger value, then
-// smaller index.
-__device__ __forceinline__ void take_better(float& bv, int& bi, float ov, int oi) {
-  if (ov > bv || (ov == bv && oi < bi)) {
-    bv = ov;
-    bi = oi;
-  }
-}
-
-// The highest-ranking (value, index) pair of the wave, in every lane.
-__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
-  auto within_rows = [&](auto h) {
-    constexpr int H = decltype(h)::value;
-    const float ov = xor_lane<H>(bv);
-    const int oi = __float_as_int(xor_lane<H>(__int_as_float(bi)));
-    take_better(bv, bi, ov, oi);
-  };
-  within_rows(std::integral_constant<int, 1>{});
-  within_rows(std::integral_constant<int, 2>{});
-  within_rows(std::integral_constant<int, 4>{});
-  within_rows(std::integral_constant<int, 8>{});
-  // rows 16 apart, then halves 32 apart: both lanes of a pair see the same
-  // two candidates (r[0], r[1]) and keep the same one
-  {
-    const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-    const auto ri = __builtin_amdgcn_permlane16_swap((unsigned)bi, (unsigned)bi, false, false);
-    bv = __uint_as_float(rv[0]);
-    bi = (int)ri[0];
-    take_better(bv, bi, __uint_as_float(rv[1]), (int)ri[1]);
-  }
-  {
-    const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
-    const auto ri = __builtin_amdgcn_permlane32_swap((unsigned)bi, (unsigned)bi, false, false);
-    bv = __uint_as_float(rv[0]);
-    bi = (int)ri[0];
-    take_better(bv, bi, __uint_as_float(rv[1]), (int)ri[1]);
-  }
-}
-
+// Router step on its own: one wave per token. grid.x = n_tokens, block = 64.
 template <int kMaxPer>
 __global__ __launch_bounds__(64) void k_route_topk(const float* __restrict__ logits, int E, int k,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
-  const float* l = logits + (size_t)t * E;
-  float v[kMaxPer];
-  uint32_t taken = 0;
-  float m = -INFINITY;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? l[e] : -INFINITY;
-    m = fmaxf(m, v[j]);
-    if (e >= E) taken |= 1u << j;
-  }
-  m = wave_max(m);
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxPer; ++j)
-    if (lane + 64 * j < E) s += expf(v[j] - m);
-  s = wave_sum(s);
-  for (int r = 0; r < k; ++r) {
-    // lane-local best untaken, then the wave's
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < kMaxPer; ++j)
-      if (!(taken & (1u << j))) take_better(bv, bi, v[j], lane + 64 * j);
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+  wave_topk<kMaxPer>(logits + (size_t)t * E, E, k, lane, [&](int r, int e, float wr) {
     if (lane == 0) {
-      ids[(size_t)t * k + r] = bi;
-      w[(size_t)t * k + r] = expf(bv - m) / s;
+      ids[(size_t)t * k + r] = e;
+      w[(size_t)t * k + r] = wr;
     }
-  }
+  });
 }
 
 // ------------------------------------------------------------------------

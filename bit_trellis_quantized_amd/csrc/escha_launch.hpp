@@ -18,6 +18,18 @@ namespace escha {
 // the RMSNorm (unit weight, eps) and rounds to bf16 itself, and writes those
 // bf16 rows to x_out when x_out is not null. partial: fp32
 // [n_pairs][in_f/128][out_f].
+// Router step inside the streaming gate_up kernel: experts per lane of its
+// top-k (n_experts <= 64 kRouteFusedPer).
+constexpr int kRouteFusedPer = 4;
+// The selections of a router step run inside a layer's first kernel: from
+// logits ([n_tokens][n_experts]) to ids_out / w_out ([n_tokens][top_k]).
+struct RouteOut {
+  const float* logits;
+  int top_k;
+  int32_t* ids_out;
+  float* w_out;
+};
+
 struct InPartialArgs {
   const uint16_t* code;
   const uint16_t* rin;
@@ -25,6 +37,12 @@ struct InPartialArgs {
   int32_t n_experts, in_f, out_f, n_pairs, top_k;
   const int32_t* ids;
   int32_t fixed_expert;
+  // logits non-null: the router step runs here (fp32 [n_pairs / top_k]
+  // [n_experts]; ids is unused) and its selections go to ids_out / w_out
+  // ([n_pairs], pair order)
+  const float* logits;
+  int32_t* ids_out;
+  float* w_out;
   const uint16_t* x_bf16;
   const float* y_prev;
   const float* ss_prev;

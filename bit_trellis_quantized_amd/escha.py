@@ -80,6 +80,8 @@ _SIGS = {
                                 ctypes.c_int),
     "escha_moe_layer_decode_static": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp],
                                       ctypes.c_int),
+    "escha_moe_layer_decode_logits": ([_P(escha_moe_layer_t), _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                       _vp], ctypes.c_int),
     "escha_dense_mlp_workspace_bytes": ([_P(escha_dense_mlp_t), _i32, _i32], _sz),
     "escha_dense_mlp_decode": ([_P(escha_dense_mlp_t), _vp, _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "escha_dense_mlp_prefill": ([_P(escha_dense_mlp_t), _vp, _i32, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -272,10 +274,14 @@ def escha_hadamard128(x: torch.Tensor, out: torch.Tensor | None = None, stream=N
     return out
 
 
-def escha_route_topk(logits: torch.Tensor, top_k: int, stream=None):
+def escha_route_topk(logits: torch.Tensor, top_k: int, stream=None, ids=None, w=None):
     T, E = logits.shape
-    ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
-    w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    if ids is None:
+        ids = torch.empty(T, top_k, dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty(T, top_k, dtype=torch.float32, device=logits.device)
+    _check_out(ids, (T, top_k), torch.int32, "ids")
+    _check_out(w, (T, top_k), torch.float32, "w")
     _check(_lib.escha_route_topk(_ptr(logits, torch.float32, "logits"), T, E, top_k,
                                  _ptr(ids), _ptr(w), _stream(stream)))
     return ids, w
@@ -366,6 +372,36 @@ def escha_moe_layer_decode(layer: MoeLayer, x_bf16, topk_ids, topk_w, out=None, 
                            workspace=None, stream=None):
     return _moe_call(_lib.escha_moe_layer_decode, layer, x_bf16, topk_ids, topk_w, out, inter_out,
                      workspace, stream, False)
+
+
+def escha_moe_layer_decode_logits(layer: MoeLayer, x_bf16, logits, out=None, topk_ids=None, topk_w=None,
+                                  inter_out=None, workspace=None, stream=None):
+    """The layer with its router step: returns (y, topk_ids, topk_w)."""
+    T = x_bf16.shape[0]
+    dev = x_bf16.device
+    lc = layer.c()
+    if out is None:
+        out = torch.empty(T, layer.hidden, dtype=torch.float32, device=dev)
+    if topk_ids is None:
+        topk_ids = torch.empty(T, layer.top_k, dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty(T, layer.top_k, dtype=torch.float32, device=dev)
+    _check_out(x_bf16, (T, layer.hidden), _BF16, "x_bf16")
+    _check_out(logits, (T, layer.gate_up.n_experts), torch.float32, "logits")
+    _check_out(out, (T, layer.hidden), torch.float32, "out")
+    _check_out(topk_ids, (T, layer.top_k), torch.int32, "topk_ids")
+    _check_out(topk_w, (T, layer.top_k), torch.float32, "topk_w")
+    if inter_out is not None:
+        _check_out(inter_out, (T * layer.top_k, layer.inter), torch.float32, "inter_out")
+    nbytes = _lib.escha_moe_workspace_bytes(ctypes.byref(lc), T, 0)
+    if workspace is None:
+        workspace = _ws(nbytes, dev)
+    _check(_lib.escha_moe_layer_decode_logits(
+        ctypes.byref(lc), _ptr(x_bf16, _BF16, "x"), T, _ptr(logits, torch.float32, "logits"),
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(topk_w, torch.float32, "topk_w"),
+        _ptr(out, torch.float32, "y"), _ptr(inter_out, torch.float32, "inter_out"), _ptr(workspace),
+        workspace.numel(), _stream(stream)))
+    return out, topk_ids, topk_w
 
 
 def escha_moe_layer_prefill(layer: MoeLayer, x_bf16, topk_ids, topk_w, out=None, inter_out=None,

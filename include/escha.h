@@ -251,6 +251,23 @@ ESCHA_API int escha_moe_layer_prefill(const escha_moe_layer_t* L, const uint16_t
                             void* stream);
 
 /*
+ * escha_moe_layer_decode with the router step inside: topk_ids / topk_w are
+ * outputs, the selections escha_route_topk makes from the router logits
+ * (fp32 [n_tokens][n_experts of the layer]), and the layer then runs on
+ * them. Below 16 tokens, with at most 256 experts and top_k <= 8, every
+ * streaming gate_up work-group selects its own pair's expert (and one per
+ * token stores the selections), which saves the router step's own launch;
+ * otherwise escha_route_topk's kernel runs first. topk_ids, topk_w and y
+ * are the same bits as escha_route_topk followed by escha_moe_layer_decode
+ * on the same inputs. Same workspace as escha_moe_layer_decode
+ * (escha_moe_workspace_bytes(L, n_tokens, 0)); top_k <= 32.
+ */
+ESCHA_API int escha_moe_layer_decode_logits(const escha_moe_layer_t* L, const uint16_t* x_bf16,
+                                            int32_t n_tokens, const float* logits, int32_t* topk_ids,
+                                            float* topk_w, float* y, float* inter_out, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
+/*
  * escha_moe_layer_decode for callers that cannot allocate device memory
  * (code under graph capture, tight serving loops, harnesses that forbid
  * allocation): no workspace argument. Its scratch is one array of

@@ -121,6 +121,31 @@ def test_layer_validation(lib):
     assert f(ctypes.byref(ok), None, 0, None, None, None, None, None, 0, None) == 0
 
 
+def test_layer_decode_logits_validation(lib):
+    f = lib.escha_moe_layer_decode_logits
+    f.argtypes = [ctypes.POINTER(Layer), ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    ok = _layer()
+    big = 1 << 40
+    assert f(None, FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == -1
+    assert f(ctypes.byref(_layer(top_k=0)), FAKE, 1, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == -7
+    assert f(ctypes.byref(ok), FAKE, -1, FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == -7
+    # logits, topk_ids (an output here), topk_w and y are required
+    for i in range(4):
+        args = [FAKE, FAKE, FAKE, FAKE]
+        args[i] = None
+        assert f(ctypes.byref(ok), FAKE, 1, *args, None, FAKE, big, None) == -1
+        assert "NULL" in _err(lib)
+    ws = lib.escha_moe_workspace_bytes
+    ws.argtypes = [ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_int32]
+    ws.restype = ctypes.c_size_t
+    need = ws(ctypes.byref(ok), 3, 0)
+    assert f(ctypes.byref(ok), FAKE, 3, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, None) == -4
+    # zero tokens: a no-op
+    assert f(ctypes.byref(ok), None, 0, None, None, None, None, None, None, 0, None) == 0
+
+
 def test_route_and_group_validation(lib):
     r = lib.escha_route_topk
     r.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,

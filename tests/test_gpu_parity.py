@@ -241,6 +241,44 @@ def test_group_bad_ids(escha, T):
     _group_check(escha, ids, 256, f"bad ids T={T}")
 
 
+@pytest.mark.parametrize("T,zipf", [(1, False), (3, False), (15, True), (16, False), (64, True)])
+def test_layer_decode_logits(escha, layer2, layer2_dev, T, zipf):
+    """The layer with its router step inside (top-k in the streaming gate_up
+    kernel below 16 tokens, a router kernel of its own from 16 on): the
+    selections are the router step's bits, and y is the bits of the router
+    step followed by the layer call; y also against the oracle."""
+    announce(f"layer decode with routing, T={T} zipf={zipf}")
+    x = synth.activations(70 + T, T, 2048)
+    logits = synth.zipf_logits(3, T) if zipf else synth.normal_logits(70 + T, T)
+    xd, ld = to_dev(x), to_dev(logits.astype(np.float32))
+    y, ids, w = escha.escha_moe_layer_decode_logits(layer2_dev, xd, ld)
+    ids2, w2 = escha.escha_route_topk(ld, 8)
+    assert torch.equal(ids, ids2)
+    assert torch.equal(w.view(torch.int32), w2.view(torch.int32))
+    y2 = escha.escha_moe_layer_decode(layer2_dev, xd, ids2, w2)
+    assert torch.equal(y.view(torch.int32), y2.view(torch.int32))
+    ref_ids, ref_w = oracle.route_topk(logits, 8)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    ref = oracle.moe_layer(layer2, x, ref_ids, w.cpu().numpy())
+    assert_close(y.cpu().numpy(), ref, f"decode with routing T={T}")
+
+
+def test_layer_decode_logits_ties(escha, layer2, layer2_dev):
+    """Tied logits inside the fused router step: ties go to the lower expert
+    index, as in the router step of its own."""
+    announce("layer decode with routing, tied logits")
+    T = 20
+    logits = np.zeros((T, 256), dtype=np.float32)
+    logits[0, [200, 17, 90, 3, 250, 11, 40, 8, 9]] = 1.0
+    logits[1:, :] = 0.5
+    x = synth.activations(7, T, 2048)
+    for n in (2, T):  # router step in the streaming kernel; a router kernel of its own
+        ld = to_dev(logits[:n])
+        _, ids, w = escha.escha_moe_layer_decode_logits(layer2_dev, to_dev(x[:n]), ld)
+        ref_ids, _ = oracle.route_topk(logits[:n], 8)
+        assert np.array_equal(ids.cpu().numpy(), ref_ids)
+
+
 # ------------------------------------------------------------------ projections
 
 @pytest.mark.parametrize("T", [1, 3])
