@@ -264,6 +264,8 @@ struct GroupedWs {
   float* yd;        // fp32 [P][hidden]
   int32_t* xg_exp;  // [P]
   int32_t* xd_exp;  // [P][inter/128]
+  int32_t* sctl;    // control blocks of the one-launch small-tile layer kernel, sctl_words per layer
+  int32_t sctl_words;
 };
 
 // Carves the grouped workspace; with ws == nullptr only sizes it. The
@@ -301,6 +303,8 @@ size_t grouped_ws(const escha_moe_layer_t* L, int64_t T, void* ws, GroupedWs* ou
   g.yd = (float*)take((size_t)P * L->hidden * sizeof(float));
   g.xg_exp = (int32_t*)take((size_t)P * sizeof(int32_t));
   g.xd_exp = (int32_t*)take((size_t)P * (L->inter / 128) * sizeof(int32_t));
+  g.sctl_words = (int32_t)round_up(escha::small_ctl_words(mt, L->inter) * sizeof(int32_t)) / sizeof(int32_t);
+  g.sctl = (int32_t*)take(nl * (size_t)g.sctl_words * sizeof(int32_t));
   if (out) *out = g;
   return off;
 }
@@ -313,6 +317,7 @@ GroupedWs grouped_layer(const GroupedWs& g, const escha_moe_layer_t* L, int64_t 
   const size_t chunks = ((size_t)P + 63) / 64;
   const int32_t mt = grouped_max_tiles(L, T, true);
   GroupedWs v = g;
+  v.sctl += (size_t)l * g.sctl_words;
   v.hist += (size_t)l * chunks * E;
   v.base += (size_t)l * chunks * E;
   v.rank += (size_t)l * P;
@@ -335,9 +340,12 @@ int group_layers(const escha_moe_layer_t* L, int T, const int32_t* ids, const Gr
   const int E = L->gate_up.n_experts;
   const bool small = grouped_small(L, T, prefill);
   if (escha::group_small_ok(P, E)) {
+    // also zeroes the layers' control blocks of the one-launch small-tile
+    // layer kernel (run_layer_grouped uses it after this grouping only)
     const hipError_t e = escha::launch_group_small(
         ids, P, E, g.counts, g.offsets, g.perm, g.inv, small ? kSmallTileTokens : kTileTokens,
-        grouped_max_tiles(L, T, true), g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s, n_layers);
+        grouped_max_tiles(L, T, true), g.t_expert, g.t_row0, g.t_rows, g.n_tiles, s, n_layers, g.sctl,
+        g.sctl_words);
     return e == hipSuccess ? ESCHA_OK : hip_fail(e, "group launch");
   }
   hipError_t e = escha::launch_group(ids, P, E, g.counts, g.offsets, g.perm, g.inv, g.hist, g.base,
@@ -399,9 +407,14 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   gu.bias = gu_bias;
   int rc = probe_proj(0, s);
   if (rc) return rc;
-  e = small ? escha::launch_small_gate_up(gu, max_tiles, L->gate_up.k_bits, s)
-            : escha::launch_grouped_gate_up(gu, max_tiles, L->gate_up.k_bits, s);
-  if (e != hipSuccess) return hip_fail(e, "grouped gate_up launch");
+  // small tiles after the one-work-group grouping (which zeroed the control
+  // block): both projections in one launch
+  const bool one_launch = small && escha::group_small_ok(P, E);
+  if (!one_launch) {
+    e = small ? escha::launch_small_gate_up(gu, max_tiles, L->gate_up.k_bits, s)
+              : escha::launch_grouped_gate_up(gu, max_tiles, L->gate_up.k_bits, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped gate_up launch");
+  }
   escha::GroupedArgs dn = gu;
   dn.code = (const uint16_t*)L->down.code;
   dn.rout = (const uint16_t*)L->down.rout;
@@ -413,9 +426,14 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
   dn.y_out = g.yd;
   dn.inter_out = nullptr;
   dn.bias = nullptr;
-  e = small ? escha::launch_small_down(dn, max_tiles, L->down.k_bits, s)
-            : escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
-  if (e != hipSuccess) return hip_fail(e, "grouped down launch");
+  if (one_launch) {
+    e = escha::launch_small_layer(gu, dn, max_tiles, L->gate_up.k_bits, L->down.k_bits, g.sctl, s);
+    if (e != hipSuccess) return hip_fail(e, "small-tile layer launch");
+  } else {
+    e = small ? escha::launch_small_down(dn, max_tiles, L->down.k_bits, s)
+              : escha::launch_grouped_down(dn, max_tiles, L->down.k_bits, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped down launch");
+  }
   rc = probe_proj(1, s);
   if (rc) return rc;
   if (!combine) return ESCHA_OK;

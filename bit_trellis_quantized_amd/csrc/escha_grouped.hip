@@ -687,7 +687,7 @@ struct SmallLds {
 // tile is skipped, and each chunk's activations are rescaled to the row's
 // exponent before their contraction; the lanes n < 16 store the row
 // exponent of token n at rexp_out[n] when rexp_out is not null.
-template <int K, bool RESCALE>
+template <int K, bool RESCALE, bool FRESH = false>
 __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code_e, int n_nt, int c0,
                                                int nch, int nt0, const _Float16* __restrict__ X,
                                                int x_pitch, const int32_t* __restrict__ xexp, int nblk,
@@ -716,11 +716,17 @@ __device__ __forceinline__ void small_mainloop(const uint16_t* __restrict__ code
     const int32_t* erow = xexp + (size_t)xr * nblk;
     // clamped indices: every load is issued unconditionally, back to back
     // (a load under a branch would be waited for before the branch)
+    auto ld = [&](int b) {  // FRESH: past the compute unit's cache (written during this launch)
+      if constexpr (FRESH)
+        return __hip_atomic_load(const_cast<int32_t*>(erow + b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        return erow[b];
+    };
     int eb_all[kSmallMaxBlocks], eb_half[kSmallMaxBlocks / 2];
 #pragma unroll
-    for (int b = 0; b < kSmallMaxBlocks; ++b) eb_all[b] = erow[b < nblk ? b : nblk - 1];
+    for (int b = 0; b < kSmallMaxBlocks; ++b) eb_all[b] = ld(b < nblk ? b : nblk - 1);
 #pragma unroll
-    for (int ch = 0; ch < kSmallMaxBlocks / 2; ++ch) eb_half[ch] = erow[c0 + (ch < nch ? ch : 0)];
+    for (int ch = 0; ch < kSmallMaxBlocks / 2; ++ch) eb_half[ch] = ld(c0 + (ch < nch ? ch : 0));
     int emin = kExpZeroBlock;
 #pragma unroll
     for (int b = 0; b < kSmallMaxBlocks; ++b) emin = eb_all[b] < emin ? eb_all[b] : emin;
@@ -854,11 +860,7 @@ __device__ __forceinline__ void small_pairs_to_lds(const f32x4 (&D)[2], SmallLds
 // rows' exponents undone, h = SiLU(gate) * up for the block's channels,
 // then down's rotated input with the block's exponent.
 template <int K>
-__global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
-  const int nb = a.inter / 128;
-  const int c = blockIdx.x % nb;
-  const int tile = blockIdx.x / nb;
-  if (tile >= *a.n_tiles) return;  // uniform
+__device__ __forceinline__ void small_gate_up_block(const GroupedArgs& a, int tile, int c, SmallLds& sh) {
   const int e = a.t_expert[tile];
   const int row0 = a.t_row0[tile];
   const int rows = a.t_rows[tile];
@@ -869,7 +871,6 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   const int ncg = a.hidden / 128;
   const int nt0 = nq < 2 ? 8 * c + 4 * nq : a.inter / 16 + 8 * c + 4 * (nq - 2);
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncg * 8 * n_nt * (16 * K);
-  __shared__ SmallLds sh;
   if (threadIdx.x < rows) sh.rexp[threadIdx.x] = a.x_exp_in[row0 + threadIdx.x];  // read after the barrier below
   bool pairs = false;
   if constexpr (K == 2) pairs = rows <= 8;  // uniform
@@ -922,17 +923,26 @@ __global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
   }
 }
 
+template <int K>
+__global__ __launch_bounds__(512, 4) void k_small_gate_up(GroupedArgs a) {
+  const int nb = a.inter / 128;
+  const int c = blockIdx.x % nb;
+  const int tile = blockIdx.x / nb;
+  if (tile >= *a.n_tiles) return;  // uniform
+  __shared__ SmallLds sh;
+  small_gate_up_block<K>(a, tile, c, sh);
+}
+
 // down, small tiles. grid.x = max_tiles * (hidden / 256), block = 512. The
 // epilogue undoes the row's exponent, applies H_n, rout and the pair's
 // router weight and stores the pair's 256 outputs (fp32) at its sorted
 // index. 128-channel blocks that are zero for every token of the tile are
 // skipped.
-template <int K>
-__global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
-  const int ng = a.hidden / 256;
-  const int r = blockIdx.x % ng;
-  const int tile = blockIdx.x / ng;
-  if (tile >= *a.n_tiles) return;  // uniform
+// FRESH: down's input exponents were written during this launch (by the
+// gate_up blocks of the one-launch layer kernel), so they are read with
+// loads that go past the compute unit's cache.
+template <int K, bool FRESH = false>
+__device__ __forceinline__ void small_down_block(const GroupedArgs& a, int tile, int r, SmallLds& sh) {
   const int e = a.t_expert[tile];
   const int row0 = a.t_row0[tile];
   const int rows = a.t_rows[tile];
@@ -942,9 +952,8 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
   const int n_nt = a.hidden / 16;
   const int ncd = a.inter / 128;
   const uint16_t* code_e = a.code + (size_t)e * (size_t)ncd * 8 * n_nt * (16 * K);
-  __shared__ SmallLds sh;
   f32x4 D[4];
-  small_mainloop<K, true>(code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq,
+  small_mainloop<K, true, FRESH>(code_e, n_nt, kh * (ncd / 2), ncd / 2, 16 * r + 4 * nq,
                           reinterpret_cast<const _Float16*>(a.x_in), a.inter, a.x_exp_in, ncd, row0, rows,
                           sh.stage + wave * Stage<K>::kDw, lane, D, wave == 0 ? sh.rexp : nullptr);
   small_to_lds(D, sh, kh, nq, lane);
@@ -968,6 +977,95 @@ __global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
     yo[lane + 64] = z1 * kInvSqrt128 * r01 * wt;
     yo[128 + lane] = z2 * kInvSqrt128 * r10 * wt;
     yo[192 + lane] = z3 * kInvSqrt128 * r11 * wt;
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(512, 4) void k_small_down(GroupedArgs a) {
+  const int ng = a.hidden / 256;
+  const int r = blockIdx.x % ng;
+  const int tile = blockIdx.x / ng;
+  if (tile >= *a.n_tiles) return;  // uniform
+  __shared__ SmallLds sh;
+  small_down_block<K>(a, tile, r, sh);
+}
+
+// ------------------------------------------------------------------------
+// One small-tile layer in one launch: the gate_up blocks of every tile and
+// then its down blocks, as tasks that the work-groups of each XCD claim in
+// order from the XCD's ticket (task 8 j + x is the j-th claim on XCD x). All
+// of tile t's tasks run on XCD t % 8, so the hand-off of down's input stays
+// in that XCD's L2: a gate_up block stores its part of the input, waits
+// until the stores are done and sets its flag with a plain store (which
+// lands in the L2); a down block polls the tile's flags with loads that
+// read the L2 and then reads the input. No compute unit can hold a stale
+// copy of that input in its cache: each 1 KiB row belongs to one tile and
+// is read only after the tile's flags, and the exponents (16 bytes per row,
+// several tiles to a cache line) are read past the cache. A down block
+// waits only for gate_up blocks, which have smaller numbers on the same XCD
+// and are claimed first, so the smallest unfinished task can always run.
+// Waits are bounded (0.5 s of the 100 MHz clock) and set the error word
+// when they give up. The down blocks of the first tiles run while the last
+// gate_up blocks do, where two launches would leave the device part idle.
+// Control block, zeroed before the launch (by the grouping kernel): ticket
+// of XCD x at word 32 x, the error word at kSmallCtlErr, and from
+// kSmallCtlFlags the flag of tile t's gate_up block c at t * (inter / 128) + c.
+// ------------------------------------------------------------------------
+constexpr long long kSmallWaitTicks = 50000000;
+
+__device__ __forceinline__ int xcd_of_this_wave() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF;  // HW_REG_XCC_ID, bits 3:0
+}
+
+template <int KG, int KD>
+__global__ __launch_bounds__(512, 4) void k_small_layer(GroupedArgs gu, GroupedArgs dn, int32_t* ctl) {
+  __shared__ SmallLds sh;
+  __shared__ int claim[2];
+  if (threadIdx.x == 0) {
+    const int x = xcd_of_this_wave();
+    const int nt = *gu.n_tiles;
+    const int j = x < 8 ? __hip_atomic_fetch_add(ctl + 32 * x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    claim[0] = x < 8 ? 8 * j + x : -1;
+    claim[1] = nt;
+  }
+  __syncthreads();
+  const int task = claim[0], nt = claim[1];
+  const int nb = gu.inter / 128, ng = dn.hidden / 256;
+  const int n8 = (nt + 7) / 8;
+  const int n_gu = 8 * nb * n8, n_dn = 8 * ng * n8;
+  if (task < 0 || task >= n_gu + n_dn) return;  // uniform: a surplus work-group
+  int32_t* flags = ctl + kSmallCtlFlags;
+  if (task < n_gu) {
+    const int j = task >> 3;
+    const int tile = 8 * (j / nb) + (task & 7);
+    const int c = j % nb;
+    if (tile >= nt) return;
+    small_gate_up_block<KG>(gu, tile, c, sh);
+    // every wave's stores of down's input are done, then the flag
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) *(volatile int32_t*)(flags + tile * nb + c) = 1;
+  } else {
+    const int t2 = task - n_gu;
+    const int j = t2 >> 3;
+    const int tile = 8 * (j / ng) + (t2 & 7);
+    const int r = j % ng;
+    if (tile >= nt) return;
+    if (threadIdx.x < 64) {  // wave 0: lane c < nb polls gate_up block c's flag
+      int32_t* f = flags + tile * nb + (threadIdx.x < nb ? threadIdx.x : 0);
+      const long long t0 = wall_clock64();
+      for (int it = 0;; ++it) {
+        const int v = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__ballot(v == 0) == 0) break;
+        if ((it & 15) == 15 && wall_clock64() - t0 > kSmallWaitTicks) {
+          if (threadIdx.x == 0) __hip_atomic_store(ctl + kSmallCtlErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    __syncthreads();
+    small_down_block<KD, true>(dn, tile, r, sh);
   }
 }
 
@@ -1346,6 +1444,26 @@ hipError_t launch_small_gate_up(const GroupedArgs& a, int max_tiles, int k_bits,
     hipLaunchKernelGGL(k_small_gate_up<2>, dim3(grid), dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL(k_small_gate_up<3>, dim3(grid), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+unsigned small_layer_grid(int max_tiles, int inter, int hidden) {
+  return (unsigned)(8 * ((max_tiles + 7) / 8) * (inter / 128 + hidden / 256) + 64);
+}
+
+hipError_t launch_small_layer(const GroupedArgs& gu, const GroupedArgs& dn, int max_tiles, int k_gu, int k_dn,
+                              int32_t* ctl, hipStream_t s) {
+  const dim3 grid(small_layer_grid(max_tiles, gu.inter, dn.hidden)), block(512);
+  if (k_gu == 2 && k_dn == 3)
+    hipLaunchKernelGGL((k_small_layer<2, 3>), grid, block, 0, s, gu, dn, ctl);
+  else if (k_gu == 2 && k_dn == 2)
+    hipLaunchKernelGGL((k_small_layer<2, 2>), grid, block, 0, s, gu, dn, ctl);
+  else if (k_gu == 3 && k_dn == 3)
+    hipLaunchKernelGGL((k_small_layer<3, 3>), grid, block, 0, s, gu, dn, ctl);
+  else if (k_gu == 3 && k_dn == 2)
+    hipLaunchKernelGGL((k_small_layer<3, 2>), grid, block, 0, s, gu, dn, ctl);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

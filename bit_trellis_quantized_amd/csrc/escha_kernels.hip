@@ -783,7 +783,8 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
                                                       int tm, int max_tiles, int32_t* __restrict__ t_expert,
                                                       int32_t* __restrict__ t_row0,
                                                       int32_t* __restrict__ t_rows,
-                                                      int32_t* __restrict__ n_tiles) {
+                                                      int32_t* __restrict__ n_tiles,
+                                                      int32_t* __restrict__ clear, int n_clear) {
   __shared__ int32_t cnt[kGroupSmallExperts];       // per expert: running count, then its offset
   __shared__ int32_t wc[16][kGroupSmallExperts];    // per wave of the chunk and expert: its count
   __shared__ int32_t scan[1024];
@@ -795,6 +796,9 @@ __global__ __launch_bounds__(1024) void k_group_small(const int32_t* __restrict_
   offsets += ly * (E + 1);
   perm += ly * P;
   if (inv) inv += ly * P;
+  // the layer's control block of the one-launch small-tile layer kernel
+  if (clear)
+    for (int i = tid; i < n_clear; i += 1024) clear[ly * n_clear + i] = 0;
   // pass 1: counts (LDS atomics on integers: exact, order-free)
   if (tid < E) cnt[tid] = 0;
   __syncthreads();
@@ -1009,9 +1013,10 @@ bool group_small_ok(int P, int E) { return P <= kGroupSmallPairs && E <= kGroupS
 
 hipError_t launch_group_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                               int32_t* perm, int32_t* inv, int tm, int max_tiles, int32_t* t_expert,
-                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s, int n_layers) {
+                              int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s, int n_layers,
+                              int32_t* clear, int n_clear) {
   hipLaunchKernelGGL(k_group_small, dim3(1, (unsigned)n_layers), dim3(1024), 0, s, ids, P, E, counts, offsets,
-                     perm, inv, tm, max_tiles, t_expert, t_row0, t_rows, n_tiles);
+                     perm, inv, tm, max_tiles, t_expert, t_row0, t_rows, n_tiles, clear, n_clear);
   return last_launch();
 }
 

@@ -208,6 +208,16 @@ hipError_t launch_grouped_down(const GroupedArgs& a, int max_tiles, int k_bits, 
 // Small tiles (at most 16 tokens of one expert; inter and hidden multiples
 // of 256): weights decoded straight into matrix-core operands.
 hipError_t launch_small_gate_up(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
+// Both small-tile projections of a layer in one launch (gate_up blocks,
+// then down blocks that wait for their tile's gate_up blocks on the same
+// XCD). ctl: the control block, kSmallCtlFlags + max_tiles * (inter / 128)
+// words, zero before the launch; word kSmallCtlErr is 1 afterwards if a
+// wait gave up.
+constexpr int kSmallCtlErr = 256;
+constexpr int kSmallCtlFlags = 288;
+inline size_t small_ctl_words(int max_tiles, int inter) { return kSmallCtlFlags + (size_t)max_tiles * (inter / 128); }
+hipError_t launch_small_layer(const GroupedArgs& gu, const GroupedArgs& dn, int max_tiles, int k_gu, int k_dn,
+                              int32_t* ctl, hipStream_t s);
 hipError_t launch_small_down(const GroupedArgs& a, int max_tiles, int k_bits, hipStream_t s);
 hipError_t launch_combine_sorted(const SortedCombineArgs& a, hipStream_t s);
 hipError_t launch_combine_next(const CombineNextArgs& a, hipStream_t s);
@@ -285,10 +295,12 @@ hipError_t launch_router_logits(const RouterArgs& a, hipStream_t s);
 // One work-group per layer doing all of the grouping (and, with t_expert
 // non-null, the tile list of launch_make_tiles) when group_small_ok(P, E).
 bool group_small_ok(int P, int E);
+// clear (nullable): n_clear words per layer zeroed as well (layer l's at
+// clear + l n_clear), the small-tile layer kernel's control blocks.
 hipError_t launch_group_small(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                               int32_t* perm, int32_t* inv, int tm, int max_tiles, int32_t* t_expert,
                               int32_t* t_row0, int32_t* t_rows, int32_t* n_tiles, hipStream_t s,
-                              int n_layers = 1);
+                              int n_layers = 1, int32_t* clear = nullptr, int n_clear = 0);
 hipError_t launch_group(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                         int32_t* perm, int32_t* inv, int32_t* hist, int32_t* base, int32_t* rank,
                         hipStream_t s, int n_layers = 1);
