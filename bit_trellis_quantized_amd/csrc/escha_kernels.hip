@@ -762,10 +762,10 @@ __global__ __launch_bounds__(64) void k_group_scatter(const int32_t* __restrict_
 
 // ------------------------------------------------------------------------
 // Grouping of up to kGroupSmallPairs pairs in one work-group of 1024 threads
-// (decode-sized calls: one launch instead of count, scan, offsets, scatter
-// and tile list): the same results as the multi-pass path -- counts,
-// offsets, the stable permutation (sorted index -> pair, ties in pair
-// order), its inverse, and optionally the tile list (tiles of tm
+// (one launch instead of count, scan, offsets, scatter and tile list): the
+// same results as the multi-pass path -- counts, offsets, the stable
+// permutation (sorted index -> pair, ties in pair order), its inverse, and
+// optionally the tile list (tiles of tm
 // consecutive sorted pairs of one expert, experts in order). Pairs are
 // taken 1024 at a time; inside a wave, the lanes holding the same expert
 // are found with one ballot per bit of the expert index; a wave's count per

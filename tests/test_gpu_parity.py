@@ -211,11 +211,11 @@ def _group_check(escha, ids, E, what):
     assert np.array_equal(perm.cpu().numpy()[:n], rp[:n]), what
 
 
-@pytest.mark.parametrize("T", [1024, 1025])
+@pytest.mark.parametrize("T", [1024, 1025, 8192])
 def test_group_one_expert_for_all(escha, T):
-    """Every pair on one expert: 8192 pairs (the most one work-group groups)
-    and 8200 (the multi-pass path); ranks in pair order across all waves and
-    chunks."""
+    """Every pair on one expert: 8192 pairs (the most one work-group groups),
+    8200 and 65536 (the multi-pass path); ranks in pair order across all
+    waves and chunks."""
     _group_check(escha, np.full((T, 8), 77, dtype=np.int32), 256, f"one expert T={T}")
 
 
