@@ -42,11 +42,18 @@ GU_BYTES_PER_PAIR = 2048 // 16 * 1024 // 16 * 32 * 2   # 524,288
 DN_BYTES_PER_PAIR = 512 // 16 * 2048 // 16 * 48 * 2    # 393,216
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3  # MI355X fp32 vector peak (FMA = 2 flops)
-# VALU view of the same launches: decode costs 5.6 VALU lane-operations per
-# weight (721 VALU instructions per wave and 128 weights per lane in the
-# gfx950 ISA of the operand decoder); MI355X issues 256 CUs x 4 SIMDs x 16
-# lanes per clock at 2.4 GHz = 39.32 T lane-operations/s (non-packed).
+# VALU view of the same launches: the decode arithmetic in VALU
+# lane-operations per weight, counted in the gfx950 ISA of each decoder: 5.6
+# for the quarter, operand and LDS-tile layouts (11 operations per pair of
+# weights plus addressing: 721 VALU instructions per wave and 128 weights
+# per lane in the operand decoder), 4.6 for the K=2 column-pair layouts (9
+# per pair plus addressing) that the one-launch gate_up tasks and the
+# small-tile gate_up blocks of up to 8 tokens use. A pair's gate_up holds
+# two thirds of its weights. MI355X issues 256 CUs x 4 SIMDs x 16 lanes per
+# clock at 2.4 GHz = 39.32 T lane-operations/s (non-packed).
 DECODE_OPS_PER_WEIGHT = 5.6
+DECODE_OPS_PAIRS = 4.6
+DECODE_OPS_PAIRED_GU = round((2 * DECODE_OPS_PAIRS + DECODE_OPS_PER_WEIGHT) / 3, 2)  # 4.93
 VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 WEIGHTS_PER_PAIR = 2048 * 1024 + 512 * 2048  # 3,145,728
 
@@ -326,17 +333,17 @@ def router_workload(args, log):
     print(json.dumps(out), flush=True)
 
 
-def roofline_hbm(kernel, launch_bytes, launch_ms, traffic, samples):
+def roofline_hbm(kernel, launch_bytes, launch_ms, traffic, samples, ops_per_weight=DECODE_OPS_PER_WEIGHT):
     achieved = launch_bytes / (launch_ms / 1e3) / 1e9
     decodes = launch_bytes / (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR) * WEIGHTS_PER_PAIR
-    valu = decodes * DECODE_OPS_PER_WEIGHT / (launch_ms / 1e3) / 1e12
+    valu = decodes * ops_per_weight / (launch_ms / 1e3) / 1e12
     return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
             "bytes_per_launch": int(launch_bytes), "avg_launch_us": round(launch_ms * 1e3, 3),
             "samples": samples,
             "valu": {"bound": "alu", "achieved": round(valu, 2), "peak": round(VALU_PEAK_TOPS, 2),
                      "unit": "T lane-op/s", "frac": round(valu / VALU_PEAK_TOPS, 4),
-                     "decodes_per_launch": int(decodes), "ops_per_weight": DECODE_OPS_PER_WEIGHT}}
+                     "decodes_per_launch": int(decodes), "ops_per_weight": ops_per_weight}}
 
 
 def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
@@ -451,17 +458,19 @@ def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
     roofline = None
     if probe_avg_ms and probe_ok:
         launch_bytes = code_bytes_step if one_launch else code_bytes_step / NL
+        ops = DECODE_OPS_PAIRED_GU
         if one_launch:
             kernel = "k_stack_flow<2,3> (one launch: every layer's tasks)"
         elif T < 16:
             kernel = "one layer's decode launches (k_in_partial + k_down_partial + k_combine)"
+            ops = DECODE_OPS_PER_WEIGHT
         else:
-            kernel = ("one layer's grouped launches (k_small_gate_up + k_small_down + k_combine_next: "
-                      "combine, RMSNorm and the next layer's input rotation; the pairs of all layers "
-                      "are grouped once per step)")
+            kernel = ("one layer's grouped launches (k_small_layer: the small-tile gate_up and down blocks "
+                      "in one launch; k_combine_next: combine, RMSNorm and the next layer's input rotation; "
+                      "the pairs of all layers are grouped once per step)")
         key = {1: "stack_b1", 8: "stack_b8", 64: "stack_b64"}.get(T)
         traffic = measured_traffic(key) if key else None
-        roofline = roofline_hbm(kernel, launch_bytes, probe_avg_ms, traffic, len(probe_ms))
+        roofline = roofline_hbm(kernel, launch_bytes, probe_avg_ms, traffic, len(probe_ms), ops)
     status = None
     if one_launch:  # every timed call completed (no wait gave up)
         status = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pool))
@@ -591,9 +600,10 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
             "code_bytes": int(code_bytes), "code_gbs": round(code_bytes / (proj_ms / 1e3) / 1e9, 1)}
     else:
         kernel = ("k_in_partial (with the router step) + k_down_partial (streaming decode)" if T < 16 else
-                  "k_small_gate_up + k_small_down (small-tile grouped decode, MFMA 16x16x32)")
+                  "k_small_layer (small-tile gate_up and down blocks in one launch, MFMA 16x16x32)")
         entry["roofline"] = roofline_hbm(kernel, code_bytes, proj_ms,
-                                         measured_traffic("layer_cfg2" if T < 16 else "layer_cfg3"), NLc)
+                                         measured_traffic("layer_cfg2" if T < 16 else "layer_cfg3"), NLc,
+                                         DECODE_OPS_PER_WEIGHT if T < 16 else DECODE_OPS_PAIRED_GU)
     return entry
 
 
