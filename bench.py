@@ -111,7 +111,7 @@ def parse():
     ap.add_argument("--path", choices=["auto", "flow", "layered"], default="auto",
                     help="stack: one launch for all layers (flow), the layer-by-layer path "
                          "(layered: per-pair streaming below 16 tokens, grouped kernels from 16 "
-                         "on), or auto: flow below 16 tokens, layered from 16 on")
+                         "on), or auto: flow up to 16 tokens, layered above")
     ap.add_argument("--also-batches", default="8,64",
                     help="stack: further decode batches timed after the main one on the same "
                          "resident stack and reported under 'batches' (empty: none)")
@@ -353,7 +353,7 @@ def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
     import torch
     NL, R = len(stack.layers), args.pool
     hidden, E, k = synth.HIDDEN, synth.N_EXPERTS, synth.TOP_K
-    path = args.path if args.path != "auto" else ("flow" if T < 16 else "layered")
+    path = args.path if args.path != "auto" else ("flow" if T <= 16 else "layered")
     one_launch = path == "flow"
     n_probe = 2 if one_launch else 2 * NL
 

@@ -234,8 +234,10 @@ __device__ __forceinline__ bool all_ok(const Lds& sh) {
 // tiles 4nq..4nq+3) with the block's activations on the matrix cores and
 // leave the 64 sums in sh.red[0][stride * cl + 16 (4nq + j) + n] (output
 // 16 (4nq + j) + n of the task).
-__device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq,
-                                           int stride, int lane) {
+// OPS: the operands of tile-row pair pp, OPS(pp, A4) (decoded beforehand,
+// or just now when the task decodes after its wait).
+template <class OPS>
+__device__ __forceinline__ void mfma_block(Lds& sh, OPS&& ops, int cl, int nq, int stride, int lane) {
   // B operands of the four tile-row pairs: column 0 of B = high parts,
   // column 1 = low parts, other columns zero; only the lanes of columns 0
   // and 1 read LDS
@@ -252,10 +254,13 @@ __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int 
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
+  for (int pp = 0; pp < 4; ++pp) {
+    h16x8 A[4];
+    ops(pp, A);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B[pp], D[j], 0, 0, 0);
+      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], B[pp], D[j], 0, 0, 0);
+  }
   float4 zr[4];
   finish_mfma(D, sh.xe[cl], zr);
   if ((lane & 15) == 0) {
@@ -272,7 +277,8 @@ __device__ __forceinline__ void mfma_block(Lds& sh, const h16x8 (&A)[4][4], int 
 // D[m][2 q + h] with m = 8 set + c collects output column c (parity 0) or
 // c + 8 (parity 1) over the set's input rows. The two sets' sums go to
 // sh.red[set] and are added in sum_transform_store.
-__device__ __forceinline__ void mfma_pairs(Lds& sh, const h16x8 (&A)[4][4], int cl, int nq, int lane) {
+template <class OPS>
+__device__ __forceinline__ void mfma_pairs(Lds& sh, OPS&& ops, int cl, int nq, int lane) {
   const int col = lane & 15;
   const int g = lane >> 4;
   h16x8 B[4];
@@ -292,10 +298,13 @@ __device__ __forceinline__ void mfma_pairs(Lds& sh, const h16x8 (&A)[4][4], int 
 #pragma unroll
   for (int j = 0; j < 4; ++j) D[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
+  for (int pp = 0; pp < 4; ++pp) {
+    h16x8 A[4];
+    ops(pp, A);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[pp][j], B[pp], D[j], 0, 0, 0);
+      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], B[pp], D[j], 0, 0, 0);
+  }
   // high + low part into the even columns (finish_mfma), then lanes (col
   // 4 set + 2 parity, g) with set = g >> 1 hold outputs 8 parity + 4 (g &
   // 1) .. + 3 of each tile for that set
@@ -306,6 +315,18 @@ __device__ __forceinline__ void mfma_pairs(Lds& sh, const h16x8 (&A)[4][4], int 
     const int off = 128 * cl + 8 * ((col >> 1) & 1) + 4 * (g & 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<float4*>(&sh.red[set][off + 16 * (4 * nq + j)]) = zr[j];
+  }
+}
+
+// Tile-row pair pp's operands from a decoder whose decode takes the pair
+// as a template argument (pp is a constant once the callers are unrolled).
+template <class DEC>
+__device__ __forceinline__ void decode_pp(const DEC& dec, int pp, h16x8 (&A)[4]) {
+  switch (pp) {
+    case 0: dec.template decode<0>(A); break;
+    case 1: dec.template decode<1>(A); break;
+    case 2: dec.template decode<2>(A); break;
+    default: dec.template decode<3>(A); break;
   }
 }
 
@@ -360,8 +381,13 @@ __device__ __forceinline__ void store_combined(const FlowArgs& a, bool last, int
 
 }  // namespace
 
-template <int KG, int KD>
-__global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a) {
+// LATE: a task stages its codes before its wait but decodes them only
+// after it, each tile-row pair just before its MFMAs, so that it holds 32
+// rather than 64 registers of operands while it waits and three work-groups
+// fit on a compute unit (larger batches, where a layer's tasks are many
+// times the device's slots, so decode ahead of the chain matters little).
+template <int KG, int KD, bool LATE>
+__global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const FlowArgs a) {
   __shared__ Lds sh;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -438,16 +464,18 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
       sd[lane + 64] = f16_to_f32(s1);
     }
     h16x8 A[4][4];
-    if constexpr (KG == 2) {  // column-pair layout: 9 VALU operations per pair of weights
-      const PairDecoder dec(stage, lane);
-      dec.template decode<0>(A[0]);
-      dec.template decode<1>(A[1]);
-      dec.template decode<2>(A[2]);
-      dec.template decode<3>(A[3]);
-    } else {
-      decode_stage_mfma<KG>(stage, lane, A);
+    if constexpr (!LATE) {
+      if constexpr (KG == 2) {  // column-pair layout: 9 VALU operations per pair of weights
+        const PairDecoder dec(stage, lane);
+        dec.template decode<0>(A[0]);
+        dec.template decode<1>(A[1]);
+        dec.template decode<2>(A[2]);
+        dec.template decode<3>(A[3]);
+      } else {
+        decode_stage_mfma<KG>(stage, lane, A);
+      }
+      pin_operands(A);
     }
-    pin_operands(A);
     // arguments the normalisation needs, read now rather than after the wait
     float eps = a.eps;
     float inv_h = __int_as_float((96 + __builtin_clz(H)) << 23);  // 1 / H (a power of two)
@@ -495,10 +523,25 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
     if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
-      if constexpr (KG == 2)
-        mfma_pairs(sh, A, cl, nq, lane);
-      else
-        mfma_block(sh, A, cl, nq, 128, lane);
+      auto held = [&](int pp, h16x8(&A4)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A4[j] = A[pp][j];
+      };
+      if constexpr (KG == 2) {
+        if constexpr (LATE) {
+          const PairDecoder dec(stage, lane);
+          mfma_pairs(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, lane);
+        } else {
+          mfma_pairs(sh, held, cl, nq, lane);
+        }
+      } else {
+        if constexpr (LATE) {
+          const OperandDecoder<KG> dec(stage, lane);
+          mfma_block(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, 128, lane);
+        } else {
+          mfma_block(sh, held, cl, nq, 128, lane);
+        }
+      }
       __syncthreads();
       sum_transform_store<false, KG == 2>(sh, kChunks, 1.0f, out, tag, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
@@ -537,8 +580,10 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
       sd[lane] = f16_to_f32(s0);
       sd[lane + 64] = f16_to_f32(s1);
     }
-    if (active) decode_stage_mfma<KD>(stage, lane, A);
-    pin_operands(A);
+    if constexpr (!LATE) {
+      if (active) decode_stage_mfma<KD>(stage, lane, A);
+      pin_operands(A);
+    }
     __syncthreads();  // sh.ok initialised
     // gate and up sums of the chunk's channels over gate_up's input parts,
     // once every gate_up task of this pair has written them: the chunk's
@@ -585,7 +630,18 @@ __global__ __launch_bounds__(64 * kWaves, 4) void k_stack_flow(const FlowArgs a)
     __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
       if (active && !sh.skip[cl]) {
-        mfma_block(sh, A, cl, nq, 128, lane);
+        if constexpr (LATE) {
+          const OperandDecoder<KD> dec(stage, lane);
+          mfma_block(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, 128, lane);
+        } else {
+          mfma_block(
+              sh,
+              [&](int pp, h16x8(&A4)[4]) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) A4[j] = A[pp][j];
+              },
+              cl, nq, 128, lane);
+        }
       } else if (active && (lane & 15) == 0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -714,12 +770,17 @@ int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens, bo
          (fold ? 0 : (int64_t)n_tokens * ((hidden / 128 + 3) / 4) * 8);
 }
 
-hipError_t flow_groups_per_cu(int k_gu, int k_dn, int* n) {
-  const void* f = k_gu == 2 && k_dn == 3   ? (const void*)k_stack_flow<2, 3>
-                  : k_gu == 2 && k_dn == 2 ? (const void*)k_stack_flow<2, 2>
-                  : k_gu == 3 && k_dn == 3 ? (const void*)k_stack_flow<3, 3>
-                  : k_gu == 3 && k_dn == 2 ? (const void*)k_stack_flow<3, 2>
-                                           : nullptr;
+template <bool LATE>
+const void* flow_kernel(int k_gu, int k_dn) {
+  return k_gu == 2 && k_dn == 3   ? (const void*)k_stack_flow<2, 3, LATE>
+         : k_gu == 2 && k_dn == 2 ? (const void*)k_stack_flow<2, 2, LATE>
+         : k_gu == 3 && k_dn == 3 ? (const void*)k_stack_flow<3, 3, LATE>
+         : k_gu == 3 && k_dn == 2 ? (const void*)k_stack_flow<3, 2, LATE>
+                                  : nullptr;
+}
+
+hipError_t flow_groups_per_cu(int k_gu, int k_dn, bool late, int* n) {
+  const void* f = late ? flow_kernel<true>(k_gu, k_dn) : flow_kernel<false>(k_gu, k_dn);
   if (!f) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, f, 64 * kWaves, 0);
 }
@@ -728,18 +789,11 @@ hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t 
   const int64_t blocks =
       flow_blocks_per_layer(a.hidden, a.inter, a.top_k, a.n_tokens, a.fold != 0) * a.n_layers +
       kFlowSpare;
-  const dim3 grid((unsigned)blocks), block(64 * kWaves);
-  if (k_gu == 2 && k_dn == 3)
-    hipLaunchKernelGGL((k_stack_flow<2, 3>), grid, block, 0, s, a);
-  else if (k_gu == 2 && k_dn == 2)
-    hipLaunchKernelGGL((k_stack_flow<2, 2>), grid, block, 0, s, a);
-  else if (k_gu == 3 && k_dn == 3)
-    hipLaunchKernelGGL((k_stack_flow<3, 3>), grid, block, 0, s, a);
-  else if (k_gu == 3 && k_dn == 2)
-    hipLaunchKernelGGL((k_stack_flow<3, 2>), grid, block, 0, s, a);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  const void* f = a.late ? flow_kernel<true>(k_gu, k_dn) : flow_kernel<false>(k_gu, k_dn);
+  if (!f) return hipErrorInvalidValue;
+  FlowArgs arg = a;
+  void* args[] = {&arg};
+  return hipLaunchKernel(f, dim3((unsigned)blocks), dim3(64 * kWaves), args, 0, s);
 }
 
 }  // namespace escha
