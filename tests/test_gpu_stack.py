@@ -213,14 +213,16 @@ def test_flow_sampled_vs_oracle(escha, stack, T):
                       [1, T - 2], [0, 1, 20, NL - 2, NL - 1], SEED, f"T={T}")
 
 
-def test_flow_deterministic_and_graph_replay(escha, stack):
+@pytest.mark.parametrize("T", [1, 8])
+def test_flow_deterministic_and_graph_replay(escha, stack, T):
     """Two calls on one workspace give the same bits; so does every replay of
-    a captured graph, with eager work and synchronisation between replays."""
-    announce("one-launch stack: repeat calls and graph replays, T=1")
-    x0, logits = synth.stack_token_inputs(SEED, NL, 1, 6)
+    a captured graph, with eager work and synchronisation between replays
+    (decode before the wait at 1 token, after it at 8)."""
+    announce(f"one-launch stack: repeat calls and graph replays, T={T}")
+    x0, logits = synth.stack_token_inputs(SEED, NL, T, 6)
     ids, w = _route(escha, logits)
     x0d = to_dev(x0)
-    ws = torch.zeros(stack.workspace_bytes(1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda")
     y1, c1 = _flow(escha, stack, x0d, ids, w, ws)
     y2, c2 = _flow(escha, stack, x0d, ids, w, ws)
     assert escha.escha_moe_stack_status(ws) == 0
@@ -244,13 +246,15 @@ def test_flow_deterministic_and_graph_replay(escha, stack):
         assert torch.equal(chain, c1), f"replay {rep}: layer inputs differ"
 
 
-def test_flow_small_stack_edge_cases(escha):
-    """3 layers x 16 experts, 3 tokens: out-of-range expert ids (the pair
-    contributes zero), an expert whose up-projection output is pruned on a
-    whole 128-channel chunk (that down chunk is skipped), and n_tokens that
-    is not a multiple of anything; every layer checked against the oracle."""
-    announce("one-launch small stack, bad ids and pruned chunk, T=3")
-    E, NLs, T = 16, 3, 3
+@pytest.mark.parametrize("T", [3, 9])
+def test_flow_small_stack_edge_cases(escha, T):
+    """3 layers x 16 experts, 3 or 9 tokens (decode before / after the wait):
+    out-of-range expert ids (the pair contributes zero), an expert whose
+    up-projection output is pruned on a whole 128-channel chunk (that down
+    chunk is skipped), and n_tokens that is not a multiple of anything; every
+    layer checked against the oracle."""
+    announce(f"one-launch small stack, bad ids and pruned chunk, T={T}")
+    E, NLs = 16, 3
     host = [synth.layer_tensors(11, l, n_experts=E) for l in range(NLs)]
     # expert 5 of layer 1: up rows 0..127 of the intermediate have rout = 0
     host[1]["gu_rout"][5, synth.INTER:synth.INTER + 128] = 0
@@ -286,7 +290,7 @@ def test_flow_small_stack_edge_cases(escha):
 
 
 @pytest.mark.parametrize("hidden,inter,k,T", [(1024, 256, 4, 5), (1024, 512, 6, 2), (2048, 256, 8, 3),
-                                              (1024, 256, 10, 2)])
+                                              (1024, 256, 10, 2), (1024, 256, 4, 12), (2048, 256, 8, 10)])
 def test_flow_other_shapes(escha, hidden, inter, k, T):
     """The one-launch kernel away from the benchmark's shapes: hidden 1024
     (two gate_up input parts), inter 256 (two channel chunks), top_k 4 and 6
