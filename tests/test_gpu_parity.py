@@ -438,6 +438,31 @@ def test_grouped_small_batches_and_bad_ids(escha, layer2, layer2_dev, T):
     assert_close(y, ref, f"grouped T={T}")
 
 
+@pytest.mark.parametrize("T", [20, 48])
+def test_small_tile_decode_bad_ids(escha, layer2, layer2_dev, T):
+    """The decode entry from 16 tokens (the one-launch small-tile layer):
+    ids below 0 or at/above the expert count contribute nothing, the other
+    pairs are exact to tolerance, pruned channels stay exactly zero."""
+    announce(f"small-tile decode, T={T}, bad ids")
+    x = synth.activations(60 + T, T, 2048)
+    ids, w = oracle.route_topk(synth.normal_logits(60 + T, T), 8)
+    bad = ids.copy()
+    bad[0, 5] = 256
+    bad[T - 1, 0] = -1
+    bad[T // 2, 7] = 1 << 20
+    inter = torch.empty(T * 8, 512, dtype=torch.float32, device="cuda")
+    y = escha.escha_moe_layer_decode(layer2_dev, to_dev(x), to_dev(bad), to_dev(w.astype(np.float32)),
+                                     inter_out=inter).cpu().numpy()
+    w0 = w.astype(np.float32).copy()
+    w0[bad != ids] = 0.0
+    ref, ref_inter = oracle.moe_layer(layer2, x, ids, w0, want_inter=True)
+    assert_close(y, ref, f"small-tile decode T={T} with bad ids")
+    got = inter.cpu().numpy()
+    ok = (bad == ids).reshape(-1)
+    assert_close(got[ok], ref_inter[ok], f"small-tile decode T={T} h")
+    assert np.all(got[ok][ref_inter[ok] == 0] == 0)
+
+
 def test_grouped_one_hot_expert(escha, layer2, layer2_dev):
     """Every token routed to the same 8 experts: 130 tokens per expert = 3 tiles."""
     announce("grouped, all tokens on the same experts")
