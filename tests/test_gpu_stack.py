@@ -321,3 +321,46 @@ def test_flow_other_shapes(escha, hidden, inter, k, T):
         else:
             mx, frac = _bf16_steps(ch[l + 1], oracle.rmsnorm_bf16(ref))
             assert mx <= 1 and frac < 0.02, f"layer {l}: {mx} steps on {frac:.3%}"
+
+
+@pytest.mark.parametrize("hidden,inter,k,T", [(2048, 512, 8, 20), (1024, 256, 4, 37), (2048, 256, 6, 16),
+                                              (1024, 256, 10, 16)])
+def test_grouped_stack_linked_shapes(escha, hidden, inter, k, T):
+    """The layer-by-layer grouped stack (16 tokens and more) away from the
+    benchmark's shapes, with the one-launch small-tile layer kernel and the
+    kernel that links two layers (combine, RMSNorm, the next layer's rotated
+    inputs): token counts that are not a multiple of 8, hidden 1024, top_k
+    4, 6 and 10, out-of-range and negative expert ids, a pruned 128-channel
+    chunk. The stack must equal its single-layer calls chained with the
+    RMSNorm, bit for bit, with and without the chain written out, and its
+    last layer must match the oracle on the chain's input."""
+    announce(f"grouped stack links, hidden={hidden} inter={inter} top_k={k} T={T}")
+    E, NLs = 16, 3
+    host = [synth.layer_tensors(31, l, n_experts=E, hidden=hidden, inter=inter) for l in range(NLs)]
+    host[1]["gu_rout"][3, inter:inter + 128] = 0
+    layers = [layer_to_dev(L, top_k=k) for L in host]
+    st = escha.Stack(layers)
+    rs = np.random.default_rng(hidden + inter + k + T)
+    ids = np.stack([np.stack([rs.permutation(E)[:k] for _ in range(T)]) for _ in range(NLs)])
+    ids = ids.astype(np.int32)
+    ids[1, :3, 0] = 3
+    ids[0, 1, 2] = -1
+    ids[1, T - 1, k - 1] = E  # out of range
+    w = rs.random((NLs, T, k)).astype(np.float32)
+    x0 = synth.activations(31, T, hidden, layer=5)
+    idd, wd, x0d = to_dev(ids), to_dev(w), to_dev(x0)
+    ws = torch.zeros(st.workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    chain = torch.empty(NLs, T, hidden, dtype=torch.int16, device="cuda")
+    y = escha.escha_moe_stack_decode(st, x0d, idd, wd, x_chain=chain, workspace=ws)
+    y2 = escha.escha_moe_stack_decode(st, x0d, idd, wd, workspace=ws)  # no chain written
+    x = x0d
+    for l in range(NLs):
+        assert torch.equal(chain[l], x), f"layer {l} input differs"
+        yl = escha.escha_moe_layer_decode(layers[l], x, idd[l].contiguous(), wd[l].contiguous())
+        x = escha.escha_rmsnorm_bf16(yl)
+    assert torch.equal(y, yl)
+    assert torch.equal(y2, yl)
+    bad = (ids[-1] < 0) | (ids[-1] >= E)
+    ref = oracle.moe_layer(host[-1], u16(chain)[-1], np.where(bad, 0, ids[-1]).astype(np.int32),
+                           np.where(bad, 0.0, w[-1]).astype(np.float32))
+    assert_close(y.cpu().numpy(), ref, f"linked stack {hidden}/{inter}/{k} last layer")
