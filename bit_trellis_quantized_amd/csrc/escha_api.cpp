@@ -385,8 +385,8 @@ int run_layer_grouped(const escha_moe_layer_t* L, const uint16_t* x, int T, cons
     if (rc) return rc;
   }
   if (gather) {
-    escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.perm, g.offsets, E, L->hidden,
-                         L->top_k, g.xg, g.xg_exp};
+    escha::GatherArgs ga{x, (const uint16_t*)L->gate_up.rin, ids, g.inv, P, L->hidden, L->top_k, g.xg,
+                         g.xg_exp};
     e = escha::launch_xin_gather(ga, P, s);
     if (e != hipSuccess) return hip_fail(e, "input gather launch");
   }

@@ -113,19 +113,29 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
 // is at most 16 max|rin (.) x| in magnitude (the 128 terms of a row of
 // H_n each have magnitude 1/sqrt(128) < 16/128), so e is taken from that
 // bound: 2^13 <= 16 max|rin (.) x| 2^e < 2^14, and the rotated values stay
-// below 2^14. grid.x = n_pairs, block = 256 (each 16 lanes one 128-input
-// block, 8 consecutive inputs per lane).
+// below 2^14. One wave per pair, kGatherRows consecutive pairs per
+// work-group (with top_k 8, one token's: its input row is fetched once and
+// read by the group from the cache), each written to its sorted row: lane l
+// takes inputs 8 l .. 8 l + 7 of every 512-input chunk, so each 16 lanes
+// hold one 128-input block; rows of up to kGatherHeld chunks stay in
+// registers between the row maximum and the transform (every load issued
+// up front), longer rows are read twice.
 // ------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
-  __shared__ float wmax[4];
-  const int i = blockIdx.x;
-  if (i >= a.offsets[a.n_experts]) return;
-  const int p = a.perm[i];
+constexpr int kGatherRows = 8;
+constexpr int kGatherHeld = 4;
+
+__global__ __launch_bounds__(64 * kGatherRows) void k_xin_gather(GatherArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int p = kGatherRows * blockIdx.x + (threadIdx.x >> 6);
+  if (p >= a.n_pairs) return;  // uniform over the wave
+  const int i = a.inv[p];
+  if (i < 0) return;  // an out-of-range expert id: no row
   const int e = a.ids[p];
   const int t = p / a.top_k;
-  const int lane = threadIdx.x & 63;
-  const uint16_t* xrow = a.x_bf16 + (size_t)t * a.hidden;
-  const uint16_t* rrow = a.rin + (size_t)e * a.hidden;
+  const int H = a.hidden;
+  const int nch = (H + 511) / 512;
+  const uint16_t* xrow = a.x_bf16 + (size_t)t * H;
+  const uint16_t* rrow = a.rin + (size_t)e * H;
   auto load8 = [&](int base, float (&v)[8]) {
     const u32x4 xq = *reinterpret_cast<const u32x4*>(xrow + base);
     const u32x4 rq = *reinterpret_cast<const u32x4*>(rrow + base);
@@ -135,30 +145,13 @@ __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
       v[2 * q + 1] = bf16_to_f32((uint16_t)(xq[q] >> 16)) * f16_to_f32((uint16_t)(rq[q] >> 16));
     }
   };
-  // the row's largest |rin (.) x| -> its exponent
-  float m = 0.f;
-  for (int base = 8 * threadIdx.x; base < a.hidden; base += 8 * 256) {
-    float v[8];
-    load8(base, v);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
-  }
-  m = wave_max(m);
-  if (lane == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  int ex = fp16_block_exp(16.0f * m);
-  if (ex == kExpZeroBlock) ex = 0;
-  if (threadIdx.x == 0) a.xg_exp[i] = ex;
-  const float scale = kInvSqrt128 * exp2i(ex);
   // The butterflies run in fwht128's order (bit 6, then bits 0-5), so the
   // rounded results are the same: bit 6 and bits 3-5 across lanes, bits
-  // 0-2 inside the lane.
+  // 0-2 inside the lane. The 16 lanes of a block are all in or all out of
+  // the row (hidden is a multiple of 128).
   const float s1 = lane_sign(lane, 1), s2 = lane_sign(lane, 2), s4 = lane_sign(lane, 4);
   const float s8 = lane_sign(lane, 8);
-  for (int base = 8 * threadIdx.x; base < a.hidden; base += 8 * 256) {
-    float v[8];
-    load8(base, v);
+  auto transform_store = [&](int base, float (&v)[8], float scale) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = butterfly<8>(v[q], s8);  // bit 6
 #pragma unroll
@@ -179,7 +172,48 @@ __global__ __launch_bounds__(256) void k_xin_gather(GatherArgs a) {
       const _Float16 hi = (_Float16)(v[2 * q + 1] * scale);
       o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
-    *reinterpret_cast<u32x4*>(a.xg + (size_t)i * a.hidden + base) = o;
+    *reinterpret_cast<u32x4*>(a.xg + (size_t)i * H + base) = o;
+  };
+  // the row's largest |rin (.) x| -> its exponent
+  auto row_scale = [&](float m) {
+    m = wave_max(m);
+    int ex = fp16_block_exp(16.0f * m);
+    if (ex == kExpZeroBlock) ex = 0;
+    if (lane == 0) a.xg_exp[i] = ex;
+    return kInvSqrt128 * exp2i(ex);
+  };
+  if (nch <= kGatherHeld) {
+    float v[kGatherHeld][8];
+    float m = 0.f;
+#pragma unroll
+    for (int j = 0; j < kGatherHeld; ++j) {
+      const int base = 8 * lane + 512 * j;
+      if (j < nch && base < H) {
+        load8(base, v[j]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[j][q]));
+      }
+    }
+    const float scale = row_scale(m);
+#pragma unroll
+    for (int j = 0; j < kGatherHeld; ++j) {
+      const int base = 8 * lane + 512 * j;
+      if (j < nch && base < H) transform_store(base, v[j], scale);
+    }
+  } else {
+    float m = 0.f;
+    for (int base = 8 * lane; base < H; base += 512) {
+      float v[8];
+      load8(base, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+    }
+    const float scale = row_scale(m);
+    for (int base = 8 * lane; base < H; base += 512) {
+      float v[8];
+      load8(base, v);
+      transform_store(base, v, scale);
+    }
   }
 }
 
@@ -1416,7 +1450,9 @@ hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tile
 }
 
 hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s) {
-  hipLaunchKernelGGL(k_xin_gather, dim3(n_pairs), dim3(256), 0, s, a);
+  if (n_pairs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_xin_gather, dim3((unsigned)((n_pairs + kGatherRows - 1) / kGatherRows)),
+                     dim3(64 * kGatherRows), 0, s, a);
   return hipGetLastError();
 }
 

@@ -93,9 +93,8 @@ struct GatherArgs {
   const uint16_t* x_bf16;  // [T][hidden]
   const uint16_t* rin;     // gate_up rin [E][hidden]
   const int32_t* ids;      // [T*top_k]
-  const int32_t* perm;     // sorted index -> pair
-  const int32_t* offsets;  // [E+1]; offsets[E] = number of sorted pairs
-  int32_t n_experts, hidden, top_k;
+  const int32_t* inv;      // pair -> sorted index (-1: the pair has no row)
+  int32_t n_pairs, hidden, top_k;
   uint16_t* xg;            // fp16 [P][hidden] at the sorted index, row i scaled by 2^xg_exp[i]
   int32_t* xg_exp;         // [P]: each row's power-of-two exponent
 };
