@@ -238,6 +238,11 @@ constexpr int32_t kGroupedDecodeTokens = 16;
 // One-launch stack: from this many tokens its tasks decode after their wait
 // (three work-groups per compute unit instead of two).
 constexpr int32_t kFlowLateTokens = 8;
+// With top_k <= 8, from kFlowWideTokens to kFlowWideMaxTokens tokens its
+// tasks are 4 waves holding two chunks' decoded operands per wave instead
+// (measured faster than both 8-wave forms there).
+constexpr int32_t kFlowWideTokens = 3;
+constexpr int32_t kFlowWideMaxTokens = 16;
 constexpr int32_t kTileTokens = 128;      // tokens per grouped tile (escha_grouped.hip)
 constexpr int32_t kSmallTileTokens = 16;  // tokens per small tile
 
@@ -1119,9 +1124,12 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   int dev = 0, n_cu = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
-  // from kFlowLateTokens tokens the tasks decode after their wait
-  const bool late = n_tokens >= kFlowLateTokens;
-  if (e == hipSuccess) e = escha::flow_groups_per_cu(L0->gate_up.k_bits, L0->down.k_bits, late, &per_cu);
+  // the 4-wave form between kFlowWideTokens and kFlowWideMaxTokens tokens;
+  // otherwise from kFlowLateTokens tokens the tasks decode after their wait
+  const bool wide = k <= 8 && n_tokens >= kFlowWideTokens && n_tokens <= kFlowWideMaxTokens;
+  const bool late = !wide && n_tokens >= kFlowLateTokens;
+  if (e == hipSuccess)
+    e = escha::flow_groups_per_cu(L0->gate_up.k_bits, L0->down.k_bits, late, wide, &per_cu);
   if (e != hipSuccess) return hip_fail(e, "device query");
   const int64_t p8 = (T * k + 7) / 8 * 8;
   const bool fold = k <= 8 && (p8 / 8) * (H / 128) <= (int64_t)(n_cu / 8) * per_cu;
@@ -1170,6 +1178,7 @@ int escha_moe_stack_decode_persistent(const escha_moe_layer_t* layers, int32_t n
   a.error = ctl + 1;
   a.fold = fold ? 1 : 0;
   a.late = late ? 1 : 0;
+  a.wide = wide ? 1 : 0;
 
   // status, tickets and flags to zero, the call number one further
   e = escha::launch_flow_prepare(ctl, (size_t)f.ctl_ints, s);

@@ -186,6 +186,8 @@ struct FlowArgs {
   int32_t* error;      // 1: a wait gave up
   int32_t fold;        // 1: the down tasks combine the pair outputs (no combine tasks)
   int32_t late;        // 1: tasks decode after their wait (three work-groups per compute unit)
+  int32_t wide;        // 1: 4-wave tasks holding two chunks' operands per wave (decode before the
+                       // wait, fold only; three work-groups per compute unit)
 };
 constexpr int kFlowSpare = 64;  // work-groups launched beyond the task count (8 per XCD)
 
@@ -195,8 +197,8 @@ int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens, bo
 hipError_t launch_flow_prepare(int32_t* ctl, size_t n, hipStream_t s);
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s);
 // Work-groups of the one-launch kernel (late: the form that decodes after
-// the wait) that one compute unit holds at once.
-hipError_t flow_groups_per_cu(int k_gu, int k_dn, bool late, int* n);
+// the wait; wide: the 4-wave form) that one compute unit holds at once.
+hipError_t flow_groups_per_cu(int k_gu, int k_dn, bool late, bool wide, int* n);
 
 // n_layers tile lists at once (layer l: offsets + l (E + 1), t_* + l max_tiles,
 // n_tiles + l).

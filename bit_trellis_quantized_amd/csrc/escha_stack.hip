@@ -236,19 +236,27 @@ __device__ __forceinline__ bool all_ok(const Lds& sh) {
 // 16 (4nq + j) + n of the task).
 // OPS: the operands of tile-row pair pp, OPS(pp, A4) (decoded beforehand,
 // or just now when the task decodes after its wait).
-template <class OPS>
+// LEAN: each B operand is read from LDS just before its pair's MFMAs
+// instead of all four up front (12 fewer registers live at the start of
+// the contraction, for a form that holds 128 registers of operands).
+template <bool LEAN = false, class OPS>
 __device__ __forceinline__ void mfma_block(Lds& sh, OPS&& ops, int cl, int nq, int stride, int lane) {
   // B operands of the four tile-row pairs: column 0 of B = high parts,
   // column 1 = low parts, other columns zero; only the lanes of columns 0
   // and 1 read LDS
   const int col = lane & 15;
+  const _Float16* src = (col == 0 ? sh.xh[cl] : sh.xl[cl]) + 8 * (lane >> 4);
+  auto load_b = [&](int pp) {
+    return col < 2 ? *reinterpret_cast<const h16x8*>(src + 32 * pp) : h16x8{};
+  };
   h16x8 B[4];
+  if constexpr (!LEAN) {
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) B[pp] = h16x8{};
-  if (col < 2) {
-    const _Float16* src = (col == 0 ? sh.xh[cl] : sh.xl[cl]) + 8 * (lane >> 4);
+    for (int pp = 0; pp < 4; ++pp) B[pp] = h16x8{};
+    if (col < 2) {
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) B[pp] = *reinterpret_cast<const h16x8*>(src + 32 * pp);
+      for (int pp = 0; pp < 4; ++pp) B[pp] = *reinterpret_cast<const h16x8*>(src + 32 * pp);
+    }
   }
   f32x4 D[4];
 #pragma unroll
@@ -257,9 +265,10 @@ __device__ __forceinline__ void mfma_block(Lds& sh, OPS&& ops, int cl, int nq, i
   for (int pp = 0; pp < 4; ++pp) {
     h16x8 A[4];
     ops(pp, A);
+    const h16x8 Bp = LEAN ? load_b(pp) : B[pp];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], B[pp], D[j], 0, 0, 0);
+      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], Bp, D[j], 0, 0, 0);
   }
   float4 zr[4];
   finish_mfma(D, sh.xe[cl], zr);
@@ -277,21 +286,28 @@ __device__ __forceinline__ void mfma_block(Lds& sh, OPS&& ops, int cl, int nq, i
 // D[m][2 q + h] with m = 8 set + c collects output column c (parity 0) or
 // c + 8 (parity 1) over the set's input rows. The two sets' sums go to
 // sh.red[set] and are added in sum_transform_store.
-template <class OPS>
+template <bool LEAN = false, class OPS>
 __device__ __forceinline__ void mfma_pairs(Lds& sh, OPS&& ops, int cl, int nq, int lane) {
   const int col = lane & 15;
   const int g = lane >> 4;
+  const int set = col >> 2, par = (col >> 1) & 1;
+  // input rows 8 set + 4 (g & 1) + i of tile-row 2 pp + (g >> 1): inputs
+  // 32 pp + 16 (g >> 1) + 8 set + 4 (g & 1) + i of the chunk
+  const _Float16* src = ((col & 1) ? sh.xl[cl] : sh.xh[cl]) + 16 * (g >> 1) + 8 * set + 4 * (g & 1);
+  // LEAN: the four pairs' activations kept packed (2 registers each) and
+  // spread into B just before use
+  u32x2 Braw[4];
   h16x8 B[4];
 #pragma unroll
-  for (int pp = 0; pp < 4; ++pp) B[pp] = h16x8{};
+  for (int pp = 0; pp < 4; ++pp) {
+    Braw[pp] = u32x2{0u, 0u};
+    B[pp] = h16x8{};
+  }
   if (col < 8) {
-    const int set = col >> 2, par = (col >> 1) & 1;
-    // input rows 8 set + 4 (g & 1) + i of tile-row 2 pp + (g >> 1): inputs
-    // 32 pp + 16 (g >> 1) + 8 set + 4 (g & 1) + i of the chunk
-    const _Float16* src = ((col & 1) ? sh.xl[cl] : sh.xh[cl]) + 16 * (g >> 1) + 8 * set + 4 * (g & 1);
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp) {
-      B[pp] = parity_operand(*reinterpret_cast<const u32x2*>(src + 32 * pp), par);
+      Braw[pp] = *reinterpret_cast<const u32x2*>(src + 32 * pp);
+      if constexpr (!LEAN) B[pp] = parity_operand(Braw[pp], par);
     }
   }
   f32x4 D[4];
@@ -301,9 +317,10 @@ __device__ __forceinline__ void mfma_pairs(Lds& sh, OPS&& ops, int cl, int nq, i
   for (int pp = 0; pp < 4; ++pp) {
     h16x8 A[4];
     ops(pp, A);
+    const h16x8 Bp = LEAN ? (col < 8 ? parity_operand(Braw[pp], par) : h16x8{}) : B[pp];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], B[pp], D[j], 0, 0, 0);
+      D[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], Bp, D[j], 0, 0, 0);
   }
   // high + low part into the even columns (finish_mfma), then lanes (col
   // 4 set + 2 parity, g) with set = g >> 1 hold outputs 8 parity + 4 (g &
@@ -386,8 +403,16 @@ __device__ __forceinline__ void store_combined(const FlowArgs& a, bool last, int
 // rather than 64 registers of operands while it waits and three work-groups
 // fit on a compute unit (larger batches, where a layer's tasks are many
 // times the device's slots, so decode ahead of the chain matters little).
-template <int KG, int KD, bool LATE>
-__global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const FlowArgs a) {
+// WIDE (decode before the wait, top_k <= 8): a task is 4 waves, each
+// holding the decoded operands of two chunks (128 registers), and three
+// work-groups share a compute unit: the device then holds 1.5 times the
+// decoded weights of the 8-wave form (two work-groups of 8 waves with 64
+// registers of operands each).
+template <int KG, int KD, bool LATE, bool WIDE = false>
+__global__ __launch_bounds__(WIDE ? 256 : 64 * kWaves, LATE ? 6 : (WIDE ? 3 : 4)) void k_stack_flow(
+    const FlowArgs a) {
+  static_assert(!(LATE && WIDE), "the wide form decodes before its wait");
+  constexpr int CPW = WIDE ? 2 : 1;  // chunks per wave
   __shared__ Lds sh;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -428,15 +453,16 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     // ------------------------------------------------------------ gate_up
     // task (pair p, inputs 512 hh .. 512 hh + 511, outputs 128 g .. 128 g +
     // 127); wave w: input chunk cl = w / 2 of the four (its 8 tile-rows),
-    // output tiles 4 nq .. 4 nq + 3 (nq = w % 2) of the block
-    const int cl = wave >> 1;
+    // output tiles 4 nq .. 4 nq + 3 (nq = w % 2) of the block (WIDE: input
+    // chunks 2 (w / 2) and 2 (w / 2) + 1)
+    const int cl = WIDE ? 2 * (wave >> 1) : wave >> 1;  // first chunk of the wave
     const int nq = wave & 1;
     const int p = r % P8;
     if (p >= P) return;
     r /= P8;
     const int g = r % ngb;
     const int hh = r / ngb;
-    const int c = kChunks * hh + cl;  // this wave's input chunk
+    const int c = kChunks * hh + cl;  // this wave's (first) input chunk
     const int t = p / k;
     const int x = p & 7;
     const int e = a.ids[(size_t)l * P + p];
@@ -448,33 +474,49 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     // which keeps the register state the same on every path
     const int es = valid ? e : 0;
     const uint16_t* code_e = Ly.gu_code + (size_t)es * (size_t)ncg * 8 * n_nt * (16 * KG);
-    u32x4 cv[Stage<KG>::kPerLane];
-    stage_issue<KG>(code_e, n_nt, 8 * c, 8 * g + 4 * nq, lane, cv);
+    u32x4 cv[CPW][Stage<KG>::kPerLane];
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) stage_issue<KG>(code_e, n_nt, 8 * (c + ci), 8 * g + 4 * nq, lane, cv[ci]);
     // the chunk's input scales and the block's output scales, kept in LDS
-    // until they are needed
-    const uint16_t* rr = Ly.gu_rin + (size_t)es * H + c * 128;
+    // until they are needed (WIDE: wave w loads chunk w's, wave 1 also the
+    // output scales)
+    const int cn = WIDE ? wave : cl;  // the chunk this wave normalises (nq == 0 or WIDE)
+    const uint16_t* rr = Ly.gu_rin + (size_t)es * H + (kChunks * hh + cn) * 128;
     const uint16_t* ro = Ly.gu_rout + (size_t)es * (2 * I) + g * 128;
-    const uint16_t* rs = nq == 0 ? rr : ro;
+    const uint16_t* rs = (WIDE || nq == 0) ? rr : ro;
     const uint16_t s0 = rs[lane], s1 = rs[lane + 64];
-    uint32_t* stage = sh.code + wave * Stage<KG>::kDw;
-    stage_store<KG>(stage, lane, cv);
-    float* sd = nq == 0 ? sh.rin[cl] : sh.rout;
-    if (nq == 0 || wave == 1) {
+    uint16_t o0 = 0, o1 = 0;
+    if (WIDE && wave == 1) {
+      o0 = ro[lane];
+      o1 = ro[lane + 64];
+    }
+    uint32_t* stage = sh.code + CPW * wave * Stage<KG>::kDw;
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci) stage_store<KG>(stage + ci * Stage<KG>::kDw, lane, cv[ci]);
+    float* sd = (WIDE || nq == 0) ? sh.rin[cn] : sh.rout;
+    if (WIDE || nq == 0 || wave == 1) {
       sd[lane] = f16_to_f32(s0);
       sd[lane + 64] = f16_to_f32(s1);
     }
-    h16x8 A[4][4];
+    if (WIDE && wave == 1) {
+      sh.rout[lane] = f16_to_f32(o0);
+      sh.rout[lane + 64] = f16_to_f32(o1);
+    }
+    h16x8 A[CPW][4][4];
     if constexpr (!LATE) {
-      if constexpr (KG == 2) {  // column-pair layout: 9 VALU operations per pair of weights
-        const PairDecoder dec(stage, lane);
-        dec.template decode<0>(A[0]);
-        dec.template decode<1>(A[1]);
-        dec.template decode<2>(A[2]);
-        dec.template decode<3>(A[3]);
-      } else {
-        decode_stage_mfma<KG>(stage, lane, A);
+#pragma unroll
+      for (int ci = 0; ci < CPW; ++ci) {
+        if constexpr (KG == 2) {  // column-pair layout: 9 VALU operations per pair of weights
+          const PairDecoder dec(stage + ci * Stage<KG>::kDw, lane);
+          dec.template decode<0>(A[ci][0]);
+          dec.template decode<1>(A[ci][1]);
+          dec.template decode<2>(A[ci][2]);
+          dec.template decode<3>(A[ci][3]);
+        } else {
+          decode_stage_mfma<KG>(stage + ci * Stage<KG>::kDw, lane, A[ci]);
+        }
+        pin_operands(A[ci]);
       }
-      pin_operands(A);
     }
     // arguments the normalisation needs, read now rather than after the wait
     float eps = a.eps;
@@ -482,17 +524,18 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     uint16_t* x_chain = a.x_chain;
     asm volatile("" : "+s"(eps), "+s"(inv_h), "+s"(x_chain));
     __syncthreads();  // sh.ok initialised
-    if (nq == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
+    if (WIDE || nq == 0) {  // one wave per chunk: x~ = H_n(rin (.) x)
+      const int cc = kChunks * hh + cn;
       float x0, x1;
       if (l == 0) {
-        const uint16_t* xr = a.x0 + (size_t)t * H + c * 128;
+        const uint16_t* xr = a.x0 + (size_t)t * H + cc * 128;
         x0 = bf16_to_f32(xr[lane]);
         x1 = bf16_to_f32(xr[lane + 64]);
       } else {
         // the previous layer's combine tasks of this token on this XCD wrote
         // the chunk's outputs y and every block's sum of squares: RMSNorm,
         // rounded to bf16
-        const uint64_t* yr = a.ycb + ((size_t)t * 8 + x) * H + c * 128 + lane;
+        const uint64_t* yr = a.ycb + ((size_t)t * 8 + x) * H + cc * 128 + lane;
         const uint64_t* sr = a.sscb + ((size_t)t * 8 + x) * 32 + (lane < ncg ? lane : 0);
         float v[3];
         const bool ok = wave_fetch<3>([&](int i) { return i < 2 ? yr + 64 * i : sr; }, 3, tag - 1u, v,
@@ -509,37 +552,40 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
         x1 = bf16_to_f32(b1);
       }
       if (x_chain && g == 0 && p % k == 0) {  // the layer input, recorded by one pair per token
-        uint16_t* xo = x_chain + ((size_t)l * T + t) * H + c * 128;
+        uint16_t* xo = x_chain + ((size_t)l * T + t) * H + cc * 128;
         xo[lane] = f32_to_bf16_rne(x0);
         xo[lane + 64] = f32_to_bf16_rne(x1);
       }
-      float v0 = x0 * sh.rin[cl][lane];
-      float v1 = x1 * sh.rin[cl][lane + 64];
+      float v0 = x0 * sh.rin[cn][lane];
+      float v1 = x1 * sh.rin[cn][lane + 64];
       fwht128(v0, v1);
-      const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cl], sh.xl[cl], lane);
-      if (lane == 0) sh.xe[cl] = xe;
+      const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cn], sh.xl[cn], lane);
+      if (lane == 0) sh.xe[cn] = xe;
     }
     __syncthreads();
     if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
-      auto held = [&](int pp, h16x8(&A4)[4]) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) A4[j] = A[pp][j];
-      };
-      if constexpr (KG == 2) {
-        if constexpr (LATE) {
-          const PairDecoder dec(stage, lane);
-          mfma_pairs(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, lane);
+      for (int ci = 0; ci < CPW; ++ci) {
+        auto held = [&](int pp, h16x8(&A4)[4]) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) A4[j] = A[ci][pp][j];
+        };
+        if constexpr (KG == 2) {
+          if constexpr (LATE) {
+            const PairDecoder dec(stage, lane);
+            mfma_pairs(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, lane);
+          } else {
+            mfma_pairs<WIDE>(sh, held, cl + ci, nq, lane);
+          }
         } else {
-          mfma_pairs(sh, held, cl, nq, lane);
-        }
-      } else {
-        if constexpr (LATE) {
-          const OperandDecoder<KG> dec(stage, lane);
-          mfma_block(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, 128, lane);
-        } else {
-          mfma_block(sh, held, cl, nq, 128, lane);
+          if constexpr (LATE) {
+            const OperandDecoder<KG> dec(stage, lane);
+            mfma_block(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, 128, lane);
+          } else {
+            mfma_block<WIDE>(sh, held, cl + ci, nq, 128, lane);
+          }
         }
       }
       __syncthreads();
@@ -552,37 +598,56 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     // --------------------------------------------------------------- down
     // task (pair p, outputs 128 g .. 128 g + 127); wave w: channel chunk
     // cl = w / 2 (its 8 tile-rows), output tiles 4 nq .. 4 nq + 3 (nq = w % 2)
-    const int cl = wave >> 1;
+    // (WIDE: channel chunks 2 (w / 2) and 2 (w / 2) + 1)
+    const int cl = WIDE ? 2 * (wave >> 1) : wave >> 1;
     const int nq = wave & 1;
     const int p = r % P8;
     if (p >= P) return;
     const int g = r / P8;
     const int e = a.ids[(size_t)l * P + p];
     const bool valid = e >= 0 && e < a.n_experts;
-    const bool active = cl < ncd;  // this wave has tile-rows
+    const bool active = cl < ncd;  // this wave has tile-rows (of its first chunk)
+    const int cn = WIDE ? wave : cl;  // the chunk this wave forms h of (nq == 0 or WIDE)
+    const bool nactive = cn < ncd;
     const int n_nt = H / 16;
     uint64_t* out = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)p * H + g * 128;
 
     const int es = valid ? e : 0;
     const uint16_t* code_e = Ly.dn_code + (size_t)es * (size_t)ncd * 8 * n_nt * (16 * KD);
-    u32x4 cv[Stage<KD>::kPerLane];
-    if (active) stage_issue<KD>(code_e, n_nt, 8 * cl, 8 * g + 4 * nq, lane, cv);
-    const uint16_t* rr = Ly.dn_rin + (size_t)es * I + (active ? cl : 0) * 128;
+    u32x4 cv[CPW][Stage<KD>::kPerLane];
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci)
+      if (cl + ci < ncd) stage_issue<KD>(code_e, n_nt, 8 * (cl + ci), 8 * g + 4 * nq, lane, cv[ci]);
+    const uint16_t* rr = Ly.dn_rin + (size_t)es * I + (nactive ? cn : 0) * 128;
     const uint16_t* ro = Ly.dn_rout + (size_t)es * H + g * 128;
-    const uint16_t* rs = nq == 0 ? rr : ro;
+    const uint16_t* rs = (WIDE || nq == 0) ? rr : ro;
     const uint16_t s0 = rs[lane], s1 = rs[lane + 64];
+    uint16_t o0 = 0, o1 = 0;
+    if (WIDE && wave == 1) {
+      o0 = ro[lane];
+      o1 = ro[lane + 64];
+    }
     const float wt = a.w[(size_t)l * P + p];
-    uint32_t* stage = sh.code + wave * Stage<KD>::kDw;
-    h16x8 A[4][4];
-    if (active) stage_store<KD>(stage, lane, cv);
-    float* sd = nq == 0 ? sh.rin[cl] : sh.rout;
-    if ((nq == 0 && active) || wave == 1) {
+    uint32_t* stage = sh.code + CPW * wave * Stage<KD>::kDw;
+    h16x8 A[CPW][4][4];
+#pragma unroll
+    for (int ci = 0; ci < CPW; ++ci)
+      if (cl + ci < ncd) stage_store<KD>(stage + ci * Stage<KD>::kDw, lane, cv[ci]);
+    float* sd = (WIDE || nq == 0) ? sh.rin[cn] : sh.rout;
+    if (((WIDE || nq == 0) && nactive) || (!WIDE && wave == 1)) {
       sd[lane] = f16_to_f32(s0);
       sd[lane + 64] = f16_to_f32(s1);
     }
+    if (WIDE && wave == 1) {
+      sh.rout[lane] = f16_to_f32(o0);
+      sh.rout[lane + 64] = f16_to_f32(o1);
+    }
     if constexpr (!LATE) {
-      if (active) decode_stage_mfma<KD>(stage, lane, A);
-      pin_operands(A);
+#pragma unroll
+      for (int ci = 0; ci < CPW; ++ci) {
+        if (cl + ci < ncd) decode_stage_mfma<KD>(stage + ci * Stage<KD>::kDw, lane, A[ci]);
+        pin_operands(A[ci]);
+      }
     }
     __syncthreads();  // sh.ok initialised
     // gate and up sums of the chunk's channels over gate_up's input parts,
@@ -590,23 +655,38 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     // wave nq fetches parts 2 nq and 2 nq + 1, and the sum is (part 0 +
     // part 1) + (part 2 + part 3)
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (active && valid && 2 * nq < nh) {
-      const uint64_t* src = a.gu_part + ((size_t)p * nh + 2 * nq) * (2 * I) + 128 * cl + lane;
-      auto word = [&](int i) {  // part 2 nq + i / 4; gate, gate + 64, up, up + 64
+    // parts 2 h and 2 h + 1 of chunk ch's gate and up sums, from 0
+    auto fetch_half = [&](int ch, int h, float4& out) {
+      const uint64_t* src = a.gu_part + ((size_t)p * nh + 2 * h) * (2 * I) + 128 * ch + lane;
+      auto word = [&](int i) {  // part 2 h + i / 4; gate, gate + 64, up, up + 64
         return src + (size_t)(i >> 2) * (2 * I) + ((i & 1) ? 64 : 0) + ((i & 2) ? I : 0);
       };
-      const bool ok = wave_fetch_sum4(word, nh - 2 * nq < 2 ? nh - 2 * nq : 2, tag,
-                                      make_float4(0.f, 0.f, 0.f, 0.f), sum, a.error);
-      if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
-      if (nq == 1) sh.part[cl][lane] = sum;
+      return wave_fetch_sum4(word, nh - 2 * h < 2 ? nh - 2 * h : 2, tag, make_float4(0.f, 0.f, 0.f, 0.f),
+                             out, a.error);
+    };
+    float4 second = make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (WIDE) {
+      // one wave per chunk fetches both halves
+      if (nactive && valid) {
+        bool ok = fetch_half(cn, 0, sum);
+        if (nh > 2) ok = ok && fetch_half(cn, 1, second);
+        if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
+      }
+    } else {
+      if (active && valid && 2 * nq < nh) {
+        const bool ok = fetch_half(cl, nq, sum);
+        if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
+        if (nq == 1) sh.part[cl][lane] = sum;
+      }
+      if (nh > 2) __syncthreads();  // second halves in LDS
+      if (nq == 0 && active && valid && nh > 2) second = sh.part[cl][lane];
     }
-    if (nh > 2) __syncthreads();  // second halves in LDS
-    if (nq == 0 && active) {  // one wave per 128-channel chunk
+    if ((WIDE || nq == 0) && nactive) {  // one wave per 128-channel chunk
       int skip = 1;
       if (valid) {
         __builtin_amdgcn_s_setprio(3);
         if (nh > 2) {
-          const float4 q = sh.part[cl][lane];
+          const float4 q = second;
           sum.x += q.x;
           sum.y += q.y;
           sum.z += q.z;
@@ -616,37 +696,41 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
         const float h0 = silu_fast(g0) * u0;
         const float h1 = silu_fast(g1) * u1;
         skip = __ballot((h0 != 0.f) || (h1 != 0.f)) == 0;
-        float v0 = h0 * sh.rin[cl][lane];
-        float v1 = h1 * sh.rin[cl][lane + 64];
+        float v0 = h0 * sh.rin[cn][lane];
+        float v1 = h1 * sh.rin[cn][lane + 64];
         fwht128(v0, v1);
-        const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cl], sh.xl[cl], lane);
-        if (lane == 0) sh.xe[cl] = xe;
+        const float xe = split_hilo(v0 * kInvSqrt128, v1 * kInvSqrt128, sh.xh[cn], sh.xl[cn], lane);
+        if (lane == 0) sh.xe[cn] = xe;
       }
       // a chunk whose h is all zero contributes exactly zero: its MAC is skipped
-      if (lane == 0) sh.skip[cl] = skip;
+      if (lane == 0) sh.skip[cn] = skip;
     }
     __syncthreads();
     if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
     if (valid) {  // uniform over the group
-      if (active && !sh.skip[cl]) {
-        if constexpr (LATE) {
-          const OperandDecoder<KD> dec(stage, lane);
-          mfma_block(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, 128, lane);
-        } else {
-          mfma_block(
-              sh,
-              [&](int pp, h16x8(&A4)[4]) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) A4[j] = A[pp][j];
-              },
-              cl, nq, 128, lane);
+      for (int ci = 0; ci < CPW; ++ci) {
+        const int ch = cl + ci;
+        if (ch < ncd && !sh.skip[ch]) {
+          if constexpr (LATE) {
+            const OperandDecoder<KD> dec(stage, lane);
+            mfma_block(sh, [&](int pp, h16x8(&A4)[4]) { decode_pp(dec, pp, A4); }, cl, nq, 128, lane);
+          } else {
+            mfma_block<WIDE>(
+                sh,
+                [&](int pp, h16x8(&A4)[4]) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) A4[j] = A[ci][pp][j];
+                },
+                ch, nq, 128, lane);
+          }
+        } else if (ch < ncd && (lane & 15) == 0) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(&sh.red[0][128 * ch + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
+                make_float4(0.f, 0.f, 0.f, 0.f);
         }
-      } else if (active && (lane & 15) == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<float4*>(&sh.red[0][128 * cl + 16 * (4 * nq + j) + 4 * (lane >> 4)]) =
-              make_float4(0.f, 0.f, 0.f, 0.f);
       }
       __syncthreads();
       sum_transform_store<true>(sh, ncd, wt, out, tag, wave, lane);
@@ -702,7 +786,7 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     const int x_first = (t * k) & 7;
     const bool last = l == a.n_layers - 1;
     if (last ? x != x_first : (k < 8 && ((x - x_first) & 7) >= k)) return;
-    const int b = 4 * hf + (wave >> 1);  // this wave's 128-block
+    const int b = 4 * hf + (WIDE ? wave : wave >> 1);  // this wave's 128-block
     if (wave == 0) {
       // the down tasks of the token's pairs for these outputs have flagged
       const int32_t* df = a.dflag + ((size_t)l * P8 + (size_t)t * k) * a.df_pair + 4 * hf;
@@ -715,6 +799,29 @@ __global__ __launch_bounds__(64 * kWaves, LATE ? 6 : 4) void k_stack_flow(const 
     if (!all_ok(sh)) return;
     __builtin_amdgcn_s_setprio(3);
     const int half = (k + 1) / 2;
+    if constexpr (WIDE) {
+      // one wave per block (top_k <= 8): both halves of the slots, each
+      // summed from zero in order, then added (first + second)
+      if (b < nb) {
+        const uint64_t* pp = a.dn_part + (size_t)(l & 1) * a.dn_copy + (size_t)(t * k) * H + 128 * b + lane;
+        float v[16];
+        const bool ok = wave_fetch<16>([&](int i) { return pp + (size_t)(i >> 1) * H + ((i & 1) ? 64 : 0); },
+                                       2 * k, tag, v, a.error);
+        float f0 = 0.f, f1 = 0.f, s0 = 0.f, s1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (j < half) {
+            f0 += v[2 * j];
+            f1 += v[2 * j + 1];
+          } else if (j < k) {
+            s0 += v[2 * j];
+            s1 += v[2 * j + 1];
+          }
+        }
+        if (ok) store_combined(a, last, t, x, b, lane, f0 + s0, f1 + s1, tag);
+      }
+      return;
+    }
     const int j0 = (wave & 1) ? half : 0;  // this wave's slots j0 .. j1 - 1
     const int j1 = (wave & 1) ? k : half;
     const uint64_t* pp =
@@ -770,30 +877,38 @@ int64_t flow_blocks_per_layer(int hidden, int inter, int top_k, int n_tokens, bo
          (fold ? 0 : (int64_t)n_tokens * ((hidden / 128 + 3) / 4) * 8);
 }
 
-template <bool LATE>
+template <bool LATE, bool WIDE>
 const void* flow_kernel(int k_gu, int k_dn) {
-  return k_gu == 2 && k_dn == 3   ? (const void*)k_stack_flow<2, 3, LATE>
-         : k_gu == 2 && k_dn == 2 ? (const void*)k_stack_flow<2, 2, LATE>
-         : k_gu == 3 && k_dn == 3 ? (const void*)k_stack_flow<3, 3, LATE>
-         : k_gu == 3 && k_dn == 2 ? (const void*)k_stack_flow<3, 2, LATE>
+  return k_gu == 2 && k_dn == 3   ? (const void*)k_stack_flow<2, 3, LATE, WIDE>
+         : k_gu == 2 && k_dn == 2 ? (const void*)k_stack_flow<2, 2, LATE, WIDE>
+         : k_gu == 3 && k_dn == 3 ? (const void*)k_stack_flow<3, 3, LATE, WIDE>
+         : k_gu == 3 && k_dn == 2 ? (const void*)k_stack_flow<3, 2, LATE, WIDE>
                                   : nullptr;
 }
 
-hipError_t flow_groups_per_cu(int k_gu, int k_dn, bool late, int* n) {
-  const void* f = late ? flow_kernel<true>(k_gu, k_dn) : flow_kernel<false>(k_gu, k_dn);
+const void* flow_kernel(int k_gu, int k_dn, bool late, bool wide) {
+  return late ? flow_kernel<true, false>(k_gu, k_dn)
+              : (wide ? flow_kernel<false, true>(k_gu, k_dn) : flow_kernel<false, false>(k_gu, k_dn));
+}
+
+hipError_t flow_groups_per_cu(int k_gu, int k_dn, bool late, bool wide, int* n) {
+  if (late && wide) return hipErrorInvalidValue;
+  const void* f = flow_kernel(k_gu, k_dn, late, wide);
   if (!f) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, f, 64 * kWaves, 0);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(n, f, wide ? 256 : 64 * kWaves, 0);
 }
 
 hipError_t launch_stack_flow(const FlowArgs& a, int k_gu, int k_dn, hipStream_t s) {
+  // the wide form decodes before its wait, and its combine tasks take top_k <= 8
+  if (a.wide && (a.late || a.top_k > 8)) return hipErrorInvalidValue;
   const int64_t blocks =
       flow_blocks_per_layer(a.hidden, a.inter, a.top_k, a.n_tokens, a.fold != 0) * a.n_layers +
       kFlowSpare;
-  const void* f = a.late ? flow_kernel<true>(k_gu, k_dn) : flow_kernel<false>(k_gu, k_dn);
+  const void* f = flow_kernel(k_gu, k_dn, a.late != 0, a.wide != 0);
   if (!f) return hipErrorInvalidValue;
   FlowArgs arg = a;
   void* args[] = {&arg};
-  return hipLaunchKernel(f, dim3((unsigned)blocks), dim3(64 * kWaves), args, 0, s);
+  return hipLaunchKernel(f, dim3((unsigned)blocks), dim3(a.wide ? 256 : 64 * kWaves), args, 0, s);
 }
 
 }  // namespace escha

@@ -213,11 +213,12 @@ def test_flow_sampled_vs_oracle(escha, stack, T):
                       [1, T - 2], [0, 1, 20, NL - 2, NL - 1], SEED, f"T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 4, 8, 20])
 def test_flow_deterministic_and_graph_replay(escha, stack, T):
     """Two calls on one workspace give the same bits; so does every replay of
     a captured graph, with eager work and synchronisation between replays
-    (decode before the wait at 1 token, after it at 8)."""
+    (decode before the wait at 1 token, the same in 4-wave tasks at 4 and 8,
+    after the wait at 20)."""
     announce(f"one-launch stack: repeat calls and graph replays, T={T}")
     x0, logits = synth.stack_token_inputs(SEED, NL, T, 6)
     ids, w = _route(escha, logits)
@@ -246,9 +247,11 @@ def test_flow_deterministic_and_graph_replay(escha, stack, T):
         assert torch.equal(chain, c1), f"replay {rep}: layer inputs differ"
 
 
-@pytest.mark.parametrize("T", [3, 9])
+@pytest.mark.parametrize("T", [3, 7, 20])
 def test_flow_small_stack_edge_cases(escha, T):
-    """3 layers x 16 experts, 3 or 9 tokens (decode before / after the wait):
+    """3 layers x 16 experts, 3, 7 or 20 tokens (4-wave tasks with the
+    combine folded into the down tasks, 4-wave tasks with combine tasks,
+    8-wave tasks decoding after their wait):
     out-of-range expert ids (the pair contributes zero), an expert whose
     up-projection output is pruned on a whole 128-channel chunk (that down
     chunk is skipped), and n_tokens that is not a multiple of anything; every
@@ -290,13 +293,14 @@ def test_flow_small_stack_edge_cases(escha, T):
 
 
 @pytest.mark.parametrize("hidden,inter,k,T", [(1024, 256, 4, 5), (1024, 512, 6, 2), (2048, 256, 8, 3),
-                                              (1024, 256, 10, 2), (1024, 256, 4, 12), (2048, 256, 8, 10)])
+                                              (1024, 256, 10, 2), (1024, 256, 4, 12), (2048, 256, 8, 10),
+                                              (1024, 256, 10, 9)])
 def test_flow_other_shapes(escha, hidden, inter, k, T):
     """The one-launch kernel away from the benchmark's shapes: hidden 1024
     (two gate_up input parts), inter 256 (two channel chunks), top_k 4 and 6
     (the combine folded into the down tasks, fewer experts than XCDs) and 10
-    (combine tasks, two pairs of a token on one XCD); every layer against the
-    oracle."""
+    (combine tasks, two pairs of a token on one XCD; at 9 tokens in the 8-wave
+    tasks that decode after their wait); every layer against the oracle."""
     announce(f"one-launch stack, hidden={hidden} inter={inter} top_k={k} T={T}")
     E, NLs = 16, 3
     host = [synth.layer_tensors(21, l, n_experts=E, hidden=hidden, inter=inter) for l in range(NLs)]
