@@ -123,6 +123,7 @@ __global__ __launch_bounds__(1024) void k_make_tiles(const int32_t* __restrict__
 // ------------------------------------------------------------------------
 constexpr int kGatherRows = 8;
 constexpr int kGatherHeld = 4;
+constexpr int kGatherSmallPairs = 8192;  // below: k_xin_gather_small
 
 __global__ __launch_bounds__(64 * kGatherRows) void k_xin_gather(GatherArgs a) {
   const int lane = threadIdx.x & 63;
@@ -214,6 +215,75 @@ __global__ __launch_bounds__(64 * kGatherRows) void k_xin_gather(GatherArgs a) {
       load8(base, v);
       transform_store(base, v, scale);
     }
+  }
+}
+
+// The same rows for small batches, where the work-groups of k_xin_gather
+// would be too few to spread over the device: one work-group of 256 threads
+// per pair (16 lanes per 128-input block, 8 inputs per lane), the row
+// maximum across the four waves in LDS; the same arithmetic in the same
+// order.
+__global__ __launch_bounds__(256) void k_xin_gather_small(GatherArgs a) {
+  __shared__ float wmax[4];
+  const int p = blockIdx.x;
+  const int i = a.inv[p];
+  if (i < 0) return;  // uniform: an out-of-range expert id has no row
+  const int e = a.ids[p];
+  const int t = p / a.top_k;
+  const int lane = threadIdx.x & 63;
+  const int H = a.hidden;
+  const uint16_t* xrow = a.x_bf16 + (size_t)t * H;
+  const uint16_t* rrow = a.rin + (size_t)e * H;
+  auto load8 = [&](int base, float (&v)[8]) {
+    const u32x4 xq = *reinterpret_cast<const u32x4*>(xrow + base);
+    const u32x4 rq = *reinterpret_cast<const u32x4*>(rrow + base);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf16_to_f32((uint16_t)(xq[q] & 0xFFFFu)) * f16_to_f32((uint16_t)(rq[q] & 0xFFFFu));
+      v[2 * q + 1] = bf16_to_f32((uint16_t)(xq[q] >> 16)) * f16_to_f32((uint16_t)(rq[q] >> 16));
+    }
+  };
+  float m = 0.f;
+  for (int base = 8 * threadIdx.x; base < H; base += 8 * 256) {
+    float v[8];
+    load8(base, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));
+  }
+  m = wave_max(m);
+  if (lane == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  int ex = fp16_block_exp(16.0f * m);
+  if (ex == kExpZeroBlock) ex = 0;
+  if (threadIdx.x == 0) a.xg_exp[i] = ex;
+  const float scale = kInvSqrt128 * exp2i(ex);
+  const float s1 = lane_sign(lane, 1), s2 = lane_sign(lane, 2), s4 = lane_sign(lane, 4);
+  const float s8 = lane_sign(lane, 8);
+  for (int base = 8 * threadIdx.x; base < H; base += 8 * 256) {
+    float v[8];
+    load8(base, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = butterfly<8>(v[q], s8);  // bit 6
+#pragma unroll
+    for (int h = 1; h <= 4; h <<= 1)  // bits 0-2
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (!(q & h)) {
+          const float lo = v[q], hi = v[q + h];
+          v[q] = lo + hi;
+          v[q + h] = lo - hi;
+        }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = butterfly<4>(butterfly<2>(butterfly<1>(v[q], s1), s2), s4);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const _Float16 lo = (_Float16)(v[2 * q] * scale);
+      const _Float16 hi = (_Float16)(v[2 * q + 1] * scale);
+      o[q] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    *reinterpret_cast<u32x4*>(a.xg + (size_t)i * H + base) = o;
   }
 }
 
@@ -1451,8 +1521,11 @@ hipError_t launch_make_tiles(const int32_t* offsets, int E, int tm, int max_tile
 
 hipError_t launch_xin_gather(const GatherArgs& a, int n_pairs, hipStream_t s) {
   if (n_pairs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_xin_gather, dim3((unsigned)((n_pairs + kGatherRows - 1) / kGatherRows)),
-                     dim3(64 * kGatherRows), 0, s, a);
+  if (n_pairs < kGatherSmallPairs)
+    hipLaunchKernelGGL(k_xin_gather_small, dim3((unsigned)n_pairs), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_xin_gather, dim3((unsigned)((n_pairs + kGatherRows - 1) / kGatherRows)),
+                       dim3(64 * kGatherRows), 0, s, a);
   return hipGetLastError();
 }
 
