@@ -122,6 +122,8 @@ def parse():
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert timing")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--probe-every", type=int, default=4,
+                    help="probe events in every n-th of the pooled steps (each probe node lengthens its step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=16)
     ap.add_argument("--workload", choices=["stack", "layer", "copy", "router"], default="stack",
@@ -366,13 +368,14 @@ def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
             logits=torch.from_numpy(logits.reshape(NL * T, E).copy()).cuda(),
             y=torch.empty(T, hidden, dtype=torch.float32, device="cuda"),
             ws=torch.zeros(stack.workspace_bytes(T), dtype=torch.uint8, device="cuda"),
-            probes=None if args.no_probe else [hip.event() for _ in range(n_probe)],
+            probes=None if args.no_probe or r % max(1, args.probe_every) else
+            [hip.event() for _ in range(n_probe)],
         ))
 
     def step(p, probes=True):
         ids, w = escha.escha_route_topk(p["logits"], k)
         p["ids"], p["w"] = ids, w  # keep the graph's buffers alive
-        ev = p["probes"] if probes else None
+        ev = p["probes"] if probes else None  # None on the pool entries without probes
         if one_launch:
             escha.escha_moe_stack_decode_persistent(stack, p["x0"], ids.view(NL, T, k), w.view(NL, T, k),
                                                     out=p["y"], workspace=p["ws"],
@@ -441,6 +444,8 @@ def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
     probe_ms, per_step_probe = [], []
     if not args.no_probe:
         for p in ran:
+            if p["probes"] is None:
+                continue
             ms = [hip.elapsed_ms(p["probes"][2 * j], p["probes"][2 * j + 1]) for j in range(n_probe // 2)]
             probe_ms += ms
             per_step_probe.append(sum(ms))
@@ -475,7 +480,9 @@ def time_stack(args, escha, synth, hip, stack, T, steps, warmup, log):
     if one_launch:  # every timed call completed (no wait gave up)
         status = int(max(escha.escha_moe_stack_status(p["ws"]) for p in pool))
     if roofline is not None:
-        roofline["probe"] = ("HIP events recorded as graph nodes in the timed replays" if probe_in_graph
+        n_probed = sum(1 for p in pool if p["probes"] is not None)
+        roofline["probe"] = ((f"HIP events recorded as graph nodes in the timed replays ({n_probed} of the {R} "
+                              "pooled steps carry them)") if probe_in_graph
                              else "HIP events around eager launches after the timed replays"
                              if use_graph else "HIP events in the timed (eager) steps")
     res = dict(T=T, path=path, one_launch=one_launch, use_graph=use_graph, ms_per_step=ms_per_step,
@@ -499,8 +506,9 @@ LAYER_CONFIGS = {
 def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, n_inputs=8):
     """One MoE layer call per step (config 2, 3 or 5), each step on the next
     of the given resident layers; the calls of a sweep over the layers are
-    captured in one graph. Probe events around each call's gate_up and down
-    projection kernels (escha_probe_events_set) give the kernels' time."""
+    captured in one graph. Probe events around the gate_up and down
+    projection kernels (escha_probe_events_set) of every probe_every-th call
+    give the kernels' time."""
     import torch
     c = LAYER_CONFIGS[cfg]
     T, prefill = c["T"], c["prefill"]
@@ -517,6 +525,7 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
                      device="cuda")
     y = torch.empty(T, synth.HIDDEN, dtype=torch.float32, device="cuda")
     probe_ev = [(hip.event(), hip.event()) for _ in range(NLc)]
+    pe = max(1, args.probe_every)  # calls l with l % pe == 0 carry probe events
     routed = [None] * NLc
 
     # the decode configs route inside the layer call (the router step in the
@@ -531,7 +540,7 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
             if prefill:
                 escha.escha_route_topk(inp["logits"], k, ids=ids, w=w)
             routed[l] = (ids, w)
-            escha.escha_probe_events_set(probe_ev[l] if probes else None)
+            escha.escha_probe_events_set(probe_ev[l] if probes and l % pe == 0 else None)
             try:
                 if prefill:
                     fn(layers[l], inp["x"], ids, w, out=y, workspace=ws)
@@ -577,14 +586,15 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
     if use_graph and not probe_in_graph:
         sweep()  # eager calls with plain probe records, after the timed region
         torch.cuda.synchronize()
-    proj_ms = float(np.mean([hip.elapsed_ms(a, b) for a, b in probe_ev]))
+    proj_ms = float(np.mean([hip.elapsed_ms(a, b) for l, (a, b) in enumerate(probe_ev) if l % pe == 0]))
     distinct = float(np.mean([len(set(ids.cpu().numpy().ravel().tolist())) for ids, _ in routed]))
     code_bytes = distinct * (GU_BYTES_PER_PAIR + DN_BYTES_PER_PAIR)
     entry = {"workload": c["name"], "tokens": T, "value": round(T / (ms / 1e3), 2), "unit": "tokens/s",
              "us_per_layer": round(ms * 1e3, 3), "calls": calls, "graph": use_graph,
              "distinct_experts": round(distinct, 2), "layers_cycled": NLc,
              "probe_ok": proj_ms <= ms * 1.02,
-             "probe": ("HIP events recorded as graph nodes in the timed replays" if probe_in_graph
+             "probe": (f"HIP events recorded as graph nodes in the timed replays (every {pe}th call)"
+                       if probe_in_graph
                        else "HIP events around eager calls after the timed replays" if use_graph
                        else "HIP events in the timed (eager) calls")}
     if not entry["probe_ok"]:
@@ -596,13 +606,13 @@ def time_layer_config(args, escha, synth, hip, layers, cfg, steps, warmup, log, 
             "kernel": "k_grouped_gate_up + k_grouped_down (fp16 MFMA 32x32x16, fp32 accumulate)",
             "bound": "mfma", "achieved": round(achieved, 1), "peak": 2500.0, "unit": "TFLOP/s",
             "frac": round(achieved / 2500.0, 4), "traffic": measured_traffic("layer_cfg5"),
-            "flops_per_launch": flops, "avg_launch_us": round(proj_ms * 1e3, 3), "samples": NLc,
+            "flops_per_launch": flops, "avg_launch_us": round(proj_ms * 1e3, 3), "samples": -(-NLc // pe),
             "code_bytes": int(code_bytes), "code_gbs": round(code_bytes / (proj_ms / 1e3) / 1e9, 1)}
     else:
         kernel = ("k_in_partial (with the router step) + k_down_partial (streaming decode)" if T < 16 else
                   "k_small_layer (small-tile gate_up and down blocks in one launch, MFMA 16x16x32)")
         entry["roofline"] = roofline_hbm(kernel, code_bytes, proj_ms,
-                                         measured_traffic("layer_cfg2" if T < 16 else "layer_cfg3"), NLc,
+                                         measured_traffic("layer_cfg2" if T < 16 else "layer_cfg3"), -(-NLc // pe),
                                          DECODE_OPS_PER_WEIGHT if T < 16 else DECODE_OPS_PAIRED_GU)
     return entry
 
