@@ -235,14 +235,15 @@ int run_layer_decode(const escha_moe_layer_t* L, const LayerInput& in, int T, co
 // this many tokens take the grouped path: pairs sorted by expert, each
 // weight tile decoded once for all of an expert's tokens in a tile.
 constexpr int32_t kGroupedDecodeTokens = 16;
-// One-launch stack: from this many tokens its tasks decode after their wait
-// (three work-groups per compute unit instead of two).
-constexpr int32_t kFlowLateTokens = 8;
-// With top_k <= 8, from kFlowWideTokens to kFlowWideMaxTokens tokens its
-// tasks are 4 waves holding two chunks' decoded operands per wave instead
-// (measured faster than both 8-wave forms there).
-constexpr int32_t kFlowWideTokens = 3;
+// One-launch stack: with top_k <= 8, from kFlowWideTokens to
+// kFlowWideMaxTokens tokens its tasks are 4 waves holding two chunks'
+// decoded operands per wave (three work-groups per compute unit; measured
+// faster than both 8-wave forms there). Otherwise from kFlowLateTokens
+// tokens its 8-wave tasks decode after their wait (three work-groups per
+// compute unit), and below that before it (two).
+constexpr int32_t kFlowWideTokens = 1;
 constexpr int32_t kFlowWideMaxTokens = 16;
+constexpr int32_t kFlowLateTokens = 8;
 constexpr int32_t kTileTokens = 128;      // tokens per grouped tile (escha_grouped.hip)
 constexpr int32_t kSmallTileTokens = 16;  // tokens per small tile
 

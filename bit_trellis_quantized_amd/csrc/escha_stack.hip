@@ -1,8 +1,9 @@
 // escha_stack.hip -- decode of a whole stack of MoE layers in one launch
 // (small batches: the token-by-token generation case).
 //
-// Every task of every layer is one work-group of 8 waves (two work-groups
-// share a compute unit), and the tasks are numbered in dependency order:
+// Every task of every layer is one work-group (8 waves, or 4 in the wide
+// form; two or three work-groups share a compute unit), and the tasks are
+// numbered in dependency order:
 // layer by layer, first the layer's gate_up tasks, then its down tasks, then
 // (larger batches only) its combine tasks.
 //   gate_up (pair p, part hh = four 128-input chunks, 128-output block g):
@@ -220,6 +221,7 @@ struct Lds {
   int skip[kChunks];
   int ok[kWaves];
   int task;
+  float wt;  // down: the pair's router weight (kept here across the wait)
 };
 
 // True when no wave of the group recorded a failed wait; after a barrier.
@@ -627,7 +629,7 @@ __global__ __launch_bounds__(WIDE ? 256 : 64 * kWaves, LATE ? 6 : (WIDE ? 3 : 4)
       o0 = ro[lane];
       o1 = ro[lane + 64];
     }
-    const float wt = a.w[(size_t)l * P + p];
+    const float wt_ld = a.w[(size_t)l * P + p];
     uint32_t* stage = sh.code + CPW * wave * Stage<KD>::kDw;
     h16x8 A[CPW][4][4];
 #pragma unroll
@@ -649,7 +651,8 @@ __global__ __launch_bounds__(WIDE ? 256 : 64 * kWaves, LATE ? 6 : (WIDE ? 3 : 4)
         pin_operands(A[ci]);
       }
     }
-    __syncthreads();  // sh.ok initialised
+    if (tid == 0) sh.wt = wt_ld;
+    __syncthreads();  // sh.ok and sh.wt initialised
     // gate and up sums of the chunk's channels over gate_up's input parts,
     // once every gate_up task of this pair has written them: the chunk's
     // wave nq fetches parts 2 nq and 2 nq + 1, and the sum is (part 0 +
@@ -669,7 +672,14 @@ __global__ __launch_bounds__(WIDE ? 256 : 64 * kWaves, LATE ? 6 : (WIDE ? 3 : 4)
       // one wave per chunk fetches both halves
       if (nactive && valid) {
         bool ok = fetch_half(cn, 0, sum);
-        if (nh > 2) ok = ok && fetch_half(cn, 1, second);
+        if (nh > 2) {
+          ok = ok && fetch_half(cn, 1, second);
+          sum.x += second.x;
+          sum.y += second.y;
+          sum.z += second.z;
+          sum.w += second.w;
+          second = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         if (lane == 0) sh.ok[wave] = ok ? 1 : 0;
       }
     } else {
@@ -685,7 +695,7 @@ __global__ __launch_bounds__(WIDE ? 256 : 64 * kWaves, LATE ? 6 : (WIDE ? 3 : 4)
       int skip = 1;
       if (valid) {
         __builtin_amdgcn_s_setprio(3);
-        if (nh > 2) {
+        if (!WIDE && nh > 2) {
           const float4 q = second;
           sum.x += q.x;
           sum.y += q.y;
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(WIDE ? 256 : 64 * kWaves, LATE ? 6 : (WIDE ? 3 : 4)
         }
       }
       __syncthreads();
-      sum_transform_store<true>(sh, ncd, wt, out, tag, wave, lane);
+      sum_transform_store<true>(sh, ncd, sh.wt, out, tag, wave, lane);
     } else if (wave == 0) {  // an out-of-range expert id contributes nothing
       st_remote64(out + lane, tag_word(0.f, tag));
       st_remote64(out + lane + 64, tag_word(0.f, tag));

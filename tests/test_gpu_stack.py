@@ -217,8 +217,8 @@ def test_flow_sampled_vs_oracle(escha, stack, T):
 def test_flow_deterministic_and_graph_replay(escha, stack, T):
     """Two calls on one workspace give the same bits; so does every replay of
     a captured graph, with eager work and synchronisation between replays
-    (decode before the wait at 1 token, the same in 4-wave tasks at 4 and 8,
-    after the wait at 20)."""
+    (4-wave tasks decoding before the wait at 1, 4 and 8 tokens, 8-wave
+    tasks decoding after it at 20)."""
     announce(f"one-launch stack: repeat calls and graph replays, T={T}")
     x0, logits = synth.stack_token_inputs(SEED, NL, T, 6)
     ids, w = _route(escha, logits)
