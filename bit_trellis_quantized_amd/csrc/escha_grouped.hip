@@ -1184,12 +1184,26 @@ __global__ __launch_bounds__(64) void k_combine_sorted(SortedCombineArgs a) {
   const int t = blockIdx.x / nb;
   const int lane = threadIdx.x;
   float acc0 = 0.f, acc1 = 0.f;
-  for (int j = 0; j < a.top_k; ++j) {
-    const int i = a.inv[t * a.top_k + j];
-    if (i < 0) continue;
-    const float* yr = a.rows + (size_t)i * a.hidden + 128 * b;
-    acc0 += yr[lane];
-    acc1 += yr[lane + 64];
+  // slots in groups of 8: every load of a group issued before its adds (a
+  // slot without a row reads row 0 and adds nothing)
+  const int k = a.top_k;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int iv[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) iv[q] = j0 + q < k ? a.inv[t * k + j0 + q] : -1;
+    float v0[8], v1[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float* yr = a.rows + (size_t)(iv[q] >= 0 ? iv[q] : 0) * a.hidden + 128 * b;
+      v0[q] = yr[lane];
+      v1[q] = yr[lane + 64];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (iv[q] >= 0) {
+        acc0 += v0[q];
+        acc1 += v1[q];
+      }
   }
   if (a.bias) {  // the dense export's output bias, after the sum
     acc0 += a.bias[128 * b + lane];

@@ -338,6 +338,8 @@ __global__ __launch_bounds__(512) void k_down_partial(DownPartialArgs a) {
 // ------------------------------------------------------------------------
 // Finish one projection per pair: the fixed-order sum of its chunks.
 // grid.x = n_pairs * (out_f / 128), block = 64.
+constexpr int kCombineRows = 32;  // partial rows whose loads are all issued before the first add
+
 // ------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
   const int nb = a.out_f / 128;
@@ -346,10 +348,21 @@ __global__ __launch_bounds__(64) void k_proj_finish(FinishArgs a) {
   const int lane = threadIdx.x;
   float z0 = 0.f, z1 = 0.f;
   const float* pp = a.partial + (size_t)p * a.n_chunks * a.out_f + 128 * b;
-#pragma unroll 8
-  for (int cc = 0; cc < a.n_chunks; ++cc) {
-    z0 += pp[(size_t)cc * a.out_f + lane];
-    z1 += pp[(size_t)cc * a.out_f + lane + 64];
+  // every load of a group of kCombineRows chunks issued before the adds
+  for (int c0 = 0; c0 < a.n_chunks; c0 += kCombineRows) {
+    float v0[kCombineRows], v1[kCombineRows];
+#pragma unroll
+    for (int q = 0; q < kCombineRows; ++q) {
+      const int cc = c0 + q < a.n_chunks ? c0 + q : a.n_chunks - 1;  // clamped: read, not added
+      v0[q] = pp[(size_t)cc * a.out_f + lane];
+      v1[q] = pp[(size_t)cc * a.out_f + lane + 64];
+    }
+#pragma unroll
+    for (int q = 0; q < kCombineRows; ++q)
+      if (c0 + q < a.n_chunks) {
+        z0 += v0[q];
+        z1 += v1[q];
+      }
   }
   if (a.bias) {
     z0 += a.bias[128 * b + lane];
@@ -373,10 +386,22 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
   const int n = a.top_k * a.n_chunks;  // partial rows of this token, in order
   const float* pp = a.partial + (size_t)t * n * a.hidden + 128 * b;
   float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll 8
-  for (int r = 0; r < n; ++r) {
-    acc0 += pp[(size_t)r * a.hidden + lane];
-    acc1 += pp[(size_t)r * a.hidden + lane + 64];
+  // groups of kCombineRows rows: every load of a group issued first (one
+  // round trip per group), then the adds in row order
+  for (int r0 = 0; r0 < n; r0 += kCombineRows) {
+    float v0[kCombineRows], v1[kCombineRows];
+#pragma unroll
+    for (int q = 0; q < kCombineRows; ++q) {
+      const int r = r0 + q < n ? r0 + q : n - 1;  // clamped: the row is read, not added
+      v0[q] = pp[(size_t)r * a.hidden + lane];
+      v1[q] = pp[(size_t)r * a.hidden + lane + 64];
+    }
+#pragma unroll
+    for (int q = 0; q < kCombineRows; ++q)
+      if (r0 + q < n) {
+        acc0 += v0[q];
+        acc1 += v1[q];
+      }
   }
   if (a.bias) {  // the dense export's output bias, after the sum
     acc0 += a.bias[128 * b + lane];
