@@ -177,8 +177,17 @@ __global__ __launch_bounds__(256) void k_in_partial(InPartialArgs a) {
       // RMSNorm of the previous layer's output row, rounded to bf16
       const int nb = a.in_f / 128;
       const float* ss = a.ss_prev + (size_t)t * nb;
+      // the blocks' sums of squares added in block order, the loads of each
+      // group of 16 issued before its adds
       float tot = 0.f;
-      for (int b = 0; b < nb; ++b) tot += ss[b];
+      for (int b0 = 0; b0 < nb; b0 += 16) {
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) v[q] = ss[b0 + q < nb ? b0 + q : nb - 1];
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          if (b0 + q < nb) tot += v[q];
+      }
       const float inv = 1.0f / sqrtf(tot / (float)a.in_f + a.eps);
       const float* yr = a.y_prev + (size_t)t * a.in_f + c * 128;
       const uint16_t b0 = f32_to_bf16_rne(yr[lane] * inv);
